@@ -1,0 +1,442 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the group-quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load this file's library. The product path
+ * (the HIP library under quantized_gemm_q4_amd/) shares no code with it and
+ * never calls it.
+ *
+ * Every function follows the formulas of the quantization pages, written out
+ * step by step with no blocking, fusion or reordering:
+ *   - "Quantization operators guide" = blog.freezetheflame.cc, "Quantization
+ *     operators from basics to practice: INT8/INT4/FP8".
+ *   - "Core ideas" = ai-infra.cypggs.com, "2. Core ideas: numeric
+ *     representation, rounding, scaling and difficulty migration".
+ *   - "Method boundaries" = llm-glossary.tokens-kit.com, "Method boundaries
+ *     of GPTQ, AWQ, SmoothQuant and FP8".
+ *   - "Quantization notes" = learn.longtimenohack.com, chasing/quantization.
+ *
+ * Arithmetic rules. The quantizers decide integers (codes, zero-points) from
+ * floating point, so they run in IEEE binary32 with round-to-nearest-even:
+ * true division, no FMA contraction (built with -ffp-contract=off), rintf()
+ * under the default FE_TONEAREST mode. The GEMM references are exact: fp64
+ * sums of exactly dequantized operands (W4A16) and int64 sums (W8A8).
+ *
+ * Precondition for every function: inputs are finite. Non-finite inputs give
+ * unspecified codes.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16 <-> binary32, written from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; exponent 0 holds
+ * zero and the subnormals (fraction * 2^-24), exponent 31 holds Inf/NaN.
+ * (Core ideas, §2.1: FP16 = 1 + 5 + 10, range +-65504.)                     */
+
+float orc_h2f(uint16_t h)
+{
+    int sign = h >> 15;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)f, -24);                 /* subnormal or zero */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(1024 + f), e - 25);     /* 1.f * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Round a binary32 value to the nearest binary16, ties to even. The value is
+ * written as r * q with q the binary16 spacing of its binade (2^-24 below the
+ * normal range); r is rounded to the nearest integer with ties to even, which
+ * is the same as an even last fraction bit. Magnitudes >= 65520 (half-way
+ * between 65504 and 2^16) round to infinity.                                 */
+uint16_t orc_f2h(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs((double)x);
+    if (isnan(x))
+        return sign | 0x7e00;
+    if (a >= 65520.0)
+        return sign | 0x7c00;
+    if (a == 0.0)
+        return sign;
+    int ex;
+    frexp(a, &ex);                 /* a = fr * 2^ex, fr in [0.5, 1) */
+    int b = ex - 1;                /* binade: 2^b <= a < 2^(b+1)     */
+    double q = (b < -14) ? ldexp(1.0, -24) : ldexp(1.0, b - 10);
+    double r = nearbyint(a / q);   /* a / q is exact; ties to even   */
+    double v = r * q;              /* the rounded magnitude           */
+    if (v == 0.0)
+        return sign;
+    if (v < ldexp(1.0, -14))       /* subnormal result */
+        return sign | (uint16_t)(v / ldexp(1.0, -24));
+    frexp(v, &ex);
+    b = ex - 1;
+    if (b > 15)
+        return sign | 0x7c00;
+    uint16_t frac = (uint16_t)(v / ldexp(1.0, b - 10) - 1024.0);
+    return sign | (uint16_t)((b + 15) << 10) | frac;
+}
+
+void orc_h2f_array(const uint16_t *h, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = orc_h2f(h[i]);
+}
+
+void orc_f2h_array(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = orc_f2h(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Group-wise INT4 RTN quantizer.
+ *
+ * Asymmetric (Core ideas §2.2; Quantization operators guide §2.1):
+ *   s = (max - min) / (2^b - 1),  zp = round(-min / s),
+ *   q = clip(round(x / s) + zp, 0, 2^b - 1),  x_hat = (q - zp) * s.
+ * Symmetric (Core ideas §2.2):
+ *   s = max|x| / (2^(b-1) - 1),  q = clip(round(x / s), -2^(b-1), 2^(b-1) - 1).
+ * One fp16 scale and one zero-point per group of g consecutive elements of a
+ * weight row (Quantization notes, item (1) group quantization; Quantization
+ * operators guide §2.2 per-group, §3.3). Rounding is to nearest, ties to
+ * even (Core ideas §2.2).
+ *
+ * Readings where the pages leave a step open:
+ *   - the range is widened to contain 0 (lo = min(0, min x), hi = max(0,
+ *     max x)), so zp stays in [0, 15] and 0 is exact; on a group with both
+ *     signs this is the pages' formula unchanged;
+ *   - s is computed in fp32 and rounded once to the stored fp16 scale; the
+ *     codes are made from that stored scale, so quantize and dequantize use
+ *     the same s; a scale that rounds to 0 is replaced by 1.0;
+ *   - round first, then add zp (the order the formula is written in);
+ *   - true division x / s, not a multiply by 1/s;
+ *   - symmetric codes are stored offset-binary, u = q + 8.
+ * Packing: codes[n][i] = u[n][2i] | u[n][2i+1] << 4 (even k in the low
+ * nibble); zeros[n][i] = zp[n][2i] | zp[n][2i+1] << 4, a zero nibble pads an
+ * odd group count. All arrays row-major.                                    */
+
+static void quant_group(const uint16_t *w, int g, int sym, uint8_t *u,
+                        uint16_t *scale16, int *zp_out)
+{
+    float lo = 0.0f, hi = 0.0f, amax = 0.0f;
+    for (int k = 0; k < g; k++) {
+        float x = orc_h2f(w[k]);
+        if (x < lo) lo = x;
+        if (x > hi) hi = x;
+        if (fabsf(x) > amax) amax = fabsf(x);
+    }
+    float s32 = sym ? amax / 7.0f : (hi - lo) / 15.0f;
+    uint16_t s16 = orc_f2h(s32);
+    if ((s16 & 0x7fff) == 0)
+        s16 = 0x3c00;                          /* 1.0 */
+    float sf = orc_h2f(s16);
+    int zp;
+    if (sym) {
+        zp = 8;
+    } else {
+        float z = rintf(-lo / sf);
+        zp = (int)z;
+        if (zp < 0) zp = 0;
+        if (zp > 15) zp = 15;
+    }
+    for (int k = 0; k < g; k++) {
+        float x = orc_h2f(w[k]);
+        int q = (int)rintf(x / sf);
+        if (sym) {
+            if (q < -8) q = -8;
+            if (q > 7) q = 7;
+            u[k] = (uint8_t)(q + 8);
+        } else {
+            q += zp;
+            if (q < 0) q = 0;
+            if (q > 15) q = 15;
+            u[k] = (uint8_t)q;
+        }
+    }
+    *scale16 = s16;
+    *zp_out = zp;
+}
+
+/* W fp16 [N, K] -> codes u8 [N, K/2], scales fp16 [N, K/g],
+ * zeros u8 [N, ceil(K/g/2)] (asymmetric only; ignored when sym).
+ * Returns 0, or -1 on a shape it does not accept.                           */
+int orc_q4_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int g,
+                         int sym, uint8_t *codes, uint16_t *scales,
+                         uint8_t *zeros)
+{
+    if (N < 0 || K <= 0 || g <= 0 || K % g != 0 || K % 2 != 0 || g % 2 != 0)
+        return -1;
+    int64_t G = K / g, Gz = (G + 1) / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        uint8_t *u = (uint8_t *)malloc((size_t)K);
+        int *zp = (int *)malloc(sizeof(int) * (size_t)G);
+        for (int64_t j = 0; j < G; j++)
+            quant_group(W + n * K + j * g, g, sym, u + j * g, &scales[n * G + j],
+                        &zp[j]);
+        for (int64_t i = 0; i < K / 2; i++)
+            codes[n * (K / 2) + i] = (uint8_t)(u[2 * i] | (u[2 * i + 1] << 4));
+        if (!sym && zeros) {
+            for (int64_t i = 0; i < Gz; i++) {
+                int lo = zp[2 * i];
+                int hi = (2 * i + 1 < G) ? zp[2 * i + 1] : 0;
+                zeros[n * Gz + i] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+        free(zp);
+        free(u);
+    }
+    return 0;
+}
+
+/* Dequantize rows [n0, n1) of a packed INT4 weight into fp64:
+ * w_hat[n][k] = (u - zp) * s (Core ideas §2.2, dequantization), exact in
+ * fp64. Symmetric weights (zeros == NULL) use zp = 8.                       */
+void orc_q4_dequant_rows(const uint8_t *codes, const uint16_t *scales,
+                         const uint8_t *zeros, int64_t K, int g, int64_t n0,
+                         int64_t n1, double *out)
+{
+    int64_t G = K / g, Gz = (G + 1) / 2;
+    for (int64_t n = n0; n < n1; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            uint8_t byte = codes[n * (K / 2) + k / 2];
+            int u = (k % 2 == 0) ? (byte & 0xf) : (byte >> 4);
+            int64_t j = k / g;
+            int zp = 8;
+            if (zeros) {
+                uint8_t zb = zeros[n * Gz + j / 2];
+                zp = (j % 2 == 0) ? (zb & 0xf) : (zb >> 4);
+            }
+            double s = (double)orc_h2f(scales[n * G + j]);
+            out[(n - n0) * K + k] = (double)(u - zp) * s;
+        }
+    }
+}
+
+/* W4A16 reference: Y[m][n] = sum_k x[m][k] * w_hat[n][k] in fp64 for the
+ * listed rows m (all rows when rows == NULL), and the error scale
+ * B[m][n] = sum_k |x| |w_hat|. Outputs are [n_rows, N]. The product is the
+ * plain linear layer Y = X W^T over the dequantized weight (Quantization
+ * operators guide §1.2: quantize, compute, dequantize).                    */
+void orc_w4a16_ref(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes,
+                   const uint16_t *scales, const uint8_t *zeros, int64_t N,
+                   int g, const int64_t *rows, int64_t n_rows, double *Y,
+                   double *B)
+{
+    (void)M;
+    if (!rows) n_rows = M;
+    double *xr = (double *)malloc(sizeof(double) * (size_t)(n_rows * K));
+    for (int64_t i = 0; i < n_rows; i++) {
+        int64_t m = rows ? rows[i] : i;
+        for (int64_t k = 0; k < K; k++)
+            xr[i * K + k] = (double)orc_h2f(X[m * K + k]);
+    }
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; n++) {
+        double *w = (double *)malloc(sizeof(double) * (size_t)K);
+        orc_q4_dequant_rows(codes, scales, zeros, K, g, n, n + 1, w);
+        for (int64_t i = 0; i < n_rows; i++) {
+            double acc = 0.0, bnd = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                acc += xr[i * K + k] * w[k];
+                bnd += fabs(xr[i * K + k]) * fabs(w[k]);
+            }
+            Y[i * N + n] = acc;
+            if (B) B[i * N + n] = bnd;
+        }
+        free(w);
+    }
+    free(xr);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-channel INT8 weight with the SmoothQuant fold (Quantization operators
+ * guide §2.2 per-channel: one scale per output row, max|w| / 127, codes
+ * clamped to [-127, 127]; §5.1 and Core ideas §2.4: W' = W diag(s)).
+ *   w'[n][k] = x * s[k]            (fp32 multiply; s == NULL means s = 1)
+ *   a_n = max(max_k |w'|, 1e-8)    (the 1e-8 floor of the Method boundaries
+ *                                   example's clamp_min)
+ *   sw[n] = a_n / 127
+ *   q = clip(rne(w' / sw[n]), -127, 127)                                    */
+void orc_q8_quantize_weight(const uint16_t *W, const float *s, int64_t N,
+                            int64_t K, int8_t *Wq, float *sw)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float w = orc_h2f(W[n * K + k]) * (s ? s[k] : 1.0f);
+            if (fabsf(w) > a) a = fabsf(w);
+        }
+        if (a < 1e-8f) a = 1e-8f;
+        float scale = a / 127.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float w = orc_h2f(W[n * K + k]) * (s ? s[k] : 1.0f);
+            int q = (int)rintf(w / scale);
+            if (q < -127) q = -127;
+            if (q > 127) q = 127;
+            Wq[n * K + k] = (int8_t)q;
+        }
+        sw[n] = scale;
+    }
+}
+
+/* Per-token dynamic INT8 activation quantization of the smoothed input
+ * (Quantization schemes notes on per-token scales; Quantization operators
+ * guide §5.1 transform X / s and §5.3 the online divide):
+ *   x'[m][k] = x / s[k]            (fp32 division; s == NULL: x' = x)
+ *   a_m = max(max_k |x'|, 1e-8),  sx[m] = a_m / 127,
+ *   q = clip(rne(x' / sx[m]), -127, 127)                                   */
+void orc_q8_quantize_act(const uint16_t *X, const float *s, int64_t M,
+                         int64_t K, int8_t *Xq, float *sx)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float x = orc_h2f(X[m * K + k]);
+            if (s) x = x / s[k];
+            if (fabsf(x) > a) a = fabsf(x);
+        }
+        if (a < 1e-8f) a = 1e-8f;
+        float scale = a / 127.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float x = orc_h2f(X[m * K + k]);
+            if (s) x = x / s[k];
+            int q = (int)rintf(x / scale);
+            if (q < -127) q = -127;
+            if (q > 127) q = 127;
+            Xq[m * K + k] = (int8_t)q;
+        }
+        sx[m] = scale;
+    }
+}
+
+/* INT8 GEMM with exact integer accumulation (Quantization operators guide
+ * §2.3: C_int32 = sum(A_int8 * B_int8); §5.2 path A: C = X_int8 W_int8^T).
+ * acc[i][n] = sum_k Xq[m][k] * Wq[n][k] for the listed rows m (all when
+ * rows == NULL), in int64; returns the number of results outside int32.     */
+int64_t orc_int8_gemm(const int8_t *Xq, int64_t M, int64_t K, const int8_t *Wq,
+                      int64_t N, const int64_t *rows, int64_t n_rows,
+                      int64_t *acc, int64_t *abs_acc)
+{
+    if (!rows) n_rows = M;
+    int64_t overflow = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(+ : overflow)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t i = 0; i < n_rows; i++) {
+            int64_t m = rows ? rows[i] : i;
+            int64_t a = 0, b = 0;
+            for (int64_t k = 0; k < K; k++) {
+                int64_t p = (int64_t)Xq[m * K + k] * (int64_t)Wq[n * K + k];
+                a += p;
+                b += p < 0 ? -p : p;
+            }
+            acc[i * N + n] = a;
+            if (abs_acc) abs_acc[i * N + n] = b;
+            if (a > INT32_MAX || a < INT32_MIN) overflow++;
+        }
+    }
+    return overflow;
+}
+
+/* W8A8 epilogue (Quantization operators guide §2.3 DequantizeOp and §5.2:
+ * C_fp16 = C_int32 * scale_X * scale_W).
+ * Reference, fp64: Y = sx[m] * sw[n] * acc, B = sx[m] * sw[n] * sum|qx||qw|.
+ * The same expression in fp32, ((float)acc * sx) * sw rounded once to fp16,
+ * is returned in y16 (may be NULL).                                         */
+void orc_w8a8_epilogue(const int64_t *acc, const int64_t *abs_acc,
+                       const float *sx, const int64_t *rows, int64_t n_rows,
+                       const float *sw, int64_t N, double *Y, double *B,
+                       uint16_t *y16)
+{
+    for (int64_t i = 0; i < n_rows; i++) {
+        int64_t m = rows ? rows[i] : i;
+        for (int64_t n = 0; n < N; n++) {
+            int64_t a = acc[i * N + n];
+            Y[i * N + n] = (double)sx[m] * (double)sw[n] * (double)a;
+            if (B) B[i * N + n] = (double)sx[m] * (double)sw[n] * (double)abs_acc[i * N + n];
+            if (y16) {
+                float f = (float)(int32_t)a;
+                f = f * sx[m];
+                f = f * sw[n];
+                y16[i * N + n] = orc_f2h(f);
+            }
+        }
+    }
+}
+
+/* SmoothQuant migration factor (Quantization operators guide §5.1; Core
+ * ideas §2.4; Quantization notes, SmoothQuant):
+ *   s_j = max|X_j|^alpha / max|W_j|^(1 - alpha),
+ * with X the calibration activations [R, K] and W the weight [N, K]; the
+ * weight maximum for input channel j is taken over the output rows. Both
+ * maxima are floored at 1e-8. At alpha = 0.5 the powers are square roots,
+ * computed with the correctly rounded sqrtf.                               */
+void orc_smooth_scales(const uint16_t *Xcal, int64_t R, const uint16_t *W,
+                       int64_t N, int64_t K, float alpha, float *s)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < K; j++) {
+        float ax = 0.0f, aw = 0.0f;
+        for (int64_t r = 0; r < R; r++) {
+            float v = fabsf(orc_h2f(Xcal[r * K + j]));
+            if (v > ax) ax = v;
+        }
+        for (int64_t n = 0; n < N; n++) {
+            float v = fabsf(orc_h2f(W[n * K + j]));
+            if (v > aw) aw = v;
+        }
+        if (ax < 1e-8f) ax = 1e-8f;
+        if (aw < 1e-8f) aw = 1e-8f;
+        if (alpha == 0.5f)
+            s[j] = sqrtf(ax) / sqrtf(aw);
+        else
+            s[j] = powf(ax, alpha) / powf(aw, 1.0f - alpha);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Small-float decoders written from the format definitions (Core ideas
+ * §2.1: E4M3 = 1+4+3 with S.1111.111 as NaN, E5M2 = 1+5+2 IEEE-style with
+ * the all-ones exponent for Inf/NaN, E2M1 = 1+2+1). Exponent bias is
+ * 2^(e-1) - 1; exponent field 0 is subnormal (no implicit 1).               */
+static float decode_minifloat(unsigned code, int ebits, int mbits, int ieee_specials,
+                              int nan_all_ones)
+{
+    unsigned sign = (code >> (ebits + mbits)) & 1;
+    unsigned e = (code >> mbits) & ((1u << ebits) - 1);
+    unsigned m = code & ((1u << mbits) - 1);
+    unsigned emax = (1u << ebits) - 1;
+    int bias = (1 << (ebits - 1)) - 1;
+    float v;
+    if (ieee_specials && e == emax)
+        v = m ? NAN : INFINITY;
+    else if (nan_all_ones && e == emax && m == (1u << mbits) - 1)
+        v = NAN;
+    else if (e == 0)
+        v = ldexpf((float)m, 1 - bias - mbits);
+    else
+        v = ldexpf((float)((1u << mbits) + m), (int)e - bias - mbits);
+    return sign ? -v : v;
+}
+
+float orc_e4m3_decode(unsigned code) { return decode_minifloat(code & 0xff, 4, 3, 0, 1); }
+float orc_e5m2_decode(unsigned code) { return decode_minifloat(code & 0xff, 5, 2, 1, 0); }
+float orc_e2m1_decode(unsigned code) { return decode_minifloat(code & 0xf, 2, 1, 0, 0); }
+
+/* Number of OpenMP threads a parallel region of this library uses. */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_num_threads(void) { return 1; }
+#endif
