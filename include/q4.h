@@ -1,0 +1,208 @@
+/*
+ * q4.h -- C ABI of the MI355X (gfx950) group-quantized linear layer library.
+ *
+ * The library computes the quantized linear layer Y = X * W_hat^T of the
+ * quantization pages in two forms:
+ *   - W4A16: INT4 weights with one fp16 scale and one 4-bit zero-point per
+ *     group of g input channels, dequantized inside the GEMM, fp16
+ *     activations, fp32 accumulation, fp16 output;
+ *   - W8A8: SmoothQuant-migrated per-output-channel INT8 weights, per-token
+ *     dynamic INT8 activations, int32 accumulation, fp16 output.
+ * Pages cited below:
+ *   "Core ideas"        ai-infra.cypggs.com, "2. Core ideas: numeric
+ *                       representation, rounding, scaling and difficulty
+ *                       migration";
+ *   "Operators guide"   blog.freezetheflame.cc, "Quantization operators from
+ *                       basics to practice: INT8/INT4/FP8";
+ *   "Method boundaries" llm-glossary.tokens-kit.com, "Method boundaries of
+ *                       GPTQ, AWQ, SmoothQuant and FP8";
+ *   "Quantization notes" learn.longtimenohack.com, chasing/quantization;
+ *   "Schemes notes"     lib.uml.com.cn, FDE e-book, quantization-schemes.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or keeps caller memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the null stream). Results are ready when the stream is.
+ *   - fp16 means IEEE binary16 (passed as void*); all arrays are row-major
+ *     and densely packed.
+ *   - Arguments are checked on the host before any launch. On an error
+ *     nothing is launched and nothing is written; the call returns a status
+ *     and q4_last_error() holds a message (thread-local). A failed launch
+ *     returns Q4_ERR_HIP. A fault inside a kernel surfaces at the caller's
+ *     next synchronization. No C++ exception crosses the ABI.
+ *   - A zero-sized M or N is a valid no-op.
+ *   - Inputs must be finite; non-finite inputs give unspecified codes and
+ *     outputs (never an out-of-bounds access).
+ *   - Rounding is IEEE round-to-nearest-even everywhere; divisions are true
+ *     IEEE divisions. Codes, scales, zero-points and int32 accumulators are
+ *     bit-reproducible.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_API __attribute__((visibility("default")))
+
+typedef enum {
+    Q4_OK = 0,
+    Q4_ERR_INVALID_ARG = 1,   /* a null pointer, a bad size or shape */
+    Q4_ERR_UNSUPPORTED = 2,   /* a valid request this build does not serve */
+    Q4_ERR_MISALIGNED = 3,    /* a tensor pointer not 16-byte aligned */
+    Q4_ERR_HIP = 4            /* the HIP runtime reported an error */
+} q4_status;
+
+/* Version of the packed layouts below (codes, scales, zeros). Bumped on any
+ * change, so a stored checkpoint can be checked against the runtime's
+ * packing (Method boundaries, production acceptance: the checkpoint schema
+ * must match the runtime's packing). */
+Q4_API int q4_layout_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+Q4_API const char *q4_last_error(void);
+
+/* ----------------------------------------------------------------------------
+ * q4_quantize_pack -- group-wise round-to-nearest INT4 quantization + packing.
+ *
+ * Formulas (Core ideas §2.2; Operators guide §2.1, §2.2 per-group, §3.3;
+ * Quantization notes item (1) group quantization, item (2) sym/asym):
+ *   asymmetric: lo = min(0, min x), hi = max(0, max x) over the group,
+ *               s = fp16((hi - lo) / 15), zp = clip(rne(-lo / s), 0, 15),
+ *               u = clip(rne(x / s) + zp, 0, 15);
+ *   symmetric:  s = fp16(max|x| / 7), q = clip(rne(x / s), -8, 7), u = q + 8.
+ * All in fp32 with true division; s is rounded once to fp16 (RNE) and the
+ * codes are made from that stored scale; a scale that rounds to 0 becomes
+ * 1.0. The dequantized weight is w_hat = (u - zp) * s (symmetric: zp = 8).
+ *
+ * W       fp16 [N, K], input, 16-byte aligned.
+ * N       rows (output channels), >= 0.     K  input channels, > 0.
+ * g       group size along K: 32, 64 or 128; K % g == 0.
+ * sym     0 = asymmetric (zeros written), 1 = symmetric (zeros ignored).
+ * codes   u8 [N, K/2] output: byte i of row n = u[n][2i] | u[n][2i+1] << 4
+ *         (even k in the low nibble). 16-byte aligned.
+ * scales  fp16 [N, K/g] output.
+ * zeros   u8 [N, ceil(K/g/2)] output when sym == 0 (zp of group 2i in the
+ *         low nibble, 2i+1 in the high nibble, 0 pads an odd count); may be
+ *         NULL when sym == 1.
+ * Errors: INVALID_ARG (null pointer, K % g != 0, bad g, zeros NULL with
+ *         sym == 0), MISALIGNED (W or codes), HIP.
+ * Storage: 4 + 16/g bits per weight symmetric, + 4/g asymmetric (4.125 and
+ * 4.15625 at g = 128; Operators guide §3.3).
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status q4_quantize_pack(const void *W, int64_t N, int64_t K, int32_t g,
+                                  int32_t sym, uint8_t *codes, void *scales,
+                                  uint8_t *zeros, void *stream);
+
+/* ----------------------------------------------------------------------------
+ * w4a16_linear -- Y = X * W_hat^T with the INT4 weight dequantized inside the
+ * GEMM (Operators guide §1.2, the quantize/compute/dequantize pipeline fused
+ * into one kernel; Method boundaries, GPTQ section: small-batch decode is
+ * bound by the weight read, prefill by the dequant + matrix-core path).
+ *   W_hat[n][k] = (u - zp) * s for the group of k; fp32 accumulation;
+ *   Y rounded once to fp16 (RNE).
+ * Accuracy: |Y - Y_ref| <= 2^-10 * sum_k |x||w_hat| (+2^-25) elementwise and
+ * relative L2 <= 5e-4 against the exact product over the dequantized weight.
+ *
+ * X       fp16 [M, K] input, 16-byte aligned.
+ * M       tokens, >= 0.   N output channels, >= 0.   K input channels, > 0.
+ * g       group size: a multiple of 128 (128 is the layout's design point).
+ * codes, scales, zeros   as written by q4_quantize_pack; zeros == NULL means
+ *         symmetric (zp = 8). codes 16-byte aligned.
+ * Y       fp16 [M, N] output.
+ * Errors: INVALID_ARG (null pointer, K % g != 0, K % 2 != 0),
+ *         UNSUPPORTED (g % 128 != 0), MISALIGNED (X, codes), HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status w4a16_linear(const void *X, int64_t M, int64_t N, int64_t K,
+                              int32_t g, const uint8_t *codes, const void *scales,
+                              const uint8_t *zeros, void *Y, void *stream);
+
+/* ----------------------------------------------------------------------------
+ * q8_quantize_weight -- per-output-channel INT8 of the smoothed weight
+ * (Operators guide §2.2 per-channel, §5.1/§5.3: W' = W diag(s) folded offline;
+ * Core ideas §2.4):
+ *   w' = x * s[k] (fp32 multiply; smooth_s == NULL means s = 1),
+ *   w_scale[n] = max(max_k |w'|, 1e-8) / 127,
+ *   Wq = clip(rne(w' / w_scale[n]), -127, 127).
+ * W fp16 [N, K] (16-byte aligned); smooth_s fp32 [K] or NULL;
+ * Wq int8 [N, K] output (16-byte aligned); w_scale fp32 [N] output.
+ * Errors: INVALID_ARG, MISALIGNED (W, Wq; K % 8 != 0 is INVALID_ARG), HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status q8_quantize_weight(const void *W, const float *smooth_s, int64_t N,
+                                    int64_t K, int8_t *Wq, float *w_scale, void *stream);
+
+/* ----------------------------------------------------------------------------
+ * q8_quantize_act -- per-token dynamic INT8 of the smoothed activation
+ * (Schemes notes, per-token scales computed at inference; Operators guide
+ * §5.1 X / s, §5.3 the online divide):
+ *   x' = x / s[k] (fp32 division; smooth_s == NULL means x' = x),
+ *   x_scale[m] = max(max_k |x'|, 1e-8) / 127,
+ *   Xq = clip(rne(x' / x_scale[m]), -127, 127).
+ * X fp16 [M, K] (16-byte aligned); smooth_s fp32 [K] or NULL;
+ * Xq int8 [M, K] output (16-byte aligned); x_scale fp32 [M] output.
+ * Errors: INVALID_ARG (K % 8 != 0 included), MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status q8_quantize_act(const void *X, const float *smooth_s, int64_t M,
+                                 int64_t K, int8_t *Xq, float *x_scale, void *stream);
+
+/* ----------------------------------------------------------------------------
+ * w8a8_gemm -- INT8 GEMM with exact int32 accumulation and the scale
+ * epilogue (Operators guide §2.3 INT8 GEMM + DequantizeOp, §5.2 path A):
+ *   acc[m][n] = sum_k Xq[m][k] * Wq[n][k]   (exact; |acc| <= 127^2 K),
+ *   Y[m][n]   = fp16(((float)acc * x_scale[m]) * w_scale[n]).
+ * Xq int8 [M, K], Wq int8 [N, K] (both 16-byte aligned, K % 16 == 0 and
+ * K <= 133143 so the int32 sum cannot overflow); x_scale fp32 [M];
+ * w_scale fp32 [N]; Y fp16 [M, N] output; acc_out optional int32 [M, N]
+ * output (for bit-exact checks; NULL in production).
+ * Errors: INVALID_ARG, MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status w8a8_gemm(const int8_t *Xq, const float *x_scale, const int8_t *Wq,
+                           const float *w_scale, int64_t M, int64_t N, int64_t K,
+                           void *Y, int32_t *acc_out, void *stream);
+
+/* Bytes of workspace w8a8_linear needs for M tokens of width K: the int8
+ * codes [M, K] (rounded up to 256 bytes) followed by the fp32 scales [M]. */
+Q4_API size_t w8a8_workspace_bytes(int64_t M, int64_t K);
+
+/* ----------------------------------------------------------------------------
+ * w8a8_linear -- the SmoothQuant W8A8 linear layer: q8_quantize_act of X
+ * (with /smooth_s fused in) into the workspace, then w8a8_gemm.
+ * smooth_s == NULL means X is already smoothed (the divide was folded into
+ * the previous layer); passing s here AND folding it upstream would apply
+ * it twice (Method boundaries, SmoothQuant: never apply s twice).
+ * workspace: device memory of at least w8a8_workspace_bytes(M, K) bytes,
+ * 256-byte aligned; after the call it holds Xq [M, K] then x_scale [M]
+ * (at offset round_up(M*K, 256)).
+ * Errors: INVALID_ARG (workspace too small included), MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status w8a8_linear(const void *X, int64_t M, int64_t N, int64_t K,
+                             const int8_t *Wq, const float *w_scale,
+                             const float *smooth_s, void *Y, void *workspace,
+                             size_t workspace_bytes, int32_t *acc_out, void *stream);
+
+/* ----------------------------------------------------------------------------
+ * smoothquant_scales -- the SmoothQuant migration factor from calibration
+ * activations (Operators guide §5.1; Core ideas §2.4; Quantization notes,
+ * SmoothQuant):
+ *   s[j] = max(ax_j, 1e-8)^alpha / max(aw_j, 1e-8)^(1 - alpha),
+ *   ax_j = max_r |Xcal[r][j]|, aw_j = max_n |W[n][j]|.
+ * At alpha == 0.5 the powers are correctly rounded square roots and s is
+ * bit-reproducible; other alpha in [0, 1] use powf (within a few ulp).
+ * Xcal fp16 [R, K], W fp16 [N, K] (both 16-byte aligned, K % 8 == 0);
+ * s fp32 [K] output. This is an offline step; it is not on the hot path.
+ * Errors: INVALID_ARG (R or N < 1, alpha outside [0, 1]), MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status smoothquant_scales(const void *Xcal, int64_t R, const void *W,
+                                    int64_t N, int64_t K, float alpha, float *s,
+                                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

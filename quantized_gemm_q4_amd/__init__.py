@@ -1,0 +1,234 @@
+"""MI355X (gfx950) group-quantized linear layers: W4A16 and SmoothQuant W8A8.
+
+Thin Python binding of the C ABI in ``include/q4.h`` (library
+``libq4amd.so`` in this directory). This module only marshals arguments:
+PyTorch supplies device memory and the current HIP stream; every step of
+the computation runs in the library's HIP kernels. If the library is not
+built, every call raises -- there is no fallback path.
+
+Functions (same names as the C ABI):
+  q4_quantize_pack(W, g=128, sym=False) -> (codes, scales, zeros | None)
+  w4a16_linear(X, codes, scales, zeros, g=128) -> Y
+  q8_quantize_weight(W, smooth_s=None) -> (Wq, w_scale)
+  q8_quantize_act(X, smooth_s=None) -> (Xq, x_scale)
+  w8a8_gemm(Xq, x_scale, Wq, w_scale, acc_out=None) -> Y
+  w8a8_linear(X, Wq, w_scale, smooth_s=None, workspace=None, acc_out=None) -> Y
+  smoothquant_scales(Xcal, W, alpha=0.5) -> s
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4amd.so")
+
+Q4_OK, Q4_ERR_INVALID_ARG, Q4_ERR_UNSUPPORTED, Q4_ERR_MISALIGNED, Q4_ERR_HIP = range(5)
+_STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "MISALIGNED", 4: "HIP"}
+
+# name -> (restype, argtypes), exactly the declarations of include/q4.h
+_vp, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+SIGNATURES = {
+    "q4_layout_version": (ctypes.c_int, []),
+    "q4_last_error": (ctypes.c_char_p, []),
+    "q4_quantize_pack": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "w4a16_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "q8_quantize_weight": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "q8_quantize_act": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "w8a8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "w8a8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "w8a8_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
+                                   ctypes.c_size_t, _vp, _vp]),
+    "smoothquant_scales": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, ctypes.c_float, _vp, _vp]),
+}
+
+_lib = None
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libq4amd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_gemm_q4_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != Q4_OK:
+        raise Q4Error(status, lib().q4_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def layout_version() -> int:
+    return int(lib().q4_layout_version())
+
+
+def q4_quantize_pack(W: torch.Tensor, g: int = 128, sym: bool = False, out=None):
+    """Group-wise RTN INT4 of W fp16 [N, K]: (codes u8 [N, K/2],
+    scales fp16 [N, K/g], zeros u8 [N, ceil(K/g/2)] or None when sym)."""
+    _need(W, torch.float16, "W", 2)
+    N, K = W.shape
+    G = K // g if g > 0 else 0
+    if out is None:
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+        scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
+        zeros = None if sym else torch.empty((N, (G + 1) // 2), dtype=torch.uint8, device=W.device)
+    else:
+        codes, scales, zeros = out
+    _check(lib().q4_quantize_pack(_ptr(W), N, K, g, int(bool(sym)), _ptr(codes), _ptr(scales),
+                                  _ptr(zeros), _stream(W)))
+    return codes, scales, zeros
+
+
+def w4a16_linear(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                 zeros: torch.Tensor | None, g: int = 128, out: torch.Tensor | None = None):
+    """Y fp16 [M, N] = X fp16 [M, K] x W_hat^T, W_hat dequantized in the GEMM."""
+    _need(X, torch.float16, "X", 2)
+    _need(codes, torch.uint8, "codes", 2)
+    _need(scales, torch.float16, "scales", 2)
+    if zeros is not None:
+        _need(zeros, torch.uint8, "zeros", 2)
+    M, K = X.shape
+    N = codes.shape[0]
+    if codes.shape[1] * 2 != K:
+        raise ValueError(f"codes {tuple(codes.shape)} does not match K={K}")
+    if scales.shape != (N, K // g):
+        raise ValueError(f"scales {tuple(scales.shape)} does not match [N, K/g]=[{N}, {K // g}]")
+    if zeros is not None and zeros.shape != (N, (K // g + 1) // 2):
+        raise ValueError(f"zeros {tuple(zeros.shape)} does not match [N, ceil(K/g/2)]")
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _check(lib().w4a16_linear(_ptr(X), M, N, K, g, _ptr(codes), _ptr(scales), _ptr(zeros),
+                              _ptr(Y), _stream(X)))
+    return Y
+
+
+def q8_quantize_weight(W: torch.Tensor, smooth_s: torch.Tensor | None = None):
+    """Per-output-channel INT8 of W diag(s): (Wq int8 [N, K], w_scale fp32 [N])."""
+    _need(W, torch.float16, "W", 2)
+    if smooth_s is not None:
+        _need(smooth_s, torch.float32, "smooth_s", 1)
+    N, K = W.shape
+    Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    sw = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check(lib().q8_quantize_weight(_ptr(W), _ptr(smooth_s), N, K, _ptr(Wq), _ptr(sw), _stream(W)))
+    return Wq, sw
+
+
+def q8_quantize_act(X: torch.Tensor, smooth_s: torch.Tensor | None = None, out=None):
+    """Per-token dynamic INT8 of X / s: (Xq int8 [M, K], x_scale fp32 [M])."""
+    _need(X, torch.float16, "X", 2)
+    if smooth_s is not None:
+        _need(smooth_s, torch.float32, "smooth_s", 1)
+    M, K = X.shape
+    if out is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
+    else:
+        Xq, sx = out
+    _check(lib().q8_quantize_act(_ptr(X), _ptr(smooth_s), M, K, _ptr(Xq), _ptr(sx), _stream(X)))
+    return Xq, sx
+
+
+def w8a8_gemm(Xq: torch.Tensor, x_scale: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
+              acc_out: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """Y fp16 [M, N] = fp16((Xq Wq^T) * x_scale[m] * w_scale[n]); optional
+    int32 accumulator written to acc_out [M, N]."""
+    _need(Xq, torch.int8, "Xq", 2)
+    _need(Wq, torch.int8, "Wq", 2)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or x_scale.numel() != M or w_scale.numel() != N:
+        raise ValueError("w8a8_gemm: shape mismatch")
+    if acc_out is not None:
+        _need(acc_out, torch.int32, "acc_out", 2)
+        if acc_out.shape != (M, N):
+            raise ValueError("acc_out must be [M, N]")
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    _check(lib().w8a8_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y),
+                           _ptr(acc_out), _stream(Xq)))
+    return Y
+
+
+def w8a8_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().w8a8_workspace_bytes(M, K))
+
+
+def w8a8_workspace(M: int, K: int, device) -> torch.Tensor:
+    """A workspace tensor for w8a8_linear (torch's allocations are 256-byte aligned)."""
+    return torch.empty((max(1, w8a8_workspace_bytes(M, K)),), dtype=torch.uint8, device=device)
+
+
+def w8a8_linear(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
+                smooth_s: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                acc_out: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """SmoothQuant W8A8 linear layer: per-token INT8 of X / s, INT8 GEMM,
+    fp16 epilogue. smooth_s=None means X is already smoothed."""
+    _need(X, torch.float16, "X", 2)
+    _need(Wq, torch.int8, "Wq", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    if smooth_s is not None:
+        _need(smooth_s, torch.float32, "smooth_s", 1)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K:
+        raise ValueError("w8a8_linear: Wq must be [N, K]")
+    if workspace is None:
+        workspace = w8a8_workspace(M, K, X.device)
+    _need(workspace, torch.uint8, "workspace", 1)
+    if acc_out is not None:
+        _need(acc_out, torch.int32, "acc_out", 2)
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _check(lib().w8a8_linear(_ptr(X), M, N, K, _ptr(Wq), _ptr(w_scale), _ptr(smooth_s), _ptr(Y),
+                             _ptr(workspace), workspace.numel(), _ptr(acc_out), _stream(X)))
+    return Y
+
+
+def smoothquant_scales(Xcal: torch.Tensor, W: torch.Tensor, alpha: float = 0.5):
+    """SmoothQuant factor s[K] = max|Xcal_j|^alpha / max|W_j|^(1-alpha)."""
+    _need(Xcal, torch.float16, "Xcal", 2)
+    _need(W, torch.float16, "W", 2)
+    R, K = Xcal.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("smoothquant_scales: Xcal and W must share K")
+    s = torch.empty((K,), dtype=torch.float32, device=W.device)
+    _check(lib().smoothquant_scales(_ptr(Xcal), R, _ptr(W), N, K, ctypes.c_float(alpha), _ptr(s),
+                                    _stream(W)))
+    return s

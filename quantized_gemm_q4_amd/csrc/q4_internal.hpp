@@ -1,0 +1,40 @@
+// Internal declarations of the gfx950 kernels' launchers and the device
+// helpers they share. Not part of the ABI (see include/q4.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace q4k {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// binary16 bits <-> fp32 with the hardware converts (v_cvt_f32_f16 is exact;
+// v_cvt_f16_f32 rounds to nearest even, subnormals kept).
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Launchers. Arguments were validated by the C-ABI layer; every launcher
+// enqueues on `st` and returns the launch status.
+hipError_t launch_q4_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int g, int sym,
+                                   uint8_t *codes, uint16_t *scales, uint8_t *zeros,
+                                   hipStream_t st);
+hipError_t launch_q8_weight(const uint16_t *W, const float *s, int64_t N, int64_t K,
+                            int8_t *Wq, float *sw, hipStream_t st);
+hipError_t launch_q8_act(const uint16_t *X, const float *s, int64_t M, int64_t K,
+                         int8_t *Xq, float *sx, hipStream_t st);
+hipError_t launch_smooth_scales(const uint16_t *Xcal, int64_t R, const uint16_t *W, int64_t N,
+                                int64_t K, float alpha, float *s, hipStream_t st);
+hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,
+                        const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                        uint16_t *Y, hipStream_t st);
+hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
+                            const float *sw, int64_t M, int64_t N, int64_t K, uint16_t *Y,
+                            int32_t *acc_out, hipStream_t st);
+
+}  // namespace q4k

@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every symbol include/q4.h declares, and
+rejects bad arguments on the host before any launch (no GPU needed: every
+call here fails validation or is a zero-size no-op, so nothing is launched).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_gemm_q4_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"Q4_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q4.LIB_PATH):
+        from quantized_gemm_q4_amd import build
+        build.build()
+    return q4.lib()
+
+
+def test_header_declares_the_binding(lib):
+    names = declared_functions()
+    assert names == sorted(q4.SIGNATURES), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", q4.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared_functions()) <= exported
+    # nothing else of ours leaks out (internal launchers are hidden)
+    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "smoothquant", "_ZN3q4k"))}
+    assert ours == set(declared_functions())
+
+
+def test_layout_version_and_workspace(lib):
+    assert lib.q4_layout_version() == 1
+    assert lib.w8a8_workspace_bytes(2048, 8192) == 2048 * 8192 + 2048 * 4
+    assert lib.w8a8_workspace_bytes(3, 16) == 256 + 12
+    assert lib.w8a8_workspace_bytes(0, 16) == 0
+
+
+FAKE = 0x10000          # never dereferenced: validation fails first
+MISAL = 0x10001
+
+
+@pytest.mark.parametrize("call,status", [
+    # bad group size / shape
+    (lambda L: L.q4_quantize_pack(FAKE, 4, 512, 100, 0, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.q4_quantize_pack(FAKE, 4, 500, 128, 0, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.q4_quantize_pack(FAKE, -1, 512, 128, 0, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.q4_quantize_pack(FAKE, 4, 512, 128, 0, FAKE, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.q4_quantize_pack(None, 4, 512, 128, 1, FAKE, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.q4_quantize_pack(MISAL, 4, 512, 128, 1, FAKE, FAKE, None, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.q4_quantize_pack(FAKE, 0, 512, 128, 0, None, None, None, None), q4.Q4_OK),
+    (lambda L: L.w4a16_linear(FAKE, 1, 16, 512, 64, FAKE, FAKE, FAKE, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.w4a16_linear(FAKE, 1, 16, 500, 128, FAKE, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w4a16_linear(MISAL, 1, 16, 512, 128, FAKE, FAKE, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.w4a16_linear(FAKE, 1, 16, 512, 128, MISAL, FAKE, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.w4a16_linear(FAKE, 1, 16, 512, 128, None, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w4a16_linear(FAKE, 0, 16, 512, 128, None, None, None, None, None), q4.Q4_OK),
+    (lambda L: L.w4a16_linear(FAKE, 3, 0, 512, 128, None, None, None, None, None), q4.Q4_OK),
+    (lambda L: L.q8_quantize_weight(FAKE, None, 4, 100, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.q8_quantize_weight(FAKE, MISAL, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.q8_quantize_act(FAKE, None, 4, 128, MISAL, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.q8_quantize_act(FAKE, None, 4, 128, None, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 140000, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w8a8_gemm(MISAL, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, None, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.w8a8_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE, 100, None, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w8a8_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE + 16, 4096, None, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.smoothquant_scales(FAKE, 4, FAKE, 4, 128, 1.5, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.smoothquant_scales(FAKE, 0, FAKE, 4, 128, 0.5, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+])
+def test_host_validation(lib, call, status):
+    assert call(lib) == status
+    msg = lib.q4_last_error().decode()
+    assert (msg == "") == (status == q4.Q4_OK)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        q4.w4a16_linear(torch.zeros(1, 128, dtype=torch.float16),
+                        torch.zeros(4, 64, dtype=torch.uint8),
+                        torch.zeros(4, 1, dtype=torch.float16), None)

@@ -1,0 +1,115 @@
+"""GPU parity of w4a16_linear against the oracle's exact fp64 product over
+the dequantized weight: small shapes that span several tiles with ragged M
+and N (both the skinny M <= 64 kernel and the tiled prefill kernel), one-hot
+inputs that pin nibble order and scale/zero indexing bit for bit, and the
+full-size decode, batched-decode and prefill workloads in the launch
+configuration the benchmark times (prefill on sampled rows)."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_gemm_q4_amd as q4
+import workloads
+from parity import check_gemm, gpu, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def quantize_gpu(W, g, sym):
+    return q4.q4_quantize_pack(gpu(W), g=g, sym=sym)
+
+
+def run_case(orc, W, X, g, sym, rows=None, what=""):
+    codes, scales, zeros = orc.q4_quantize_pack(W, g=g, sym=sym)
+    Y = host(q4.w4a16_linear(gpu(X), gpu(codes), gpu(scales.view(np.float16)),
+                             None if zeros is None else gpu(zeros), g=g))
+    Yref, B = orc.w4a16_ref(X, codes, scales, zeros, g=g, rows=rows)
+    Ysel = Y if rows is None else Y[rows]
+    return check_gemm(Ysel, Yref, B, what)
+
+
+def test_tiny_workload(orc):
+    w = workloads.tiny()
+    run_case(orc, w["W"], w["X"], w["g"], w["sym"], what="tiny")
+
+
+SHAPES = [(1, 16, 128), (1, 1000, 1024), (2, 33, 256), (3, 77, 256), (16, 300, 640),
+          (17, 129, 384), (33, 64, 256), (64, 130, 512), (65, 129, 384), (128, 128, 128),
+          (200, 260, 1024), (300, 1000, 768)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("sym", [False, True])
+def test_shapes(orc, M, N, K, sym):
+    W, X = workloads.small_case(M * 7919 + N * 31 + K, M, N, K)
+    run_case(orc, W, X, 128, sym, what=f"M={M} N={N} K={K} sym={sym}")
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 256, 100), (7, 384, 33), (256, 256, 130)])
+def test_one_hot_pins_layout(orc, M, K, N):
+    """X = rows of the identity: Y[m, n] = fp16(w_hat[n, m]) exactly."""
+    rng = np.random.default_rng(M + K + N)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    codes, scales, zeros = orc.q4_quantize_pack(W, g=128, sym=False)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), np.arange(M)] = 1.0
+    Y = host(q4.w4a16_linear(gpu(X), gpu(codes), gpu(scales.view(np.float16)), gpu(zeros)))
+    w_hat = orc.q4_dequant(codes, scales, zeros, K, 128)
+    expect = w_hat[:, :M].T.astype(np.float16)
+    assert np.array_equal(Y.view(np.uint16), expect.view(np.uint16))
+
+
+def test_codes_at_zero_point_give_zero(orc):
+    M, N, K = 70, 50, 512
+    X = workloads.normal_fp16(5, (M, K))
+    codes = np.full((N, K // 2), 0x33, np.uint8)
+    zeros = np.full((N, 2), 0x33, np.uint8)
+    scales = np.full((N, 4), 0.7, np.float16)
+    for m in (1, 20, M):
+        Y = host(q4.w4a16_linear(gpu(X[:m]), gpu(codes), gpu(scales), gpu(zeros)))
+        assert np.all(Y == 0)
+
+
+@pytest.mark.parametrize("N", [11008, 4096])
+def test_decode_workload(orc, N):
+    w = workloads.decode(N)
+    q = quantize_gpu(w["W"], w["g"], w["sym"])
+    codes, scales, zeros = (None if t is None else host(t) for t in q)
+    Y = host(q4.w4a16_linear(gpu(w["X"]), *q))
+    Yref, B = orc.w4a16_ref(w["X"], codes, scales, zeros)
+    check_gemm(Y, Yref, B, f"decode N={N}")
+
+
+@pytest.mark.parametrize("M", [16, 64])
+def test_batched_decode_workload(orc, M):
+    w = workloads.quant(M)
+    q = quantize_gpu(w["W"], w["g"], w["sym"])
+    codes, scales, zeros = (None if t is None else host(t) for t in q)
+    Y = host(q4.w4a16_linear(gpu(w["X"]), *q))
+    Yref, B = orc.w4a16_ref(w["X"], codes, scales, zeros)
+    check_gemm(Y, Yref, B, f"batched decode M={M}")
+
+
+def test_prefill_workload_sampled(orc):
+    w = workloads.prefill()
+    q = quantize_gpu(w["W"], w["g"], w["sym"])
+    codes, scales, zeros = (None if t is None else host(t) for t in q)
+    Y = host(q4.w4a16_linear(gpu(w["X"]), *q))
+    rows = sample_rows(w["X"].shape[0])
+    Yref, B = orc.w4a16_ref(w["X"], codes, scales, zeros, rows=rows)
+    check_gemm(Y[rows], Yref, B, "prefill")
+    assert np.isfinite(Y.astype(np.float32)).all()
+
+
+def test_errors_and_empty():
+    X = torch.zeros((4, 256), dtype=torch.float16, device="cuda")
+    codes = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
+    with pytest.raises(q4.Q4Error) as e:
+        q4.w4a16_linear(X, codes, torch.zeros((8, 4), dtype=torch.float16, device="cuda"), None, g=64)
+    assert e.value.status == q4.Q4_ERR_UNSUPPORTED
+    Y = q4.w4a16_linear(X[:0], codes, torch.zeros((8, 2), dtype=torch.float16, device="cuda"), None)
+    assert Y.shape == (0, 8)
+    with pytest.raises(q4.Q4Error) as e:
+        q4.w4a16_linear(X.view(-1)[1:257].view(1, 256), codes,
+                        torch.zeros((8, 2), dtype=torch.float16, device="cuda"), None)
+    assert e.value.status == q4.Q4_ERR_MISALIGNED

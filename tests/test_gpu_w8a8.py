@@ -1,0 +1,128 @@
+"""GPU parity of the W8A8 path against the oracle: INT8 weight and per-token
+activation codes and scales bit for bit, the SmoothQuant factor bit for bit
+at alpha = 0.5, int32 accumulators bit for bit, fp16 outputs bit for bit with
+the oracle's fp32 epilogue expression and within tolerance of the exact
+product; full-size W8A8 workload (GEMM checked on sampled rows)."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_gemm_q4_amd as q4
+import workloads
+from parity import check_gemm, gpu, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("N,K", [(1, 8), (7, 64), (100, 1000), (33, 8200), (5, 16384), (64, 4096)])
+@pytest.mark.parametrize("smooth", [False, True])
+def test_q8_weight(orc, N, K, smooth):
+    rng = np.random.default_rng(N + K)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    s = rng.uniform(0.2, 5.0, K).astype(np.float32) if smooth else None
+    Wq_ref, sw_ref = orc.q8_quantize_weight(W, s)
+    Wq, sw = q4.q8_quantize_weight(gpu(W), None if s is None else gpu(s))
+    assert np.array_equal(host(Wq), Wq_ref)
+    assert np.array_equal(host(sw).view(np.uint32), sw_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K", [(1, 8), (3, 64), (100, 1000), (33, 8200), (2, 16384), (64, 4096)])
+@pytest.mark.parametrize("smooth", [False, True])
+def test_q8_act(orc, M, K, smooth):
+    rng = np.random.default_rng(M * 3 + K)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    X[:, : max(1, K // 100)] *= 30
+    if M > 2:
+        X[1] = 0
+    X = X.astype(np.float16)
+    s = rng.uniform(0.2, 8.0, K).astype(np.float32) if smooth else None
+    Xq_ref, sx_ref = orc.q8_quantize_act(X, s)
+    Xq, sx = q4.q8_quantize_act(gpu(X), None if s is None else gpu(s))
+    assert np.array_equal(host(Xq), Xq_ref)
+    assert np.array_equal(host(sx).view(np.uint32), sx_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("alpha", [0.5, 0.25, 1.0, 0.0])
+def test_smoothquant_scales_small(orc, alpha):
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((300, 520)).astype(np.float32)
+    X[:, 3] *= 30
+    X[:, 10] = 0
+    W = (rng.standard_normal((77, 520)) * 0.02).astype(np.float32)
+    W[:, 11] = 0
+    X, W = X.astype(np.float16), W.astype(np.float16)
+    s_ref = orc.smooth_scales(X, W, alpha)
+    s = host(q4.smoothquant_scales(gpu(X), gpu(W), alpha))
+    if alpha == 0.5:
+        assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    else:
+        assert np.allclose(s, s_ref, rtol=8 * 2.0 ** -23, atol=0)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (5, 7, 48), (64, 64, 128), (130, 257, 272),
+                                   (128, 128, 1024), (300, 200, 8192)])
+def test_gemm_shapes(orc, M, N, K):
+    W, X = workloads.small_case(M * 131 + N * 7 + K, M, N, K)
+    Xq, sx = orc.q8_quantize_act(X)
+    Wq, sw = orc.q8_quantize_weight(W)
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    Y = host(q4.w8a8_gemm(gpu(Xq), gpu(sx), gpu(Wq), gpu(sw), acc_out=acc))
+    acc_ref, aacc, ovf = orc.int8_gemm(Xq, Wq)
+    assert ovf == 0
+    assert np.array_equal(host(acc).astype(np.int64), acc_ref)
+    Yref, B, y16 = orc.w8a8_epilogue(acc_ref, aacc, sx, sw)
+    assert np.array_equal(Y.view(np.uint16), y16)
+    check_gemm(Y, Yref, B, f"w8a8 M={M} N={N} K={K}")
+
+
+def test_closed_form_accumulator():
+    K = 8192
+    Xq = torch.full((3, K), 127, dtype=torch.int8, device="cuda")
+    Wq = torch.full((5, K), -127, dtype=torch.int8, device="cuda")
+    one = torch.ones(3, dtype=torch.float32, device="cuda")
+    acc = torch.empty((3, 5), dtype=torch.int32, device="cuda")
+    q4.w8a8_gemm(Xq, one, Wq, torch.ones(5, dtype=torch.float32, device="cuda"), acc_out=acc)
+    assert torch.all(acc == -16129 * K)
+
+
+def test_w8a8_workload(orc):
+    w = workloads.w8a8()
+    s_ref = orc.smooth_scales(w["Xcal"], w["W"], 0.5)
+    s = q4.smoothquant_scales(gpu(w["Xcal"]), gpu(w["W"]), 0.5)
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    Wq_ref, sw_ref = orc.q8_quantize_weight(w["W"], s_ref)
+    Wq, sw = q4.q8_quantize_weight(gpu(w["W"]), s)
+    assert np.array_equal(host(Wq), Wq_ref)
+    assert np.array_equal(host(sw).view(np.uint32), sw_ref.view(np.uint32))
+    M, K = w["X"].shape
+    N = w["W"].shape[0]
+    ws = q4.w8a8_workspace(M, K, "cuda")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    Y = host(q4.w8a8_linear(gpu(w["X"]), Wq, sw, s, workspace=ws, acc_out=acc))
+    # the workspace holds the per-token codes and scales: bit for bit
+    Xq_ref, sx_ref = orc.q8_quantize_act(w["X"], s_ref)
+    wsh = host(ws)
+    assert np.array_equal(wsh[: M * K].view(np.int8).reshape(M, K), Xq_ref)
+    off = (M * K + 255) // 256 * 256
+    assert np.array_equal(wsh[off: off + 4 * M].view(np.uint32), sx_ref.view(np.uint32))
+    rows = sample_rows(M)
+    acc_ref, aacc, ovf = orc.int8_gemm(Xq_ref, Wq_ref, rows=rows)
+    assert ovf == 0
+    assert np.array_equal(host(acc)[rows].astype(np.int64), acc_ref)
+    Yref, B, y16 = orc.w8a8_epilogue(acc_ref, aacc, sx_ref, sw_ref, rows=rows)
+    assert np.array_equal(Y[rows].view(np.uint16), y16)
+    check_gemm(Y[rows], Yref, B, "w8a8 workload")
+
+
+def test_errors():
+    Xq = torch.zeros((4, 100), dtype=torch.int8, device="cuda")
+    with pytest.raises(q4.Q4Error) as e:
+        q4.w8a8_gemm(Xq, torch.ones(4, device="cuda"), torch.zeros((4, 100), dtype=torch.int8, device="cuda"),
+                     torch.ones(4, device="cuda"))
+    assert e.value.status == q4.Q4_ERR_INVALID_ARG
+    X = torch.zeros((4, 128), dtype=torch.float16, device="cuda")
+    with pytest.raises(q4.Q4Error) as e:
+        q4.w8a8_linear(X, torch.zeros((4, 128), dtype=torch.int8, device="cuda"),
+                       torch.ones(4, device="cuda"),
+                       workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == q4.Q4_ERR_INVALID_ARG
