@@ -1,0 +1,304 @@
+"""Benchmark of the group-quantized linear layer on one MI355X.
+
+Headline workload (one step): Llama-shaped W4A16 decode, M = 1 token,
+K = 4096, g = 128 asymmetric INT4, packed ahead of time; a step runs the
+N = 11008 layer and then the N = 4096 layer. The metric is HBM throughput:
+the algorithmic bytes of a step (packed codes + fp16 scales + 4-bit
+zero-points + X + Y) over its time. Inputs are resident in HBM before the
+timed region; every step reads a different copy of the packed weights
+(copies totalling more than 512 MB), so the 256 MB Infinity Cache cannot
+serve repeats. Launches are captured in a HIP graph (one graph holds one
+pass over the weight copies) and replayed.
+
+The JSON line also carries:
+  roofline      the dominant kernel (the N = 11008 GEMV) timed alone with HIP
+                events on its stream, against 8 TB/s;
+  cpu_baseline  the CPU oracle (fp64 reference over the dequantized weights)
+                timed on this host's cores on the same step;
+  extra         prefill (M = 2048, sym) TFLOP/s against the fp16 MFMA peak,
+                W8A8 (M = 2048, K = N = 8192) TOP/s against the int8 peak,
+                quantize + pack GB/s, batched decode M = 16 / 64.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
+                       [--only decode|prefill|w8a8|quant|batched] [--eager]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16
+INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8
+METRIC = "W4A16 g128 GEMM: GB/s at M=1, TFLOP/s at M=2048 (% of roofline)"
+MALL_BYTES = 512 * 2 ** 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def w4a16_bytes(M: int, N: int, K: int, g: int = 128, sym: bool = False) -> int:
+    """Algorithmic HBM bytes of one W4A16 call: packed codes, fp16 scales,
+    4-bit zero-points (asym), fp16 X read once, fp16 Y written once."""
+    G = K // g
+    return N * K // 2 + N * G * 2 + (0 if sym else N * ((G + 1) // 2)) + M * K * 2 + M * N * 2
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--only", default=None, choices=["decode", "prefill", "w8a8", "quant", "batched"])
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a graph")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this layer has no multi-GPU path to time.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_gemm_q4_amd as q4
+    import workloads
+
+    if not os.path.exists(q4.LIB_PATH):
+        from quantized_gemm_q4_amd import build
+        build.build()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def gpu(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.float16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.float16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    def timed(fn, n):
+        """Run fn(i) for i < n between two HIP events on the current stream."""
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3  # seconds
+
+    def graph_of(fn, n):
+        """Capture fn(0..n-1) into one HIP graph (eager fallback with --eager)."""
+        if args.eager:
+            return lambda: [fn(i) for i in range(n)]
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream(dev)
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            fn(0)
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        torch.cuda.synchronize()
+        return g.replay
+
+    out = {"metric": METRIC, "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f16", "data": "synthetic"}
+    extra = {}
+    only = args.only
+
+    # ---- headline: decode step (N = 11008 then N = 4096, M = 1) ------------
+    if only in (None, "decode"):
+        layers = []
+        for N in (11008, 4096):
+            w = workloads.decode(N)
+            packed = q4.q4_quantize_pack(gpu(w["W"]), g=128, sym=False)
+            layers.append(dict(N=N, X=gpu(w["X"]), packed=packed,
+                               Y=torch.empty((1, N), dtype=torch.float16, device=dev)))
+        step_bytes = sum(w4a16_bytes(1, L["N"], 4096) for L in layers)
+        # enough copies that even the N = 11008 layer alone cycles > 512 MB
+        copies = max(2, math.ceil(MALL_BYTES / w4a16_bytes(1, 11008, 4096)) + 1)
+        for L in layers:
+            L["copies"] = [tuple(t.clone() for t in L["packed"]) for _ in range(copies)]
+
+        def step(i):
+            c = i % copies
+            for L in layers:
+                q4.w4a16_linear(L["X"], *L["copies"][c], out=L["Y"])
+
+        for i in range(args.warmup):
+            step(i)
+        K = args.steps
+        full = graph_of(step, copies)
+        rem = K % copies
+        tail = graph_of(step, rem) if rem else None
+        full()
+        torch.cuda.synchronize()
+        t = timed(lambda i: full() if i < K // copies else tail(), K // copies + (1 if rem else 0))
+        out.update(value=step_bytes * K / t / 1e9, unit="GB/s", steps=K, warmup=args.warmup,
+                   ms_per_step=t / K * 1e3)
+        out["config"] = {"workload": "W4A16 decode: M=1, K=4096, N=11008 then N=4096, asym INT4 "
+                                     "g=128 pre-packed; X ~ N(0,1), W ~ N(0,0.02) with 1% of "
+                                     "K-channels x10",
+                         "bytes_per_step": step_bytes, "weight_copies": copies,
+                         "launch": "eager" if args.eager else "hip-graph",
+                         "seeds": {"W": 1002, "X": 2002, "outliers": 4002}}
+
+        # dominant kernel alone: the N = 11008 GEMV
+        L = layers[0]
+        ncopy = len(L["copies"])
+        g11 = graph_of(lambda i: q4.w4a16_linear(L["X"], *L["copies"][i % ncopy], out=L["Y"]), ncopy)
+        g11()
+        reps = max(1, 4000 // ncopy)
+        t11 = timed(lambda i: g11(), reps) / (reps * ncopy)
+        b11 = w4a16_bytes(1, 11008, 4096)
+        out["roofline"] = {"kernel": "w4a16_skinny_kernel<1,1,8> (M=1, N=11008, K=4096)",
+                           "bound": "hbm", "achieved": b11 / t11 / 1e9, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": b11 / t11 / 1e9 / HBM_PEAK_GBS,
+                           "traffic": None, "avg_launch_us": t11 * 1e6,
+                           "algorithmic_bytes_per_launch": b11}
+        L4 = layers[1]
+        g4 = graph_of(lambda i: q4.w4a16_linear(L4["X"], *L4["copies"][i % ncopy], out=L4["Y"]), ncopy)
+        g4()
+        t4 = timed(lambda i: g4(), reps) / (reps * ncopy)
+        b4 = w4a16_bytes(1, 4096, 4096)
+        extra["decode_n4096"] = {"us": t4 * 1e6, "GB/s": b4 / t4 / 1e9, "frac_hbm": b4 / t4 / 1e9 / HBM_PEAK_GBS}
+        extra["decode_n11008"] = {"us": t11 * 1e6, "GB/s": b11 / t11 / 1e9, "frac_hbm": b11 / t11 / 1e9 / HBM_PEAK_GBS}
+        del layers, L, L4
+        torch.cuda.empty_cache()
+
+        if not args.skip_cpu:
+            out["cpu_baseline"] = cpu_baseline(step_bytes)
+
+    # ---- batched decode M = 16, 64 ---------------------------------------------
+    if only in (None, "batched"):
+        w = workloads.quant()
+        packed = q4.q4_quantize_pack(gpu(w["W"]), g=128, sym=False)
+        bytes1 = w4a16_bytes(16, 11008, 4096)
+        copies = max(2, math.ceil(MALL_BYTES / bytes1) + 1)
+        cps = [tuple(t.clone() for t in packed) for _ in range(copies)]
+        for M in (16, 64):
+            X = gpu(workloads.quant(M)["X"])
+            Y = torch.empty((M, 11008), dtype=torch.float16, device=dev)
+            gr = graph_of(lambda i: q4.w4a16_linear(X, *cps[i % copies], out=Y), copies)
+            gr()
+            reps = max(1, 1000 // copies)
+            tt = timed(lambda i: gr(), reps) / (reps * copies)
+            nb = w4a16_bytes(M, 11008, 4096)
+            extra[f"batched_m{M}"] = {"us": tt * 1e6, "GB/s": nb / tt / 1e9,
+                                      "frac_hbm": nb / tt / 1e9 / HBM_PEAK_GBS,
+                                      "TFLOP/s": 2 * M * 11008 * 4096 / tt / 1e12}
+        del cps, packed
+        torch.cuda.empty_cache()
+
+    # ---- quantize + pack -----------------------------------------------------
+    if only in (None, "quant"):
+        w = workloads.quant()
+        W = gpu(w["W"])
+        nW = max(2, math.ceil(MALL_BYTES / W.numel() / 2) + 1)
+        Ws = [W.clone() for _ in range(nW)]
+        res = q4.q4_quantize_pack(W)
+        for i in range(5):
+            q4.q4_quantize_pack(Ws[i % nW], out=res)
+        reps = 60
+        tq = timed(lambda i: q4.q4_quantize_pack(Ws[i % nW], out=res), reps) / reps
+        qbytes = 11008 * 4096 * 2 + 11008 * 2048 + 11008 * 32 * 2 + 11008 * 16
+        extra["quantize_pack"] = {"shape": [11008, 4096], "us": tq * 1e6, "GB/s": qbytes / tq / 1e9,
+                                  "frac_hbm": qbytes / tq / 1e9 / HBM_PEAK_GBS, "bytes": qbytes}
+        del Ws, W, res
+        torch.cuda.empty_cache()
+
+    # ---- prefill M = 2048 --------------------------------------------------------
+    if only in (None, "prefill"):
+        w = workloads.prefill()
+        packed = q4.q4_quantize_pack(gpu(w["W"]), g=128, sym=True)
+        X = gpu(w["X"])
+        Y = torch.empty((2048, 11008), dtype=torch.float16, device=dev)
+        for _ in range(3):
+            q4.w4a16_linear(X, *packed, out=Y)
+        reps = 30
+        tp = timed(lambda i: q4.w4a16_linear(X, *packed, out=Y), reps) / reps
+        flops = 2 * 2048 * 11008 * 4096
+        extra["prefill"] = {"shape": [2048, 11008, 4096], "us": tp * 1e6,
+                            "TFLOP/s": flops / tp / 1e12,
+                            "frac_mfma_fp16": flops / tp / 1e12 / FP16_MFMA_PEAK_TFLOPS}
+        del packed, X, Y
+        torch.cuda.empty_cache()
+
+    # ---- W8A8 M = 2048, K = N = 8192 ------------------------------------------
+    if only in (None, "w8a8"):
+        w = workloads.w8a8()
+        s = q4.smoothquant_scales(gpu(w["Xcal"]), gpu(w["W"]), 0.5)
+        Wq, sw = q4.q8_quantize_weight(gpu(w["W"]), s)
+        X = gpu(w["X"])
+        M, K = X.shape
+        N = Wq.shape[0]
+        ws = q4.w8a8_workspace(M, K, dev)
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        Xq, sx = q4.q8_quantize_act(X, s)
+        for _ in range(3):
+            q4.w8a8_linear(X, Wq, sw, s, workspace=ws, out=Y)
+        reps = 30
+        tl = timed(lambda i: q4.w8a8_linear(X, Wq, sw, s, workspace=ws, out=Y), reps) / reps
+        tg = timed(lambda i: q4.w8a8_gemm(Xq, sx, Wq, sw, out=Y), reps) / reps
+        ta = timed(lambda i: q4.q8_quantize_act(X, s, out=(Xq, sx)), reps) / reps
+        ops = 2 * M * N * K
+        abytes = M * K * 2 + K * 4 + M * K + M * 4
+        extra["w8a8"] = {"shape": [M, N, K], "linear_us": tl * 1e6, "linear_TOP/s": ops / tl / 1e12,
+                         "gemm_us": tg * 1e6, "gemm_TOP/s": ops / tg / 1e12,
+                         "gemm_frac_mfma_int8": ops / tg / 1e12 / INT8_MFMA_PEAK_TOPS,
+                         "act_quant_us": ta * 1e6, "act_quant_GB/s": abytes / ta / 1e9}
+
+    if extra:
+        out["extra"] = extra
+    if "value" not in out:
+        out.update(value=None, unit="GB/s", steps=0, warmup=args.warmup, ms_per_step=None,
+                   config={"workload": f"partial run: {only}"})
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(step_bytes: int) -> dict:
+    """The CPU oracle on the decode step: the exact fp64 product over the
+    dequantized weights for N = 11008 and N = 4096 at M = 1, repeated until
+    about 10 s of work."""
+    import oracle
+    import workloads
+
+    layers = []
+    for N in (11008, 4096):
+        w = workloads.decode(N)
+        c, s, z = oracle.q4_quantize_pack(w["W"], g=128, sym=False)
+        layers.append((w["X"], c, s, z))
+
+    def one():
+        for X, c, s, z in layers:
+            oracle.w4a16_ref(X, c, s, z)
+
+    t0 = time.perf_counter()
+    one()
+    t1 = time.perf_counter() - t0
+    reps = max(1, min(60, int(10.0 / max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        one()
+    t = time.perf_counter() - t0
+    return {"value": step_bytes * reps / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": t,
+            "sample": f"the full decode step (M=1, K=4096, N=11008 then N=4096) x {reps}; "
+                      "fp64 reference product over the dequantized weights"}
+
+
+if __name__ == "__main__":
+    main()

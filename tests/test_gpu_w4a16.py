@@ -113,3 +113,16 @@ def test_errors_and_empty():
         q4.w4a16_linear(X.view(-1)[1:257].view(1, 256), codes,
                         torch.zeros((8, 2), dtype=torch.float16, device="cuda"), None)
     assert e.value.status == q4.Q4_ERR_MISALIGNED
+
+
+# Shapes that route to each launch variant of the decode GEMV kernel
+# (wavefronts per block x k-blocks per wavefront): (11008, 4096) -> 4 x 8,
+# (4096, 4096) -> 8 x 4, (1000, 4096) -> 16 x 2 with a ragged last tile,
+# (4096, 8192) -> 8 x 8; M up to 7 (X must fit in 64 KiB of LDS).
+@pytest.mark.parametrize("M,N,K", [(1, 11008, 4096), (3, 11008, 4096), (1, 4096, 4096),
+                                   (7, 4096, 4096), (2, 1000, 4096), (1, 4096, 8192),
+                                   (5, 4096, 8192)])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemv_variants(orc, M, N, K, sym):
+    W, X = workloads.small_case(M * 13 + N + K * 3 + int(sym), M, N, K)
+    run_case(orc, W, X, 128, sym, what=f"gemv M={M} N={N} K={K} sym={sym}")
