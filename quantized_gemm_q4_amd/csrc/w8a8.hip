@@ -114,6 +114,178 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_gemm_kernel(
         }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel (K % 256 == 0). Built around v_mfma_i32_32x32x32_i8, which
+// runs near the int8 peak on gfx950 where the 16x16x64 form does not. A
+// 512-thread block computes a 256 x 256 tile of Y; its 8 wavefronts form a
+// 2 (M) x 4 (N) grid of 128 x 64 sub-tiles (4 x 2 MFMA tiles of 32 x 32, 128
+// int32 accumulators per lane).
+//
+// Operand staging: K advances 64 bytes per step through four LDS stages
+// (32 KB each: 256 rows of X and 256 rows of W, 64 bytes per row), filled
+// by direct global-to-LDS loads (global_load_lds_dwordx4, lane i of a load
+// lands at base + 16 i) issued three steps ahead, so a step's data has three
+// steps of MFMA work to arrive in and no registers are spent on staging.
+// Before a stage is read every wavefront waits for its own loads of that
+// stage (vmcnt) and for its earlier LDS reads (lgkmcnt), then the block
+// meets at a barrier. The 16-byte chunks of a row are stored XOR-swizzled
+// (chunk c of row r at c ^ ((r >> 2) & 3)) so the 32 rows an operand read
+// touches fall in distinct banks.
+//
+// MFMA output layout: lane l holds column l % 32 and rows
+// 8 (r / 4) + 4 (l / 32) + r % 4 of its 32 x 32 tile.
+//
+// Tile order is XCD-aware: consecutive block ids go to the 8 XCDs in turn, so
+// block b computes tile t = (b % 8) * (blocks / 8) + b / 8; each XCD then owns
+// whole columns of N-tiles, and its L2 serves their reuse of the W tiles.
+constexpr int LBM = 256, LBN = 256, LBK = 64, LSTAGES = 4;
+constexpr int LSTAGE_BYTES = (LBM + LBN) * LBK;   // 32 KB
+
+// s_waitcnt with vmcnt = n (lgkmcnt 0, expcnt no wait); gfx9 encoding.
+#define Q4_WAIT_VM_LGKM0(n) \
+    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (0 << 8))
+
+__global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
+    const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
+    const float *__restrict__ sw, int M, int N, int K, int tiles_m, uint16_t *__restrict__ Y,
+    int32_t *__restrict__ acc_out)
+{
+    __shared__ __attribute__((aligned(1024))) int8_t st0[LSTAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t st1[LSTAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t st2[LSTAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t st3[LSTAGE_BYTES];
+    int8_t *const stages[LSTAGES] = {st0, st1, st2, st3};
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    const int blocks = gridDim.x;
+    const int b = blockIdx.x;
+    const int t = (blocks % 8 == 0) ? (b % 8) * (blocks / 8) + b / 8 : b;
+    const int m0 = (t % tiles_m) * LBM, n0 = (t / tiles_m) * LBN;
+    const int KT = K / LBK;
+
+    // Direct-load assignment: a stage holds 32 blocks of 1 KB (16 rows x 64 B):
+    // blocks 0-15 are X rows, 16-31 W rows; wavefront w loads blocks 2w, 2w+1
+    // (X) and 16 + 2w, 16 + 2w + 1 (W). Lane i of block q writes row
+    // 16 q + i / 4, stored chunk i % 4, which holds logical chunk
+    // (i % 4) ^ ((i >> 4) & 3).
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    uint32_t goff[4];                    // byte offsets from Xq (j < 2) or Wq (j >= 2)
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        int m = m0 + (2 * wave + j) * 16 + (lane >> 2);
+        int n = n0 + (2 * wave + j) * 16 + (lane >> 2);
+        m = m < M ? m : M - 1;
+        n = n < N ? n : N - 1;
+        goff[j] = (uint32_t)m * (uint32_t)K + 16 * dchunk;
+        goff[2 + j] = (uint32_t)n * (uint32_t)K + 16 * dchunk;
+    }
+    auto issue = [&](int8_t *stage, int kt) {
+        const uint32_t kofs = (uint32_t)kt * LBK;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            __builtin_amdgcn_global_load_lds(Xq + goff[j] + kofs, stage + (2 * wave + j) * 1024, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Wq + goff[2 + j] + kofs,
+                                             stage + (16 + 2 * wave + j) * 1024, 16, 0, 0);
+        }
+    };
+
+    // operand read offsets inside a stage (swizzled chunk per k32 step s)
+    const int swz = (l32 >> 2) & 3;
+    const int co0 = 16 * ((0 + h) ^ swz), co1 = 16 * ((2 + h) ^ swz);
+    const int arow = (wm * 128 + l32) * LBK;
+    const int brow = LBM * LBK + (wn * 64 + l32) * LBK;
+
+    intx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
+
+    // Operand fragments of one 64-byte step: both k32 halves are read before
+    // the first MFMA, so the second half's LDS latency hides under the first
+    // half's MFMAs.
+    struct Frags {
+        intx4 a[2][4], b[2][2];
+    };
+    auto read = [&](const int8_t *stage, Frags &f) {
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            const int co = s ? co1 : co0;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                f.a[s][i] = *reinterpret_cast<const intx4 *>(stage + arow + i * 32 * LBK + co);
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                f.b[s][j] = *reinterpret_cast<const intx4 *>(stage + brow + j * 32 * LBK + co);
+        }
+    };
+    auto mma = [&](const Frags &f) {
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[s][i], f.b[s][j], acc[i][j], 0, 0, 0);
+    };
+
+    // Software pipeline (four LDS stages, two register fragment sets): in
+    // step k the wavefront waits for its loads of stage k + 1 and meets the
+    // block at the barrier, reads stage k + 1's fragments, refills stage k
+    // (drained into registers one step ago) with step k + 4, then runs step
+    // k's MFMAs from registers while those reads and loads are in flight.
+    issue(stages[0], 0);
+    if (1 < KT) issue(stages[1], 1);
+    if (2 < KT) issue(stages[2], 2);
+    if (3 < KT) issue(stages[3], 3);
+    Frags f[2];
+    if (3 < KT) Q4_WAIT_VM_LGKM0(12);
+    else Q4_WAIT_VM_LGKM0(0);
+    __builtin_amdgcn_s_barrier();
+    read(stages[0], f[0]);
+    for (int kt = 0; kt < KT; kt += LSTAGES) {
+#pragma unroll
+        for (int u = 0; u < LSTAGES; u++) {
+            const int k = kt + u;
+            if (k + 1 < KT) {
+                // loads outstanding: stages k + 1 .. min(k + 3, KT - 1)
+                if (k + 3 < KT) Q4_WAIT_VM_LGKM0(8);
+                else if (k + 2 < KT) Q4_WAIT_VM_LGKM0(4);
+                else Q4_WAIT_VM_LGKM0(0);
+                __builtin_amdgcn_s_barrier();
+                read(stages[(u + 1) % LSTAGES], f[(u + 1) & 1]);
+                if (k + 4 < KT) issue(stages[u], k + 4);
+            }
+            mma(f[u & 1]);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (m >= M) continue;
+            const float xs = sx[m];
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int n = n0 + wn * 64 + j * 32 + l32;
+                if (n >= N) continue;
+                const int32_t a = acc[i][j][r];
+                if (acc_out) acc_out[(int64_t)m * N + n] = a;
+                float f = (float)a * xs;
+                f = f * sw[n];
+                asm volatile("" : "+v"(f));   // keep the fp32 product (see the small kernel)
+                Y[(int64_t)m * N + n] = f2h(f);
+            }
+        }
+}
+
 }  // namespace
 
 hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
@@ -121,6 +293,12 @@ hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
                             hipStream_t st)
 {
     if (M == 0 || N == 0) return hipSuccess;
+    if (K % (LSTAGES * LBK) == 0 && M * K < (int64_t)1 << 31 && N * K < (int64_t)1 << 31) {
+        const int tiles_m = (int)((M + LBM - 1) / LBM), tiles_n = (int)((N + LBN - 1) / LBN);
+        w8a8_gemm_large_kernel<<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N,
+                                                                 (int)K, tiles_m, Y, acc_out);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((N + QBN - 1) / QBN), (unsigned)((M + QBM - 1) / QBM));
     w8a8_gemm_kernel<<<grid, kThreads, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N, (int)K, Y, acc_out);
     return hipGetLastError();
