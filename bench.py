@@ -21,6 +21,7 @@ The JSON line also carries:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
                        [--only decode|prefill|w8a8|quant|batched] [--eager]
+                       [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -41,6 +42,12 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16
 INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8
 METRIC = "W4A16 g128 GEMM: GB/s at M=1, TFLOP/s at M=2048 (% of roofline)"
 MALL_BYTES = 512 * 2 ** 20
+COPY_BYTES = 2 ** 30
+# The kernel the dispatcher picks for M = 1, N = 11008, K = 4096, g = 128 asym
+# (688 blocks of 8 wavefronts, 4 k-blocks per wavefront).
+DECODE_KERNEL = "w4a16_gemv_kernel<8, 4, true>"
+DECODE_SOURCE = os.path.join(ROOT, "quantized_gemm_q4_amd", "csrc", "w4a16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_gemv_decode_n11008_traffic.json")
 
 
 def log(*a):
@@ -62,6 +69,8 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--only", default=None, choices=["decode", "prefill", "w8a8", "quant", "batched"])
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -161,14 +170,14 @@ def main():
         ncopy = len(L["copies"])
         g11 = graph_of(lambda i: q4.w4a16_linear(L["X"], *L["copies"][i % ncopy], out=L["Y"]), ncopy)
         g11()
-        reps = max(1, 4000 // ncopy)
+        reps = max(1, 2 * K // ncopy)
         t11 = timed(lambda i: g11(), reps) / (reps * ncopy)
         b11 = w4a16_bytes(1, 11008, 4096)
-        out["roofline"] = {"kernel": "w4a16_skinny_kernel<1,1,8> (M=1, N=11008, K=4096)",
+        out["roofline"] = {"kernel": DECODE_KERNEL + " (M=1, N=11008, K=4096)",
                            "bound": "hbm", "achieved": b11 / t11 / 1e9, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": b11 / t11 / 1e9 / HBM_PEAK_GBS,
-                           "traffic": None, "avg_launch_us": t11 * 1e6,
-                           "algorithmic_bytes_per_launch": b11}
+                           "traffic": measured_traffic(), "avg_launch_us": t11 * 1e6,
+                           "algorithmic_bytes_per_launch": b11, "launches": reps * ncopy}
         L4 = layers[1]
         g4 = graph_of(lambda i: q4.w4a16_linear(L4["X"], *L4["copies"][i % ncopy], out=L4["Y"]), ncopy)
         g4()
@@ -261,12 +270,41 @@ def main():
                          "gemm_frac_mfma_int8": ops / tg / 1e12 / INT8_MFMA_PEAK_TOPS,
                          "act_quant_us": ta * 1e6, "act_quant_GB/s": abytes / ta / 1e9}
 
+    # ---- known-size copy: scales the HBM byte counters (profiling runs only) -
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_calibration"] = {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                                     "launches": 4}
+        del src, dst
+
     if extra:
         out["extra"] = extra
     if "value" not in out:
         out.update(value=None, unit="GB/s", steps=0, warmup=args.warmup, ms_per_step=None,
                    config={"workload": f"partial run: {only}"})
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode GEMV from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads
+    for a copy of known size). None when that summary is missing or was
+    taken on a different revision of the kernel source."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(DECODE_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha or rec.get("kernel") != DECODE_KERNEL:
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(step_bytes: int) -> dict:
@@ -289,7 +327,7 @@ def cpu_baseline(step_bytes: int) -> dict:
     t0 = time.perf_counter()
     one()
     t1 = time.perf_counter() - t0
-    reps = max(1, min(60, int(10.0 / max(t1, 1e-3))))
+    reps = max(1, min(5000, int(10.0 / max(t1, 1e-3))))
     t0 = time.perf_counter()
     for _ in range(reps):
         one()
