@@ -24,7 +24,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-fvisibility=
 SOURCES = {
     "abi.hip": [],
     "quantize.hip": ["-ffp-contract=off"],
-    "w4a16.hip": [],
+    "w4a16.hip": ["-ffp-contract=off"],
     "w8a8.hip": ["-ffp-contract=off"],
 }
 

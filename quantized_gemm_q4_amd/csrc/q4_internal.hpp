@@ -16,6 +16,11 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// s_waitcnt with vmcnt = n, lgkmcnt = 0, expcnt not waited (gfx9 encoding:
+// vmcnt low bits 3:0 and high bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+#define Q4_WAIT_VM_LGKM0(n) \
+    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (0 << 8))
+
 // binary16 bits <-> fp32 with the hardware converts (v_cvt_f32_f16 is exact;
 // v_cvt_f16_f32 rounds to nearest even, subnormals kept).
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }

@@ -43,6 +43,15 @@ int gemv_waves_override()
     return v;
 }
 
+// Tuning override for the large-M GEMM: Q4_GEMM_NU=4|8|11 forces the tile
+// width (32 NU columns). Read at every call.
+int gemm_nu_override()
+{
+    const char *e = std::getenv("Q4_GEMM_NU");
+    const int v = e ? std::atoi(e) : 0;
+    return (v == 4 || v == 8 || v == 11) ? v : 0;
+}
+
 constexpr int kThreads = 256;
 
 // Dequantize the 8 nibbles of one code dword (nib_i at bits 4i, k offset i)
@@ -458,6 +467,248 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_prefill_kernel(
             }
 }
 
+// ---------------------------------------------------------------------------
+// Large-M GEMM (prefill), M >= 256, g a multiple of 128. Compute bound.
+//
+// A block of 8 / WM wavefronts owns a 256 x (32 NU) tile of Y; wavefront w
+// owns rows 32 WM w .. 32 WM (w + 1) - 1 of it across all 32 NU columns
+// (WM x NU accumulators of v_mfma_f32_32x32x16_f16). K advances 32 at a time.
+// Every global read is a direct-to-LDS load (global_load_lds), issued three
+// steps ahead into one of four stages; a stage holds
+//   - X: 256 rows x 32 fp16 (16 KB, 64-byte rows);
+//   - the 16-byte code run (32 nibbles) of each of the tile's weight rows;
+//   - the dword holding each row's group scale, and (asymmetric) the dword
+//     holding its zero-point nibble.
+// One step ahead of the MFMAs, thread t dequantizes weight row t of the next
+// step from its stage into one of two LDS buffers as fp16 (u - zp) * s, one
+// code dword in the shadow of each column tile's MFMAs. LDS rows of X and of
+// the dequantized W are 64 bytes (4 chunks of 8 k); chunk c of row r is
+// stored at c ^ ((r >> 2) & 3), which keeps the 16-byte operand reads
+// conflict-free. Waits are explicit vmcnt counts (every wavefront issues the
+// same loads each step), so the loads of later steps stay in flight across
+// the per-step barrier.
+//
+// Arithmetic. Unlike the decode kernels, the scale is folded into the
+// operand: each dequantized weight is f2h((u - zp) * s) with one rounding
+// ((u - zp) is exact in fp16 and v_pk_mul_f16 rounds the exact product), so
+// one fp32 accumulator serves all groups. The weights' rounding (relative
+// <= 2^-11 each) and the fp16 output rounding stay inside the
+// 2^-10 * sum |x||w_hat| bound; the X operand is permuted to the dequant's
+// k order (0,4,1,5,2,6,3,7) in registers after its LDS read.
+constexpr int GBM = 256, GBK = 32;
+constexpr int G_X_BYTES = GBM * GBK * 2;            // 16 KB of X per stage
+
+// fp16 (u - zp) * s of the 8 nibbles of one code dword, in the operand k
+// order (0,4,1,5,2,6,3,7). The bit-0 pairs give (1024 + u) - (1024 + zp), the
+// bit-4 pairs (1024 + 16u) / 16 - (64 + zp) in one fma; both are exact.
+__device__ __forceinline__ u32x4 dequant8_scaled(uint32_t w, half2v zlo, half2v zhi, half2v s)
+{
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
+    const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const uint32_t w8 = w >> 8;
+    const half2v d0 = (__builtin_bit_cast(half2v, and_or(w, lo, magic)) + zlo) * s;
+    const half2v d1 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, and_or(w, hi, magic)), sixteenth, zhi) * s;
+    const half2v d2 = (__builtin_bit_cast(half2v, and_or(w8, lo, magic)) + zlo) * s;
+    const half2v d3 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, and_or(w8, hi, magic)), sixteenth, zhi) * s;
+    const u32x4 r = {__builtin_bit_cast(uint32_t, d0), __builtin_bit_cast(uint32_t, d1),
+                     __builtin_bit_cast(uint32_t, d2), __builtin_bit_cast(uint32_t, d3)};
+    return r;
+}
+
+template <int NU, int WM, bool ASYM>
+__global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
+    const uint16_t *__restrict__ X, int M, int N, int K, int gsteps,
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+    const uint8_t *__restrict__ zeros, int tiles_m, uint16_t *__restrict__ Y)
+{
+    constexpr int BN = 32 * NU;
+    constexpr int THREADS = 512 / WM, WAVES = 8 / WM;
+    static_assert(BN <= THREADS, "one weight row per thread");
+    constexpr int XL = G_X_BYTES / 1024 / WAVES;        // X loads per wavefront per step
+    constexpr int NS = XL + 2 + (ASYM ? 1 : 0);         // loads per wavefront per step
+    // stage layout: X | codes (16 B per thread) | scale dwords | zero dwords
+    constexpr int ST_C = G_X_BYTES, ST_S = ST_C + 16 * THREADS, ST_Z = ST_S + 4 * THREADS;
+    constexpr int ST_BYTES = ST_Z + (ASYM ? 4 * THREADS : 0);
+    constexpr int B_BYTES = BN * GBK * 2;
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[ST_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[ST_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[ST_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[ST_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb1[B_BYTES];
+    unsigned char *const stg[4] = {st0, st1, st2, st3};
+    unsigned char *const sb[2] = {sb0, sb1};
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int blocks = gridDim.x, b = blockIdx.x;
+    // consecutive tiles go to one XCD (blocks are dealt to the 8 XCDs round robin)
+    const int t = (blocks % 8 == 0) ? (b % 8) * (blocks / 8) + b / 8 : b;
+    const int m0 = (t % tiles_m) * GBM, n0 = (t / tiles_m) * BN;
+    const int KT = K / GBK;
+    const uint32_t G = (uint32_t)(KT / gsteps), Gz = (G + 1) >> 1;
+
+    // X loads: 1 KB blocks of 16 rows; wavefront w fills blocks XL w ..
+    // XL w + XL - 1. Lane i of block q lands on row 16 q + i / 4, stored chunk
+    // i % 4, and so fetches logical chunk (i % 4) ^ ((i >> 4) & 3).
+    const unsigned char *Xb = reinterpret_cast<const unsigned char *>(X);
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    static_assert(XL <= 4, "X loads per wavefront");
+    uint32_t xoff[4];   // fixed size: with a template-dependent size captured by the lambdas
+                        // below, the host pass silently dropped the kernel launch stub
+#pragma unroll
+    for (int j = 0; j < XL; j++) {
+        int m = m0 + (XL * wave + j) * 16 + (lane >> 2);
+        m = m < M ? m : M - 1;
+        xoff[j] = (uint32_t)m * (uint32_t)K * 2u + 16u * (uint32_t)dchunk;
+    }
+    // Weight loads: thread t fetches row t of the tile (rows past the tile or
+    // past N refetch a valid row; they are never stored).
+    int wrow = tid < BN ? tid : BN - 1;
+    const uint32_t n_w = (uint32_t)(n0 + wrow < N ? n0 + wrow : N - 1);
+    const uint32_t coff = n_w * (uint32_t)(K >> 1);
+    const uint32_t soff = n_w * G;    // in halves
+    const uint32_t zoff = n_w * Gz;   // in bytes
+
+    auto issue = [&](int k, int st) {   // st = k % 4, a compile-time constant
+        unsigned char *s = stg[st];
+        const uint32_t grp = (uint32_t)k / (uint32_t)gsteps;
+#pragma unroll
+        for (int j = 0; j < XL; j++)
+            __builtin_amdgcn_global_load_lds(Xb + xoff[j] + (uint32_t)k * (GBK * 2),
+                                             s + (XL * wave + j) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(codes + coff + (uint32_t)k * 16u, s + ST_C + wave * 1024, 16, 0, 0);
+        // the aligned dword that holds the scale (and the one that holds the
+        // zero-point byte); an aligned dword holding a valid byte never
+        // crosses into an unmapped page
+        const uintptr_t sa_ = reinterpret_cast<uintptr_t>(scales) + 2u * (soff + grp);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char *>(sa_ & ~(uintptr_t)3),
+                                         s + ST_S + wave * 256, 4, 0, 0);
+        if (ASYM) {
+            const uintptr_t za = reinterpret_cast<uintptr_t>(zeros) + zoff + (grp >> 1);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char *>(za & ~(uintptr_t)3),
+                                             s + ST_Z + wave * 256, 4, 0, 0);
+        }
+    };
+    // Dequantize code dword i (0..3) of this thread's row from stage st into dst.
+    auto dequant_word = [&](int k, int st, int i, unsigned char *dst) {
+        if (BN == THREADS || tid < BN) {
+            const unsigned char *s = stg[st];
+            const uint32_t grp = (uint32_t)k / (uint32_t)gsteps;
+            const uint32_t sd = *reinterpret_cast<const uint32_t *>(s + ST_S + tid * 4);
+            const uint32_t sbyte = (uint32_t)(reinterpret_cast<uintptr_t>(scales) + 2u * (soff + grp)) & 3u;
+            const uint32_t sh = (sd >> (8u * sbyte)) & 0xffffu;
+            uint32_t zp = 8u;
+            if (ASYM) {
+                const uint32_t zd = *reinterpret_cast<const uint32_t *>(s + ST_Z + tid * 4);
+                const uint32_t zbyte = (uint32_t)(reinterpret_cast<uintptr_t>(zeros) + zoff + (grp >> 1)) & 3u;
+                zp = (zd >> (8u * zbyte + 4u * (grp & 1u))) & 15u;
+            }
+            const half2v zlo = __builtin_bit_cast(half2v, (0xE400u + zp) * 0x10001u);        // -(1024 + zp)
+            const half2v zhi = __builtin_bit_cast(half2v, (0xD400u + 16u * zp) * 0x10001u);  // -(64 + zp)
+            const half2v s2 = __builtin_bit_cast(half2v, sh * 0x10001u);
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(s + ST_C + tid * 16 + i * 4);
+            *reinterpret_cast<u32x4 *>(dst + tid * 64 + 16 * (i ^ ((tid >> 2) & 3))) =
+                dequant8_scaled(w, zlo, zhi, s2);
+        }
+    };
+
+    floatx16 acc[WM][NU];
+#pragma unroll
+    for (int i = 0; i < WM; i++)
+#pragma unroll
+        for (int j = 0; j < NU; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    const int swz = (l32 >> 2) & 3;
+    auto read_a = [&](const unsigned char *x_st, int s, int i) {
+        const int co = 16 * ((2 * s + h) ^ swz);
+        return __builtin_bit_cast(half8, permute_x(*reinterpret_cast<const u32x4 *>(
+                                             x_st + (wave * 32 * WM + i * 32 + l32) * 64 + co)));
+    };
+    auto read_b = [&](const unsigned char *b_st, int f) {   // f = s * NU + j
+        const int s = f / NU, j = f % NU;
+        const int co = 16 * ((2 * s + h) ^ swz);
+        return *reinterpret_cast<const half8 *>(b_st + (j * 32 + l32) * 64 + co);
+    };
+    // One step: 2 k16 sub-steps x NU column tiles x WM row tiles of MFMAs, B
+    // fragments read two column tiles ahead, and (when dq) the four code
+    // dwords of step k + 1 dequantized in the shadow of the first four column
+    // tiles. The scheduling barriers keep the compiler from hoisting every LDS
+    // read to the top, which would take NU more fragment registers.
+    auto mma_step = [&](int k, int u, bool dq) {
+        constexpr int F = 2 * NU;
+        const unsigned char *x_st = stg[u];
+        const unsigned char *b_st = sb[u & 1];
+        half8 a0[WM], a1[WM];
+#pragma unroll
+        for (int i = 0; i < WM; i++) a0[i] = read_a(x_st, 0, i);
+        half8 bq[3];
+        bq[0] = read_b(b_st, 0);
+        bq[1] = read_b(b_st, 1);
+#pragma unroll
+        for (int f = 0; f < F; f++) {
+            if (f + 2 < F) bq[(f + 2) % 3] = read_b(b_st, f + 2);
+            if (f == NU - 2) {
+#pragma unroll
+                for (int i = 0; i < WM; i++) a1[i] = read_a(x_st, 1, i);
+            }
+            const int j = f % NU;
+            const half8 *a = f < NU ? a0 : a1;
+#pragma unroll
+            for (int i = 0; i < WM; i++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bq[f % 3], acc[i][j], 0, 0, 0);
+            if (f < 4 && dq) dequant_word(k + 1, (u + 1) & 3, f, sb[(u + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Pipeline. Step k: wait until this wavefront's loads of step k + 1 have
+    // landed (only step k + 2's, issued one step ago, may be outstanding) and
+    // its LDS writes are done, then meet at the barrier: after it stage k
+    // and k + 1 and the dequantized W of step k are in LDS, and every
+    // wavefront is done with step k - 1 (its stage and its W buffer). Issue
+    // step k + 3 into step k - 1's stage, then run step k's MFMAs while
+    // dequantizing step k + 1 into step k - 1's W buffer. The loop runs whole
+    // groups of 4 steps (KT is a multiple of 4 since K % 128 == 0); only the
+    // last group checks for steps past the end.
+    auto step = [&](int k, int u, bool last_group) {
+        if (!last_group || k + 2 < KT) Q4_WAIT_VM_LGKM0(NS);
+        else Q4_WAIT_VM_LGKM0(0);
+        __builtin_amdgcn_s_barrier();
+        if (!last_group || k + 3 < KT) issue(k + 3, (u + 3) & 3);
+        mma_step(k, u, !last_group || k + 1 < KT);
+    };
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    Q4_WAIT_VM_LGKM0(NS);   // stages 0 and 1 landed (KT >= 4)
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; i++) dequant_word(0, 0, i, sb[0]);
+    int kt = 0;
+    for (; kt + 4 < KT; kt += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; u++) step(kt + u, u, false);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) step(kt + u, u, true);
+
+#pragma unroll
+    for (int i = 0; i < WM; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int m = m0 + wave * 32 * WM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < NU; j++) {
+                const int n = n0 + j * 32 + l32;
+                if (n < N) Y[(int64_t)m * N + n] = f2h(acc[i][j][r]);
+            }
+        }
+}
+
 template <int MT, int NT, int PF>
 hipError_t launch_skinny(const uint16_t *X, int M, int N, int K, int g, const uint8_t *codes,
                          const uint16_t *scales, const uint8_t *zeros, uint16_t *Y, hipStream_t st)
@@ -521,6 +772,32 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
                 asym ? launch(w4a16_gemv_kernel<16, 2, true>) : launch(w4a16_gemv_kernel<16, 2, false>);
             return hipGetLastError();
         }
+    }
+    if (M >= 256 && g % 128 == 0 && M * K * 2 < ((int64_t)1 << 31) && N * (K / 2) < ((int64_t)1 << 31)) {
+        // Tile width 32 NU: one block per CU, so the time is about the number
+        // of full-chip rounds of 256 tiles times (tile width + a fixed
+        // per-tile cost of ~2 units for pipeline fill and the epilogue).
+        int best = gemm_nu_override();
+        const int tiles_m = (m + GBM - 1) / GBM;
+        if (best == 0) {
+            int64_t best_cost = 0;
+            const int nus[3] = {4, 8, 11};
+            for (int c = 0; c < 3; c++) {
+                const int64_t tiles = (int64_t)tiles_m * ((n + 32 * nus[c] - 1) / (32 * nus[c]));
+                const int64_t cost = (tiles + 255) / 256 * (nus[c] + 2);
+                if (best == 0 || cost < best_cost) { best = nus[c]; best_cost = cost; }
+            }
+        }
+        const int tiles = tiles_m * ((n + 32 * best - 1) / (32 * best));
+        const int gsteps = g / GBK;
+        auto launch = [&](auto kernel, int threads) {
+            kernel<<<tiles, threads, 0, st>>>(X, m, n, k, gsteps, codes, scales, zeros, tiles_m, Y);
+        };
+        const bool asym = zeros != nullptr;
+        if (best == 4) asym ? launch(w4a16_gemm_kernel<4, 2, true>, 256) : launch(w4a16_gemm_kernel<4, 2, false>, 256);
+        else if (best == 8) asym ? launch(w4a16_gemm_kernel<8, 2, true>, 256) : launch(w4a16_gemm_kernel<8, 2, false>, 256);
+        else asym ? launch(w4a16_gemm_kernel<11, 1, true>, 512) : launch(w4a16_gemm_kernel<11, 1, false>, 512);
+        return hipGetLastError();
     }
     if (M <= 16) return launch_skinny<1, 1, 8>(X, m, n, k, g, codes, scales, zeros, Y, st);
     if (M <= 32) return launch_skinny<2, 2, 4>(X, m, n, k, g, codes, scales, zeros, Y, st);

@@ -141,9 +141,6 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_gemm_kernel(
 constexpr int LBM = 256, LBN = 256, LBK = 64, LSTAGES = 4;
 constexpr int LSTAGE_BYTES = (LBM + LBN) * LBK;   // 32 KB
 
-// s_waitcnt with vmcnt = n (lgkmcnt 0, expcnt no wait); gfx9 encoding.
-#define Q4_WAIT_VM_LGKM0(n) \
-    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (0 << 8))
 
 __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,

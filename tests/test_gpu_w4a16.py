@@ -35,7 +35,7 @@ def test_tiny_workload(orc):
 
 SHAPES = [(1, 16, 128), (1, 1000, 1024), (2, 33, 256), (3, 77, 256), (16, 300, 640),
           (17, 129, 384), (33, 64, 256), (64, 130, 512), (65, 129, 384), (128, 128, 128),
-          (200, 260, 1024), (300, 1000, 768)]
+          (200, 260, 1024), (300, 1000, 768), (256, 130, 256), (257, 1, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -59,13 +59,63 @@ def test_one_hot_pins_layout(orc, M, K, N):
     assert np.array_equal(Y.view(np.uint16), expect.view(np.uint16))
 
 
+# The large-M kernel (M >= 256) at each of its tile widths (32 * nu output
+# columns per tile), ragged in M and N, with one 32-wide k step per group
+# quarter: K = 128 is a single group, g = 256 spans two steps' worth of groups.
+LARGE_SHAPES = [(256, 352, 128, 128), (300, 1000, 768, 128), (513, 700, 1280, 128),
+                (260, 383, 1024, 256)]
+
+
+@pytest.mark.parametrize("nu", [4, 8, 11])
+@pytest.mark.parametrize("M,N,K,g", LARGE_SHAPES)
+@pytest.mark.parametrize("sym", [False, True])
+def test_large_m_tile_widths(orc, monkeypatch, nu, M, N, K, g, sym):
+    monkeypatch.setenv("Q4_GEMM_NU", str(nu))
+    W, X = workloads.small_case(M * 3 + N * 5 + K + g + nu, M, N, K)
+    run_case(orc, W, X, g, sym, what=f"large-M nu={nu} M={M} N={N} K={K} g={g} sym={sym}")
+
+
+@pytest.mark.parametrize("nu", [4, 8, 11])
+@pytest.mark.parametrize("sym", [False, True])
+def test_large_m_one_hot(orc, monkeypatch, nu, sym):
+    """X[m, k(m)] = 1 for a spread of k: Y[m, n] = fp16(w_hat[n, k(m)])
+    exactly, which pins the dequantized value of every weight used, its
+    scale and zero-point indexing and the X/W k order, bit for bit."""
+    monkeypatch.setenv("Q4_GEMM_NU", str(nu))
+    M, N, K, g = 300, 385, 512, 256
+    rng = np.random.default_rng(nu * 2 + int(sym))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    codes, scales, zeros = orc.q4_quantize_pack(W, g=g, sym=sym)
+    kk = (np.arange(M) * 7 + 3) % K
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), kk] = 1.0
+    Y = host(q4.w4a16_linear(gpu(X), gpu(codes), gpu(scales.view(np.float16)),
+                             None if zeros is None else gpu(zeros), g=g))
+    w_hat = orc.q4_dequant(codes, scales, zeros, K, g)
+    expect = w_hat[:, kk].T.astype(np.float16)
+    assert np.array_equal(Y.view(np.uint16), expect.view(np.uint16))
+
+
+def test_prefill_shape_asym_sampled(orc):
+    """The prefill shape with asymmetric codes at M = 512 (the tile-width
+    choice differs from M = 2048), checked on sampled rows."""
+    w = workloads.prefill()
+    X = w["X"][:512]
+    q = quantize_gpu(w["W"], 128, False)
+    codes, scales, zeros = (host(t) for t in q)
+    Y = host(q4.w4a16_linear(gpu(X), *q))
+    rows = sample_rows(X.shape[0])
+    Yref, B = orc.w4a16_ref(X, codes, scales, zeros, rows=rows)
+    check_gemm(Y[rows], Yref, B, "prefill shape asym M=512")
+
+
 def test_codes_at_zero_point_give_zero(orc):
-    M, N, K = 70, 50, 512
+    M, N, K = 300, 50, 512
     X = workloads.normal_fp16(5, (M, K))
     codes = np.full((N, K // 2), 0x33, np.uint8)
     zeros = np.full((N, 2), 0x33, np.uint8)
     scales = np.full((N, 4), 0.7, np.float16)
-    for m in (1, 20, M):
+    for m in (1, 20, 70, M):
         Y = host(q4.w4a16_linear(gpu(X[:m]), gpu(codes), gpu(scales), gpu(zeros)))
         assert np.all(Y == 0)
 
