@@ -498,26 +498,25 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_prefill_kernel(
 constexpr int GBM = 256, GBK = 32;
 constexpr int G_X_BYTES = GBM * GBK * 2;            // 16 KB of X per stage
 
-// fp16 (u - zp) * s of the 8 nibbles of one code dword, in the operand k
-// order (0,4,1,5,2,6,3,7). The bit-0 pairs give (1024 + u) - (1024 + zp), the
-// bit-4 pairs (1024 + 16u) / 16 - (64 + zp) in one fma; both are exact.
-__device__ __forceinline__ u32x4 dequant8_scaled(uint32_t w, half2v zlo, half2v zhi, half2v s)
+// fp16 (u - zp) * s of nibbles 2p and 2p + 1 of a code dword, as one fp16
+// pair in natural k order. v_perm_b32 copies byte p of w into bytes 0 and 2;
+// masking puts the low nibble at bit 0 of the low half (fp16 1024 + u0) and
+// the high nibble at bit 4 of the high half (fp16 1024 + 16 u1); one packed
+// fma with multipliers (1, 1/16) and addends (-(1024 + zp), -(64 + zp))
+// leaves (u0 - zp, u1 - zp) exactly, and one packed multiply by s rounds
+// the exact products once.
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int p, uint32_t zadd, uint32_t s2)
 {
-    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
-    const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-    const uint32_t w8 = w >> 8;
-    const half2v d0 = (__builtin_bit_cast(half2v, and_or(w, lo, magic)) + zlo) * s;
-    const half2v d1 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, and_or(w, hi, magic)), sixteenth, zhi) * s;
-    const half2v d2 = (__builtin_bit_cast(half2v, and_or(w8, lo, magic)) + zlo) * s;
-    const half2v d3 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, and_or(w8, hi, magic)), sixteenth, zhi) * s;
-    const u32x4 r = {__builtin_bit_cast(uint32_t, d0), __builtin_bit_cast(uint32_t, d1),
-                     __builtin_bit_cast(uint32_t, d2), __builtin_bit_cast(uint32_t, d3)};
-    return r;
+    const uint32_t t = __builtin_amdgcn_perm(w, w, 0x01010101u * (uint32_t)p);
+    const half2v x = __builtin_bit_cast(half2v, and_or(t, 0x00F0000Fu, 0x64006400u));
+    const half2v mul = __builtin_bit_cast(half2v, 0x2C003C00u);   // (1, 1/16)
+    const half2v v = __builtin_elementwise_fma(x, mul, __builtin_bit_cast(half2v, zadd));
+    return __builtin_bit_cast(uint32_t, v * __builtin_bit_cast(half2v, s2));
 }
 
 template <int NU, int WM, bool ASYM>
 __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
-    const uint16_t *__restrict__ X, int M, int N, int K, int gsteps,
+    const uint16_t *__restrict__ X, int M, int N, int K, int gshift,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint8_t *__restrict__ zeros, int tiles_m, uint16_t *__restrict__ Y)
 {
@@ -525,17 +524,23 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
     constexpr int THREADS = 512 / WM, WAVES = 8 / WM;
     static_assert(BN <= THREADS, "one weight row per thread");
     constexpr int XL = G_X_BYTES / 1024 / WAVES;        // X loads per wavefront per step
-    constexpr int NS = XL + 2 + (ASYM ? 1 : 0);         // loads per wavefront per step
+    constexpr int WQ = (BN + 63) / 64;                  // wavefronts that fetch weight rows
+    constexpr int NS = XL + 2 + (ASYM ? 1 : 0);         // loads per step of such a wavefront
     // stage layout: X | codes (16 B per thread) | scale dwords | zero dwords
-    constexpr int ST_C = G_X_BYTES, ST_S = ST_C + 16 * THREADS, ST_Z = ST_S + 4 * THREADS;
-    constexpr int ST_BYTES = ST_Z + (ASYM ? 4 * THREADS : 0);
+    constexpr int ST_C = G_X_BYTES, ST_S = ST_C + 1024 * WQ, ST_Z = ST_S + 256 * WQ;
+    constexpr int ST_BYTES = ST_Z + (ASYM ? 256 * WQ : 0);
     constexpr int B_BYTES = BN * GBK * 2;
     __shared__ __attribute__((aligned(1024))) unsigned char st0[ST_BYTES];
     __shared__ __attribute__((aligned(1024))) unsigned char st1[ST_BYTES];
     __shared__ __attribute__((aligned(1024))) unsigned char st2[ST_BYTES];
     __shared__ __attribute__((aligned(1024))) unsigned char st3[ST_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char sb1[B_BYTES];
+    // Threads past the tile's rows dequantize a copy of the last row (their
+    // stage slots hold its data) into a spare 16-byte slot of their own after
+    // the tile in the same buffer: no branch in the loop, and every LDS store
+    // provably misses the stages, so the compiler's waits stay exact.
+    constexpr int B_SPARE = B_BYTES + (THREADS > BN ? THREADS - BN : 0) * 16;
+    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_SPARE];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb1[B_SPARE];
     unsigned char *const stg[4] = {st0, st1, st2, st3};
     unsigned char *const sb[2] = {sb0, sb1};
 
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
     const int t = (blocks % 8 == 0) ? (b % 8) * (blocks / 8) + b / 8 : b;
     const int m0 = (t % tiles_m) * GBM, n0 = (t / tiles_m) * BN;
     const int KT = K / GBK;
-    const uint32_t G = (uint32_t)(KT / gsteps), Gz = (G + 1) >> 1;
+    const uint32_t G = (uint32_t)KT >> gshift, Gz = (G + 1) >> 1;   // g = 32 << gshift
 
     // X loads: 1 KB blocks of 16 rows; wavefront w fills blocks XL w ..
     // XL w + XL - 1. Lane i of block q lands on row 16 q + i / 4, stored chunk
@@ -562,9 +567,14 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
         m = m < M ? m : M - 1;
         xoff[j] = (uint32_t)m * (uint32_t)K * 2u + 16u * (uint32_t)dchunk;
     }
-    // Weight loads: thread t fetches row t of the tile (rows past the tile or
-    // past N refetch a valid row; they are never stored).
-    int wrow = tid < BN ? tid : BN - 1;
+    // Weight loads: wavefront w < WQ fetches rows 64 w .. 64 w + 63 of the tile
+    // into slots 64 w ..; the wavefronts past WQ repeat exactly the loads of
+    // wavefront WQ - 1 (same rows, same slots, same bytes), so every
+    // wavefront issues the same loads and the stage holds only WQ slots.
+    // Rows past the tile or past N refetch a valid row and are never stored.
+    const int wq = wave < WQ ? wave : WQ - 1;
+    const int slot = 64 * wq + lane;
+    int wrow = slot < BN ? slot : BN - 1;
     const uint32_t n_w = (uint32_t)(n0 + wrow < N ? n0 + wrow : N - 1);
     const uint32_t coff = n_w * (uint32_t)(K >> 1);
     const uint32_t soff = n_w * G;    // in halves
@@ -572,47 +582,26 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
 
     auto issue = [&](int k, int st) {   // st = k % 4, a compile-time constant
         unsigned char *s = stg[st];
-        const uint32_t grp = (uint32_t)k / (uint32_t)gsteps;
+        const uint32_t grp = (uint32_t)k >> gshift;
 #pragma unroll
         for (int j = 0; j < XL; j++)
             __builtin_amdgcn_global_load_lds(Xb + xoff[j] + (uint32_t)k * (GBK * 2),
                                              s + (XL * wave + j) * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(codes + coff + (uint32_t)k * 16u, s + ST_C + wave * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(codes + coff + (uint32_t)k * 16u, s + ST_C + wq * 1024, 16, 0, 0);
         // the aligned dword that holds the scale (and the one that holds the
         // zero-point byte); an aligned dword holding a valid byte never
         // crosses into an unmapped page
         const uintptr_t sa_ = reinterpret_cast<uintptr_t>(scales) + 2u * (soff + grp);
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char *>(sa_ & ~(uintptr_t)3),
-                                         s + ST_S + wave * 256, 4, 0, 0);
+                                         s + ST_S + wq * 256, 4, 0, 0);
         if (ASYM) {
             const uintptr_t za = reinterpret_cast<uintptr_t>(zeros) + zoff + (grp >> 1);
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char *>(za & ~(uintptr_t)3),
-                                             s + ST_Z + wave * 256, 4, 0, 0);
+                                             s + ST_Z + wq * 256, 4, 0, 0);
         }
     };
-    // Dequantize code dword i (0..3) of this thread's row from stage st into dst.
-    auto dequant_word = [&](int k, int st, int i, unsigned char *dst) {
-        if (BN == THREADS || tid < BN) {
-            const unsigned char *s = stg[st];
-            const uint32_t grp = (uint32_t)k / (uint32_t)gsteps;
-            const uint32_t sd = *reinterpret_cast<const uint32_t *>(s + ST_S + tid * 4);
-            const uint32_t sbyte = (uint32_t)(reinterpret_cast<uintptr_t>(scales) + 2u * (soff + grp)) & 3u;
-            const uint32_t sh = (sd >> (8u * sbyte)) & 0xffffu;
-            uint32_t zp = 8u;
-            if (ASYM) {
-                const uint32_t zd = *reinterpret_cast<const uint32_t *>(s + ST_Z + tid * 4);
-                const uint32_t zbyte = (uint32_t)(reinterpret_cast<uintptr_t>(zeros) + zoff + (grp >> 1)) & 3u;
-                zp = (zd >> (8u * zbyte + 4u * (grp & 1u))) & 15u;
-            }
-            const half2v zlo = __builtin_bit_cast(half2v, (0xE400u + zp) * 0x10001u);        // -(1024 + zp)
-            const half2v zhi = __builtin_bit_cast(half2v, (0xD400u + 16u * zp) * 0x10001u);  // -(64 + zp)
-            const half2v s2 = __builtin_bit_cast(half2v, sh * 0x10001u);
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(s + ST_C + tid * 16 + i * 4);
-            *reinterpret_cast<u32x4 *>(dst + tid * 64 + 16 * (i ^ ((tid >> 2) & 3))) =
-                dequant8_scaled(w, zlo, zhi, s2);
-        }
-    };
-
+    // wait until at most one step of this wavefront's loads is in flight
+    auto wait_one_step = [&]() { Q4_WAIT_VM_LGKM0(NS); };
     floatx16 acc[WM][NU];
 #pragma unroll
     for (int i = 0; i < WM; i++)
@@ -624,8 +613,7 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
     const int swz = (l32 >> 2) & 3;
     auto read_a = [&](const unsigned char *x_st, int s, int i) {
         const int co = 16 * ((2 * s + h) ^ swz);
-        return __builtin_bit_cast(half8, permute_x(*reinterpret_cast<const u32x4 *>(
-                                             x_st + (wave * 32 * WM + i * 32 + l32) * 64 + co)));
+        return *reinterpret_cast<const half8 *>(x_st + (wave * 32 * WM + i * 32 + l32) * 64 + co);
     };
     auto read_b = [&](const unsigned char *b_st, int f) {   // f = s * NU + j
         const int s = f / NU, j = f % NU;
@@ -633,67 +621,127 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
         return *reinterpret_cast<const half8 *>(b_st + (j * 32 + l32) * 64 + co);
     };
     // One step: 2 k16 sub-steps x NU column tiles x WM row tiles of MFMAs, B
-    // fragments read two column tiles ahead, and (when dq) the four code
-    // dwords of step k + 1 dequantized in the shadow of the first four column
-    // tiles. The scheduling barriers keep the compiler from hoisting every LDS
-    // read to the top, which would take NU more fragment registers.
-    auto mma_step = [&](int k, int u, bool dq) {
+    // fragments read two column tiles ahead. This thread's weight row of step
+    // k + 1 (16 code bytes, its scale and zero-point dwords) is
+    // read from its stage first and dequantized one fp16 pair at a time in
+    // the shadow of the MFMAs, 16 bytes written to LDS per 4 pairs. The
+    // scheduling barriers keep the compiler from hoisting every LDS read to
+    // the top (which would take NU more fragment registers).
+    // This thread's weight row of step k from stage st: its 16 code bytes, the
+    // fp16 scale pair (s, s) and the fma addends (-(1024 + zp), -(64 + zp)).
+    auto row_inputs = [&](int k, int st, u32x4 &cw, uint32_t &s2, uint32_t &zadd) {
+        const unsigned char *w_st = stg[st];
+        const uint32_t grp = (uint32_t)k >> gshift;
+        cw = *reinterpret_cast<const u32x4 *>(w_st + ST_C + slot * 16);
+        const uint32_t sd = *reinterpret_cast<const uint32_t *>(w_st + ST_S + slot * 4);
+        const uint32_t sbyte = (uint32_t)(reinterpret_cast<uintptr_t>(scales) + 2u * (soff + grp)) & 3u;
+        s2 = ((sd >> (8u * sbyte)) & 0xffffu) * 0x10001u;
+        uint32_t zp = 8u;
+        if (ASYM) {
+            const uint32_t zd = *reinterpret_cast<const uint32_t *>(w_st + ST_Z + slot * 4);
+            const uint32_t zbyte = (uint32_t)(reinterpret_cast<uintptr_t>(zeros) + zoff + (grp >> 1)) & 3u;
+            zp = (zd >> (8u * zbyte + 4u * (grp & 1u))) & 15u;
+        }
+        zadd = (0xE400u + zp) | ((0xD400u + 16u * zp) << 16);
+    };
+    auto mma_step = [&](int k, int u, int k_issue) {
         constexpr int F = 2 * NU;
+        constexpr int PPF = (16 + F - 1) / F;   // dequant pairs per column tile
         const unsigned char *x_st = stg[u];
         const unsigned char *b_st = sb[u & 1];
+        unsigned char *const dq_dst = sb[(u + 1) & 1];
+        u32x4 cw = {0u, 0u, 0u, 0u};
+        uint32_t s2 = 0, zadd = 0;
+        row_inputs(k + 1, (u + 1) & 3, cw, s2, zadd);
+        int dq_off = tid * 64, dq_swz = (tid >> 2) & 3, dq_cs = 16;
+        if (BN < THREADS && tid >= BN) {   // all four chunks into the thread's one spare slot
+            dq_off = B_BYTES + (tid - BN) * 16;
+            dq_swz = 0;
+            dq_cs = 0;
+        }
+        unsigned char *const dq_row = dq_dst + dq_off;
         half8 a0[WM], a1[WM];
 #pragma unroll
-        for (int i = 0; i < WM; i++) a0[i] = read_a(x_st, 0, i);
+        for (int i = 0; i < WM; i++) {
+            a0[i] = read_a(x_st, 0, i);
+            a1[i] = read_a(x_st, 1, i);
+        }
+        // Only now refill step k - 1's stage: with the stage reads above kept
+        // first, the compiler sees no read that could race the new loads
+        // (and inserts no wait for them).
+        __builtin_amdgcn_sched_barrier(0);
+        issue(k_issue, (u + 3) & 3);
+        __builtin_amdgcn_sched_barrier(0);
         half8 bq[3];
         bq[0] = read_b(b_st, 0);
         bq[1] = read_b(b_st, 1);
+        u32x4 out = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int f = 0; f < F; f++) {
             if (f + 2 < F) bq[(f + 2) % 3] = read_b(b_st, f + 2);
-            if (f == NU - 2) {
-#pragma unroll
-                for (int i = 0; i < WM; i++) a1[i] = read_a(x_st, 1, i);
-            }
             const int j = f % NU;
             const half8 *a = f < NU ? a0 : a1;
 #pragma unroll
             for (int i = 0; i < WM; i++)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bq[f % 3], acc[i][j], 0, 0, 0);
-            if (f < 4 && dq) dequant_word(k + 1, (u + 1) & 3, f, sb[(u + 1) & 1]);
+            {
+#pragma unroll
+                for (int q = 0; q < PPF; q++) {
+                    const int pr = f * PPF + q;   // pair pr: nibbles 2 (pr % 4), +1 of code dword pr / 4
+                    if (pr < 16) {
+                        out[pr & 3] = dequant_pair(cw[pr >> 2], pr & 3, zadd, s2);
+                        if ((pr & 3) == 3)
+                            *reinterpret_cast<u32x4 *>(dq_row + dq_cs * ((pr >> 2) ^ dq_swz)) = out;
+                    }
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     // Pipeline. Step k: wait until this wavefront's loads of step k + 1 have
     // landed (only step k + 2's, issued one step ago, may be outstanding) and
-    // its LDS writes are done, then meet at the barrier: after it stage k
+    // its LDS writes are done, then meet at the barrier: after it stages k
     // and k + 1 and the dequantized W of step k are in LDS, and every
     // wavefront is done with step k - 1 (its stage and its W buffer). Issue
     // step k + 3 into step k - 1's stage, then run step k's MFMAs while
-    // dequantizing step k + 1 into step k - 1's W buffer. The loop runs whole
-    // groups of 4 steps (KT is a multiple of 4 since K % 128 == 0); only the
-    // last group checks for steps past the end.
-    auto step = [&](int k, int u, bool last_group) {
-        if (!last_group || k + 2 < KT) Q4_WAIT_VM_LGKM0(NS);
-        else Q4_WAIT_VM_LGKM0(0);
-        __builtin_amdgcn_s_barrier();
-        if (!last_group || k + 3 < KT) issue(k + 3, (u + 3) & 3);
-        mma_step(k, u, !last_group || k + 1 < KT);
-    };
+    // dequantizing step k + 1 into step k - 1's W buffer. Every step has the
+    // same shape: past the end the loads refetch the last step and the
+    // dequantized tile is never read, so there are no branches in the loop
+    // (KT is a multiple of 4 since K % 128 == 0).
     issue(0, 0);
     issue(1, 1);
     issue(2, 2);
-    Q4_WAIT_VM_LGKM0(NS);   // stages 0 and 1 landed (KT >= 4)
+    wait_one_step();   // stages 0 and 1 landed (KT >= 4)
     __builtin_amdgcn_s_barrier();
+    {
+        u32x4 cw;
+        uint32_t s2, zadd;
+        row_inputs(0, 0, cw, s2, zadd);
+        int off0 = tid * 64, swz0 = (tid >> 2) & 3, cs0 = 16;
+        if (BN < THREADS && tid >= BN) {
+            off0 = B_BYTES + (tid - BN) * 16;
+            swz0 = 0;
+            cs0 = 0;
+        }
+        unsigned char *const row = sb[0] + off0;
 #pragma unroll
-    for (int i = 0; i < 4; i++) dequant_word(0, 0, i, sb[0]);
-    int kt = 0;
-    for (; kt + 4 < KT; kt += 4) {
-#pragma unroll
-        for (int u = 0; u < 4; u++) step(kt + u, u, false);
+        for (int i = 0; i < 4; i++) {
+            const u32x4 out = {dequant_pair(cw[i], 0, zadd, s2), dequant_pair(cw[i], 1, zadd, s2),
+                               dequant_pair(cw[i], 2, zadd, s2), dequant_pair(cw[i], 3, zadd, s2)};
+            *reinterpret_cast<u32x4 *>(row + cs0 * (i ^ swz0)) = out;
+        }
     }
+    for (int kt = 0; kt < KT; kt += 4) {
 #pragma unroll
-    for (int u = 0; u < 4; u++) step(kt + u, u, true);
+        for (int u = 0; u < 4; u++) {
+            const int k = kt + u;
+            wait_one_step();
+            __builtin_amdgcn_s_barrier();
+            mma_step(k, u, k + 3 < KT ? k + 3 : KT - 1);
+        }
+    }
+    Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
 
 #pragma unroll
     for (int i = 0; i < WM; i++)
@@ -773,7 +821,8 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
             return hipGetLastError();
         }
     }
-    if (M >= 256 && g % 128 == 0 && M * K * 2 < ((int64_t)1 << 31) && N * (K / 2) < ((int64_t)1 << 31)) {
+    if (M >= 256 && g % 128 == 0 && (g & (g - 1)) == 0 && M * K * 2 < ((int64_t)1 << 31) &&
+        N * (K / 2) < ((int64_t)1 << 31)) {
         // Tile width 32 NU: one block per CU, so the time is about the number
         // of full-chip rounds of 256 tiles times (tile width + a fixed
         // per-tile cost of ~2 units for pipeline fill and the epilogue).
@@ -789,9 +838,9 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
             }
         }
         const int tiles = tiles_m * ((n + 32 * best - 1) / (32 * best));
-        const int gsteps = g / GBK;
+        const int gshift = __builtin_ctz((unsigned)(g / GBK));
         auto launch = [&](auto kernel, int threads) {
-            kernel<<<tiles, threads, 0, st>>>(X, m, n, k, gsteps, codes, scales, zeros, tiles_m, Y);
+            kernel<<<tiles, threads, 0, st>>>(X, m, n, k, gshift, codes, scales, zeros, tiles_m, Y);
         };
         const bool asym = zeros != nullptr;
         if (best == 4) asym ? launch(w4a16_gemm_kernel<4, 2, true>, 256) : launch(w4a16_gemm_kernel<4, 2, false>, 256);
