@@ -468,35 +468,34 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large-M GEMM (prefill), M >= 256, g a multiple of 128. Compute bound.
+// Large-M GEMM (prefill), M >= 256, g a power of two >= 128. Compute bound.
 //
 // A block of 8 / WM wavefronts owns a 256 x (32 NU) tile of Y; wavefront w
 // owns rows 32 WM w .. 32 WM (w + 1) - 1 of it across all 32 NU columns
 // (WM x NU accumulators of v_mfma_f32_32x32x16_f16). K advances 32 at a time.
-// Every global read is a direct-to-LDS load (global_load_lds), issued three
-// steps ahead into one of four stages; a stage holds
-//   - X: 256 rows x 32 fp16 (16 KB, 64-byte rows);
-//   - the 16-byte code run (32 nibbles) of each of the tile's weight rows;
-//   - the dword holding each row's group scale, and (asymmetric) the dword
-//     holding its zero-point nibble.
-// One step ahead of the MFMAs, thread t dequantizes weight row t of the next
-// step from its stage into one of two LDS buffers as fp16 (u - zp) * s, one
-// code dword in the shadow of each column tile's MFMAs. LDS rows of X and of
-// the dequantized W are 64 bytes (4 chunks of 8 k); chunk c of row r is
-// stored at c ^ ((r >> 2) & 3), which keeps the 16-byte operand reads
-// conflict-free. Waits are explicit vmcnt counts (every wavefront issues the
-// same loads each step), so the loads of later steps stay in flight across
-// the per-step barrier.
+//   - X never touches LDS: a wavefront's rows are its own, so each lane loads
+//     its two 16-byte A fragments of a step straight into registers, two
+//     steps ahead.
+//   - Thread t owns weight row t of the tile: its 16-byte code run (32
+//     nibbles), group scale and zero-point byte come into a four-deep
+//     register ring three steps ahead. While the MFMAs of step k run, the
+//     thread dequantizes step k + 1's row into one of two LDS buffers as fp16
+//     (u - zp) * s, one fp16 pair in the shadow of each column tile.
+//   - One barrier per step: after it the dequantized tile of step k is
+//     complete and every wavefront is done with the buffer it overwrites.
+// LDS rows of the dequantized tile are 64 bytes (4 chunks of 8 k); chunk c
+// of row r is stored at c ^ ((r >> 2) & 3), which keeps the 16-byte operand
+// reads conflict-free. Every step has the same shape (past the end the last
+// step is reloaded), so the loop has no branches and the compiler's waits
+// for the register loads stay partial.
 //
 // Arithmetic. Unlike the decode kernels, the scale is folded into the
 // operand: each dequantized weight is f2h((u - zp) * s) with one rounding
 // ((u - zp) is exact in fp16 and v_pk_mul_f16 rounds the exact product), so
 // one fp32 accumulator serves all groups. The weights' rounding (relative
 // <= 2^-11 each) and the fp16 output rounding stay inside the
-// 2^-10 * sum |x||w_hat| bound; the X operand is permuted to the dequant's
-// k order (0,4,1,5,2,6,3,7) in registers after its LDS read.
+// 2^-10 * sum |x||w_hat| bound.
 constexpr int GBM = 256, GBK = 32;
-constexpr int G_X_BYTES = GBM * GBK * 2;            // 16 KB of X per stage
 
 // fp16 (u - zp) * s of nibbles 2p and 2p + 1 of a code dword, as one fp16
 // pair in natural k order. v_perm_b32 copies byte p of w into bytes 0 and 2;
@@ -521,87 +520,53 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
     const uint8_t *__restrict__ zeros, int tiles_m, uint16_t *__restrict__ Y)
 {
     constexpr int BN = 32 * NU;
-    constexpr int THREADS = 512 / WM, WAVES = 8 / WM;
+    constexpr int THREADS = 512 / WM;
     static_assert(BN <= THREADS, "one weight row per thread");
-    constexpr int XL = G_X_BYTES / 1024 / WAVES;        // X loads per wavefront per step
-    constexpr int WQ = (BN + 63) / 64;                  // wavefronts that fetch weight rows
-    constexpr int NS = XL + 2 + (ASYM ? 1 : 0);         // loads per step of such a wavefront
-    // stage layout: X | codes (16 B per thread) | scale dwords | zero dwords
-    constexpr int ST_C = G_X_BYTES, ST_S = ST_C + 1024 * WQ, ST_Z = ST_S + 256 * WQ;
-    constexpr int ST_BYTES = ST_Z + (ASYM ? 256 * WQ : 0);
     constexpr int B_BYTES = BN * GBK * 2;
-    __shared__ __attribute__((aligned(1024))) unsigned char st0[ST_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char st1[ST_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char st2[ST_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char st3[ST_BYTES];
-    // Threads past the tile's rows dequantize a copy of the last row (their
-    // stage slots hold its data) into a spare 16-byte slot of their own after
-    // the tile in the same buffer: no branch in the loop, and every LDS store
-    // provably misses the stages, so the compiler's waits stay exact.
     constexpr int B_SPARE = B_BYTES + (THREADS > BN ? THREADS - BN : 0) * 16;
     __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_SPARE];
     __shared__ __attribute__((aligned(1024))) unsigned char sb1[B_SPARE];
-    unsigned char *const stg[4] = {st0, st1, st2, st3};
     unsigned char *const sb[2] = {sb0, sb1};
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
     const int blocks = gridDim.x, b = blockIdx.x;
-    // consecutive tiles go to one XCD (blocks are dealt to the 8 XCDs round robin)
     const int t = (blocks % 8 == 0) ? (b % 8) * (blocks / 8) + b / 8 : b;
     const int m0 = (t % tiles_m) * GBM, n0 = (t / tiles_m) * BN;
     const int KT = K / GBK;
-    const uint32_t G = (uint32_t)KT >> gshift, Gz = (G + 1) >> 1;   // g = 32 << gshift
+    const uint32_t G = (uint32_t)KT >> gshift, Gz = (G + 1) >> 1;
 
-    // X loads: 1 KB blocks of 16 rows; wavefront w fills blocks XL w ..
-    // XL w + XL - 1. Lane i of block q lands on row 16 q + i / 4, stored chunk
-    // i % 4, and so fetches logical chunk (i % 4) ^ ((i >> 4) & 3).
-    const unsigned char *Xb = reinterpret_cast<const unsigned char *>(X);
-    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
-    static_assert(XL <= 4, "X loads per wavefront");
-    uint32_t xoff[4];   // fixed size: with a template-dependent size captured by the lambdas
-                        // below, the host pass silently dropped the kernel launch stub
+    // this lane's X rows (one per 32-row tile) at k offset 8 h
+    uint32_t xoff[WM];
 #pragma unroll
-    for (int j = 0; j < XL; j++) {
-        int m = m0 + (XL * wave + j) * 16 + (lane >> 2);
+    for (int i = 0; i < WM; i++) {
+        int m = m0 + wave * 32 * WM + i * 32 + l32;
         m = m < M ? m : M - 1;
-        xoff[j] = (uint32_t)m * (uint32_t)K * 2u + 16u * (uint32_t)dchunk;
+        xoff[i] = ((uint32_t)m * (uint32_t)K + 8u * (uint32_t)h) * 2u;
     }
-    // Weight loads: wavefront w < WQ fetches rows 64 w .. 64 w + 63 of the tile
-    // into slots 64 w ..; the wavefronts past WQ repeat exactly the loads of
-    // wavefront WQ - 1 (same rows, same slots, same bytes), so every
-    // wavefront issues the same loads and the stage holds only WQ slots.
-    // Rows past the tile or past N refetch a valid row and are never stored.
-    const int wq = wave < WQ ? wave : WQ - 1;
-    const int slot = 64 * wq + lane;
-    int wrow = slot < BN ? slot : BN - 1;
+    const unsigned char *Xb = reinterpret_cast<const unsigned char *>(X);
+    // this thread's weight row (threads past the tile repeat the last row)
+    const int wrow = tid < BN ? tid : BN - 1;
     const uint32_t n_w = (uint32_t)(n0 + wrow < N ? n0 + wrow : N - 1);
-    const uint32_t coff = n_w * (uint32_t)(K >> 1);
-    const uint32_t soff = n_w * G;    // in halves
-    const uint32_t zoff = n_w * Gz;   // in bytes
+    const uint32_t coff = n_w * (uint32_t)(K >> 1), soff = n_w * G, zoff = n_w * Gz;
 
-    auto issue = [&](int k, int st) {   // st = k % 4, a compile-time constant
-        unsigned char *s = stg[st];
-        const uint32_t grp = (uint32_t)k >> gshift;
+    u32x4 xa[2][WM][2];   // X fragments, ring of 2 steps
+    u32x4 wc[4];          // code runs, ring of 4 steps
+    uint32_t ws[4], wz[4];
+    auto load_x = [&](int k, int q) {
 #pragma unroll
-        for (int j = 0; j < XL; j++)
-            __builtin_amdgcn_global_load_lds(Xb + xoff[j] + (uint32_t)k * (GBK * 2),
-                                             s + (XL * wave + j) * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(codes + coff + (uint32_t)k * 16u, s + ST_C + wq * 1024, 16, 0, 0);
-        // the aligned dword that holds the scale (and the one that holds the
-        // zero-point byte); an aligned dword holding a valid byte never
-        // crosses into an unmapped page
-        const uintptr_t sa_ = reinterpret_cast<uintptr_t>(scales) + 2u * (soff + grp);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char *>(sa_ & ~(uintptr_t)3),
-                                         s + ST_S + wq * 256, 4, 0, 0);
-        if (ASYM) {
-            const uintptr_t za = reinterpret_cast<uintptr_t>(zeros) + zoff + (grp >> 1);
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char *>(za & ~(uintptr_t)3),
-                                             s + ST_Z + wq * 256, 4, 0, 0);
-        }
+        for (int i = 0; i < WM; i++)
+#pragma unroll
+            for (int s = 0; s < 2; s++)
+                xa[q][i][s] = *reinterpret_cast<const u32x4 *>(Xb + xoff[i] + (uint32_t)k * 64u + 32u * s);
     };
-    // wait until at most one step of this wavefront's loads is in flight
-    auto wait_one_step = [&]() { Q4_WAIT_VM_LGKM0(NS); };
+    auto load_w = [&](int k, int q) {
+        const uint32_t grp = (uint32_t)k >> gshift;
+        wc[q] = *reinterpret_cast<const u32x4 *>(codes + coff + (uint32_t)k * 16u);
+        ws[q] = scales[soff + grp];
+        if (ASYM) wz[q] = zeros[zoff + (grp >> 1)];   // nibble picked at use: no wait here
+    };
+
     floatx16 acc[WM][NU];
 #pragma unroll
     for (int i = 0; i < WM; i++)
@@ -611,67 +576,32 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
     const int swz = (l32 >> 2) & 3;
-    auto read_a = [&](const unsigned char *x_st, int s, int i) {
-        const int co = 16 * ((2 * s + h) ^ swz);
-        return *reinterpret_cast<const half8 *>(x_st + (wave * 32 * WM + i * 32 + l32) * 64 + co);
-    };
     auto read_b = [&](const unsigned char *b_st, int f) {   // f = s * NU + j
         const int s = f / NU, j = f % NU;
         const int co = 16 * ((2 * s + h) ^ swz);
         return *reinterpret_cast<const half8 *>(b_st + (j * 32 + l32) * 64 + co);
     };
-    // One step: 2 k16 sub-steps x NU column tiles x WM row tiles of MFMAs, B
-    // fragments read two column tiles ahead. This thread's weight row of step
-    // k + 1 (16 code bytes, its scale and zero-point dwords) is
-    // read from its stage first and dequantized one fp16 pair at a time in
-    // the shadow of the MFMAs, 16 bytes written to LDS per 4 pairs. The
-    // scheduling barriers keep the compiler from hoisting every LDS read to
-    // the top (which would take NU more fragment registers).
-    // This thread's weight row of step k from stage st: its 16 code bytes, the
-    // fp16 scale pair (s, s) and the fma addends (-(1024 + zp), -(64 + zp)).
-    auto row_inputs = [&](int k, int st, u32x4 &cw, uint32_t &s2, uint32_t &zadd) {
-        const unsigned char *w_st = stg[st];
-        const uint32_t grp = (uint32_t)k >> gshift;
-        cw = *reinterpret_cast<const u32x4 *>(w_st + ST_C + slot * 16);
-        const uint32_t sd = *reinterpret_cast<const uint32_t *>(w_st + ST_S + slot * 4);
-        const uint32_t sbyte = (uint32_t)(reinterpret_cast<uintptr_t>(scales) + 2u * (soff + grp)) & 3u;
-        s2 = ((sd >> (8u * sbyte)) & 0xffffu) * 0x10001u;
-        uint32_t zp = 8u;
-        if (ASYM) {
-            const uint32_t zd = *reinterpret_cast<const uint32_t *>(w_st + ST_Z + slot * 4);
-            const uint32_t zbyte = (uint32_t)(reinterpret_cast<uintptr_t>(zeros) + zoff + (grp >> 1)) & 3u;
-            zp = (zd >> (8u * zbyte + 4u * (grp & 1u))) & 15u;
-        }
-        zadd = (0xE400u + zp) | ((0xD400u + 16u * zp) << 16);
+    int dq_off = tid * 64, dq_swz = (tid >> 2) & 3, dq_cs = 16;
+    if (BN < THREADS && tid >= BN) {   // all four chunks into the thread's one spare slot
+        dq_off = B_BYTES + (tid - BN) * 16;
+        dq_swz = 0;
+        dq_cs = 0;
+    }
+    auto wconst = [&](int k, int q, uint32_t &s2, uint32_t &zadd) {
+        s2 = (ws[q] & 0xffffu) * 0x10001u;
+        const uint32_t zp = ASYM ? (wz[q] >> (4u * (((uint32_t)k >> gshift) & 1u))) & 15u : 8u;
+        zadd = (0xE400u + zp) | ((0xD400u + 16u * zp) << 16);   // (-(1024 + zp), -(64 + zp))
     };
-    auto mma_step = [&](int k, int u, int k_issue) {
+    // step k from X slot xq and W buffer u & 1; dequantize W slot (u + 1) & 3
+    // (step k + 1) into the other buffer, one pair per column tile
+    auto mma_step = [&](int k, int u, int xq) {
         constexpr int F = 2 * NU;
-        constexpr int PPF = (16 + F - 1) / F;   // dequant pairs per column tile
-        const unsigned char *x_st = stg[u];
+        constexpr int PPF = (16 + F - 1) / F;
         const unsigned char *b_st = sb[u & 1];
-        unsigned char *const dq_dst = sb[(u + 1) & 1];
-        u32x4 cw = {0u, 0u, 0u, 0u};
-        uint32_t s2 = 0, zadd = 0;
-        row_inputs(k + 1, (u + 1) & 3, cw, s2, zadd);
-        int dq_off = tid * 64, dq_swz = (tid >> 2) & 3, dq_cs = 16;
-        if (BN < THREADS && tid >= BN) {   // all four chunks into the thread's one spare slot
-            dq_off = B_BYTES + (tid - BN) * 16;
-            dq_swz = 0;
-            dq_cs = 0;
-        }
-        unsigned char *const dq_row = dq_dst + dq_off;
-        half8 a0[WM], a1[WM];
-#pragma unroll
-        for (int i = 0; i < WM; i++) {
-            a0[i] = read_a(x_st, 0, i);
-            a1[i] = read_a(x_st, 1, i);
-        }
-        // Only now refill step k - 1's stage: with the stage reads above kept
-        // first, the compiler sees no read that could race the new loads
-        // (and inserts no wait for them).
-        __builtin_amdgcn_sched_barrier(0);
-        issue(k_issue, (u + 3) & 3);
-        __builtin_amdgcn_sched_barrier(0);
+        unsigned char *const dq_row = sb[(u + 1) & 1] + dq_off;
+        const int wq = (u + 1) & 3;
+        uint32_t s2, zadd;
+        wconst(k + 1, wq, s2, zadd);
         half8 bq[3];
         bq[0] = read_b(b_st, 0);
         bq[1] = read_b(b_st, 1);
@@ -679,69 +609,61 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
 #pragma unroll
         for (int f = 0; f < F; f++) {
             if (f + 2 < F) bq[(f + 2) % 3] = read_b(b_st, f + 2);
-            const int j = f % NU;
-            const half8 *a = f < NU ? a0 : a1;
+            const int j = f % NU, s = f / NU;
 #pragma unroll
             for (int i = 0; i < WM; i++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bq[f % 3], acc[i][j], 0, 0, 0);
-            {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, xa[xq][i][s]),
+                                                                   bq[f % 3], acc[i][j], 0, 0, 0);
 #pragma unroll
-                for (int q = 0; q < PPF; q++) {
-                    const int pr = f * PPF + q;   // pair pr: nibbles 2 (pr % 4), +1 of code dword pr / 4
-                    if (pr < 16) {
-                        out[pr & 3] = dequant_pair(cw[pr >> 2], pr & 3, zadd, s2);
-                        if ((pr & 3) == 3)
-                            *reinterpret_cast<u32x4 *>(dq_row + dq_cs * ((pr >> 2) ^ dq_swz)) = out;
-                    }
+            for (int q = 0; q < PPF; q++) {
+                const int pr = f * PPF + q;
+                if (pr < 16) {
+                    out[pr & 3] = dequant_pair(wc[wq][pr >> 2], pr & 3, zadd, s2);
+                    if ((pr & 3) == 3)
+                        *reinterpret_cast<u32x4 *>(dq_row + dq_cs * ((pr >> 2) ^ dq_swz)) = out;
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    auto barrier = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt not waited
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
 
-    // Pipeline. Step k: wait until this wavefront's loads of step k + 1 have
-    // landed (only step k + 2's, issued one step ago, may be outstanding) and
-    // its LDS writes are done, then meet at the barrier: after it stages k
-    // and k + 1 and the dequantized W of step k are in LDS, and every
-    // wavefront is done with step k - 1 (its stage and its W buffer). Issue
-    // step k + 3 into step k - 1's stage, then run step k's MFMAs while
-    // dequantizing step k + 1 into step k - 1's W buffer. Every step has the
-    // same shape: past the end the loads refetch the last step and the
-    // dequantized tile is never read, so there are no branches in the loop
-    // (KT is a multiple of 4 since K % 128 == 0).
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    wait_one_step();   // stages 0 and 1 landed (KT >= 4)
-    __builtin_amdgcn_s_barrier();
+    // prologue: X of steps 0, 1; W of steps 0, 1, 2; W of step 0 dequantized
+    load_x(0, 0);
+    load_w(0, 0);
+    load_x(1, 1);
+    load_w(1, 1);
+    load_w(2 < KT ? 2 : KT - 1, 2);
     {
-        u32x4 cw;
         uint32_t s2, zadd;
-        row_inputs(0, 0, cw, s2, zadd);
-        int off0 = tid * 64, swz0 = (tid >> 2) & 3, cs0 = 16;
-        if (BN < THREADS && tid >= BN) {
-            off0 = B_BYTES + (tid - BN) * 16;
-            swz0 = 0;
-            cs0 = 0;
-        }
-        unsigned char *const row = sb[0] + off0;
+        wconst(0, 0, s2, zadd);
+        unsigned char *const row = sb[0] + dq_off;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const u32x4 out = {dequant_pair(cw[i], 0, zadd, s2), dequant_pair(cw[i], 1, zadd, s2),
-                               dequant_pair(cw[i], 2, zadd, s2), dequant_pair(cw[i], 3, zadd, s2)};
-            *reinterpret_cast<u32x4 *>(row + cs0 * (i ^ swz0)) = out;
+            const u32x4 out = {dequant_pair(wc[0][i], 0, zadd, s2), dequant_pair(wc[0][i], 1, zadd, s2),
+                               dequant_pair(wc[0][i], 2, zadd, s2), dequant_pair(wc[0][i], 3, zadd, s2)};
+            *reinterpret_cast<u32x4 *>(row + dq_cs * (i ^ dq_swz)) = out;
         }
     }
+    // Step k (u = k % 4): barrier (W of step k is in its buffer, every
+    // wavefront is done with step k - 1); the weights of step k + 3 go to W
+    // slot (k + 3) % 4, free since step k - 1's dequant; X of step k + 2 goes
+    // to X slot k % 2 once this step's MFMAs have been issued.
     for (int kt = 0; kt < KT; kt += 4) {
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const int k = kt + u;
-            wait_one_step();
-            __builtin_amdgcn_s_barrier();
-            mma_step(k, u, k + 3 < KT ? k + 3 : KT - 1);
+            barrier();
+            load_w(k + 3 < KT ? k + 3 : KT - 1, (u + 3) & 3);
+            mma_step(k, u, u & 1);
+            load_x(k + 2 < KT ? k + 2 : KT - 1, u & 1);
         }
     }
-    Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
 
 #pragma unroll
     for (int i = 0; i < WM; i++)
