@@ -633,12 +633,14 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
         asm volatile("" ::: "memory");
     };
 
-    // prologue: X of steps 0, 1; W of steps 0, 1, 2; W of step 0 dequantized
-    load_x(0, 0);
+    // prologue: W of steps 0, 1, 2 and X of steps 0, 1, in the order the
+    // loop issues them (so the compiler's wait counts at the loop head agree
+    // on both incoming paths); W of step 0 dequantized
     load_w(0, 0);
-    load_x(1, 1);
     load_w(1, 1);
+    load_x(0, 0);
     load_w(2 < KT ? 2 : KT - 1, 2);
+    load_x(1, 1);
     {
         uint32_t s2, zadd;
         wconst(0, 0, s2, zadd);
