@@ -45,7 +45,7 @@ MALL_BYTES = 512 * 2 ** 20
 COPY_BYTES = 2 ** 30
 # The kernel the dispatcher picks for M = 1, N = 11008, K = 4096, g = 128 asym
 # (688 blocks of 8 wavefronts, 4 k-blocks per wavefront).
-DECODE_KERNEL = "w4a16_gemv_kernel<8, 4, true>"
+DECODE_KERNEL = "w4a16_gemv_kernel<8, 4, true, true>"
 DECODE_SOURCE = os.path.join(ROOT, "quantized_gemm_q4_amd", "csrc", "w4a16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_gemv_decode_n11008_traffic.json")
 

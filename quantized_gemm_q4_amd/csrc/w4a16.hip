@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_skinny_kernel(
 // A lane whose X row m is >= M feeds row M - 1 instead: MFMA output rows do
 // not mix, and rows >= M are never stored. The wavefronts' partial sums meet
 // in LDS.
-template <int WAVES, int KBW, bool ASYM>
+template <int WAVES, int KBW, bool ASYM, bool ONE_ROW>
 __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
     const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
@@ -275,9 +275,22 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
     const uint32_t G = (uint32_t)K >> 7, Gz = (G + 1) >> 1;
     const int xchunks = K >> 3;                              // 16-byte chunks per X row
 
-    // 1. loads: X (first row, one chunk per thread), scales, zero-points, codes
+    // 1. loads: X, scales, zero-points, codes. With one X row each wavefront
+    //    fetches just its own k-range of X (no block barrier before the
+    //    compute); otherwise the block stages all of X (first row here, one
+    //    chunk per thread).
+    constexpr int XW = (KBW * 16 + 63) / 64;                 // 16-byte X chunks per lane
+    u32x4 xw[XW];
     u32x4 x0 = {0u, 0u, 0u, 0u};
-    if ((int)threadIdx.x < xchunks) x0 = *reinterpret_cast<const u32x4 *>(X + threadIdx.x * 8);
+    if (ONE_ROW) {
+#pragma unroll
+        for (int i = 0; i < XW; i++) {
+            const int c = lane + 64 * i;
+            if (c < KBW * 16) xw[i] = *reinterpret_cast<const u32x4 *>(X + kb0 * 128 + c * 8);
+        }
+    } else if ((int)threadIdx.x < xchunks) {
+        x0 = *reinterpret_cast<const u32x4 *>(X + threadIdx.x * 8);
+    }
     uint32_t sraw[KBW / 2];
     if constexpr (KBW == 8) {
         const u32x4 s8 = *reinterpret_cast<const u32x4 *>(scales + (nrow * G + kb0));
@@ -302,14 +315,24 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
         cw[p] = *reinterpret_cast<const u32x4 *>(codes + (nrow * (uint32_t)kh + (kb0 + p) * 64 + q * 16));
 
     // 2. X to LDS in the operand order
-    if ((int)threadIdx.x < xchunks) *reinterpret_cast<u32x4 *>(xs + threadIdx.x * 4) = permute_x(x0);
-    for (int m = 0; m < M; m++) {
-        for (int c = threadIdx.x + (m == 0 ? kT : 0); c < xchunks; c += kT) {
-            const u32x4 d = *reinterpret_cast<const u32x4 *>(X + (int64_t)m * K + c * 8);
-            *reinterpret_cast<u32x4 *>(xs + m * kh + c * 4) = permute_x(d);
+    if (ONE_ROW) {
+        // only this wavefront reads its k-range: LDS keeps one wavefront's
+        // accesses in order, so no barrier
+#pragma unroll
+        for (int i = 0; i < XW; i++) {
+            const int c = lane + 64 * i;
+            if (c < KBW * 16) *reinterpret_cast<u32x4 *>(xs + kb0 * 64 + c * 4) = permute_x(xw[i]);
         }
+    } else {
+        if ((int)threadIdx.x < xchunks) *reinterpret_cast<u32x4 *>(xs + threadIdx.x * 4) = permute_x(x0);
+        for (int m = 0; m < M; m++) {
+            for (int c = threadIdx.x + (m == 0 ? kT : 0); c < xchunks; c += kT) {
+                const u32x4 d = *reinterpret_cast<const u32x4 *>(X + (int64_t)m * K + c * 8);
+                *reinterpret_cast<u32x4 *>(xs + m * kh + c * 4) = permute_x(d);
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     // 3. compute, k-block by k-block
     const uint32_t *arow = xs + (r16 < M ? r16 : M - 1) * kh + q * 16 + kb0 * 64;
@@ -723,25 +746,24 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
             auto launch = [&](auto kernel) {
                 kernel<<<blocks, waves * 64, lds, st>>>(X, m, n, k, codes, scales, zeros, Y);
             };
-            const bool asym = zeros != nullptr;
-            if (waves == 4 && kbw == 8)
-                asym ? launch(w4a16_gemv_kernel<4, 8, true>) : launch(w4a16_gemv_kernel<4, 8, false>);
-            else if (waves == 4 && kbw == 4)
-                asym ? launch(w4a16_gemv_kernel<4, 4, true>) : launch(w4a16_gemv_kernel<4, 4, false>);
-            else if (waves == 4)
-                asym ? launch(w4a16_gemv_kernel<4, 2, true>) : launch(w4a16_gemv_kernel<4, 2, false>);
-            else if (waves == 8 && kbw == 8)
-                asym ? launch(w4a16_gemv_kernel<8, 8, true>) : launch(w4a16_gemv_kernel<8, 8, false>);
-            else if (waves == 8 && kbw == 4)
-                asym ? launch(w4a16_gemv_kernel<8, 4, true>) : launch(w4a16_gemv_kernel<8, 4, false>);
-            else if (waves == 8)
-                asym ? launch(w4a16_gemv_kernel<8, 2, true>) : launch(w4a16_gemv_kernel<8, 2, false>);
-            else if (kbw == 8)
-                asym ? launch(w4a16_gemv_kernel<16, 8, true>) : launch(w4a16_gemv_kernel<16, 8, false>);
-            else if (kbw == 4)
-                asym ? launch(w4a16_gemv_kernel<16, 4, true>) : launch(w4a16_gemv_kernel<16, 4, false>);
-            else
-                asym ? launch(w4a16_gemv_kernel<16, 2, true>) : launch(w4a16_gemv_kernel<16, 2, false>);
+            // ASYM x ONE_ROW variants of one (waves, kbw) configuration
+            auto launch4 = [&](auto k_a1, auto k_a0, auto k_s1, auto k_s0) {
+                if (zeros) m == 1 ? launch(k_a1) : launch(k_a0);
+                else m == 1 ? launch(k_s1) : launch(k_s0);
+            };
+#define Q4_GEMV4(W, B)                                                                          \
+    launch4(w4a16_gemv_kernel<W, B, true, true>, w4a16_gemv_kernel<W, B, true, false>,          \
+            w4a16_gemv_kernel<W, B, false, true>, w4a16_gemv_kernel<W, B, false, false>)
+            if (waves == 4 && kbw == 8) Q4_GEMV4(4, 8);
+            else if (waves == 4 && kbw == 4) Q4_GEMV4(4, 4);
+            else if (waves == 4) Q4_GEMV4(4, 2);
+            else if (waves == 8 && kbw == 8) Q4_GEMV4(8, 8);
+            else if (waves == 8 && kbw == 4) Q4_GEMV4(8, 4);
+            else if (waves == 8) Q4_GEMV4(8, 2);
+            else if (kbw == 8) Q4_GEMV4(16, 8);
+            else if (kbw == 4) Q4_GEMV4(16, 4);
+            else Q4_GEMV4(16, 2);
+#undef Q4_GEMV4
             return hipGetLastError();
         }
     }
