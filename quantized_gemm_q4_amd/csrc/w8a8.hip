@@ -221,46 +221,62 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
                 f.b[s][j] = *reinterpret_cast<const intx4 *>(stage + brow + j * 32 * LBK + co);
         }
     };
-    auto mma = [&](const Frags &f) {
+    auto mma_half = [&](const Frags &f, int s) {   // the 8 MFMAs of k32 half s
 #pragma unroll
-        for (int s = 0; s < 2; s++)
+        for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[s][i], f.b[s][j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 2; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[s][i], f.b[s][j], acc[i][j], 0, 0, 0);
     };
 
-    // Software pipeline (four LDS stages, two register fragment sets): in
-    // step k the wavefront waits for its loads of stage k + 1 and meets the
-    // block at the barrier, reads stage k + 1's fragments, refills stage k
-    // (drained into registers one step ago) with step k + 4, then runs step
-    // k's MFMAs from registers while those reads and loads are in flight.
+    // Software pipeline (four LDS stages, two register fragment sets). Step
+    // k: run the first half of step k's MFMAs from registers, wait for this
+    // wavefront's loads of stage k + 1 and meet the block at the barrier
+    // (after it stage k + 1 is complete and everyone is done reading stage
+    // k), then interleave the second half of the MFMAs with the reads of
+    // stage k + 1's fragments and the refill of stage k with step k + 4, so
+    // the matrix pipe never waits on the barrier's LDS and load traffic.
+    // Every step has the same shape: past the end the last step is
+    // refetched into stages nobody reads, so the wait counts are uniform.
     issue(stages[0], 0);
-    if (1 < KT) issue(stages[1], 1);
-    if (2 < KT) issue(stages[2], 2);
-    if (3 < KT) issue(stages[3], 3);
+    issue(stages[1], 1 < KT ? 1 : KT - 1);
+    issue(stages[2], 2 < KT ? 2 : KT - 1);
+    issue(stages[3], 3 < KT ? 3 : KT - 1);
     Frags f[2];
-    if (3 < KT) Q4_WAIT_VM_LGKM0(12);
-    else Q4_WAIT_VM_LGKM0(0);
+    asm volatile("" ::: "memory");
+    Q4_WAIT_VM_LGKM0(12);
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     read(stages[0], f[0]);
     for (int kt = 0; kt < KT; kt += LSTAGES) {
 #pragma unroll
         for (int u = 0; u < LSTAGES; u++) {
             const int k = kt + u;
-            if (k + 1 < KT) {
-                // loads outstanding: stages k + 1 .. min(k + 3, KT - 1)
-                if (k + 3 < KT) Q4_WAIT_VM_LGKM0(8);
-                else if (k + 2 < KT) Q4_WAIT_VM_LGKM0(4);
-                else Q4_WAIT_VM_LGKM0(0);
-                __builtin_amdgcn_s_barrier();
-                read(stages[(u + 1) % LSTAGES], f[(u + 1) & 1]);
-                if (k + 4 < KT) issue(stages[u], k + 4);
+            mma_half(f[u & 1], 0);
+            // nothing may move across the barrier (the scheduler does not
+            // treat s_barrier as a boundary for LDS reads by itself)
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
+            Q4_WAIT_VM_LGKM0(8);   // loads outstanding: stages k + 2, k + 3
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            read(stages[(u + 1) % LSTAGES], f[(u + 1) & 1]);
+            issue(stages[u], k + 4 < KT ? k + 4 : KT - 1);
+            mma_half(f[u & 1], 1);
+            // 12 fragment reads and 4 loads between the 8 MFMAs
+#pragma unroll
+            for (int g = 0; g < 6; g++) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
             }
-            mma(f[u & 1]);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);       // VMEM read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
     }
+    Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
 
 #pragma unroll
     for (int i = 0; i < 4; i++)
