@@ -19,83 +19,112 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
-// INT4 quantize + pack. Each lane owns 8 consecutive weights (one 16-byte
-// load); the g/8 lanes of a group reduce min/max (or max|x|) with xor
-// shuffles inside the wavefront, so every lane of the group holds the group
-// statistics without a broadcast. A block covers 2048 consecutive weights of
-// one row: 2048/g whole groups. Codes leave as one 32-bit store per lane
-// (8 nibbles, even k low), so a wavefront writes 256 contiguous bytes.
+// INT4 quantize + pack. Each lane owns CH chunks of 8 consecutive weights
+// (16-byte loads, all issued before any compute); for each chunk the g/8
+// lanes of a group reduce min/max (or max|x|) with xor shuffles inside the
+// wavefront, so every lane of the group holds the group statistics without a
+// broadcast. A block covers CH * 2048 consecutive weights of one row (whole
+// groups). Codes leave as one 32-bit store per lane and chunk (8 nibbles,
+// even k low), so a wavefront writes 256 contiguous bytes per chunk.
 // Zero-points of neighbouring groups meet in LDS to be packed two per byte.
-template <int LANES, bool SYM>
+//
+// Codes without a division per weight: with x and the fp16 scale sf both
+// binary16 values, the exact quotient x / sf is either a tie k + 1/2 or at
+// least 2^-16 (relative) away from every tie, while x * rcp(sf) is within a
+// few ulp of it; so k = rint(x * rcp(sf)) is rint of the exact quotient
+// except at ties, and the remainder r = x - k sf (exact in one fma: both
+// terms are multiples of the same power of two and span < 24 bits) is
+// exactly +-sf/2 there, where k moves to the even neighbour. The result is
+// rint(fl(x / sf)) bit for bit (fl(x / sf) is a tie only when x / sf is).
+__device__ __forceinline__ float code_rne(float x, float sf, float inv)
+{
+    float k = rintf(x * inv);
+    const float r = fmaf(-k, sf, x);
+    const float half = 0.5f * sf;
+    const bool odd = fabsf(k) < 16777216.0f && (((int)k) & 1) != 0;   // |k| >= 2^24 is even
+    if (r == half && odd) k += 1.0f;
+    if (r == -half && odd) k -= 1.0f;
+    return k;
+}
+
+template <int LANES, int CH, bool SYM>
 __global__ __launch_bounds__(kThreads) void q4_quantize_pack_kernel(
     const uint16_t *__restrict__ W, int64_t K, int G, int chunks_per_row,
     uint8_t *__restrict__ codes, uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros)
 {
-    constexpr int GPB = kThreads / LANES;   // groups per block
+    constexpr int GPB = kThreads / LANES;   // groups per block and chunk pass
     constexpr int g = LANES * 8;
-    __shared__ uint8_t zp_s[GPB];
+    __shared__ uint8_t zp_s[GPB * CH];
 
     const int64_t n = blockIdx.x / chunks_per_row;
     const int c = blockIdx.x % chunks_per_row;
     const int t = threadIdx.x;
     const int gi = t / LANES, li = t % LANES;
-    const int j = c * GPB + gi;
-    const bool valid = j < G;
-    const int64_t elem = n * K + (int64_t)j * g + li * 8;
 
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (valid) raw = *reinterpret_cast<const u32x4 *>(W + elem);
-    float x[8];
+    u32x4 raw[CH];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        x[2 * i] = h2f((uint16_t)(raw[i] & 0xffffu));
-        x[2 * i + 1] = h2f((uint16_t)(raw[i] >> 16));
+    for (int p = 0; p < CH; p++) {
+        const int j = (c * CH + p) * GPB + gi;
+        raw[p] = u32x4{0u, 0u, 0u, 0u};
+        if (j < G) raw[p] = *reinterpret_cast<const u32x4 *>(W + n * K + (int64_t)j * g + li * 8);
     }
-
-    float lo = 0.0f, hi = 0.0f;   // SYM: hi carries max|x|
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        if (SYM) {
-            hi = fmaxf(hi, fabsf(x[i]));
-        } else {
-            lo = fminf(lo, x[i]);
-            hi = fmaxf(hi, x[i]);
+    for (int p = 0; p < CH; p++) {
+        const int j = (c * CH + p) * GPB + gi;
+        const bool valid = j < G;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            x[2 * i] = h2f((uint16_t)(raw[p][i] & 0xffffu));
+            x[2 * i + 1] = h2f((uint16_t)(raw[p][i] >> 16));
         }
-    }
+        float lo = 0.0f, hi = 0.0f;   // SYM: hi carries max|x|
 #pragma unroll
-    for (int off = LANES / 2; off > 0; off >>= 1) {
-        if (!SYM) lo = fminf(lo, __shfl_xor(lo, off));
-        hi = fmaxf(hi, __shfl_xor(hi, off));
-    }
-
-    const float s32 = SYM ? hi / 7.0f : (hi - lo) / 15.0f;
-    uint16_t s16 = f2h(s32);
-    if ((s16 & 0x7fffu) == 0) s16 = 0x3c00u;   // 1.0
-    const float sf = h2f(s16);
-    float zp = 8.0f;
-    if (!SYM) zp = fminf(fmaxf(rintf(-lo / sf), 0.0f), 15.0f);
-
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        float q = rintf(x[i] / sf);
-        if (SYM) {
-            q = fminf(fmaxf(q, -8.0f), 7.0f) + 8.0f;
-        } else {
-            q = fminf(fmaxf(q + zp, 0.0f), 15.0f);
+        for (int i = 0; i < 8; i++) {
+            if (SYM) {
+                hi = fmaxf(hi, fabsf(x[i]));
+            } else {
+                lo = fminf(lo, x[i]);
+                hi = fmaxf(hi, x[i]);
+            }
         }
-        word |= (uint32_t)q << (4 * i);
-    }
-    if (valid) {
-        *reinterpret_cast<uint32_t *>(codes + elem / 2) = word;
-        if (li == 0) scales[n * G + j] = s16;
+#pragma unroll
+        for (int off = LANES / 2; off > 0; off >>= 1) {
+            if (!SYM) lo = fminf(lo, __shfl_xor(lo, off));
+            hi = fmaxf(hi, __shfl_xor(hi, off));
+        }
+
+        const float s32 = SYM ? hi / 7.0f : (hi - lo) / 15.0f;   // IEEE division: rounded to fp16 next
+        uint16_t s16 = f2h(s32);
+        if ((s16 & 0x7fffu) == 0) s16 = 0x3c00u;   // 1.0
+        const float sf = h2f(s16);
+        const float inv = __builtin_amdgcn_rcpf(sf);
+        float zp = 8.0f;
+        if (!SYM) zp = fminf(fmaxf(code_rne(-lo, sf, inv), 0.0f), 15.0f);
+
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            float q = code_rne(x[i], sf, inv);
+            if (SYM) {
+                q = fminf(fmaxf(q, -8.0f), 7.0f) + 8.0f;
+            } else {
+                q = fminf(fmaxf(q + zp, 0.0f), 15.0f);
+            }
+            word |= (uint32_t)q << (4 * i);
+        }
+        if (valid) {
+            const int64_t elem = n * K + (int64_t)j * g + li * 8;
+            *reinterpret_cast<uint32_t *>(codes + elem / 2) = word;
+            if (li == 0) scales[n * G + j] = s16;
+        }
+        if (!SYM && li == 0) zp_s[p * GPB + gi] = valid ? (uint8_t)zp : 0;
     }
     if (!SYM) {
-        if (li == 0) zp_s[gi] = valid ? (uint8_t)zp : 0;
         __syncthreads();
         const int Gz = (G + 1) / 2;
-        if (t < GPB / 2) {
-            const int jz = c * (GPB / 2) + t;
+        if (t < GPB * CH / 2) {
+            const int jz = c * (GPB * CH / 2) + t;
             if (2 * jz < G)
                 zeros[n * Gz + jz] = (uint8_t)(zp_s[2 * t] | (zp_s[2 * t + 1] << 4));
         }
@@ -107,16 +136,17 @@ hipError_t launch_q4_g(const uint16_t *W, int64_t N, int64_t K, int sym, uint8_t
                        uint16_t *scales, uint8_t *zeros, hipStream_t st)
 {
     constexpr int GPB = kThreads / LANES;
+    constexpr int CH = 2;
     const int G = (int)(K / (LANES * 8));
-    const int chunks = (G + GPB - 1) / GPB;
+    const int chunks = (G + GPB * CH - 1) / (GPB * CH);
     const int64_t blocks = N * chunks;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (sym)
-        q4_quantize_pack_kernel<LANES, true><<<(unsigned)blocks, kThreads, 0, st>>>(
+        q4_quantize_pack_kernel<LANES, CH, true><<<(unsigned)blocks, kThreads, 0, st>>>(
             W, K, G, chunks, codes, scales, zeros);
     else
-        q4_quantize_pack_kernel<LANES, false><<<(unsigned)blocks, kThreads, 0, st>>>(
+        q4_quantize_pack_kernel<LANES, CH, false><<<(unsigned)blocks, kThreads, 0, st>>>(
             W, K, G, chunks, codes, scales, zeros);
     return hipGetLastError();
 }
