@@ -46,7 +46,10 @@ COPY_BYTES = 2 ** 30
 # The kernel the dispatcher picks for M = 1, N = 11008, K = 4096, g = 128 asym
 # (688 blocks of 8 wavefronts, 4 k-blocks per wavefront).
 DECODE_KERNEL = "w4a16_gemv_kernel<8, 4, true, true>"
-DECODE_SOURCE = os.path.join(ROOT, "quantized_gemm_q4_amd", "csrc", "w4a16.hip")
+# the decode GEMV's source files: the committed traffic figures are valid only
+# for the revision of these files they were taken on
+DECODE_SOURCES = [os.path.join(ROOT, "quantized_gemm_q4_amd", "csrc", f)
+                  for f in ("w4a16_gemv.hip", "w4a16_dequant.hpp", "q4_internal.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_gemv_decode_n11008_traffic.json")
 
 
@@ -298,8 +301,11 @@ def measured_traffic():
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        with open(DECODE_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        h = hashlib.sha256()
+        for path in DECODE_SOURCES:
+            with open(path, "rb") as f:
+                h.update(f.read())
+        sha = h.hexdigest()
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != sha or rec.get("kernel") != DECODE_KERNEL:

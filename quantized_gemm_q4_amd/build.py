@@ -25,6 +25,7 @@ SOURCES = {
     "abi.hip": [],
     "quantize.hip": ["-ffp-contract=off"],
     "w4a16.hip": ["-ffp-contract=off"],
+    "w4a16_gemv.hip": ["-ffp-contract=off"],
     "w8a8.hip": ["-ffp-contract=off"],
 }
 

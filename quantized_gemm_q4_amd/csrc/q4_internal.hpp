@@ -40,6 +40,11 @@ hipError_t launch_smooth_scales(const uint16_t *Xcal, int64_t R, const uint16_t 
 hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,
                         const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
                         uint16_t *Y, hipStream_t st);
+// Decode GEMV (M <= 16, g = 128); hipErrorNotSupported when the shape or the
+// alignment of scales / zeros does not suit it.
+hipError_t launch_w4a16_gemv(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,
+                             const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                             uint16_t *Y, hipStream_t st);
 hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
                             const float *sw, int64_t M, int64_t N, int64_t K, uint16_t *Y,
                             int32_t *acc_out, hipStream_t st);

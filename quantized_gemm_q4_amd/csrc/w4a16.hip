@@ -4,44 +4,25 @@
 // the GEMM; Core ideas, ai-infra.cypggs.com, §2.2: w_hat = (u - zp) * s;
 // Method boundaries, llm-glossary.tokens-kit.com, GPTQ section: decode is
 // bound by the weight read, prefill by the dequant + matrix-core path).
+// This file holds the dispatch and the kernels for M > 16; the decode GEMV
+// (M <= 16, g = 128) is in w4a16_gemv.hip.
 //
-// Arithmetic. Both kernels feed v_mfma_f32_16x16x32_f16 with the exact
-// integers (u - zp) in fp16 and x in fp16: every product is exact in fp32.
-// The fp32 partial sum of one 128-wide k-block is multiplied by the fp32
-// value of the block's group scale and added to the fp32 total. The only
-// roundings are fp32 additions and the final fp16 store.
-//
-// Operand layout. In a 16x16x32 MFMA lane l feeds row (l % 16) of A and column
-// (l % 16) of B with 8 k-values each; A and B see the same k order, so the
-// product does not depend on which k sits where. We pick the order that makes
-// the INT4 unpack cheap: lane group q = l / 16 owns the 32 consecutive k of
-// a 128-wide k-block starting at 32q (one 16-byte load of codes), and
-// MFMA step t takes the 8 nibbles of the lane's dword t. Masks of the form
-// 0x000F000F lift nibbles i and i+4 into the two fp16 halves of a register at
-// once, so the B operand holds k offsets (0,4,1,5,2,6,3,7); the X operand is
-// permuted the same way.
+// Arithmetic. The skinny and 128 x 128 kernels feed v_mfma_f32_16x16x32_f16
+// with the exact integers (u - zp) in fp16 (unpacked as in w4a16_dequant.hpp)
+// and x in fp16: every product is exact in fp32. The fp32 partial sum of one
+// 128-wide k-block is multiplied by the fp32 value of the block's group scale
+// and added to the fp32 total. The large-M kernel dequantizes to fp16
+// (u - zp) * s once per weight (one rounding) and accumulates in fp32.
 //
 // The packed weight is read in place in the layout q4_quantize_pack writes
 // (row-major codes [N, K/2], scales [N, K/g], zeros [N, ceil(K/g/2)]); it is
 // never expanded in memory.
 #include <cstdlib>
 
-#include "q4_internal.hpp"
+#include "w4a16_dequant.hpp"
 
 namespace q4k {
 namespace {
-
-// Tuning override for the decode GEMV: Q4_GEMV_WAVES=4|8|16 forces the
-// wavefronts per block when that configuration is valid for the shape.
-int gemv_waves_override()
-{
-    static const int v = [] {
-        const char *e = std::getenv("Q4_GEMV_WAVES");
-        const int w = e ? std::atoi(e) : 0;
-        return (w == 4 || w == 8 || w == 16) ? w : 0;
-    }();
-    return v;
-}
 
 // Tuning override for the large-M GEMM: Q4_GEMM_NU=4|8|11 forces the tile
 // width (32 NU columns). Read at every call.
@@ -53,72 +34,6 @@ int gemm_nu_override()
 }
 
 constexpr int kThreads = 256;
-
-// Dequantize the 8 nibbles of one code dword (nib_i at bits 4i, k offset i)
-// into 16 * (nib - zp) as exact fp16 integers, in the operand k order
-// (0,4,1,5,2,6,3,7). OR-ing a nibble into the mantissa of fp16 1024.0
-// (0x6400) makes 1024 + nib when the nibble sits at bits 0-3 of a half and
-// 1024 + 16 * nib when it sits at bits 4-7; both are exact. So one mask
-// serves nibbles i and i+4 at bit 0 and another nibbles i+1 and i+5 at bit 4;
-// only one shift (by 8) is needed per dword. The bit-0 pairs are brought to
-// the same 16x scale with one fused multiply-add, the bit-4 pairs with one
-// subtraction: 16 (1024 + n) - (16384 + 16 zp) and (1024 + 16 n) - (1024 + 16
-// zp) are exact. The caller folds the factor 1/16 into the fp32 scale.
-struct ZeroConst {
-    uint32_t lo;   // fp16 pair -(16384 + 16 zp)
-    uint32_t hi;   // fp16 pair   1024 + 16 zp
-};
-
-__device__ __forceinline__ ZeroConst zero_const(int zp)
-{
-    return ZeroConst{(uint32_t)(0xF400 + zp) * 0x10001u, (uint32_t)(0x6400 + 16 * zp) * 0x10001u};
-}
-
-// (w & mask) | magic in one v_and_or_b32. The backend does not fuse the two
-// when both constants are literals; this is plain ALU, no memory operand.
-__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic)
-{
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
-    return r;
-}
-
-__device__ __forceinline__ half8 dequant8(uint32_t w, ZeroConst z)
-{
-    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
-    const half2v sixteen = {(_Float16)16.0f, (_Float16)16.0f};
-    const half2v zl = __builtin_bit_cast(half2v, z.lo);
-    const half2v zh = __builtin_bit_cast(half2v, z.hi);
-    const uint32_t w8 = w >> 8;
-    const half2v p0 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, and_or(w, lo, magic)), sixteen, zl);
-    const half2v p1 = __builtin_bit_cast(half2v, and_or(w, hi, magic)) - zh;
-    const half2v p2 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, and_or(w8, lo, magic)), sixteen, zl);
-    const half2v p3 = __builtin_bit_cast(half2v, and_or(w8, hi, magic)) - zh;
-    const u32x4 r = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-    return __builtin_bit_cast(half8, r);
-}
-
-// fp32 value of a group scale with the 1/16 of dequant8 folded in (exact).
-__device__ __forceinline__ float scale16(uint16_t s) { return h2f(s) * 0.0625f; }
-
-// Natural-order fp16 x0..x7 (four dwords) -> (x0,x4,x1,x5,x2,x6,x3,x7).
-__device__ __forceinline__ u32x4 permute_x(u32x4 d)
-{
-    u32x4 r;
-    r[0] = (d[0] & 0xffffu) | (d[2] << 16);
-    r[1] = (d[0] >> 16) | (d[2] & 0xffff0000u);
-    r[2] = (d[1] & 0xffffu) | (d[3] << 16);
-    r[3] = (d[1] >> 16) | (d[3] & 0xffff0000u);
-    return r;
-}
-
-__device__ __forceinline__ int group_zp(const uint8_t *__restrict__ zeros, int64_t n, int Gz,
-                                        int grp)
-{
-    if (!zeros) return 8;
-    return (zeros[n * Gz + (grp >> 1)] >> ((grp & 1) * 4)) & 15;
-}
 
 // ---------------------------------------------------------------------------
 // Skinny kernel, M <= 64 (decode and batched decode). Memory bound: the
@@ -236,133 +151,6 @@ __global__ __launch_bounds__(kThreads) void w4a16_skinny_kernel(
         const int m = mt * 16 + 4 * (l >> 4) + r;
         const int n = n_base + nt * 16 + (l & 15);
         if (m < M && n < N) Y[(int64_t)m * N + n] = f2h(v);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// GEMV kernel, small M (decode), g = 128. A block of WAVES wavefronts owns
-// 16 output channels and all of K; wavefront w owns exactly KBW k-blocks
-// (K = 128 * WAVES * KBW; other shapes take the skinny kernel). Order of
-// work, so that compute overlaps the weight stream instead of following it:
-//   1. each thread issues its X load (M x K fp16, small, mostly L2 hits),
-//      the scales (one vector load) and zero-points (one load) of its
-//      k-blocks, then the code loads of all its k-blocks;
-//   2. X goes to LDS in the operand k order; the barrier waits only for the
-//      X load (loads complete in issue order and X was issued first);
-//   3. each k-block is computed as soon as its own codes have landed.
-// With every block resident, the whole packed weight is in flight at once.
-// A lane whose X row m is >= M feeds row M - 1 instead: MFMA output rows do
-// not mix, and rows >= M are never stored. The wavefronts' partial sums meet
-// in LDS.
-template <int WAVES, int KBW, bool ASYM, bool ONE_ROW>
-__global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
-    const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
-    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-    uint16_t *__restrict__ Y)
-{
-    static_assert(KBW == 2 || KBW == 4 || KBW == 8, "vector scale / zero-point loads of 2, 4, 8 groups");
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int kh = K >> 1;                                   // dwords per X row
-    uint32_t *xs = reinterpret_cast<uint32_t *>(smem);      // [M][K/2] dwords
-    float *red = reinterpret_cast<float *>(xs + M * kh);    // [WAVES][4][64]
-    constexpr int kT = WAVES * 64;
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r16 = lane & 15, q = lane >> 4;
-    const int kb0 = wave * KBW;
-    const int n = blockIdx.x * 16 + r16;
-    const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
-    const uint32_t G = (uint32_t)K >> 7, Gz = (G + 1) >> 1;
-    const int xchunks = K >> 3;                              // 16-byte chunks per X row
-
-    // 1. loads: X, scales, zero-points, codes. With one X row each wavefront
-    //    fetches just its own k-range of X (no block barrier before the
-    //    compute); otherwise the block stages all of X (first row here, one
-    //    chunk per thread).
-    constexpr int XW = (KBW * 16 + 63) / 64;                 // 16-byte X chunks per lane
-    u32x4 xw[XW];
-    u32x4 x0 = {0u, 0u, 0u, 0u};
-    if (ONE_ROW) {
-#pragma unroll
-        for (int i = 0; i < XW; i++) {
-            const int c = lane + 64 * i;
-            if (c < KBW * 16) xw[i] = *reinterpret_cast<const u32x4 *>(X + kb0 * 128 + c * 8);
-        }
-    } else if ((int)threadIdx.x < xchunks) {
-        x0 = *reinterpret_cast<const u32x4 *>(X + threadIdx.x * 8);
-    }
-    uint32_t sraw[KBW / 2];
-    if constexpr (KBW == 8) {
-        const u32x4 s8 = *reinterpret_cast<const u32x4 *>(scales + (nrow * G + kb0));
-#pragma unroll
-        for (int i = 0; i < 4; i++) sraw[i] = s8[i];
-    } else if constexpr (KBW == 4) {
-        const u32x2 s4 = *reinterpret_cast<const u32x2 *>(scales + (nrow * G + kb0));
-        sraw[0] = s4[0];
-        sraw[1] = s4[1];
-    } else {
-        sraw[0] = *reinterpret_cast<const uint32_t *>(scales + (nrow * G + kb0));
-    }
-    uint32_t zraw = 0x88888888u;   // symmetric: zp = 8 (no branch, so no early wait)
-    if (ASYM) {
-        if constexpr (KBW == 8) zraw = *reinterpret_cast<const uint32_t *>(zeros + (nrow * Gz + (kb0 >> 1)));
-        else if constexpr (KBW == 4) zraw = *reinterpret_cast<const uint16_t *>(zeros + (nrow * Gz + (kb0 >> 1)));
-        else zraw = zeros[nrow * Gz + (kb0 >> 1)];
-    }
-    u32x4 cw[KBW];
-#pragma unroll
-    for (int p = 0; p < KBW; p++)
-        cw[p] = *reinterpret_cast<const u32x4 *>(codes + (nrow * (uint32_t)kh + (kb0 + p) * 64 + q * 16));
-
-    // 2. X to LDS in the operand order
-    if (ONE_ROW) {
-        // only this wavefront reads its k-range: LDS keeps one wavefront's
-        // accesses in order, so no barrier
-#pragma unroll
-        for (int i = 0; i < XW; i++) {
-            const int c = lane + 64 * i;
-            if (c < KBW * 16) *reinterpret_cast<u32x4 *>(xs + kb0 * 64 + c * 4) = permute_x(xw[i]);
-        }
-    } else {
-        if ((int)threadIdx.x < xchunks) *reinterpret_cast<u32x4 *>(xs + threadIdx.x * 4) = permute_x(x0);
-        for (int m = 0; m < M; m++) {
-            for (int c = threadIdx.x + (m == 0 ? kT : 0); c < xchunks; c += kT) {
-                const u32x4 d = *reinterpret_cast<const u32x4 *>(X + (int64_t)m * K + c * 8);
-                *reinterpret_cast<u32x4 *>(xs + m * kh + c * 4) = permute_x(d);
-            }
-        }
-        __syncthreads();
-    }
-
-    // 3. compute, k-block by k-block
-    const uint32_t *arow = xs + (r16 < M ? r16 : M - 1) * kh + q * 16 + kb0 * 64;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < KBW; p++) {
-        const ZeroConst zc = zero_const((zraw >> (4 * p)) & 15);
-        floatx4 part = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            const half8 a = *reinterpret_cast<const half8 *>(arow + p * 64 + t * 4);
-            part = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, dequant8(cw[p][t], zc), part, 0, 0, 0);
-        }
-        const uint32_t sw = sraw[p >> 1];
-        const float sc = h2f((uint16_t)((p & 1) ? (sw >> 16) : (sw & 0xffffu)));
-#pragma unroll
-        for (int r = 0; r < 4; r++) acc[r] = fmaf(part[r], sc, acc[r]);
-    }
-
-#pragma unroll
-    for (int r = 0; r < 4; r++) red[(wave * 4 + r) * 64 + lane] = acc[r];
-    __syncthreads();
-    if (threadIdx.x < 256) {
-        const int r = threadIdx.x >> 6, l = threadIdx.x & 63;
-        float v = 0.0f;
-#pragma unroll
-        for (int w = 0; w < WAVES; w++) v += red[(w * 4 + r) * 64 + l];
-        const int m = 4 * (l >> 4) + r;
-        const int nn = blockIdx.x * 16 + (l & 15);
-        if (m < M && nn < N) Y[(int64_t)m * N + nn] = f2h(v * 0.0625f);   // the 1/16 of dequant8
     }
 }
 
@@ -722,50 +510,9 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
 {
     if (M == 0 || N == 0) return hipSuccess;
     const int m = (int)M, n = (int)N, k = (int)K;
-    // GEMV path (g = 128): X fits in LDS next to the reduction buffer and
-    // the k-blocks divide evenly over the wavefronts (2, 4 or 8 each). The
-    // block takes the most wavefronts (16, else 8, else 4) that keep every
-    // block resident at once (256 CUs x 32 wavefronts), so the whole weight
-    // is in flight from the start (measured best for N = 11008 and 4096).
-    if (g == 128 && M <= 16 && N * K / 2 < (int64_t)0xFFFFFF00) {   // 32-bit offsets in the kernel
-        const int blocks = (n + 15) / 16;
-        const int KB = k / 128;
-        const int G = KB, Gz = (G + 1) / 2;
-        const int forced = gemv_waves_override();
-        for (int waves : {16, 8, 4}) {
-            if (forced && waves != forced) continue;
-            if (!forced && waves > 4 && (int64_t)blocks * waves > 256 * 32) continue;
-            if (KB % waves != 0) continue;
-            const int kbw = KB / waves;
-            const size_t lds = (size_t)M * K * 2 + (size_t)waves * 4 * 64 * 4;
-            if ((kbw != 2 && kbw != 4 && kbw != 8) || lds > 64 * 1024) continue;
-            // vector scale / zero-point loads: whole, aligned runs of kbw groups
-            if (G % kbw != 0 || (kbw >= 4 && Gz % (kbw / 2) != 0)) continue;
-            if ((reinterpret_cast<uintptr_t>(scales) & (kbw * 2 - 1)) != 0) continue;
-            if (zeros && (reinterpret_cast<uintptr_t>(zeros) & (kbw / 2 - 1)) != 0) continue;
-            auto launch = [&](auto kernel) {
-                kernel<<<blocks, waves * 64, lds, st>>>(X, m, n, k, codes, scales, zeros, Y);
-            };
-            // ASYM x ONE_ROW variants of one (waves, kbw) configuration
-            auto launch4 = [&](auto k_a1, auto k_a0, auto k_s1, auto k_s0) {
-                if (zeros) m == 1 ? launch(k_a1) : launch(k_a0);
-                else m == 1 ? launch(k_s1) : launch(k_s0);
-            };
-#define Q4_GEMV4(W, B)                                                                          \
-    launch4(w4a16_gemv_kernel<W, B, true, true>, w4a16_gemv_kernel<W, B, true, false>,          \
-            w4a16_gemv_kernel<W, B, false, true>, w4a16_gemv_kernel<W, B, false, false>)
-            if (waves == 4 && kbw == 8) Q4_GEMV4(4, 8);
-            else if (waves == 4 && kbw == 4) Q4_GEMV4(4, 4);
-            else if (waves == 4) Q4_GEMV4(4, 2);
-            else if (waves == 8 && kbw == 8) Q4_GEMV4(8, 8);
-            else if (waves == 8 && kbw == 4) Q4_GEMV4(8, 4);
-            else if (waves == 8) Q4_GEMV4(8, 2);
-            else if (kbw == 8) Q4_GEMV4(16, 8);
-            else if (kbw == 4) Q4_GEMV4(16, 4);
-            else Q4_GEMV4(16, 2);
-#undef Q4_GEMV4
-            return hipGetLastError();
-        }
+    if (g == 128 && M <= 16) {
+        const hipError_t e = launch_w4a16_gemv(X, M, N, K, g, codes, scales, zeros, Y, st);
+        if (e != hipErrorNotSupported) return e;
     }
     if (M >= 256 && g % 128 == 0 && (g & (g - 1)) == 0 && M * K * 2 < ((int64_t)1 << 31) &&
         N * (K / 2) < ((int64_t)1 << 31)) {

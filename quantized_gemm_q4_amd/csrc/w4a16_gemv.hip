@@ -1,0 +1,221 @@
+// W4A16 decode GEMV on gfx950: Y[M,N] = X[M,K] * W_hat[N,K]^T for M <= 16 and
+// group size 128, with the INT4 weight dequantized in registers (Core ideas,
+// ai-infra.cypggs.com, section 2.2: w_hat = (u - zp) * s; Method boundaries,
+// llm-glossary.tokens-kit.com, GPTQ section: decode is bound by the weight read).
+//
+// Arithmetic. v_mfma_f32_16x16x32_f16 takes x in fp16 and 16 (u - zp) as exact
+// fp16 integers, so every product is exact in fp32. The fp32 partial sum of one
+// 128-wide k-block is multiplied by the fp32 value of the block's group scale
+// and added to the fp32 total; the factor 16 is removed at the store. The only
+// roundings are fp32 additions and the final fp16 store.
+#include <cstdlib>
+
+#include "w4a16_dequant.hpp"
+
+namespace q4k {
+namespace {
+
+// Tuning override for the decode GEMV: Q4_GEMV_WAVES=4|8|16 forces the
+// wavefronts per block when that configuration is valid for the shape.
+int gemv_waves_override()
+{
+    static const int v = [] {
+        const char *e = std::getenv("Q4_GEMV_WAVES");
+        const int w = e ? std::atoi(e) : 0;
+        return (w == 4 || w == 8 || w == 16) ? w : 0;
+    }();
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// GEMV kernel, small M (decode), g = 128. A block of WAVES wavefronts owns
+// 16 output channels and all of K; wavefront w owns exactly KBW k-blocks
+// (K = 128 * WAVES * KBW; other shapes take the skinny kernel). Order of
+// work, so that compute overlaps the weight stream instead of following it:
+//   1. each thread issues its X load (M x K fp16, small, mostly L2 hits),
+//      the scales (one vector load) and zero-points (one load) of its
+//      k-blocks, then the code loads of all its k-blocks;
+//   2. X goes to LDS in the operand k order; the barrier waits only for the
+//      X load (loads complete in issue order and X was issued first);
+//   3. each k-block is computed as soon as its own codes have landed.
+// With every block resident, the whole packed weight is in flight at once.
+// A lane whose X row m is >= M feeds row M - 1 instead: MFMA output rows do
+// not mix, and rows >= M are never stored. The wavefronts' partial sums meet
+// in LDS.
+template <int WAVES, int KBW, bool ASYM, bool ONE_ROW>
+__global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
+    const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    uint16_t *__restrict__ Y)
+{
+    static_assert(KBW == 2 || KBW == 4 || KBW == 8, "vector scale / zero-point loads of 2, 4, 8 groups");
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int kh = K >> 1;                                   // dwords per X row
+    uint32_t *xs = reinterpret_cast<uint32_t *>(smem);      // [M][K/2] dwords
+    float *red = reinterpret_cast<float *>(xs + M * kh);    // [WAVES][4][64]
+    constexpr int kT = WAVES * 64;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int kb0 = wave * KBW;
+    const int n = blockIdx.x * 16 + r16;
+    const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
+    const uint32_t G = (uint32_t)K >> 7, Gz = (G + 1) >> 1;
+    const int xchunks = K >> 3;                              // 16-byte chunks per X row
+
+    // 1. loads: X, scales, zero-points, codes. With one X row each wavefront
+    //    fetches just its own k-range of X (no block barrier before the
+    //    compute); otherwise the block stages all of X (first row here, one
+    //    chunk per thread).
+    constexpr int XW = (KBW * 16 + 63) / 64;                 // 16-byte X chunks per lane
+    u32x4 xw[XW];
+    u32x4 x0 = {0u, 0u, 0u, 0u};
+    if (ONE_ROW) {
+#pragma unroll
+        for (int i = 0; i < XW; i++) {
+            const int c = lane + 64 * i;
+            if (c < KBW * 16) xw[i] = *reinterpret_cast<const u32x4 *>(X + kb0 * 128 + c * 8);
+        }
+    } else if ((int)threadIdx.x < xchunks) {
+        x0 = *reinterpret_cast<const u32x4 *>(X + threadIdx.x * 8);
+    }
+    uint32_t sraw[KBW / 2];
+    if constexpr (KBW == 8) {
+        const u32x4 s8 = *reinterpret_cast<const u32x4 *>(scales + (nrow * G + kb0));
+#pragma unroll
+        for (int i = 0; i < 4; i++) sraw[i] = s8[i];
+    } else if constexpr (KBW == 4) {
+        const u32x2 s4 = *reinterpret_cast<const u32x2 *>(scales + (nrow * G + kb0));
+        sraw[0] = s4[0];
+        sraw[1] = s4[1];
+    } else {
+        sraw[0] = *reinterpret_cast<const uint32_t *>(scales + (nrow * G + kb0));
+    }
+    uint32_t zraw = 0x88888888u;   // symmetric: zp = 8 (no branch, so no early wait)
+    if (ASYM) {
+        if constexpr (KBW == 8) zraw = *reinterpret_cast<const uint32_t *>(zeros + (nrow * Gz + (kb0 >> 1)));
+        else if constexpr (KBW == 4) zraw = *reinterpret_cast<const uint16_t *>(zeros + (nrow * Gz + (kb0 >> 1)));
+        else zraw = zeros[nrow * Gz + (kb0 >> 1)];
+    }
+    u32x4 cw[KBW];
+#pragma unroll
+    for (int p = 0; p < KBW; p++)
+        cw[p] = *reinterpret_cast<const u32x4 *>(codes + (nrow * (uint32_t)kh + (kb0 + p) * 64 + q * 16));
+
+    // 2. X to LDS in the operand order
+    if (ONE_ROW) {
+        // only this wavefront reads its k-range: LDS keeps one wavefront's
+        // accesses in order, so no barrier
+#pragma unroll
+        for (int i = 0; i < XW; i++) {
+            const int c = lane + 64 * i;
+            if (c < KBW * 16) *reinterpret_cast<u32x4 *>(xs + kb0 * 64 + c * 4) = permute_x(xw[i]);
+        }
+    } else {
+        if ((int)threadIdx.x < xchunks) *reinterpret_cast<u32x4 *>(xs + threadIdx.x * 4) = permute_x(x0);
+        for (int m = 0; m < M; m++) {
+            for (int c = threadIdx.x + (m == 0 ? kT : 0); c < xchunks; c += kT) {
+                const u32x4 d = *reinterpret_cast<const u32x4 *>(X + (int64_t)m * K + c * 8);
+                *reinterpret_cast<u32x4 *>(xs + m * kh + c * 4) = permute_x(d);
+            }
+        }
+        __syncthreads();
+    }
+
+    // 3. compute, k-block by k-block. Each k-block has an accumulator of its
+    //    own, so one block's MFMA chain never waits on the previous block's
+    //    scaling (a shared accumulator serialises all of them).
+    const uint32_t *arow = xs + (r16 < M ? r16 : M - 1) * kh + q * 16 + kb0 * 64;
+    floatx4 part[KBW];
+#pragma unroll
+    for (int p = 0; p < KBW; p++) {
+        const ZeroConst zc = zero_const((zraw >> (4 * p)) & 15);
+        part[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const half8 a = *reinterpret_cast<const half8 *>(arow + p * 64 + t * 4);
+            part[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, dequant8(cw[p][t], zc), part[p], 0, 0, 0);
+        }
+    }
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < KBW; p++) {
+        const uint32_t sw = sraw[p >> 1];
+        const float sc = h2f((uint16_t)((p & 1) ? (sw >> 16) : (sw & 0xffffu)));
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[r] = fmaf(part[p][r], sc, acc[r]);
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; r++) red[(wave * 4 + r) * 64 + lane] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int r = threadIdx.x >> 6, l = threadIdx.x & 63;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; w++) v += red[(w * 4 + r) * 64 + l];
+        const int m = 4 * (l >> 4) + r;
+        const int nn = blockIdx.x * 16 + (l & 15);
+        if (m < M && nn < N) Y[(int64_t)m * N + nn] = f2h(v * 0.0625f);   // the 1/16 of dequant8
+    }
+}
+
+}  // namespace
+
+// Launches the GEMV when the shape and the alignment of the scale and
+// zero-point arrays suit it; hipErrorNotSupported otherwise (the caller then
+// takes another kernel).
+hipError_t launch_w4a16_gemv(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,
+                             const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                             uint16_t *Y, hipStream_t st)
+{
+    const int m = (int)M, n = (int)N, k = (int)K;
+    // GEMV path (g = 128): X fits in LDS next to the reduction buffer and
+    // the k-blocks divide evenly over the wavefronts (2, 4 or 8 each). The
+    // block takes the most wavefronts (16, else 8, else 4) that keep every
+    // block resident at once (256 CUs x 32 wavefronts), so the whole weight
+    // is in flight from the start (measured best for N = 11008 and 4096).
+    if (g == 128 && M <= 16 && N * K / 2 < (int64_t)0xFFFFFF00) {   // 32-bit offsets in the kernel
+        const int blocks = (n + 15) / 16;
+        const int KB = k / 128;
+        const int G = KB, Gz = (G + 1) / 2;
+        const int forced = gemv_waves_override();
+        for (int waves : {16, 8, 4}) {
+            if (forced && waves != forced) continue;
+            if (!forced && waves > 4 && (int64_t)blocks * waves > 256 * 32) continue;
+            if (KB % waves != 0) continue;
+            const int kbw = KB / waves;
+            const size_t lds = (size_t)M * K * 2 + (size_t)waves * 4 * 64 * 4;
+            if ((kbw != 2 && kbw != 4 && kbw != 8) || lds > 64 * 1024) continue;
+            // vector scale / zero-point loads: whole, aligned runs of kbw groups
+            if (G % kbw != 0 || (kbw >= 4 && Gz % (kbw / 2) != 0)) continue;
+            if ((reinterpret_cast<uintptr_t>(scales) & (kbw * 2 - 1)) != 0) continue;
+            if (zeros && (reinterpret_cast<uintptr_t>(zeros) & (kbw / 2 - 1)) != 0) continue;
+            auto launch = [&](auto kernel) {
+                kernel<<<blocks, waves * 64, lds, st>>>(X, m, n, k, codes, scales, zeros, Y);
+            };
+            // ASYM x ONE_ROW variants of one (waves, kbw) configuration
+            auto launch4 = [&](auto k_a1, auto k_a0, auto k_s1, auto k_s0) {
+                if (zeros) m == 1 ? launch(k_a1) : launch(k_a0);
+                else m == 1 ? launch(k_s1) : launch(k_s0);
+            };
+#define Q4_GEMV4(W, B)                                                                          \
+    launch4(w4a16_gemv_kernel<W, B, true, true>, w4a16_gemv_kernel<W, B, true, false>,          \
+            w4a16_gemv_kernel<W, B, false, true>, w4a16_gemv_kernel<W, B, false, false>)
+            if (waves == 4 && kbw == 8) Q4_GEMV4(4, 8);
+            else if (waves == 4 && kbw == 4) Q4_GEMV4(4, 4);
+            else if (waves == 4) Q4_GEMV4(4, 2);
+            else if (waves == 8 && kbw == 8) Q4_GEMV4(8, 8);
+            else if (waves == 8 && kbw == 4) Q4_GEMV4(8, 4);
+            else if (waves == 8) Q4_GEMV4(8, 2);
+            else if (kbw == 8) Q4_GEMV4(16, 8);
+            else if (kbw == 4) Q4_GEMV4(16, 4);
+            else Q4_GEMV4(16, 2);
+#undef Q4_GEMV4
+            return hipGetLastError();
+        }
+    }
+    return hipErrorNotSupported;
+}
+
+}  // namespace q4k
