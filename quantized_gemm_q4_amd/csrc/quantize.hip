@@ -19,135 +19,189 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
-// INT4 quantize + pack. Each lane owns CH chunks of 8 consecutive weights
-// (16-byte loads, all issued before any compute); for each chunk the g/8
-// lanes of a group reduce min/max (or max|x|) with xor shuffles inside the
-// wavefront, so every lane of the group holds the group statistics without a
-// broadcast. A block covers CH * 2048 consecutive weights of one row (whole
-// groups). Codes leave as one 32-bit store per lane and chunk (8 nibbles,
-// even k low), so a wavefront writes 256 contiguous bytes per chunk.
-// Zero-points of neighbouring groups meet in LDS to be packed two per byte.
+// INT4 quantize + pack. Each lane owns 16 consecutive weights of one group
+// (two 16-byte loads); the g/16 lanes of a group (2, 4 or 8, inside one
+// half-row of 8 lanes) reduce the group's minimum and maximum (or max |x|)
+// with DPP lane exchanges, so every lane holds the group statistics without
+// a broadcast. A block covers 4096 consecutive weights of one row (whole
+// groups). Minimum and maximum are exact in any precision, so they are taken
+// on packed fp16 pairs and the exchanges move (min, -max) together in one
+// register.
 //
 // Codes without a division per weight: with x and the fp16 scale sf both
 // binary16 values, the exact quotient x / sf is either a tie k + 1/2 or at
-// least 2^-16 (relative) away from every tie, while x * rcp(sf) is within a
-// few ulp of it; so k = rint(x * rcp(sf)) is rint of the exact quotient
-// except at ties, and the remainder r = x - k sf (exact in one fma: both
-// terms are multiples of the same power of two and span < 24 bits) is
-// exactly +-sf/2 there, where k moves to the even neighbour. The result is
-// rint(fl(x / sf)) bit for bit (fl(x / sf) is a tie only when x / sf is).
-__device__ __forceinline__ float code_rne(float x, float sf, float inv)
+// least 2^-12 (relative) away from every tie, while x * rcp(sf) is within a
+// few ulp of it. One fma t = x * rcp(sf) + (1.5 * 2^23 + zp) therefore
+// rounds to 1.5 * 2^23 + zp + rint(x / sf) except at ties (adding the
+// integer zp cannot move a value that is not a tie across a rounding
+// boundary), and a med3 clamps t to [1.5 * 2^23, 1.5 * 2^23 + 15], whose low
+// four bits are then the code. Ties are found exactly: the remainder
+// r = x - k sf (one fma, exact: both terms are multiples of the same power of
+// two and span < 24 bits) is +-sf / 2 there, and k then moves to its even
+// neighbour. Ties are rare (a few weights in 10^4 on Gaussian weights), so
+// the fix-up runs only in wavefronts that have one. The result is
+// clamp(rint(fl(x / sf)) + zp, 0, 15) bit for bit (fl(x / sf) is a tie only
+// when x / sf is).
+
+// Lane exchange for the group reductions (DPP): CTRL 0xB1 and 0x4E swap
+// lanes 1 and 2 apart inside a quad, 0x141 mirrors each half-row of 8 lanes.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_lanes(uint32_t v)
 {
-    float k = rintf(x * inv);
-    const float r = fmaf(-k, sf, x);
-    const float half = 0.5f * sf;
-    const bool odd = fabsf(k) < 16777216.0f && (((int)k) & 1) != 0;   // |k| >= 2^24 is even
-    if (r == half && odd) k += 1.0f;
-    if (r == -half && odd) k -= 1.0f;
-    return k;
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-template <int LANES, int CH, bool SYM>
+// kMagic + rint(x / sf) for a binary16 x (see above): one fma gives it except
+// at an exact tie, where the exact remainder is +-sf/2 and k moves to the
+// even neighbour. Used per group (zero-point), not per weight.
+__device__ __forceinline__ float rint_quotient(float x, float sf, float inv, float half)
+{
+    constexpr float kMagic = 12582912.0f;
+    const float k = fmaf(x, inv, kMagic) - kMagic;
+    const float r = fmaf(-k, sf, x);
+    const bool odd = (((int)k) & 1) != 0;   // -lo / sf <= 23 for the zero-point
+    return (fabsf(r) == half && odd) ? k + (r > 0.0f ? 1.0f : -1.0f) : k;
+}
+
+template <int LPG, bool SYM>
 __global__ __launch_bounds__(kThreads) void q4_quantize_pack_kernel(
-    const uint16_t *__restrict__ W, int64_t K, int G, int chunks_per_row,
+    const uint16_t *__restrict__ W, int64_t K, int G, int blocks_per_row,
     uint8_t *__restrict__ codes, uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros)
 {
-    constexpr int GPB = kThreads / LANES;   // groups per block and chunk pass
-    constexpr int g = LANES * 8;
-    __shared__ uint8_t zp_s[GPB * CH];
+    static_assert(LPG == 2 || LPG == 4 || LPG == 8, "lanes per group");
+    constexpr int V = 16;                   // weights per lane
+    constexpr int g = LPG * V;
+    constexpr int GPB = kThreads / LPG;     // groups per block
+    constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23: integers in its binade, low bits = value
 
-    const int64_t n = blockIdx.x / chunks_per_row;
-    const int c = blockIdx.x % chunks_per_row;
+    const int64_t n = blockIdx.x / blocks_per_row;
+    const int c = blockIdx.x % blocks_per_row;
     const int t = threadIdx.x;
-    const int gi = t / LANES, li = t % LANES;
+    const int gi = t / LPG, li = t % LPG;
+    const int j = c * GPB + gi;
+    const bool valid = j < G;
+    const int64_t elem = n * K + (int64_t)j * g + li * V;
 
-    u32x4 raw[CH];
+    u32x4 raw[2];
 #pragma unroll
-    for (int p = 0; p < CH; p++) {
-        const int j = (c * CH + p) * GPB + gi;
-        raw[p] = u32x4{0u, 0u, 0u, 0u};
-        if (j < G) raw[p] = *reinterpret_cast<const u32x4 *>(W + n * K + (int64_t)j * g + li * 8);
+    for (int q = 0; q < 2; q++) {
+        raw[q] = u32x4{0u, 0u, 0u, 0u};
+        if (valid) raw[q] = *reinterpret_cast<const u32x4 *>(W + elem + 8 * q);
     }
+    // (each dword goes through a scalar first: __builtin_bit_cast of a vector
+    // element reads element 0 with this compiler)
+    half2v d[V / 2];
 #pragma unroll
-    for (int p = 0; p < CH; p++) {
-        const int j = (c * CH + p) * GPB + gi;
-        const bool valid = j < G;
-        float x[8];
+    for (int i = 0; i < V / 2; i++) {
+        const uint32_t e = raw[i >> 2][i & 3];
+        d[i] = __builtin_bit_cast(half2v, e);
+    }
+
+    // group statistics: (lo, -hi) as one fp16 pair, min-reduced over the group's lanes
+    half2v st;
+    if (SYM) {
+        half2v a = __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, d[0]) & 0x7fff7fffu);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            x[2 * i] = h2f((uint16_t)(raw[p][i] & 0xffffu));
-            x[2 * i + 1] = h2f((uint16_t)(raw[p][i] >> 16));
+        for (int i = 1; i < V / 2; i++)
+            a = __builtin_elementwise_max(a, __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, d[i]) & 0x7fff7fffu));
+        const _Float16 m = a[0] > a[1] ? a[0] : a[1];
+        st = half2v{(_Float16)0.0f, -m};
+    } else {
+        half2v mn = d[0], mx = d[0];
+#pragma unroll
+        for (int i = 1; i < V / 2; i++) {
+            mn = __builtin_elementwise_min(mn, d[i]);
+            mx = __builtin_elementwise_max(mx, d[i]);
         }
-        float lo = 0.0f, hi = 0.0f;   // SYM: hi carries max|x|
+        const _Float16 lo = mn[0] < mn[1] ? mn[0] : mn[1];
+        const _Float16 hi = mx[0] > mx[1] ? mx[0] : mx[1];
+        st = half2v{lo, -hi};
+    }
+    st = __builtin_elementwise_min(st, __builtin_bit_cast(half2v, dpp_lanes<0xB1>(__builtin_bit_cast(uint32_t, st))));
+    if (LPG >= 4)
+        st = __builtin_elementwise_min(st, __builtin_bit_cast(half2v, dpp_lanes<0x4E>(__builtin_bit_cast(uint32_t, st))));
+    if (LPG >= 8)
+        st = __builtin_elementwise_min(st, __builtin_bit_cast(half2v, dpp_lanes<0x141>(__builtin_bit_cast(uint32_t, st))));
+    const float lo = fminf((float)st[0], 0.0f);
+    const float hi = fmaxf(-(float)st[1], 0.0f);   // SYM: max |x|
+
+    const float s32 = SYM ? hi / 7.0f : (hi - lo) / 15.0f;   // IEEE division: rounded to fp16 next
+    uint16_t s16 = f2h(s32);
+    if ((s16 & 0x7fffu) == 0) s16 = 0x3c00u;   // 1.0
+    const float sf = h2f(s16);
+    const float inv = __builtin_amdgcn_rcpf(sf);
+    const float half = 0.5f * sf;
+    float zp = 8.0f;
+    if (!SYM) zp = fminf(fmaxf(rint_quotient(-lo, sf, inv, half), 0.0f), 15.0f);
+    const float mz = kMagic + zp;
+
+    // codes: kMagic + zp + rint(x / sf), ties fixed per run of 8, clamped to [0, 15]
+    float tq[V];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            if (SYM) {
-                hi = fmaxf(hi, fabsf(x[i]));
-            } else {
-                lo = fminf(lo, x[i]);
-                hi = fmaxf(hi, x[i]);
+    for (int h8 = 0; h8 < V / 8; h8++) {
+        bool tie = false;
+#pragma unroll
+        for (int i = 8 * h8; i < 8 * h8 + 8; i++) {
+            const float x = (float)d[i >> 1][i & 1];
+            tq[i] = fmaf(x, inv, mz);
+            const float r = fmaf(-(tq[i] - mz), sf, x);
+            tie |= fabsf(r) == half;
+        }
+        if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+#pragma unroll
+            for (int i = 8 * h8; i < 8 * h8 + 8; i++) {
+                const float x = (float)d[i >> 1][i & 1];
+                const float k = tq[i] - mz;
+                const float r = fmaf(-k, sf, x);
+                const bool odd = fabsf(k) < 16777216.0f && (((int)k) & 1) != 0;
+                if (fabsf(r) == half && odd) tq[i] += r > 0.0f ? 1.0f : -1.0f;
             }
         }
+    }
+    uint32_t b[V / 2];
 #pragma unroll
-        for (int off = LANES / 2; off > 0; off >>= 1) {
-            if (!SYM) lo = fminf(lo, __shfl_xor(lo, off));
-            hi = fmaxf(hi, __shfl_xor(hi, off));
-        }
-
-        const float s32 = SYM ? hi / 7.0f : (hi - lo) / 15.0f;   // IEEE division: rounded to fp16 next
-        uint16_t s16 = f2h(s32);
-        if ((s16 & 0x7fffu) == 0) s16 = 0x3c00u;   // 1.0
-        const float sf = h2f(s16);
-        const float inv = __builtin_amdgcn_rcpf(sf);
-        float zp = 8.0f;
-        if (!SYM) zp = fminf(fmaxf(code_rne(-lo, sf, inv), 0.0f), 15.0f);
-
-        uint32_t word = 0;
+    for (int p = 0; p < V / 2; p++) {
+        const uint32_t e = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(tq[2 * p], kMagic, kMagic + 15.0f));
+        const uint32_t o = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(tq[2 * p + 1], kMagic, kMagic + 15.0f));
+        b[p] = (o << 4) | e;   // low byte: code 2p | code 2p+1 << 4 (the magic's low 12 bits are 0)
+    }
+    u32x2 word;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            float q = code_rne(x[i], sf, inv);
-            if (SYM) {
-                q = fminf(fmaxf(q, -8.0f), 7.0f) + 8.0f;
-            } else {
-                q = fminf(fmaxf(q + zp, 0.0f), 15.0f);
-            }
-            word |= (uint32_t)q << (4 * i);
-        }
-        if (valid) {
-            const int64_t elem = n * K + (int64_t)j * g + li * 8;
-            *reinterpret_cast<uint32_t *>(codes + elem / 2) = word;
-            if (li == 0) scales[n * G + j] = s16;
-        }
-        if (!SYM && li == 0) zp_s[p * GPB + gi] = valid ? (uint8_t)zp : 0;
+    for (int w = 0; w < 2; w++) {
+        const uint32_t lo2 = __builtin_amdgcn_perm(b[4 * w + 1], b[4 * w], 0x0c0c0400u);
+        const uint32_t hi2 = __builtin_amdgcn_perm(b[4 * w + 3], b[4 * w + 2], 0x0c0c0400u);
+        word[w] = __builtin_amdgcn_perm(hi2, lo2, 0x05040100u);
+    }
+    if (valid) {
+        *reinterpret_cast<u32x2 *>(codes + elem / 2) = word;
+        if (li == 0) scales[n * G + j] = s16;
     }
     if (!SYM) {
-        __syncthreads();
-        const int Gz = (G + 1) / 2;
-        if (t < GPB * CH / 2) {
-            const int jz = c * (GPB * CH / 2) + t;
-            if (2 * jz < G)
-                zeros[n * Gz + jz] = (uint8_t)(zp_s[2 * t] | (zp_s[2 * t + 1] << 4));
-        }
+        // zero-points of groups 2i and 2i + 1 meet through a lane swizzle
+        // (xor LPG: the partner group's lanes); a missing last group packs 0
+        const int z = valid ? (int)zp : 0;
+        const int zo = __builtin_amdgcn_ds_swizzle(z, (LPG << 10) | 0x1F);
+        if (li == 0 && (gi & 1) == 0 && valid)
+            zeros[n * ((G + 1) / 2) + (j >> 1)] = (uint8_t)(z | (zo << 4));
     }
 }
 
-template <int LANES>
+template <int LPG>
 hipError_t launch_q4_g(const uint16_t *W, int64_t N, int64_t K, int sym, uint8_t *codes,
                        uint16_t *scales, uint8_t *zeros, hipStream_t st)
 {
-    constexpr int GPB = kThreads / LANES;
-    constexpr int CH = 2;
-    const int G = (int)(K / (LANES * 8));
-    const int chunks = (G + GPB * CH - 1) / (GPB * CH);
-    const int64_t blocks = N * chunks;
+    constexpr int GPB = kThreads / LPG;
+    const int G = (int)(K / (LPG * 16));
+    const int per_row = (G + GPB - 1) / GPB;
+    const int64_t blocks = N * per_row;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (sym)
-        q4_quantize_pack_kernel<LANES, CH, true><<<(unsigned)blocks, kThreads, 0, st>>>(
-            W, K, G, chunks, codes, scales, zeros);
+        q4_quantize_pack_kernel<LPG, true><<<(unsigned)blocks, kThreads, 0, st>>>(
+            W, K, G, per_row, codes, scales, zeros);
     else
-        q4_quantize_pack_kernel<LANES, CH, false><<<(unsigned)blocks, kThreads, 0, st>>>(
-            W, K, G, chunks, codes, scales, zeros);
+        q4_quantize_pack_kernel<LPG, false><<<(unsigned)blocks, kThreads, 0, st>>>(
+            W, K, G, per_row, codes, scales, zeros);
     return hipGetLastError();
 }
 
@@ -337,9 +391,9 @@ hipError_t launch_q4_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int 
                                    hipStream_t st)
 {
     switch (g) {
-    case 32: return launch_q4_g<4>(W, N, K, sym, codes, scales, zeros, st);
-    case 64: return launch_q4_g<8>(W, N, K, sym, codes, scales, zeros, st);
-    case 128: return launch_q4_g<16>(W, N, K, sym, codes, scales, zeros, st);
+    case 32: return launch_q4_g<2>(W, N, K, sym, codes, scales, zeros, st);
+    case 64: return launch_q4_g<4>(W, N, K, sym, codes, scales, zeros, st);
+    case 128: return launch_q4_g<8>(W, N, K, sym, codes, scales, zeros, st);
     default: return hipErrorInvalidValue;
     }
 }
