@@ -143,7 +143,8 @@ Q4_API q4_status q8_quantize_weight(const void *W, const float *smooth_s, int64_
  *   x' = x / s[k] (fp32 division; smooth_s == NULL means x' = x),
  *   x_scale[m] = max(max_k |x'|, 1e-8) / 127,
  *   Xq = clip(rne(x' / x_scale[m]), -127, 127).
- * X fp16 [M, K] (16-byte aligned); smooth_s fp32 [K] or NULL;
+ * X fp16 [M, K] (16-byte aligned); smooth_s fp32 [K] or NULL, entries finite
+ * and nonzero (others give unspecified codes);
  * Xq int8 [M, K] output (16-byte aligned); x_scale fp32 [M] output.
  * Errors: INVALID_ARG (K % 8 != 0 included), MISALIGNED, HIP.
  * -------------------------------------------------------------------------- */

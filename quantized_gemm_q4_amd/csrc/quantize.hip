@@ -11,6 +11,8 @@
 // (blog.freezetheflame.cc) §2.1 sym/asym, §2.2 per-channel/per-group, §2.3
 // quantize kernel, §5.1 SmoothQuant factor; Quantization notes
 // (learn.longtimenohack.com) item (1) group quantization.
+#include <type_traits>
+
 #include "q4_internal.hpp"
 
 namespace q4k {
@@ -209,10 +211,9 @@ hipError_t launch_q4_g(const uint16_t *W, int64_t N, int64_t K, int sym, uint8_t
 // Per-row INT8 (Operators guide §2.2 per-channel; the same arithmetic serves
 // per-token activations): row values v = x * s (weights, DIV = false) or
 // v = x / s (activations, DIV = true), scale = max(max|v|, 1e-8) / 127,
-// q = clip(rne(v / scale), -127, 127). One block per row; each lane owns
-// 8-element chunks (16-byte loads, 8-byte stores). With CPT > 0 the row's
-// values stay in registers between the max pass and the code pass
-// (K <= CPT * 2048); CPT == 0 re-reads the row.
+// q = clip(rne(v / scale), -127, 127). The generic kernel (rows wider than
+// 8192) has one block per row, IEEE divisions, and reads the row twice; each
+// lane owns 8-element chunks (16-byte loads, 8-byte stores).
 __device__ __forceinline__ float block_max(float v, float *red)
 {
 #pragma unroll
@@ -263,7 +264,7 @@ __device__ __forceinline__ u32x2 q8_codes(const float v[8], float scale)
 }
 
 template <bool DIV, int CPT>
-__global__ __launch_bounds__(kThreads) void q8_rows_kernel(const uint16_t *__restrict__ X,
+__global__ __launch_bounds__(kThreads) void q8_rows_generic_kernel(const uint16_t *__restrict__ X,
                                                           const float *__restrict__ s,
                                                           int64_t K, int8_t *__restrict__ Q,
                                                           float *__restrict__ scale_out)
@@ -310,22 +311,165 @@ __global__ __launch_bounds__(kThreads) void q8_rows_kernel(const uint16_t *__res
     }
 }
 
+// Quotients without a division. For binary32 (or binary16-valued) a and a
+// binary32 b the exact quotient a / b never lies on the midpoint between two
+// binary32 neighbours, and when it does not it is at least 2^-47 (relative)
+// away from one: a - m b, for a midpoint m, is a multiple of a power of two
+// that is at least 2^-48 of a. So a product a * r in fp64 with r within
+// 2^-50 of 1 / b (relative) rounds to the same binary32 value as a / b:
+// fl32(fl64(a * r)) = fl32(a / b). r is the hardware's fp64 reciprocal
+// refined by two Newton steps (each squares the relative error; rounding
+// keeps it near 2^-53). b must be finite and nonzero.
+__device__ __forceinline__ double recip64(double b)
+{
+    double r = __builtin_amdgcn_rcp(b);
+    r = fma(fma(-b, r, 1.0), r, r);
+    return fma(fma(-b, r, 1.0), r, r);
+}
+
+// max over each half-wavefront (lanes 0-31 and 32-63 each end with their own):
+// DPP quad swaps, half-row and row mirrors, then a lane swizzle across 16
+__device__ __forceinline__ float halfwave_max(float a)
+{
+    auto dpp = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    a = fmaxf(a, dpp(a, std::integral_constant<int, 0xB1>{}));
+    a = fmaxf(a, dpp(a, std::integral_constant<int, 0x4E>{}));
+    a = fmaxf(a, dpp(a, std::integral_constant<int, 0x141>{}));
+    a = fmaxf(a, dpp(a, std::integral_constant<int, 0x140>{}));
+    return fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, a), (16 << 10) | 0x1F)));
+}
+
+// Per-row INT8 for rows of at most 8192 values: a block of T threads owns
+// RPB rows and each thread the same CPT chunks of 8 columns in every row, so
+// the per-column factor (the fp64 reciprocal of s for activations, s itself
+// for weights) is formed once per block. Every load is issued up front and
+// none is conditional (rows past M and chunks past K read clamped, valid
+// addresses and are masked afterwards), so the compiler's waits stay partial
+// and row rr is worked on as soon as its own bytes have landed. Per row: the
+// values v, the block's max |v| (one LDS slot per row, one barrier), the
+// scale by an IEEE fp32 division, and the codes rint(fl32(v / scale)) from
+// one fp64 multiply.
+template <bool DIV, bool HAS_S, int CPT, int RPB, int T>
+__global__ __launch_bounds__(T) void q8_rows_kernel(const uint16_t *__restrict__ X,
+                                                    const float *__restrict__ s, int64_t M,
+                                                    int64_t K, int8_t *__restrict__ Q,
+                                                    float *__restrict__ scale_out)
+{
+    constexpr int HW = T / 32;   // half-wavefronts per block
+    __shared__ float red[RPB][HW];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t r0 = (int64_t)blockIdx.x * RPB;
+    constexpr int64_t step = (int64_t)T * 8;
+
+    int64_t kc[CPT];
+    bool kin[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; c++) {
+        const int64_t k0 = t * 8 + c * step;
+        kin[c] = k0 < K;
+        kc[c] = kin[c] ? k0 : K - 8;
+    }
+    // the column factors first (they are needed first), then the rows in order
+    floatx4 slo[CPT], shi[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; c++) {
+        slo[c] = floatx4{1.f, 1.f, 1.f, 1.f};
+        shi[c] = floatx4{1.f, 1.f, 1.f, 1.f};
+        if (HAS_S) {
+            slo[c] = *reinterpret_cast<const floatx4 *>(s + kc[c]);
+            shi[c] = *reinterpret_cast<const floatx4 *>(s + kc[c] + 4);
+        }
+    }
+    u32x4 raw[RPB][CPT];
+#pragma unroll
+    for (int rr = 0; rr < RPB; rr++) {
+        const int64_t r = r0 + rr < M ? r0 + rr : M - 1;
+#pragma unroll
+        for (int c = 0; c < CPT; c++) raw[rr][c] = *reinterpret_cast<const u32x4 *>(X + r * K + kc[c]);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the arithmetic
+    float sv[CPT][8];
+    double rd[CPT][8];
+#pragma unroll
+    for (int c = 0; c < CPT; c++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            sv[c][i] = slo[c][i];
+            sv[c][4 + i] = shi[c][i];
+        }
+        if (DIV && HAS_S) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) rd[c][i] = recip64((double)sv[c][i]);
+        }
+    }
+
+#pragma unroll
+    for (int rr = 0; rr < RPB; rr++) {
+        float v[CPT][8];
+        float a = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPT; c++) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const uint32_t d = raw[rr][c][i >> 1];
+                const float x = h2f((uint16_t)((i & 1) ? (d >> 16) : (d & 0xffffu)));
+                if (!HAS_S) v[c][i] = x;
+                else if (DIV) v[c][i] = (float)((double)x * rd[c][i]);   // fl32(x / s)
+                else v[c][i] = x * sv[c][i];
+            }
+            float m = fmaxf(fmaxf(fabsf(v[c][0]), fabsf(v[c][1])), fabsf(v[c][2]));
+            m = fmaxf(fmaxf(m, fabsf(v[c][3])), fabsf(v[c][4]));
+            m = fmaxf(fmaxf(m, fabsf(v[c][5])), fabsf(v[c][6]));
+            m = fmaxf(m, fabsf(v[c][7]));
+            if (kin[c]) a = fmaxf(a, m);   // chunks past K hold a clamped copy: not counted
+        }
+        a = halfwave_max(a);
+        if ((lane & 31) == 0) red[rr][wave * 2 + (lane >> 5)] = a;
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < HW; h += 4) {
+            const floatx4 m = *reinterpret_cast<const floatx4 *>(&red[rr][h]);
+            a = fmaxf(a, fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
+        }
+        a = fmaxf(a, 1e-8f);
+        const float scale = a / 127.0f;
+        const double rs = recip64((double)scale);
+        const int64_t r = r0 + rr;
+        if (r < M) {
+#pragma unroll
+            for (int c = 0; c < CPT; c++) {
+                u32x2 out = {0u, 0u};
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const float q = fminf(fmaxf(rintf((float)((double)v[c][i] * rs)), -127.0f), 127.0f);
+                    out[i / 4] |= ((uint32_t)(int32_t)q & 0xffu) << (8 * (i % 4));
+                }
+                if (kin[c]) *reinterpret_cast<u32x2 *>(Q + r * K + kc[c]) = out;
+            }
+            if (t == 0) scale_out[r] = scale;
+        }
+    }
+}
+
 template <bool DIV>
 hipError_t launch_q8_rows(const uint16_t *X, const float *s, int64_t rows, int64_t K, int8_t *Q,
                           float *scale, hipStream_t st)
 {
     if (rows == 0) return hipSuccess;
     if (rows > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const int64_t per = (int64_t)kThreads * 8;
-    const int64_t cpt = (K + per - 1) / per;
-    const unsigned grid = (unsigned)rows;
-    switch (cpt) {
-    case 1: q8_rows_kernel<DIV, 1><<<grid, kThreads, 0, st>>>(X, s, K, Q, scale); break;
-    case 2: q8_rows_kernel<DIV, 2><<<grid, kThreads, 0, st>>>(X, s, K, Q, scale); break;
-    case 3:
-    case 4: q8_rows_kernel<DIV, 4><<<grid, kThreads, 0, st>>>(X, s, K, Q, scale); break;
-    default: q8_rows_kernel<DIV, 0><<<grid, kThreads, 0, st>>>(X, s, K, Q, scale); break;
-    }
+    constexpr int RPB = 4, T = 512;
+    const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
+    if (K <= 4096) {
+        if (s) q8_rows_kernel<DIV, true, 1, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
+        else q8_rows_kernel<DIV, false, 1, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
+    } else if (K <= 8192) {
+        if (s) q8_rows_kernel<DIV, true, 2, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
+        else q8_rows_kernel<DIV, false, 2, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
+    } else   // wider rows: one row per block, the row read twice
+        q8_rows_generic_kernel<DIV, 0><<<(unsigned)rows, kThreads, 0, st>>>(X, s, K, Q, scale);
     return hipGetLastError();
 }
 
