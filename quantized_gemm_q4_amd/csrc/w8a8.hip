@@ -133,13 +133,19 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_gemm_kernel(
 // touches fall in distinct banks.
 //
 // MFMA output layout: lane l holds column l % 32 and rows
-// 8 (r / 4) + 4 (l / 32) + r % 4 of its 32 x 32 tile.
+// 8 (r / 4) + 4 (l / 32) + r % 4 of its 32 x 32 tile. In that layout a lane
+// can only store 2 bytes at a time, in 64-byte runs; so the epilogue scales
+// the accumulators in registers, stages the block's 256 x 256 fp16 tile in
+// the (then free) LDS and writes it back as whole rows with 16-byte stores
+// (about 20 us less than direct stores at 2048 x 8192).
 //
 // Tile order is XCD-aware: consecutive block ids go to the 8 XCDs in turn, so
 // block b computes tile t = (b % 8) * (blocks / 8) + b / 8; each XCD then owns
 // whole columns of N-tiles, and its L2 serves their reuse of the W tiles.
 constexpr int LBM = 256, LBN = 256, LBK = 64, LSTAGES = 4;
 constexpr int LSTAGE_BYTES = (LBM + LBN) * LBK;   // 32 KB
+constexpr int OUT_STRIDE = LBN * 2 + 16;            // bytes per row of the staged fp16 output tile
+constexpr int LDS_BYTES = LBM * OUT_STRIDE > LSTAGES * LSTAGE_BYTES ? LBM * OUT_STRIDE : LSTAGES * LSTAGE_BYTES;
 
 
 __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
@@ -147,11 +153,8 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
     const float *__restrict__ sw, int M, int N, int K, int tiles_m, uint16_t *__restrict__ Y,
     int32_t *__restrict__ acc_out)
 {
-    __shared__ __attribute__((aligned(1024))) int8_t st0[LSTAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) int8_t st1[LSTAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) int8_t st2[LSTAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) int8_t st3[LSTAGE_BYTES];
-    int8_t *const stages[LSTAGES] = {st0, st1, st2, st3};
+    __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
+    int8_t *const stages[LSTAGES] = {lds, lds + LSTAGE_BYTES, lds + 2 * LSTAGE_BYTES, lds + 3 * LSTAGE_BYTES};
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
@@ -277,26 +280,61 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
         }
     }
     Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
-
+    if (acc_out) {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const int n = n0 + wn * 64 + j * 32 + l32;
+                    if (m < M && n < N) acc_out[(int64_t)m * N + n] = acc[i][j][r];
+                }
+            }
+    }
+    // Epilogue: y = f2h((acc * sx[m]) * sw[n]) in the MFMA layout, staged
+    // through LDS as the block's 256 x 256 fp16 tile, then written back as
+    // whole rows with 16-byte stores.
+    __syncthreads();   // every wavefront is done with the stages
+    float swv[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int n = n0 + wn * 64 + j * 32 + l32;
+        swv[j] = sw[n < N ? n : N - 1];
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-            const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (m >= M) continue;
-            const float xs = sx[m];
+            const int ml = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int m = m0 + ml;
+            const float xs = sx[m < M ? m : M - 1];
 #pragma unroll
             for (int j = 0; j < 2; j++) {
-                const int n = n0 + wn * 64 + j * 32 + l32;
-                if (n >= N) continue;
-                const int32_t a = acc[i][j][r];
-                if (acc_out) acc_out[(int64_t)m * N + n] = a;
-                float f = (float)a * xs;
-                f = f * sw[n];
-                asm volatile("" : "+v"(f));   // keep the fp32 product (see the small kernel)
-                Y[(int64_t)m * N + n] = f2h(f);
+                float f = (float)acc[i][j][r] * xs;
+                f = f * swv[j];
+                asm volatile("" : "+v"(f));
+                *reinterpret_cast<uint16_t *>(lds + ml * OUT_STRIDE + (wn * 64 + j * 32 + l32) * 2) = f2h(f);
             }
         }
+    __syncthreads();
+    // wavefront w writes rows 32 w .. 32 w + 31, two rows per instruction;
+    // 16-byte stores need every row start 16-byte aligned
+    const bool vec_ok = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+#pragma unroll 4
+    for (int it = 0; it < 16; it++) {
+        const int ml = wave * 32 + 2 * it + (lane >> 5);
+        const int cl = (lane & 31) * 8;
+        const int m = m0 + ml, n = n0 + cl;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + ml * OUT_STRIDE + cl * 2);
+        if (m < M && n + 8 <= N && vec_ok) *reinterpret_cast<u32x4 *>(Y + (int64_t)m * N + n) = v;
+        else if (m < M) {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                if (n + e < N) Y[(int64_t)m * N + n + e] = (uint16_t)(v[e / 2] >> (16 * (e & 1)));
+        }
+    }
 }
 
 }  // namespace
