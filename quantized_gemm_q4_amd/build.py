@@ -61,6 +61,17 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
+        # a kernel whose host launch stub went missing shows up as an undefined
+        # library-internal symbol; fail here rather than at load time
+        try:
+            und = subprocess.run(["nm", "-D", "--undefined-only", tmp_lib], check=True,
+                                 capture_output=True, text=True).stdout
+        except (OSError, subprocess.CalledProcessError):
+            und = ""
+        missing = [ln.split()[-1] for ln in und.splitlines() if "q4k" in ln]
+        if missing:
+            os.remove(tmp_lib)
+            raise RuntimeError("HIP build left undefined internal symbols: " + ", ".join(missing))
         os.replace(tmp_lib, LIB)
     return LIB
 

@@ -279,6 +279,320 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Batched decode, 1 < M <= 64, g = 128. A block of 4 wavefronts owns 64
+// output channels; wavefront w owns 16 of them (one MFMA column tile) across
+// all of K, so no wavefront waits on another's partial sums. X is the operand
+// all four share: one k-block of it (16 MT rows x 128 k, rows past M repeat
+// row M - 1) at a time goes straight from global memory into an R-slot LDS
+// ring with direct-to-LDS loads issued R - 1 k-blocks ahead; its 16-byte
+// chunks are XOR-swizzled (chunk c of row m at c ^ (m % 16)) so the
+// fragment reads, 16 rows of one chunk, are conflict-free. Each wavefront
+// streams its own code runs, scales and zero-points through a DC-deep
+// register ring. One barrier per k-block: before it every wavefront waits
+// for its share of the k-block's X (the wait counts are fixed: past the end
+// the last k-block is fetched again into slots nobody reads).
+// Natural k order: lane (r16, q) takes k = 32 q .. 32 q + 31 of each k-block
+// for both operands; MFMA step t pairs dword t of its code run with
+// X[m][32 q + 8 t .. + 7]. Unpack (exact, natural order, 3 operations per
+// pair): v_perm copies byte p of a code dword into bytes 0 and 2, one
+// v_and_or lifts its low nibble to bit 0 of the low fp16 half (1024 + u0) and
+// its high nibble to bit 4 of the high half (1024 + 16 u1), and one packed fma
+// with (1, 1/16) and (-(1024 + zp), -(64 + zp)) leaves (u0 - zp, u1 - zp).
+// Each product x (u - zp) is exact in fp32; the fp32 partial sum of a k-block
+// is scaled by its group scale in fp32.
+__device__ __forceinline__ uint32_t unpack_pair(uint32_t w, int p, uint32_t zadd)
+{
+    const uint32_t t = __builtin_amdgcn_perm(w, w, 0x01010101u * (uint32_t)p);
+    const half2v x = __builtin_bit_cast(half2v, and_or(t, 0x00F0000Fu, 0x64006400u));
+    const half2v mul = __builtin_bit_cast(half2v, 0x2C003C00u);   // (1, 1/16)
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(x, mul, __builtin_bit_cast(half2v, zadd)));
+}
+
+template <int MT, int KS, int R, int DC, bool ASYM>
+__global__ __launch_bounds__(256 * KS) void w4a16_batched_kernel(
+    const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    uint16_t *__restrict__ Y)
+{
+    static_assert(MT <= 4 && R <= 4 && DC <= 16 && KS * R * MT <= 32, "ring sizes");
+    constexpr int SLOT = MT * 16 * 256;          // bytes of one k-block of X
+    constexpr int LPC = ASYM ? 3 : 2;            // loads per code-ring refill
+    // (fixed-size arrays: arrays sized by a template parameter and captured by
+    // the lambdas below make this compiler drop the kernel's host stub)
+    __shared__ __attribute__((aligned(1024))) unsigned char xs[32 * 16 * 256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave & 3, ks = wave >> 2;     // column tile, k-split group
+    const int r16 = lane & 15, q = lane >> 4;
+    const int KBS = (K >> 7) / KS;               // k-blocks per group
+    const int kbase = ks * KBS;
+    // every block walks its k-blocks from a different start, so that at any
+    // moment the blocks read different parts of X (all starting at the same
+    // k-block would put every block on the same few L2 lines at once)
+    const int rot = (int)(blockIdx.x % (unsigned)KBS);
+    auto kblock = [&](int kb) {   // iteration -> global k-block (kb may be past the end)
+        const int kk = (kb < KBS ? kb : KBS - 1) + rot;
+        return kbase + (kk < KBS ? kk : kk - KBS);
+    };
+    const uint32_t G = (uint32_t)(K >> 7), Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
+    const int n = blockIdx.x * 64 + wn * 16 + r16;
+    const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
+    unsigned char *ring = xs + ks * R * SLOT;
+
+    // direct-to-LDS X loads: instruction j of wavefront wn fills rows
+    // 4 (4 j + wn) .. + 3 of a slot; lane i: row 4 (4 j + wn) + i / 16, stored
+    // chunk i % 16, logical chunk (i % 16) ^ (row % 16)
+    uint32_t xoff[4];
+#pragma unroll
+    for (int j = 0; j < MT; j++) {
+        const int m = 4 * (4 * j + wn) + (lane >> 4);
+        const int c = (lane & 15) ^ (m & 15);
+        xoff[j] = ((uint32_t)(m < M ? m : M - 1) * (uint32_t)K + 8u * (uint32_t)c) * 2u;
+    }
+    const unsigned char *Xb = reinterpret_cast<const unsigned char *>(X);
+    auto issue_x = [&](int kb) {   // kb >= 0: the group's kb-th iteration
+        const int kc = kblock(kb);
+        unsigned char *slot = ring + (kb % R) * SLOT;
+#pragma unroll
+        for (int j = 0; j < MT; j++)
+            __builtin_amdgcn_global_load_lds(Xb + xoff[j] + (uint32_t)kc * 256u, slot + (4 * j + wn) * 1024,
+                                             16, 0, 0);
+    };
+    u32x4 cw[16];
+    uint32_t sc[16], zb[16];
+    auto issue_w = [&](int kb) {
+        const int kc = kblock(kb);
+        cw[kb % DC] = *reinterpret_cast<const u32x4 *>(codes + (nrow * kh + (uint32_t)kc * 64u + q * 16u));
+        sc[kb % DC] = scales[nrow * G + kc];
+        if (ASYM) zb[kb % DC] = zeros[nrow * Gz + (kc >> 1)];
+    };
+    auto wait_x = [&]() {   // this wavefront's share of the oldest X slot has landed
+        asm volatile("" ::: "memory");
+        Q4_WAIT_VM_LGKM0(LPC + (R - 2) * (MT + LPC));
+    };
+
+    floatx4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // One issue step per k-block: X of k-block i + R - 1, then the code run,
+    // scale and zero-point of k-block i + DC - 1, in that order (the fences
+    // keep the compiler from reordering the two groups, which the fixed wait
+    // counts rely on). The prologue runs the same steps for i = -(DC - 1) ..
+    // -1 (X indices below 0 fetch k-block 0 into slot 0 again), so the loop
+    // head sees one pattern of outstanding loads from both sides.
+    auto step_issue = [&](int i) {
+        asm volatile("" ::: "memory");
+        issue_x(i + R - 1 < 0 ? 0 : i + R - 1);
+        asm volatile("" ::: "memory");
+        issue_w(i + DC - 1);
+        asm volatile("" ::: "memory");
+    };
+#pragma unroll
+    for (int i = -(DC - 1); i < 0; i++) step_issue(i);
+    // the group's k-blocks are a multiple of DC (and DC of R): ring slots are
+    // compile-time; every group runs the same number of steps, so the block
+    // barrier serves all of them
+    for (int kb0 = 0; kb0 < KBS; kb0 += DC) {
+#pragma unroll
+        for (int u = 0; u < DC; u++) {
+            const int kb = kb0 + u;
+            wait_x();
+            __builtin_amdgcn_s_barrier();
+            step_issue(kb);
+            const unsigned char *slot = ring + (kb % R) * SLOT;
+            const int kg = kblock(kb);
+            const uint32_t zp = ASYM ? (zb[u] >> (4 * (kg & 1))) & 15u : 8u;
+            const uint32_t zadd = (0xE400u + zp) | ((0xD400u + 16u * zp) << 16);   // 1 at 1024, 1/16 at 64
+            floatx4 part[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) part[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint32_t w = cw[u][t];
+                const u32x4 bv = {unpack_pair(w, 0, zadd), unpack_pair(w, 1, zadd),
+                                  unpack_pair(w, 2, zadd), unpack_pair(w, 3, zadd)};
+                const half8 b = __builtin_bit_cast(half8, bv);
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++) {
+                    const int m = mt * 16 + r16;
+                    const half8 a = *reinterpret_cast<const half8 *>(slot + m * 256 + 16 * ((4 * q + t) ^ r16));
+                    part[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, part[mt], 0, 0, 0);
+                }
+            }
+            const float s = h2f((uint16_t)sc[u]);
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[mt][r] = fmaf(part[mt][r], s, acc[mt][r]);
+        }
+    }
+    Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
+
+    if (KS > 1) {
+        // the k-split groups' partial sums meet in LDS (group order fixed)
+        float *red = reinterpret_cast<float *>(xs);   // [KS - 1][4 wn][MT * 4][64]
+        __syncthreads();
+        if (ks > 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) red[(((ks - 1) * 4 + wn) * MT * 4 + mt * 4 + r) * 64 + lane] = acc[mt][r];
+        }
+        __syncthreads();
+        if (ks > 0) return;
+#pragma unroll
+        for (int g2 = 1; g2 < KS; g2++)
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[mt][r] += red[(((g2 - 1) * 4 + wn) * MT * 4 + mt * 4 + r) * 64 + lane];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int m = mt * 16 + 4 * q + r;
+            if (m < M && n < N) Y[(int64_t)m * N + n] = f2h(acc[mt][r]);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Batched decode with X resident in LDS (16 MT rows x K fp16 <= 128 KB; in
+// practice M <= 16 at K <= 4096). Same block shape, operand order, unpack
+// and swizzle as w4a16_batched_kernel, but all of X is loaded once (each
+// k-split group its own part, direct to LDS), then every code run, scale and
+// zero-point of the wavefront's KBW k-blocks; one wait and one barrier make
+// X visible, and from there the only waits are the compiler's, in issue
+// order, on the code runs. (With a ring, every wait for an X slot would also
+// wait for all code loads issued before it: memory loads complete in order,
+// so the code prefetch could run no deeper than the X ring.)
+template <int MT, int KS, int KBW, bool ASYM>
+__global__ __launch_bounds__(256 * KS) void w4a16_batched_xres_kernel(
+    const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    uint16_t *__restrict__ Y)
+{
+    static_assert(KS * KBW * MT <= 32, "X must fit the 128 KB of LDS");
+    constexpr int SLOT = MT * 16 * 256;          // bytes of one k-block of X
+    __shared__ __attribute__((aligned(1024))) unsigned char xs[32 * 16 * 256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave & 3, ks = wave >> 2;     // column tile, k-split group
+    const int r16 = lane & 15, q = lane >> 4;
+    const int kbase = ks * KBW;
+    const uint32_t G = (uint32_t)(K >> 7), Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
+    const int n = blockIdx.x * 64 + wn * 16 + r16;
+    const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
+
+    // X: slot kb holds k-block kb of all 16 MT rows; instruction j of
+    // wavefront wn fills rows 4 (4 j + wn) .. + 3; lane i: row 4 (4 j + wn) +
+    // i / 16, stored chunk i % 16, logical chunk (i % 16) ^ (row % 16)
+    const unsigned char *Xb = reinterpret_cast<const unsigned char *>(X);
+#pragma unroll
+    for (int j = 0; j < MT; j++) {
+        const int m = 4 * (4 * j + wn) + (lane >> 4);
+        const int c = (lane & 15) ^ (m & 15);
+        const uint32_t xoff = ((uint32_t)(m < M ? m : M - 1) * (uint32_t)K + 8u * (uint32_t)c) * 2u;
+#pragma unroll
+        for (int p = 0; p < KBW; p++)
+            __builtin_amdgcn_global_load_lds(Xb + xoff + (uint32_t)(kbase + p) * 256u,
+                                             xs + (kbase + p) * SLOT + (4 * j + wn) * 1024, 16, 0, 0);
+    }
+    // then the scales and zero-points (needed first), then the code runs
+    asm volatile("" ::: "memory");
+    uint32_t sraw[KBW / 2], zraw = 0x88888888u;
+    {
+        const uint16_t *sp = scales + (nrow * G + kbase);
+        if constexpr (KBW == 8) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(sp);
+#pragma unroll
+            for (int i = 0; i < 4; i++) sraw[i] = v[i];
+        } else if constexpr (KBW == 4) {
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(sp);
+            sraw[0] = v[0];
+            sraw[1] = v[1];
+        } else {
+            sraw[0] = *reinterpret_cast<const uint32_t *>(sp);
+        }
+        if (ASYM) {
+            const uint8_t *zpp = zeros + (nrow * Gz + (kbase >> 1));
+            if constexpr (KBW == 8) zraw = *reinterpret_cast<const uint32_t *>(zpp);
+            else if constexpr (KBW == 4) zraw = *reinterpret_cast<const uint16_t *>(zpp);
+            else zraw = *zpp;
+        }
+    }
+    asm volatile("" ::: "memory");
+    u32x4 cw[KBW];
+#pragma unroll
+    for (int p = 0; p < KBW; p++)
+        cw[p] = *reinterpret_cast<const u32x4 *>(codes + (nrow * kh + (uint32_t)(kbase + p) * 64u + q * 16u));
+    // X landed (everything issued after it may still be in flight), then the
+    // whole block's X is visible after the barrier
+    asm volatile("" ::: "memory");
+    Q4_WAIT_VM_LGKM0(KBW + 1 + (ASYM ? 1 : 0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    floatx4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < KBW; p++) {
+        const unsigned char *slot = xs + (kbase + p) * SLOT;
+        const uint32_t zp = (zraw >> (4 * p)) & 15u;
+        const uint32_t zadd = (0xE400u + zp) | ((0xD400u + 16u * zp) << 16);   // 1 at 1024, 1/16 at 64
+        floatx4 part[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) part[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const uint32_t w = cw[p][t];
+            const u32x4 bv = {unpack_pair(w, 0, zadd), unpack_pair(w, 1, zadd),
+                              unpack_pair(w, 2, zadd), unpack_pair(w, 3, zadd)};
+            const half8 b = __builtin_bit_cast(half8, bv);
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+                const int m = mt * 16 + r16;
+                const half8 a = *reinterpret_cast<const half8 *>(slot + m * 256 + 16 * ((4 * q + t) ^ r16));
+                part[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, part[mt], 0, 0, 0);
+            }
+        }
+        const uint32_t sw = sraw[p >> 1];
+        const float s = h2f((uint16_t)((p & 1) ? (sw >> 16) : (sw & 0xffffu)));
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[mt][r] = fmaf(part[mt][r], s, acc[mt][r]);
+    }
+
+    if (KS > 1) {
+        // the k-split groups' partial sums meet in LDS (group order fixed)
+        float *red = reinterpret_cast<float *>(xs);   // [KS - 1][4 wn][MT * 4][64]
+        __syncthreads();
+        if (ks > 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) red[(((ks - 1) * 4 + wn) * MT * 4 + mt * 4 + r) * 64 + lane] = acc[mt][r];
+        }
+        __syncthreads();
+        if (ks > 0) return;
+#pragma unroll
+        for (int g2 = 1; g2 < KS; g2++)
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[mt][r] += red[(((g2 - 1) * 4 + wn) * MT * 4 + mt * 4 + r) * 64 + lane];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int m = mt * 16 + 4 * q + r;
+            if (m < M && n < N) Y[(int64_t)m * N + n] = f2h(acc[mt][r]);
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Large-M GEMM (prefill), M >= 256, g a power of two >= 128. Compute bound.
 //
 // A block of 8 / WM wavefronts owns a 256 x (32 NU) tile of Y; wavefront w
@@ -502,6 +816,51 @@ hipError_t launch_skinny(const uint16_t *X, int M, int N, int K, int g, const ui
     return hipGetLastError();
 }
 
+// Batched decode launcher (g = 128 assumed). K is split over KS groups of
+// wavefronts inside a block; each group's k-blocks must be a multiple of the
+// code ring depth.
+hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t *codes,
+                          const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
+                          hipStream_t st)
+{
+    if (M < 1 || M > 64 || K % 128 != 0) return hipErrorNotSupported;
+    const int KB = K / 128;
+    const int blocks = (N + 63) / 64;
+    // X resident in LDS: 16 rows x K fp16 within 128 KB, 4 k-split groups of
+    // 2, 4 or 8 k-blocks each, whole-run vector loads of scales / zero-points
+    if (M <= 16 && (KB == 8 || KB == 16 || KB == 32)) {
+        const int kbw = KB / 4;
+        const int Gz = (KB + 1) / 2;
+        const bool aligned = (reinterpret_cast<uintptr_t>(scales) & (kbw * 2 - 1)) == 0 &&
+                             (!zeros || ((reinterpret_cast<uintptr_t>(zeros) & (kbw / 2 - 1)) == 0 &&
+                                         Gz % (kbw / 2) == 0));
+        if (aligned) {
+            auto go = [&](auto kernel) { kernel<<<blocks, 1024, 0, st>>>(X, M, N, K, codes, scales, zeros, Y); };
+            if (kbw == 8) zeros ? go(w4a16_batched_xres_kernel<1, 4, 8, true>) : go(w4a16_batched_xres_kernel<1, 4, 8, false>);
+            else if (kbw == 4) zeros ? go(w4a16_batched_xres_kernel<1, 4, 4, true>) : go(w4a16_batched_xres_kernel<1, 4, 4, false>);
+            else zeros ? go(w4a16_batched_xres_kernel<1, 4, 2, true>) : go(w4a16_batched_xres_kernel<1, 4, 2, false>);
+            return hipGetLastError();
+        }
+    }
+    auto launch = [&](auto kernel, int ks) {
+        kernel<<<blocks, 256 * ks, 0, st>>>(X, M, N, K, codes, scales, zeros, Y);
+    };
+#define Q4_B(MT, KS, DC)                                                                    \
+    (zeros ? launch(w4a16_batched_kernel<MT, KS, 4, DC, true>, KS)                          \
+           : launch(w4a16_batched_kernel<MT, KS, 4, DC, false>, KS))
+    if (M <= 32) {   // 16 wavefronts: four k-split groups
+        if (KB % 32 == 0) M <= 16 ? Q4_B(1, 4, 8) : Q4_B(2, 4, 8);
+        else if (KB % 16 == 0) M <= 16 ? Q4_B(1, 4, 4) : Q4_B(2, 4, 4);
+        else return hipErrorNotSupported;
+    } else {         // 8 wavefronts: two k-split groups (the X rings need 2 x 64 KB)
+        if (KB % 32 == 0) Q4_B(4, 2, 16);
+        else if (KB % 16 == 0) Q4_B(4, 2, 8);
+        else return hipErrorNotSupported;
+    }
+#undef Q4_B
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,
@@ -540,6 +899,10 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
         else if (best == 8) asym ? launch(w4a16_gemm_kernel<8, 2, true>, 256) : launch(w4a16_gemm_kernel<8, 2, false>, 256);
         else asym ? launch(w4a16_gemm_kernel<11, 1, true>, 512) : launch(w4a16_gemm_kernel<11, 1, false>, 512);
         return hipGetLastError();
+    }
+    if (g == 128 && M <= 64) {
+        const hipError_t e = launch_batched(X, m, n, k, codes, scales, zeros, Y, st);
+        if (e != hipErrorNotSupported) return e;
     }
     if (M <= 16) return launch_skinny<1, 1, 8>(X, m, n, k, g, codes, scales, zeros, Y, st);
     if (M <= 32) return launch_skinny<2, 2, 4>(X, m, n, k, g, codes, scales, zeros, Y, st);
