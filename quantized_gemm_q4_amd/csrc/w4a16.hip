@@ -818,7 +818,7 @@ hipError_t launch_skinny(const uint16_t *X, int M, int N, int K, int g, const ui
 
 // Batched decode launcher (g = 128 assumed). K is split over KS groups of
 // wavefronts inside a block; each group's k-blocks must be a multiple of the
-// code ring depth.
+// ring depth.
 hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t *codes,
                           const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
                           hipStream_t st)
@@ -845,17 +845,18 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t 
     auto launch = [&](auto kernel, int ks) {
         kernel<<<blocks, 256 * ks, 0, st>>>(X, M, N, K, codes, scales, zeros, Y);
     };
-#define Q4_B(MT, KS, DC)                                                                    \
-    (zeros ? launch(w4a16_batched_kernel<MT, KS, 4, DC, true>, KS)                          \
-           : launch(w4a16_batched_kernel<MT, KS, 4, DC, false>, KS))
-    if (M <= 32) {   // 16 wavefronts: four k-split groups
-        if (KB % 32 == 0) M <= 16 ? Q4_B(1, 4, 8) : Q4_B(2, 4, 8);
-        else if (KB % 16 == 0) M <= 16 ? Q4_B(1, 4, 4) : Q4_B(2, 4, 4);
+#define Q4_B(MT, KS)                                                                        \
+    (zeros ? launch(w4a16_batched_kernel<MT, KS, 4, 4, true>, KS)                           \
+           : launch(w4a16_batched_kernel<MT, KS, 4, 4, false>, KS))
+    // X ring and code ring equally deep (4): loads complete in order, so a
+    // deeper code ring would only wait behind the X slots anyway
+    if (M <= 16) {   // 16 wavefronts: four k-split groups
+        if (KB % 16 == 0) Q4_B(1, 4);
         else return hipErrorNotSupported;
-    } else {         // 8 wavefronts: two k-split groups (the X rings need 2 x 64 KB)
-        if (KB % 32 == 0) Q4_B(4, 2, 16);
-        else if (KB % 16 == 0) Q4_B(4, 2, 8);
-        else return hipErrorNotSupported;
+    } else {         // 8 wavefronts: two k-split groups
+        if (KB % 8 != 0) return hipErrorNotSupported;
+        if (M <= 32) Q4_B(2, 2);
+        else Q4_B(4, 2);
     }
 #undef Q4_B
     return hipGetLastError();

@@ -178,12 +178,13 @@ def test_gemv_variants(orc, M, N, K, sym):
     run_case(orc, W, X, 128, sym, what=f"gemv M={M} N={N} K={K} sym={sym}")
 
 
-# Shapes that route to each variant of the batched-decode kernel (8 <= M <= 64
-# here; K a multiple of 1024): row tiles of 16, 32 and 64 (M = 8, 16 / 20, 32
-# / 33, 64), code rings of 8 (K = 1024, 3072) and 16 k-blocks (K = 2048, 4096),
-# ragged M and N (the last block's columns run past N).
+# Shapes that route to each variant of the batched-decode kernels (8 <= M <=
+# 64): X resident in LDS (M <= 16, K = 1024, 2048, 4096), the X ring with row
+# tiles of 16 (M <= 16, K = 6144), 32 (M = 20) and 64 (M = 33, 64), the
+# skinny fallback (M <= 16, K = 3072); ragged M and N (the last block's
+# columns run past N).
 @pytest.mark.parametrize("M", [8, 16, 20, 33, 64])
-@pytest.mark.parametrize("K", [1024, 2048, 3072, 4096])
+@pytest.mark.parametrize("K", [1024, 2048, 3072, 4096, 6144])
 @pytest.mark.parametrize("sym", [False, True])
 def test_batched_variants(orc, M, K, sym):
     N = 300
