@@ -457,45 +457,47 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Batched decode with X resident in LDS (16 MT rows x K fp16 <= 128 KB; in
-// practice M <= 16 at K <= 4096). Same block shape, operand order, unpack
-// and swizzle as w4a16_batched_kernel, but all of X is loaded once (each
-// k-split group its own part, direct to LDS), then every code run, scale and
-// zero-point of the wavefront's KBW k-blocks; one wait and one barrier make
-// X visible, and from there the only waits are the compiler's, in issue
-// order, on the code runs. (With a ring, every wait for an X slot would also
-// wait for all code loads issued before it: memory loads complete in order,
-// so the code prefetch could run no deeper than the X ring.)
-template <int MT, int KS, int KBW, bool ASYM>
-__global__ __launch_bounds__(256 * KS) void w4a16_batched_xres_kernel(
+// Batched decode with X resident in LDS (16 rows x K fp16 <= 128 KB: M <= 16
+// at K <= 4096). A block of KS x WN wavefronts owns 16 WN output channels;
+// wavefront (ks, wn) owns column tile wn over k-split group ks. All of X is
+// loaded once (through registers), stored in LDS in the operand k order of
+// the decode GEMV's unpack (each 16-byte chunk permuted to k offsets
+// 0,4,1,5,2,6,3,7) and XOR-swizzled (chunk c of row m at c ^ (m % 16)); then
+// every scale, zero-point and code run of the wavefront's KBW k-blocks is
+// issued; one wait and one barrier make X visible, and from there the only
+// waits are the compiler's, in issue order, on the code runs. The unpack is
+// the GEMV's (9 operations per 8 weights, 16 (u - zp) exact; the 1/16 is
+// folded into the fp32 group scale).
+template <int WN, int KS, int KBW, bool ASYM>
+__global__ __launch_bounds__(64 * WN * KS) void w4a16_batched_xres_kernel(
     const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
     uint16_t *__restrict__ Y)
 {
-    static_assert(KS * KBW * MT <= 32, "X must fit the 128 KB of LDS");
-    constexpr int SLOT = MT * 16 * 256;          // bytes of one k-block of X
+    static_assert(KS * KBW <= 32, "X must fit the 128 KB of LDS");
+    constexpr int T = 64 * WN * KS;
     __shared__ __attribute__((aligned(1024))) unsigned char xs[32 * 16 * 256];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = wave & 3, ks = wave >> 2;     // column tile, k-split group
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % WN, ks = wave / WN;    // column tile, k-split group
     const int r16 = lane & 15, q = lane >> 4;
     const int kbase = ks * KBW;
-    const uint32_t G = (uint32_t)(K >> 7), Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
-    const int n = blockIdx.x * 64 + wn * 16 + r16;
+    const int KB = KS * KBW;
+    const uint32_t G = (uint32_t)KB, Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
+    const int n = blockIdx.x * 16 * WN + wn * 16 + r16;
     const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
 
-    // X: slot kb holds k-block kb of all 16 MT rows; instruction j of
-    // wavefront wn fills rows 4 (4 j + wn) .. + 3; lane i: row 4 (4 j + wn) +
-    // i / 16, stored chunk i % 16, logical chunk (i % 16) ^ (row % 16)
-    const unsigned char *Xb = reinterpret_cast<const unsigned char *>(X);
+    // X: 16 B chunk P (= k-block P / 256, row (P / 16) % 16, stored chunk
+    // P % 16) at LDS byte 16 P holds logical chunk (P % 16) ^ row, permuted
+    constexpr int NCH = 32 * 16 * 16;                         // chunks when K = 4096
+    constexpr int PER = (NCH + T - 1) / T;
+    u32x4 xv[PER];
 #pragma unroll
-    for (int j = 0; j < MT; j++) {
-        const int m = 4 * (4 * j + wn) + (lane >> 4);
-        const int c = (lane & 15) ^ (m & 15);
-        const uint32_t xoff = ((uint32_t)(m < M ? m : M - 1) * (uint32_t)K + 8u * (uint32_t)c) * 2u;
-#pragma unroll
-        for (int p = 0; p < KBW; p++)
-            __builtin_amdgcn_global_load_lds(Xb + xoff + (uint32_t)(kbase + p) * 256u,
-                                             xs + (kbase + p) * SLOT + (4 * j + wn) * 1024, 16, 0, 0);
+    for (int i = 0; i < PER; i++) {
+        const int P = tid + i * T;
+        const int kb = P >> 8, m = (P >> 4) & 15, c = (P & 15) ^ m;
+        const int mc = m < M ? m : M - 1;
+        xv[i] = u32x4{0u, 0u, 0u, 0u};
+        if (kb < KB) xv[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)mc * K + kb * 128 + c * 8);
     }
     // then the scales and zero-points (needed first), then the code runs
     asm volatile("" ::: "memory");
@@ -525,71 +527,51 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_xres_kernel(
 #pragma unroll
     for (int p = 0; p < KBW; p++)
         cw[p] = *reinterpret_cast<const u32x4 *>(codes + (nrow * kh + (uint32_t)(kbase + p) * 64u + q * 16u));
-    // X landed (everything issued after it may still be in flight), then the
-    // whole block's X is visible after the barrier
-    asm volatile("" ::: "memory");
-    Q4_WAIT_VM_LGKM0(KBW + 1 + (ASYM ? 1 : 0));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-
-    floatx4 acc[MT];
+    // X to LDS in the operand order, then visible to the block
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < PER; i++) {
+        const int P = tid + i * T;
+        if ((P >> 8) < KB) *reinterpret_cast<u32x4 *>(xs + P * 16) = permute_x(xv[i]);
+    }
+    __syncthreads();
+
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < KBW; p++) {
-        const unsigned char *slot = xs + (kbase + p) * SLOT;
-        const uint32_t zp = (zraw >> (4 * p)) & 15u;
-        const uint32_t zadd = (0xE400u + zp) | ((0xD400u + 16u * zp) << 16);   // 1 at 1024, 1/16 at 64
-        floatx4 part[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++) part[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const unsigned char *slot = xs + (kbase + p) * 4096 + r16 * 256;
+        const ZeroConst zc = zero_const((zraw >> (4 * p)) & 15);
+        floatx4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-            const uint32_t w = cw[p][t];
-            const u32x4 bv = {unpack_pair(w, 0, zadd), unpack_pair(w, 1, zadd),
-                              unpack_pair(w, 2, zadd), unpack_pair(w, 3, zadd)};
-            const half8 b = __builtin_bit_cast(half8, bv);
-#pragma unroll
-            for (int mt = 0; mt < MT; mt++) {
-                const int m = mt * 16 + r16;
-                const half8 a = *reinterpret_cast<const half8 *>(slot + m * 256 + 16 * ((4 * q + t) ^ r16));
-                part[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, part[mt], 0, 0, 0);
-            }
+            const half8 a = *reinterpret_cast<const half8 *>(slot + 16 * ((4 * q + t) ^ r16));
+            part = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, dequant8(cw[p][t], zc), part, 0, 0, 0);
         }
         const uint32_t sw = sraw[p >> 1];
-        const float s = h2f((uint16_t)((p & 1) ? (sw >> 16) : (sw & 0xffffu)));
+        const float s = scale16((uint16_t)((p & 1) ? (sw >> 16) : (sw & 0xffffu)));
 #pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) acc[mt][r] = fmaf(part[mt][r], s, acc[mt][r]);
+        for (int r = 0; r < 4; r++) acc[r] = fmaf(part[r], s, acc[r]);
     }
 
     if (KS > 1) {
         // the k-split groups' partial sums meet in LDS (group order fixed)
-        float *red = reinterpret_cast<float *>(xs);   // [KS - 1][4 wn][MT * 4][64]
+        float *red = reinterpret_cast<float *>(xs);   // [KS - 1][WN][4][64]
         __syncthreads();
         if (ks > 0) {
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) red[(((ks - 1) * 4 + wn) * MT * 4 + mt * 4 + r) * 64 + lane] = acc[mt][r];
+            for (int r = 0; r < 4; r++) red[(((ks - 1) * WN + wn) * 4 + r) * 64 + lane] = acc[r];
         }
         __syncthreads();
         if (ks > 0) return;
 #pragma unroll
         for (int g2 = 1; g2 < KS; g2++)
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) acc[mt][r] += red[(((g2 - 1) * 4 + wn) * MT * 4 + mt * 4 + r) * 64 + lane];
+            for (int r = 0; r < 4; r++) acc[r] += red[(((g2 - 1) * WN + wn) * 4 + r) * 64 + lane];
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int m = mt * 16 + 4 * q + r;
-            if (m < M && n < N) Y[(int64_t)m * N + n] = f2h(acc[mt][r]);
-        }
+    for (int r = 0; r < 4; r++) {
+        const int m = 4 * q + r;
+        if (m < M && n < N) Y[(int64_t)m * N + n] = f2h(acc[r]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -827,7 +809,8 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t 
     const int KB = K / 128;
     const int blocks = (N + 63) / 64;
     // X resident in LDS: 16 rows x K fp16 within 128 KB, 4 k-split groups of
-    // 2, 4 or 8 k-blocks each, whole-run vector loads of scales / zero-points
+    // 2, 4 or 8 k-blocks each, whole-run vector loads of scales / zero-points;
+    // 3 column tiles per block when that fills the CUs better than 4
     if (M <= 16 && (KB == 8 || KB == 16 || KB == 32)) {
         const int kbw = KB / 4;
         const int Gz = (KB + 1) / 2;
@@ -835,10 +818,19 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t 
                              (!zeros || ((reinterpret_cast<uintptr_t>(zeros) & (kbw / 2 - 1)) == 0 &&
                                          Gz % (kbw / 2) == 0));
         if (aligned) {
-            auto go = [&](auto kernel) { kernel<<<blocks, 1024, 0, st>>>(X, M, N, K, codes, scales, zeros, Y); };
-            if (kbw == 8) zeros ? go(w4a16_batched_xres_kernel<1, 4, 8, true>) : go(w4a16_batched_xres_kernel<1, 4, 8, false>);
-            else if (kbw == 4) zeros ? go(w4a16_batched_xres_kernel<1, 4, 4, true>) : go(w4a16_batched_xres_kernel<1, 4, 4, false>);
-            else zeros ? go(w4a16_batched_xres_kernel<1, 4, 2, true>) : go(w4a16_batched_xres_kernel<1, 4, 2, false>);
+            const int b4 = (N + 63) / 64, b3 = (N + 47) / 48;
+            const bool three = b3 <= 256 && b4 < 256;   // every CU busy with 3, some idle with 4
+            const int nb = three ? b3 : b4;
+            auto go = [&](auto kernel, int wn) { kernel<<<nb, 256 * wn, 0, st>>>(X, M, N, K, codes, scales, zeros, Y); };
+#define Q4_XRES(WN)                                                                                   \
+    do {                                                                                              \
+        if (kbw == 8) zeros ? go(w4a16_batched_xres_kernel<WN, 4, 8, true>, WN) : go(w4a16_batched_xres_kernel<WN, 4, 8, false>, WN); \
+        else if (kbw == 4) zeros ? go(w4a16_batched_xres_kernel<WN, 4, 4, true>, WN) : go(w4a16_batched_xres_kernel<WN, 4, 4, false>, WN); \
+        else zeros ? go(w4a16_batched_xres_kernel<WN, 4, 2, true>, WN) : go(w4a16_batched_xres_kernel<WN, 4, 2, false>, WN); \
+    } while (0)
+            if (three) Q4_XRES(3);
+            else Q4_XRES(4);
+#undef Q4_XRES
             return hipGetLastError();
         }
     }

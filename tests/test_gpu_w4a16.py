@@ -190,3 +190,13 @@ def test_batched_variants(orc, M, K, sym):
     N = 300
     W, X = workloads.small_case(M * 7 + K + int(sym), M, N, K)
     run_case(orc, W, X, 128, sym, what=f"batched M={M} N={N} K={K} sym={sym}")
+
+
+# N large enough that 48-column blocks would not fit one round of the CUs:
+# the X-resident kernel then uses 64-column blocks (4 column tiles).
+@pytest.mark.parametrize("M", [8, 16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_batched_wide_n(orc, M, sym):
+    N, K = 12800, 1024
+    W, X = workloads.small_case(M * 11 + int(sym), M, N, K)
+    run_case(orc, W, X, 128, sym, what=f"batched wide M={M} N={N} K={K} sym={sym}")
