@@ -115,34 +115,36 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile kernel (K % 256 == 0). Built around v_mfma_i32_32x32x32_i8, which
+// Large-tile kernel (K % 128 == 0). Built around v_mfma_i32_32x32x32_i8, which
 // runs near the int8 peak on gfx950 where the 16x16x64 form does not. A
 // 512-thread block computes a 256 x 256 tile of Y; its 8 wavefronts form a
 // 2 (M) x 4 (N) grid of 128 x 64 sub-tiles (4 x 2 MFMA tiles of 32 x 32, 128
 // int32 accumulators per lane).
 //
-// Operand staging: K advances 64 bytes per step through four LDS stages
-// (32 KB each: 256 rows of X and 256 rows of W, 64 bytes per row), filled
-// by direct global-to-LDS loads (global_load_lds_dwordx4, lane i of a load
-// lands at base + 16 i) issued three steps ahead, so a step's data has three
-// steps of MFMA work to arrive in and no registers are spent on staging.
-// Before a stage is read every wavefront waits for its own loads of that
-// stage (vmcnt) and for its earlier LDS reads (lgkmcnt), then the block
-// meets at a barrier. The 16-byte chunks of a row are stored XOR-swizzled
-// (chunk c of row r at c ^ ((r >> 2) & 3)) so the 32 rows an operand read
-// touches fall in distinct banks.
+// Operand staging: K advances 64 bytes per step through five LDS stages
+// (32 KB each: 256 rows of X and 256 rows of W, 64 bytes per row; the five
+// fill the 160 KB of LDS), filled by direct global-to-LDS loads
+// (global_load_lds_dwordx4, lane i of a load lands at base + 16 i) issued
+// four steps ahead, so a step's data has four steps of MFMA work to arrive
+// in and no registers are spent on staging. Before a stage is read every
+// wavefront waits for its own loads of that stage (vmcnt) and for its
+// earlier LDS reads (lgkmcnt), then the block meets at a barrier. The
+// 16-byte chunks of a row are stored XOR-swizzled (chunk c of row r at
+// c ^ ((r >> 2) & 3)) so the 32 rows an operand read touches fall in
+// distinct banks.
 //
-// MFMA output layout: lane l holds column l % 32 and rows
-// 8 (r / 4) + 4 (l / 32) + r % 4 of its 32 x 32 tile. In that layout a lane
-// can only store 2 bytes at a time, in 64-byte runs; so the epilogue scales
-// the accumulators in registers, stages the block's 256 x 256 fp16 tile in
-// the (then free) LDS and writes it back as whole rows with 16-byte stores
-// (about 20 us less than direct stores at 2048 x 8192).
+// Output layout: the MFMAs take W as their first operand and X as their
+// second, so each 32 x 32 accumulator tile is a tile of Y transposed: lane l
+// holds row l % 32 of Y and columns 8 (r / 4) + 4 (l / 32) + r % 4, i.e. four
+// consecutive outputs of one row per group of four registers. The epilogue
+// needs one per-token scale per 32-row tile and writes each group as one
+// 8-byte LDS store; the block's 256 x 256 fp16 tile is staged in the (then
+// free) LDS and written back as whole rows with 16-byte stores.
 //
 // Tile order is XCD-aware: consecutive block ids go to the 8 XCDs in turn, so
 // block b computes tile t = (b % 8) * (blocks / 8) + b / 8; each XCD then owns
 // whole columns of N-tiles, and its L2 serves their reuse of the W tiles.
-constexpr int LBM = 256, LBN = 256, LBK = 64, LSTAGES = 4;
+constexpr int LBM = 256, LBN = 256, LBK = 64, LSTAGES = 5;
 constexpr int LSTAGE_BYTES = (LBM + LBN) * LBK;   // 32 KB
 constexpr int OUT_STRIDE = LBN * 2 + 16;            // bytes per row of the staged fp16 output tile
 constexpr int LDS_BYTES = LBM * OUT_STRIDE > LSTAGES * LSTAGE_BYTES ? LBM * OUT_STRIDE : LSTAGES * LSTAGE_BYTES;
@@ -154,7 +156,6 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
     int32_t *__restrict__ acc_out)
 {
     __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
-    int8_t *const stages[LSTAGES] = {lds, lds + LSTAGE_BYTES, lds + 2 * LSTAGE_BYTES, lds + 3 * LSTAGE_BYTES};
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
@@ -229,44 +230,44 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
         for (int i = 0; i < 4; i++)
 #pragma unroll
             for (int j = 0; j < 2; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[s][i], f.b[s][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[s][j], f.a[s][i], acc[i][j], 0, 0, 0);
     };
 
-    // Software pipeline (four LDS stages, two register fragment sets). Step
+    // Software pipeline (five LDS stages, two register fragment sets). Step
     // k: run the first half of step k's MFMAs from registers, wait for this
     // wavefront's loads of stage k + 1 and meet the block at the barrier
     // (after it stage k + 1 is complete and everyone is done reading stage
     // k), then interleave the second half of the MFMAs with the reads of
-    // stage k + 1's fragments and the refill of stage k with step k + 4, so
+    // stage k + 1's fragments and the refill of stage k with step k + 5, so
     // the matrix pipe never waits on the barrier's LDS and load traffic.
     // Every step has the same shape: past the end the last step is
     // refetched into stages nobody reads, so the wait counts are uniform.
-    issue(stages[0], 0);
-    issue(stages[1], 1 < KT ? 1 : KT - 1);
-    issue(stages[2], 2 < KT ? 2 : KT - 1);
-    issue(stages[3], 3 < KT ? 3 : KT - 1);
+#pragma unroll
+    for (int p = 0; p < LSTAGES; p++) issue(lds + p * LSTAGE_BYTES, p < KT ? p : KT - 1);
     Frags f[2];
     asm volatile("" ::: "memory");
-    Q4_WAIT_VM_LGKM0(12);
+    Q4_WAIT_VM_LGKM0(4 * (LSTAGES - 1));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    read(stages[0], f[0]);
-    for (int kt = 0; kt < KT; kt += LSTAGES) {
+    read(lds, f[0]);
+    int sc = 0;   // stage of step k (k mod 5)
+    for (int kt = 0; kt < KT; kt += 2) {
 #pragma unroll
-        for (int u = 0; u < LSTAGES; u++) {
+        for (int u = 0; u < 2; u++) {
             const int k = kt + u;
-            mma_half(f[u & 1], 0);
+            const int sn = sc == LSTAGES - 1 ? 0 : sc + 1;
+            mma_half(f[u], 0);
             // nothing may move across the barrier (the scheduler does not
             // treat s_barrier as a boundary for LDS reads by itself)
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("" ::: "memory");
-            Q4_WAIT_VM_LGKM0(8);   // loads outstanding: stages k + 2, k + 3
+            Q4_WAIT_VM_LGKM0(4 * (LSTAGES - 2));   // loads outstanding: stages k + 2 .. k + 4
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            read(stages[(u + 1) % LSTAGES], f[(u + 1) & 1]);
-            issue(stages[u], k + 4 < KT ? k + 4 : KT - 1);
-            mma_half(f[u & 1], 1);
+            read(lds + sn * LSTAGE_BYTES, f[u ^ 1]);
+            issue(lds + sc * LSTAGE_BYTES, k + LSTAGES < KT ? k + LSTAGES : KT - 1);
+            mma_half(f[u], 1);
             // 12 fragment reads and 4 loads between the 8 MFMAs
 #pragma unroll
             for (int g = 0; g < 6; g++) {
@@ -277,45 +278,77 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            sc = sn;
         }
     }
     Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
+    // lane's outputs: row wm * 128 + 32 i + l32 of the block tile, columns
+    // wn * 64 + 32 j + 8 q + 4 h + e for accumulator r = 4 q + e
     if (acc_out) {
+        const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(acc_out) & 15) == 0;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 4; i++) {
+            const int m = m0 + wm * 128 + i * 32 + l32;
+            if (m >= M) continue;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            for (int j = 0; j < 2; j++)
 #pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const int n = n0 + wn * 64 + j * 32 + l32;
-                    if (m < M && n < N) acc_out[(int64_t)m * N + n] = acc[i][j][r];
+                for (int q = 0; q < 4; q++) {
+                    const int n = n0 + wn * 64 + j * 32 + 8 * q + 4 * h;
+                    int32_t *const dst = acc_out + (int64_t)m * N + n;
+                    if (vec_ok && n + 4 <= N) {
+                        *reinterpret_cast<intx4 *>(dst) =
+                            intx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            if (n + e < N) dst[e] = acc[i][j][4 * q + e];
+                    }
                 }
-            }
+        }
     }
-    // Epilogue: y = f2h((acc * sx[m]) * sw[n]) in the MFMA layout, staged
-    // through LDS as the block's 256 x 256 fp16 tile, then written back as
-    // whole rows with 16-byte stores.
+    // Epilogue: y = f2h((acc * sx[m]) * sw[n]), staged through LDS as the
+    // block's 256 x 256 fp16 tile, then written back as whole rows with
+    // 16-byte stores.
+    float xsv[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int m = m0 + wm * 128 + i * 32 + l32;
+        xsv[i] = sx[m < M ? m : M - 1];
+    }
     __syncthreads();   // every wavefront is done with the stages
-    float swv[2];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int n = n0 + wn * 64 + j * 32 + l32;
-        swv[j] = sw[n < N ? n : N - 1];
-    }
+    for (int j = 0; j < 2; j++)
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+        for (int q = 0; q < 4; q++) {
+            const int nl = wn * 64 + j * 32 + 8 * q + 4 * h;
+            float swv[4];
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int ml = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const int m = m0 + ml;
-            const float xs = sx[m < M ? m : M - 1];
+            for (int e = 0; e < 4; e++) {
+                const int n = n0 + nl + e;
+                swv[e] = sw[n < N ? n : N - 1];
+            }
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                float f = (float)acc[i][j][r] * xs;
-                f = f * swv[j];
-                asm volatile("" : "+v"(f));
-                *reinterpret_cast<uint16_t *>(lds + ml * OUT_STRIDE + (wn * 64 + j * 32 + l32) * 2) = f2h(f);
+            for (int i = 0; i < 4; i++) {
+                uint32_t pk[2];
+#pragma unroll
+                for (int e2 = 0; e2 < 2; e2++) {
+                    uint32_t hv[2];
+#pragma unroll
+                    for (int e1 = 0; e1 < 2; e1++) {
+                        const int e = 2 * e2 + e1;
+                        float f = (float)acc[i][j][4 * q + e] * xsv[i];
+                        f = f * swv[e];
+                        // Keep the fp32 product: without this the backend
+                        // folds the multiply and the fp16 convert into one
+                        // v_fma_mix (a single rounding).
+                        asm volatile("" : "+v"(f));
+                        hv[e1] = f2h(f);
+                    }
+                    pk[e2] = hv[0] | (hv[1] << 16);
+                }
+                const int ml = wm * 128 + i * 32 + l32;
+                *reinterpret_cast<u32x2 *>(lds + ml * OUT_STRIDE + nl * 2) = u32x2{pk[0], pk[1]};
             }
         }
     __syncthreads();
@@ -344,7 +377,7 @@ hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
                             hipStream_t st)
 {
     if (M == 0 || N == 0) return hipSuccess;
-    if (K % (LSTAGES * LBK) == 0 && M * K < (int64_t)1 << 31 && N * K < (int64_t)1 << 31) {
+    if (K % (2 * LBK) == 0 && M * K < (int64_t)1 << 31 && N * K < (int64_t)1 << 31) {
         const int tiles_m = (int)((M + LBM - 1) / LBM), tiles_n = (int)((N + LBN - 1) / LBN);
         w8a8_gemm_large_kernel<<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N,
                                                                  (int)K, tiles_m, Y, acc_out);
