@@ -61,7 +61,7 @@ def test_smoothquant_scales_small(orc, alpha):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (5, 7, 48), (64, 64, 128), (130, 257, 272),
                                    (128, 128, 1024), (300, 200, 8192), (513, 300, 256),
-                                   (257, 511, 768)])
+                                   (257, 511, 768), (300, 520, 384), (70, 260, 640)])
 def test_gemm_shapes(orc, M, N, K):
     W, X = workloads.small_case(M * 131 + N * 7 + K, M, N, K)
     Xq, sx = orc.q8_quantize_act(X)
