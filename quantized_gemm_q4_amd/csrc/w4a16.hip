@@ -457,6 +457,163 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Batched decode, 16 < M <= 64, with the wavefront's whole weight slice in
+// registers. The ring kernel above keeps only R - 1 k-blocks of code runs in
+// flight per row, so HBM sees each 2 KB weight row as 64-byte pieces spread
+// over the whole kernel, and a step costs about one memory latency over the
+// ring depth. Here a wavefront issues the code runs, scales and zero-points
+// of all its KBS (<= 16) k-blocks at once, right behind the first R - 1 X
+// slots, so the weight streams at the rate of the decode GEMV; from then on
+// only X (L2-resident) goes through the R-slot LDS ring. The first X wait
+// also waits for the code runs (loads complete in order); that is the
+// weight's own stream time, paid once. Same operand order, unpack and
+// arithmetic as the ring kernel.
+template <int MT, int KS, int R, int KBS, bool ASYM>
+__global__ __launch_bounds__(256 * KS) void w4a16_batched_cres_kernel(
+    const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    uint16_t *__restrict__ Y)
+{
+    static_assert(MT <= 4 && KS * R * MT <= 32 && (KBS == 8 || KBS == 16) && (R - 2) * MT <= 63, "ring sizes");
+    constexpr int SLOT = MT * 16 * 256;          // bytes of one k-block of X
+    __shared__ __attribute__((aligned(1024))) unsigned char xs[32 * 16 * 256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave & 3, ks = wave >> 2;     // column tile, k-split group
+    const int r16 = lane & 15, q = lane >> 4;
+    const int kbase = ks * KBS;
+    auto kblock = [&](int i) { return kbase + (i < KBS ? i : KBS - 1); };   // i may be past the end
+    const uint32_t G = (uint32_t)(K >> 7), Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
+    const int n = blockIdx.x * 64 + wn * 16 + r16;
+    const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
+    unsigned char *ring = xs + ks * R * SLOT;
+
+    // direct-to-LDS X loads: instruction j of wavefront wn fills rows
+    // 4 (4 j + wn) .. + 3 of a slot; lane i: row 4 (4 j + wn) + i / 16, stored
+    // chunk i % 16, logical chunk (i % 16) ^ (row % 16). (Fixed-size arrays:
+    // arrays sized by a template parameter and captured by the lambdas make
+    // this compiler drop the kernel's host stub.)
+    uint32_t xoff[4];
+#pragma unroll
+    for (int j = 0; j < MT; j++) {
+        const int m = 4 * (4 * j + wn) + (lane >> 4);
+        const int c = (lane & 15) ^ (m & 15);
+        xoff[j] = ((uint32_t)(m < M ? m : M - 1) * (uint32_t)K + 8u * (uint32_t)c) * 2u;
+    }
+    const unsigned char *Xb = reinterpret_cast<const unsigned char *>(X);
+    auto issue_x = [&](int i) {
+        const int kc = kblock(i);
+        unsigned char *slot = ring + (i % R) * SLOT;
+#pragma unroll
+        for (int j = 0; j < MT; j++)
+            __builtin_amdgcn_global_load_lds(Xb + xoff[j] + (uint32_t)kc * 256u, slot + (4 * j + wn) * 1024,
+                                             16, 0, 0);
+    };
+
+#pragma unroll
+    for (int i = 0; i < R - 1; i++) issue_x(i);
+    asm volatile("" ::: "memory");
+    // the group's scales and zero-points as whole runs (the host checks the
+    // alignment): 2 KBS bytes of scales, KBS / 2 bytes of zero-points
+    uint32_t sraw[8];
+    uint64_t zraw = 0x8888888888888888ull;
+    {
+        const u32x4 *sp = reinterpret_cast<const u32x4 *>(scales + (nrow * G + kbase));
+#pragma unroll
+        for (int v = 0; v < KBS / 8; v++) {
+            const u32x4 t = sp[v];
+#pragma unroll
+            for (int e = 0; e < 4; e++) sraw[4 * v + e] = t[e];
+        }
+        if (ASYM) {
+            const uint8_t *zpp = zeros + (nrow * Gz + (kbase >> 1));
+            if constexpr (KBS == 16) {
+                const u32x2 t = *reinterpret_cast<const u32x2 *>(zpp);
+                zraw = (uint64_t)t[0] | ((uint64_t)t[1] << 32);
+            } else {
+                zraw = *reinterpret_cast<const uint32_t *>(zpp);
+            }
+        }
+    }
+    u32x4 cw[16];
+#pragma unroll
+    for (int i = 0; i < KBS; i++)
+        cw[i] = *reinterpret_cast<const u32x4 *>(codes + (nrow * kh + (uint32_t)kblock(i) * 64u + q * 16u));
+    asm volatile("" ::: "memory");
+
+    floatx4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Step i: wait until at most the X loads of steps i + 1 .. i + R - 2 are
+    // outstanding (for i <= R - 2 that also takes every code run, issued
+    // after X slot i: a stricter wait, never a looser one), meet the block
+    // (every wavefront is done with slot i - 1), refill slot i - 1 with step
+    // i + R - 1 (past the end: the last k-block again, into slots nobody
+    // reads), then compute step i from slot i.
+#pragma unroll
+    for (int i = 0; i < KBS; i++) {
+        asm volatile("" ::: "memory");
+        Q4_WAIT_VM_LGKM0((R - 2) * MT);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue_x(i + R - 1);
+        asm volatile("" ::: "memory");
+        const unsigned char *slot = ring + (i % R) * SLOT;
+        const uint32_t zp = (uint32_t)(zraw >> (4 * i)) & 15u;
+        const uint32_t zadd = (0xE400u + zp) | ((0xD400u + 16u * zp) << 16);   // 1 at 1024, 1/16 at 64
+        floatx4 part[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) part[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const uint32_t w = cw[i][t];
+            const u32x4 bv = {unpack_pair(w, 0, zadd), unpack_pair(w, 1, zadd),
+                              unpack_pair(w, 2, zadd), unpack_pair(w, 3, zadd)};
+            const half8 b = __builtin_bit_cast(half8, bv);
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+                const int m = mt * 16 + r16;
+                const half8 a = *reinterpret_cast<const half8 *>(slot + m * 256 + 16 * ((4 * q + t) ^ r16));
+                part[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, part[mt], 0, 0, 0);
+            }
+        }
+        const float s = h2f((uint16_t)(sraw[i >> 1] >> (16 * (i & 1))));
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[mt][r] = fmaf(part[mt][r], s, acc[mt][r]);
+    }
+    Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
+
+    if (KS > 1) {
+        // the k-split groups' partial sums meet in LDS (group order fixed)
+        float *red = reinterpret_cast<float *>(xs);   // [KS - 1][4 wn][MT * 4][64]
+        __syncthreads();
+        if (ks > 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) red[(((ks - 1) * 4 + wn) * MT * 4 + mt * 4 + r) * 64 + lane] = acc[mt][r];
+        }
+        __syncthreads();
+        if (ks > 0) return;
+#pragma unroll
+        for (int g2 = 1; g2 < KS; g2++)
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[mt][r] += red[(((g2 - 1) * 4 + wn) * MT * 4 + mt * 4 + r) * 64 + lane];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int m = mt * 16 + 4 * q + r;
+            if (m < M && n < N) Y[(int64_t)m * N + n] = f2h(acc[mt][r]);
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Batched decode with X resident in LDS (16 rows x K fp16 <= 128 KB: M <= 16
 // at K <= 4096). A block of KS x WN wavefronts owns 16 WN output channels;
 // wavefront (ks, wn) owns column tile wn over k-split group ks. All of X is
@@ -837,6 +994,22 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t 
     auto launch = [&](auto kernel, int ks) {
         kernel<<<blocks, 256 * ks, 0, st>>>(X, M, N, K, codes, scales, zeros, Y);
     };
+    // M > 16 with at most 16 k-blocks per k-split group: the wavefront's
+    // weight slice is held in registers, only X goes through the LDS ring
+    // (8 slots, or 4 when 4 m-tiles and 2 groups share the 128 KB)
+    const bool runs_aligned = (reinterpret_cast<uintptr_t>(scales) & 15) == 0 &&
+                              (!zeros || (reinterpret_cast<uintptr_t>(zeros) & 7) == 0);
+    if (M > 16 && (KB == 8 || KB == 16 || KB == 32) && runs_aligned) {
+#define Q4_C(MT, KS, KBS)                                                                                  \
+    (zeros ? launch(w4a16_batched_cres_kernel<MT, KS, (32 / (MT * KS) > 8 ? 8 : 32 / (MT * KS)), KBS, true>, KS) \
+           : launch(w4a16_batched_cres_kernel<MT, KS, (32 / (MT * KS) > 8 ? 8 : 32 / (MT * KS)), KBS, false>, KS))
+        const bool mt2 = M <= 32;
+        if (KB == 32) mt2 ? Q4_C(2, 2, 16) : Q4_C(4, 2, 16);
+        else if (KB == 16) mt2 ? Q4_C(2, 2, 8) : Q4_C(4, 2, 8);
+        else mt2 ? Q4_C(2, 1, 8) : Q4_C(4, 1, 8);
+#undef Q4_C
+        return hipGetLastError();
+    }
 #define Q4_B(MT, KS)                                                                        \
     (zeros ? launch(w4a16_batched_kernel<MT, KS, 4, 4, true>, KS)                           \
            : launch(w4a16_batched_kernel<MT, KS, 4, 4, false>, KS))
