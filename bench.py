@@ -2,20 +2,22 @@
 
 Headline workload (one step): Llama-shaped W4A16 decode, M = 1 token,
 K = 4096, g = 128 asymmetric INT4, packed ahead of time; a step runs the
-N = 11008 layer and then the N = 4096 layer. The metric is HBM throughput:
-the algorithmic bytes of a step (packed codes + fp16 scales + 4-bit
-zero-points + X + Y) over its time. Inputs are resident in HBM before the
-timed region; every step reads a different copy of the packed weights
-(copies totalling more than 512 MB), so the 256 MB Infinity Cache cannot
-serve repeats. Launches are captured in a HIP graph (one graph holds one
-pass over the weight copies) and replayed.
+N = 11008 layer and the N = 4096 layer on the same X, as one
+w4a16_linear_multi launch. The metric is HBM throughput: the algorithmic
+bytes of a step (packed codes + fp16 scales + 4-bit zero-points + X + Y of
+both layers) over its time. Inputs are resident in HBM before the timed
+region; every step reads a different copy of the packed weights (copies
+totalling more than 512 MB), so the 256 MB Infinity Cache cannot serve
+repeats. Launches are captured in a HIP graph (one graph holds one pass over
+the weight copies) and replayed.
 
 The JSON line also carries:
-  roofline      the dominant kernel (the N = 11008 GEMV) timed alone with HIP
-                events on its stream, against 8 TB/s;
+  roofline      the dominant kernel (the two-layer decode GEMV launch) timed
+                with HIP events on its stream, against 8 TB/s;
   cpu_baseline  the CPU oracle (fp64 reference over the dequantized weights)
                 timed on this host's cores on the same step;
-  extra         prefill (M = 2048, sym) TFLOP/s against the fp16 MFMA peak,
+  extra         the same step as two w4a16_linear launches, each layer alone,
+                prefill (M = 2048, sym) TFLOP/s against the fp16 MFMA peak,
                 W8A8 (M = 2048, K = N = 8192) TOP/s against the int8 peak,
                 quantize + pack GB/s, batched decode M = 16 / 64.
 
@@ -43,14 +45,15 @@ INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8
 METRIC = "W4A16 g128 GEMM: GB/s at M=1, TFLOP/s at M=2048 (% of roofline)"
 MALL_BYTES = 512 * 2 ** 20
 COPY_BYTES = 2 ** 30
-# The kernel the dispatcher picks for M = 1, N = 11008, K = 4096, g = 128 asym
-# (688 blocks of 8 wavefronts, 4 k-blocks per wavefront).
-DECODE_KERNEL = "w4a16_gemv_kernel<8, 4, true, true>"
+# The kernel the dispatcher picks for the decode step: both layers (N = 11008
+# and 4096, M = 1, K = 4096, g = 128 asym) in one launch of 688 + 256 blocks
+# of 8 wavefronts, 4 k-blocks per wavefront.
+DECODE_KERNEL = "w4a16_gemv_multi_kernel<8, 4, true, true>"
 # the decode GEMV's source files: the committed traffic figures are valid only
 # for the revision of these files they were taken on
 DECODE_SOURCES = [os.path.join(ROOT, "quantized_gemm_q4_amd", "csrc", f)
                   for f in ("w4a16_gemv.hip", "w4a16_dequant.hpp", "q4_internal.hpp")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_gemv_decode_n11008_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_gemv_decode_step_traffic.json")
 
 
 def log(*a):
@@ -131,24 +134,26 @@ def main():
     extra = {}
     only = args.only
 
-    # ---- headline: decode step (N = 11008 then N = 4096, M = 1) ------------
+    # ---- headline: decode step (N = 11008 and N = 4096 on one X, M = 1) ----
     if only in (None, "decode"):
         layers = []
+        X = None
         for N in (11008, 4096):
             w = workloads.decode(N)
+            X = gpu(w["X"])    # the same X for both layers
             packed = q4.q4_quantize_pack(gpu(w["W"]), g=128, sym=False)
-            layers.append(dict(N=N, X=gpu(w["X"]), packed=packed,
+            layers.append(dict(N=N, packed=packed,
                                Y=torch.empty((1, N), dtype=torch.float16, device=dev)))
-        step_bytes = sum(w4a16_bytes(1, L["N"], 4096) for L in layers)
+        step_bytes = sum(w4a16_bytes(1, L["N"], 4096) for L in layers) - 4096 * 2   # X read once
         # enough copies that even the N = 11008 layer alone cycles > 512 MB
         copies = max(2, math.ceil(MALL_BYTES / w4a16_bytes(1, 11008, 4096)) + 1)
         for L in layers:
             L["copies"] = [tuple(t.clone() for t in L["packed"]) for _ in range(copies)]
+        Ys = [L["Y"] for L in layers]
 
         def step(i):
             c = i % copies
-            for L in layers:
-                q4.w4a16_linear(L["X"], *L["copies"][c], out=L["Y"])
+            q4.w4a16_linear_multi(X, [L["copies"][c] for L in layers], out=Ys)
 
         for i in range(args.warmup):
             step(i)
@@ -161,34 +166,41 @@ def main():
         t = timed(lambda i: full() if i < K // copies else tail(), K // copies + (1 if rem else 0))
         out.update(value=step_bytes * K / t / 1e9, unit="GB/s", steps=K, warmup=args.warmup,
                    ms_per_step=t / K * 1e3)
-        out["config"] = {"workload": "W4A16 decode: M=1, K=4096, N=11008 then N=4096, asym INT4 "
-                                     "g=128 pre-packed; X ~ N(0,1), W ~ N(0,0.02) with 1% of "
-                                     "K-channels x10",
+        out["config"] = {"workload": "W4A16 decode: M=1, K=4096, N=11008 and N=4096 on the same X "
+                                     "(one w4a16_linear_multi launch), asym INT4 g=128 pre-packed; "
+                                     "X ~ N(0,1), W ~ N(0,0.02) with 1% of K-channels x10",
                          "bytes_per_step": step_bytes, "weight_copies": copies,
                          "launch": "eager" if args.eager else "hip-graph",
                          "seeds": {"W": 1002, "X": 2002, "outliers": 4002}}
 
-        # dominant kernel alone: the N = 11008 GEMV
-        L = layers[0]
-        ncopy = len(L["copies"])
-        g11 = graph_of(lambda i: q4.w4a16_linear(L["X"], *L["copies"][i % ncopy], out=L["Y"]), ncopy)
-        g11()
-        reps = max(1, 2 * K // ncopy)
-        t11 = timed(lambda i: g11(), reps) / (reps * ncopy)
-        b11 = w4a16_bytes(1, 11008, 4096)
-        out["roofline"] = {"kernel": DECODE_KERNEL + " (M=1, N=11008, K=4096)",
-                           "bound": "hbm", "achieved": b11 / t11 / 1e9, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": b11 / t11 / 1e9 / HBM_PEAK_GBS,
-                           "traffic": measured_traffic(), "avg_launch_us": t11 * 1e6,
-                           "algorithmic_bytes_per_launch": b11, "launches": reps * ncopy}
-        L4 = layers[1]
-        g4 = graph_of(lambda i: q4.w4a16_linear(L4["X"], *L4["copies"][i % ncopy], out=L4["Y"]), ncopy)
-        g4()
-        t4 = timed(lambda i: g4(), reps) / (reps * ncopy)
-        b4 = w4a16_bytes(1, 4096, 4096)
-        extra["decode_n4096"] = {"us": t4 * 1e6, "GB/s": b4 / t4 / 1e9, "frac_hbm": b4 / t4 / 1e9 / HBM_PEAK_GBS}
-        extra["decode_n11008"] = {"us": t11 * 1e6, "GB/s": b11 / t11 / 1e9, "frac_hbm": b11 / t11 / 1e9 / HBM_PEAK_GBS}
-        del layers, L, L4
+        # dominant kernel: the two-layer launch, on its own graph
+        reps = max(1, 2 * K // copies)
+        gm = graph_of(step, copies)
+        gm()
+        tm = timed(lambda i: gm(), reps) / (reps * copies)
+        out["roofline"] = {"kernel": DECODE_KERNEL + " (M=1, N=11008 + 4096, K=4096)",
+                           "bound": "hbm", "achieved": step_bytes / tm / 1e9, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": step_bytes / tm / 1e9 / HBM_PEAK_GBS,
+                           "traffic": measured_traffic(), "avg_launch_us": tm * 1e6,
+                           "algorithmic_bytes_per_launch": step_bytes, "launches": reps * copies}
+
+        # the same step as two single-layer launches, and each layer alone
+        def step2(i):
+            c = i % copies
+            for L in layers:
+                q4.w4a16_linear(X, *L["copies"][c], out=L["Y"])
+        g2 = graph_of(step2, copies)
+        g2()
+        t2 = timed(lambda i: g2(), reps) / (reps * copies)
+        extra["decode_two_launches"] = {"us": t2 * 1e6, "GB/s": (step_bytes + 4096 * 2) / t2 / 1e9}
+        for L in layers:
+            gl = graph_of(lambda i, L=L: q4.w4a16_linear(X, *L["copies"][i % copies], out=L["Y"]), copies)
+            gl()
+            tl = timed(lambda i: gl(), reps) / (reps * copies)
+            bl = w4a16_bytes(1, L["N"], 4096)
+            extra[f"decode_n{L['N']}"] = {"us": tl * 1e6, "GB/s": bl / tl / 1e9,
+                                          "frac_hbm": bl / tl / 1e9 / HBM_PEAK_GBS}
+        del layers
         torch.cuda.empty_cache()
 
         if not args.skip_cpu:

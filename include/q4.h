@@ -123,6 +123,40 @@ Q4_API q4_status w4a16_linear(const void *X, int64_t M, int64_t N, int64_t K,
                               const uint8_t *zeros, void *Y, void *stream);
 
 /* ----------------------------------------------------------------------------
+ * w4a16_linear_multi -- several W4A16 layers that read the same input X
+ * (for example the projections that share one normalised hidden state),
+ * each computed exactly as w4a16_linear defines it:
+ *   Y_i = X * W_hat_i^T,   i = 0 .. count - 1.
+ * With M <= 16, g == 128 and all layers symmetric or all asymmetric, the
+ * layers run as one launch, so the weight stream starts and drains once for
+ * all of them; otherwise (or when a layer's scale / zero-point arrays are
+ * not aligned for whole-run vector loads) each layer takes its own launch.
+ * Accuracy as for w4a16_linear; the k-split of the one-launch form can
+ * differ from a single-layer call's, so results may differ from separate
+ * w4a16_linear calls in the last bit.
+ *
+ * X, M, K, g   as for w4a16_linear, shared by all layers.
+ * layers  HOST array of `count` descriptors (read during the call only):
+ *         codes, scales, zeros as written by q4_quantize_pack for a weight
+ *         [N, K] (zeros == NULL: symmetric), Y fp16 [M, N] output, N >= 0.
+ * count   0 .. Q4_MAX_MULTI_LAYERS (0 is a no-op).
+ * Errors: as for w4a16_linear, per layer; INVALID_ARG for a NULL `layers`
+ *         with count > 0 or count out of range. Every layer is checked
+ *         before anything is launched.
+ * -------------------------------------------------------------------------- */
+#define Q4_MAX_MULTI_LAYERS 8
+typedef struct q4_w4a16_layer {
+    const uint8_t *codes;
+    const void *scales;
+    const uint8_t *zeros;
+    void *Y;
+    int64_t N;
+} q4_w4a16_layer;
+Q4_API q4_status w4a16_linear_multi(const void *X, int64_t M, int64_t K, int32_t g,
+                                    const q4_w4a16_layer *layers, int32_t count,
+                                    void *stream);
+
+/* ----------------------------------------------------------------------------
  * q8_quantize_weight -- per-output-channel INT8 of the smoothed weight
  * (Operators guide §2.2 per-channel, §5.1/§5.3: W' = W diag(s) folded offline;
  * Core ideas §2.4):

@@ -9,6 +9,7 @@ built, every call raises -- there is no fallback path.
 Functions (same names as the C ABI):
   q4_quantize_pack(W, g=128, sym=False) -> (codes, scales, zeros | None)
   w4a16_linear(X, codes, scales, zeros, g=128) -> Y
+  w4a16_linear_multi(X, [(codes, scales, zeros), ...], g=128) -> [Y, ...]
   q8_quantize_weight(W, smooth_s=None) -> (Wq, w_scale)
   q8_quantize_act(X, smooth_s=None) -> (Xq, x_scale)
   w8a8_gemm(Xq, x_scale, Wq, w_scale, acc_out=None) -> Y
@@ -30,11 +31,20 @@ _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "MISALIGNED", 4: "HIP
 
 # name -> (restype, argtypes), exactly the declarations of include/q4.h
 _vp, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+
+
+class W4A16Layer(ctypes.Structure):
+    """q4_w4a16_layer: one layer of w4a16_linear_multi."""
+    _fields_ = [("codes", _vp), ("scales", _vp), ("zeros", _vp), ("Y", _vp), ("N", _i64)]
+
+
+MAX_MULTI_LAYERS = 8
 SIGNATURES = {
     "q4_layout_version": (ctypes.c_int, []),
     "q4_last_error": (ctypes.c_char_p, []),
     "q4_quantize_pack": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "w4a16_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "w4a16_linear_multi": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(W4A16Layer), _i32, _vp]),
     "q8_quantize_weight": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "q8_quantize_act": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
@@ -119,22 +129,59 @@ def w4a16_linear(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
                  zeros: torch.Tensor | None, g: int = 128, out: torch.Tensor | None = None):
     """Y fp16 [M, N] = X fp16 [M, K] x W_hat^T, W_hat dequantized in the GEMM."""
     _need(X, torch.float16, "X", 2)
-    _need(codes, torch.uint8, "codes", 2)
-    _need(scales, torch.float16, "scales", 2)
-    if zeros is not None:
-        _need(zeros, torch.uint8, "zeros", 2)
     M, K = X.shape
-    N = codes.shape[0]
-    if codes.shape[1] * 2 != K:
-        raise ValueError(f"codes {tuple(codes.shape)} does not match K={K}")
-    if scales.shape != (N, K // g):
-        raise ValueError(f"scales {tuple(scales.shape)} does not match [N, K/g]=[{N}, {K // g}]")
-    if zeros is not None and zeros.shape != (N, (K // g + 1) // 2):
-        raise ValueError(f"zeros {tuple(zeros.shape)} does not match [N, ceil(K/g/2)]")
-    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=X.device)
+    N = _check_packed(codes, scales, zeros, K, g)
+    Y = _output(out, M, N, X.device)
     _check(lib().w4a16_linear(_ptr(X), M, N, K, g, _ptr(codes), _ptr(scales), _ptr(zeros),
                               _ptr(Y), _stream(X)))
     return Y
+
+
+def _check_packed(codes, scales, zeros, K: int, g: int, what: str = "") -> int:
+    """Shapes of one packed weight [N, K] as q4_quantize_pack writes it; returns N."""
+    _need(codes, torch.uint8, what + "codes", 2)
+    _need(scales, torch.float16, what + "scales", 2)
+    if zeros is not None:
+        _need(zeros, torch.uint8, what + "zeros", 2)
+    N = codes.shape[0]
+    if codes.shape[1] * 2 != K:
+        raise ValueError(f"{what}codes {tuple(codes.shape)} does not match K={K}")
+    if g <= 0 or scales.shape != (N, K // g):
+        raise ValueError(f"{what}scales {tuple(scales.shape)} does not match [N, K/g]=[{N}, {K // max(g, 1)}]")
+    if zeros is not None and zeros.shape != (N, (K // g + 1) // 2):
+        raise ValueError(f"{what}zeros {tuple(zeros.shape)} does not match [N, ceil(K/g/2)]")
+    return N
+
+
+def _output(out, M: int, N: int, device):
+    if out is None:
+        return torch.empty((M, N), dtype=torch.float16, device=device)
+    _need(out, torch.float16, "out", 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out {tuple(out.shape)} does not match [M, N]=[{M}, {N}]")
+    return out
+
+
+def w4a16_linear_multi(X: torch.Tensor, layers, g: int = 128, out=None):
+    """Y_i fp16 [M, N_i] = X x W_hat_i^T for every packed weight
+    (codes, scales, zeros) in `layers`, all reading the same X; one launch
+    when the shapes allow it (M <= 16, g = 128, all layers sym or all asym)."""
+    _need(X, torch.float16, "X", 2)
+    M, K = X.shape
+    layers = list(layers)
+    if len(layers) > MAX_MULTI_LAYERS:
+        raise ValueError(f"at most {MAX_MULTI_LAYERS} layers per call, got {len(layers)}")
+    if out is not None and len(out) != len(layers):
+        raise ValueError("out must hold one tensor per layer")
+    table = (W4A16Layer * max(len(layers), 1))()
+    Ys = []
+    for i, (codes, scales, zeros) in enumerate(layers):
+        N = _check_packed(codes, scales, zeros, K, g, f"layer {i}: ")
+        Y = _output(None if out is None else out[i], M, N, X.device)
+        table[i] = W4A16Layer(_ptr(codes), _ptr(scales), _ptr(zeros), _ptr(Y), N)
+        Ys.append(Y)
+    _check(lib().w4a16_linear_multi(_ptr(X), M, K, g, table, len(layers), _stream(X)))
+    return Ys
 
 
 def q8_quantize_weight(W: torch.Tensor, smooth_s: torch.Tensor | None = None):

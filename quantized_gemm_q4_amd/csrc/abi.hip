@@ -10,6 +10,7 @@
 namespace {
 
 constexpr int kLayoutVersion = 1;
+static_assert(Q4_MAX_MULTI_LAYERS == q4k::kMaxGemvLayers, "one layer table size");
 thread_local char g_err[512] = "";
 
 q4_status fail(q4_status st, const char *fmt, ...)
@@ -93,6 +94,49 @@ Q4_API q4_status w4a16_linear(const void *X, int64_t M, int64_t N, int64_t K, in
                                      static_cast<const uint16_t *>(scales), zeros,
                                      static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
     return from_hip(e, "w4a16_linear");
+}
+
+Q4_API q4_status w4a16_linear_multi(const void *X, int64_t M, int64_t K, int32_t g,
+                                    const q4_w4a16_layer *layers, int32_t count, void *stream)
+{
+    Q4_REQUIRE(count >= 0 && count <= Q4_MAX_MULTI_LAYERS, Q4_ERR_INVALID_ARG,
+               "w4a16_linear_multi: count=%d not in 0..%d", count, Q4_MAX_MULTI_LAYERS);
+    Q4_REQUIRE(count == 0 || layers, Q4_ERR_INVALID_ARG, "w4a16_linear_multi: layers is NULL");
+    Q4_REQUIRE(M >= 0 && K > 0 && M <= kIntMax && K <= kIntMax, Q4_ERR_INVALID_ARG,
+               "w4a16_linear_multi: bad shape M=%lld K=%lld", (long long)M, (long long)K);
+    Q4_REQUIRE(g > 0 && K % g == 0 && K % 2 == 0, Q4_ERR_INVALID_ARG,
+               "w4a16_linear_multi: K=%lld must be even and a multiple of g=%d", (long long)K, g);
+    Q4_REQUIRE(g % 128 == 0, Q4_ERR_UNSUPPORTED,
+               "w4a16_linear_multi: group size %d unsupported (must be a multiple of 128)", g);
+    Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "w4a16_linear_multi: M=%lld too large",
+               (long long)M);
+    for (int i = 0; i < count; i++) {
+        const q4_w4a16_layer &l = layers[i];
+        Q4_REQUIRE(l.N >= 0 && l.N <= kIntMax, Q4_ERR_INVALID_ARG,
+                   "w4a16_linear_multi: layer %d: bad N=%lld", i, (long long)l.N);
+        if (M == 0 || l.N == 0) continue;
+        Q4_REQUIRE(X && l.codes && l.scales && l.Y, Q4_ERR_INVALID_ARG,
+                   "w4a16_linear_multi: layer %d: null pointer", i);
+        Q4_REQUIRE(aligned16(X) && aligned16(l.codes), Q4_ERR_MISALIGNED,
+                   "w4a16_linear_multi: layer %d: X and codes must be 16-byte aligned", i);
+    }
+    if (M == 0 || count == 0) return ok();
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    q4k::GemvLayerDesc d[Q4_MAX_MULTI_LAYERS];
+    int nd = 0;
+    for (int i = 0; i < count; i++)
+        if (layers[i].N > 0)
+            d[nd++] = q4k::GemvLayerDesc{layers[i].codes, static_cast<const uint16_t *>(layers[i].scales),
+                                         layers[i].zeros, static_cast<uint16_t *>(layers[i].Y), layers[i].N};
+    if (nd == 0) return ok();
+    hipError_t e = q4k::launch_w4a16_gemv_multi(static_cast<const uint16_t *>(X), M, K, g, d, nd, st);
+    if (e == hipErrorNotSupported) {   // one launch per layer
+        e = hipSuccess;
+        for (int i = 0; i < nd && e == hipSuccess; i++)
+            e = q4k::launch_w4a16(static_cast<const uint16_t *>(X), M, d[i].N, K, g, d[i].codes,
+                                  d[i].scales, d[i].zeros, d[i].Y, st);
+    }
+    return from_hip(e, "w4a16_linear_multi");
 }
 
 Q4_API q4_status q8_quantize_weight(const void *W, const float *smooth_s, int64_t N, int64_t K,

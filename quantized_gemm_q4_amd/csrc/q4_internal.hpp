@@ -45,6 +45,20 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
 hipError_t launch_w4a16_gemv(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,
                              const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
                              uint16_t *Y, hipStream_t st);
+
+// Several decode GEMVs that read the same X (M <= 16, g = 128) in one launch,
+// up to kMaxGemvLayers layers, all symmetric or all asymmetric;
+// hipErrorNotSupported when the shapes or alignments do not suit it.
+constexpr int kMaxGemvLayers = 8;
+struct GemvLayerDesc {
+    const uint8_t *codes;
+    const uint16_t *scales;
+    const uint8_t *zeros;
+    uint16_t *Y;
+    int64_t N;
+};
+hipError_t launch_w4a16_gemv_multi(const uint16_t *X, int64_t M, int64_t K, int g,
+                                   const GemvLayerDesc *layers, int count, hipStream_t st);
 hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
                             const float *sw, int64_t M, int64_t N, int64_t K, uint16_t *Y,
                             int32_t *acc_out, hipStream_t st);

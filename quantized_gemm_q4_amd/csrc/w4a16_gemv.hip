@@ -43,10 +43,11 @@ int gemv_waves_override()
 // not mix, and rows >= M are never stored. The wavefronts' partial sums meet
 // in LDS.
 template <int WAVES, int KBW, bool ASYM, bool ONE_ROW>
-__global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
-    const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
-    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-    uint16_t *__restrict__ Y)
+__device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M, int N, int K,
+                                           const uint8_t *__restrict__ codes,
+                                           const uint16_t *__restrict__ scales,
+                                           const uint8_t *__restrict__ zeros, uint16_t *__restrict__ Y,
+                                           int blk)
 {
     static_assert(KBW == 2 || KBW == 4 || KBW == 8, "vector scale / zero-point loads of 2, 4, 8 groups");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, q = lane >> 4;
     const int kb0 = wave * KBW;
-    const int n = blockIdx.x * 16 + r16;
+    const int n = blk * 16 + r16;
     const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
     const uint32_t G = (uint32_t)K >> 7, Gz = (G + 1) >> 1;
     const int xchunks = K >> 3;                              // 16-byte chunks per X row
@@ -155,9 +156,81 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
 #pragma unroll
         for (int w = 0; w < WAVES; w++) v += red[(w * 4 + r) * 64 + l];
         const int m = 4 * (l >> 4) + r;
-        const int nn = blockIdx.x * 16 + (l & 15);
+        const int nn = blk * 16 + (l & 15);
         if (m < M && nn < N) Y[(int64_t)m * N + nn] = f2h(v * 0.0625f);   // the 1/16 of dequant8
     }
+}
+
+template <int WAVES, int KBW, bool ASYM, bool ONE_ROW>
+__global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
+    const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    uint16_t *__restrict__ Y)
+{
+    gemv_block<WAVES, KBW, ASYM, ONE_ROW>(X, M, N, K, codes, scales, zeros, Y, (int)blockIdx.x);
+}
+
+// Several layers that read the same X in one launch: layer i owns blocks
+// [first_block_i, first_block_{i+1}); every block runs the GEMV block above
+// for its layer. One launch pays the start-up and drain of the weight stream
+// once for all the layers.
+struct GemvLayer {
+    const uint8_t *codes;
+    const uint16_t *scales;
+    const uint8_t *zeros;
+    uint16_t *Y;
+    int N, first_block;
+};
+struct GemvLayers {
+    GemvLayer l[kMaxGemvLayers];
+    int count;
+};
+
+template <int WAVES, int KBW, bool ASYM, bool ONE_ROW>
+__global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_multi_kernel(const uint16_t *__restrict__ X,
+                                                                     int M, int K, const GemvLayers L)
+{
+    const int b = (int)blockIdx.x;
+    GemvLayer my = L.l[0];
+#pragma unroll
+    for (int i = 1; i < kMaxGemvLayers; i++)   // uniform selects, no indexing of the argument
+        if (i < L.count && b >= L.l[i].first_block) my = L.l[i];
+    gemv_block<WAVES, KBW, ASYM, ONE_ROW>(X, M, my.N, K, my.codes, my.scales, my.zeros, my.Y,
+                                          b - my.first_block);
+}
+
+// (waves, k-blocks per wavefront) for `blocks` blocks of 16 channels: the
+// most wavefronts (16, else 8, else 4) that keep every block resident at once
+// (256 CUs x 32 wavefronts), so the whole weight is in flight from the start
+// (measured best for N = 11008 and 4096); the k-blocks must divide evenly (2,
+// 4 or 8 per wavefront), X must fit in LDS next to the reduction buffer, and
+// the scale / zero-point runs of every layer must suit whole vector loads.
+bool pick_gemv(int64_t M, int64_t K, int64_t blocks, const uint16_t *const *scales,
+               const uint8_t *const *zeros, int count, int &waves_out, int &kbw_out, size_t &lds_out)
+{
+    const int KB = (int)(K / 128);
+    const int G = KB, Gz = (G + 1) / 2;
+    const int forced = gemv_waves_override();
+    for (int waves : {16, 8, 4}) {
+        if (forced && waves != forced) continue;
+        if (!forced && waves > 4 && blocks * waves > 256 * 32) continue;
+        if (KB % waves != 0) continue;
+        const int kbw = KB / waves;
+        const size_t lds = (size_t)M * K * 2 + (size_t)waves * 4 * 64 * 4;
+        if ((kbw != 2 && kbw != 4 && kbw != 8) || lds > 64 * 1024) continue;
+        if (G % kbw != 0 || (kbw >= 4 && Gz % (kbw / 2) != 0)) continue;
+        bool ok = true;
+        for (int i = 0; i < count; i++) {
+            if ((reinterpret_cast<uintptr_t>(scales[i]) & (kbw * 2 - 1)) != 0) ok = false;
+            if (zeros[i] && (reinterpret_cast<uintptr_t>(zeros[i]) & (kbw / 2 - 1)) != 0) ok = false;
+        }
+        if (!ok) continue;
+        waves_out = waves;
+        kbw_out = kbw;
+        lds_out = lds;
+        return true;
+    }
+    return false;
 }
 
 }  // namespace
@@ -165,57 +238,76 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
 // Launches the GEMV when the shape and the alignment of the scale and
 // zero-point arrays suit it; hipErrorNotSupported otherwise (the caller then
 // takes another kernel).
+// Q4_GEMV_DISPATCH(KERNEL) calls launch(KERNEL<waves, kbw, asym, one_row>).
+#define Q4_GEMV_DISPATCH(KERNEL)                                                                  \
+    do {                                                                                          \
+        auto launch4 = [&](auto k_a1, auto k_a0, auto k_s1, auto k_s0) {                          \
+            if (asym) one_row ? launch(k_a1) : launch(k_a0);                                      \
+            else one_row ? launch(k_s1) : launch(k_s0);                                           \
+        };                                                                                        \
+        if (waves == 4 && kbw == 8) Q4_GEMV4(KERNEL, 4, 8);                                       \
+        else if (waves == 4 && kbw == 4) Q4_GEMV4(KERNEL, 4, 4);                                  \
+        else if (waves == 4) Q4_GEMV4(KERNEL, 4, 2);                                              \
+        else if (waves == 8 && kbw == 8) Q4_GEMV4(KERNEL, 8, 8);                                  \
+        else if (waves == 8 && kbw == 4) Q4_GEMV4(KERNEL, 8, 4);                                  \
+        else if (waves == 8) Q4_GEMV4(KERNEL, 8, 2);                                              \
+        else if (kbw == 8) Q4_GEMV4(KERNEL, 16, 8);                                               \
+        else if (kbw == 4) Q4_GEMV4(KERNEL, 16, 4);                                               \
+        else Q4_GEMV4(KERNEL, 16, 2);                                                             \
+    } while (0)
+#define Q4_GEMV4(KERNEL, W, B)                                                                    \
+    launch4(KERNEL<W, B, true, true>, KERNEL<W, B, true, false>, KERNEL<W, B, false, true>,       \
+            KERNEL<W, B, false, false>)
+
 hipError_t launch_w4a16_gemv(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,
                              const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
                              uint16_t *Y, hipStream_t st)
 {
+    if (g != 128 || M > 16 || N * K / 2 >= (int64_t)0xFFFFFF00)   // 32-bit offsets in the kernel
+        return hipErrorNotSupported;
     const int m = (int)M, n = (int)N, k = (int)K;
-    // GEMV path (g = 128): X fits in LDS next to the reduction buffer and
-    // the k-blocks divide evenly over the wavefronts (2, 4 or 8 each). The
-    // block takes the most wavefronts (16, else 8, else 4) that keep every
-    // block resident at once (256 CUs x 32 wavefronts), so the whole weight
-    // is in flight from the start (measured best for N = 11008 and 4096).
-    if (g == 128 && M <= 16 && N * K / 2 < (int64_t)0xFFFFFF00) {   // 32-bit offsets in the kernel
-        const int blocks = (n + 15) / 16;
-        const int KB = k / 128;
-        const int G = KB, Gz = (G + 1) / 2;
-        const int forced = gemv_waves_override();
-        for (int waves : {16, 8, 4}) {
-            if (forced && waves != forced) continue;
-            if (!forced && waves > 4 && (int64_t)blocks * waves > 256 * 32) continue;
-            if (KB % waves != 0) continue;
-            const int kbw = KB / waves;
-            const size_t lds = (size_t)M * K * 2 + (size_t)waves * 4 * 64 * 4;
-            if ((kbw != 2 && kbw != 4 && kbw != 8) || lds > 64 * 1024) continue;
-            // vector scale / zero-point loads: whole, aligned runs of kbw groups
-            if (G % kbw != 0 || (kbw >= 4 && Gz % (kbw / 2) != 0)) continue;
-            if ((reinterpret_cast<uintptr_t>(scales) & (kbw * 2 - 1)) != 0) continue;
-            if (zeros && (reinterpret_cast<uintptr_t>(zeros) & (kbw / 2 - 1)) != 0) continue;
-            auto launch = [&](auto kernel) {
-                kernel<<<blocks, waves * 64, lds, st>>>(X, m, n, k, codes, scales, zeros, Y);
-            };
-            // ASYM x ONE_ROW variants of one (waves, kbw) configuration
-            auto launch4 = [&](auto k_a1, auto k_a0, auto k_s1, auto k_s0) {
-                if (zeros) m == 1 ? launch(k_a1) : launch(k_a0);
-                else m == 1 ? launch(k_s1) : launch(k_s0);
-            };
-#define Q4_GEMV4(W, B)                                                                          \
-    launch4(w4a16_gemv_kernel<W, B, true, true>, w4a16_gemv_kernel<W, B, true, false>,          \
-            w4a16_gemv_kernel<W, B, false, true>, w4a16_gemv_kernel<W, B, false, false>)
-            if (waves == 4 && kbw == 8) Q4_GEMV4(4, 8);
-            else if (waves == 4 && kbw == 4) Q4_GEMV4(4, 4);
-            else if (waves == 4) Q4_GEMV4(4, 2);
-            else if (waves == 8 && kbw == 8) Q4_GEMV4(8, 8);
-            else if (waves == 8 && kbw == 4) Q4_GEMV4(8, 4);
-            else if (waves == 8) Q4_GEMV4(8, 2);
-            else if (kbw == 8) Q4_GEMV4(16, 8);
-            else if (kbw == 4) Q4_GEMV4(16, 4);
-            else Q4_GEMV4(16, 2);
-#undef Q4_GEMV4
-            return hipGetLastError();
-        }
-    }
-    return hipErrorNotSupported;
+    const int blocks = (n + 15) / 16;
+    int waves, kbw;
+    size_t lds;
+    if (!pick_gemv(M, K, blocks, &scales, &zeros, 1, waves, kbw, lds)) return hipErrorNotSupported;
+    const bool asym = zeros != nullptr, one_row = m == 1;
+    auto launch = [&](auto kernel) {
+        kernel<<<blocks, waves * 64, lds, st>>>(X, m, n, k, codes, scales, zeros, Y);
+    };
+    Q4_GEMV_DISPATCH(w4a16_gemv_kernel);
+    return hipGetLastError();
 }
+
+hipError_t launch_w4a16_gemv_multi(const uint16_t *X, int64_t M, int64_t K, int g,
+                                   const GemvLayerDesc *layers, int count, hipStream_t st)
+{
+    if (g != 128 || M > 16 || count < 1 || count > kMaxGemvLayers) return hipErrorNotSupported;
+    const bool asym = layers[0].zeros != nullptr;
+    GemvLayers L{};
+    const uint16_t *sc[kMaxGemvLayers];
+    const uint8_t *zp[kMaxGemvLayers];
+    int64_t blocks = 0;
+    for (int i = 0; i < count; i++) {
+        const GemvLayerDesc &d = layers[i];
+        if ((d.zeros != nullptr) != asym || d.N * K / 2 >= (int64_t)0xFFFFFF00)
+            return hipErrorNotSupported;
+        L.l[i] = GemvLayer{d.codes, d.scales, d.zeros, d.Y, (int)d.N, (int)blocks};
+        sc[i] = d.scales;
+        zp[i] = d.zeros;
+        blocks += (d.N + 15) / 16;
+    }
+    L.count = count;
+    if (blocks == 0) return hipSuccess;
+    int waves, kbw;
+    size_t lds;
+    if (!pick_gemv(M, K, blocks, sc, zp, count, waves, kbw, lds)) return hipErrorNotSupported;
+    const int m = (int)M, k = (int)K;
+    const bool one_row = m == 1;
+    auto launch = [&](auto kernel) { kernel<<<(int)blocks, waves * 64, lds, st>>>(X, m, k, L); };
+    Q4_GEMV_DISPATCH(w4a16_gemv_multi_kernel);
+    return hipGetLastError();
+}
+#undef Q4_GEMV4
+#undef Q4_GEMV_DISPATCH
 
 }  // namespace q4k

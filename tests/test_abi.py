@@ -56,6 +56,14 @@ FAKE = 0x10000          # never dereferenced: validation fails first
 MISAL = 0x10001
 
 
+def layers(*descs):
+    """A q4_w4a16_layer array from (codes, scales, zeros, Y, N) tuples."""
+    table = (q4.W4A16Layer * len(descs))()
+    for i, d in enumerate(descs):
+        table[i] = q4.W4A16Layer(*d)
+    return table
+
+
 @pytest.mark.parametrize("call,status", [
     # bad group size / shape
     (lambda L: L.q4_quantize_pack(FAKE, 4, 512, 100, 0, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
@@ -72,6 +80,27 @@ MISAL = 0x10001
     (lambda L: L.w4a16_linear(FAKE, 1, 16, 512, 128, None, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.w4a16_linear(FAKE, 0, 16, 512, 128, None, None, None, None, None), q4.Q4_OK),
     (lambda L: L.w4a16_linear(FAKE, 3, 0, 512, 128, None, None, None, None, None), q4.Q4_OK),
+    (lambda L: L.w4a16_linear_multi(FAKE, 1, 512, 128, layers((FAKE, FAKE, FAKE, FAKE, 16)), 9, None),
+     q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w4a16_linear_multi(FAKE, 1, 512, 128, None, 1, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w4a16_linear_multi(FAKE, 1, 512, 64, layers((FAKE, FAKE, FAKE, FAKE, 16)), 1, None),
+     q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.w4a16_linear_multi(FAKE, 1, 500, 128, layers((FAKE, FAKE, FAKE, FAKE, 16)), 1, None),
+     q4.Q4_ERR_INVALID_ARG),
+    # the second layer is checked before anything runs
+    (lambda L: L.w4a16_linear_multi(FAKE, 1, 512, 128, layers((FAKE, FAKE, FAKE, FAKE, 16),
+                                                                (MISAL, FAKE, FAKE, FAKE, 16)), 2, None),
+     q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.w4a16_linear_multi(FAKE, 1, 512, 128, layers((FAKE, FAKE, FAKE, FAKE, 16),
+                                                                (None, FAKE, FAKE, FAKE, 16)), 2, None),
+     q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w4a16_linear_multi(FAKE, 1, 512, 128, layers((FAKE, FAKE, FAKE, FAKE, -1)), 1, None),
+     q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w4a16_linear_multi(FAKE, 1, 512, 128, None, 0, None), q4.Q4_OK),
+    (lambda L: L.w4a16_linear_multi(FAKE, 0, 512, 128, layers((None, None, None, None, 16)), 1, None),
+     q4.Q4_OK),
+    (lambda L: L.w4a16_linear_multi(FAKE, 2, 512, 128, layers((None, None, None, None, 0)), 1, None),
+     q4.Q4_OK),
     (lambda L: L.q8_quantize_weight(FAKE, None, 4, 100, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.q8_quantize_weight(FAKE, MISAL, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.q8_quantize_act(FAKE, None, 4, 128, MISAL, FAKE, None), q4.Q4_ERR_MISALIGNED),
@@ -96,3 +125,7 @@ def test_binding_refuses_cpu_tensors():
         q4.w4a16_linear(torch.zeros(1, 128, dtype=torch.float16),
                         torch.zeros(4, 64, dtype=torch.uint8),
                         torch.zeros(4, 1, dtype=torch.float16), None)
+    with pytest.raises(ValueError):
+        q4.w4a16_linear_multi(torch.zeros(1, 128, dtype=torch.float16),
+                              [(torch.zeros(4, 64, dtype=torch.uint8),
+                                torch.zeros(4, 1, dtype=torch.float16), None)])

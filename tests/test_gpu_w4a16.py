@@ -179,8 +179,10 @@ def test_gemv_variants(orc, M, N, K, sym):
 
 
 # Shapes that route to each variant of the batched-decode kernels (8 <= M <=
-# 64): X resident in LDS (M <= 16, K = 1024, 2048, 4096), the X ring with row
-# tiles of 16 (M <= 16, K = 6144), 32 (M = 20) and 64 (M = 33, 64), the
+# 64): X resident in LDS (M <= 16, K = 1024, 2048, 4096), code runs resident
+# in registers with X through the LDS ring (M = 20, 33, 64 at K = 1024, 2048,
+# 4096: one or two k-split groups), the X ring with row tiles of 16 (M <= 16,
+# K = 6144), 32 (M = 20) and 64 (M = 33, 64) at K = 3072 and 6144, the
 # skinny fallback (M <= 16, K = 3072); ragged M and N (the last block's
 # columns run past N).
 @pytest.mark.parametrize("M", [8, 16, 20, 33, 64])
