@@ -62,6 +62,10 @@ def _load():
         "orc_e4m3_decode": (ctypes.c_float, [ctypes.c_uint]),
         "orc_e5m2_decode": (ctypes.c_float, [ctypes.c_uint]),
         "orc_e2m1_decode": (ctypes.c_float, [ctypes.c_uint]),
+        "orc_e4m3_encode": (ctypes.c_uint, [ctypes.c_float]),
+        "orc_fp8_quantize_weight": (None, [_u16p, _f32p, _i64, _i64, _u8p, _f32p]),
+        "orc_fp8_quantize_act": (None, [_u16p, _f32p, _i64, _i64, _u8p, _f32p]),
+        "orc_fp8_gemm": (None, [_u8p, _i64, _i64, _u8p, _i64, _i64p, _i64, _f64p, _f64p]),
         "orc_num_threads": (_int, []),
     }
     for name, (res, args) in sig.items():
@@ -266,3 +270,61 @@ def e5m2_decode(code: int) -> float:
 
 def e2m1_decode(code: int) -> float:
     return float(_load().orc_e2m1_decode(code))
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest E4M3 code to x (ties to even, saturating at +-448)."""
+    return int(_load().orc_e4m3_encode(ctypes.c_float(x)))
+
+
+# --- FP8 E4M3 path (Quantization operators guide §4.1, §4.2) ------------------
+
+def fp8_quantize_weight(W, s=None):
+    """Per-output-channel E4M3 of W diag(s): (Wq uint8 codes [N,K], sw f32 [N]),
+    sw = max|w'| / 448."""
+    W = _half_bits(W)
+    N, K = W.shape
+    s = _smooth(s)
+    Wq = np.empty((N, K), np.uint8)
+    sw = np.empty(N, np.float32)
+    _load().orc_fp8_quantize_weight(_ptr(W, _u16p), _ptr(s, _f32p), N, K,
+                                    _ptr(Wq, _u8p), _ptr(sw, _f32p))
+    return Wq, sw
+
+
+def fp8_quantize_act(X, s=None):
+    """Per-token dynamic E4M3 of X / s: (Xq uint8 codes [M,K], sx f32 [M])."""
+    X = _half_bits(X)
+    M, K = X.shape
+    s = _smooth(s)
+    Xq = np.empty((M, K), np.uint8)
+    sx = np.empty(M, np.float32)
+    _load().orc_fp8_quantize_act(_ptr(X, _u16p), _ptr(s, _f32p), M, K,
+                                 _ptr(Xq, _u8p), _ptr(sx, _f32p))
+    return Xq, sx
+
+
+def fp8_gemm(Xq, Wq, rows=None):
+    """Exact acc = e4m3(Xq) e4m3(Wq)^T in fp64 and sum |products| ([rows or M, N])."""
+    Xq = np.ascontiguousarray(Xq, dtype=np.uint8)
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    r = _rows(rows)
+    n_rows = M if r is None else r.size
+    acc = np.empty((n_rows, N), np.float64)
+    aacc = np.empty((n_rows, N), np.float64)
+    _load().orc_fp8_gemm(_ptr(Xq, _u8p), M, K, _ptr(Wq, _u8p), N, _ptr(r, _i64p), n_rows,
+                         _ptr(acc, _f64p), _ptr(aacc, _f64p))
+    return acc, aacc
+
+
+def fp8_reference(acc, abs_acc, sx, sw, rows=None):
+    """Y = sx sw acc and its error scale B = sx sw sum|products| (fp64)
+    (Quantization operators guide §4.2: C = scale_A scale_B (A_fp8 @ B_fp8))."""
+    sx = np.asarray(sx, dtype=np.float64)
+    sw = np.asarray(sw, dtype=np.float64)
+    if rows is not None:
+        sx = sx[np.asarray(rows)]
+    scale = sx[:, None] * sw[None, :]
+    return scale * acc, scale * abs_acc

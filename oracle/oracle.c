@@ -433,6 +433,102 @@ float orc_e4m3_decode(unsigned code) { return decode_minifloat(code & 0xff, 4, 3
 float orc_e5m2_decode(unsigned code) { return decode_minifloat(code & 0xff, 5, 2, 1, 0); }
 float orc_e2m1_decode(unsigned code) { return decode_minifloat(code & 0xf, 2, 1, 0, 0); }
 
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 path (Quantization operators guide §4.1 formats, §4.2 scaled FP8
+ * GEMM: C = scale_A * scale_B * (A_fp8 @ B_fp8); Core ideas §2.1 E4M3 range
+ * +-448). Weights and activations both in E4M3, scaled per output channel
+ * and per token like the INT8 path, with 448 in place of 127.               */
+
+/* Nearest E4M3 value to x, ties to the even mantissa, saturating at +-448
+ * (the guide clamps to the format maximum before the cast), sign kept on
+ * zero. Written from the format: bias 7, three mantissa bits, exponent field
+ * 0 holds the subnormals m * 2^-9, the largest finite value is 1.75 * 2^8.  */
+unsigned orc_e4m3_encode(float x)
+{
+    unsigned sign = signbit(x) ? 0x80u : 0u;
+    float a = fabsf(x);
+    if (a >= 448.0f) return sign | 0x7Eu;
+    if (a < ldexpf(1.0f, -6)) {                 /* subnormal range: quantum 2^-9 */
+        int q = (int)rintf(ldexpf(a, 9));       /* exact scaling, RNE */
+        return sign | (unsigned)q;              /* q == 8 is the smallest normal, 0x08 */
+    }
+    int e;
+    frexpf(a, &e);                              /* a = f * 2^e, f in [0.5, 1) */
+    e -= 1;                                     /* a in [2^e, 2^(e+1)) */
+    int q = (int)rintf(ldexpf(a, 3 - e));       /* 8 .. 16: mantissa with the implicit 1 */
+    if (q == 16) {
+        q = 8;
+        e += 1;
+    }
+    unsigned code = (unsigned)((e + 7) << 3) | (unsigned)(q - 8);
+    if (code > 0x7Eu) code = 0x7Eu;             /* rounding up past 448 saturates */
+    return sign | code;
+}
+
+/* One row of the FP8 quantizer: v[k] = x * s[k] (weight, mul != 0) or
+ * x / s[k] (activation), a = max(max_k |v|, 1e-8), scale = a / 448,
+ * q[k] = e4m3(v[k] / scale).                                                */
+static void fp8_row(const uint16_t *x, const float *s, int64_t K, int mul, uint8_t *q,
+                    float *scale_out)
+{
+    float a = 0.0f;
+    for (int64_t k = 0; k < K; k++) {
+        float v = orc_h2f(x[k]);
+        if (s) v = mul ? v * s[k] : v / s[k];
+        if (fabsf(v) > a) a = fabsf(v);
+    }
+    if (a < 1e-8f) a = 1e-8f;
+    float scale = a / 448.0f;
+    for (int64_t k = 0; k < K; k++) {
+        float v = orc_h2f(x[k]);
+        if (s) v = mul ? v * s[k] : v / s[k];
+        q[k] = (uint8_t)orc_e4m3_encode(v / scale);
+    }
+    *scale_out = scale;
+}
+
+/* Per-output-channel E4M3 weight of W diag(s) (s == NULL: s = 1). */
+void orc_fp8_quantize_weight(const uint16_t *W, const float *s, int64_t N, int64_t K,
+                             uint8_t *Wq, float *sw)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) fp8_row(W + n * K, s, K, 1, Wq + n * K, sw + n);
+}
+
+/* Per-token dynamic E4M3 activation of X / s (s == NULL: X as is). */
+void orc_fp8_quantize_act(const uint16_t *X, const float *s, int64_t M, int64_t K,
+                          uint8_t *Xq, float *sx)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) fp8_row(X + m * K, s, K, 0, Xq + m * K, sx + m);
+}
+
+/* FP8 GEMM reference: acc[i][n] = sum_k e4m3(Xq[m][k]) * e4m3(Wq[n][k]) for
+ * the listed rows (all when rows == NULL), and sum_k |product|. Each product
+ * is a multiple of 2^-18 below 2^18, so K <= 2^16 of them sum exactly in
+ * fp64: the reference is the exact sum.                                      */
+void orc_fp8_gemm(const uint8_t *Xq, int64_t M, int64_t K, const uint8_t *Wq, int64_t N,
+                  const int64_t *rows, int64_t n_rows, double *acc, double *abs_acc)
+{
+    if (!rows) n_rows = M;
+    float lut[256];
+    for (int c = 0; c < 256; c++) lut[c] = orc_e4m3_decode((unsigned)c);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t i = 0; i < n_rows; i++) {
+            int64_t m = rows ? rows[i] : i;
+            double a = 0.0, b = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = (double)lut[Xq[m * K + k]] * (double)lut[Wq[n * K + k]];
+                a += p;
+                b += fabs(p);
+            }
+            acc[i * N + n] = a;
+            abs_acc[i * N + n] = b;
+        }
+    }
+}
+
 /* Number of OpenMP threads a parallel region of this library uses. */
 #ifdef _OPENMP
 #include <omp.h>
