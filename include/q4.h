@@ -221,6 +221,56 @@ Q4_API q4_status w8a8_linear(const void *X, int64_t M, int64_t N, int64_t K,
                              size_t workspace_bytes, int32_t *acc_out, void *stream);
 
 /* ----------------------------------------------------------------------------
+ * FP8 E4M3 variant of the W8A8 path (Operators guide §4.1 formats: E4M3 for
+ * weights and activations; §4.2 scaled FP8 GEMM, C = scale_A * scale_B *
+ * (A_fp8 @ B_fp8); Core ideas §2.1: E4M3 range +-448). The scales are
+ * per output channel and per token as in the INT8 path, with 448 for 127.
+ * Codes are OCP E4M3 bytes (bias 7, S.1111.111 is NaN and never produced).
+ *
+ * fp8_quantize_weight / fp8_quantize_act -- per-row E4M3 of W diag(s) /
+ * of X / s (smooth_s == NULL: s = 1):
+ *   v = w * s[k] (weights) or x / s[k] (activations, IEEE fp32),
+ *   scale[row] = max(max_k |v|, 1e-8) / 448,
+ *   q = e4m3(v / scale): the nearest E4M3 value, ties to even, sign kept on
+ *       zero (the quotient never exceeds 448 by more than rounding).
+ * Codes and scales are bit-exact with the IEEE definition.
+ * W / X fp16 [rows, K] (16-byte aligned, K % 8 == 0); smooth_s fp32 [K] or
+ * NULL (16-byte aligned); codes u8 [rows, K] (16-byte aligned); scale fp32
+ * [rows]. Errors: INVALID_ARG, MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status fp8_quantize_weight(const void *W, const float *smooth_s, int64_t N,
+                                     int64_t K, uint8_t *Wq, float *w_scale, void *stream);
+Q4_API q4_status fp8_quantize_act(const void *X, const float *smooth_s, int64_t M,
+                                  int64_t K, uint8_t *Xq, float *x_scale, void *stream);
+
+/* ----------------------------------------------------------------------------
+ * fp8_gemm -- E4M3 GEMM with fp32 accumulation and the scale epilogue:
+ *   acc[m][n] = sum_k e4m3(Xq[m][k]) * e4m3(Wq[n][k])   (fp32 sums of exact
+ *               products, in the matrix cores' order),
+ *   Y[m][n]   = fp16((acc * x_scale[m]) * w_scale[n]).
+ * Accuracy: |Y - Y_ref| <= 2^-10 * x_scale w_scale sum_k |products| (+2^-25)
+ * against the exact sum (K <= 8192 keeps the fp32 sum within half of it).
+ * Xq, Wq u8 E4M3 codes [M, K], [N, K] (16-byte aligned); x_scale fp32 [M];
+ * w_scale fp32 [N]; Y fp16 [M, N] output. K must be a multiple of 128.
+ * Errors: INVALID_ARG (shape; K > 8192), UNSUPPORTED (K % 128 != 0),
+ *         MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status fp8_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t *Wq,
+                          const float *w_scale, int64_t M, int64_t N, int64_t K, void *Y,
+                          void *stream);
+
+/* ----------------------------------------------------------------------------
+ * fp8_linear -- fp8_quantize_act of X (with /smooth_s fused in) into the
+ * workspace, then fp8_gemm; the workspace is sized and laid out as for
+ * w8a8_linear (w8a8_workspace_bytes(M, K) bytes, 256-byte aligned: E4M3 codes
+ * [M, K], then x_scale [M] at offset round_up(M*K, 256)). smooth_s as for
+ * w8a8_linear. Errors: as for fp8_gemm, plus a too small workspace.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status fp8_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *Wq,
+                            const float *w_scale, const float *smooth_s, void *Y,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* ----------------------------------------------------------------------------
  * smoothquant_scales -- the SmoothQuant migration factor from calibration
  * activations (Operators guide §5.1; Core ideas §2.4; Quantization notes,
  * SmoothQuant):

@@ -15,6 +15,10 @@ Functions (same names as the C ABI):
   w8a8_gemm(Xq, x_scale, Wq, w_scale, acc_out=None) -> Y
   w8a8_linear(X, Wq, w_scale, smooth_s=None, workspace=None, acc_out=None) -> Y
   smoothquant_scales(Xcal, W, alpha=0.5) -> s
+  fp8_quantize_weight(W, smooth_s=None) -> (Wq, w_scale)      E4M3 codes as uint8
+  fp8_quantize_act(X, smooth_s=None) -> (Xq, x_scale)
+  fp8_gemm(Xq, x_scale, Wq, w_scale) -> Y
+  fp8_linear(X, Wq, w_scale, smooth_s=None, workspace=None) -> Y
 """
 from __future__ import annotations
 
@@ -52,6 +56,10 @@ SIGNATURES = {
     "w8a8_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                                    ctypes.c_size_t, _vp, _vp]),
     "smoothquant_scales": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, ctypes.c_float, _vp, _vp]),
+    "fp8_quantize_weight": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_quantize_act": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "fp8_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -184,12 +192,30 @@ def w4a16_linear_multi(X: torch.Tensor, layers, g: int = 128, out=None):
     return Ys
 
 
+def _need_smooth(smooth_s, K: int):
+    if smooth_s is not None:
+        _need(smooth_s, torch.float32, "smooth_s", 1)
+        if smooth_s.numel() != K:
+            raise ValueError(f"smooth_s has {smooth_s.numel()} entries, K={K}")
+
+
+def _row_outputs(out, rows: int, K: int, code_dtype, device):
+    if out is None:
+        return (torch.empty((rows, K), dtype=code_dtype, device=device),
+                torch.empty((rows,), dtype=torch.float32, device=device))
+    q, sc = out
+    _need(q, code_dtype, "codes", 2)
+    _need(sc, torch.float32, "scale", 1)
+    if tuple(q.shape) != (rows, K) or sc.numel() != rows:
+        raise ValueError("out tensors do not match the input's shape")
+    return q, sc
+
+
 def q8_quantize_weight(W: torch.Tensor, smooth_s: torch.Tensor | None = None):
     """Per-output-channel INT8 of W diag(s): (Wq int8 [N, K], w_scale fp32 [N])."""
     _need(W, torch.float16, "W", 2)
-    if smooth_s is not None:
-        _need(smooth_s, torch.float32, "smooth_s", 1)
     N, K = W.shape
+    _need_smooth(smooth_s, K)
     Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
     sw = torch.empty((N,), dtype=torch.float32, device=W.device)
     _check(lib().q8_quantize_weight(_ptr(W), _ptr(smooth_s), N, K, _ptr(Wq), _ptr(sw), _stream(W)))
@@ -199,14 +225,9 @@ def q8_quantize_weight(W: torch.Tensor, smooth_s: torch.Tensor | None = None):
 def q8_quantize_act(X: torch.Tensor, smooth_s: torch.Tensor | None = None, out=None):
     """Per-token dynamic INT8 of X / s: (Xq int8 [M, K], x_scale fp32 [M])."""
     _need(X, torch.float16, "X", 2)
-    if smooth_s is not None:
-        _need(smooth_s, torch.float32, "smooth_s", 1)
     M, K = X.shape
-    if out is None:
-        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
-        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
-    else:
-        Xq, sx = out
+    _need_smooth(smooth_s, K)
+    Xq, sx = _row_outputs(out, M, K, torch.int8, X.device)
     _check(lib().q8_quantize_act(_ptr(X), _ptr(smooth_s), M, K, _ptr(Xq), _ptr(sx), _stream(X)))
     return Xq, sx
 
@@ -227,7 +248,7 @@ def w8a8_gemm(Xq: torch.Tensor, x_scale: torch.Tensor, Wq: torch.Tensor, w_scale
         _need(acc_out, torch.int32, "acc_out", 2)
         if acc_out.shape != (M, N):
             raise ValueError("acc_out must be [M, N]")
-    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    Y = _output(out, M, N, Xq.device)
     _check(lib().w8a8_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y),
                            _ptr(acc_out), _stream(Xq)))
     return Y
@@ -250,18 +271,19 @@ def w8a8_linear(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
     _need(X, torch.float16, "X", 2)
     _need(Wq, torch.int8, "Wq", 2)
     _need(w_scale, torch.float32, "w_scale", 1)
-    if smooth_s is not None:
-        _need(smooth_s, torch.float32, "smooth_s", 1)
     M, K = X.shape
     N = Wq.shape[0]
-    if Wq.shape[1] != K:
-        raise ValueError("w8a8_linear: Wq must be [N, K]")
+    _need_smooth(smooth_s, K)
+    if Wq.shape[1] != K or w_scale.numel() != N:
+        raise ValueError("w8a8_linear: Wq must be [N, K] and w_scale [N]")
     if workspace is None:
         workspace = w8a8_workspace(M, K, X.device)
     _need(workspace, torch.uint8, "workspace", 1)
     if acc_out is not None:
         _need(acc_out, torch.int32, "acc_out", 2)
-    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=X.device)
+        if acc_out.shape != (M, N):
+            raise ValueError("acc_out must be [M, N]")
+    Y = _output(out, M, N, X.device)
     _check(lib().w8a8_linear(_ptr(X), M, N, K, _ptr(Wq), _ptr(w_scale), _ptr(smooth_s), _ptr(Y),
                              _ptr(workspace), workspace.numel(), _ptr(acc_out), _stream(X)))
     return Y
@@ -279,3 +301,63 @@ def smoothquant_scales(Xcal: torch.Tensor, W: torch.Tensor, alpha: float = 0.5):
     _check(lib().smoothquant_scales(_ptr(Xcal), R, _ptr(W), N, K, ctypes.c_float(alpha), _ptr(s),
                                     _stream(W)))
     return s
+
+
+# --- FP8 E4M3 variant of the W8A8 path ------------------------------------------
+
+def fp8_quantize_weight(W: torch.Tensor, smooth_s: torch.Tensor | None = None, out=None):
+    """Per-output-channel E4M3 of W diag(s): (Wq uint8 codes [N, K], w_scale fp32 [N])."""
+    _need(W, torch.float16, "W", 2)
+    N, K = W.shape
+    _need_smooth(smooth_s, K)
+    Wq, sw = _row_outputs(out, N, K, torch.uint8, W.device)
+    _check(lib().fp8_quantize_weight(_ptr(W), _ptr(smooth_s), N, K, _ptr(Wq), _ptr(sw), _stream(W)))
+    return Wq, sw
+
+
+def fp8_quantize_act(X: torch.Tensor, smooth_s: torch.Tensor | None = None, out=None):
+    """Per-token dynamic E4M3 of X / s: (Xq uint8 codes [M, K], x_scale fp32 [M])."""
+    _need(X, torch.float16, "X", 2)
+    M, K = X.shape
+    _need_smooth(smooth_s, K)
+    Xq, sx = _row_outputs(out, M, K, torch.uint8, X.device)
+    _check(lib().fp8_quantize_act(_ptr(X), _ptr(smooth_s), M, K, _ptr(Xq), _ptr(sx), _stream(X)))
+    return Xq, sx
+
+
+def fp8_gemm(Xq: torch.Tensor, x_scale: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
+             out: torch.Tensor | None = None):
+    """Y fp16 [M, N] = fp16((e4m3(Xq) e4m3(Wq)^T) * x_scale[m] * w_scale[n]), fp32 sums."""
+    _need(Xq, torch.uint8, "Xq", 2)
+    _need(Wq, torch.uint8, "Wq", 2)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or x_scale.numel() != M or w_scale.numel() != N:
+        raise ValueError("fp8_gemm: shape mismatch")
+    Y = _output(out, M, N, Xq.device)
+    _check(lib().fp8_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y),
+                          _stream(Xq)))
+    return Y
+
+
+def fp8_linear(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
+               smooth_s: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+               out: torch.Tensor | None = None):
+    """FP8 E4M3 linear layer: per-token E4M3 of X / s, E4M3 GEMM, fp16 epilogue."""
+    _need(X, torch.float16, "X", 2)
+    _need(Wq, torch.uint8, "Wq", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = X.shape
+    N = Wq.shape[0]
+    _need_smooth(smooth_s, K)
+    if Wq.shape[1] != K or w_scale.numel() != N:
+        raise ValueError("fp8_linear: Wq must be [N, K] and w_scale [N]")
+    if workspace is None:
+        workspace = w8a8_workspace(M, K, X.device)
+    _need(workspace, torch.uint8, "workspace", 1)
+    Y = _output(out, M, N, X.device)
+    _check(lib().fp8_linear(_ptr(X), M, N, K, _ptr(Wq), _ptr(w_scale), _ptr(smooth_s), _ptr(Y),
+                            _ptr(workspace), workspace.numel(), _stream(X)))
+    return Y

@@ -223,6 +223,79 @@ Q4_API q4_status w8a8_linear(const void *X, int64_t M, int64_t N, int64_t K, con
     return w8a8_gemm(xq, sx, Wq, w_scale, M, N, K, Y, acc_out, stream);
 }
 
+Q4_API q4_status fp8_quantize_weight(const void *W, const float *smooth_s, int64_t N, int64_t K,
+                                     uint8_t *Wq, float *w_scale, void *stream)
+{
+    Q4_REQUIRE(N >= 0 && K > 0 && N <= kIntMax && K <= kIntMax && K % 8 == 0, Q4_ERR_INVALID_ARG,
+               "fp8_quantize_weight: bad shape N=%lld K=%lld (K must be a positive multiple of 8)",
+               (long long)N, (long long)K);
+    if (N == 0) return ok();
+    Q4_REQUIRE(W && Wq && w_scale, Q4_ERR_INVALID_ARG, "fp8_quantize_weight: null pointer");
+    Q4_REQUIRE(aligned16(W) && aligned16(Wq) && (!smooth_s || aligned16(smooth_s)),
+               Q4_ERR_MISALIGNED, "fp8_quantize_weight: W, Wq and smooth_s must be 16-byte aligned");
+    hipError_t e = q4k::launch_fp8_weight(static_cast<const uint16_t *>(W), smooth_s, N, K, Wq,
+                                          w_scale, static_cast<hipStream_t>(stream));
+    return from_hip(e, "fp8_quantize_weight");
+}
+
+Q4_API q4_status fp8_quantize_act(const void *X, const float *smooth_s, int64_t M, int64_t K,
+                                  uint8_t *Xq, float *x_scale, void *stream)
+{
+    Q4_REQUIRE(M >= 0 && K > 0 && M <= kIntMax && K <= kIntMax && K % 8 == 0, Q4_ERR_INVALID_ARG,
+               "fp8_quantize_act: bad shape M=%lld K=%lld (K must be a positive multiple of 8)",
+               (long long)M, (long long)K);
+    if (M == 0) return ok();
+    Q4_REQUIRE(X && Xq && x_scale, Q4_ERR_INVALID_ARG, "fp8_quantize_act: null pointer");
+    Q4_REQUIRE(aligned16(X) && aligned16(Xq) && (!smooth_s || aligned16(smooth_s)),
+               Q4_ERR_MISALIGNED, "fp8_quantize_act: X, Xq and smooth_s must be 16-byte aligned");
+    hipError_t e = q4k::launch_fp8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, Xq, x_scale,
+                                       static_cast<hipStream_t>(stream));
+    return from_hip(e, "fp8_quantize_act");
+}
+
+Q4_API q4_status fp8_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t *Wq,
+                          const float *w_scale, int64_t M, int64_t N, int64_t K, void *Y,
+                          void *stream)
+{
+    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= 8192,
+               Q4_ERR_INVALID_ARG, "fp8_gemm: bad shape M=%lld N=%lld K=%lld (K <= 8192)",
+               (long long)M, (long long)N, (long long)K);
+    Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "fp8_gemm: K=%lld must be a multiple of 128",
+               (long long)K);
+    Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "fp8_gemm: M=%lld too large", (long long)M);
+    if (M == 0 || N == 0) return ok();
+    Q4_REQUIRE(Xq && x_scale && Wq && w_scale && Y, Q4_ERR_INVALID_ARG, "fp8_gemm: null pointer");
+    Q4_REQUIRE(aligned16(Xq) && aligned16(Wq), Q4_ERR_MISALIGNED,
+               "fp8_gemm: Xq and Wq must be 16-byte aligned");
+    hipError_t e = q4k::launch_fp8_gemm(Xq, x_scale, Wq, w_scale, M, N, K,
+                                        static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
+    return from_hip(e, "fp8_gemm");
+}
+
+Q4_API q4_status fp8_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *Wq,
+                            const float *w_scale, const float *smooth_s, void *Y, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= 8192,
+               Q4_ERR_INVALID_ARG, "fp8_linear: bad shape M=%lld N=%lld K=%lld (K <= 8192)",
+               (long long)M, (long long)N, (long long)K);
+    Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "fp8_linear: K=%lld must be a multiple of 128",
+               (long long)K);
+    if (M == 0 || N == 0) return ok();
+    Q4_REQUIRE(X && Wq && w_scale && Y && workspace, Q4_ERR_INVALID_ARG, "fp8_linear: null pointer");
+    Q4_REQUIRE(workspace_bytes >= w8a8_workspace_bytes(M, K), Q4_ERR_INVALID_ARG,
+               "fp8_linear: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+               w8a8_workspace_bytes(M, K));
+    Q4_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, Q4_ERR_MISALIGNED,
+               "fp8_linear: workspace must be 256-byte aligned");
+    uint8_t *xq = static_cast<uint8_t *>(workspace);
+    float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                          ((size_t)M * (size_t)K + 255) / 256 * 256);
+    q4_status st = fp8_quantize_act(X, smooth_s, M, K, xq, sx, stream);
+    if (st != Q4_OK) return st;
+    return fp8_gemm(xq, sx, Wq, w_scale, M, N, K, Y, stream);
+}
+
 Q4_API q4_status smoothquant_scales(const void *Xcal, int64_t R, const void *W, int64_t N,
                                     int64_t K, float alpha, float *s, void *stream)
 {

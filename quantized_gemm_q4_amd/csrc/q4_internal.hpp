@@ -11,6 +11,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef int intx16 __attribute__((ext_vector_type(16)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -62,5 +63,13 @@ hipError_t launch_w4a16_gemv_multi(const uint16_t *X, int64_t M, int64_t K, int 
 hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
                             const float *sw, int64_t M, int64_t N, int64_t K, uint16_t *Y,
                             int32_t *acc_out, hipStream_t st);
+// FP8 E4M3 path: per-row quantizers (codes as bytes) and the GEMM (K % 128
+// == 0; hipErrorNotSupported otherwise).
+hipError_t launch_fp8_weight(const uint16_t *W, const float *s, int64_t N, int64_t K, uint8_t *Wq,
+                             float *sw, hipStream_t st);
+hipError_t launch_fp8_act(const uint16_t *X, const float *s, int64_t M, int64_t K, uint8_t *Xq,
+                          float *sx, hipStream_t st);
+hipError_t launch_fp8_gemm(const uint8_t *Xq, const float *sx, const uint8_t *Wq, const float *sw,
+                           int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t st);
 
 }  // namespace q4k

@@ -252,27 +252,48 @@ __device__ __forceinline__ void load_row_chunk(const uint16_t *__restrict__ row,
     }
 }
 
-__device__ __forceinline__ u32x2 q8_codes(const float v[8], float scale)
+// Row formats: INT8 codes rint(v / scale) clipped to +-127, or FP8 E4M3
+// codes of v / scale (the nearest E4M3 value, ties to even, sign kept on
+// zero; the hardware conversion v_cvt_pk_fp8_f32 rounds to nearest even and
+// the quotient is clamped to +-448 first, so nothing saturates in it). The
+// scale is max |v| / 127 or max |v| / 448 (Quantization operators guide
+// §2.1, §4.2).
+template <bool FP8> constexpr float kRowMax = FP8 ? 448.0f : 127.0f;
+
+// four quotients -> four code bytes (quotient i in byte i)
+template <bool FP8>
+__device__ __forceinline__ uint32_t row_codes4(float q0, float q1, float q2, float q3)
 {
-    u32x2 out = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const float q = fminf(fmaxf(rintf(v[i] / scale), -127.0f), 127.0f);
-        out[i / 4] |= ((uint32_t)(int32_t)q & 0xffu) << (8 * (i % 4));
+    if constexpr (FP8) {
+        auto c = [](float q) { return fminf(fmaxf(q, -448.0f), 448.0f); };
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(q0), c(q1), 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(c(q2), c(q3), w, true);
+        return (uint32_t)w;
+    } else {
+        auto c = [](float q) { return (uint32_t)(int32_t)fminf(fmaxf(rintf(q), -127.0f), 127.0f) & 0xffu; };
+        return c(q0) | (c(q1) << 8) | (c(q2) << 16) | (c(q3) << 24);
     }
-    return out;
 }
 
-template <bool DIV, int CPT>
+template <bool FP8>
+__device__ __forceinline__ u32x2 row_codes8(const float v[8], float scale)
+{
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) q[i] = v[i] / scale;
+    return u32x2{row_codes4<FP8>(q[0], q[1], q[2], q[3]), row_codes4<FP8>(q[4], q[5], q[6], q[7])};
+}
+
+template <bool FP8, bool DIV, int CPT>
 __global__ __launch_bounds__(kThreads) void q8_rows_generic_kernel(const uint16_t *__restrict__ X,
                                                           const float *__restrict__ s,
-                                                          int64_t K, int8_t *__restrict__ Q,
+                                                          int64_t K, uint8_t *__restrict__ Q,
                                                           float *__restrict__ scale_out)
 {
     __shared__ float red[4];
     const int64_t r = blockIdx.x;
     const uint16_t *row = X + r * K;
-    int8_t *qrow = Q + r * K;
+    uint8_t *qrow = Q + r * K;
     const int64_t step = (int64_t)kThreads * 8;
     float a = 0.0f;
     if (CPT > 0) {
@@ -287,11 +308,11 @@ __global__ __launch_bounds__(kThreads) void q8_rows_generic_kernel(const uint16_
             }
         }
         a = fmaxf(block_max(a, red), 1e-8f);
-        const float scale = a / 127.0f;
+        const float scale = a / kRowMax<FP8>;
 #pragma unroll
         for (int c = 0; c < CPT; c++) {
             const int64_t k0 = threadIdx.x * 8 + c * step;
-            if (k0 < K) *reinterpret_cast<u32x2 *>(qrow + k0) = q8_codes(v[c], scale);
+            if (k0 < K) *reinterpret_cast<u32x2 *>(qrow + k0) = row_codes8<FP8>(v[c], scale);
         }
         if (threadIdx.x == 0) scale_out[r] = scale;
     } else {
@@ -302,10 +323,10 @@ __global__ __launch_bounds__(kThreads) void q8_rows_generic_kernel(const uint16_
             for (int i = 0; i < 8; i++) a = fmaxf(a, fabsf(v[i]));
         }
         a = fmaxf(block_max(a, red), 1e-8f);
-        const float scale = a / 127.0f;
+        const float scale = a / kRowMax<FP8>;
         for (int64_t k0 = threadIdx.x * 8; k0 < K; k0 += step) {
             load_row_chunk<DIV>(row, s, k0, v);
-            *reinterpret_cast<u32x2 *>(qrow + k0) = q8_codes(v, scale);
+            *reinterpret_cast<u32x2 *>(qrow + k0) = row_codes8<FP8>(v, scale);
         }
         if (threadIdx.x == 0) scale_out[r] = scale;
     }
@@ -352,10 +373,10 @@ __device__ __forceinline__ float halfwave_max(float a)
 // values v, the block's max |v| (one LDS slot per row, one barrier), the
 // scale by an IEEE fp32 division, and the codes rint(fl32(v / scale)) from
 // one fp64 multiply.
-template <bool DIV, bool HAS_S, int CPT, int RPB, int T>
+template <bool FP8, bool DIV, bool HAS_S, int CPT, int RPB, int T>
 __global__ __launch_bounds__(T) void q8_rows_kernel(const uint16_t *__restrict__ X,
                                                     const float *__restrict__ s, int64_t M,
-                                                    int64_t K, int8_t *__restrict__ Q,
+                                                    int64_t K, uint8_t *__restrict__ Q,
                                                     float *__restrict__ scale_out)
 {
     constexpr int HW = T / 32;   // half-wavefronts per block
@@ -435,18 +456,17 @@ __global__ __launch_bounds__(T) void q8_rows_kernel(const uint16_t *__restrict__
             a = fmaxf(a, fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
         }
         a = fmaxf(a, 1e-8f);
-        const float scale = a / 127.0f;
+        const float scale = a / kRowMax<FP8>;
         const double rs = recip64((double)scale);
         const int64_t r = r0 + rr;
         if (r < M) {
 #pragma unroll
             for (int c = 0; c < CPT; c++) {
-                u32x2 out = {0u, 0u};
+                float q[8];
 #pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    const float q = fminf(fmaxf(rintf((float)((double)v[c][i] * rs)), -127.0f), 127.0f);
-                    out[i / 4] |= ((uint32_t)(int32_t)q & 0xffu) << (8 * (i % 4));
-                }
+                for (int i = 0; i < 8; i++) q[i] = (float)((double)v[c][i] * rs);   // fl32(v / scale)
+                const u32x2 out = {row_codes4<FP8>(q[0], q[1], q[2], q[3]),
+                                   row_codes4<FP8>(q[4], q[5], q[6], q[7])};
                 if (kin[c]) *reinterpret_cast<u32x2 *>(Q + r * K + kc[c]) = out;
             }
             if (t == 0) scale_out[r] = scale;
@@ -454,8 +474,8 @@ __global__ __launch_bounds__(T) void q8_rows_kernel(const uint16_t *__restrict__
     }
 }
 
-template <bool DIV>
-hipError_t launch_q8_rows(const uint16_t *X, const float *s, int64_t rows, int64_t K, int8_t *Q,
+template <bool FP8, bool DIV>
+hipError_t launch_q8_rows(const uint16_t *X, const float *s, int64_t rows, int64_t K, uint8_t *Q,
                           float *scale, hipStream_t st)
 {
     if (rows == 0) return hipSuccess;
@@ -463,13 +483,13 @@ hipError_t launch_q8_rows(const uint16_t *X, const float *s, int64_t rows, int64
     constexpr int RPB = 4, T = 512;
     const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
     if (K <= 4096) {
-        if (s) q8_rows_kernel<DIV, true, 1, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
-        else q8_rows_kernel<DIV, false, 1, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
+        if (s) q8_rows_kernel<FP8, DIV, true, 1, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
+        else q8_rows_kernel<FP8, DIV, false, 1, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
     } else if (K <= 8192) {
-        if (s) q8_rows_kernel<DIV, true, 2, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
-        else q8_rows_kernel<DIV, false, 2, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
+        if (s) q8_rows_kernel<FP8, DIV, true, 2, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
+        else q8_rows_kernel<FP8, DIV, false, 2, RPB, T><<<grid, T, 0, st>>>(X, s, rows, K, Q, scale);
     } else   // wider rows: one row per block, the row read twice
-        q8_rows_generic_kernel<DIV, 0><<<(unsigned)rows, kThreads, 0, st>>>(X, s, K, Q, scale);
+        q8_rows_generic_kernel<FP8, DIV, 0><<<(unsigned)rows, kThreads, 0, st>>>(X, s, K, Q, scale);
     return hipGetLastError();
 }
 
@@ -545,13 +565,25 @@ hipError_t launch_q4_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int 
 hipError_t launch_q8_weight(const uint16_t *W, const float *s, int64_t N, int64_t K, int8_t *Wq,
                             float *sw, hipStream_t st)
 {
-    return launch_q8_rows<false>(W, s, N, K, Wq, sw, st);
+    return launch_q8_rows<false, false>(W, s, N, K, reinterpret_cast<uint8_t *>(Wq), sw, st);
 }
 
 hipError_t launch_q8_act(const uint16_t *X, const float *s, int64_t M, int64_t K, int8_t *Xq,
                          float *sx, hipStream_t st)
 {
-    return launch_q8_rows<true>(X, s, M, K, Xq, sx, st);
+    return launch_q8_rows<false, true>(X, s, M, K, reinterpret_cast<uint8_t *>(Xq), sx, st);
+}
+
+hipError_t launch_fp8_weight(const uint16_t *W, const float *s, int64_t N, int64_t K, uint8_t *Wq,
+                             float *sw, hipStream_t st)
+{
+    return launch_q8_rows<true, false>(W, s, N, K, Wq, sw, st);
+}
+
+hipError_t launch_fp8_act(const uint16_t *X, const float *s, int64_t M, int64_t K, uint8_t *Xq,
+                          float *sx, hipStream_t st)
+{
+    return launch_q8_rows<true, true>(X, s, M, K, Xq, sx, st);
 }
 
 hipError_t launch_smooth_scales(const uint16_t *Xcal, int64_t R, const uint16_t *W, int64_t N,

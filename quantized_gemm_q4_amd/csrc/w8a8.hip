@@ -12,6 +12,8 @@
 //
 // Built with -ffp-contract=off: the epilogue is ((float)acc * sx) * sw, two
 // fp32 roundings then one fp16 rounding, the same expression as the pages'.
+#include <type_traits>
+
 #include "q4_internal.hpp"
 
 namespace q4k {
@@ -150,11 +152,19 @@ constexpr int OUT_STRIDE = LBN * 2 + 16;            // bytes per row of the stag
 constexpr int LDS_BYTES = LBM * OUT_STRIDE > LSTAGES * LSTAGE_BYTES ? LBM * OUT_STRIDE : LSTAGES * LSTAGE_BYTES;
 
 
+// The same kernel serves FP8 E4M3 operands (FP8 = true; Quantization
+// operators guide §4.2: C = scale_A scale_B (A_fp8 @ B_fp8)): each 64-byte
+// step is then one v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 tile (both k32
+// halves' fragments side by side: A and B agree on the k order, so the sum
+// is the same), with fp32 accumulators; the first half of a step's MFMAs is
+// tiles i = 0, 1, the second i = 2, 3. No int32 output in that form.
+template <bool FP8>
 __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int M, int N, int K, int tiles_m, uint16_t *__restrict__ Y,
     int32_t *__restrict__ acc_out)
 {
+    using Acc = typename std::conditional<FP8, floatx16, intx16>::type;
     __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -199,7 +209,7 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
     const int arow = (wm * 128 + l32) * LBK;
     const int brow = LBM * LBK + (wn * 64 + l32) * LBK;
 
-    intx16 acc[4][2];
+    Acc acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -225,12 +235,24 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
                 f.b[s][j] = *reinterpret_cast<const intx4 *>(stage + brow + j * 32 * LBK + co);
         }
     };
-    auto mma_half = [&](const Frags &f, int s) {   // the 8 MFMAs of k32 half s
+    auto mma_half = [&](const Frags &f, int s) {   // the first or second half of a step's MFMAs
+        if constexpr (FP8) {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+            for (int i = 2 * s; i < 2 * s + 2; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[s][j], f.a[s][i], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 2; j++) {
+                    const intx8 a = __builtin_shufflevector(f.a[0][i], f.a[1][i], 0, 1, 2, 3, 4, 5, 6, 7);
+                    const intx8 bb = __builtin_shufflevector(f.b[0][j], f.b[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
+                    // format 0 = E4M3 for both operands; scale operands 0 select the unscaled form
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bb, a, acc[i][j], 0, 0, 0, 0, 0, 0);
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[s][j], f.a[s][i], acc[i][j], 0, 0, 0);
+        }
     };
 
     // Software pipeline (five LDS stages, two register fragment sets). Step
@@ -268,22 +290,33 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
             read(lds + sn * LSTAGE_BYTES, f[u ^ 1]);
             issue(lds + sc * LSTAGE_BYTES, k + LSTAGES < KT ? k + LSTAGES : KT - 1);
             mma_half(f[u], 1);
-            // 12 fragment reads and 4 loads between the 8 MFMAs
+            if constexpr (FP8) {
+                // 12 fragment reads and 4 loads between the 4 MFMAs
 #pragma unroll
-            for (int g = 0; g < 6; g++) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                for (int g = 0; g < 4; g++) {
+                    if (g >= 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM read
+                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);               // DS read
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+                }
+            } else {
+                // 12 fragment reads and 4 loads between the 8 MFMAs
+#pragma unroll
+                for (int g = 0; g < 6; g++) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                }
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);       // VMEM read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);       // VMEM read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             sc = sn;
         }
     }
     Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
     // lane's outputs: row wm * 128 + 32 i + l32 of the block tile, columns
     // wn * 64 + 32 j + 8 q + 4 h + e for accumulator r = 4 q + e
+    if constexpr (!FP8) {
     if (acc_out) {
         const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(acc_out) & 15) == 0;
 #pragma unroll
@@ -306,6 +339,7 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
                     }
                 }
         }
+    }
     }
     // Epilogue: y = f2h((acc * sx[m]) * sw[n]), staged through LDS as the
     // block's 256 x 256 fp16 tile, then written back as whole rows with
@@ -379,12 +413,25 @@ hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
     if (M == 0 || N == 0) return hipSuccess;
     if (K % (2 * LBK) == 0 && M * K < (int64_t)1 << 31 && N * K < (int64_t)1 << 31) {
         const int tiles_m = (int)((M + LBM - 1) / LBM), tiles_n = (int)((N + LBN - 1) / LBN);
-        w8a8_gemm_large_kernel<<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N,
-                                                                 (int)K, tiles_m, Y, acc_out);
+        w8a8_gemm_large_kernel<false><<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N,
+                                                                        (int)K, tiles_m, Y, acc_out);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((N + QBN - 1) / QBN), (unsigned)((M + QBM - 1) / QBM));
     w8a8_gemm_kernel<<<grid, kThreads, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N, (int)K, Y, acc_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const uint8_t *Xq, const float *sx, const uint8_t *Wq, const float *sw,
+                           int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t st)
+{
+    if (M == 0 || N == 0) return hipSuccess;
+    if (K % (2 * LBK) != 0 || M * K >= (int64_t)1 << 31 || N * K >= (int64_t)1 << 31)
+        return hipErrorNotSupported;
+    const int tiles_m = (int)((M + LBM - 1) / LBM), tiles_n = (int)((N + LBN - 1) / LBN);
+    w8a8_gemm_large_kernel<true><<<tiles_m * tiles_n, 512, 0, st>>>(
+        reinterpret_cast<const int8_t *>(Xq), sx, reinterpret_cast<const int8_t *>(Wq), sw, (int)M,
+        (int)N, (int)K, tiles_m, Y, nullptr);
     return hipGetLastError();
 }
 
