@@ -19,10 +19,11 @@ The JSON line also carries:
   extra         the same step as two w4a16_linear launches, each layer alone,
                 prefill (M = 2048, sym) TFLOP/s against the fp16 MFMA peak,
                 W8A8 (M = 2048, K = N = 8192) TOP/s against the int8 peak,
+                its FP8 E4M3 variant TFLOP/s against the fp8 peak,
                 quantize + pack GB/s, batched decode M = 16 / 64.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
-                       [--only decode|prefill|w8a8|quant|batched] [--eager]
+                       [--only decode|prefill|w8a8|fp8|quant|batched] [--eager]
                        [--copy-calibration]
 """
 from __future__ import annotations
@@ -42,6 +43,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16
 INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # dense fp8
 METRIC = "W4A16 g128 GEMM: GB/s at M=1, TFLOP/s at M=2048 (% of roofline)"
 MALL_BYTES = 512 * 2 ** 20
 COPY_BYTES = 2 ** 30
@@ -73,7 +75,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", default=None, choices=["decode", "prefill", "w8a8", "quant", "batched"])
+    ap.add_argument("--only", default=None, choices=["decode", "prefill", "w8a8", "fp8", "quant", "batched"])
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference for the HBM byte counters)")
@@ -284,6 +286,32 @@ def main():
                          "gemm_us": tg * 1e6, "gemm_TOP/s": ops / tg / 1e12,
                          "gemm_frac_mfma_int8": ops / tg / 1e12 / INT8_MFMA_PEAK_TOPS,
                          "act_quant_us": ta * 1e6, "act_quant_GB/s": abytes / ta / 1e9}
+        del Wq, Xq
+
+    # ---- FP8 E4M3 variant of the same layer ------------------------------------
+    if only in (None, "w8a8", "fp8"):
+        w = workloads.w8a8()
+        s = q4.smoothquant_scales(gpu(w["Xcal"]), gpu(w["W"]), 0.5)
+        Wq, sw = q4.fp8_quantize_weight(gpu(w["W"]), s)
+        X = gpu(w["X"])
+        M, K = X.shape
+        N = Wq.shape[0]
+        ws = q4.w8a8_workspace(M, K, dev)
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        Xq, sx = q4.fp8_quantize_act(X, s)
+        for _ in range(3):
+            q4.fp8_linear(X, Wq, sw, s, workspace=ws, out=Y)
+        reps = 30
+        tl = timed(lambda i: q4.fp8_linear(X, Wq, sw, s, workspace=ws, out=Y), reps) / reps
+        tg = timed(lambda i: q4.fp8_gemm(Xq, sx, Wq, sw, out=Y), reps) / reps
+        ta = timed(lambda i: q4.fp8_quantize_act(X, s, out=(Xq, sx)), reps) / reps
+        ops = 2 * M * N * K
+        abytes = M * K * 2 + K * 4 + M * K + M * 4
+        extra["fp8"] = {"shape": [M, N, K], "linear_us": tl * 1e6, "linear_TFLOP/s": ops / tl / 1e12,
+                        "gemm_us": tg * 1e6, "gemm_TFLOP/s": ops / tg / 1e12,
+                        "gemm_frac_mfma_fp8": ops / tg / 1e12 / FP8_MFMA_PEAK_TFLOPS,
+                        "act_quant_us": ta * 1e6, "act_quant_GB/s": abytes / ta / 1e9}
+        del Wq, Xq
 
     # ---- known-size copy: scales the HBM byte counters (profiling runs only) -
     if args.copy_calibration:
