@@ -66,6 +66,9 @@ def _load():
         "orc_fp8_quantize_weight": (None, [_u16p, _f32p, _i64, _i64, _u8p, _f32p]),
         "orc_fp8_quantize_act": (None, [_u16p, _f32p, _i64, _i64, _u8p, _f32p]),
         "orc_fp8_gemm": (None, [_u8p, _i64, _i64, _u8p, _i64, _i64p, _i64, _f64p, _f64p]),
+        "orc_e2m1_encode": (ctypes.c_uint, [ctypes.c_float]),
+        "orc_mxfp4_quantize_weight": (None, [_u16p, _f32p, _i64, _i64, _u8p, _u8p]),
+        "orc_mxfp4_gemm": (None, [_u8p, _i64, _i64, _u8p, _u8p, _i64, _i64p, _i64, _f64p, _f64p]),
         "orc_num_threads": (_int, []),
     }
     for name, (res, args) in sig.items():
@@ -328,3 +331,58 @@ def fp8_reference(acc, abs_acc, sx, sw, rows=None):
         sx = sx[np.asarray(rows)]
     scale = sx[:, None] * sw[None, :]
     return scale * acc, scale * abs_acc
+
+
+# --- MXFP4 weights (Quantization operators guide §4.3) ------------------------
+
+def e2m1_encode(x: float) -> int:
+    """Nearest E2M1 code to x (ties to even, saturating at +-6, sign kept on zero)."""
+    return int(_load().orc_e2m1_encode(ctypes.c_float(x)))
+
+
+def mxfp4_quantize_weight(W, s=None):
+    """MXFP4 of W diag(s): (codes uint8 [N, K/2], E8M0 scales uint8 [N, K/32])."""
+    W = _half_bits(W)
+    N, K = W.shape
+    assert K % 32 == 0
+    s = _smooth(s)
+    codes = np.empty((N, K // 2), np.uint8)
+    scales = np.empty((N, K // 32), np.uint8)
+    _load().orc_mxfp4_quantize_weight(_ptr(W, _u16p), _ptr(s, _f32p), N, K,
+                                      _ptr(codes, _u8p), _ptr(scales, _u8p))
+    return codes, scales
+
+
+def mxfp4_dequant(codes, scales) -> np.ndarray:
+    """fp64 values of an MXFP4 weight [N, K]."""
+    lut = np.array([e2m1_decode(c) for c in range(16)])
+    codes = np.asarray(codes, dtype=np.uint8)
+    u = np.empty((codes.shape[0], codes.shape[1] * 2), np.uint8)
+    u[:, 0::2] = codes & 0xF
+    u[:, 1::2] = codes >> 4
+    sc = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    return lut[u] * np.repeat(sc, 32, axis=1)
+
+
+def mxfp4_gemm(Xq, codes, scales, rows=None):
+    """Exact acc = e4m3(Xq) (MXFP4 W)^T in fp64 and sum |products| ([rows or M, N])."""
+    Xq = np.ascontiguousarray(Xq, dtype=np.uint8)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    M, K = Xq.shape
+    N = codes.shape[0]
+    r = _rows(rows)
+    n_rows = M if r is None else r.size
+    acc = np.empty((n_rows, N), np.float64)
+    aacc = np.empty((n_rows, N), np.float64)
+    _load().orc_mxfp4_gemm(_ptr(Xq, _u8p), M, K, _ptr(codes, _u8p), _ptr(scales, _u8p), N,
+                           _ptr(r, _i64p), n_rows, _ptr(acc, _f64p), _ptr(aacc, _f64p))
+    return acc, aacc
+
+
+def mxfp4_reference(acc, abs_acc, sx, rows=None):
+    """Y = sx acc and its error scale B = sx sum|products| (fp64)."""
+    sx = np.asarray(sx, dtype=np.float64)
+    if rows is not None:
+        sx = sx[np.asarray(rows)]
+    return sx[:, None] * acc, sx[:, None] * abs_acc

@@ -529,6 +529,102 @@ void orc_fp8_gemm(const uint8_t *Xq, int64_t M, int64_t K, const uint8_t *Wq, in
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* MXFP4 weights (Quantization operators guide §4.3: FP4 E2M1 elements, one
+ * E8M0 scale per block of 32; weights in FP4, activations kept in FP8; the
+ * Schemes notes list the E2M1 value set {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4,
+ * +-6}).                                                                      */
+
+/* Nearest E2M1 value to x, ties to the even mantissa, saturating at +-6,
+ * sign kept on zero. Codes: sign bit 3, exponent bits 2-1 (bias 1), mantissa
+ * bit 0; exponent 0 is the subnormal 0.5 * m.                               */
+unsigned orc_e2m1_encode(float x)
+{
+    unsigned sign = signbit(x) ? 0x8u : 0u;
+    float a = fabsf(x);
+    if (a >= 6.0f) return sign | 0x7u;
+    if (a < 1.0f) return sign | (unsigned)rintf(a * 2.0f);   /* 0, 0.5, 1.0 (code 2) */
+    int e;
+    frexpf(a, &e);
+    e -= 1;                                                   /* a in [2^e, 2^(e+1)), e in 0..2 */
+    int q = (int)rintf(ldexpf(a, 1 - e));                     /* 2 or 3; 4 carries */
+    if (q == 4) {
+        q = 2;
+        e += 1;
+    }
+    unsigned code = (unsigned)((e + 1) << 1) | (unsigned)(q - 2);
+    if (code > 0x7u) code = 0x7u;
+    return sign | code;
+}
+
+/* MXFP4 quantizer of W diag(s) (s == NULL: s = 1), block of 32 along K:
+ *   v = w * s[k] (fp32), amax = max over the block of |v|,
+ *   scale = 2^(e - 127) with e the smallest integer such that amax <= 6 * 2^(e - 127)
+ *           (the smallest power of two that keeps every element in range;
+ *           e = 0 for an all-zero block; e <= 254),
+ *   code  = e2m1(v / scale) (exact division by a power of two).
+ * Codes packed two per byte along K (even k in the low nibble) [N, K/2];
+ * scales E8M0 bytes [N, K/32].                                               */
+void orc_mxfp4_quantize_weight(const uint16_t *W, const float *s, int64_t N, int64_t K,
+                               uint8_t *codes, uint8_t *scales)
+{
+    const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t b = 0; b < nb; b++) {
+            float v[32], amax = 0.0f;
+            for (int i = 0; i < 32; i++) {
+                int64_t k = b * 32 + i;
+                v[i] = orc_h2f(W[n * K + k]) * (s ? s[k] : 1.0f);
+                if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+            }
+            int e = 0;
+            if (amax > 0.0f) {
+                e = 1;
+                while (e < 254 && amax > 6.0f * ldexpf(1.0f, e - 127)) e++;
+                /* ldexpf(1, e - 127) is the subnormal 2^-126 at e = 1, exact */
+            }
+            scales[n * nb + b] = (uint8_t)e;
+            for (int i = 0; i < 32; i += 2) {
+                unsigned lo = orc_e2m1_encode(ldexpf(v[i], 127 - e));
+                unsigned hi = orc_e2m1_encode(ldexpf(v[i + 1], 127 - e));
+                codes[n * (K / 2) + b * 16 + i / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+}
+
+/* W4A8 reference: acc[i][n] = sum_k e4m3(Xq[m][k]) * e2m1(W[n][k]) * 2^(e[n][k/32] - 127)
+ * for the listed rows m, and the sum of |products|, in fp64 (exact while the
+ * block exponents of a row span fewer than about 30 binades).                 */
+void orc_mxfp4_gemm(const uint8_t *Xq, int64_t M, int64_t K, const uint8_t *codes,
+                    const uint8_t *scales, int64_t N, const int64_t *rows, int64_t n_rows,
+                    double *acc, double *abs_acc)
+{
+    if (!rows) n_rows = M;
+    float lut8[256], lut4[16];
+    for (int c = 0; c < 256; c++) lut8[c] = orc_e4m3_decode((unsigned)c);
+    for (int c = 0; c < 16; c++) lut4[c] = orc_e2m1_decode((unsigned)c);
+    const int64_t nb = K / 32;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t i = 0; i < n_rows; i++) {
+            int64_t m = rows ? rows[i] : i;
+            double a = 0.0, b = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                uint8_t byte = codes[n * (K / 2) + k / 2];
+                unsigned c4 = (k & 1) ? (byte >> 4) : (byte & 0xFu);
+                double w = ldexp((double)lut4[c4], (int)scales[n * nb + k / 32] - 127);
+                double p = (double)lut8[Xq[m * K + k]] * w;
+                a += p;
+                b += fabs(p);
+            }
+            acc[i * N + n] = a;
+            abs_acc[i * N + n] = b;
+        }
+    }
+}
+
 /* Number of OpenMP threads a parallel region of this library uses. */
 #ifdef _OPENMP
 #include <omp.h>
