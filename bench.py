@@ -19,11 +19,13 @@ The JSON line also carries:
   extra         the same step as two w4a16_linear launches, each layer alone,
                 prefill (M = 2048, sym) TFLOP/s against the fp16 MFMA peak,
                 W8A8 (M = 2048, K = N = 8192) TOP/s against the int8 peak,
-                its FP8 E4M3 variant TFLOP/s against the fp8 peak,
+                its FP8 E4M3 variant TFLOP/s against the fp8 peak, MXFP4
+                weights x E4M3 activations on that layer and on the prefill
+                shape,
                 quantize + pack GB/s, batched decode M = 16 / 64.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
-                       [--only decode|prefill|w8a8|fp8|quant|batched] [--eager]
+                       [--only decode|prefill|w8a8|fp8|mxfp4|quant|batched] [--eager]
                        [--copy-calibration]
 """
 from __future__ import annotations
@@ -75,7 +77,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", default=None, choices=["decode", "prefill", "w8a8", "fp8", "quant", "batched"])
+    ap.add_argument("--only", default=None, choices=["decode", "prefill", "w8a8", "fp8", "mxfp4", "quant",
+                                                     "batched"])
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference for the HBM byte counters)")
@@ -312,6 +315,33 @@ def main():
                         "gemm_frac_mfma_fp8": ops / tg / 1e12 / FP8_MFMA_PEAK_TFLOPS,
                         "act_quant_us": ta * 1e6, "act_quant_GB/s": abytes / ta / 1e9}
         del Wq, Xq
+
+    # ---- MXFP4 weights x E4M3 activations (W4A8) ------------------------------
+    if only in (None, "w8a8", "mxfp4"):
+        res = {}
+        # the W8A8 workload's layer, and the prefill workload's shape
+        for name in ("w8a8", "prefill"):
+            w = workloads.w8a8() if name == "w8a8" else workloads.prefill()
+            X = gpu(w["X"])
+            s = q4.smoothquant_scales(gpu(w["Xcal"]), gpu(w["W"]), 0.5) if name == "w8a8" else None
+            codes, sc = q4.mxfp4_quantize_weight(gpu(w["W"]), s)
+            M, K = X.shape
+            N = codes.shape[0]
+            ws = q4.w8a8_workspace(M, K, dev)
+            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            Xq, sx = q4.fp8_quantize_act(X, s)
+            for _ in range(3):
+                q4.mxfp4_linear(X, codes, sc, s, workspace=ws, out=Y)
+            reps = 30
+            tl = timed(lambda i: q4.mxfp4_linear(X, codes, sc, s, workspace=ws, out=Y), reps) / reps
+            tg = timed(lambda i: q4.mxfp4_gemm(Xq, sx, codes, sc, out=Y), reps) / reps
+            ops = 2 * M * N * K
+            res[name] = {"shape": [M, N, K], "linear_us": tl * 1e6, "linear_TFLOP/s": ops / tl / 1e12,
+                         "gemm_us": tg * 1e6, "gemm_TFLOP/s": ops / tg / 1e12,
+                         "gemm_frac_mfma_fp8": ops / tg / 1e12 / FP8_MFMA_PEAK_TFLOPS}
+            del codes, sc, Xq, X, Y, ws
+        extra["mxfp4_w4a8"] = res
+        torch.cuda.empty_cache()
 
     # ---- known-size copy: scales the HBM byte counters (profiling runs only) -
     if args.copy_calibration:

@@ -271,6 +271,54 @@ Q4_API q4_status fp8_linear(const void *X, int64_t M, int64_t N, int64_t K, cons
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* ----------------------------------------------------------------------------
+ * MXFP4 weights with E4M3 activations (W4A8) (Operators guide §4.3: FP4
+ * E2M1 elements sharing one E8M0 scale per block of 32, weights in FP4 and
+ * activations kept in FP8; Schemes notes: E2M1 = {0, +-0.5, ..., +-4, +-6}).
+ *
+ * mxfp4_quantize_weight -- per row n and block j of 32 along K:
+ *   v = w * s[k] (fp32; smooth_s == NULL: s = 1), amax = max_block |v|,
+ *   scale = 2^(e - 127), e = the smallest integer >= 1 with
+ *           amax <= 6 * 2^(e - 127) (e = 0 for an all-zero block),
+ *   code = e2m1(v / scale): the nearest E2M1 value, ties to the even code,
+ *          sign kept on zero (|v / scale| <= 6 by the choice of e).
+ * W fp16 [N, K] (16-byte aligned, K % 32 == 0); smooth_s fp32 [K] or NULL
+ * (16-byte aligned); codes u8 [N, K/2] output, two codes per byte along K
+ * (even k in the low nibble), 4-byte aligned; scales u8 [N, K/32] output
+ * (E8M0). 4.25 bits per weight. Codes and scales are bit-exact.
+ * Errors: INVALID_ARG, MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status mxfp4_quantize_weight(const void *W, const float *smooth_s, int64_t N,
+                                       int64_t K, uint8_t *codes, uint8_t *scales,
+                                       void *stream);
+
+/* ----------------------------------------------------------------------------
+ * mxfp4_gemm -- W4A8 GEMM on the scaled matrix cores:
+ *   acc[m][n] = sum_k e4m3(Xq[m][k]) * e2m1(code[n][k]) * 2^(scales[n][k/32] - 127)
+ *               (fp32 sums of exact products, in the matrix cores' order),
+ *   Y[m][n]   = fp16(acc * x_scale[m]).
+ * Accuracy: |Y - Y_ref| <= 2^-10 * x_scale sum_k |products| (+2^-25).
+ * Xq u8 E4M3 [M, K] and x_scale fp32 [M] as written by fp8_quantize_act;
+ * codes, scales as written by mxfp4_quantize_weight (Xq and codes 16-byte
+ * aligned); Y fp16 [M, N] output. K a multiple of 128, at most 8192.
+ * Errors: INVALID_ARG (shape, K > 8192), UNSUPPORTED (K % 128 != 0),
+ *         MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status mxfp4_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t *codes,
+                            const uint8_t *scales, int64_t M, int64_t N, int64_t K, void *Y,
+                            void *stream);
+
+/* ----------------------------------------------------------------------------
+ * mxfp4_linear -- fp8_quantize_act of X (with /smooth_s fused in) into the
+ * workspace (laid out as for w8a8_linear, w8a8_workspace_bytes(M, K) bytes,
+ * 256-byte aligned), then mxfp4_gemm. smooth_s as for w8a8_linear.
+ * Errors: as for mxfp4_gemm, plus a too small workspace.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status mxfp4_linear(const void *X, int64_t M, int64_t N, int64_t K,
+                              const uint8_t *codes, const uint8_t *scales,
+                              const float *smooth_s, void *Y, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* ----------------------------------------------------------------------------
  * smoothquant_scales -- the SmoothQuant migration factor from calibration
  * activations (Operators guide §5.1; Core ideas §2.4; Quantization notes,
  * SmoothQuant):

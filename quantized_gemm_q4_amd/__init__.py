@@ -19,6 +19,9 @@ Functions (same names as the C ABI):
   fp8_quantize_act(X, smooth_s=None) -> (Xq, x_scale)
   fp8_gemm(Xq, x_scale, Wq, w_scale) -> Y
   fp8_linear(X, Wq, w_scale, smooth_s=None, workspace=None) -> Y
+  mxfp4_quantize_weight(W, smooth_s=None) -> (codes, scales)  E2M1 + E8M0 per 32
+  mxfp4_gemm(Xq, x_scale, codes, scales) -> Y                 W4A8
+  mxfp4_linear(X, codes, scales, smooth_s=None, workspace=None) -> Y
 """
 from __future__ import annotations
 
@@ -60,6 +63,9 @@ SIGNATURES = {
     "fp8_quantize_act": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "fp8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "mxfp4_quantize_weight": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "mxfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "mxfp4_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -360,4 +366,59 @@ def fp8_linear(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
     Y = _output(out, M, N, X.device)
     _check(lib().fp8_linear(_ptr(X), M, N, K, _ptr(Wq), _ptr(w_scale), _ptr(smooth_s), _ptr(Y),
                             _ptr(workspace), workspace.numel(), _stream(X)))
+    return Y
+
+
+# --- MXFP4 weights with E4M3 activations (W4A8) ---------------------------------
+
+def mxfp4_quantize_weight(W: torch.Tensor, smooth_s: torch.Tensor | None = None):
+    """MXFP4 of W diag(s): (codes uint8 [N, K/2], E8M0 scales uint8 [N, K/32])."""
+    _need(W, torch.float16, "W", 2)
+    N, K = W.shape
+    _need_smooth(smooth_s, K)
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((N, K // 32), dtype=torch.uint8, device=W.device)
+    _check(lib().mxfp4_quantize_weight(_ptr(W), _ptr(smooth_s), N, K, _ptr(codes), _ptr(scales),
+                                       _stream(W)))
+    return codes, scales
+
+
+def _check_mxfp4(codes, scales, K: int) -> int:
+    _need(codes, torch.uint8, "codes", 2)
+    _need(scales, torch.uint8, "scales", 2)
+    N = codes.shape[0]
+    if codes.shape[1] * 2 != K or tuple(scales.shape) != (N, K // 32):
+        raise ValueError(f"codes {tuple(codes.shape)} / scales {tuple(scales.shape)} do not match K={K}")
+    return N
+
+
+def mxfp4_gemm(Xq: torch.Tensor, x_scale: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+               out: torch.Tensor | None = None):
+    """Y fp16 [M, N] = fp16(x_scale[m] * sum_k e4m3(Xq) e2m1(code) 2^(scale - 127))."""
+    _need(Xq, torch.uint8, "Xq", 2)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    M, K = Xq.shape
+    N = _check_mxfp4(codes, scales, K)
+    if x_scale.numel() != M:
+        raise ValueError("x_scale must have M entries")
+    Y = _output(out, M, N, Xq.device)
+    _check(lib().mxfp4_gemm(_ptr(Xq), _ptr(x_scale), _ptr(codes), _ptr(scales), M, N, K, _ptr(Y),
+                            _stream(Xq)))
+    return Y
+
+
+def mxfp4_linear(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                 smooth_s: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None):
+    """W4A8 linear layer: per-token E4M3 of X / s, MXFP4 weight, fp16 out."""
+    _need(X, torch.float16, "X", 2)
+    M, K = X.shape
+    N = _check_mxfp4(codes, scales, K)
+    _need_smooth(smooth_s, K)
+    if workspace is None:
+        workspace = w8a8_workspace(M, K, X.device)
+    _need(workspace, torch.uint8, "workspace", 1)
+    Y = _output(out, M, N, X.device)
+    _check(lib().mxfp4_linear(_ptr(X), M, N, K, _ptr(codes), _ptr(scales), _ptr(smooth_s), _ptr(Y),
+                              _ptr(workspace), workspace.numel(), _stream(X)))
     return Y

@@ -27,6 +27,7 @@ SOURCES = {
     "w4a16.hip": ["-ffp-contract=off"],
     "w4a16_gemv.hip": ["-ffp-contract=off"],
     "w8a8.hip": ["-ffp-contract=off"],
+    "mxfp4.hip": ["-ffp-contract=off"],
 }
 
 

@@ -296,6 +296,67 @@ Q4_API q4_status fp8_linear(const void *X, int64_t M, int64_t N, int64_t K, cons
     return fp8_gemm(xq, sx, Wq, w_scale, M, N, K, Y, stream);
 }
 
+Q4_API q4_status mxfp4_quantize_weight(const void *W, const float *smooth_s, int64_t N, int64_t K,
+                                       uint8_t *codes, uint8_t *scales, void *stream)
+{
+    Q4_REQUIRE(N >= 0 && K > 0 && N <= kIntMax && K <= kIntMax && K % 32 == 0, Q4_ERR_INVALID_ARG,
+               "mxfp4_quantize_weight: bad shape N=%lld K=%lld (K must be a positive multiple of 32)",
+               (long long)N, (long long)K);
+    if (N == 0) return ok();
+    Q4_REQUIRE(W && codes && scales, Q4_ERR_INVALID_ARG, "mxfp4_quantize_weight: null pointer");
+    Q4_REQUIRE(aligned16(W) && (!smooth_s || aligned16(smooth_s)) &&
+                   (reinterpret_cast<uintptr_t>(codes) & 3u) == 0,
+               Q4_ERR_MISALIGNED,
+               "mxfp4_quantize_weight: W and smooth_s must be 16-byte aligned, codes 4-byte aligned");
+    hipError_t e = q4k::launch_mxfp4_quantize(static_cast<const uint16_t *>(W), smooth_s, N, K, codes,
+                                              scales, static_cast<hipStream_t>(stream));
+    return from_hip(e, "mxfp4_quantize_weight");
+}
+
+Q4_API q4_status mxfp4_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t *codes,
+                            const uint8_t *scales, int64_t M, int64_t N, int64_t K, void *Y,
+                            void *stream)
+{
+    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= 8192,
+               Q4_ERR_INVALID_ARG, "mxfp4_gemm: bad shape M=%lld N=%lld K=%lld (K <= 8192)",
+               (long long)M, (long long)N, (long long)K);
+    Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "mxfp4_gemm: K=%lld must be a multiple of 128",
+               (long long)K);
+    Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "mxfp4_gemm: M=%lld too large", (long long)M);
+    if (M == 0 || N == 0) return ok();
+    Q4_REQUIRE(Xq && x_scale && codes && scales && Y, Q4_ERR_INVALID_ARG, "mxfp4_gemm: null pointer");
+    Q4_REQUIRE(aligned16(Xq) && aligned16(codes), Q4_ERR_MISALIGNED,
+               "mxfp4_gemm: Xq and codes must be 16-byte aligned");
+    hipError_t e = q4k::launch_mxfp4_gemm(Xq, x_scale, codes, scales, M, N, K,
+                                          static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
+    return from_hip(e, "mxfp4_gemm");
+}
+
+Q4_API q4_status mxfp4_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                              const uint8_t *scales, const float *smooth_s, void *Y, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= 8192,
+               Q4_ERR_INVALID_ARG, "mxfp4_linear: bad shape M=%lld N=%lld K=%lld (K <= 8192)",
+               (long long)M, (long long)N, (long long)K);
+    Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "mxfp4_linear: K=%lld must be a multiple of 128",
+               (long long)K);
+    if (M == 0 || N == 0) return ok();
+    Q4_REQUIRE(X && codes && scales && Y && workspace, Q4_ERR_INVALID_ARG,
+               "mxfp4_linear: null pointer");
+    Q4_REQUIRE(workspace_bytes >= w8a8_workspace_bytes(M, K), Q4_ERR_INVALID_ARG,
+               "mxfp4_linear: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+               w8a8_workspace_bytes(M, K));
+    Q4_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, Q4_ERR_MISALIGNED,
+               "mxfp4_linear: workspace must be 256-byte aligned");
+    uint8_t *xq = static_cast<uint8_t *>(workspace);
+    float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                          ((size_t)M * (size_t)K + 255) / 256 * 256);
+    q4_status st = fp8_quantize_act(X, smooth_s, M, K, xq, sx, stream);
+    if (st != Q4_OK) return st;
+    return mxfp4_gemm(xq, sx, codes, scales, M, N, K, Y, stream);
+}
+
 Q4_API q4_status smoothquant_scales(const void *Xcal, int64_t R, const void *W, int64_t N,
                                     int64_t K, float alpha, float *s, void *stream)
 {

@@ -1,0 +1,322 @@
+// MXFP4 weights with FP8 E4M3 activations (W4A8) on gfx950 (Quantization
+// operators guide §4.3: FP4 E2M1 elements with one E8M0 scale per block of
+// 32, weights in FP4 while the activations stay in FP8; Core ideas §2.1 and
+// the Schemes notes: E2M1 holds {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6}).
+//
+// Layout: codes [N, K/2], two E2M1 codes per byte along K (even k in the low
+// nibble), scales [N, K/32] E8M0 bytes (value 2^(e - 127)). The activations
+// are the per-token E4M3 codes and fp32 scales of fp8_quantize_act.
+//
+// The GEMM runs on v_mfma_scale_f32_32x32x64_f8f6f4 with the weight as the
+// first operand (format E2M1) and X as the second (format E4M3): each weight
+// lane supplies 32 consecutive k of one row, i.e. exactly one MX block, with
+// that block's E8M0 byte as its scale operand; X's scale operand is 1.0 (127).
+// Products are exact in fp32; the sums are fp32 in the matrix cores' order;
+// the epilogue is y = fp16(acc * x_scale[m]).
+#include <type_traits>
+
+#include "q4_internal.hpp"
+
+namespace q4k {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Quantizer. A lane owns 8 consecutive weights of a row (one 16-byte load),
+// four lanes one block of 32; the block's max |v| is a quad reduction. The
+// scale is the smallest power of two 2^(e - 127) with amax <= 6 * 2^(e - 127),
+// found from amax's exponent with one exact comparison (e = 0 for an all-zero
+// block); v * 2^(127 - e) is exact, and its E2M1 code is counted against the
+// rounding thresholds of the format with ties to the even code:
+// 0.25 (down), 0.75 (up), 1.25 (down), 1.75 (up), 2.5 (down), 3.5 (up),
+// 5 (down).
+__device__ __forceinline__ uint32_t e2m1_code(float x)
+{
+    const float a = fabsf(x);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return c | ((__builtin_bit_cast(uint32_t, x) >> 28) & 8u);   // sign bit of x
+}
+
+__device__ __forceinline__ float quad_max(float a)
+{
+    auto dpp = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    a = fmaxf(a, dpp(a, std::integral_constant<int, 0xB1>{}));   // quad swap 1 0 3 2
+    return fmaxf(a, dpp(a, std::integral_constant<int, 0x4E>{}));   // quad swap 2 3 0 1
+}
+
+template <bool HAS_S>
+__global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t *__restrict__ W,
+                                                             const float *__restrict__ s, int64_t N,
+                                                             int64_t K, uint8_t *__restrict__ codes,
+                                                             uint8_t *__restrict__ scales)
+{
+    const int64_t chunks = K >> 3;                        // 8-weight chunks per row
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = c < N * chunks;
+    const int64_t cc = live ? c : N * chunks - 1;         // idle lanes redo the last chunk
+    const int64_t row = cc / chunks, k0 = (cc % chunks) * 8;
+    const u32x4 raw = *reinterpret_cast<const u32x4 *>(W + row * K + k0);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        v[2 * i] = h2f((uint16_t)(raw[i] & 0xffffu));
+        v[2 * i + 1] = h2f((uint16_t)(raw[i] >> 16));
+    }
+    if (HAS_S) {
+        const floatx4 a = *reinterpret_cast<const floatx4 *>(s + k0);
+        const floatx4 b = *reinterpret_cast<const floatx4 *>(s + k0 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            v[i] *= a[i];
+            v[4 + i] *= b[i];
+        }
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+    const float amax = quad_max(m);   // the four lanes of a block are a quad (K % 32 == 0)
+    int e = 0;
+    if (amax > 0.0f) {
+        int ex;
+        const float f = frexpf(amax, &ex);   // amax = f * 2^ex, f in [0.5, 1)
+        // 6 * 2^(e - 127) = 0.75 * 2^(e - 124): e = ex + 124 if f <= 0.75, else ex + 125
+        e = ex + 124 + (f > 0.75f ? 1 : 0);
+        e = e < 1 ? 1 : (e > 254 ? 254 : e);
+    }
+    // 2^(127 - e), exact (a subnormal only at e = 254); an all-zero block
+    // multiplies by 0, which keeps every code 0 and every sign
+    const float mul = e == 0 ? 0.0f : ldexpf(1.0f, 127 - e);
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) out |= e2m1_code(v[i] * mul) << (4 * i);
+    if (live) {
+        *reinterpret_cast<uint32_t *>(codes + row * (K >> 1) + (k0 >> 1)) = out;
+        if ((threadIdx.x & 3) == 0) scales[row * (K >> 5) + (k0 >> 5)] = (uint8_t)e;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// W4A8 GEMM. The 256 x 256 tile kernel of the INT8 / FP8 path with a stage
+// per 64 k of: X 256 rows x 64 B (E4M3), W 256 rows x 32 B (E2M1) and the
+// W block scales 256 rows x 2 blocks, six stages (156 KB) filled by direct
+// global-to-LDS loads five steps ahead. Per stage a wavefront issues two X
+// loads (16 rows x 64 B each, 16-byte chunks XOR-swizzled by (row >> 2) & 3),
+// one W load (32 rows x 32 B) and one byte load of 64 scale bytes (32 rows x
+// 2 blocks; a byte-sized direct load still fills one dword of LDS per lane,
+// so the scale of row r, block h sits at dword 2 r + h), so the wait counts
+// are those of the FP8 kernel. The 8
+// wavefronts form a 2 (M) x 4 (N) grid of 128 x 64 sub-tiles; each step is
+// one MFMA per 32 x 32 tile (4 before the barrier, 4 after it, interleaved
+// with the next stage's reads). Accumulator tiles are Y transposed (the
+// weight is the first operand): a lane holds one row of Y and four
+// consecutive columns per group of four registers; the epilogue stages the
+// fp16 tile in LDS and writes whole rows with 16-byte stores.
+constexpr int MBM = 256, MBN = 256, MBK = 64, MSTAGES = 6;
+constexpr int MX_BYTES = MBM * MBK;                       // 16 KB of X
+constexpr int MW_BYTES = MBN * MBK / 2;                   // 8 KB of codes
+constexpr int MS_BYTES = MBN * 2 * 4;                     // 512 scale bytes, one per dword
+constexpr int MSTAGE_BYTES = MX_BYTES + MW_BYTES + MS_BYTES;
+constexpr int MOUT_STRIDE = MBN * 2 + 16;
+constexpr int MLDS_BYTES =
+    MBM * MOUT_STRIDE > MSTAGES * MSTAGE_BYTES ? MBM * MOUT_STRIDE : MSTAGES * MSTAGE_BYTES;
+
+__global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
+    const uint8_t *__restrict__ Xq, const float *__restrict__ sx, const uint8_t *__restrict__ Wc,
+    const uint8_t *__restrict__ Ws, int M, int N, int K, int tiles_m, uint16_t *__restrict__ Y)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[MLDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int blocks = gridDim.x, b = blockIdx.x;
+    const int t = (blocks % 8 == 0) ? (b % 8) * (blocks / 8) + b / 8 : b;
+    const int m0 = (t % tiles_m) * MBM, n0 = (t / tiles_m) * MBN;
+    const int KT = K / MBK;
+    const uint32_t KC = (uint32_t)K >> 1, KS = (uint32_t)K >> 5;   // bytes per code / scale row
+
+    // direct-load addresses (rows past M or N read the last row)
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    uint32_t xoff[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        int m = m0 + (2 * wave + j) * 16 + (lane >> 2);
+        m = m < M ? m : M - 1;
+        xoff[j] = (uint32_t)m * (uint32_t)K + 16 * dchunk;
+    }
+    int nw = n0 + wave * 32 + (lane >> 1);
+    nw = nw < N ? nw : N - 1;
+    const uint32_t woff = (uint32_t)nw * KC + 16 * (lane & 1);
+    const uint32_t soff = (uint32_t)nw * KS + (lane & 1);
+    auto issue = [&](uint8_t *stage, int kt) {
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+            __builtin_amdgcn_global_load_lds(Xq + xoff[j] + (uint32_t)kt * MBK, stage + (2 * wave + j) * 1024,
+                                             16, 0, 0);
+        __builtin_amdgcn_global_load_lds(Wc + woff + (uint32_t)kt * 32, stage + MX_BYTES + wave * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(Ws + soff + (uint32_t)kt * 2, stage + MX_BYTES + MW_BYTES + wave * 256,
+                                         1, 0, 0);
+    };
+
+    // Operand layout of the instruction with these formats (measured): an
+    // E2M1 lane of half h holds k = 32h .. 32h + 31 of the 64-k step, one MX
+    // block, and its scale is that block's; an E4M3 lane of half h holds
+    // k = 16h .. 16h + 15 in bytes 0-15 and k = 32 + 16h .. 32 + 16h + 15 in
+    // bytes 16-31. So: X row wm*128 + 32 i + l32, logical chunks h and 2 + h;
+    // W row wn*64 + 32 j + l32, code bytes 16h .. 16h + 15; its scale in
+    // dword 2 row + h.
+    const int swz = (l32 >> 2) & 3;
+    const int xa = (wm * 128 + l32) * MBK, xc0 = 16 * (h ^ swz), xc1 = 16 * ((2 + h) ^ swz);
+    const int wrow = wn * 64 + l32;
+    const int wb = MX_BYTES + wrow * 32 + 16 * h;
+    const int sb = MX_BYTES + MW_BYTES + (wrow * 2 + h) * 4;
+
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    struct Frags {
+        intx8 a[4];
+        intx4 w[2];
+        int s[2];
+    };
+    auto read = [&](const uint8_t *stage, Frags &f) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const intx4 lo = *reinterpret_cast<const intx4 *>(stage + xa + i * 32 * MBK + xc0);
+            const intx4 hi = *reinterpret_cast<const intx4 *>(stage + xa + i * 32 * MBK + xc1);
+            f.a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            f.w[j] = *reinterpret_cast<const intx4 *>(stage + wb + j * 32 * 32);
+            f.s[j] = stage[sb + j * 32 * 2 * 4];
+        }
+    };
+    auto mma_half = [&](const Frags &f, int s) {   // tiles i = 2s, 2s + 1
+#pragma unroll
+        for (int i = 2 * s; i < 2 * s + 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const intx8 w8 = __builtin_shufflevector(f.w[j], intx4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+                // first operand E2M1 (format 4) with its block scale, second E4M3 (format 0) at 1.0
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, f.a[i], acc[i][j], 4, 0, 0,
+                                                                             f.s[j], 0, 127);
+            }
+    };
+
+    // Software pipeline as in the INT8 / FP8 kernel (six stages here).
+#pragma unroll
+    for (int p = 0; p < MSTAGES; p++) issue(lds + p * MSTAGE_BYTES, p < KT ? p : KT - 1);
+    Frags f[2];
+    asm volatile("" ::: "memory");
+    Q4_WAIT_VM_LGKM0(4 * (MSTAGES - 1));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read(lds, f[0]);
+    int sc = 0;   // stage of step k (k mod 6)
+    for (int kt = 0; kt < KT; kt += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int k = kt + u;
+            const int sn = sc == MSTAGES - 1 ? 0 : sc + 1;
+            mma_half(f[u], 0);
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
+            Q4_WAIT_VM_LGKM0(4 * (MSTAGES - 2));   // loads outstanding: stages k + 2 .. k + 5
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            read(lds + sn * MSTAGE_BYTES, f[u ^ 1]);
+            issue(lds + sc * MSTAGE_BYTES, k + MSTAGES < KT ? k + MSTAGES : KT - 1);
+            mma_half(f[u], 1);
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                if (g >= 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM read
+                __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);               // DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+            }
+            sc = sn;
+        }
+    }
+    Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
+
+    // Epilogue: y = f2h(acc * sx[m]) through an LDS-staged fp16 tile
+    float xsv[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int m = m0 + wm * 128 + i * 32 + l32;
+        xsv[i] = sx[m < M ? m : M - 1];
+    }
+    __syncthreads();   // every wavefront is done with the stages
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int nl = wn * 64 + j * 32 + 8 * q + 4 * h;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                uint32_t pk[2];
+#pragma unroll
+                for (int e2 = 0; e2 < 2; e2++) {
+                    const uint32_t lo = f2h(acc[i][j][4 * q + 2 * e2] * xsv[i]);
+                    const uint32_t hi = f2h(acc[i][j][4 * q + 2 * e2 + 1] * xsv[i]);
+                    pk[e2] = lo | (hi << 16);
+                }
+                const int ml = wm * 128 + i * 32 + l32;
+                *reinterpret_cast<u32x2 *>(lds + ml * MOUT_STRIDE + nl * 2) = u32x2{pk[0], pk[1]};
+            }
+        }
+    __syncthreads();
+    const bool vec_ok = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+#pragma unroll 4
+    for (int it = 0; it < 16; it++) {
+        const int ml = wave * 32 + 2 * it + (lane >> 5);
+        const int cl = (lane & 31) * 8;
+        const int m = m0 + ml, n = n0 + cl;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + ml * MOUT_STRIDE + cl * 2);
+        if (m < M && n + 8 <= N && vec_ok) *reinterpret_cast<u32x4 *>(Y + (int64_t)m * N + n) = v;
+        else if (m < M) {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                if (n + e < N) Y[(int64_t)m * N + n + e] = (uint16_t)(v[e / 2] >> (16 * (e & 1)));
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mxfp4_quantize(const uint16_t *W, const float *s, int64_t N, int64_t K,
+                                 uint8_t *codes, uint8_t *scales, hipStream_t st)
+{
+    if (N == 0) return hipSuccess;
+    const int64_t threads = N * (K >> 3);
+    const int64_t grid = (threads + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (s) mxfp4_quantize_kernel<true><<<(unsigned)grid, 256, 0, st>>>(W, s, N, K, codes, scales);
+    else mxfp4_quantize_kernel<false><<<(unsigned)grid, 256, 0, st>>>(W, s, N, K, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_gemm(const uint8_t *Xq, const float *sx, const uint8_t *codes,
+                             const uint8_t *scales, int64_t M, int64_t N, int64_t K, uint16_t *Y,
+                             hipStream_t st)
+{
+    if (M == 0 || N == 0) return hipSuccess;
+    if (K % (2 * MBK) != 0 || M * K >= (int64_t)1 << 31 || N * K >= (int64_t)1 << 31)
+        return hipErrorNotSupported;
+    const int tiles_m = (int)((M + MBM - 1) / MBM), tiles_n = (int)((N + MBN - 1) / MBN);
+    mxfp4_gemm_kernel<<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N,
+                                                       (int)K, tiles_m, Y);
+    return hipGetLastError();
+}
+
+}  // namespace q4k

@@ -71,5 +71,12 @@ hipError_t launch_fp8_act(const uint16_t *X, const float *s, int64_t M, int64_t 
                           float *sx, hipStream_t st);
 hipError_t launch_fp8_gemm(const uint8_t *Xq, const float *sx, const uint8_t *Wq, const float *sw,
                            int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t st);
+// MXFP4 weights (E2M1 codes [N, K/2], E8M0 block scales [N, K/32]) and the
+// W4A8 GEMM with per-token E4M3 activations (K % 128 == 0 for the GEMM).
+hipError_t launch_mxfp4_quantize(const uint16_t *W, const float *s, int64_t N, int64_t K,
+                                 uint8_t *codes, uint8_t *scales, hipStream_t st);
+hipError_t launch_mxfp4_gemm(const uint8_t *Xq, const float *sx, const uint8_t *codes,
+                             const uint8_t *scales, int64_t M, int64_t N, int64_t K, uint16_t *Y,
+                             hipStream_t st);
 
 }  // namespace q4k

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared_functions()) <= exported
     # nothing else of ours leaks out (internal launchers are hidden)
-    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "fp8", "smoothquant", "_ZN3q4k"))}
+    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "fp8", "mxfp4", "smoothquant", "_ZN3q4k"))}
     assert ours == set(declared_functions())
 
 
@@ -123,6 +123,17 @@ def layers(*descs):
     (lambda L: L.fp8_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE, 100, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.fp8_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE + 16, 4096, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.fp8_linear(FAKE, 4, 4, 96, FAKE, FAKE, None, FAKE, FAKE, 4096, None), q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.mxfp4_quantize_weight(FAKE, None, 4, 48, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.mxfp4_quantize_weight(MISAL, None, 4, 64, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.mxfp4_quantize_weight(FAKE, None, 4, 64, FAKE + 2, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.mxfp4_quantize_weight(FAKE, None, 4, 64, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.mxfp4_quantize_weight(FAKE, None, 0, 64, None, None, None), q4.Q4_OK),
+    (lambda L: L.mxfp4_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 192, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.mxfp4_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 8320, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.mxfp4_gemm(FAKE, FAKE, MISAL, FAKE, 4, 4, 128, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.mxfp4_gemm(FAKE, FAKE, FAKE, None, 4, 4, 128, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.mxfp4_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE, 100, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.mxfp4_linear(FAKE, 4, 0, 128, None, None, None, None, None, 0, None), q4.Q4_OK),
     (lambda L: L.smoothquant_scales(FAKE, 4, FAKE, 4, 128, 1.5, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.smoothquant_scales(FAKE, 0, FAKE, 4, 128, 0.5, FAKE, None), q4.Q4_ERR_INVALID_ARG),
 ])
