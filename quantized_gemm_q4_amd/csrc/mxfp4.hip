@@ -115,20 +115,36 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t *__r
 // weight is the first operand): a lane holds one row of Y and four
 // consecutive columns per group of four registers; the epilogue stages the
 // fp16 tile in LDS and writes whole rows with 16-byte stores.
+//
+// With K % 512 == 0 (SG = true) the scales take another route: every 8 steps
+// wavefronts 0-3 load the next 8 steps' scales of the tile's 256 rows (16
+// bytes per row, one 16-byte load per lane) into one of two 4 KB LDS
+// buffers, so a step's scale traffic is 32 requests of 16 bytes instead of
+// 256 single bytes. Those loads are issued after the step's stage loads:
+// for wavefronts 0-3 the fixed wait counts then also cover them (a stricter
+// wait, never a looser one), and the group is first read 7 steps later,
+// after the wait for a younger stage and a barrier.
 constexpr int MBM = 256, MBN = 256, MBK = 64, MSTAGES = 6;
 constexpr int MX_BYTES = MBM * MBK;                       // 16 KB of X
 constexpr int MW_BYTES = MBN * MBK / 2;                   // 8 KB of codes
-constexpr int MS_BYTES = MBN * 2 * 4;                     // 512 scale bytes, one per dword
-constexpr int MSTAGE_BYTES = MX_BYTES + MW_BYTES + MS_BYTES;
 constexpr int MOUT_STRIDE = MBN * 2 + 16;
-constexpr int MLDS_BYTES =
-    MBM * MOUT_STRIDE > MSTAGES * MSTAGE_BYTES ? MBM * MOUT_STRIDE : MSTAGES * MSTAGE_BYTES;
+template <bool SG> constexpr int ms_bytes = SG ? 0 : MBN * 2 * 4;   // per-step scales, one per dword
+template <bool SG> constexpr int mstage_bytes = MX_BYTES + MW_BYTES + ms_bytes<SG>;
+constexpr int MSG_BYTES = 2 * MBN * 16;                   // two groups of 8 steps' scales
+template <bool SG>
+constexpr int mlds_bytes = MBM * MOUT_STRIDE > MSTAGES * mstage_bytes<SG> + (SG ? MSG_BYTES : 0)
+                               ? MBM * MOUT_STRIDE
+                               : MSTAGES * mstage_bytes<SG> + (SG ? MSG_BYTES : 0);
 
+template <bool SG>
 __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
     const uint8_t *__restrict__ Xq, const float *__restrict__ sx, const uint8_t *__restrict__ Wc,
     const uint8_t *__restrict__ Ws, int M, int N, int K, int tiles_m, uint16_t *__restrict__ Y)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[MLDS_BYTES];
+    constexpr int MSTAGE_BYTES = mstage_bytes<SG>;
+    constexpr int LPS = SG ? 3 : 4;   // direct loads per stage and wavefront
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[mlds_bytes<SG>];
+    uint8_t *const sreg = lds + MSTAGES * MSTAGE_BYTES;   // SG: the two scale groups
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
@@ -158,8 +174,23 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
             __builtin_amdgcn_global_load_lds(Xq + xoff[j] + (uint32_t)kt * MBK, stage + (2 * wave + j) * 1024,
                                              16, 0, 0);
         __builtin_amdgcn_global_load_lds(Wc + woff + (uint32_t)kt * 32, stage + MX_BYTES + wave * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(Ws + soff + (uint32_t)kt * 2, stage + MX_BYTES + MW_BYTES + wave * 256,
-                                         1, 0, 0);
+        if constexpr (!SG)
+            __builtin_amdgcn_global_load_lds(Ws + soff + (uint32_t)kt * 2, stage + MX_BYTES + MW_BYTES + wave * 256,
+                                             1, 0, 0);
+    };
+    // SG: scale group g (steps 8g .. 8g + 7) into buffer g & 1; wavefront w
+    // < 4 loads rows 64 w .. 64 w + 63, lane i row 64 w + i (past the end:
+    // the last group again)
+    int ns = n0 + (wave & 3) * 64 + lane;
+    ns = ns < N ? ns : N - 1;
+    const uint32_t sgoff = (uint32_t)ns * KS;
+    const int ngroups = KT >> 3;
+    auto issue_scales = [&](int g) {
+        if (SG && wave < 4) {
+            const int gg = g < ngroups ? g : ngroups - 1;
+            __builtin_amdgcn_global_load_lds(Ws + sgoff + (uint32_t)gg * 16, sreg + (g & 1) * 4096 + wave * 1024,
+                                             16, 0, 0);
+        }
     };
 
     // Operand layout of the instruction with these formats (measured): an
@@ -173,7 +204,8 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
     const int xa = (wm * 128 + l32) * MBK, xc0 = 16 * (h ^ swz), xc1 = 16 * ((2 + h) ^ swz);
     const int wrow = wn * 64 + l32;
     const int wb = MX_BYTES + wrow * 32 + 16 * h;
-    const int sb = MX_BYTES + MW_BYTES + (wrow * 2 + h) * 4;
+    const int sb = MX_BYTES + MW_BYTES + (wrow * 2 + h) * 4;   // !SG: inside the stage
+    const int sgb = wrow * 16 + h;                              // SG: inside a scale group
 
     floatx16 acc[4][2];
 #pragma unroll
@@ -188,7 +220,7 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
         intx4 w[2];
         int s[2];
     };
-    auto read = [&](const uint8_t *stage, Frags &f) {
+    auto read = [&](const uint8_t *stage, int step, Frags &f) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const intx4 lo = *reinterpret_cast<const intx4 *>(stage + xa + i * 32 * MBK + xc0);
@@ -198,7 +230,8 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             f.w[j] = *reinterpret_cast<const intx4 *>(stage + wb + j * 32 * 32);
-            f.s[j] = stage[sb + j * 32 * 2 * 4];
+            if constexpr (SG) f.s[j] = sreg[((step >> 3) & 1) * 4096 + sgb + j * 32 * 16 + 2 * (step & 7)];
+            else f.s[j] = stage[sb + j * 32 * 2 * 4];
         }
     };
     auto mma_half = [&](const Frags &f, int s) {   // tiles i = 2s, 2s + 1
@@ -214,14 +247,15 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
     };
 
     // Software pipeline as in the INT8 / FP8 kernel (six stages here).
+    issue_scales(0);
 #pragma unroll
     for (int p = 0; p < MSTAGES; p++) issue(lds + p * MSTAGE_BYTES, p < KT ? p : KT - 1);
     Frags f[2];
     asm volatile("" ::: "memory");
-    Q4_WAIT_VM_LGKM0(4 * (MSTAGES - 1));
+    Q4_WAIT_VM_LGKM0(LPS * (MSTAGES - 1));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    read(lds, f[0]);
+    read(lds, 0, f[0]);
     int sc = 0;   // stage of step k (k mod 6)
     for (int kt = 0; kt < KT; kt += 2) {
 #pragma unroll
@@ -231,12 +265,13 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
             mma_half(f[u], 0);
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("" ::: "memory");
-            Q4_WAIT_VM_LGKM0(4 * (MSTAGES - 2));   // loads outstanding: stages k + 2 .. k + 5
+            Q4_WAIT_VM_LGKM0(LPS * (MSTAGES - 2));   // loads outstanding: stages k + 2 .. k + 5
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            read(lds + sn * MSTAGE_BYTES, f[u ^ 1]);
+            read(lds + sn * MSTAGE_BYTES, k + 1, f[u ^ 1]);
             issue(lds + sc * MSTAGE_BYTES, k + MSTAGES < KT ? k + MSTAGES : KT - 1);
+            if (SG && (k & 7) == 0) issue_scales((k >> 3) + 1);
             mma_half(f[u], 1);
 #pragma unroll
             for (int g = 0; g < 4; g++) {
@@ -314,8 +349,13 @@ hipError_t launch_mxfp4_gemm(const uint8_t *Xq, const float *sx, const uint8_t *
     if (K % (2 * MBK) != 0 || M * K >= (int64_t)1 << 31 || N * K >= (int64_t)1 << 31)
         return hipErrorNotSupported;
     const int tiles_m = (int)((M + MBM - 1) / MBM), tiles_n = (int)((N + MBN - 1) / MBN);
-    mxfp4_gemm_kernel<<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N,
-                                                       (int)K, tiles_m, Y);
+    // 16-byte scale group loads need whole, aligned 16-byte runs per row
+    if (K % 512 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0)
+        mxfp4_gemm_kernel<true><<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N,
+                                                                 (int)K, tiles_m, Y);
+    else
+        mxfp4_gemm_kernel<false><<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N,
+                                                                  (int)K, tiles_m, Y);
     return hipGetLastError();
 }
 
