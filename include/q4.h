@@ -251,9 +251,10 @@ Q4_API q4_status fp8_quantize_act(const void *X, const float *smooth_s, int64_t 
  * Accuracy: |Y - Y_ref| <= 2^-10 * x_scale w_scale sum_k |products| (+2^-25)
  * against the exact sum (K <= 8192 keeps the fp32 sum within half of it).
  * Xq, Wq u8 E4M3 codes [M, K], [N, K] (16-byte aligned); x_scale fp32 [M];
- * w_scale fp32 [N]; Y fp16 [M, N] output. K must be a multiple of 128.
- * Errors: INVALID_ARG (shape; K > 8192), UNSUPPORTED (K % 128 != 0),
- *         MISALIGNED, HIP.
+ * w_scale fp32 [N]; Y fp16 [M, N] output. K must be a multiple of 128;
+ * M*K and N*K below 2^31.
+ * Errors: INVALID_ARG (shape; K > 8192), UNSUPPORTED (K % 128 != 0, M*K or
+ *         N*K >= 2^31), MISALIGNED, HIP.
  * -------------------------------------------------------------------------- */
 Q4_API q4_status fp8_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t *Wq,
                           const float *w_scale, int64_t M, int64_t N, int64_t K, void *Y,
@@ -299,9 +300,10 @@ Q4_API q4_status mxfp4_quantize_weight(const void *W, const float *smooth_s, int
  * Accuracy: |Y - Y_ref| <= 2^-10 * x_scale sum_k |products| (+2^-25).
  * Xq u8 E4M3 [M, K] and x_scale fp32 [M] as written by fp8_quantize_act;
  * codes, scales as written by mxfp4_quantize_weight (Xq and codes 16-byte
- * aligned); Y fp16 [M, N] output. K a multiple of 128, at most 8192.
- * Errors: INVALID_ARG (shape, K > 8192), UNSUPPORTED (K % 128 != 0),
- *         MISALIGNED, HIP.
+ * aligned); Y fp16 [M, N] output. K a multiple of 128, at most 8192; M*K
+ * and N*K below 2^31.
+ * Errors: INVALID_ARG (shape, K > 8192), UNSUPPORTED (K % 128 != 0, M*K or
+ *         N*K >= 2^31), MISALIGNED, HIP.
  * -------------------------------------------------------------------------- */
 Q4_API q4_status mxfp4_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t *codes,
                             const uint8_t *scales, int64_t M, int64_t N, int64_t K, void *Y,

@@ -262,7 +262,9 @@ Q4_API q4_status fp8_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t
                (long long)M, (long long)N, (long long)K);
     Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "fp8_gemm: K=%lld must be a multiple of 128",
                (long long)K);
-    Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "fp8_gemm: M=%lld too large", (long long)M);
+    Q4_REQUIRE(M * K < (1LL << 31) && N * K < (1LL << 31), Q4_ERR_UNSUPPORTED,
+               "fp8_gemm: M*K and N*K must stay below 2^31 (M=%lld N=%lld K=%lld)", (long long)M,
+               (long long)N, (long long)K);
     if (M == 0 || N == 0) return ok();
     Q4_REQUIRE(Xq && x_scale && Wq && w_scale && Y, Q4_ERR_INVALID_ARG, "fp8_gemm: null pointer");
     Q4_REQUIRE(aligned16(Xq) && aligned16(Wq), Q4_ERR_MISALIGNED,
@@ -322,7 +324,9 @@ Q4_API q4_status mxfp4_gemm(const uint8_t *Xq, const float *x_scale, const uint8
                (long long)M, (long long)N, (long long)K);
     Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "mxfp4_gemm: K=%lld must be a multiple of 128",
                (long long)K);
-    Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "mxfp4_gemm: M=%lld too large", (long long)M);
+    Q4_REQUIRE(M * K < (1LL << 31) && N * K < (1LL << 31), Q4_ERR_UNSUPPORTED,
+               "mxfp4_gemm: M*K and N*K must stay below 2^31 (M=%lld N=%lld K=%lld)", (long long)M,
+               (long long)N, (long long)K);
     if (M == 0 || N == 0) return ok();
     Q4_REQUIRE(Xq && x_scale && codes && scales && Y, Q4_ERR_INVALID_ARG, "mxfp4_gemm: null pointer");
     Q4_REQUIRE(aligned16(Xq) && aligned16(codes), Q4_ERR_MISALIGNED,

@@ -120,6 +120,8 @@ def layers(*descs):
     (lambda L: L.fp8_gemm(MISAL, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.fp8_gemm(FAKE, FAKE, None, FAKE, 4, 4, 128, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.fp8_gemm(FAKE, FAKE, FAKE, FAKE, 0, 4, 128, FAKE, None), q4.Q4_OK),
+    (lambda L: L.fp8_gemm(FAKE, FAKE, FAKE, FAKE, 1 << 18, 4, 8192, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.mxfp4_gemm(FAKE, FAKE, FAKE, FAKE, 4, 1 << 18, 8192, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
     (lambda L: L.fp8_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE, 100, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.fp8_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE + 16, 4096, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.fp8_linear(FAKE, 4, 4, 96, FAKE, FAKE, None, FAKE, FAKE, 4096, None), q4.Q4_ERR_UNSUPPORTED),
