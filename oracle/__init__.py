@@ -69,6 +69,8 @@ def _load():
         "orc_e2m1_encode": (ctypes.c_uint, [ctypes.c_float]),
         "orc_mxfp4_quantize_weight": (None, [_u16p, _f32p, _i64, _i64, _u8p, _u8p]),
         "orc_mxfp4_gemm": (None, [_u8p, _i64, _i64, _u8p, _u8p, _i64, _i64p, _i64, _f64p, _f64p]),
+        "orc_nf4_quantize": (None, [_u16p, _i64, _i64, _u16p, _u8p, _f32p]),
+        "orc_nf4_ref": (None, [_u16p, _i64, _i64, _u8p, _f32p, _u16p, _i64, _i64p, _i64, _f64p, _f64p]),
         "orc_num_threads": (_int, []),
     }
     for name, (res, args) in sig.items():
@@ -386,3 +388,54 @@ def mxfp4_reference(acc, abs_acc, sx, rows=None):
     if rows is not None:
         sx = sx[np.asarray(rows)]
     return sx[:, None] * acc, sx[:, None] * abs_acc
+
+
+# --- NF4 weights (Quantization operators guide §3.4) ---------------------------
+
+def nf4_levels() -> np.ndarray:
+    """The guide's 16 NF4 levels: the N(0, 1) quantiles at the midpoints of 16
+    equal-probability intervals, (i + 0.5) / 16, divided by the largest
+    magnitude and rounded to fp16 (ascending)."""
+    from scipy.stats import norm
+    lv = norm.ppf((np.arange(16) + 0.5) / 16)
+    return (lv / np.abs(lv).max()).astype(np.float16)
+
+
+def nf4_quantize(W):
+    """NF4 of W [N, K] (K % 64 == 0): (codes uint8 [N, K/2], scales f32 [N, K/64])."""
+    W = _half_bits(W)
+    N, K = W.shape
+    assert K % 64 == 0
+    lv = _half_bits(nf4_levels())
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.empty((N, K // 64), np.float32)
+    _load().orc_nf4_quantize(_ptr(W, _u16p), N, K, _ptr(lv, _u16p), _ptr(codes, _u8p),
+                             _ptr(scales, _f32p))
+    return codes, scales
+
+
+def nf4_dequant(codes, scales) -> np.ndarray:
+    """fp64 w_hat = level[code] * scale of an NF4 weight [N, K]."""
+    lv = nf4_levels().astype(np.float64)
+    codes = np.asarray(codes, dtype=np.uint8)
+    u = np.empty((codes.shape[0], codes.shape[1] * 2), np.uint8)
+    u[:, 0::2] = codes & 0xF
+    u[:, 1::2] = codes >> 4
+    return lv[u] * np.repeat(np.asarray(scales, dtype=np.float64), 64, axis=1)
+
+
+def nf4_ref(X, codes, scales, rows=None):
+    """fp64 Y = X W_hat^T and B = |X| |W_hat|^T for an NF4 weight."""
+    X = _half_bits(X)
+    M, K = X.shape
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    N = codes.shape[0]
+    lv = _half_bits(nf4_levels())
+    r = _rows(rows)
+    n_rows = M if r is None else r.size
+    Y = np.empty((n_rows, N), np.float64)
+    B = np.empty((n_rows, N), np.float64)
+    _load().orc_nf4_ref(_ptr(X, _u16p), M, K, _ptr(codes, _u8p), _ptr(scales, _f32p),
+                        _ptr(lv, _u16p), N, _ptr(r, _i64p), n_rows, _ptr(Y, _f64p), _ptr(B, _f64p))
+    return Y, B

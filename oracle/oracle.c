@@ -625,6 +625,82 @@ void orc_mxfp4_gemm(const uint8_t *Xq, int64_t M, int64_t K, const uint8_t *code
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* NF4 weights (Quantization operators guide §3.4: 16 non-uniform levels, the
+ * medians of 16 equal-probability intervals of N(0, 1) normalised to
+ * [-1, 1] and stored in fp16; per block of 64 weights one fp32 scale, the
+ * block's max |w|; code = index of the nearest level to w / scale).
+ * The level table is an input (fp16 bit patterns, ascending), so the
+ * quantile function stays with its library.                                  */
+
+/* codes [N, K/2] (two per byte along K, even k in the low nibble), scales
+ * fp32 [N, K/64]: scale = max(max_block |w|, 1e-8), x = w / scale (fp32
+ * IEEE), code = the first index i minimising fabsf(x - level[i]) (fp32).    */
+void orc_nf4_quantize(const uint16_t *W, int64_t N, int64_t K, const uint16_t *levels,
+                      uint8_t *codes, float *scales)
+{
+    float lv[16];
+    for (int i = 0; i < 16; i++) lv[i] = orc_h2f(levels[i]);
+    const int64_t nb = K / 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t b = 0; b < nb; b++) {
+            float a = 0.0f;
+            for (int i = 0; i < 64; i++) {
+                float v = fabsf(orc_h2f(W[n * K + b * 64 + i]));
+                if (v > a) a = v;
+            }
+            if (a < 1e-8f) a = 1e-8f;
+            scales[n * nb + b] = a;
+            for (int i = 0; i < 64; i++) {
+                float x = orc_h2f(W[n * K + b * 64 + i]) / a;
+                int best = 0;
+                float bd = fabsf(x - lv[0]);
+                for (int l = 1; l < 16; l++) {
+                    float d = fabsf(x - lv[l]);
+                    if (d < bd) {
+                        bd = d;
+                        best = l;
+                    }
+                }
+                int64_t k = b * 64 + i;
+                uint8_t *byte = &codes[n * (K / 2) + k / 2];
+                if (k & 1) *byte = (uint8_t)((*byte & 0x0F) | (best << 4));
+                else *byte = (uint8_t)((*byte & 0xF0) | best);
+            }
+        }
+    }
+}
+
+/* fp64 reference of Y = X W_hat^T with w_hat = level[code] * scale (exact in
+ * fp64), and B = sum |x| |w_hat|, for the listed rows of X.                 */
+void orc_nf4_ref(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes,
+                 const float *scales, const uint16_t *levels, int64_t N,
+                 const int64_t *rows, int64_t n_rows, double *Y, double *B)
+{
+    if (!rows) n_rows = M;
+    double lv[16];
+    for (int i = 0; i < 16; i++) lv[i] = (double)orc_h2f(levels[i]);
+    const int64_t nb = K / 64;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t i = 0; i < n_rows; i++) {
+            int64_t m = rows ? rows[i] : i;
+            double y = 0.0, bb = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                uint8_t byte = codes[n * (K / 2) + k / 2];
+                int c = (k & 1) ? (byte >> 4) : (byte & 0xF);
+                double w = lv[c] * (double)scales[n * nb + k / 64];
+                double x = (double)orc_h2f(X[m * K + k]);
+                y += x * w;
+                bb += fabs(x) * fabs(w);
+            }
+            Y[i * N + n] = y;
+            B[i * N + n] = bb;
+        }
+    }
+}
+
 /* Number of OpenMP threads a parallel region of this library uses. */
 #ifdef _OPENMP
 #include <omp.h>
