@@ -21,11 +21,11 @@ The JSON line also carries:
                 W8A8 (M = 2048, K = N = 8192) TOP/s against the int8 peak,
                 its FP8 E4M3 variant TFLOP/s against the fp8 peak, MXFP4
                 weights x E4M3 activations on that layer and on the prefill
-                shape,
+                shape, NF4 decode GB/s,
                 quantize + pack GB/s, batched decode M = 16 / 64.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
-                       [--only decode|prefill|w8a8|fp8|mxfp4|quant|batched] [--eager]
+                       [--only decode|prefill|w8a8|fp8|mxfp4|nf4|quant|batched] [--eager]
                        [--copy-calibration]
 """
 from __future__ import annotations
@@ -77,8 +77,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", default=None, choices=["decode", "prefill", "w8a8", "fp8", "mxfp4", "quant",
-                                                     "batched"])
+    ap.add_argument("--only", default=None, choices=["decode", "prefill", "w8a8", "fp8", "mxfp4", "nf4",
+                                                     "quant", "batched"])
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference for the HBM byte counters)")
@@ -341,6 +341,27 @@ def main():
                          "gemm_frac_mfma_fp8": ops / tg / 1e12 / FP8_MFMA_PEAK_TFLOPS}
             del codes, sc, Xq, X, Y, ws
         extra["mxfp4_w4a8"] = res
+        torch.cuda.empty_cache()
+
+    # ---- NF4 decode (M = 1, K = 4096, N = 11008 and 4096) --------------------------
+    if only in (None, "nf4"):
+        res = {}
+        for N in (11008, 4096):
+            w = workloads.decode(N)
+            X = gpu(w["X"])
+            codes, sc = q4.nf4_quantize(gpu(w["W"]))
+            nb = N * 4096 // 2 + N * 4096 // 64 * 4 + 4096 * 2 + N * 2
+            copies = max(2, math.ceil(MALL_BYTES / nb) + 1)
+            cps = [(codes.clone(), sc.clone()) for _ in range(copies)]
+            Y = torch.empty((1, N), dtype=torch.float16, device=dev)
+            gr = graph_of(lambda i: q4.nf4_linear(X, *cps[i % copies], out=Y), copies)
+            gr()
+            reps = max(1, 2000 // copies)
+            tt = timed(lambda i: gr(), reps) / (reps * copies)
+            res[f"n{N}"] = {"us": tt * 1e6, "GB/s": nb / tt / 1e9, "frac_hbm": nb / tt / 1e9 / HBM_PEAK_GBS,
+                            "bytes": nb}
+            del cps, codes, sc
+        extra["nf4_decode"] = res
         torch.cuda.empty_cache()
 
     # ---- known-size copy: scales the HBM byte counters (profiling runs only) -

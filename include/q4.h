@@ -321,6 +321,35 @@ Q4_API q4_status mxfp4_linear(const void *X, int64_t M, int64_t N, int64_t K,
                               size_t workspace_bytes, void *stream);
 
 /* ----------------------------------------------------------------------------
+ * NF4 weights (Operators guide §3.4: 16 non-uniform levels, the medians of
+ * 16 equal-probability intervals of N(0, 1), scaled to [-1, 1] and kept in
+ * fp16; one fp32 scale, the block's max |w|, per block of 64 weights; code =
+ * the index of the level nearest to w / scale; w_hat = level[code] * scale).
+ *
+ * nf4_levels -- copies the 16 levels (fp16 bit patterns, ascending:
+ *   Phi^-1((i + 0.5) / 16) / Phi^-1(31 / 32) rounded to fp16) to the HOST
+ *   array `out`. No GPU work.
+ * nf4_quantize -- scale = max(max_block |w|, 1e-8); x = w / scale (IEEE
+ *   fp32); code = the first index minimising fabsf(x - level[i]) in fp32.
+ *   W fp16 [N, K] (16-byte aligned, K % 64 == 0); codes u8 [N, K/2] output,
+ *   two codes per byte along K (even k in the low nibble), 4-byte aligned;
+ *   scales fp32 [N, K/64] output. Codes and scales are bit-exact.
+ * nf4_linear -- Y = X * W_hat^T, fp32 accumulation, fp16 output; the levels
+ *   enter the matrix cores exactly and each 64-block's fp32 partial sum is
+ *   multiplied by its scale. Built for decode: X is processed in row chunks
+ *   of at most 16 (fewer when K is large), each chunk reading the whole
+ *   weight once. X fp16 [M, K] and codes 16-byte aligned; scales 8-byte
+ *   aligned; K % 128 == 0 and at most 28672; Y fp16 [M, N] output.
+ * Accuracy: as for w4a16_linear.
+ * Errors: INVALID_ARG, UNSUPPORTED (K too large for the LDS), MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API void nf4_levels(uint16_t *out);
+Q4_API q4_status nf4_quantize(const void *W, int64_t N, int64_t K, uint8_t *codes, float *scales,
+                              void *stream);
+Q4_API q4_status nf4_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                            const float *scales, void *Y, void *stream);
+
+/* ----------------------------------------------------------------------------
  * smoothquant_scales -- the SmoothQuant migration factor from calibration
  * activations (Operators guide §5.1; Core ideas §2.4; Quantization notes,
  * SmoothQuant):

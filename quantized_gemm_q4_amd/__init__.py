@@ -22,6 +22,9 @@ Functions (same names as the C ABI):
   mxfp4_quantize_weight(W, smooth_s=None) -> (codes, scales)  E2M1 + E8M0 per 32
   mxfp4_gemm(Xq, x_scale, codes, scales) -> Y                 W4A8
   mxfp4_linear(X, codes, scales, smooth_s=None, workspace=None) -> Y
+  nf4_levels() -> 16 fp16 levels (host)
+  nf4_quantize(W) -> (codes, scales)                         absmax per 64
+  nf4_linear(X, codes, scales) -> Y
 """
 from __future__ import annotations
 
@@ -66,6 +69,9 @@ SIGNATURES = {
     "mxfp4_quantize_weight": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "mxfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "mxfp4_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "nf4_levels": (None, [_vp]),
+    "nf4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "nf4_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -421,4 +427,38 @@ def mxfp4_linear(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
     Y = _output(out, M, N, X.device)
     _check(lib().mxfp4_linear(_ptr(X), M, N, K, _ptr(codes), _ptr(scales), _ptr(smooth_s), _ptr(Y),
                               _ptr(workspace), workspace.numel(), _stream(X)))
+    return Y
+
+
+# --- NF4 weights ------------------------------------------------------------------
+
+def nf4_levels():
+    """The library's 16 NF4 levels (numpy float16, ascending)."""
+    import numpy as np
+    out = (ctypes.c_uint16 * 16)()
+    lib().nf4_levels(ctypes.cast(out, _vp))
+    return np.array(out[:], dtype=np.uint16).view(np.float16)
+
+
+def nf4_quantize(W: torch.Tensor):
+    """NF4 of W fp16 [N, K]: (codes uint8 [N, K/2], scales fp32 [N, K/64])."""
+    _need(W, torch.float16, "W", 2)
+    N, K = W.shape
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((N, max(K // 64, 0)), dtype=torch.float32, device=W.device)
+    _check(lib().nf4_quantize(_ptr(W), N, K, _ptr(codes), _ptr(scales), _stream(W)))
+    return codes, scales
+
+
+def nf4_linear(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor | None = None):
+    """Y fp16 [M, N] = X W_hat^T with W_hat = level[code] * scale (NF4)."""
+    _need(X, torch.float16, "X", 2)
+    _need(codes, torch.uint8, "codes", 2)
+    _need(scales, torch.float32, "scales", 2)
+    M, K = X.shape
+    N = codes.shape[0]
+    if codes.shape[1] * 2 != K or tuple(scales.shape) != (N, K // 64):
+        raise ValueError(f"codes {tuple(codes.shape)} / scales {tuple(scales.shape)} do not match K={K}")
+    Y = _output(out, M, N, X.device)
+    _check(lib().nf4_linear(_ptr(X), M, N, K, _ptr(codes), _ptr(scales), _ptr(Y), _stream(X)))
     return Y

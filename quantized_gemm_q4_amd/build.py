@@ -28,6 +28,7 @@ SOURCES = {
     "w4a16_gemv.hip": ["-ffp-contract=off"],
     "w8a8.hip": ["-ffp-contract=off"],
     "mxfp4.hip": ["-ffp-contract=off"],
+    "nf4.hip": ["-ffp-contract=off"],
 }
 
 

@@ -361,6 +361,45 @@ Q4_API q4_status mxfp4_linear(const void *X, int64_t M, int64_t N, int64_t K, co
     return mxfp4_gemm(xq, sx, codes, scales, M, N, K, Y, stream);
 }
 
+Q4_API void nf4_levels(uint16_t *out)
+{
+    if (!out) return;
+    for (int i = 0; i < 16; i++) out[i] = q4k::kNf4Levels[i];
+}
+
+Q4_API q4_status nf4_quantize(const void *W, int64_t N, int64_t K, uint8_t *codes, float *scales,
+                              void *stream)
+{
+    Q4_REQUIRE(N >= 0 && K > 0 && N <= kIntMax && K <= kIntMax && K % 64 == 0, Q4_ERR_INVALID_ARG,
+               "nf4_quantize: bad shape N=%lld K=%lld (K must be a positive multiple of 64)",
+               (long long)N, (long long)K);
+    if (N == 0) return ok();
+    Q4_REQUIRE(W && codes && scales, Q4_ERR_INVALID_ARG, "nf4_quantize: null pointer");
+    Q4_REQUIRE(aligned16(W) && (reinterpret_cast<uintptr_t>(codes) & 3u) == 0, Q4_ERR_MISALIGNED,
+               "nf4_quantize: W must be 16-byte aligned, codes 4-byte aligned");
+    hipError_t e = q4k::launch_nf4_quantize(static_cast<const uint16_t *>(W), N, K, codes, scales,
+                                            static_cast<hipStream_t>(stream));
+    return from_hip(e, "nf4_quantize");
+}
+
+Q4_API q4_status nf4_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                            const float *scales, void *Y, void *stream)
+{
+    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K % 128 == 0,
+               Q4_ERR_INVALID_ARG, "nf4_linear: bad shape M=%lld N=%lld K=%lld (K a multiple of 128)",
+               (long long)M, (long long)N, (long long)K);
+    Q4_REQUIRE(K <= 28672, Q4_ERR_UNSUPPORTED, "nf4_linear: K=%lld larger than 28672", (long long)K);
+    Q4_REQUIRE(N * (K / 2) < 0xFFFFFF00LL, Q4_ERR_UNSUPPORTED, "nf4_linear: weight of %lld x %lld too large",
+               (long long)N, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    Q4_REQUIRE(X && codes && scales && Y, Q4_ERR_INVALID_ARG, "nf4_linear: null pointer");
+    Q4_REQUIRE(aligned16(X) && aligned16(codes) && (reinterpret_cast<uintptr_t>(scales) & 7u) == 0,
+               Q4_ERR_MISALIGNED, "nf4_linear: X and codes must be 16-byte aligned, scales 8-byte aligned");
+    hipError_t e = q4k::launch_nf4_linear(static_cast<const uint16_t *>(X), M, N, K, codes, scales,
+                                          static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
+    return from_hip(e, "nf4_linear");
+}
+
 Q4_API q4_status smoothquant_scales(const void *Xcal, int64_t R, const void *W, int64_t N,
                                     int64_t K, float alpha, float *s, void *stream)
 {

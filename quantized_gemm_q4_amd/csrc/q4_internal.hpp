@@ -78,5 +78,13 @@ hipError_t launch_mxfp4_quantize(const uint16_t *W, const float *s, int64_t N, i
 hipError_t launch_mxfp4_gemm(const uint8_t *Xq, const float *sx, const uint8_t *codes,
                              const uint8_t *scales, int64_t M, int64_t N, int64_t K, uint16_t *Y,
                              hipStream_t st);
+// NF4 weights: the level table (fp16 bit patterns, ascending), the quantizer
+// (codes [N, K/2], fp32 scales [N, K/64]) and the decode GEMV over row chunks
+// of X (K % 128 == 0; hipErrorNotSupported otherwise).
+extern const uint16_t kNf4Levels[16];
+hipError_t launch_nf4_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *codes, float *scales,
+                               hipStream_t st);
+hipError_t launch_nf4_linear(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                             const float *scales, uint16_t *Y, hipStream_t st);
 
 }  // namespace q4k

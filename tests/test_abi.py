@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared_functions()) <= exported
     # nothing else of ours leaks out (internal launchers are hidden)
-    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "fp8", "mxfp4", "smoothquant", "_ZN3q4k"))}
+    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "fp8", "mxfp4", "nf4", "smoothquant", "_ZN3q4k"))}
     assert ours == set(declared_functions())
 
 
@@ -136,6 +136,14 @@ def layers(*descs):
     (lambda L: L.mxfp4_gemm(FAKE, FAKE, FAKE, None, 4, 4, 128, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.mxfp4_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE, 100, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.mxfp4_linear(FAKE, 4, 0, 128, None, None, None, None, None, 0, None), q4.Q4_OK),
+    (lambda L: L.nf4_quantize(FAKE, 4, 96, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.nf4_quantize(MISAL, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.nf4_quantize(FAKE, 0, 128, None, None, None), q4.Q4_OK),
+    (lambda L: L.nf4_linear(FAKE, 1, 16, 192, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.nf4_linear(FAKE, 1, 16, 32768, FAKE, FAKE, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.nf4_linear(FAKE, 1, 16, 256, FAKE, FAKE + 4, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.nf4_linear(FAKE, 1, 16, 256, None, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.nf4_linear(FAKE, 0, 16, 256, None, None, None, None), q4.Q4_OK),
     (lambda L: L.smoothquant_scales(FAKE, 4, FAKE, 4, 128, 1.5, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.smoothquant_scales(FAKE, 0, FAKE, 4, 128, 0.5, FAKE, None), q4.Q4_ERR_INVALID_ARG),
 ])
@@ -155,3 +163,10 @@ def test_binding_refuses_cpu_tensors():
         q4.w4a16_linear_multi(torch.zeros(1, 128, dtype=torch.float16),
                               [(torch.zeros(4, 64, dtype=torch.uint8),
                                 torch.zeros(4, 1, dtype=torch.float16), None)])
+
+
+def test_nf4_levels_match_the_oracle(lib, orc):
+    """The library's level table (constants in the HIP source) equals the
+    oracle's, computed from the guide's formula with the normal quantile."""
+    import numpy as np
+    assert np.array_equal(q4.nf4_levels().view(np.uint16), orc.nf4_levels().view(np.uint16))

@@ -1,0 +1,73 @@
+"""GPU parity of the NF4 path against the oracle: codes and block scales bit
+for bit (every fp16 value of magnitude <= 1 at scale 1 and at a non-power-of-
+two scale, zero and constant blocks, random weights), and the NF4 decode
+GEMV within tolerance of the exact product over the dequantized weight, over
+ragged shapes, row chunks of X and the decode workload's layers."""
+import numpy as np
+import pytest
+
+import quantized_gemm_q4_amd as q4
+import workloads
+from parity import check_gemm, gpu, host
+
+pytestmark = pytest.mark.gpu
+
+
+def compare_quant(orc, W):
+    codes, sc = q4.nf4_quantize(gpu(W))
+    codes_ref, sc_ref = orc.nf4_quantize(W)
+    assert np.array_equal(host(sc).view(np.uint32), sc_ref.view(np.uint32))
+    bad = np.nonzero(host(codes) != codes_ref)
+    assert bad[0].size == 0, f"{bad[0].size} code bytes differ, first at {bad[0][0]}, {bad[1][0]}"
+    return codes_ref, sc_ref
+
+
+@pytest.mark.parametrize("lead", [1.0, 0.75])
+def test_every_small_fp16_value(orc, lead):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    f = h[np.isfinite(h) & (np.abs(h.astype(np.float32)) <= lead)]
+    nblk = (f.size + 62) // 63
+    vals = np.zeros(nblk * 63, np.float16)
+    vals[: f.size] = f
+    blocks = np.concatenate([np.full((nblk, 1), lead, np.float16), vals.reshape(nblk, 63)], axis=1)
+    K = 1024
+    row = np.zeros(((blocks.size + K - 1) // K) * K, np.float16)
+    row[: blocks.size] = blocks.reshape(-1)
+    compare_quant(orc, row.reshape(-1, K))
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (7, 128), (100, 1024), (33, 8256), (64, 4096)])
+def test_quantizer_shapes(orc, N, K):
+    rng = np.random.default_rng(N + K)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[0, :64] = 0
+    if N > 2:
+        W[1, :64] = -0.3
+        W[2] *= 100
+    compare_quant(orc, W.astype(np.float16))
+
+
+def run_linear(orc, M, N, K, seed):
+    W, X = workloads.small_case(seed, M, N, K)
+    codes, sc = orc.nf4_quantize(W)
+    Y = host(q4.nf4_linear(gpu(X), gpu(codes), gpu(sc)))
+    Yref, B = orc.nf4_ref(X, codes, sc)
+    return check_gemm(Y, Yref, B, f"nf4 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (1, 300, 1024), (3, 77, 256), (16, 300, 640),
+                                   (17, 129, 384), (40, 64, 4096), (1, 11008, 4096), (2, 4096, 11008),
+                                   (5, 1000, 8192)])
+def test_linear_shapes(orc, M, N, K):
+    run_linear(orc, M, N, K, M * 71 + N + K)
+
+
+@pytest.mark.parametrize("N", [11008, 4096])
+def test_decode_workload(orc, N):
+    w = workloads.decode(N)
+    codes, sc = q4.nf4_quantize(gpu(w["W"]))
+    codes_ref, sc_ref = orc.nf4_quantize(w["W"])
+    assert np.array_equal(host(codes), codes_ref)
+    Y = host(q4.nf4_linear(gpu(w["X"]), codes, sc))
+    Yref, B = orc.nf4_ref(w["X"], codes_ref, sc_ref)
+    check_gemm(Y, Yref, B, f"nf4 decode N={N}")
