@@ -344,24 +344,30 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
     // Epilogue: y = f2h((acc * sx[m]) * sw[n]), staged through LDS as the
     // block's 256 x 256 fp16 tile, then written back as whole rows with
     // 16-byte stores.
-    float xsv[4];
+    // All 36 scale loads of a lane go out at once, so the epilogue pays one
+    // memory latency rather than one per column group.
+    float xsv[4], swv[2][4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int m = m0 + wm * 128 + i * 32 + l32;
         xsv[i] = sx[m < M ? m : M - 1];
     }
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int n = n0 + wn * 64 + j * 32 + 8 * q + 4 * h + e;
+                swv[j][q][e] = sw[n < N ? n : N - 1];
+            }
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();   // every wavefront is done with the stages
 #pragma unroll
     for (int j = 0; j < 2; j++)
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const int nl = wn * 64 + j * 32 + 8 * q + 4 * h;
-            float swv[4];
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int n = n0 + nl + e;
-                swv[e] = sw[n < N ? n : N - 1];
-            }
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 uint32_t pk[2];
@@ -372,7 +378,7 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
                     for (int e1 = 0; e1 < 2; e1++) {
                         const int e = 2 * e2 + e1;
                         float f = (float)acc[i][j][4 * q + e] * xsv[i];
-                        f = f * swv[e];
+                        f = f * swv[j][q][e];
                         // Keep the fp32 product: without this the backend
                         // folds the multiply and the fp16 convert into one
                         // v_fma_mix (a single rounding).
