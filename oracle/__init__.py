@@ -53,6 +53,8 @@ def _load():
         "orc_q4_dequant_rows": (None, [_u8p, _u16p, _u8p, _i64, _int, _i64, _i64, _f64p]),
         "orc_w4a16_ref": (None, [_u16p, _i64, _i64, _u8p, _u16p, _u8p, _i64, _int,
                                  _i64p, _i64, _f64p, _f64p]),
+        "orc_awq_scale_weight": (None, [_u16p, _f32p, _i64, _i64, _u16p]),
+        "orc_awq_scale_act": (None, [_u16p, _f32p, _i64, _i64, _u16p]),
         "orc_q8_quantize_weight": (None, [_u16p, _f32p, _i64, _i64, _i8p, _f32p]),
         "orc_q8_quantize_act": (None, [_u16p, _f32p, _i64, _i64, _i8p, _f32p]),
         "orc_int8_gemm": (_i64, [_i8p, _i64, _i64, _i8p, _i64, _i64p, _i64, _i64p, _i64p]),
@@ -182,6 +184,30 @@ def w4a16_ref(X, codes, scales, zeros, g: int = 128, rows=None):
                           _ptr(zeros, _u8p), N, g, _ptr(r, _i64p), n_rows,
                           _ptr(Y, _f64p), _ptr(B, _f64p))
     return Y, B
+
+
+# --- AWQ-style per-input-channel scaling (W4A16) -----------------------------
+
+def awq_scale_weight(W, s) -> np.ndarray:
+    """w'' = f2h(h2f(W) * s[k]) (fp32 multiply, then binary16). fp16 bits [N, K]."""
+    W = _half_bits(W)
+    N, K = W.shape
+    s = np.ascontiguousarray(np.asarray(s, dtype=np.float32))
+    assert s.shape == (K,)
+    out = np.empty((N, K), np.uint16)
+    _load().orc_awq_scale_weight(_ptr(W, _u16p), _ptr(s, _f32p), N, K, _ptr(out, _u16p))
+    return out
+
+
+def awq_scale_act(X, s) -> np.ndarray:
+    """x'' = f2h(h2f(X) / s[k]) (fp32 division, then binary16). fp16 bits [M, K]."""
+    X = _half_bits(X)
+    M, K = X.shape
+    s = np.ascontiguousarray(np.asarray(s, dtype=np.float32))
+    assert s.shape == (K,)
+    out = np.empty((M, K), np.uint16)
+    _load().orc_awq_scale_act(_ptr(X, _u16p), _ptr(s, _f32p), M, K, _ptr(out, _u16p))
+    return out
 
 
 # --- INT8 path ----------------------------------------------------------------

@@ -258,6 +258,39 @@ void orc_w4a16_ref(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes
 }
 
 /* ------------------------------------------------------------------------ */
+/* AWQ-style per-input-channel scaling on the W4A16 path (Quantization
+ * operators guide §3.2: W'' = W * s and x'' = x / s for every input channel;
+ * Schemes notes, AWQ section: Y = X W = (X / s)(W * s)). The search for s is
+ * offline; here s is given. Both operands stay binary16 (W4A16 keeps 16-bit
+ * activations and quantizes 16-bit weights), so each scaled value is the
+ * IEEE binary32 product or quotient, rounded once more to binary16:
+ *   w''[n][k] = f2h(h2f(W[n][k]) * s[k])
+ *   x''[m][k] = f2h(h2f(X[m][k]) / s[k])
+ * The scaled layer is then the plain W4A16 product of x'' with the INT4
+ * quantization of w'' (orc_q4_quantize_pack, orc_w4a16_ref).               */
+void orc_awq_scale_weight(const uint16_t *W, const float *s, int64_t N, int64_t K,
+                          uint16_t *Ws)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) {
+            float w = orc_h2f(W[n * K + k]) * s[k];
+            Ws[n * K + k] = orc_f2h(w);
+        }
+}
+
+void orc_awq_scale_act(const uint16_t *X, const float *s, int64_t M, int64_t K,
+                       uint16_t *Xs)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t k = 0; k < K; k++) {
+            float x = orc_h2f(X[m * K + k]) / s[k];
+            Xs[m * K + k] = orc_f2h(x);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Per-channel INT8 weight with the SmoothQuant fold (Quantization operators
  * guide §2.2 per-channel: one scale per output row, max|w| / 127, codes
  * clamped to [-127, 127]; §5.1 and Core ideas §2.4: W' = W diag(s)).
