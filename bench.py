@@ -205,6 +205,18 @@ def main():
             bl = w4a16_bytes(1, L["N"], 4096)
             extra[f"decode_n{L['N']}"] = {"us": tl * 1e6, "GB/s": bl / tl / 1e9,
                                           "frac_hbm": bl / tl / 1e9 / HBM_PEAK_GBS}
+        # the N = 11008 layer in its AWQ form: x / s fused into the GEMV's X loads
+        L = next(L for L in layers if L["N"] == 11008)
+        s_awq = torch.from_numpy(np.exp(np.random.default_rng(5002).uniform(-0.5, 0.5, 4096))
+                                 .astype(np.float32)).to(dev)
+        ws = torch.empty((q4.w4a16_awq_workspace_bytes(1, 4096),), dtype=torch.uint8, device=dev)
+        ga = graph_of(lambda i: q4.w4a16_linear_awq(X, *L["copies"][i % copies], s_awq,
+                                                   workspace=ws, out=L["Y"]), copies)
+        ga()
+        ta = timed(lambda i: ga(), reps) / (reps * copies)
+        ba = w4a16_bytes(1, 11008, 4096) + 4096 * 4
+        extra["awq_decode_n11008"] = {"us": ta * 1e6, "GB/s": ba / ta / 1e9,
+                                      "frac_hbm": ba / ta / 1e9 / HBM_PEAK_GBS}
         del layers
         torch.cuda.empty_cache()
 

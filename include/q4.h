@@ -157,6 +157,54 @@ Q4_API q4_status w4a16_linear_multi(const void *X, int64_t M, int64_t K, int32_t
                                     void *stream);
 
 /* ----------------------------------------------------------------------------
+ * AWQ-style per-input-channel scaling on the W4A16 path (Operators guide
+ * §3.2: W'' = W * s and x'' = x / s for every input channel k, so that
+ * X W^T = (X / s)(W s)^T; Schemes notes, AWQ section). The search for s is
+ * offline (outside this library); s is given, fp32 [K], finite and nonzero.
+ * Both operands stay fp16: each scaled value is the IEEE fp32 product or
+ * quotient rounded once more to fp16 (RNE), bit-exact with that definition.
+ *
+ * awq_scale_weight -- Ws[n][k] = f2h(h2f(W[n][k]) * awq_s[k]); quantize Ws
+ *         with q4_quantize_pack to get the AWQ layer's packed weight.
+ * awq_scale_act -- Xs[m][k] = f2h(h2f(X[m][k]) / awq_s[k]).
+ * W / X fp16 [rows, K], K % 8 == 0; Ws / Xs fp16 [rows, K] output, which may
+ * be the input array itself but must not partly overlap it; all three
+ * pointers 16-byte aligned.
+ * Errors: INVALID_ARG (shape, null pointer, partial overlap), MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status awq_scale_weight(const void *W, const float *awq_s, int64_t N, int64_t K,
+                                  void *Ws, void *stream);
+Q4_API q4_status awq_scale_act(const void *X, const float *awq_s, int64_t M, int64_t K,
+                               void *Xs, void *stream);
+
+/* Bytes of workspace w4a16_linear_awq needs for M tokens of width K: the
+ * scaled input [M, K] fp16, rounded up to 256 bytes. */
+Q4_API size_t w4a16_awq_workspace_bytes(int64_t M, int64_t K);
+
+/* ----------------------------------------------------------------------------
+ * w4a16_linear_awq -- the AWQ layer at run time: Y = X'' * W_hat^T with
+ * X'' = awq_scale_act(X, awq_s) and W_hat the dequantized INT4 weight of
+ * awq_scale_weight(W, awq_s) (codes, scales, zeros from q4_quantize_pack).
+ * With one token (M == 1, g == 128) the division is fused into the decode
+ * GEMV's loads of X and the workspace is not touched; otherwise X'' is
+ * written to the workspace first and w4a16_linear runs on it.
+ * Accuracy as for w4a16_linear, against the exact product over X'' and
+ * W_hat.
+ *
+ * X, M, N, K, g, codes, scales, zeros, Y   as for w4a16_linear.
+ * awq_s     fp32 [K], 16-byte aligned.
+ * workspace device memory of at least w4a16_awq_workspace_bytes(M, K)
+ *           bytes, 16-byte aligned (required for every M).
+ * Errors: as for w4a16_linear, plus INVALID_ARG for a NULL awq_s or
+ *         workspace or a too small workspace, MISALIGNED for awq_s or the
+ *         workspace.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status w4a16_linear_awq(const void *X, int64_t M, int64_t N, int64_t K, int32_t g,
+                                  const uint8_t *codes, const void *scales,
+                                  const uint8_t *zeros, const float *awq_s, void *Y,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* ----------------------------------------------------------------------------
  * q8_quantize_weight -- per-output-channel INT8 of the smoothed weight
  * (Operators guide §2.2 per-channel, §5.1/§5.3: W' = W diag(s) folded offline;
  * Core ideas §2.4):

@@ -55,6 +55,11 @@ SIGNATURES = {
     "q4_quantize_pack": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "w4a16_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
     "w4a16_linear_multi": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(W4A16Layer), _i32, _vp]),
+    "awq_scale_weight": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "awq_scale_act": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "w4a16_awq_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "w4a16_linear_awq": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        ctypes.c_size_t, _vp]),
     "q8_quantize_weight": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "q8_quantize_act": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
@@ -202,6 +207,59 @@ def w4a16_linear_multi(X: torch.Tensor, layers, g: int = 128, out=None):
         Ys.append(Y)
     _check(lib().w4a16_linear_multi(_ptr(X), M, K, g, table, len(layers), _stream(X)))
     return Ys
+
+
+# --- AWQ-style per-input-channel scaling (W4A16) -------------------------------
+
+def _need_awq(awq_s, K: int):
+    _need(awq_s, torch.float32, "awq_s", 1)
+    if awq_s.numel() != K:
+        raise ValueError(f"awq_s has {awq_s.numel()} entries, K={K}")
+
+
+def awq_scale_weight(W: torch.Tensor, awq_s: torch.Tensor, out: torch.Tensor | None = None):
+    """W'' fp16 [N, K] = f2h(W * awq_s[k]); quantize it with q4_quantize_pack.
+    out may be W itself."""
+    _need(W, torch.float16, "W", 2)
+    N, K = W.shape
+    _need_awq(awq_s, K)
+    Ws = _output(out, N, K, W.device)
+    _check(lib().awq_scale_weight(_ptr(W), _ptr(awq_s), N, K, _ptr(Ws), _stream(W)))
+    return Ws
+
+
+def awq_scale_act(X: torch.Tensor, awq_s: torch.Tensor, out: torch.Tensor | None = None):
+    """X'' fp16 [M, K] = f2h(X / awq_s[k]). out may be X itself."""
+    _need(X, torch.float16, "X", 2)
+    M, K = X.shape
+    _need_awq(awq_s, K)
+    Xs = _output(out, M, K, X.device)
+    _check(lib().awq_scale_act(_ptr(X), _ptr(awq_s), M, K, _ptr(Xs), _stream(X)))
+    return Xs
+
+
+def w4a16_awq_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().w4a16_awq_workspace_bytes(M, K))
+
+
+def w4a16_linear_awq(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                     zeros: torch.Tensor | None, awq_s: torch.Tensor, g: int = 128,
+                     workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """Y fp16 [M, N] = (X / awq_s) x W_hat^T for the packed AWQ-scaled weight;
+    the division is fused into the decode GEMV when M == 1."""
+    _need(X, torch.float16, "X", 2)
+    M, K = X.shape
+    N = _check_packed(codes, scales, zeros, K, g)
+    _need_awq(awq_s, K)
+    if workspace is None:
+        workspace = torch.empty((max(w4a16_awq_workspace_bytes(M, K), 1),), dtype=torch.uint8,
+                                device=X.device)
+    _need(workspace, torch.uint8, "workspace", 1)
+    Y = _output(out, M, N, X.device)
+    _check(lib().w4a16_linear_awq(_ptr(X), M, N, K, g, _ptr(codes), _ptr(scales), _ptr(zeros),
+                                  _ptr(awq_s), _ptr(Y), _ptr(workspace), workspace.numel(),
+                                  _stream(X)))
+    return Y
 
 
 def _need_smooth(smooth_s, K: int):

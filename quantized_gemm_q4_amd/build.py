@@ -29,6 +29,7 @@ SOURCES = {
     "w8a8.hip": ["-ffp-contract=off"],
     "mxfp4.hip": ["-ffp-contract=off"],
     "nf4.hip": ["-ffp-contract=off"],
+    "awq.hip": ["-ffp-contract=off"],
 }
 
 

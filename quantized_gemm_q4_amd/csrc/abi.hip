@@ -139,6 +139,79 @@ Q4_API q4_status w4a16_linear_multi(const void *X, int64_t M, int64_t K, int32_t
     return from_hip(e, "w4a16_linear_multi");
 }
 
+static q4_status awq_scale(const char *what, const void *A, const float *awq_s, int64_t rows,
+                           int64_t K, void *out, bool div, void *stream)
+{
+    Q4_REQUIRE(rows >= 0 && K > 0 && rows <= kIntMax && K <= kIntMax && K % 8 == 0,
+               Q4_ERR_INVALID_ARG, "%s: bad shape rows=%lld K=%lld (K a multiple of 8)", what,
+               (long long)rows, (long long)K);
+    if (rows == 0) return ok();
+    Q4_REQUIRE(A && awq_s && out, Q4_ERR_INVALID_ARG, "%s: null pointer", what);
+    Q4_REQUIRE(aligned16(A) && aligned16(awq_s) && aligned16(out), Q4_ERR_MISALIGNED,
+               "%s: the operands and awq_s must be 16-byte aligned", what);
+    const char *a = static_cast<const char *>(A), *o = static_cast<const char *>(out);
+    const size_t bytes = (size_t)rows * (size_t)K * 2;
+    Q4_REQUIRE(o == a || o + bytes <= a || a + bytes <= o, Q4_ERR_INVALID_ARG,
+               "%s: the output overlaps the input without being the same array", what);
+    hipError_t e = q4k::launch_awq_scale(static_cast<const uint16_t *>(A), awq_s, rows, K, div,
+                                         static_cast<uint16_t *>(out), static_cast<hipStream_t>(stream));
+    return from_hip(e, what);
+}
+
+Q4_API q4_status awq_scale_weight(const void *W, const float *awq_s, int64_t N, int64_t K, void *Ws,
+                                  void *stream)
+{
+    return awq_scale("awq_scale_weight", W, awq_s, N, K, Ws, false, stream);
+}
+
+Q4_API q4_status awq_scale_act(const void *X, const float *awq_s, int64_t M, int64_t K, void *Xs,
+                               void *stream)
+{
+    return awq_scale("awq_scale_act", X, awq_s, M, K, Xs, true, stream);
+}
+
+Q4_API size_t w4a16_awq_workspace_bytes(int64_t M, int64_t K)
+{
+    if (M <= 0 || K <= 0) return 0;
+    return ((size_t)M * (size_t)K * 2 + 255) / 256 * 256;
+}
+
+Q4_API q4_status w4a16_linear_awq(const void *X, int64_t M, int64_t N, int64_t K, int32_t g,
+                                  const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                                  const float *awq_s, void *Y, void *workspace,
+                                  size_t workspace_bytes, void *stream)
+{
+    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= kIntMax,
+               Q4_ERR_INVALID_ARG, "w4a16_linear_awq: bad shape M=%lld N=%lld K=%lld", (long long)M,
+               (long long)N, (long long)K);
+    Q4_REQUIRE(g > 0 && K % g == 0 && K % 2 == 0, Q4_ERR_INVALID_ARG,
+               "w4a16_linear_awq: K=%lld must be even and a multiple of g=%d", (long long)K, g);
+    Q4_REQUIRE(g % 128 == 0, Q4_ERR_UNSUPPORTED,
+               "w4a16_linear_awq: group size %d unsupported (must be a multiple of 128)", g);
+    Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "w4a16_linear_awq: M=%lld too large",
+               (long long)M);
+    if (M == 0 || N == 0) return ok();
+    Q4_REQUIRE(X && codes && scales && awq_s && Y && workspace, Q4_ERR_INVALID_ARG,
+               "w4a16_linear_awq: null pointer");
+    Q4_REQUIRE(workspace_bytes >= w4a16_awq_workspace_bytes(M, K), Q4_ERR_INVALID_ARG,
+               "w4a16_linear_awq: workspace of %zu bytes is smaller than the %zu needed",
+               workspace_bytes, w4a16_awq_workspace_bytes(M, K));
+    Q4_REQUIRE(aligned16(X) && aligned16(codes) && aligned16(awq_s) && aligned16(workspace),
+               Q4_ERR_MISALIGNED, "w4a16_linear_awq: X, codes, awq_s and workspace must be 16-byte aligned");
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = q4k::launch_w4a16_gemv_awq(static_cast<const uint16_t *>(X), M, N, K, g, codes,
+                                              static_cast<const uint16_t *>(scales), zeros, awq_s,
+                                              static_cast<uint16_t *>(Y), st);
+    if (e != hipErrorNotSupported) return from_hip(e, "w4a16_linear_awq");
+    // other shapes: x'' into the workspace, then the plain W4A16 product
+    uint16_t *xs = static_cast<uint16_t *>(workspace);
+    e = q4k::launch_awq_scale(static_cast<const uint16_t *>(X), awq_s, M, K, true, xs, st);
+    if (e != hipSuccess) return from_hip(e, "w4a16_linear_awq");
+    e = q4k::launch_w4a16(xs, M, N, K, g, codes, static_cast<const uint16_t *>(scales), zeros,
+                          static_cast<uint16_t *>(Y), st);
+    return from_hip(e, "w4a16_linear_awq");
+}
+
 Q4_API q4_status q8_quantize_weight(const void *W, const float *smooth_s, int64_t N, int64_t K,
                                     int8_t *Wq, float *w_scale, void *stream)
 {

@@ -27,6 +27,24 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
+// AWQ-style activation scaling of eight fp16 values: f2h(h2f(x_j) / s_j),
+// an IEEE fp32 division (the library is built with correctly rounded fp32
+// division) rounded once more to fp16. s0 holds s_0..s_3, s1 s_4..s_7.
+__device__ __forceinline__ u32x4 awq_div8(u32x4 x, floatx4 s0, floatx4 s1)
+{
+    const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint32_t d = x[j];
+        float lo = h2f((uint16_t)(d & 0xffffu)) / sv[2 * j];
+        float hi = h2f((uint16_t)(d >> 16)) / sv[2 * j + 1];
+        asm volatile("" : "+v"(lo), "+v"(hi));   // the fp32 quotients, then fp16
+        r[j] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
+    }
+    return r;
+}
+
 // Launchers. Arguments were validated by the C-ABI layer; every launcher
 // enqueues on `st` and returns the launch status.
 hipError_t launch_q4_quantize_pack(const uint16_t *W, int64_t N, int64_t K, int g, int sym,
@@ -60,6 +78,15 @@ struct GemvLayerDesc {
 };
 hipError_t launch_w4a16_gemv_multi(const uint16_t *X, int64_t M, int64_t K, int g,
                                    const GemvLayerDesc *layers, int count, hipStream_t st);
+// AWQ-style per-input-channel scaling (K % 8 == 0): out = f2h(A * s[k])
+// when div is false (weights), f2h(A / s[k]) when it is true (activations).
+hipError_t launch_awq_scale(const uint16_t *A, const float *s, int64_t rows, int64_t K, bool div,
+                            uint16_t *out, hipStream_t st);
+// The decode GEMV on x'' = f2h(x / awq_s) with the division fused into its X
+// staging (M == 1, g = 128); hipErrorNotSupported when it does not apply.
+hipError_t launch_w4a16_gemv_awq(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,
+                                 const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                                 const float *awq_s, uint16_t *Y, hipStream_t st);
 hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
                             const float *sw, int64_t M, int64_t N, int64_t K, uint16_t *Y,
                             int32_t *acc_out, hipStream_t st);

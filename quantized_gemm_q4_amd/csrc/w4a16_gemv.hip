@@ -42,13 +42,17 @@ int gemv_waves_override()
 // A lane whose X row m is >= M feeds row M - 1 instead: MFMA output rows do
 // not mix, and rows >= M are never stored. The wavefronts' partial sums meet
 // in LDS.
-template <int WAVES, int KBW, bool ASYM, bool ONE_ROW>
+//
+// With SM (one X row only) x is replaced by the AWQ-scaled x'' = f2h(x /
+// as[k]) as it goes to LDS; the factors are loaded right behind X.
+template <int WAVES, int KBW, bool ASYM, bool ONE_ROW, bool SM = false>
 __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M, int N, int K,
                                            const uint8_t *__restrict__ codes,
                                            const uint16_t *__restrict__ scales,
                                            const uint8_t *__restrict__ zeros, uint16_t *__restrict__ Y,
-                                           int blk)
+                                           int blk, const float *__restrict__ as = nullptr)
 {
+    static_assert(!SM || ONE_ROW, "the fused activation scaling serves one X row");
     static_assert(KBW == 2 || KBW == 4 || KBW == 8, "vector scale / zero-point loads of 2, 4, 8 groups");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int kh = K >> 1;                                   // dwords per X row
@@ -70,12 +74,19 @@ __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M
     //    chunk per thread).
     constexpr int XW = (KBW * 16 + 63) / 64;                 // 16-byte X chunks per lane
     u32x4 xw[XW];
+    floatx4 asl[XW], ash[XW];   // SM: the factors of the chunk's 8 columns
     u32x4 x0 = {0u, 0u, 0u, 0u};
     if (ONE_ROW) {
 #pragma unroll
         for (int i = 0; i < XW; i++) {
             const int c = lane + 64 * i;
-            if (c < KBW * 16) xw[i] = *reinterpret_cast<const u32x4 *>(X + kb0 * 128 + c * 8);
+            if (c < KBW * 16) {
+                xw[i] = *reinterpret_cast<const u32x4 *>(X + kb0 * 128 + c * 8);
+                if (SM) {
+                    asl[i] = *reinterpret_cast<const floatx4 *>(as + kb0 * 128 + c * 8);
+                    ash[i] = *reinterpret_cast<const floatx4 *>(as + kb0 * 128 + c * 8 + 4);
+                }
+            }
         }
     } else if ((int)threadIdx.x < xchunks) {
         x0 = *reinterpret_cast<const u32x4 *>(X + threadIdx.x * 8);
@@ -110,7 +121,9 @@ __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M
 #pragma unroll
         for (int i = 0; i < XW; i++) {
             const int c = lane + 64 * i;
-            if (c < KBW * 16) *reinterpret_cast<u32x4 *>(xs + kb0 * 64 + c * 4) = permute_x(xw[i]);
+            if (c < KBW * 16)
+                *reinterpret_cast<u32x4 *>(xs + kb0 * 64 + c * 4) =
+                    permute_x(SM ? awq_div8(xw[i], asl[i], ash[i]) : xw[i]);
         }
     } else {
         if ((int)threadIdx.x < xchunks) *reinterpret_cast<u32x4 *>(xs + threadIdx.x * 4) = permute_x(x0);
@@ -168,6 +181,17 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
     uint16_t *__restrict__ Y)
 {
     gemv_block<WAVES, KBW, ASYM, ONE_ROW>(X, M, N, K, codes, scales, zeros, Y, (int)blockIdx.x);
+}
+
+// The decode GEMV (one X row) on the AWQ-scaled x'' = f2h(x / awq_s[k]).
+template <int WAVES, int KBW, bool ASYM>
+__global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_awq_kernel(
+    const uint16_t *__restrict__ X, int N, int K, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    const float *__restrict__ awq_s, uint16_t *__restrict__ Y)
+{
+    gemv_block<WAVES, KBW, ASYM, true, true>(X, 1, N, K, codes, scales, zeros, Y, (int)blockIdx.x,
+                                             awq_s);
 }
 
 // Several layers that read the same X in one launch: layer i owns blocks
@@ -305,6 +329,33 @@ hipError_t launch_w4a16_gemv_multi(const uint16_t *X, int64_t M, int64_t K, int 
     const bool one_row = m == 1;
     auto launch = [&](auto kernel) { kernel<<<(int)blocks, waves * 64, lds, st>>>(X, m, k, L); };
     Q4_GEMV_DISPATCH(w4a16_gemv_multi_kernel);
+    return hipGetLastError();
+}
+hipError_t launch_w4a16_gemv_awq(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,
+                                 const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                                 const float *awq_s, uint16_t *Y, hipStream_t st)
+{
+    if (g != 128 || M != 1 || N * K / 2 >= (int64_t)0xFFFFFF00) return hipErrorNotSupported;
+    const int n = (int)N, k = (int)K;
+    const int blocks = (n + 15) / 16;
+    int waves, kbw;
+    size_t lds;
+    if (!pick_gemv(M, K, blocks, &scales, &zeros, 1, waves, kbw, lds)) return hipErrorNotSupported;
+    auto launch = [&](auto kernel) {
+        kernel<<<blocks, waves * 64, lds, st>>>(X, n, k, codes, scales, zeros, awq_s, Y);
+    };
+#define Q4_AWQ(W, B)                                                                              \
+    (zeros ? launch(w4a16_gemv_awq_kernel<W, B, true>) : launch(w4a16_gemv_awq_kernel<W, B, false>))
+    if (waves == 4 && kbw == 8) Q4_AWQ(4, 8);
+    else if (waves == 4 && kbw == 4) Q4_AWQ(4, 4);
+    else if (waves == 4) Q4_AWQ(4, 2);
+    else if (waves == 8 && kbw == 8) Q4_AWQ(8, 8);
+    else if (waves == 8 && kbw == 4) Q4_AWQ(8, 4);
+    else if (waves == 8) Q4_AWQ(8, 2);
+    else if (kbw == 8) Q4_AWQ(16, 8);
+    else if (kbw == 4) Q4_AWQ(16, 4);
+    else Q4_AWQ(16, 2);
+#undef Q4_AWQ
     return hipGetLastError();
 }
 #undef Q4_GEMV4

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared_functions()) <= exported
     # nothing else of ours leaks out (internal launchers are hidden)
-    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "fp8", "mxfp4", "nf4", "smoothquant", "_ZN3q4k"))}
+    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "fp8", "mxfp4", "nf4", "awq", "smoothquant", "_ZN3q4k"))}
     assert ours == set(declared_functions())
 
 
@@ -50,6 +50,9 @@ def test_layout_version_and_workspace(lib):
     assert lib.w8a8_workspace_bytes(2048, 8192) == 2048 * 8192 + 2048 * 4
     assert lib.w8a8_workspace_bytes(3, 16) == 256 + 12
     assert lib.w8a8_workspace_bytes(0, 16) == 0
+    assert lib.w4a16_awq_workspace_bytes(1, 4096) == 8192
+    assert lib.w4a16_awq_workspace_bytes(3, 24) == 256
+    assert lib.w4a16_awq_workspace_bytes(0, 128) == 0
 
 
 FAKE = 0x10000          # never dereferenced: validation fails first
@@ -144,6 +147,24 @@ def layers(*descs):
     (lambda L: L.nf4_linear(FAKE, 1, 16, 256, FAKE, FAKE + 4, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.nf4_linear(FAKE, 1, 16, 256, None, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.nf4_linear(FAKE, 0, 16, 256, None, None, None, None), q4.Q4_OK),
+    (lambda L: L.awq_scale_weight(FAKE, FAKE, 4, 12, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.awq_scale_weight(FAKE, None, 4, 16, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.awq_scale_weight(MISAL, FAKE, 4, 16, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.awq_scale_act(FAKE, FAKE + 4, 4, 16, FAKE + 256, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.awq_scale_act(FAKE, FAKE, 4, 16, FAKE + 64, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.awq_scale_act(FAKE, FAKE, 0, 16, FAKE, None), q4.Q4_OK),
+    (lambda L: L.w4a16_linear_awq(FAKE, 1, 16, 256, 128, FAKE, FAKE, None, None, FAKE, FAKE, 512, None),
+     q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w4a16_linear_awq(FAKE, 1, 16, 256, 128, FAKE, FAKE, None, FAKE, FAKE, FAKE, 256, None),
+     q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w4a16_linear_awq(FAKE, 1, 16, 256, 128, FAKE, FAKE, None, FAKE, FAKE, None, 512, None),
+     q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w4a16_linear_awq(FAKE, 1, 16, 256, 64, FAKE, FAKE, None, FAKE, FAKE, FAKE, 512, None),
+     q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.w4a16_linear_awq(FAKE, 1, 16, 256, 128, FAKE, FAKE, None, MISAL, FAKE, FAKE, 512, None),
+     q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.w4a16_linear_awq(FAKE, 0, 16, 256, 128, None, None, None, None, None, None, 0, None),
+     q4.Q4_OK),
     (lambda L: L.smoothquant_scales(FAKE, 4, FAKE, 4, 128, 1.5, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.smoothquant_scales(FAKE, 0, FAKE, 4, 128, 0.5, FAKE, None), q4.Q4_ERR_INVALID_ARG),
 ])
