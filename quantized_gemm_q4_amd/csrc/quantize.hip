@@ -270,8 +270,16 @@ __device__ __forceinline__ uint32_t row_codes4(float q0, float q1, float q2, flo
         w = __builtin_amdgcn_cvt_pk_fp8_f32(c(q2), c(q3), w, true);
         return (uint32_t)w;
     } else {
-        auto c = [](float q) { return (uint32_t)(int32_t)fminf(fmaxf(rintf(q), -127.0f), 127.0f) & 0xffu; };
-        return c(q0) | (c(q1) << 8) | (c(q2) << 16) | (c(q3) << 24);
+        // clamp to [-127, 127] (integer bounds, so clamping before rounding
+        // is the same as after), then 1.5 * 2^23 + q rounds q to the nearest
+        // integer, ties to even, and leaves it (two's complement) in the low
+        // byte of the sum's bits; three byte permutes pack the four codes
+        auto c = [](float q) {
+            return __builtin_bit_cast(uint32_t, fminf(fmaxf(q, -127.0f), 127.0f) + 12582912.0f);
+        };
+        const uint32_t p01 = __builtin_amdgcn_perm(c(q1), c(q0), 0x0c0c0400u);
+        const uint32_t p23 = __builtin_amdgcn_perm(c(q3), c(q2), 0x0c0c0400u);
+        return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
     }
 }
 
@@ -350,17 +358,20 @@ __device__ __forceinline__ double recip64(double b)
 
 // max over each half-wavefront (lanes 0-31 and 32-63 each end with their own):
 // DPP quad swaps, half-row and row mirrors, then a lane swizzle across 16
+// (a >= 0, finite: the bit patterns order as the values, so the lanes meet
+// with integer max, which needs no NaN canonicalisation)
 __device__ __forceinline__ float halfwave_max(float a)
 {
-    auto dpp = [](float v, auto ctrl) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                     decltype(ctrl)::value, 0xF, 0xF, false));
+    auto dpp = [](uint32_t v, auto ctrl) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, decltype(ctrl)::value, 0xF, 0xF, false);
     };
-    a = fmaxf(a, dpp(a, std::integral_constant<int, 0xB1>{}));
-    a = fmaxf(a, dpp(a, std::integral_constant<int, 0x4E>{}));
-    a = fmaxf(a, dpp(a, std::integral_constant<int, 0x141>{}));
-    a = fmaxf(a, dpp(a, std::integral_constant<int, 0x140>{}));
-    return fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, a), (16 << 10) | 0x1F)));
+    uint32_t b = __builtin_bit_cast(uint32_t, a);
+    b = max(b, dpp(b, std::integral_constant<int, 0xB1>{}));
+    b = max(b, dpp(b, std::integral_constant<int, 0x4E>{}));
+    b = max(b, dpp(b, std::integral_constant<int, 0x141>{}));
+    b = max(b, dpp(b, std::integral_constant<int, 0x140>{}));
+    b = max(b, (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, (16 << 10) | 0x1F));
+    return __builtin_bit_cast(float, b);
 }
 
 // Per-row INT8 for rows of at most 8192 values: a block of T threads owns
@@ -452,8 +463,9 @@ __global__ __launch_bounds__(T) void q8_rows_kernel(const uint16_t *__restrict__
         __syncthreads();
 #pragma unroll
         for (int h = 0; h < HW; h += 4) {
-            const floatx4 m = *reinterpret_cast<const floatx4 *>(&red[rr][h]);
-            a = fmaxf(a, fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
+            const u32x4 m = *reinterpret_cast<const u32x4 *>(&red[rr][h]);   // maxima as bits
+            const uint32_t m0 = m[0], m1 = m[1], m2 = m[2], m3 = m[3];
+            a = __builtin_bit_cast(float, max(__builtin_bit_cast(uint32_t, a), max(max(m0, m1), max(m2, m3))));
         }
         a = fmaxf(a, 1e-8f);
         const float scale = a / kRowMax<FP8>;
