@@ -963,6 +963,10 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t 
                           hipStream_t st)
 {
     if (M < 1 || M > 64 || K % 128 != 0) return hipErrorNotSupported;
+    // these kernels index the codes and X with 32-bit byte offsets; larger
+    // operands take the skinny kernel (64-bit offsets)
+    if ((int64_t)N * (K / 2) >= ((int64_t)1 << 32) - 256 || (int64_t)M * K * 2 >= ((int64_t)1 << 32))
+        return hipErrorNotSupported;
     const int KB = K / 128;
     const int blocks = (N + 63) / 64;
     // X resident in LDS: 16 rows x K fp16 within 128 KB, 4 k-split groups of

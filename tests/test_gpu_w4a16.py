@@ -202,3 +202,29 @@ def test_batched_wide_n(orc, M, sym):
     N, K = 12800, 1024
     W, X = workloads.small_case(M * 11 + int(sym), M, N, K)
     run_case(orc, W, X, 128, sym, what=f"batched wide M={M} N={N} K={K} sym={sym}")
+
+
+# A packed weight past 4 GiB (codes of 2^32 + 2^20 bytes, K = 65536): byte
+# offsets beyond 32 bits. The GEMV and batched kernels decline such operands
+# and the 64-bit kernels run; sampled columns (the last rows lie past the
+# 2^32-byte mark) against the oracle. Codes, scales and zero-points are drawn
+# on the GPU from a seeded generator and copied back for the sampled rows.
+@pytest.mark.parametrize("M", [1, 20, 300])
+def test_weight_past_32bit_offsets(orc, M):
+    K = 65536
+    N = (2 ** 32 + 2 ** 20) // (K // 2)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7 + M)
+    codes = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=gen)
+    scales = (torch.rand((N, K // 128), device="cuda", generator=gen) * 0.01 + 0.002).half()
+    zeros = torch.randint(0, 256, (N, K // 256), dtype=torch.uint8, device="cuda", generator=gen)
+    X = workloads.normal_fp16(101 + M, (M, K), 1.0)
+    Y = host(q4.w4a16_linear(gpu(X), codes, scales, zeros))
+    rng = np.random.default_rng(M)
+    sel = np.unique(np.concatenate([[0, 1, N // 2, N - 33, N - 2, N - 1], rng.integers(0, N, 20)]))
+    idx = torch.from_numpy(sel).to("cuda")
+    c, s, z = (host(t.index_select(0, idx)) for t in (codes, scales, zeros))
+    Yref, B = orc.w4a16_ref(X, c, s.view(np.uint16), z)
+    check_gemm(Y[:, sel], Yref, B, f"M={M} N={N} K={K} past 32-bit offsets")
+    del codes, scales, zeros
+    torch.cuda.empty_cache()
