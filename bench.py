@@ -352,6 +352,28 @@ def main():
                          "gemm_us": tg * 1e6, "gemm_TFLOP/s": ops / tg / 1e12,
                          "gemm_frac_mfma_fp8": ops / tg / 1e12 / FP8_MFMA_PEAK_TFLOPS}
             del codes, sc, Xq, X, Y, ws
+        # the decode workload's N = 11008 layer (M = 1): the decode GEMV
+        w = workloads.decode(11008)
+        N, K = w["W"].shape
+        X = gpu(w["X"])
+        codes, sc = q4.mxfp4_quantize_weight(gpu(w["W"]))
+        Xq, sx = q4.fp8_quantize_act(X)
+        nb = N * K // 2 + N * K // 32 + K + 4 + N * 2
+        copies = max(2, math.ceil(MALL_BYTES / nb) + 1)
+        cps = [(codes.clone(), sc.clone()) for _ in range(copies)]
+        Y = torch.empty((1, N), dtype=torch.float16, device=dev)
+        ws = q4.w8a8_workspace(1, K, dev)
+        reps = max(1, 2000 // copies)
+        gg = graph_of(lambda i: q4.mxfp4_gemm(Xq, sx, *cps[i % copies], out=Y), copies)
+        gg()
+        tg = timed(lambda i: gg(), reps) / (reps * copies)
+        gl = graph_of(lambda i: q4.mxfp4_linear(X, *cps[i % copies], None, workspace=ws, out=Y), copies)
+        gl()
+        tl = timed(lambda i: gl(), reps) / (reps * copies)
+        res["decode_n11008"] = {"gemv_us": tg * 1e6, "GB/s": nb / tg / 1e9,
+                                "frac_hbm": nb / tg / 1e9 / HBM_PEAK_GBS, "bytes": nb,
+                                "linear_us": tl * 1e6}
+        del cps, codes, sc, Xq, X, Y, ws
         extra["mxfp4_w4a8"] = res
         torch.cuda.empty_cache()
 

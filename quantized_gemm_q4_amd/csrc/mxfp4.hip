@@ -327,6 +327,91 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode GEMV, M <= 32, K % 1024 == 0 (K <= 8192): the same scaled
+// instruction with 32 weight rows per block and the block's 16 wavefronts
+// splitting K into SPW 64-k steps each. A wavefront issues its X fragments,
+// its block scales (one vector load) and then the code runs of all its steps
+// at once, so the whole packed weight is in flight from the start, and each
+// step is computed as soon as its code run has landed. X rows past M repeat
+// row M - 1 (the MFMA's columns do not mix and those are never stored). The
+// wavefronts' partial sums meet in LDS in a fixed order; y = fp16(acc * sx[m]).
+constexpr int MXG_WAVES = 16;
+
+template <int SPW>
+__global__ __launch_bounds__(MXG_WAVES * 64) void mxfp4_gemv_kernel(
+    const uint8_t *__restrict__ Xq, const float *__restrict__ sx, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ scales, int M, int N, int K, uint16_t *__restrict__ Y)
+{
+    static_assert(SPW == 1 || SPW == 2 || SPW == 4 || SPW == 8, "steps per wavefront");
+    __shared__ float red[MXG_WAVES][16][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int n0 = (int)blockIdx.x * 32;
+    const uint32_t nrow = (uint32_t)(n0 + l32 < N ? n0 + l32 : N - 1);
+    const int m = l32 < M ? l32 : M - 1;
+    const int s0 = wave * SPW;                     // first 64-k step of this wavefront
+    const uint32_t kh = (uint32_t)K >> 1, ks = (uint32_t)K >> 5;
+
+    // X: row m, k = 64 s + 16 h .. + 15 (bytes 0-15) and 64 s + 32 + 16 h .. + 15
+    intx4 xlo[SPW], xhi[SPW];
+#pragma unroll
+    for (int s = 0; s < SPW; s++) {
+        const uint8_t *xp = Xq + (size_t)m * (size_t)K + (size_t)(s0 + s) * 64 + 16 * h;
+        xlo[s] = *reinterpret_cast<const intx4 *>(xp);
+        xhi[s] = *reinterpret_cast<const intx4 *>(xp + 32);
+    }
+    // the row's 2 SPW block scales from step s0 on (byte 2 s + h is step s's)
+    uint32_t sc[(2 * SPW + 3) / 4];
+    {
+        const uint8_t *sp = scales + nrow * ks + 2u * (uint32_t)s0;
+        if constexpr (SPW == 8) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(sp);
+#pragma unroll
+            for (int e = 0; e < 4; e++) sc[e] = a[e];
+        } else if constexpr (SPW == 4) {
+            const u32x2 a = *reinterpret_cast<const u32x2 *>(sp);
+            sc[0] = a[0];
+            sc[1] = a[1];
+        } else if constexpr (SPW == 2) {
+            sc[0] = *reinterpret_cast<const uint32_t *>(sp);
+        } else {
+            sc[0] = *reinterpret_cast<const uint16_t *>(sp);
+        }
+    }
+    intx4 cw[SPW];
+#pragma unroll
+    for (int s = 0; s < SPW; s++)
+        cw[s] = *reinterpret_cast<const intx4 *>(codes + nrow * kh + (uint32_t)(s0 + s) * 32u + 16u * (uint32_t)h);
+    __builtin_amdgcn_sched_barrier(0);   // every load goes out before the first product
+
+    floatx16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < SPW; s++) {
+        const intx8 w8 = __builtin_shufflevector(cw[s], intx4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+        const intx8 a = __builtin_shufflevector(xlo[s], xhi[s], 0, 1, 2, 3, 4, 5, 6, 7);
+        const uint32_t word = sc[(2 * s + h) >> 2];
+        const int e = (int)((word >> (8 * ((2 * s + h) & 3))) & 0xffu);
+        // first operand E2M1 (format 4) with its block scale, second E4M3 (format 0) at 1.0
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a, acc, 4, 0, 0, e, 0, 127);
+    }
+
+#pragma unroll
+    for (int r = 0; r < 16; r++) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    {
+        const int r = (int)threadIdx.x >> 6, l = (int)threadIdx.x & 63;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < MXG_WAVES; w++) v += red[w][r][l];
+        const int mm = l & 31;                                  // the accumulator's column: X row
+        const int nn = n0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);   // its row: weight row
+        if (mm < M && nn < N) Y[(int64_t)mm * N + nn] = f2h(v * sx[mm]);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mxfp4_quantize(const uint16_t *W, const float *s, int64_t N, int64_t K,
@@ -348,6 +433,21 @@ hipError_t launch_mxfp4_gemm(const uint8_t *Xq, const float *sx, const uint8_t *
     if (M == 0 || N == 0) return hipSuccess;
     if (K % (2 * MBK) != 0 || M * K >= (int64_t)1 << 31 || N * K >= (int64_t)1 << 31)
         return hipErrorNotSupported;
+    if (M <= 32 && K % 1024 == 0 && K <= 8192 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) {
+        const int blocks = (int)((N + 31) / 32);
+        auto go = [&](auto kernel) {
+            kernel<<<blocks, MXG_WAVES * 64, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N, (int)K, Y);
+        };
+        switch (K / 1024) {
+        case 1: go(mxfp4_gemv_kernel<1>); break;
+        case 2: go(mxfp4_gemv_kernel<2>); break;
+        case 4: go(mxfp4_gemv_kernel<4>); break;
+        case 8: go(mxfp4_gemv_kernel<8>); break;
+        default: goto gemm;   // K = 3, 5, 6, 7, ... x 1024
+        }
+        return hipGetLastError();
+    }
+gemm:
     const int tiles_m = (int)((M + MBM - 1) / MBM), tiles_n = (int)((N + MBN - 1) / MBN);
     // 16-byte scale group loads need whole, aligned 16-byte runs per row
     if (K % 512 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0)

@@ -76,11 +76,20 @@ def test_gemm_shapes(orc, M, N, K):
     run_gemm(orc, M, N, K, M * 137 + N * 11 + K)
 
 
-def test_gemm_block_scales_and_nibbles(orc):
+# Shapes that take the decode GEMV (M <= 32, K a multiple of 1024): each
+# steps-per-wavefront variant (K = 1024 .. 8192), ragged N, rows past M.
+@pytest.mark.parametrize("M,N,K", [(1, 300, 1024), (5, 77, 2048), (17, 1000, 4096), (32, 64, 8192),
+                                   (1, 11008, 4096), (3, 4096, 4096), (31, 33, 3072)])
+def test_gemv_shapes(orc, M, N, K):
+    run_gemm(orc, M, N, K, M * 31 + N + K)
+
+
+@pytest.mark.parametrize("M,K", [(64, 256), (3, 1024)])   # the GEMM, the decode GEMV
+def test_gemm_block_scales_and_nibbles(orc, M, K):
     """Each 32-block of every weight row gets its own scale and only one
     nonzero code, at a position that moves with the block: a wrong scale
     lane, block or nibble order changes the sum."""
-    M, N, K = 64, 64, 256
+    N = 64
     rng = np.random.default_rng(40)
     Xq = rng.integers(0x30, 0x48, (M, K)).astype(np.uint8)      # E4M3 values around 0.5 .. 4
     sx = np.full(M, 1.0, np.float32)
