@@ -346,6 +346,9 @@ Q4_API q4_status mxfp4_quantize_weight(const void *W, const float *smooth_s, int
  *               (fp32 sums of exact products, in the matrix cores' order),
  *   Y[m][n]   = fp16(acc * x_scale[m]).
  * Accuracy: |Y - Y_ref| <= 2^-10 * x_scale sum_k |products| (+2^-25).
+ * With M <= 32 and K a multiple of 1024 (scales 16-byte aligned) a decode
+ * GEMV runs instead of the 256 x 256 tiles; the sums' order differs, the
+ * accuracy bound is the same.
  * Xq u8 E4M3 [M, K] and x_scale fp32 [M] as written by fp8_quantize_act;
  * codes, scales as written by mxfp4_quantize_weight (Xq and codes 16-byte
  * aligned); Y fp16 [M, N] output. K a multiple of 128, at most 8192; M*K
