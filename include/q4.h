@@ -7,7 +7,10 @@
  *     group of g input channels, dequantized inside the GEMM, fp16
  *     activations, fp32 accumulation, fp16 output;
  *   - W8A8: SmoothQuant-migrated per-output-channel INT8 weights, per-token
- *     dynamic INT8 activations, int32 accumulation, fp16 output.
+ *     dynamic INT8 activations, int32 accumulation, fp16 output;
+ * and the variants the pages describe beside them: AWQ-style per-input-
+ * channel scaling on the W4A16 path, FP8 E4M3 in place of INT8, MXFP4
+ * weights with E4M3 activations, and NF4 weights.
  * Pages cited below:
  *   "Core ideas"        ai-infra.cypggs.com, "2. Core ideas: numeric
  *                       representation, rounding, scaling and difficulty
@@ -53,7 +56,7 @@ extern "C" {
 typedef enum {
     Q4_OK = 0,
     Q4_ERR_INVALID_ARG = 1,   /* a null pointer, a bad size or shape */
-    Q4_ERR_UNSUPPORTED = 2,   /* a valid request this build does not serve */
+    Q4_ERR_UNSUPPORTED = 2,   /* a valid request the library does not serve */
     Q4_ERR_MISALIGNED = 3,    /* a tensor pointer not 16-byte aligned */
     Q4_ERR_HIP = 4            /* the HIP runtime reported an error */
 } q4_status;
