@@ -238,7 +238,14 @@ hipError_t launch_nf4_linear(const uint16_t *X, int64_t M, int64_t N, int64_t K,
     const int64_t blocks = (N + 15) / 16;
     if (blocks > 0x7fffffff) return hipErrorNotSupported;
     const size_t red = (size_t)NF4_WAVES * 4 * 64 * 4;
-    const int64_t rows = std::min<int64_t>(16, (int64_t)((64 * 1024 - red) / ((size_t)K * 2)));
+    // up to 16 rows of X per pass, within the 160 KB of LDS; past 64 KB the
+    // kernel needs the larger dynamic allocation enabled (once per process)
+    constexpr size_t kMaxLds = 160 * 1024;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&nf4_gemv_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)kMaxLds);
+    if (attr != hipSuccess) return attr;
+    const int64_t rows = std::min<int64_t>(16, (int64_t)((kMaxLds - red) / ((size_t)K * 2)));
     if (rows < 1) return hipErrorNotSupported;
     for (int64_t m0 = 0; m0 < M; m0 += rows) {
         const int m = (int)std::min<int64_t>(rows, M - m0);

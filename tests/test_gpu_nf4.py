@@ -57,7 +57,7 @@ def run_linear(orc, M, N, K, seed):
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (1, 300, 1024), (3, 77, 256), (16, 300, 640),
                                    (17, 129, 384), (40, 64, 4096), (1, 11008, 4096), (2, 4096, 11008),
-                                   (5, 1000, 8192)])
+                                   (5, 1000, 8192), (16, 11008, 4096), (64, 1000, 4096)])
 def test_linear_shapes(orc, M, N, K):
     run_linear(orc, M, N, K, M * 71 + N + K)
 
