@@ -336,15 +336,24 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
 // step is computed as soon as its code run has landed. X rows past M repeat
 // row M - 1 (the MFMA's columns do not mix and those are never stored). The
 // wavefronts' partial sums meet in LDS in a fixed order; y = fp16(acc * sx[m]).
-constexpr int MXG_WAVES = 16;
 
-template <int SPW>
+//
+// With XL (M (K + 16) <= 64 KB) the block first stages X in LDS (rows K + 16
+// bytes apart, so the 16-byte operand reads of 16 rows fall in distinct
+// banks; one broadcast read when M = 1) and the wavefronts read their
+// fragments there: one or two global loads per thread instead of two per
+// step per wavefront. The stage shares its LDS with the final reduction.
+constexpr int MXG_WAVES = 16;
+constexpr int MXG_LDS = MXG_WAVES * 16 * 64 * 4;   // 64 KB
+
+template <int SPW, bool XL>
 __global__ __launch_bounds__(MXG_WAVES * 64) void mxfp4_gemv_kernel(
     const uint8_t *__restrict__ Xq, const float *__restrict__ sx, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ scales, int M, int N, int K, uint16_t *__restrict__ Y)
 {
     static_assert(SPW == 1 || SPW == 2 || SPW == 4 || SPW == 8, "steps per wavefront");
-    __shared__ float red[MXG_WAVES][16][64];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[MXG_LDS];
+    float(*red)[16][64] = reinterpret_cast<float(*)[16][64]>(lds);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, h = lane >> 5;
     const int n0 = (int)blockIdx.x * 32;
@@ -352,14 +361,26 @@ __global__ __launch_bounds__(MXG_WAVES * 64) void mxfp4_gemv_kernel(
     const int m = l32 < M ? l32 : M - 1;
     const int s0 = wave * SPW;                     // first 64-k step of this wavefront
     const uint32_t kh = (uint32_t)K >> 1, ks = (uint32_t)K >> 5;
+    const int xs = K + 16;                         // LDS row stride of the staged X
 
     // X: row m, k = 64 s + 16 h .. + 15 (bytes 0-15) and 64 s + 32 + 16 h .. + 15
     intx4 xlo[SPW], xhi[SPW];
+    constexpr int XPT = MXG_LDS / 16 / (MXG_WAVES * 64);   // 16-byte chunks per thread at most
+    intx4 xv[XPT];
+    const int nch = XL ? M * (K >> 4) : 0;
+    if (XL) {
 #pragma unroll
-    for (int s = 0; s < SPW; s++) {
-        const uint8_t *xp = Xq + (size_t)m * (size_t)K + (size_t)(s0 + s) * 64 + 16 * h;
-        xlo[s] = *reinterpret_cast<const intx4 *>(xp);
-        xhi[s] = *reinterpret_cast<const intx4 *>(xp + 32);
+        for (int i = 0; i < XPT; i++) {
+            const int c = (int)threadIdx.x + i * MXG_WAVES * 64;
+            if (c < nch) xv[i] = *reinterpret_cast<const intx4 *>(Xq + (size_t)c * 16);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < SPW; s++) {
+            const uint8_t *xp = Xq + (size_t)m * (size_t)K + (size_t)(s0 + s) * 64 + 16 * h;
+            xlo[s] = *reinterpret_cast<const intx4 *>(xp);
+            xhi[s] = *reinterpret_cast<const intx4 *>(xp + 32);
+        }
     }
     // the row's 2 SPW block scales from step s0 on (byte 2 s + h is step s's)
     uint32_t sc[(2 * SPW + 3) / 4];
@@ -384,6 +405,21 @@ __global__ __launch_bounds__(MXG_WAVES * 64) void mxfp4_gemv_kernel(
     for (int s = 0; s < SPW; s++)
         cw[s] = *reinterpret_cast<const intx4 *>(codes + nrow * kh + (uint32_t)(s0 + s) * 32u + 16u * (uint32_t)h);
     __builtin_amdgcn_sched_barrier(0);   // every load goes out before the first product
+    if (XL) {
+#pragma unroll
+        for (int i = 0; i < XPT; i++) {
+            const int c = (int)threadIdx.x + i * MXG_WAVES * 64;
+            const int r = c / (K >> 4), cc = c - r * (K >> 4);
+            if (c < nch) *reinterpret_cast<intx4 *>(lds + r * xs + cc * 16) = xv[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < SPW; s++) {
+            const unsigned char *xp = lds + m * xs + (s0 + s) * 64 + 16 * h;
+            xlo[s] = *reinterpret_cast<const intx4 *>(xp);
+            xhi[s] = *reinterpret_cast<const intx4 *>(xp + 32);
+        }
+    }
 
     floatx16 acc;
 #pragma unroll
@@ -398,6 +434,7 @@ __global__ __launch_bounds__(MXG_WAVES * 64) void mxfp4_gemv_kernel(
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a, acc, 4, 0, 0, e, 0, 127);
     }
 
+    if (XL) __syncthreads();   // every wavefront has read its X fragments
 #pragma unroll
     for (int r = 0; r < 16; r++) red[wave][r][lane] = acc[r];
     __syncthreads();
@@ -435,14 +472,16 @@ hipError_t launch_mxfp4_gemm(const uint8_t *Xq, const float *sx, const uint8_t *
         return hipErrorNotSupported;
     if (M <= 32 && K % 1024 == 0 && K <= 8192 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) {
         const int blocks = (int)((N + 31) / 32);
-        auto go = [&](auto kernel) {
-            kernel<<<blocks, MXG_WAVES * 64, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N, (int)K, Y);
+        const bool xl = M * (K + 16) <= MXG_LDS;
+        auto go = [&](auto k_lds, auto k_reg) {
+            if (xl) k_lds<<<blocks, MXG_WAVES * 64, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N, (int)K, Y);
+            else k_reg<<<blocks, MXG_WAVES * 64, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N, (int)K, Y);
         };
         switch (K / 1024) {
-        case 1: go(mxfp4_gemv_kernel<1>); break;
-        case 2: go(mxfp4_gemv_kernel<2>); break;
-        case 4: go(mxfp4_gemv_kernel<4>); break;
-        case 8: go(mxfp4_gemv_kernel<8>); break;
+        case 1: go(mxfp4_gemv_kernel<1, true>, mxfp4_gemv_kernel<1, false>); break;
+        case 2: go(mxfp4_gemv_kernel<2, true>, mxfp4_gemv_kernel<2, false>); break;
+        case 4: go(mxfp4_gemv_kernel<4, true>, mxfp4_gemv_kernel<4, false>); break;
+        case 8: go(mxfp4_gemv_kernel<8, true>, mxfp4_gemv_kernel<8, false>); break;
         default: goto gemm;   // K = 3, 5, 6, 7, ... x 1024
         }
         return hipGetLastError();
