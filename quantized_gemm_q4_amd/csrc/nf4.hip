@@ -67,7 +67,8 @@ __device__ __forceinline__ u32x4 nf4_dequant8(uint32_t d)
 // by DPP: quad swaps, then the half-row mirror). w / scale is formed exactly
 // (fp64 product with the refined reciprocal, as in the INT8 quantizer:
 // fl32(fl64(w * r)) = fl32(w / scale)); the code is the first index of the
-// smallest fp32 |x - level|, the oracle's scan.
+// smallest fp32 |x - level| over the 16 levels in ascending order (the
+// guide's argmin, ties to the lower index).
 __device__ __forceinline__ double nf4_recip64(double b)
 {
     double r = __builtin_amdgcn_rcp(b);
