@@ -449,6 +449,124 @@ __global__ __launch_bounds__(MXG_WAVES * 64) void mxfp4_gemv_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode GEMV for M <= 16 on v_mfma_scale_f32_16x16x128_f8f6f4: 16 weight
+// rows per block (twice the blocks of the 32-row kernel above, so the grid
+// spreads evenly over the CUs), 8 wavefronts splitting K into SPW 128-k steps
+// (one instruction each). Operand layout of the instruction (measured): an
+// E2M1 lane of group g = l / 16 holds k = 32 g .. 32 g + 31 of the step (its
+// MX block, so its scale is that block's byte), an E4M3 lane of group g holds
+// k = 16 g .. + 15 in bytes 0-15 and k = 64 + 16 g .. + 15 in bytes 16-31;
+// result lane l holds X row l % 16 and weight rows 4 (l / 16) .. + 3. Loads,
+// X staging (XL: M (K + 16) <= 32 KB) and the final sum as in the 32-row kernel.
+constexpr int MXH_WAVES = 8;
+constexpr int MXH_LDS = 32 * 1024;
+
+template <int SPW, bool XL>
+__global__ __launch_bounds__(MXH_WAVES * 64) void mxfp4_gemv16_kernel(
+    const uint8_t *__restrict__ Xq, const float *__restrict__ sx, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ scales, int M, int N, int K, uint16_t *__restrict__ Y)
+{
+    static_assert(SPW == 1 || SPW == 2 || SPW == 4 || SPW == 8, "steps per wavefront");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[MXH_LDS];
+    float(*red)[4][64] = reinterpret_cast<float(*)[4][64]>(lds);   // [MXH_WAVES][4][64]: 8 KB
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int n0 = (int)blockIdx.x * 16;
+    const uint32_t nrow = (uint32_t)(n0 + l16 < N ? n0 + l16 : N - 1);
+    const int m = l16 < M ? l16 : M - 1;
+    const int s0 = wave * SPW;                     // first 128-k step of this wavefront
+    const uint32_t kh = (uint32_t)K >> 1, ks = (uint32_t)K >> 5;
+    const int xs = K + 16;
+
+    intx4 xlo[SPW], xhi[SPW];
+    constexpr int XPT = MXH_LDS / 16 / (MXH_WAVES * 64);
+    intx4 xv[XPT];
+    const int nch = XL ? M * (K >> 4) : 0;
+    if (XL) {
+#pragma unroll
+        for (int i = 0; i < XPT; i++) {
+            const int c = (int)threadIdx.x + i * MXH_WAVES * 64;
+            if (c < nch) xv[i] = *reinterpret_cast<const intx4 *>(Xq + (size_t)c * 16);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < SPW; s++) {
+            const uint8_t *xp = Xq + (size_t)m * (size_t)K + (size_t)(s0 + s) * 128 + 16 * g;
+            xlo[s] = *reinterpret_cast<const intx4 *>(xp);
+            xhi[s] = *reinterpret_cast<const intx4 *>(xp + 64);
+        }
+    }
+    // the row's 4 SPW block scales from step s0 on (byte 4 s + g is step s's)
+    uint32_t sc[SPW];
+    {
+        const uint8_t *sp = scales + nrow * ks + 4u * (uint32_t)s0;
+        if constexpr (SPW == 8) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(sp);
+            const u32x4 b = *reinterpret_cast<const u32x4 *>(sp + 16);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                sc[e] = a[e];
+                sc[4 + e] = b[e];
+            }
+        } else if constexpr (SPW == 4) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(sp);
+#pragma unroll
+            for (int e = 0; e < 4; e++) sc[e] = a[e];
+        } else if constexpr (SPW == 2) {
+            const u32x2 a = *reinterpret_cast<const u32x2 *>(sp);
+            sc[0] = a[0];
+            sc[1] = a[1];
+        } else {
+            sc[0] = *reinterpret_cast<const uint32_t *>(sp);
+        }
+    }
+    intx4 cw[SPW];
+#pragma unroll
+    for (int s = 0; s < SPW; s++)
+        cw[s] = *reinterpret_cast<const intx4 *>(codes + nrow * kh + (uint32_t)(s0 + s) * 64u + 16u * (uint32_t)g);
+    __builtin_amdgcn_sched_barrier(0);   // every load goes out before the first product
+    if (XL) {
+#pragma unroll
+        for (int i = 0; i < XPT; i++) {
+            const int c = (int)threadIdx.x + i * MXH_WAVES * 64;
+            const int r = c / (K >> 4), cc = c - r * (K >> 4);
+            if (c < nch) *reinterpret_cast<intx4 *>(lds + r * xs + cc * 16) = xv[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < SPW; s++) {
+            const unsigned char *xp = lds + m * xs + (s0 + s) * 128 + 16 * g;
+            xlo[s] = *reinterpret_cast<const intx4 *>(xp);
+            xhi[s] = *reinterpret_cast<const intx4 *>(xp + 64);
+        }
+    }
+
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < SPW; s++) {
+        const intx8 w8 = __builtin_shufflevector(cw[s], intx4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+        const intx8 a = __builtin_shufflevector(xlo[s], xhi[s], 0, 1, 2, 3, 4, 5, 6, 7);
+        const int e = (int)((sc[s] >> (8 * g)) & 0xffu);
+        // first operand E2M1 (format 4) with its block scale, second E4M3 (format 0) at 1.0
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w8, a, acc, 4, 0, 0, e, 0, 127);
+    }
+
+    if (XL) __syncthreads();   // every wavefront has read its X fragments
+#pragma unroll
+    for (int r = 0; r < 4; r++) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int r = (int)threadIdx.x >> 6, l = (int)threadIdx.x & 63;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < MXH_WAVES; w++) v += red[w][r][l];
+        const int mm = l & 15;                     // the result's column: X row
+        const int nn = n0 + 4 * (l >> 4) + r;      // its row: weight row
+        if (mm < M && nn < N) Y[(int64_t)mm * N + nn] = f2h(v * sx[mm]);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mxfp4_quantize(const uint16_t *W, const float *s, int64_t N, int64_t K,
@@ -470,6 +588,22 @@ hipError_t launch_mxfp4_gemm(const uint8_t *Xq, const float *sx, const uint8_t *
     if (M == 0 || N == 0) return hipSuccess;
     if (K % (2 * MBK) != 0 || M * K >= (int64_t)1 << 31 || N * K >= (int64_t)1 << 31)
         return hipErrorNotSupported;
+    if (M <= 16 && K % 1024 == 0 && K <= 8192 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) {
+        const int blocks = (int)((N + 15) / 16);
+        const bool xl = M * (K + 16) <= MXH_LDS;
+        auto go = [&](auto k_lds, auto k_reg) {
+            if (xl) k_lds<<<blocks, MXH_WAVES * 64, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N, (int)K, Y);
+            else k_reg<<<blocks, MXH_WAVES * 64, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N, (int)K, Y);
+        };
+        switch (K / 1024) {
+        case 1: go(mxfp4_gemv16_kernel<1, true>, mxfp4_gemv16_kernel<1, false>); break;
+        case 2: go(mxfp4_gemv16_kernel<2, true>, mxfp4_gemv16_kernel<2, false>); break;
+        case 4: go(mxfp4_gemv16_kernel<4, true>, mxfp4_gemv16_kernel<4, false>); break;
+        case 8: go(mxfp4_gemv16_kernel<8, true>, mxfp4_gemv16_kernel<8, false>); break;
+        default: goto gemm;
+        }
+        return hipGetLastError();
+    }
     if (M <= 32 && K % 1024 == 0 && K <= 8192 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) {
         const int blocks = (int)((N + 31) / 32);
         const bool xl = M * (K + 16) <= MXG_LDS;

@@ -76,15 +76,18 @@ def test_gemm_shapes(orc, M, N, K):
     run_gemm(orc, M, N, K, M * 137 + N * 11 + K)
 
 
-# Shapes that take the decode GEMV (M <= 32, K a multiple of 1024): each
-# steps-per-wavefront variant (K = 1024 .. 8192), ragged N, rows past M.
+# Shapes that take the decode GEMVs (K a multiple of 1024): 16 weight rows per
+# block for M <= 16 (X staged in LDS up to 32 KB, else in registers), 32 rows
+# for 16 < M <= 32; each steps-per-wavefront variant (K = 1024 .. 8192),
+# ragged N, rows past M; K = 3072 falls back to the GEMM.
 @pytest.mark.parametrize("M,N,K", [(1, 300, 1024), (5, 77, 2048), (17, 1000, 4096), (32, 64, 8192),
-                                   (1, 11008, 4096), (3, 4096, 4096), (31, 33, 3072)])
+                                   (1, 11008, 4096), (3, 4096, 4096), (31, 33, 3072),
+                                   (16, 100, 4096), (9, 50, 8192), (20, 70, 2048)])
 def test_gemv_shapes(orc, M, N, K):
     run_gemm(orc, M, N, K, M * 31 + N + K)
 
 
-@pytest.mark.parametrize("M,K", [(64, 256), (3, 1024)])   # the GEMM, the decode GEMV
+@pytest.mark.parametrize("M,K", [(64, 256), (3, 1024), (24, 1024)])   # GEMM, 16- and 32-row GEMVs
 def test_gemm_block_scales_and_nibbles(orc, M, K):
     """Each 32-block of every weight row gets its own scale and only one
     nonzero code, at a position that moves with the block: a wrong scale
