@@ -410,6 +410,75 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// FP8 decode GEMV, M <= 16, K % 1024 == 0 (K <= 8192): the E4M3 GEMM's tiles
+// would use one row in 256, so a block owns 16 weight rows and its 8
+// wavefronts split K into 128-k steps, each one v_mfma_scale_f32_16x16x128_
+// f8f6f4 with both operands E4M3 at scale 1.0. Both operands use the same
+// byte layout (a lane of group g = l / 16 holds k = 16 g .. + 15 and
+// 64 + 16 g .. + 15 of the step), so weight and X fragments are loaded alike.
+// Every load of a wavefront is issued at once (X first), each step is
+// computed as its weight bytes land; the wavefronts' sums meet in LDS and the
+// epilogue is the GEMM's, y = fp16((acc * sx[m]) * sw[n]).
+constexpr int F8G_WAVES = 8;
+
+template <int SPW>
+__global__ __launch_bounds__(F8G_WAVES * 64) void fp8_gemv16_kernel(
+    const uint8_t *__restrict__ Xq, const float *__restrict__ sx, const uint8_t *__restrict__ Wq,
+    const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y)
+{
+    static_assert(SPW == 1 || SPW == 2 || SPW == 4 || SPW == 8, "steps per wavefront");
+    __shared__ float red[F8G_WAVES][4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int n0 = (int)blockIdx.x * 16;
+    const int64_t nrow = n0 + l16 < N ? n0 + l16 : N - 1;
+    const int m = l16 < M ? l16 : M - 1;
+    const int s0 = wave * SPW;
+
+    intx4 xlo[SPW], xhi[SPW], wlo[SPW], whi[SPW];
+#pragma unroll
+    for (int s = 0; s < SPW; s++) {
+        const uint8_t *xp = Xq + (int64_t)m * K + (s0 + s) * 128 + 16 * g;
+        xlo[s] = *reinterpret_cast<const intx4 *>(xp);
+        xhi[s] = *reinterpret_cast<const intx4 *>(xp + 64);
+    }
+#pragma unroll
+    for (int s = 0; s < SPW; s++) {
+        const uint8_t *wp = Wq + nrow * K + (s0 + s) * 128 + 16 * g;
+        wlo[s] = *reinterpret_cast<const intx4 *>(wp);
+        whi[s] = *reinterpret_cast<const intx4 *>(wp + 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load goes out before the first product
+
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < SPW; s++) {
+        const intx8 w8 = __builtin_shufflevector(wlo[s], whi[s], 0, 1, 2, 3, 4, 5, 6, 7);
+        const intx8 a = __builtin_shufflevector(xlo[s], xhi[s], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w8, a, acc, 0, 0, 0, 127, 0, 127);
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; r++) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int r = (int)threadIdx.x >> 6, l = (int)threadIdx.x & 63;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < F8G_WAVES; w++) v += red[w][r][l];
+        const int mm = l & 15;                     // the result's column: X row
+        const int nn = n0 + 4 * (l >> 4) + r;      // its row: weight row
+        if (mm < M && nn < N) {
+            float f = v * sx[mm];
+            f = f * sw[nn];
+            asm volatile("" : "+v"(f));   // two fp32 roundings, then fp16 (no fused multiply-convert)
+            Y[(int64_t)mm * N + nn] = f2h(f);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
@@ -434,6 +503,19 @@ hipError_t launch_fp8_gemm(const uint8_t *Xq, const float *sx, const uint8_t *Wq
     if (M == 0 || N == 0) return hipSuccess;
     if (K % (2 * LBK) != 0 || M * K >= (int64_t)1 << 31 || N * K >= (int64_t)1 << 31)
         return hipErrorNotSupported;
+    if (M <= 16 && K % 1024 == 0 && K <= 8192) {
+        const int blocks = (int)((N + 15) / 16);
+        auto go = [&](auto kernel) {
+            kernel<<<blocks, F8G_WAVES * 64, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N, (int)K, Y);
+        };
+        switch (K / 1024) {
+        case 1: go(fp8_gemv16_kernel<1>); return hipGetLastError();
+        case 2: go(fp8_gemv16_kernel<2>); return hipGetLastError();
+        case 4: go(fp8_gemv16_kernel<4>); return hipGetLastError();
+        case 8: go(fp8_gemv16_kernel<8>); return hipGetLastError();
+        default: break;   // K = 3, 5, 6, 7 x 1024: the GEMM
+        }
+    }
     const int tiles_m = (int)((M + LBM - 1) / LBM), tiles_n = (int)((N + LBN - 1) / LBN);
     w8a8_gemm_large_kernel<true><<<tiles_m * tiles_n, 512, 0, st>>>(
         reinterpret_cast<const int8_t *>(Xq), sx, reinterpret_cast<const int8_t *>(Wq), sw, (int)M,

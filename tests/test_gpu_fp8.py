@@ -79,6 +79,15 @@ def test_gemm_shapes(orc, M, N, K):
     run_gemm(orc, M, N, K, M * 131 + N * 7 + K)
 
 
+# Shapes that take the decode GEMV (M <= 16, K a multiple of 1024): each
+# steps-per-wavefront variant (K = 1024 .. 8192), ragged N, rows past M;
+# K = 3072 falls back to the GEMM.
+@pytest.mark.parametrize("M,N,K", [(1, 300, 1024), (5, 77, 2048), (16, 1000, 4096), (3, 64, 8192),
+                                   (1, 11008, 4096), (7, 33, 3072)])
+def test_gemv_shapes(orc, M, N, K):
+    run_gemm(orc, M, N, K, M * 29 + N + K)
+
+
 def test_gemm_closed_form():
     K = 8192
     Xq = torch.full((3, K), 0x7E, dtype=torch.uint8, device="cuda")     # 448
