@@ -301,6 +301,8 @@ Q4_API q4_status fp8_quantize_act(const void *X, const float *smooth_s, int64_t 
  *   Y[m][n]   = fp16((acc * x_scale[m]) * w_scale[n]).
  * Accuracy: |Y - Y_ref| <= 2^-10 * x_scale w_scale sum_k |products| (+2^-25)
  * against the exact sum (K <= 8192 keeps the fp32 sum within half of it).
+ * With M <= 16 and K a multiple of 1024 a decode GEMV runs instead of the
+ * 256 x 256 tiles (same formula and bound, another summation order).
  * Xq, Wq u8 E4M3 codes [M, K], [N, K] (16-byte aligned); x_scale fp32 [M];
  * w_scale fp32 [N]; Y fp16 [M, N] output. K must be a multiple of 128;
  * M*K and N*K below 2^31.
