@@ -302,6 +302,22 @@ def main():
                          "gemm_frac_mfma_int8": ops / tg / 1e12 / INT8_MFMA_PEAK_TOPS,
                          "act_quant_us": ta * 1e6, "act_quant_GB/s": abytes / ta / 1e9}
         del Wq, Xq
+        # the decode workload's N = 11008 layer (M = 1) with INT8 weights: the decode GEMV
+        w = workloads.decode(11008)
+        N, K = w["W"].shape
+        Wq, sw = q4.q8_quantize_weight(gpu(w["W"]))
+        Xq, sx = q4.q8_quantize_act(gpu(w["X"]))
+        nb = N * K + N * 4 + K + 4 + N * 2
+        copies = max(2, math.ceil(MALL_BYTES / nb) + 1)
+        cps = [(Wq.clone(), sw.clone()) for _ in range(copies)]
+        Y = torch.empty((1, N), dtype=torch.float16, device=dev)
+        reps = max(1, 2000 // copies)
+        gg = graph_of(lambda i: q4.w8a8_gemm(Xq, sx, *cps[i % copies], out=Y), copies)
+        gg()
+        tg = timed(lambda i: gg(), reps) / (reps * copies)
+        extra["w8a8"]["decode_n11008"] = {"gemv_us": tg * 1e6, "GB/s": nb / tg / 1e9,
+                                          "frac_hbm": nb / tg / 1e9 / HBM_PEAK_GBS, "bytes": nb}
+        del cps, Wq, Xq, Y
 
     # ---- FP8 E4M3 variant of the same layer ------------------------------------
     if only in (None, "w8a8", "fp8"):

@@ -245,6 +245,8 @@ Q4_API q4_status q8_quantize_act(const void *X, const float *smooth_s, int64_t M
  * K <= 133143 so the int32 sum cannot overflow); x_scale fp32 [M];
  * w_scale fp32 [N]; Y fp16 [M, N] output; acc_out optional int32 [M, N]
  * output (for bit-exact checks; NULL in production).
+ * With M <= 16 and K a multiple of 1024 up to 8192 a decode GEMV runs
+ * instead of the tiles (the same exact sums and epilogue).
  * Errors: INVALID_ARG, MISALIGNED, HIP.
  * -------------------------------------------------------------------------- */
 Q4_API q4_status w8a8_gemm(const int8_t *Xq, const float *x_scale, const int8_t *Wq,

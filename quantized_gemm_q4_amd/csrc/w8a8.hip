@@ -479,6 +479,74 @@ __global__ __launch_bounds__(F8G_WAVES * 64) void fp8_gemv16_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// INT8 decode GEMV, M <= 16, K % 1024 == 0 (K <= 8192): a block owns 16 weight
+// rows and its 8 wavefronts split K into 128-k steps of two
+// v_mfma_i32_16x16x64_i8 each; weight and X fragments use the same byte
+// layout, so they are loaded alike and the int32 sums are exact whatever the
+// order. Every load is issued at once; the wavefronts' int32 partial sums meet
+// in LDS; the epilogue is the GEMM's, y = fp16((float(acc) * sx[m]) * sw[n]),
+// and acc_out (when given) receives the int32 sums.
+constexpr int I8G_WAVES = 8;
+
+template <int SPW>
+__global__ __launch_bounds__(I8G_WAVES * 64) void w8a8_gemv16_kernel(
+    const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
+    const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y,
+    int32_t *__restrict__ acc_out)
+{
+    static_assert(SPW == 1 || SPW == 2 || SPW == 4 || SPW == 8, "steps per wavefront");
+    __shared__ int red[I8G_WAVES][4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int n0 = (int)blockIdx.x * 16;
+    const int64_t nrow = n0 + l16 < N ? n0 + l16 : N - 1;
+    const int m = l16 < M ? l16 : M - 1;
+    const int s0 = wave * SPW;
+
+    intx4 xlo[SPW], xhi[SPW], wlo[SPW], whi[SPW];
+#pragma unroll
+    for (int s = 0; s < SPW; s++) {
+        const int8_t *xp = Xq + (int64_t)m * K + (s0 + s) * 128 + 16 * g;
+        xlo[s] = *reinterpret_cast<const intx4 *>(xp);
+        xhi[s] = *reinterpret_cast<const intx4 *>(xp + 64);
+    }
+#pragma unroll
+    for (int s = 0; s < SPW; s++) {
+        const int8_t *wp = Wq + nrow * K + (s0 + s) * 128 + 16 * g;
+        wlo[s] = *reinterpret_cast<const intx4 *>(wp);
+        whi[s] = *reinterpret_cast<const intx4 *>(wp + 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load goes out before the first product
+
+    intx4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < SPW; s++) {
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo[s], xlo[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi[s], xhi[s], acc, 0, 0, 0);
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; r++) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int r = (int)threadIdx.x >> 6, l = (int)threadIdx.x & 63;
+        int v = 0;
+#pragma unroll
+        for (int w = 0; w < I8G_WAVES; w++) v += red[w][r][l];
+        const int mm = l & 15;                     // the result's column: X row
+        const int nn = n0 + 4 * (l >> 4) + r;      // its row: weight row
+        if (mm < M && nn < N) {
+            if (acc_out) acc_out[(int64_t)mm * N + nn] = v;
+            float f = (float)v * sx[mm];
+            f = f * sw[nn];
+            asm volatile("" : "+v"(f));   // two fp32 roundings, then fp16 (no fused multiply-convert)
+            Y[(int64_t)mm * N + nn] = f2h(f);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
@@ -486,6 +554,19 @@ hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
                             hipStream_t st)
 {
     if (M == 0 || N == 0) return hipSuccess;
+    if (M <= 16 && K % 1024 == 0 && K <= 8192 && N * K < (int64_t)1 << 31) {
+        const int blocks = (int)((N + 15) / 16);
+        auto go = [&](auto kernel) {
+            kernel<<<blocks, I8G_WAVES * 64, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N, (int)K, Y, acc_out);
+        };
+        switch (K / 1024) {
+        case 1: go(w8a8_gemv16_kernel<1>); return hipGetLastError();
+        case 2: go(w8a8_gemv16_kernel<2>); return hipGetLastError();
+        case 4: go(w8a8_gemv16_kernel<4>); return hipGetLastError();
+        case 8: go(w8a8_gemv16_kernel<8>); return hipGetLastError();
+        default: break;   // K = 3, 5, 6, 7 x 1024: the GEMMs
+        }
+    }
     if (K % (2 * LBK) == 0 && M * K < (int64_t)1 << 31 && N * K < (int64_t)1 << 31) {
         const int tiles_m = (int)((M + LBM - 1) / LBM), tiles_n = (int)((N + LBN - 1) / LBN);
         w8a8_gemm_large_kernel<false><<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N,

@@ -76,6 +76,15 @@ def test_gemm_shapes(orc, M, N, K):
     check_gemm(Y, Yref, B, f"w8a8 M={M} N={N} K={K}")
 
 
+# M <= 16 with K a multiple of 1024 up to 8192: the decode GEMV (16 weight
+# rows per block, K split over 8 wavefronts); K = 3072 takes the GEMMs
+@pytest.mark.parametrize("M,N,K", [(1, 300, 1024), (5, 77, 2048), (16, 1000, 4096),
+                                   (3, 64, 8192), (1, 11008, 4096), (7, 33, 3072),
+                                   (16, 17, 1024)])
+def test_gemv_shapes(orc, M, N, K):
+    test_gemm_shapes(orc, M, N, K)
+
+
 def test_closed_form_accumulator():
     K = 8192
     Xq = torch.full((3, K), 127, dtype=torch.int8, device="cuda")
