@@ -114,12 +114,17 @@ Q4_API q4_status q4_quantize_pack(const void *W, int64_t N, int64_t K, int32_t g
  *
  * X       fp16 [M, K] input, 16-byte aligned.
  * M       tokens, >= 0.   N output channels, >= 0.   K input channels, > 0.
- * g       group size: a multiple of 128 (128 is the layout's design point).
+ * g       group size: a multiple of 32 -- every size q4_quantize_pack writes
+ *         (32, 64, 128) and larger multiples of 128. 128 is the layout's
+ *         design point, which the decode and batched kernels serve; other
+ *         sizes take general kernels that apply each group's scale to the
+ *         exact fp32 sum of its own 32-wide k steps.
  * codes, scales, zeros   as written by q4_quantize_pack; zeros == NULL means
  *         symmetric (zp = 8). codes 16-byte aligned.
  * Y       fp16 [M, N] output.
  * Errors: INVALID_ARG (null pointer, K % g != 0, K % 2 != 0),
- *         UNSUPPORTED (g % 128 != 0), MISALIGNED (X, codes), HIP.
+ *         UNSUPPORTED (g % 32 != 0, M > 65535 * 128), MISALIGNED (X, codes),
+ *         HIP.
  * -------------------------------------------------------------------------- */
 Q4_API q4_status w4a16_linear(const void *X, int64_t M, int64_t N, int64_t K,
                               int32_t g, const uint8_t *codes, const void *scales,
@@ -247,7 +252,7 @@ Q4_API q4_status q8_quantize_act(const void *X, const float *smooth_s, int64_t M
  * output (for bit-exact checks; NULL in production).
  * With M <= 16 and K a multiple of 1024 up to 8192 a decode GEMV runs
  * instead of the tiles (the same exact sums and epilogue).
- * Errors: INVALID_ARG, MISALIGNED, HIP.
+ * Errors: INVALID_ARG, UNSUPPORTED (M > 65535 * 128), MISALIGNED, HIP.
  * -------------------------------------------------------------------------- */
 Q4_API q4_status w8a8_gemm(const int8_t *Xq, const float *x_scale, const int8_t *Wq,
                            const float *w_scale, int64_t M, int64_t N, int64_t K,
@@ -266,7 +271,11 @@ Q4_API size_t w8a8_workspace_bytes(int64_t M, int64_t K);
  * workspace: device memory of at least w8a8_workspace_bytes(M, K) bytes,
  * 256-byte aligned; after the call it holds Xq [M, K] then x_scale [M]
  * (at offset round_up(M*K, 256)).
- * Errors: INVALID_ARG (workspace too small included), MISALIGNED, HIP.
+ * Every precondition of both steps (w8a8_gemm's included) is checked before
+ * the first launch.
+ * Errors: INVALID_ARG (shape as for w8a8_gemm, a null pointer, workspace too
+ *         small), UNSUPPORTED (M > 65535 * 128), MISALIGNED (X, Wq,
+ *         smooth_s; the workspace must be 256-byte aligned), HIP.
  * -------------------------------------------------------------------------- */
 Q4_API q4_status w8a8_linear(const void *X, int64_t M, int64_t N, int64_t K,
                              const int8_t *Wq, const float *w_scale,
@@ -320,7 +329,9 @@ Q4_API q4_status fp8_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t
  * workspace, then fp8_gemm; the workspace is sized and laid out as for
  * w8a8_linear (w8a8_workspace_bytes(M, K) bytes, 256-byte aligned: E4M3 codes
  * [M, K], then x_scale [M] at offset round_up(M*K, 256)). smooth_s as for
- * w8a8_linear. Errors: as for fp8_gemm, plus a too small workspace.
+ * w8a8_linear. Every precondition of both steps is checked before the
+ * first launch. Errors: as for fp8_gemm, plus a too small or misaligned
+ * workspace and a misaligned X or smooth_s.
  * -------------------------------------------------------------------------- */
 Q4_API q4_status fp8_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *Wq,
                             const float *w_scale, const float *smooth_s, void *Y,
@@ -371,7 +382,9 @@ Q4_API q4_status mxfp4_gemm(const uint8_t *Xq, const float *x_scale, const uint8
  * mxfp4_linear -- fp8_quantize_act of X (with /smooth_s fused in) into the
  * workspace (laid out as for w8a8_linear, w8a8_workspace_bytes(M, K) bytes,
  * 256-byte aligned), then mxfp4_gemm. smooth_s as for w8a8_linear.
- * Errors: as for mxfp4_gemm, plus a too small workspace.
+ * Every precondition of both steps is checked before the first launch.
+ * Errors: as for mxfp4_gemm, plus a too small or misaligned workspace and a
+ * misaligned X or smooth_s.
  * -------------------------------------------------------------------------- */
 Q4_API q4_status mxfp4_linear(const void *X, int64_t M, int64_t N, int64_t K,
                               const uint8_t *codes, const uint8_t *scales,

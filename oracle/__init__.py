@@ -41,9 +41,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    # ORACLE_LIB names another build of oracle.c (the sanitizer build the
+    # test suite runs the oracle's pins against)
+    path = os.environ.get("ORACLE_LIB") or _LIB_PATH
+    if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
         _build.build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     sig = {
         "orc_h2f": (ctypes.c_float, [ctypes.c_uint16]),
         "orc_f2h": (ctypes.c_uint16, [ctypes.c_float]),

@@ -103,6 +103,12 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+def _empty(shape, dtype, device):
+    """Every buffer this binding allocates for the caller (outputs,
+    workspaces) comes from here."""
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _check(status: int):
     if status != Q4_OK:
         raise Q4Error(status, lib().q4_last_error().decode())
@@ -140,11 +146,26 @@ def q4_quantize_pack(W: torch.Tensor, g: int = 128, sym: bool = False, out=None)
     N, K = W.shape
     G = K // g if g > 0 else 0
     if out is None:
-        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
-        scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
-        zeros = None if sym else torch.empty((N, (G + 1) // 2), dtype=torch.uint8, device=W.device)
+        codes = _empty((N, K // 2), dtype=torch.uint8, device=W.device)
+        scales = _empty((N, G), dtype=torch.float16, device=W.device)
+        zeros = None if sym else _empty((N, (G + 1) // 2), dtype=torch.uint8, device=W.device)
     else:
         codes, scales, zeros = out
+        # the kernel writes whole rows of each: every buffer must be exactly the
+        # packed shape, on W's device, contiguous
+        _need(codes, torch.uint8, "codes", 2)
+        _need(scales, torch.float16, "scales", 2)
+        want = {"codes": (codes, (N, K // 2)), "scales": (scales, (N, G))}
+        if zeros is not None:
+            _need(zeros, torch.uint8, "zeros", 2)
+            want["zeros"] = (zeros, (N, (G + 1) // 2))
+        elif not sym:
+            raise ValueError("zeros must be given when sym is False")
+        for name, (t, shape) in want.items():
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} {tuple(t.shape)} does not match {shape} for W {tuple(W.shape)}, g={g}")
+            if t.device != W.device:
+                raise ValueError(f"{name} is on {t.device}, W on {W.device}")
     _check(lib().q4_quantize_pack(_ptr(W), N, K, g, int(bool(sym)), _ptr(codes), _ptr(scales),
                                   _ptr(zeros), _stream(W)))
     return codes, scales, zeros
@@ -180,10 +201,12 @@ def _check_packed(codes, scales, zeros, K: int, g: int, what: str = "") -> int:
 
 def _output(out, M: int, N: int, device):
     if out is None:
-        return torch.empty((M, N), dtype=torch.float16, device=device)
+        return _empty((M, N), dtype=torch.float16, device=device)
     _need(out, torch.float16, "out", 2)
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out {tuple(out.shape)} does not match [M, N]=[{M}, {N}]")
+    if out.device != torch.device(device):
+        raise ValueError(f"out is on {out.device}, the input on {device}")
     return out
 
 
@@ -252,7 +275,7 @@ def w4a16_linear_awq(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
     N = _check_packed(codes, scales, zeros, K, g)
     _need_awq(awq_s, K)
     if workspace is None:
-        workspace = torch.empty((max(w4a16_awq_workspace_bytes(M, K), 1),), dtype=torch.uint8,
+        workspace = _empty((max(w4a16_awq_workspace_bytes(M, K), 1),), dtype=torch.uint8,
                                 device=X.device)
     _need(workspace, torch.uint8, "workspace", 1)
     Y = _output(out, M, N, X.device)
@@ -271,13 +294,15 @@ def _need_smooth(smooth_s, K: int):
 
 def _row_outputs(out, rows: int, K: int, code_dtype, device):
     if out is None:
-        return (torch.empty((rows, K), dtype=code_dtype, device=device),
-                torch.empty((rows,), dtype=torch.float32, device=device))
+        return (_empty((rows, K), dtype=code_dtype, device=device),
+                _empty((rows,), dtype=torch.float32, device=device))
     q, sc = out
     _need(q, code_dtype, "codes", 2)
     _need(sc, torch.float32, "scale", 1)
     if tuple(q.shape) != (rows, K) or sc.numel() != rows:
         raise ValueError("out tensors do not match the input's shape")
+    if q.device != torch.device(device) or sc.device != torch.device(device):
+        raise ValueError("out tensors must be on the input's device")
     return q, sc
 
 
@@ -286,8 +311,8 @@ def q8_quantize_weight(W: torch.Tensor, smooth_s: torch.Tensor | None = None):
     _need(W, torch.float16, "W", 2)
     N, K = W.shape
     _need_smooth(smooth_s, K)
-    Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
-    sw = torch.empty((N,), dtype=torch.float32, device=W.device)
+    Wq = _empty((N, K), dtype=torch.int8, device=W.device)
+    sw = _empty((N,), dtype=torch.float32, device=W.device)
     _check(lib().q8_quantize_weight(_ptr(W), _ptr(smooth_s), N, K, _ptr(Wq), _ptr(sw), _stream(W)))
     return Wq, sw
 
@@ -330,7 +355,7 @@ def w8a8_workspace_bytes(M: int, K: int) -> int:
 
 def w8a8_workspace(M: int, K: int, device) -> torch.Tensor:
     """A workspace tensor for w8a8_linear (torch's allocations are 256-byte aligned)."""
-    return torch.empty((max(1, w8a8_workspace_bytes(M, K)),), dtype=torch.uint8, device=device)
+    return _empty((max(1, w8a8_workspace_bytes(M, K)),), dtype=torch.uint8, device=device)
 
 
 def w8a8_linear(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
@@ -367,7 +392,7 @@ def smoothquant_scales(Xcal: torch.Tensor, W: torch.Tensor, alpha: float = 0.5):
     N = W.shape[0]
     if W.shape[1] != K:
         raise ValueError("smoothquant_scales: Xcal and W must share K")
-    s = torch.empty((K,), dtype=torch.float32, device=W.device)
+    s = _empty((K,), dtype=torch.float32, device=W.device)
     _check(lib().smoothquant_scales(_ptr(Xcal), R, _ptr(W), N, K, ctypes.c_float(alpha), _ptr(s),
                                     _stream(W)))
     return s
@@ -440,8 +465,8 @@ def mxfp4_quantize_weight(W: torch.Tensor, smooth_s: torch.Tensor | None = None)
     _need(W, torch.float16, "W", 2)
     N, K = W.shape
     _need_smooth(smooth_s, K)
-    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
-    scales = torch.empty((N, K // 32), dtype=torch.uint8, device=W.device)
+    codes = _empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scales = _empty((N, K // 32), dtype=torch.uint8, device=W.device)
     _check(lib().mxfp4_quantize_weight(_ptr(W), _ptr(smooth_s), N, K, _ptr(codes), _ptr(scales),
                                        _stream(W)))
     return codes, scales
@@ -502,8 +527,8 @@ def nf4_quantize(W: torch.Tensor):
     """NF4 of W fp16 [N, K]: (codes uint8 [N, K/2], scales fp32 [N, K/64])."""
     _need(W, torch.float16, "W", 2)
     N, K = W.shape
-    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
-    scales = torch.empty((N, max(K // 64, 0)), dtype=torch.float32, device=W.device)
+    codes = _empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scales = _empty((N, max(K // 64, 0)), dtype=torch.float32, device=W.device)
     _check(lib().nf4_quantize(_ptr(W), N, K, _ptr(codes), _ptr(scales), _stream(W)))
     return codes, scales
 

@@ -82,8 +82,8 @@ Q4_API q4_status w4a16_linear(const void *X, int64_t M, int64_t N, int64_t K, in
                (long long)N, (long long)K);
     Q4_REQUIRE(g > 0 && K % g == 0 && K % 2 == 0, Q4_ERR_INVALID_ARG,
                "w4a16_linear: K=%lld must be even and a multiple of g=%d", (long long)K, g);
-    Q4_REQUIRE(g % 128 == 0, Q4_ERR_UNSUPPORTED,
-               "w4a16_linear: group size %d unsupported (must be a multiple of 128)", g);
+    Q4_REQUIRE(g % 32 == 0, Q4_ERR_UNSUPPORTED,
+               "w4a16_linear: group size %d unsupported (must be a multiple of 32)", g);
     Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "w4a16_linear: M=%lld too large",
                (long long)M);
     if (M == 0 || N == 0) return ok();
@@ -106,8 +106,8 @@ Q4_API q4_status w4a16_linear_multi(const void *X, int64_t M, int64_t K, int32_t
                "w4a16_linear_multi: bad shape M=%lld K=%lld", (long long)M, (long long)K);
     Q4_REQUIRE(g > 0 && K % g == 0 && K % 2 == 0, Q4_ERR_INVALID_ARG,
                "w4a16_linear_multi: K=%lld must be even and a multiple of g=%d", (long long)K, g);
-    Q4_REQUIRE(g % 128 == 0, Q4_ERR_UNSUPPORTED,
-               "w4a16_linear_multi: group size %d unsupported (must be a multiple of 128)", g);
+    Q4_REQUIRE(g % 32 == 0, Q4_ERR_UNSUPPORTED,
+               "w4a16_linear_multi: group size %d unsupported (must be a multiple of 32)", g);
     Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "w4a16_linear_multi: M=%lld too large",
                (long long)M);
     for (int i = 0; i < count; i++) {
@@ -186,8 +186,8 @@ Q4_API q4_status w4a16_linear_awq(const void *X, int64_t M, int64_t N, int64_t K
                (long long)N, (long long)K);
     Q4_REQUIRE(g > 0 && K % g == 0 && K % 2 == 0, Q4_ERR_INVALID_ARG,
                "w4a16_linear_awq: K=%lld must be even and a multiple of g=%d", (long long)K, g);
-    Q4_REQUIRE(g % 128 == 0, Q4_ERR_UNSUPPORTED,
-               "w4a16_linear_awq: group size %d unsupported (must be a multiple of 128)", g);
+    Q4_REQUIRE(g % 32 == 0, Q4_ERR_UNSUPPORTED,
+               "w4a16_linear_awq: group size %d unsupported (must be a multiple of 32)", g);
     Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "w4a16_linear_awq: M=%lld too large",
                (long long)M);
     if (M == 0 || N == 0) return ok();
@@ -242,22 +242,32 @@ Q4_API q4_status q8_quantize_act(const void *X, const float *smooth_s, int64_t M
     return from_hip(e, "q8_quantize_act");
 }
 
+// Preconditions of the INT8 GEMM, checked before anything is launched (also
+// by w8a8_linear, ahead of its activation quantizer).
+static q4_status check_w8a8_gemm(const char *what, const void *Xq, const float *x_scale,
+                                 const int8_t *Wq, const float *w_scale, int64_t M, int64_t N,
+                                 int64_t K, const void *Y)
+{
+    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K % 16 == 0,
+               Q4_ERR_INVALID_ARG,
+               "%s: bad shape M=%lld N=%lld K=%lld (K must be a positive multiple of 16)", what,
+               (long long)M, (long long)N, (long long)K);
+    Q4_REQUIRE(K <= 133143, Q4_ERR_INVALID_ARG,
+               "%s: K=%lld could overflow the int32 accumulator (max 133143)", what, (long long)K);
+    Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "%s: M=%lld too large", what, (long long)M);
+    if (M == 0 || N == 0) return ok();
+    Q4_REQUIRE(Xq && x_scale && Wq && w_scale && Y, Q4_ERR_INVALID_ARG, "%s: null pointer", what);
+    Q4_REQUIRE(aligned16(Xq) && aligned16(Wq), Q4_ERR_MISALIGNED,
+               "%s: Xq (or the workspace) and Wq must be 16-byte aligned", what);
+    return ok();
+}
+
 Q4_API q4_status w8a8_gemm(const int8_t *Xq, const float *x_scale, const int8_t *Wq,
                            const float *w_scale, int64_t M, int64_t N, int64_t K, void *Y,
                            int32_t *acc_out, void *stream)
 {
-    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K % 16 == 0,
-               Q4_ERR_INVALID_ARG,
-               "w8a8_gemm: bad shape M=%lld N=%lld K=%lld (K must be a positive multiple of 16)",
-               (long long)M, (long long)N, (long long)K);
-    Q4_REQUIRE(K <= 133143, Q4_ERR_INVALID_ARG,
-               "w8a8_gemm: K=%lld could overflow the int32 accumulator (max 133143)", (long long)K);
-    Q4_REQUIRE(M <= 65535LL * 128, Q4_ERR_UNSUPPORTED, "w8a8_gemm: M=%lld too large",
-               (long long)M);
-    if (M == 0 || N == 0) return ok();
-    Q4_REQUIRE(Xq && x_scale && Wq && w_scale && Y, Q4_ERR_INVALID_ARG, "w8a8_gemm: null pointer");
-    Q4_REQUIRE(aligned16(Xq) && aligned16(Wq), Q4_ERR_MISALIGNED,
-               "w8a8_gemm: Xq and Wq must be 16-byte aligned");
+    const q4_status st = check_w8a8_gemm("w8a8_gemm", Xq, x_scale, Wq, w_scale, M, N, K, Y);
+    if (st != Q4_OK || M == 0 || N == 0) return st;
     hipError_t e = q4k::launch_w8a8_gemm(Xq, x_scale, Wq, w_scale, M, N, K,
                                          static_cast<uint16_t *>(Y), acc_out,
                                          static_cast<hipStream_t>(stream));
@@ -271,29 +281,52 @@ Q4_API size_t w8a8_workspace_bytes(int64_t M, int64_t K)
     return codes + (size_t)M * sizeof(float);
 }
 
+// The per-token quantizer's own preconditions (besides the shape): X, Xq
+// and smooth_s 16-byte aligned.
+static q4_status check_act_quant(const char *what, const void *X, const float *smooth_s)
+{
+    Q4_REQUIRE(X, Q4_ERR_INVALID_ARG, "%s: null pointer", what);
+    Q4_REQUIRE(aligned16(X) && (!smooth_s || aligned16(smooth_s)), Q4_ERR_MISALIGNED,
+               "%s: X and smooth_s must be 16-byte aligned", what);
+    return ok();
+}
+
+// Where the codes and the per-token scales sit in a *_linear workspace.
+static char *workspace_scales(void *workspace, int64_t M, int64_t K)
+{
+    return static_cast<char *>(workspace) + ((size_t)M * (size_t)K + 255) / 256 * 256;
+}
+
+static q4_status check_workspace(const char *what, const void *workspace, size_t workspace_bytes,
+                                 int64_t M, int64_t K)
+{
+    Q4_REQUIRE(workspace, Q4_ERR_INVALID_ARG, "%s: null workspace", what);
+    Q4_REQUIRE(workspace_bytes >= w8a8_workspace_bytes(M, K), Q4_ERR_INVALID_ARG,
+               "%s: workspace of %zu bytes is smaller than the %zu needed", what, workspace_bytes,
+               w8a8_workspace_bytes(M, K));
+    Q4_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, Q4_ERR_MISALIGNED,
+               "%s: workspace must be 256-byte aligned", what);
+    return ok();
+}
+
 Q4_API q4_status w8a8_linear(const void *X, int64_t M, int64_t N, int64_t K, const int8_t *Wq,
                              const float *w_scale, const float *smooth_s, void *Y, void *workspace,
                              size_t workspace_bytes, int32_t *acc_out, void *stream)
 {
-    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K % 16 == 0 &&
-                   K <= 133143,
-               Q4_ERR_INVALID_ARG,
-               "w8a8_linear: bad shape M=%lld N=%lld K=%lld (K a multiple of 16, <= 133143)",
-               (long long)M, (long long)N, (long long)K);
-    if (M == 0 || N == 0) return ok();
-    Q4_REQUIRE(X && Wq && w_scale && Y && workspace, Q4_ERR_INVALID_ARG,
-               "w8a8_linear: null pointer");
-    Q4_REQUIRE(workspace_bytes >= w8a8_workspace_bytes(M, K), Q4_ERR_INVALID_ARG,
-               "w8a8_linear: workspace of %zu bytes is smaller than the %zu needed",
-               workspace_bytes, w8a8_workspace_bytes(M, K));
-    Q4_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, Q4_ERR_MISALIGNED,
-               "w8a8_linear: workspace must be 256-byte aligned");
+    // every precondition of both launches first (the workspace stands in for
+    // the codes and scales it will hold): on an error nothing runs
+    q4_status st = check_w8a8_gemm("w8a8_linear", X, static_cast<const float *>(workspace), Wq, w_scale,
+                                   M, N, K, Y);
+    if (st != Q4_OK || M == 0 || N == 0) return st;
+    if ((st = check_act_quant("w8a8_linear", X, smooth_s)) != Q4_OK) return st;
+    if ((st = check_workspace("w8a8_linear", workspace, workspace_bytes, M, K)) != Q4_OK) return st;
     int8_t *xq = static_cast<int8_t *>(workspace);
-    float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                          ((size_t)M * (size_t)K + 255) / 256 * 256);
-    q4_status st = q8_quantize_act(X, smooth_s, M, K, xq, sx, stream);
-    if (st != Q4_OK) return st;
-    return w8a8_gemm(xq, sx, Wq, w_scale, M, N, K, Y, acc_out, stream);
+    float *sx = reinterpret_cast<float *>(workspace_scales(workspace, M, K));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = q4k::launch_q8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
+    if (e == hipSuccess)
+        e = q4k::launch_w8a8_gemm(xq, sx, Wq, w_scale, M, N, K, static_cast<uint16_t *>(Y), acc_out, hs);
+    return from_hip(e, "w8a8_linear");
 }
 
 Q4_API q4_status fp8_quantize_weight(const void *W, const float *smooth_s, int64_t N, int64_t K,
@@ -326,22 +359,33 @@ Q4_API q4_status fp8_quantize_act(const void *X, const float *smooth_s, int64_t 
     return from_hip(e, "fp8_quantize_act");
 }
 
+// Preconditions of the E4M3 and MXFP4 GEMMs (Xq the E4M3 activation codes,
+// Wq the E4M3 weight codes or the MXFP4 codes, ws the weight's scales).
+static q4_status check_f8_gemm(const char *what, const void *Xq, const float *x_scale,
+                               const uint8_t *Wq, const void *ws, int64_t M, int64_t N, int64_t K,
+                               const void *Y)
+{
+    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= 8192,
+               Q4_ERR_INVALID_ARG, "%s: bad shape M=%lld N=%lld K=%lld (K <= 8192)", what,
+               (long long)M, (long long)N, (long long)K);
+    Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "%s: K=%lld must be a multiple of 128", what,
+               (long long)K);
+    Q4_REQUIRE(M * K < (1LL << 31) && N * K < (1LL << 31), Q4_ERR_UNSUPPORTED,
+               "%s: M*K and N*K must stay below 2^31 (M=%lld N=%lld K=%lld)", what, (long long)M,
+               (long long)N, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    Q4_REQUIRE(Xq && x_scale && Wq && ws && Y, Q4_ERR_INVALID_ARG, "%s: null pointer", what);
+    Q4_REQUIRE(aligned16(Xq) && aligned16(Wq), Q4_ERR_MISALIGNED,
+               "%s: Xq (or the workspace) and the weight codes must be 16-byte aligned", what);
+    return ok();
+}
+
 Q4_API q4_status fp8_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t *Wq,
                           const float *w_scale, int64_t M, int64_t N, int64_t K, void *Y,
                           void *stream)
 {
-    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= 8192,
-               Q4_ERR_INVALID_ARG, "fp8_gemm: bad shape M=%lld N=%lld K=%lld (K <= 8192)",
-               (long long)M, (long long)N, (long long)K);
-    Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "fp8_gemm: K=%lld must be a multiple of 128",
-               (long long)K);
-    Q4_REQUIRE(M * K < (1LL << 31) && N * K < (1LL << 31), Q4_ERR_UNSUPPORTED,
-               "fp8_gemm: M*K and N*K must stay below 2^31 (M=%lld N=%lld K=%lld)", (long long)M,
-               (long long)N, (long long)K);
-    if (M == 0 || N == 0) return ok();
-    Q4_REQUIRE(Xq && x_scale && Wq && w_scale && Y, Q4_ERR_INVALID_ARG, "fp8_gemm: null pointer");
-    Q4_REQUIRE(aligned16(Xq) && aligned16(Wq), Q4_ERR_MISALIGNED,
-               "fp8_gemm: Xq and Wq must be 16-byte aligned");
+    const q4_status st = check_f8_gemm("fp8_gemm", Xq, x_scale, Wq, w_scale, M, N, K, Y);
+    if (st != Q4_OK || M == 0 || N == 0) return st;
     hipError_t e = q4k::launch_fp8_gemm(Xq, x_scale, Wq, w_scale, M, N, K,
                                         static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
     return from_hip(e, "fp8_gemm");
@@ -351,24 +395,18 @@ Q4_API q4_status fp8_linear(const void *X, int64_t M, int64_t N, int64_t K, cons
                             const float *w_scale, const float *smooth_s, void *Y, void *workspace,
                             size_t workspace_bytes, void *stream)
 {
-    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= 8192,
-               Q4_ERR_INVALID_ARG, "fp8_linear: bad shape M=%lld N=%lld K=%lld (K <= 8192)",
-               (long long)M, (long long)N, (long long)K);
-    Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "fp8_linear: K=%lld must be a multiple of 128",
-               (long long)K);
-    if (M == 0 || N == 0) return ok();
-    Q4_REQUIRE(X && Wq && w_scale && Y && workspace, Q4_ERR_INVALID_ARG, "fp8_linear: null pointer");
-    Q4_REQUIRE(workspace_bytes >= w8a8_workspace_bytes(M, K), Q4_ERR_INVALID_ARG,
-               "fp8_linear: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
-               w8a8_workspace_bytes(M, K));
-    Q4_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, Q4_ERR_MISALIGNED,
-               "fp8_linear: workspace must be 256-byte aligned");
+    q4_status st = check_f8_gemm("fp8_linear", X, static_cast<const float *>(workspace), Wq, w_scale, M,
+                                 N, K, Y);
+    if (st != Q4_OK || M == 0 || N == 0) return st;
+    if ((st = check_act_quant("fp8_linear", X, smooth_s)) != Q4_OK) return st;
+    if ((st = check_workspace("fp8_linear", workspace, workspace_bytes, M, K)) != Q4_OK) return st;
     uint8_t *xq = static_cast<uint8_t *>(workspace);
-    float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                          ((size_t)M * (size_t)K + 255) / 256 * 256);
-    q4_status st = fp8_quantize_act(X, smooth_s, M, K, xq, sx, stream);
-    if (st != Q4_OK) return st;
-    return fp8_gemm(xq, sx, Wq, w_scale, M, N, K, Y, stream);
+    float *sx = reinterpret_cast<float *>(workspace_scales(workspace, M, K));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = q4k::launch_fp8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
+    if (e == hipSuccess)
+        e = q4k::launch_fp8_gemm(xq, sx, Wq, w_scale, M, N, K, static_cast<uint16_t *>(Y), hs);
+    return from_hip(e, "fp8_linear");
 }
 
 Q4_API q4_status mxfp4_quantize_weight(const void *W, const float *smooth_s, int64_t N, int64_t K,
@@ -392,18 +430,8 @@ Q4_API q4_status mxfp4_gemm(const uint8_t *Xq, const float *x_scale, const uint8
                             const uint8_t *scales, int64_t M, int64_t N, int64_t K, void *Y,
                             void *stream)
 {
-    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= 8192,
-               Q4_ERR_INVALID_ARG, "mxfp4_gemm: bad shape M=%lld N=%lld K=%lld (K <= 8192)",
-               (long long)M, (long long)N, (long long)K);
-    Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "mxfp4_gemm: K=%lld must be a multiple of 128",
-               (long long)K);
-    Q4_REQUIRE(M * K < (1LL << 31) && N * K < (1LL << 31), Q4_ERR_UNSUPPORTED,
-               "mxfp4_gemm: M*K and N*K must stay below 2^31 (M=%lld N=%lld K=%lld)", (long long)M,
-               (long long)N, (long long)K);
-    if (M == 0 || N == 0) return ok();
-    Q4_REQUIRE(Xq && x_scale && codes && scales && Y, Q4_ERR_INVALID_ARG, "mxfp4_gemm: null pointer");
-    Q4_REQUIRE(aligned16(Xq) && aligned16(codes), Q4_ERR_MISALIGNED,
-               "mxfp4_gemm: Xq and codes must be 16-byte aligned");
+    const q4_status st = check_f8_gemm("mxfp4_gemm", Xq, x_scale, codes, scales, M, N, K, Y);
+    if (st != Q4_OK || M == 0 || N == 0) return st;
     hipError_t e = q4k::launch_mxfp4_gemm(Xq, x_scale, codes, scales, M, N, K,
                                           static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
     return from_hip(e, "mxfp4_gemm");
@@ -413,25 +441,18 @@ Q4_API q4_status mxfp4_linear(const void *X, int64_t M, int64_t N, int64_t K, co
                               const uint8_t *scales, const float *smooth_s, void *Y, void *workspace,
                               size_t workspace_bytes, void *stream)
 {
-    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= 8192,
-               Q4_ERR_INVALID_ARG, "mxfp4_linear: bad shape M=%lld N=%lld K=%lld (K <= 8192)",
-               (long long)M, (long long)N, (long long)K);
-    Q4_REQUIRE(K % 128 == 0, Q4_ERR_UNSUPPORTED, "mxfp4_linear: K=%lld must be a multiple of 128",
-               (long long)K);
-    if (M == 0 || N == 0) return ok();
-    Q4_REQUIRE(X && codes && scales && Y && workspace, Q4_ERR_INVALID_ARG,
-               "mxfp4_linear: null pointer");
-    Q4_REQUIRE(workspace_bytes >= w8a8_workspace_bytes(M, K), Q4_ERR_INVALID_ARG,
-               "mxfp4_linear: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
-               w8a8_workspace_bytes(M, K));
-    Q4_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, Q4_ERR_MISALIGNED,
-               "mxfp4_linear: workspace must be 256-byte aligned");
+    q4_status st = check_f8_gemm("mxfp4_linear", X, static_cast<const float *>(workspace), codes,
+                                 scales, M, N, K, Y);
+    if (st != Q4_OK || M == 0 || N == 0) return st;
+    if ((st = check_act_quant("mxfp4_linear", X, smooth_s)) != Q4_OK) return st;
+    if ((st = check_workspace("mxfp4_linear", workspace, workspace_bytes, M, K)) != Q4_OK) return st;
     uint8_t *xq = static_cast<uint8_t *>(workspace);
-    float *sx = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                          ((size_t)M * (size_t)K + 255) / 256 * 256);
-    q4_status st = fp8_quantize_act(X, smooth_s, M, K, xq, sx, stream);
-    if (st != Q4_OK) return st;
-    return mxfp4_gemm(xq, sx, codes, scales, M, N, K, Y, stream);
+    float *sx = reinterpret_cast<float *>(workspace_scales(workspace, M, K));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = q4k::launch_fp8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
+    if (e == hipSuccess)
+        e = q4k::launch_mxfp4_gemm(xq, sx, codes, scales, M, N, K, static_cast<uint16_t *>(Y), hs);
+    return from_hip(e, "mxfp4_linear");
 }
 
 Q4_API void nf4_levels(uint16_t *out)

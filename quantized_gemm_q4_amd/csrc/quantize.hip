@@ -342,10 +342,12 @@ __global__ __launch_bounds__(kThreads) void q8_rows_generic_kernel(const uint16_
 
 // Quotients without a division. For binary32 (or binary16-valued) a and a
 // binary32 b the exact quotient a / b never lies on the midpoint between two
-// binary32 neighbours, and when it does not it is at least 2^-47 (relative)
-// away from one: a - m b, for a midpoint m, is a multiple of a power of two
-// that is at least 2^-48 of a. So a product a * r in fp64 with r within
-// 2^-50 of 1 / b (relative) rounds to the same binary32 value as a / b:
+// binary32 neighbours, and when it does not it is at least 2^-49 (relative)
+// away from one: with a = A 2^ea (A < 2^24) and a midpoint m (25 significant
+// bits), a - m b is a nonzero multiple of 2^(ea - 25), so at least 2^-49 of
+// a. So a product a * r in fp64 with r within 2^-50 of 1 / b (relative; the
+// fp64 rounding of the product adds 2^-53) rounds to the same binary32 value
+// as a / b:
 // fl32(fl64(a * r)) = fl32(a / b). r is the hardware's fp64 reciprocal
 // refined by two Newton steps (each squares the relative error; rounding
 // keeps it near 2^-53). b must be finite and nonzero.

@@ -155,6 +155,104 @@ __global__ __launch_bounds__(kThreads) void w4a16_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Small-group kernel: any g that is a multiple of 32 (the quantizer writes
+// g = 32 and 64; Core ideas, ai-infra.cypggs.com, §2.3 granularity table),
+// K a multiple of g, any M. Work advances in 32-wide k steps; a step never
+// straddles two groups, so its MFMA sums one group only and the group's
+// scale multiplies the step's exact fp32 partial sum, as in the kernels
+// above. Lane (r16, q) takes k = 32 s + 8 q .. + 7 of step s for both
+// operands: one code dword (eight nibbles) and 16 bytes of X. A block owns
+// NT * 16 output channels and 16 MT rows of Y (grid.y walks the rows); its
+// 4 wavefronts split the steps and meet in LDS for the final sum.
+template <int MT, int NT, int PF>
+__global__ __launch_bounds__(kThreads) void w4a16_subg_kernel(
+    const uint16_t *__restrict__ X, int M, int N, int K, int g, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    uint16_t *__restrict__ Y)
+{
+    __shared__ float red[4][MT * NT * 4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int S = K >> 5;                                       // 32-wide steps
+    const int s_begin = (S * wave) >> 2, s_end = (S * (wave + 1)) >> 2;
+    const int n_base = blockIdx.x * (NT * 16), m_base = blockIdx.y * (MT * 16);
+    const int G = K / g, Gz = (G + 1) >> 1, spg = g >> 5;      // steps per group
+    const int64_t row_bytes = K >> 1;
+
+    int64_t nrow[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+        const int n = n_base + nt * 16 + r16;
+        nrow[nt] = n < N ? n : N - 1;
+    }
+    const uint16_t *xrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+        const int m = m_base + mt * 16 + r16;
+        xrow[mt] = X + (int64_t)(m < M ? m : M - 1) * K + q * 8;   // rows past M repeat M - 1
+    }
+
+    floatx4 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (int s0 = s_begin; s0 < s_end; s0 += PF) {
+        uint32_t cw[PF][NT];
+        float sc[PF][NT];
+        ZeroConst zb[PF][NT];
+#pragma unroll
+        for (int p = 0; p < PF; p++) {
+            const int s = s0 + p < s_end ? s0 + p : s_end - 1;   // past the end: reloaded, unused
+            const int grp = s / spg;
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++) {
+                cw[p][nt] = *reinterpret_cast<const uint32_t *>(codes + nrow[nt] * row_bytes + s * 16 + q * 4);
+                sc[p][nt] = scale16(scales[nrow[nt] * G + grp]);
+                zb[p][nt] = zero_const(group_zp(zeros, nrow[nt], Gz, grp));
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PF; p++) {
+            const int s = s0 + p;
+            if (s >= s_end) break;
+            half8 a[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+                a[mt] = __builtin_bit_cast(half8, permute_x(*reinterpret_cast<const u32x4 *>(xrow[mt] + s * 32)));
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++) {
+                const half8 b = dequant8(cw[p][nt], zb[p][nt]);
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++) {
+                    const floatx4 part = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        a[mt], b, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) acc[mt][nt][r] = fmaf(part[r], sc[p][nt], acc[mt][nt][r]);
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) red[wave][(mt * NT + nt) * 4 + r][lane] = acc[mt][nt][r];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < MT * NT * 4 * 64; idx += kThreads) {
+        const int reg = idx >> 6, l = idx & 63;
+        const float v = red[0][reg][l] + red[1][reg][l] + red[2][reg][l] + red[3][reg][l];
+        const int mt = reg / (NT * 4), nt = (reg >> 2) % NT, r = reg & 3;
+        const int m = m_base + mt * 16 + 4 * (l >> 4) + r;
+        const int n = n_base + nt * 16 + (l & 15);
+        if (m < M && n < N) Y[(int64_t)m * N + n] = f2h(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Prefill kernel, M > 64. Compute bound. A 256-thread block computes a
 // 128 x 128 tile of Y; its 4 wavefronts form a 2 x 2 grid of 64 x 64
 // sub-tiles (4 x 4 MFMA tiles each). Per 128-wide k-block: the X tile and the
@@ -955,6 +1053,32 @@ hipError_t launch_skinny(const uint16_t *X, int M, int N, int K, int g, const ui
     return hipGetLastError();
 }
 
+// Group sizes that are not a multiple of 128: the small-group kernel, over
+// chunks of at most 65535 block rows.
+template <int MT, int NT, int PF>
+hipError_t launch_subg_tiles(const uint16_t *X, int64_t M, int N, int K, int g, const uint8_t *codes,
+                             const uint16_t *scales, const uint8_t *zeros, uint16_t *Y, hipStream_t st)
+{
+    constexpr int64_t kRows = 65535LL * MT * 16;
+    for (int64_t m0 = 0; m0 < M; m0 += kRows) {
+        const int rows = (int)(M - m0 < kRows ? M - m0 : kRows);
+        const dim3 grid((unsigned)((N + NT * 16 - 1) / (NT * 16)), (unsigned)((rows + MT * 16 - 1) / (MT * 16)));
+        w4a16_subg_kernel<MT, NT, PF><<<grid, kThreads, 0, st>>>(X + m0 * K, rows, N, K, g, codes, scales,
+                                                                  zeros, Y + m0 * N);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_subg(const uint16_t *X, int64_t M, int N, int K, int g, const uint8_t *codes,
+                       const uint16_t *scales, const uint8_t *zeros, uint16_t *Y, hipStream_t st)
+{
+    if (M <= 16) return launch_subg_tiles<1, 1, 8>(X, M, N, K, g, codes, scales, zeros, Y, st);
+    if (M <= 32) return launch_subg_tiles<2, 2, 4>(X, M, N, K, g, codes, scales, zeros, Y, st);
+    return launch_subg_tiles<4, 2, 4>(X, M, N, K, g, codes, scales, zeros, Y, st);
+}
+
 // Batched decode launcher (g = 128 assumed). K is split over KS groups of
 // wavefronts inside a block; each group's k-blocks must be a multiple of the
 // ring depth.
@@ -1043,8 +1167,8 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
         const hipError_t e = launch_w4a16_gemv(X, M, N, K, g, codes, scales, zeros, Y, st);
         if (e != hipErrorNotSupported) return e;
     }
-    if (M >= 256 && g % 128 == 0 && (g & (g - 1)) == 0 && M * K * 2 < ((int64_t)1 << 31) &&
-        N * (K / 2) < ((int64_t)1 << 31)) {
+    if (M >= 256 && g % 32 == 0 && (g & (g - 1)) == 0 && K % 128 == 0 &&
+        M * K * 2 < ((int64_t)1 << 31) && N * (K / 2) < ((int64_t)1 << 31)) {
         // Tile width 32 NU: one block per CU, so the time is about the number
         // of full-chip rounds of 256 tiles times (tile width + a fixed
         // per-tile cost of ~2 units for pipeline fill and the epilogue).
@@ -1070,6 +1194,7 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
         else asym ? launch(w4a16_gemm_kernel<11, 1, true>, 512) : launch(w4a16_gemm_kernel<11, 1, false>, 512);
         return hipGetLastError();
     }
+    if (g % 128 != 0) return launch_subg(X, M, n, k, g, codes, scales, zeros, Y, st);
     if (g == 128 && M <= 64) {
         const hipError_t e = launch_batched(X, m, n, k, codes, scales, zeros, Y, st);
         if (e != hipErrorNotSupported) return e;

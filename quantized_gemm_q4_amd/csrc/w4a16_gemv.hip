@@ -125,6 +125,12 @@ __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M
                 *reinterpret_cast<u32x4 *>(xs + kb0 * 64 + c * 4) =
                     permute_x(SM ? awq_div8(xw[i], asl[i], ash[i]) : xw[i]);
         }
+        // other lanes of this wavefront read what these lanes wrote: keep
+        // the compiler from moving any LDS access across this point (the
+        // hardware already runs one wavefront's LDS accesses in order)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
     } else {
         if ((int)threadIdx.x < xchunks) *reinterpret_cast<u32x4 *>(xs + threadIdx.x * 4) = permute_x(x0);
         for (int m = 0; m < M; m++) {

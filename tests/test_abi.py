@@ -76,7 +76,11 @@ def layers(*descs):
     (lambda L: L.q4_quantize_pack(None, 4, 512, 128, 1, FAKE, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.q4_quantize_pack(MISAL, 4, 512, 128, 1, FAKE, FAKE, None, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.q4_quantize_pack(FAKE, 0, 512, 128, 0, None, None, None, None), q4.Q4_OK),
-    (lambda L: L.w4a16_linear(FAKE, 1, 16, 512, 64, FAKE, FAKE, FAKE, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
+    # group sizes must be multiples of 32 (32, 64, 128, 256, 384, ... are served)
+    (lambda L: L.w4a16_linear(FAKE, 1, 16, 480, 80, FAKE, FAKE, FAKE, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.w4a16_linear(FAKE, 1, 16, 512, 0, FAKE, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w4a16_linear(FAKE, 65535 * 128 + 1, 16, 512, 128, FAKE, FAKE, FAKE, FAKE, None),
+     q4.Q4_ERR_UNSUPPORTED),
     (lambda L: L.w4a16_linear(FAKE, 1, 16, 500, 128, FAKE, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.w4a16_linear(MISAL, 1, 16, 512, 128, FAKE, FAKE, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.w4a16_linear(FAKE, 1, 16, 512, 128, MISAL, FAKE, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
@@ -86,7 +90,7 @@ def layers(*descs):
     (lambda L: L.w4a16_linear_multi(FAKE, 1, 512, 128, layers((FAKE, FAKE, FAKE, FAKE, 16)), 9, None),
      q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.w4a16_linear_multi(FAKE, 1, 512, 128, None, 1, None), q4.Q4_ERR_INVALID_ARG),
-    (lambda L: L.w4a16_linear_multi(FAKE, 1, 512, 64, layers((FAKE, FAKE, FAKE, FAKE, 16)), 1, None),
+    (lambda L: L.w4a16_linear_multi(FAKE, 1, 480, 80, layers((FAKE, FAKE, FAKE, FAKE, 16)), 1, None),
      q4.Q4_ERR_UNSUPPORTED),
     (lambda L: L.w4a16_linear_multi(FAKE, 1, 500, 128, layers((FAKE, FAKE, FAKE, FAKE, 16)), 1, None),
      q4.Q4_ERR_INVALID_ARG),
@@ -113,6 +117,14 @@ def layers(*descs):
     (lambda L: L.w8a8_gemm(MISAL, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, None, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.w8a8_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE, 100, None, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.w8a8_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE + 16, 4096, None, None), q4.Q4_ERR_MISALIGNED),
+    # the GEMM's own preconditions are checked before the activation quantizer
+    # would launch: a misaligned Wq, a too large M, a null w_scale
+    (lambda L: L.w8a8_linear(FAKE, 4, 4, 128, MISAL, FAKE, None, FAKE, FAKE, 4096, None, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.w8a8_linear(FAKE, 65535 * 128 + 1, 4, 128, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None, None),
+     q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.w8a8_linear(FAKE, 4, 4, 128, FAKE, None, None, FAKE, FAKE, 4096, None, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w8a8_linear(MISAL, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE, 4096, None, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.w8a8_linear(FAKE, 4, 4, 128, FAKE, FAKE, MISAL, FAKE, FAKE, 4096, None, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.fp8_quantize_weight(FAKE, None, 4, 100, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.fp8_quantize_weight(FAKE, MISAL, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.fp8_quantize_act(FAKE, None, 4, 128, MISAL, FAKE, None), q4.Q4_ERR_MISALIGNED),
@@ -128,6 +140,13 @@ def layers(*descs):
     (lambda L: L.fp8_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE, 100, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.fp8_linear(FAKE, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE + 16, 4096, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.fp8_linear(FAKE, 4, 4, 96, FAKE, FAKE, None, FAKE, FAKE, 4096, None), q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.fp8_linear(FAKE, 4, 4, 128, MISAL, FAKE, None, FAKE, FAKE, 4096, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.fp8_linear(FAKE, 1 << 18, 4, 8192, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None),
+     q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.mxfp4_linear(FAKE, 4, 4, 128, MISAL, FAKE, None, FAKE, FAKE, 4096, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.mxfp4_linear(FAKE, 4, 1 << 18, 8192, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None),
+     q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.mxfp4_linear(FAKE, 4, 4, 128, FAKE, None, None, FAKE, FAKE, 4096, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.mxfp4_quantize_weight(FAKE, None, 4, 48, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.mxfp4_quantize_weight(MISAL, None, 4, 64, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.mxfp4_quantize_weight(FAKE, None, 4, 64, FAKE + 2, FAKE, None), q4.Q4_ERR_MISALIGNED),
@@ -159,7 +178,7 @@ def layers(*descs):
      q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.w4a16_linear_awq(FAKE, 1, 16, 256, 128, FAKE, FAKE, None, FAKE, FAKE, None, 512, None),
      q4.Q4_ERR_INVALID_ARG),
-    (lambda L: L.w4a16_linear_awq(FAKE, 1, 16, 256, 64, FAKE, FAKE, None, FAKE, FAKE, FAKE, 512, None),
+    (lambda L: L.w4a16_linear_awq(FAKE, 1, 16, 480, 80, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1024, None),
      q4.Q4_ERR_UNSUPPORTED),
     (lambda L: L.w4a16_linear_awq(FAKE, 1, 16, 256, 128, FAKE, FAKE, None, MISAL, FAKE, FAKE, 512, None),
      q4.Q4_ERR_MISALIGNED),

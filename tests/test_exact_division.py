@@ -3,8 +3,10 @@ host with numpy (no GPU code involved).
 
 For a binary16-valued (or binary32) numerator a and a binary32 divisor b, the
 exact quotient a / b never lies on a midpoint between two binary32 neighbours
-and otherwise stays at least about 2^-47 (relative) away from one, so a fp64
-product with a reciprocal of b accurate to ~2^-50 rounds to the same binary32
+and otherwise stays at least 2^-49 (relative) away from one (a - m b is a
+nonzero multiple of 2^(ea - 25) for a = A 2^ea,
+A < 2^24, and a midpoint m of 25 significant bits), so a fp64 product with a
+reciprocal of b accurate to ~2^-50 rounds to the same binary32
 value as the IEEE division: fl32(fl64(a * r)) == fl32(a / b). The kernel's r is
 the fp64 hardware reciprocal refined by two Newton steps; here the starting
 point is deliberately worse (14 significant bits, perturbed) so that the

@@ -51,14 +51,22 @@ def test_scaling_random_and_in_place(orc, rows, K):
     assert np.array_equal(host(t).view(np.uint16), want_x)
 
 
-def run_awq(orc, W, X, s, sym, what):
+def run_awq(orc, W, X, s, sym, what, g=128):
     Ws = orc.awq_scale_weight(W, s)
-    codes, scales, zeros = orc.q4_quantize_pack(Ws, g=128, sym=sym)
+    codes, scales, zeros = orc.q4_quantize_pack(Ws, g=g, sym=sym)
     Y = host(q4.w4a16_linear_awq(gpu(X), gpu(codes), gpu(scales.view(np.float16)),
-                                 None if zeros is None else gpu(zeros), gpu(s)))
+                                 None if zeros is None else gpu(zeros), gpu(s), g=g))
     Xs = orc.awq_scale_act(X, s)
-    Yref, B = orc.w4a16_ref(Xs, codes, scales, zeros)
+    Yref, B = orc.w4a16_ref(Xs, codes, scales, zeros, g=g)
     check_gemm(Y, Yref, B, what)
+
+
+# g = 64 and 32: the scaled copy in the workspace, then the small-group kernel
+@pytest.mark.parametrize("M,N,K", [(1, 300, 1024), (20, 130, 512), (300, 100, 512)])
+@pytest.mark.parametrize("g", [32, 64])
+def test_linear_awq_small_groups(orc, M, N, K, g):
+    W, X = workloads.small_case(M * 3 + N + K + g, M, N, K)
+    run_awq(orc, W, X, factors(K, M + N + g), False, f"awq g={g} M={M} N={N} K={K}", g=g)
 
 
 # one token: the fused decode GEMV in each launch variant (16 / 8 / 4

@@ -152,11 +152,13 @@ def test_prefill_workload_sampled(orc):
 
 
 def test_errors_and_empty():
+    X = torch.zeros((4, 240), dtype=torch.float16, device="cuda")
+    codes = torch.zeros((8, 120), dtype=torch.uint8, device="cuda")
+    with pytest.raises(q4.Q4Error) as e:   # 80 is not a multiple of 32
+        q4.w4a16_linear(X, codes, torch.zeros((8, 3), dtype=torch.float16, device="cuda"), None, g=80)
+    assert e.value.status == q4.Q4_ERR_UNSUPPORTED
     X = torch.zeros((4, 256), dtype=torch.float16, device="cuda")
     codes = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
-    with pytest.raises(q4.Q4Error) as e:
-        q4.w4a16_linear(X, codes, torch.zeros((8, 4), dtype=torch.float16, device="cuda"), None, g=64)
-    assert e.value.status == q4.Q4_ERR_UNSUPPORTED
     Y = q4.w4a16_linear(X[:0], codes, torch.zeros((8, 2), dtype=torch.float16, device="cuda"), None)
     assert Y.shape == (0, 8)
     with pytest.raises(q4.Q4Error) as e:
@@ -228,3 +230,71 @@ def test_weight_past_32bit_offsets(orc, M):
     check_gemm(Y[:, sel], Yref, B, f"M={M} N={N} K={K} past 32-bit offsets")
     del codes, scales, zeros
     torch.cuda.empty_cache()
+
+
+# Group sizes other than 128: g = 32 and 64 (what the quantizer also writes;
+# the Core ideas granularity table uses g = 32) on every route -- the
+# small-group kernel (any M; K a multiple of g but not of 128 included) and
+# the large-M GEMM (M >= 256, K a multiple of 128) -- and g = 256, 384 (a
+# multiple of 128 that is not a power of two never takes the large-M GEMM).
+SMALL_G_SHAPES = [(1, 300, 512), (1, 1000, 96 * 4), (5, 77, 320), (16, 129, 1024),
+                  (17, 64, 192), (33, 130, 640), (64, 100, 256), (65, 129, 384),
+                  (300, 260, 512), (300, 100, 448)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_G_SHAPES)
+@pytest.mark.parametrize("g", [32, 64])
+@pytest.mark.parametrize("sym", [False, True])
+def test_small_group_sizes(orc, M, N, K, g, sym):
+    if K % g:
+        pytest.skip("K must be a multiple of g")
+    W, X = workloads.small_case(M * 5 + N * 3 + K + g + int(sym), M, N, K)
+    run_case(orc, W, X, g, sym, what=f"g={g} M={M} N={N} K={K} sym={sym}")
+
+
+@pytest.mark.parametrize("M", [1, 17, 65, 300])
+@pytest.mark.parametrize("g", [256, 384])
+@pytest.mark.parametrize("sym", [False, True])
+def test_large_group_sizes(orc, M, g, sym):
+    N, K = 200, 3 * 768
+    W, X = workloads.small_case(M * 7 + g + int(sym), M, N, K)
+    run_case(orc, W, X, g, sym, what=f"g={g} M={M} N={N} K={K} sym={sym}")
+
+
+@pytest.mark.parametrize("M,K", [(40, 192), (300, 512), (300, 96)])
+@pytest.mark.parametrize("g", [32, 64])
+def test_small_group_one_hot(orc, M, K, g):
+    """One-hot X through the small-group kernel and the large-M GEMM at g =
+    32 / 64: Y[m, n] = fp16(w_hat[n, k(m)]) exactly (pins each group's scale
+    and zero-point indexing)."""
+    if K % g:
+        pytest.skip("K must be a multiple of g")
+    N = 70
+    rng = np.random.default_rng(M + K + g)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    codes, scales, zeros = orc.q4_quantize_pack(W, g=g, sym=False)
+    kk = (np.arange(M) * 5 + 1) % K
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), kk] = 1.0
+    Y = host(q4.w4a16_linear(gpu(X), gpu(codes), gpu(scales.view(np.float16)), gpu(zeros), g=g))
+    w_hat = orc.q4_dequant(codes, scales, zeros, K, g)
+    expect = w_hat[:, kk].T.astype(np.float16)
+    assert np.array_equal(Y.view(np.uint16), expect.view(np.uint16))
+
+
+def test_quantize_out_must_match(orc):
+    """q4_quantize_pack(out=...) checks the caller's buffers before any launch."""
+    W = torch.zeros((8, 256), dtype=torch.float16, device="cuda")
+    good = (torch.empty((8, 128), dtype=torch.uint8, device="cuda"),
+            torch.empty((8, 8), dtype=torch.float16, device="cuda"),
+            torch.empty((8, 4), dtype=torch.uint8, device="cuda"))
+    q4.q4_quantize_pack(W, g=32, out=good)
+    with pytest.raises(ValueError):   # sized for g = 128, used with g = 32
+        q4.q4_quantize_pack(W, g=32, out=(good[0], torch.empty((8, 2), dtype=torch.float16, device="cuda"),
+                                          torch.empty((8, 1), dtype=torch.uint8, device="cuda")))
+    with pytest.raises(ValueError):
+        q4.q4_quantize_pack(W, g=32, out=(good[0], good[1], None))
+    with pytest.raises(TypeError):
+        q4.q4_quantize_pack(W, g=32, out=(good[0], good[1].float(), good[2]))
+    with pytest.raises(ValueError):
+        q4.q4_quantize_pack(W, g=32, out=(good[0].cpu(), good[1], good[2]))

@@ -58,6 +58,8 @@ def test_shapes(orc, M, Ns, K, sym):
     (20, [100, 200], 1024, 128, [False, False]),      # M > 16
     (64, [130, 7], 512, 128, [True, True]),
     (1, [256, 300], 512, 256, [False, False]),        # g = 256
+    (1, [256, 300], 512, 64, [False, False]),         # g = 64 and 32: small-group kernel
+    (5, [100, 77], 384, 32, [True, True]),
     (2, [300, 17], 1024, 128, [False, True]),         # mixed symmetric / asymmetric
 ])
 def test_fallback_one_launch_per_layer(orc, M, Ns, K, g, syms):

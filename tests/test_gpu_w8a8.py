@@ -9,7 +9,7 @@ import torch
 
 import quantized_gemm_q4_amd as q4
 import workloads
-from parity import check_gemm, gpu, host, sample_rows
+from parity import check_gemm, gpu, host, out_buffer, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,7 @@ def test_gemm_shapes(orc, M, N, K):
     W, X = workloads.small_case(M * 131 + N * 7 + K, M, N, K)
     Xq, sx = orc.q8_quantize_act(X)
     Wq, sw = orc.q8_quantize_weight(W)
-    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    acc = out_buffer((M, N), torch.int32)
     Y = host(q4.w8a8_gemm(gpu(Xq), gpu(sx), gpu(Wq), gpu(sw), acc_out=acc))
     acc_ref, aacc, ovf = orc.int8_gemm(Xq, Wq)
     assert ovf == 0
@@ -90,7 +90,7 @@ def test_closed_form_accumulator():
     Xq = torch.full((3, K), 127, dtype=torch.int8, device="cuda")
     Wq = torch.full((5, K), -127, dtype=torch.int8, device="cuda")
     one = torch.ones(3, dtype=torch.float32, device="cuda")
-    acc = torch.empty((3, 5), dtype=torch.int32, device="cuda")
+    acc = out_buffer((3, 5), torch.int32)
     q4.w8a8_gemm(Xq, one, Wq, torch.ones(5, dtype=torch.float32, device="cuda"), acc_out=acc)
     assert torch.all(acc == -16129 * K)
 
@@ -107,7 +107,7 @@ def test_w8a8_workload(orc):
     M, K = w["X"].shape
     N = w["W"].shape[0]
     ws = q4.w8a8_workspace(M, K, "cuda")
-    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    acc = out_buffer((M, N), torch.int32)
     Y = host(q4.w8a8_linear(gpu(w["X"]), Wq, sw, s, workspace=ws, acc_out=acc))
     # the workspace holds the per-token codes and scales: bit for bit
     Xq_ref, sx_ref = orc.q8_quantize_act(w["X"], s_ref)
@@ -136,3 +136,19 @@ def test_errors():
                        torch.ones(4, device="cuda"),
                        workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert e.value.status == q4.Q4_ERR_INVALID_ARG
+
+
+def test_linear_checks_gemm_preconditions_before_launching():
+    """A misaligned Wq is an error of the GEMM step; w8a8_linear must report
+    it before its activation quantizer runs, so the workspace stays as it
+    was."""
+    M, N, K = 4, 8, 128
+    X = torch.ones((M, K), dtype=torch.float16, device="cuda")
+    Wbuf = torch.zeros(N * K + 16, dtype=torch.int8, device="cuda")
+    Wq_mis = Wbuf[1: 1 + N * K].view(N, K)
+    ws = torch.full((q4.w8a8_workspace_bytes(M, K),), 0x5A, dtype=torch.uint8, device="cuda")
+    with pytest.raises(q4.Q4Error) as e:
+        q4.w8a8_linear(X, Wq_mis, torch.ones(N, device="cuda"), workspace=ws)
+    assert e.value.status == q4.Q4_ERR_MISALIGNED
+    torch.cuda.synchronize()
+    assert bool((ws == 0x5A).all()), "the activation quantizer ran before the GEMM's checks"
