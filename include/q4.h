@@ -283,6 +283,38 @@ Q4_API q4_status w8a8_linear(const void *X, int64_t M, int64_t N, int64_t K,
                              size_t workspace_bytes, int32_t *acc_out, void *stream);
 
 /* ----------------------------------------------------------------------------
+ * w8a8_linear_noalloc -- w8a8_linear for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, the same kernels and the same
+ * results bit for bit, with the per-token codes and scales kept in a scratch
+ * array the library holds in device memory instead of a caller workspace.
+ * The call itself allocates nothing.
+ *
+ * Scratch: Q4_NOALLOC_SCRATCH_BYTES (16 MiB + 64 KiB) per GPU, a fixed array
+ * each GPU the library runs on holds until the process ends; its device
+ * address is looked up on the first call on each device. A call needs
+ * w8a8_workspace_bytes(M, K) of it (M * K rounded up to 256, plus 4 M): the
+ * W8A8 workload's 2048 x 8192 fits. Larger M * K is refused with
+ * UNSUPPORTED before anything runs.
+ * Every call on one GPU shares that GPU's array and leaves its codes and
+ * scales in it: calls that overlap on one GPU (two streams, two threads)
+ * race on it and must be serialised by the caller. Nothing in it has to
+ * start at zero (each call writes what it reads).
+ * The stream must belong to the current device (hipSetDevice).
+ *
+ * X, M, N, K, Wq, w_scale, smooth_s, Y, acc_out, stream: as for w8a8_linear.
+ * Errors: as for w8a8_linear (no workspace arguments), plus UNSUPPORTED for
+ *         a request beyond the scratch array and HIP if the array's address
+ *         cannot be found.
+ * -------------------------------------------------------------------------- */
+#define Q4_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u + 64u * 1024u)
+Q4_API size_t w8a8_noalloc_max_bytes(void);
+Q4_API q4_status w8a8_linear_noalloc(const void *X, int64_t M, int64_t N, int64_t K,
+                                     const int8_t *Wq, const float *w_scale,
+                                     const float *smooth_s, void *Y, int32_t *acc_out,
+                                     void *stream);
+
+/* ----------------------------------------------------------------------------
  * FP8 E4M3 variant of the W8A8 path (Operators guide §4.1 formats: E4M3 for
  * weights and activations; §4.2 scaled FP8 GEMM, C = scale_A * scale_B *
  * (A_fp8 @ B_fp8); Core ideas §2.1: E4M3 range +-448). The scales are

@@ -14,6 +14,7 @@ Functions (same names as the C ABI):
   q8_quantize_act(X, smooth_s=None) -> (Xq, x_scale)
   w8a8_gemm(Xq, x_scale, Wq, w_scale, acc_out=None) -> Y
   w8a8_linear(X, Wq, w_scale, smooth_s=None, workspace=None, acc_out=None) -> Y
+  w8a8_linear_noalloc(X, Wq, w_scale, smooth_s=None, acc_out=None) -> Y  (no workspace)
   smoothquant_scales(Xcal, W, alpha=0.5) -> s
   fp8_quantize_weight(W, smooth_s=None) -> (Wq, w_scale)      E4M3 codes as uint8
   fp8_quantize_act(X, smooth_s=None) -> (Xq, x_scale)
@@ -66,6 +67,8 @@ SIGNATURES = {
     "w8a8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "w8a8_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                                    ctypes.c_size_t, _vp, _vp]),
+    "w8a8_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "w8a8_linear_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "smoothquant_scales": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, ctypes.c_float, _vp, _vp]),
     "fp8_quantize_weight": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "fp8_quantize_act": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
@@ -381,6 +384,34 @@ def w8a8_linear(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
     Y = _output(out, M, N, X.device)
     _check(lib().w8a8_linear(_ptr(X), M, N, K, _ptr(Wq), _ptr(w_scale), _ptr(smooth_s), _ptr(Y),
                              _ptr(workspace), workspace.numel(), _ptr(acc_out), _stream(X)))
+    return Y
+
+
+def w8a8_noalloc_max_bytes() -> int:
+    return int(lib().w8a8_noalloc_max_bytes())
+
+
+def w8a8_linear_noalloc(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
+                        smooth_s: torch.Tensor | None = None, acc_out: torch.Tensor | None = None,
+                        out: torch.Tensor | None = None):
+    """w8a8_linear with the per-token codes and scales in the library's own
+    scratch array (no workspace; the C call allocates nothing). Calls that
+    overlap on one GPU race on that array."""
+    _need(X, torch.float16, "X", 2)
+    _need(Wq, torch.int8, "Wq", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = X.shape
+    N = Wq.shape[0]
+    _need_smooth(smooth_s, K)
+    if Wq.shape[1] != K or w_scale.numel() != N:
+        raise ValueError("w8a8_linear_noalloc: Wq must be [N, K] and w_scale [N]")
+    if acc_out is not None:
+        _need(acc_out, torch.int32, "acc_out", 2)
+        if acc_out.shape != (M, N):
+            raise ValueError("acc_out must be [M, N]")
+    Y = _output(out, M, N, X.device)
+    _check(lib().w8a8_linear_noalloc(_ptr(X), M, N, K, _ptr(Wq), _ptr(w_scale), _ptr(smooth_s),
+                                     _ptr(Y), _ptr(acc_out), _stream(X)))
     return Y
 
 

@@ -3,6 +3,7 @@
 // allocates; errors are reported as q4_status plus a thread-local message.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "../../include/q4.h"
 #include "q4_internal.hpp"
@@ -327,6 +328,78 @@ Q4_API q4_status w8a8_linear(const void *X, int64_t M, int64_t N, int64_t K, con
     if (e == hipSuccess)
         e = q4k::launch_w8a8_gemm(xq, sx, Wq, w_scale, M, N, K, static_cast<uint16_t *>(Y), acc_out, hs);
     return from_hip(e, "w8a8_linear");
+}
+
+// ---------------------------------------------------------------------------
+// w8a8_linear without a caller workspace, for callers that cannot allocate.
+// The per-token codes and scales go to `scratch`, a fixed array in device
+// memory of its own on every GPU the library runs on (held until the process
+// ends). In host code the name `scratch` only stands in for the symbol: its
+// device address is looked up once per device, with that device current, and
+// only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[Q4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static q4_status scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return from_hip(e, "w8a8_linear_noalloc: hipGetDevice");
+    Q4_REQUIRE(dev >= 0 && dev < kMaxDevices, Q4_ERR_UNSUPPORTED,
+               "w8a8_linear_noalloc: device %d beyond the %d the library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return from_hip(e, "w8a8_linear_noalloc: hipGetSymbolAddress");
+        Q4_REQUIRE(ptr && (reinterpret_cast<uintptr_t>(ptr) & 255u) == 0, Q4_ERR_HIP,
+                   "w8a8_linear_noalloc: the scratch array's device address is not 256-byte aligned");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ok();
+}
+
+Q4_API size_t w8a8_noalloc_max_bytes(void) { return Q4_NOALLOC_SCRATCH_BYTES; }
+
+Q4_API q4_status w8a8_linear_noalloc(const void *X, int64_t M, int64_t N, int64_t K,
+                                     const int8_t *Wq, const float *w_scale,
+                                     const float *smooth_s, void *Y, int32_t *acc_out,
+                                     void *stream)
+{
+    // the shape first, so that a request beyond the scratch array is refused
+    // without touching the device
+    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K % 16 == 0 &&
+                   K <= 133143,
+               Q4_ERR_INVALID_ARG,
+               "w8a8_linear_noalloc: bad shape M=%lld N=%lld K=%lld (K a multiple of 16, <= 133143)",
+               (long long)M, (long long)N, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    const size_t need = w8a8_workspace_bytes(M, K);
+    Q4_REQUIRE(need <= (size_t)Q4_NOALLOC_SCRATCH_BYTES, Q4_ERR_UNSUPPORTED,
+               "w8a8_linear_noalloc: M=%lld, K=%lld needs %zu bytes of scratch, more than the "
+               "%zu this entry point has (use w8a8_linear with a workspace)",
+               (long long)M, (long long)K, need, (size_t)Q4_NOALLOC_SCRATCH_BYTES);
+    // the scratch array stands in for the codes and scales (X for their
+    // pointers in the GEMM's checks)
+    void *ws = nullptr;
+    q4_status st = check_w8a8_gemm("w8a8_linear_noalloc", X, static_cast<const float *>(X), Wq,
+                                   w_scale, M, N, K, Y);
+    if (st != Q4_OK) return st;
+    if ((st = check_act_quant("w8a8_linear_noalloc", X, smooth_s)) != Q4_OK) return st;
+    if ((st = scratch_address(&ws)) != Q4_OK) return st;
+    int8_t *xq = static_cast<int8_t *>(ws);
+    float *sx = reinterpret_cast<float *>(workspace_scales(ws, M, K));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = q4k::launch_q8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
+    if (e == hipSuccess)
+        e = q4k::launch_w8a8_gemm(xq, sx, Wq, w_scale, M, N, K, static_cast<uint16_t *>(Y), acc_out, hs);
+    return from_hip(e, "w8a8_linear_noalloc");
 }
 
 Q4_API q4_status fp8_quantize_weight(const void *W, const float *smooth_s, int64_t N, int64_t K,

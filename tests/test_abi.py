@@ -53,6 +53,10 @@ def test_layout_version_and_workspace(lib):
     assert lib.w4a16_awq_workspace_bytes(1, 4096) == 8192
     assert lib.w4a16_awq_workspace_bytes(3, 24) == 256
     assert lib.w4a16_awq_workspace_bytes(0, 128) == 0
+    # the no-allocation scratch array holds the W8A8 workload's codes and scales
+    assert lib.w8a8_noalloc_max_bytes() == 16 * 1024 * 1024 + 64 * 1024
+    assert lib.w8a8_workspace_bytes(2048, 8192) <= lib.w8a8_noalloc_max_bytes()
+    assert lib.w8a8_workspace_bytes(2100, 8192) > lib.w8a8_noalloc_max_bytes()
 
 
 FAKE = 0x10000          # never dereferenced: validation fails first
@@ -125,6 +129,13 @@ def layers(*descs):
     (lambda L: L.w8a8_linear(FAKE, 4, 4, 128, FAKE, None, None, FAKE, FAKE, 4096, None, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.w8a8_linear(MISAL, 4, 4, 128, FAKE, FAKE, None, FAKE, FAKE, 4096, None, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.w8a8_linear(FAKE, 4, 4, 128, FAKE, FAKE, MISAL, FAKE, FAKE, 4096, None, None), q4.Q4_ERR_MISALIGNED),
+    # the no-allocation entry point refuses before it touches the device
+    (lambda L: L.w8a8_linear_noalloc(FAKE, 4, 4, 100, FAKE, FAKE, None, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w8a8_linear_noalloc(FAKE, 2100, 4, 8192, FAKE, FAKE, None, FAKE, None, None),
+     q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.w8a8_linear_noalloc(FAKE, 4, 4, 128, MISAL, FAKE, None, FAKE, None, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.w8a8_linear_noalloc(FAKE, 4, 4, 128, FAKE, None, None, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.w8a8_linear_noalloc(FAKE, 0, 4, 128, None, None, None, None, None, None), q4.Q4_OK),
     (lambda L: L.fp8_quantize_weight(FAKE, None, 4, 100, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.fp8_quantize_weight(FAKE, MISAL, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.fp8_quantize_act(FAKE, None, 4, 128, MISAL, FAKE, None), q4.Q4_ERR_MISALIGNED),
