@@ -16,7 +16,8 @@ The JSON line also carries:
                 with HIP events on its stream, against 8 TB/s;
   cpu_baseline  the CPU oracle (fp64 reference over the dequantized weights)
                 timed on this host's cores on the same step;
-  extra         the same step as two w4a16_linear launches, each layer alone,
+  extra         (every figure the median of 5 timed repeats) the same step as
+                two w4a16_linear launches, each layer alone,
                 prefill (M = 2048, sym) TFLOP/s against the fp16 MFMA peak,
                 W8A8 (M = 2048, K = N = 8192) TOP/s against the int8 peak,
                 its FP8 E4M3 variant TFLOP/s against the fp8 peak, MXFP4
@@ -106,7 +107,7 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.float16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    def timed(fn, n):
+    def timed_once(fn, n):
         """Run fn(i) for i < n between two HIP events on the current stream."""
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -116,6 +117,10 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3  # seconds
+
+    def timed(fn, n, repeats=5):
+        """Median over `repeats` timings of fn(0..n-1) (seconds for the n calls)."""
+        return float(np.median([timed_once(fn, n) for _ in range(repeats)]))
 
     def graph_of(fn, n):
         """Capture fn(0..n-1) into one HIP graph (eager fallback with --eager)."""
@@ -168,7 +173,7 @@ def main():
         tail = graph_of(step, rem) if rem else None
         full()
         torch.cuda.synchronize()
-        t = timed(lambda i: full() if i < K // copies else tail(), K // copies + (1 if rem else 0))
+        t = timed_once(lambda i: full() if i < K // copies else tail(), K // copies + (1 if rem else 0))
         out.update(value=step_bytes * K / t / 1e9, unit="GB/s", steps=K, warmup=args.warmup,
                    ms_per_step=t / K * 1e3)
         out["config"] = {"workload": "W4A16 decode: M=1, K=4096, N=11008 and N=4096 on the same X "
@@ -190,6 +195,7 @@ def main():
                            "algorithmic_bytes_per_launch": step_bytes, "launches": reps * copies}
 
         # the same step as two single-layer launches, and each layer alone
+        # (the per-call figures go into the roofline block beside the fused launch)
         def step2(i):
             c = i % copies
             for L in layers:
@@ -205,6 +211,9 @@ def main():
             bl = w4a16_bytes(1, L["N"], 4096)
             extra[f"decode_n{L['N']}"] = {"us": tl * 1e6, "GB/s": bl / tl / 1e9,
                                           "frac_hbm": bl / tl / 1e9 / HBM_PEAK_GBS}
+            out["roofline"].setdefault("per_call", {})[f"w4a16_linear M=1 N={L['N']} K=4096"] = {
+                "avg_launch_us": tl * 1e6, "algorithmic_bytes_per_launch": bl,
+                "achieved": bl / tl / 1e9, "frac": bl / tl / 1e9 / HBM_PEAK_GBS}
         # the N = 11008 layer in its AWQ form: x / s fused into the GEMV's X loads
         L = next(L for L in layers if L["N"] == 11008)
         s_awq = torch.from_numpy(np.exp(np.random.default_rng(5002).uniform(-0.5, 0.5, 4096))
@@ -222,6 +231,7 @@ def main():
 
         if not args.skip_cpu:
             out["cpu_baseline"] = cpu_baseline(step_bytes)
+            extra["cpu_oracle"] = cpu_oracle_samples()
 
     # ---- batched decode M = 16, 64 ---------------------------------------------
     if only in (None, "batched"):
@@ -468,6 +478,55 @@ def measured_traffic():
     if rec.get("source_sha256") != sha or rec.get("kernel") != DECODE_KERNEL:
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def _wall(fn, min_s: float = 1.0):
+    """Median wall time of fn() over at least three runs and about min_s seconds."""
+    t0 = time.perf_counter()
+    fn()
+    first = time.perf_counter() - t0
+    n = max(3, min(20, int(min_s / max(first, 1e-4))))
+    ts = []
+    for _ in range(n):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def cpu_oracle_samples() -> dict:
+    """The oracle on bounded samples of the other workloads (same inputs as
+    the GPU sections; a few seconds each): quantize + pack of the full
+    [11008, 4096] weight, the fp64 W4A16 product on 256 of the prefill
+    workload's 2048 rows, and the W8A8 chain (per-token INT8 of the rows,
+    exact integer GEMM, fp32 epilogue) on 128 of its 2048 rows."""
+    import oracle
+    import workloads
+
+    res = {"cores": oracle.num_threads()}
+    w = workloads.quant()
+    qbytes = 11008 * 4096 * 2 + 11008 * 2048 + 11008 * 32 * 2 + 11008 * 16
+    t = _wall(lambda: oracle.q4_quantize_pack(w["W"], g=128, sym=False))
+    res["quantize_pack"] = {"GB/s": qbytes / t / 1e9, "s": t, "sample": "full [11008, 4096] asym g=128"}
+    w = workloads.prefill()
+    c, sc, z = oracle.q4_quantize_pack(w["W"], g=128, sym=True)
+    rows = np.arange(256)
+    t = _wall(lambda: oracle.w4a16_ref(w["X"], c, sc, z, rows=rows))
+    res["prefill_fp64"] = {"GFLOP/s": 2 * 256 * 11008 * 4096 / t / 1e9, "s": t,
+                           "sample": "256 of 2048 rows, N=11008, K=4096, sym g=128"}
+    w = workloads.w8a8()
+    s_ref = oracle.smooth_scales(w["Xcal"], w["W"], 0.5)
+    Wq, sw = oracle.q8_quantize_weight(w["W"], s_ref)
+    Xs = w["X"][:128]
+
+    def chain():
+        Xq, sx = oracle.q8_quantize_act(Xs, s_ref)
+        acc, aacc, _ = oracle.int8_gemm(Xq, Wq)
+        oracle.w8a8_epilogue(acc, aacc, sx, sw)
+    t = _wall(chain)
+    res["w8a8_int"] = {"GOP/s": 2 * 128 * 8192 * 8192 / t / 1e9, "s": t,
+                       "sample": "128 of 2048 rows, N=K=8192: per-token INT8, int64 GEMM, epilogue"}
+    return res
 
 
 def cpu_baseline(step_bytes: int) -> dict:
