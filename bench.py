@@ -325,8 +325,15 @@ def main():
         gg = graph_of(lambda i: q4.w8a8_gemm(Xq, sx, *cps[i % copies], out=Y), copies)
         gg()
         tg = timed(lambda i: gg(), reps) / (reps * copies)
+        # the whole layer from fp16 X: one launch, the per-token quantizer fused in
+        X1 = gpu(w["X"])
+        ws1 = q4.w8a8_workspace(1, K, dev)
+        gl = graph_of(lambda i: q4.w8a8_linear(X1, *cps[i % copies], None, workspace=ws1, out=Y), copies)
+        gl()
+        tl = timed(lambda i: gl(), reps) / (reps * copies)
         extra["w8a8"]["decode_n11008"] = {"gemv_us": tg * 1e6, "GB/s": nb / tg / 1e9,
-                                          "frac_hbm": nb / tg / 1e9 / HBM_PEAK_GBS, "bytes": nb}
+                                          "frac_hbm": nb / tg / 1e9 / HBM_PEAK_GBS, "bytes": nb,
+                                          "linear_fused_us": tl * 1e6}
         del cps, Wq, Xq, Y
 
     # ---- FP8 E4M3 variant of the same layer ------------------------------------
@@ -366,8 +373,14 @@ def main():
         gg = graph_of(lambda i: q4.fp8_gemm(Xq, sx, *cps[i % copies], out=Y), copies)
         gg()
         tg = timed(lambda i: gg(), reps) / (reps * copies)
+        X1 = gpu(w["X"])
+        ws1 = q4.w8a8_workspace(1, K, dev)
+        gl = graph_of(lambda i: q4.fp8_linear(X1, *cps[i % copies], None, workspace=ws1, out=Y), copies)
+        gl()
+        tl = timed(lambda i: gl(), reps) / (reps * copies)
         extra["fp8"]["decode_n11008"] = {"gemv_us": tg * 1e6, "GB/s": nb / tg / 1e9,
-                                         "frac_hbm": nb / tg / 1e9 / HBM_PEAK_GBS, "bytes": nb}
+                                         "frac_hbm": nb / tg / 1e9 / HBM_PEAK_GBS, "bytes": nb,
+                                         "linear_fused_us": tl * 1e6}
         del cps, Wq, Xq, Y
 
     # ---- MXFP4 weights x E4M3 activations (W4A8) ------------------------------

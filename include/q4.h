@@ -35,6 +35,12 @@
  *     returns Q4_ERR_HIP. A fault inside a kernel surfaces at the caller's
  *     next synchronization. No C++ exception crosses the ABI.
  *   - A zero-sized M or N is a valid no-op.
+ *   - Debug mode: with the environment variable Q4_DEBUG set (and not "0")
+ *     when the library loads, every call waits for its stream after its
+ *     launches, so a fault inside one of its kernels is returned by that
+ *     call as Q4_ERR_HIP with the call's name in q4_last_error(), and each
+ *     call writes one line ("[q4] <call>: ok" or the error) to stderr.
+ *     Calls are then synchronous; off by default.
  *   - Inputs must be finite; non-finite inputs give unspecified codes and
  *     outputs (never an out-of-bounds access).
  *   - Rounding is IEEE round-to-nearest-even everywhere; divisions are true
@@ -272,7 +278,10 @@ Q4_API size_t w8a8_workspace_bytes(int64_t M, int64_t K);
  * 256-byte aligned; after the call it holds Xq [M, K] then x_scale [M]
  * (at offset round_up(M*K, 256)).
  * Every precondition of both steps (w8a8_gemm's included) is checked before
- * the first launch.
+ * the first launch. At decode sizes (M <= 16, M * K <= 16384, K a multiple of
+ * 1024 up to 8192) the two steps are one launch: the decode GEMV quantizes X
+ * itself (the same codes and scales bit for bit) and the workspace still
+ * receives Xq and x_scale.
  * Errors: INVALID_ARG (shape as for w8a8_gemm, a null pointer, workspace too
  *         small), UNSUPPORTED (M > 65535 * 128), MISALIGNED (X, Wq,
  *         smooth_s; the workspace must be 256-byte aligned), HIP.
@@ -362,7 +371,8 @@ Q4_API q4_status fp8_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t
  * w8a8_linear (w8a8_workspace_bytes(M, K) bytes, 256-byte aligned: E4M3 codes
  * [M, K], then x_scale [M] at offset round_up(M*K, 256)). smooth_s as for
  * w8a8_linear. Every precondition of both steps is checked before the
- * first launch. Errors: as for fp8_gemm, plus a too small or misaligned
+ * first launch; at decode sizes the two steps are one launch, as for
+ * w8a8_linear. Errors: as for fp8_gemm, plus a too small or misaligned
  * workspace and a misaligned X or smooth_s.
  * -------------------------------------------------------------------------- */
 Q4_API q4_status fp8_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *Wq,
@@ -414,7 +424,9 @@ Q4_API q4_status mxfp4_gemm(const uint8_t *Xq, const float *x_scale, const uint8
  * mxfp4_linear -- fp8_quantize_act of X (with /smooth_s fused in) into the
  * workspace (laid out as for w8a8_linear, w8a8_workspace_bytes(M, K) bytes,
  * 256-byte aligned), then mxfp4_gemm. smooth_s as for w8a8_linear.
- * Every precondition of both steps is checked before the first launch.
+ * Every precondition of both steps is checked before the first launch; at
+ * decode sizes (as for w8a8_linear, with 16-byte aligned scales) the two
+ * steps are one launch.
  * Errors: as for mxfp4_gemm, plus a too small or misaligned workspace and a
  * misaligned X or smooth_s.
  * -------------------------------------------------------------------------- */

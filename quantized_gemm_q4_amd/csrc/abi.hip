@@ -3,6 +3,8 @@
 // allocates; errors are reported as q4_status plus a thread-local message.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "../../include/q4.h"
@@ -36,6 +38,31 @@ q4_status from_hip(hipError_t e, const char *what)
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Q4_DEBUG (set and not "0"): every call waits for its own stream after its
+// launches, so a fault inside one of its kernels is returned by that call as
+// Q4_ERR_HIP (instead of surfacing at a later synchronization), and writes
+// one line per call to stderr. Read once.
+bool debug_mode()
+{
+    static const bool on = [] {
+        const char *e = std::getenv("Q4_DEBUG");
+        return e && *e && std::strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
+// The status of a call whose kernels were launched with launch status e.
+q4_status done(hipError_t e, const char *what, void *stream)
+{
+    if (e == hipSuccess && debug_mode()) {
+        e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+        if (e == hipSuccess) e = hipGetLastError();
+    }
+    const q4_status st = e == hipSuccess ? ok() : fail(Q4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    if (debug_mode()) std::fprintf(stderr, "[q4] %s: %s%s%s\n", what, st == Q4_OK ? "ok" : "error", st == Q4_OK ? "" : ": ", g_err);
+    return st;
+}
 
 constexpr int64_t kIntMax = 0x7fffffff;
 
@@ -71,7 +98,7 @@ Q4_API q4_status q4_quantize_pack(const void *W, int64_t N, int64_t K, int32_t g
     hipError_t e = q4k::launch_q4_quantize_pack(
         static_cast<const uint16_t *>(W), N, K, g, sym, codes, static_cast<uint16_t *>(scales),
         sym ? nullptr : zeros, static_cast<hipStream_t>(stream));
-    return from_hip(e, "q4_quantize_pack");
+    return done(e, "q4_quantize_pack", stream);
 }
 
 Q4_API q4_status w4a16_linear(const void *X, int64_t M, int64_t N, int64_t K, int32_t g,
@@ -94,7 +121,7 @@ Q4_API q4_status w4a16_linear(const void *X, int64_t M, int64_t N, int64_t K, in
     hipError_t e = q4k::launch_w4a16(static_cast<const uint16_t *>(X), M, N, K, g, codes,
                                      static_cast<const uint16_t *>(scales), zeros,
                                      static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
-    return from_hip(e, "w4a16_linear");
+    return done(e, "w4a16_linear", stream);
 }
 
 Q4_API q4_status w4a16_linear_multi(const void *X, int64_t M, int64_t K, int32_t g,
@@ -137,7 +164,7 @@ Q4_API q4_status w4a16_linear_multi(const void *X, int64_t M, int64_t K, int32_t
             e = q4k::launch_w4a16(static_cast<const uint16_t *>(X), M, d[i].N, K, g, d[i].codes,
                                   d[i].scales, d[i].zeros, d[i].Y, st);
     }
-    return from_hip(e, "w4a16_linear_multi");
+    return done(e, "w4a16_linear_multi", stream);
 }
 
 static q4_status awq_scale(const char *what, const void *A, const float *awq_s, int64_t rows,
@@ -156,7 +183,7 @@ static q4_status awq_scale(const char *what, const void *A, const float *awq_s, 
                "%s: the output overlaps the input without being the same array", what);
     hipError_t e = q4k::launch_awq_scale(static_cast<const uint16_t *>(A), awq_s, rows, K, div,
                                          static_cast<uint16_t *>(out), static_cast<hipStream_t>(stream));
-    return from_hip(e, what);
+    return done(e, what, stream);
 }
 
 Q4_API q4_status awq_scale_weight(const void *W, const float *awq_s, int64_t N, int64_t K, void *Ws,
@@ -203,14 +230,14 @@ Q4_API q4_status w4a16_linear_awq(const void *X, int64_t M, int64_t N, int64_t K
     hipError_t e = q4k::launch_w4a16_gemv_awq(static_cast<const uint16_t *>(X), M, N, K, g, codes,
                                               static_cast<const uint16_t *>(scales), zeros, awq_s,
                                               static_cast<uint16_t *>(Y), st);
-    if (e != hipErrorNotSupported) return from_hip(e, "w4a16_linear_awq");
+    if (e != hipErrorNotSupported) return done(e, "w4a16_linear_awq", stream);
     // other shapes: x'' into the workspace, then the plain W4A16 product
     uint16_t *xs = static_cast<uint16_t *>(workspace);
     e = q4k::launch_awq_scale(static_cast<const uint16_t *>(X), awq_s, M, K, true, xs, st);
-    if (e != hipSuccess) return from_hip(e, "w4a16_linear_awq");
+    if (e != hipSuccess) return done(e, "w4a16_linear_awq", stream);
     e = q4k::launch_w4a16(xs, M, N, K, g, codes, static_cast<const uint16_t *>(scales), zeros,
                           static_cast<uint16_t *>(Y), st);
-    return from_hip(e, "w4a16_linear_awq");
+    return done(e, "w4a16_linear_awq", stream);
 }
 
 Q4_API q4_status q8_quantize_weight(const void *W, const float *smooth_s, int64_t N, int64_t K,
@@ -225,7 +252,7 @@ Q4_API q4_status q8_quantize_weight(const void *W, const float *smooth_s, int64_
                Q4_ERR_MISALIGNED, "q8_quantize_weight: W, Wq and smooth_s must be 16-byte aligned");
     hipError_t e = q4k::launch_q8_weight(static_cast<const uint16_t *>(W), smooth_s, N, K, Wq,
                                          w_scale, static_cast<hipStream_t>(stream));
-    return from_hip(e, "q8_quantize_weight");
+    return done(e, "q8_quantize_weight", stream);
 }
 
 Q4_API q4_status q8_quantize_act(const void *X, const float *smooth_s, int64_t M, int64_t K,
@@ -240,7 +267,7 @@ Q4_API q4_status q8_quantize_act(const void *X, const float *smooth_s, int64_t M
                Q4_ERR_MISALIGNED, "q8_quantize_act: X, Xq and smooth_s must be 16-byte aligned");
     hipError_t e = q4k::launch_q8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, Xq, x_scale,
                                       static_cast<hipStream_t>(stream));
-    return from_hip(e, "q8_quantize_act");
+    return done(e, "q8_quantize_act", stream);
 }
 
 // Preconditions of the INT8 GEMM, checked before anything is launched (also
@@ -272,7 +299,7 @@ Q4_API q4_status w8a8_gemm(const int8_t *Xq, const float *x_scale, const int8_t 
     hipError_t e = q4k::launch_w8a8_gemm(Xq, x_scale, Wq, w_scale, M, N, K,
                                          static_cast<uint16_t *>(Y), acc_out,
                                          static_cast<hipStream_t>(stream));
-    return from_hip(e, "w8a8_gemm");
+    return done(e, "w8a8_gemm", stream);
 }
 
 Q4_API size_t w8a8_workspace_bytes(int64_t M, int64_t K)
@@ -324,10 +351,16 @@ Q4_API q4_status w8a8_linear(const void *X, int64_t M, int64_t N, int64_t K, con
     int8_t *xq = static_cast<int8_t *>(workspace);
     float *sx = reinterpret_cast<float *>(workspace_scales(workspace, M, K));
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    hipError_t e = q4k::launch_q8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
+    // decode sizes: one launch, the quantizer fused into the GEMV
+    hipError_t e = q4k::launch_linear8_fused(static_cast<const uint16_t *>(X), smooth_s, M, N, K,
+                                             reinterpret_cast<const uint8_t *>(Wq), w_scale,
+                                             static_cast<uint16_t *>(Y), acc_out,
+                                             reinterpret_cast<uint8_t *>(xq), sx, false, hs);
+    if (e != hipErrorNotSupported) return done(e, "w8a8_linear", stream);
+    e = q4k::launch_q8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
     if (e == hipSuccess)
         e = q4k::launch_w8a8_gemm(xq, sx, Wq, w_scale, M, N, K, static_cast<uint16_t *>(Y), acc_out, hs);
-    return from_hip(e, "w8a8_linear");
+    return done(e, "w8a8_linear", stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -396,10 +429,15 @@ Q4_API q4_status w8a8_linear_noalloc(const void *X, int64_t M, int64_t N, int64_
     int8_t *xq = static_cast<int8_t *>(ws);
     float *sx = reinterpret_cast<float *>(workspace_scales(ws, M, K));
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    hipError_t e = q4k::launch_q8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
+    hipError_t e = q4k::launch_linear8_fused(static_cast<const uint16_t *>(X), smooth_s, M, N, K,
+                                             reinterpret_cast<const uint8_t *>(Wq), w_scale,
+                                             static_cast<uint16_t *>(Y), acc_out,
+                                             reinterpret_cast<uint8_t *>(xq), sx, false, hs);
+    if (e != hipErrorNotSupported) return done(e, "w8a8_linear_noalloc", stream);
+    e = q4k::launch_q8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
     if (e == hipSuccess)
         e = q4k::launch_w8a8_gemm(xq, sx, Wq, w_scale, M, N, K, static_cast<uint16_t *>(Y), acc_out, hs);
-    return from_hip(e, "w8a8_linear_noalloc");
+    return done(e, "w8a8_linear_noalloc", stream);
 }
 
 Q4_API q4_status fp8_quantize_weight(const void *W, const float *smooth_s, int64_t N, int64_t K,
@@ -414,7 +452,7 @@ Q4_API q4_status fp8_quantize_weight(const void *W, const float *smooth_s, int64
                Q4_ERR_MISALIGNED, "fp8_quantize_weight: W, Wq and smooth_s must be 16-byte aligned");
     hipError_t e = q4k::launch_fp8_weight(static_cast<const uint16_t *>(W), smooth_s, N, K, Wq,
                                           w_scale, static_cast<hipStream_t>(stream));
-    return from_hip(e, "fp8_quantize_weight");
+    return done(e, "fp8_quantize_weight", stream);
 }
 
 Q4_API q4_status fp8_quantize_act(const void *X, const float *smooth_s, int64_t M, int64_t K,
@@ -429,7 +467,7 @@ Q4_API q4_status fp8_quantize_act(const void *X, const float *smooth_s, int64_t 
                Q4_ERR_MISALIGNED, "fp8_quantize_act: X, Xq and smooth_s must be 16-byte aligned");
     hipError_t e = q4k::launch_fp8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, Xq, x_scale,
                                        static_cast<hipStream_t>(stream));
-    return from_hip(e, "fp8_quantize_act");
+    return done(e, "fp8_quantize_act", stream);
 }
 
 // Preconditions of the E4M3 and MXFP4 GEMMs (Xq the E4M3 activation codes,
@@ -461,7 +499,7 @@ Q4_API q4_status fp8_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t
     if (st != Q4_OK || M == 0 || N == 0) return st;
     hipError_t e = q4k::launch_fp8_gemm(Xq, x_scale, Wq, w_scale, M, N, K,
                                         static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
-    return from_hip(e, "fp8_gemm");
+    return done(e, "fp8_gemm", stream);
 }
 
 Q4_API q4_status fp8_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *Wq,
@@ -476,10 +514,13 @@ Q4_API q4_status fp8_linear(const void *X, int64_t M, int64_t N, int64_t K, cons
     uint8_t *xq = static_cast<uint8_t *>(workspace);
     float *sx = reinterpret_cast<float *>(workspace_scales(workspace, M, K));
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    hipError_t e = q4k::launch_fp8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
+    hipError_t e = q4k::launch_linear8_fused(static_cast<const uint16_t *>(X), smooth_s, M, N, K, Wq,
+                                             w_scale, static_cast<uint16_t *>(Y), nullptr, xq, sx, true, hs);
+    if (e != hipErrorNotSupported) return done(e, "fp8_linear", stream);
+    e = q4k::launch_fp8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
     if (e == hipSuccess)
         e = q4k::launch_fp8_gemm(xq, sx, Wq, w_scale, M, N, K, static_cast<uint16_t *>(Y), hs);
-    return from_hip(e, "fp8_linear");
+    return done(e, "fp8_linear", stream);
 }
 
 Q4_API q4_status mxfp4_quantize_weight(const void *W, const float *smooth_s, int64_t N, int64_t K,
@@ -496,7 +537,7 @@ Q4_API q4_status mxfp4_quantize_weight(const void *W, const float *smooth_s, int
                "mxfp4_quantize_weight: W and smooth_s must be 16-byte aligned, codes 4-byte aligned");
     hipError_t e = q4k::launch_mxfp4_quantize(static_cast<const uint16_t *>(W), smooth_s, N, K, codes,
                                               scales, static_cast<hipStream_t>(stream));
-    return from_hip(e, "mxfp4_quantize_weight");
+    return done(e, "mxfp4_quantize_weight", stream);
 }
 
 Q4_API q4_status mxfp4_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t *codes,
@@ -507,7 +548,7 @@ Q4_API q4_status mxfp4_gemm(const uint8_t *Xq, const float *x_scale, const uint8
     if (st != Q4_OK || M == 0 || N == 0) return st;
     hipError_t e = q4k::launch_mxfp4_gemm(Xq, x_scale, codes, scales, M, N, K,
                                           static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
-    return from_hip(e, "mxfp4_gemm");
+    return done(e, "mxfp4_gemm", stream);
 }
 
 Q4_API q4_status mxfp4_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
@@ -522,10 +563,13 @@ Q4_API q4_status mxfp4_linear(const void *X, int64_t M, int64_t N, int64_t K, co
     uint8_t *xq = static_cast<uint8_t *>(workspace);
     float *sx = reinterpret_cast<float *>(workspace_scales(workspace, M, K));
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    hipError_t e = q4k::launch_fp8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
+    hipError_t e = q4k::launch_mxfp4_linear_fused(static_cast<const uint16_t *>(X), smooth_s, M, N, K, codes,
+                                                  scales, static_cast<uint16_t *>(Y), xq, sx, hs);
+    if (e != hipErrorNotSupported) return done(e, "mxfp4_linear", stream);
+    e = q4k::launch_fp8_act(static_cast<const uint16_t *>(X), smooth_s, M, K, xq, sx, hs);
     if (e == hipSuccess)
         e = q4k::launch_mxfp4_gemm(xq, sx, codes, scales, M, N, K, static_cast<uint16_t *>(Y), hs);
-    return from_hip(e, "mxfp4_linear");
+    return done(e, "mxfp4_linear", stream);
 }
 
 Q4_API void nf4_levels(uint16_t *out)
@@ -546,7 +590,7 @@ Q4_API q4_status nf4_quantize(const void *W, int64_t N, int64_t K, uint8_t *code
                "nf4_quantize: W must be 16-byte aligned, codes 4-byte aligned");
     hipError_t e = q4k::launch_nf4_quantize(static_cast<const uint16_t *>(W), N, K, codes, scales,
                                             static_cast<hipStream_t>(stream));
-    return from_hip(e, "nf4_quantize");
+    return done(e, "nf4_quantize", stream);
 }
 
 Q4_API q4_status nf4_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
@@ -564,7 +608,7 @@ Q4_API q4_status nf4_linear(const void *X, int64_t M, int64_t N, int64_t K, cons
                Q4_ERR_MISALIGNED, "nf4_linear: X and codes must be 16-byte aligned, scales 8-byte aligned");
     hipError_t e = q4k::launch_nf4_linear(static_cast<const uint16_t *>(X), M, N, K, codes, scales,
                                           static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
-    return from_hip(e, "nf4_linear");
+    return done(e, "nf4_linear", stream);
 }
 
 Q4_API q4_status smoothquant_scales(const void *Xcal, int64_t R, const void *W, int64_t N,
@@ -581,7 +625,7 @@ Q4_API q4_status smoothquant_scales(const void *Xcal, int64_t R, const void *W, 
     hipError_t e = q4k::launch_smooth_scales(static_cast<const uint16_t *>(Xcal), R,
                                              static_cast<const uint16_t *>(W), N, K, alpha, s,
                                              static_cast<hipStream_t>(stream));
-    return from_hip(e, "smoothquant_scales");
+    return done(e, "smoothquant_scales", stream);
 }
 
 }  // extern "C"

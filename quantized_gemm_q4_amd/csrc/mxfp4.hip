@@ -16,6 +16,7 @@
 #include <type_traits>
 
 #include "q4_internal.hpp"
+#include "row_codes.hpp"
 
 namespace q4k {
 namespace {
@@ -567,7 +568,112 @@ __global__ __launch_bounds__(MXH_WAVES * 64) void mxfp4_gemv16_kernel(
     }
 }
 
+// The decode GEMV above with the per-token E4M3 quantizer of its input fused
+// in (M * K <= 16384): every block quantizes X into LDS (fused_quantize_x,
+// bit for bit fp8_quantize_act) while its weight bytes are in flight, then
+// runs the same 16-row MFMA chain with its X fragments from LDS. Block 0
+// also writes the codes and scales to the caller's workspace.
+template <int SPW, bool HAS_S>
+__global__ __launch_bounds__(MXH_WAVES * 64) void mxfp4_gemv16_fused_kernel(
+    const uint16_t *__restrict__ X, const float *__restrict__ s, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ scales, int M, int N, int K, uint16_t *__restrict__ Y,
+    uint8_t *__restrict__ ws_codes, float *__restrict__ ws_scale)
+{
+    static_assert(SPW == 1 || SPW == 2 || SPW == 4 || SPW == 8, "steps per wavefront");
+    static_assert(MXH_WAVES * 64 == 512, "the fused quantizer takes 512 threads");
+    __shared__ __attribute__((aligned(16))) uint8_t xq[kFusedMaxMK];
+    __shared__ uint32_t rmax[16];
+    __shared__ float rscale[16];
+    __shared__ float red[MXH_WAVES][4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int n0 = (int)blockIdx.x * 16;
+    const uint32_t nrow = (uint32_t)(n0 + l16 < N ? n0 + l16 : N - 1);
+    const int m = l16 < M ? l16 : M - 1;
+    const int s0 = wave * SPW;
+    const uint32_t kh = (uint32_t)K >> 1, ks = (uint32_t)K >> 5;
+    const int nchunks = (M * K) >> 3;
+
+    FusedX fx;
+    fused_load_x<HAS_S>(fx, X, s, nchunks, K);
+    uint32_t sc[SPW];
+    {
+        const uint8_t *sp = scales + nrow * ks + 4u * (uint32_t)s0;
+        if constexpr (SPW == 8) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(sp);
+            const u32x4 b = *reinterpret_cast<const u32x4 *>(sp + 16);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                sc[e] = a[e];
+                sc[4 + e] = b[e];
+            }
+        } else if constexpr (SPW == 4) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(sp);
+#pragma unroll
+            for (int e = 0; e < 4; e++) sc[e] = a[e];
+        } else if constexpr (SPW == 2) {
+            const u32x2 a = *reinterpret_cast<const u32x2 *>(sp);
+            sc[0] = a[0];
+            sc[1] = a[1];
+        } else {
+            sc[0] = *reinterpret_cast<const uint32_t *>(sp);
+        }
+    }
+    intx4 cw[SPW];
+#pragma unroll
+    for (int t = 0; t < SPW; t++)
+        cw[t] = *reinterpret_cast<const intx4 *>(codes + nrow * kh + (uint32_t)(s0 + t) * 64u + 16u * (uint32_t)g);
+    __builtin_amdgcn_sched_barrier(0);   // every load goes out before the quantizer's arithmetic
+    fused_quantize_x<true, HAS_S>(fx, nchunks, M, K, xq, rmax, rscale, ws_codes, ws_scale);
+
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < SPW; t++) {
+        const uint8_t *xp = xq + m * K + (s0 + t) * 128 + 16 * g;
+        const intx4 xlo = *reinterpret_cast<const intx4 *>(xp);
+        const intx4 xhi = *reinterpret_cast<const intx4 *>(xp + 64);
+        const intx8 w8 = __builtin_shufflevector(cw[t], intx4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+        const intx8 a = __builtin_shufflevector(xlo, xhi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const int e = (int)((sc[t] >> (8 * g)) & 0xffu);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w8, a, acc, 4, 0, 0, e, 0, 127);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int r = (int)threadIdx.x >> 6, l = (int)threadIdx.x & 63;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < MXH_WAVES; w++) v += red[w][r][l];
+        const int mm = l & 15;                     // the result's column: X row
+        const int nn = n0 + 4 * (l >> 4) + r;      // its row: weight row
+        if (mm < M && nn < N) Y[(int64_t)mm * N + nn] = f2h(v * rscale[mm]);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_mxfp4_linear_fused(const uint16_t *X, const float *s, int64_t M, int64_t N, int64_t K,
+                                     const uint8_t *codes, const uint8_t *scales, uint16_t *Y,
+                                     uint8_t *ws_codes, float *ws_scale, hipStream_t st)
+{
+    if (M < 1 || M > 16 || M * K > kFusedMaxMK || K % 1024 != 0 || K > 8192 ||
+        N * K >= (int64_t)1 << 31 || N < 1 || (reinterpret_cast<uintptr_t>(scales) & 15) != 0)
+        return hipErrorNotSupported;
+    const int blocks = (int)((N + 15) / 16);
+    auto go = [&](auto k_s, auto k_n) {
+        if (s) k_s<<<blocks, MXH_WAVES * 64, 0, st>>>(X, s, codes, scales, (int)M, (int)N, (int)K, Y, ws_codes, ws_scale);
+        else k_n<<<blocks, MXH_WAVES * 64, 0, st>>>(X, s, codes, scales, (int)M, (int)N, (int)K, Y, ws_codes, ws_scale);
+    };
+    switch (K / 1024) {
+    case 1: go(mxfp4_gemv16_fused_kernel<1, true>, mxfp4_gemv16_fused_kernel<1, false>); break;
+    case 2: go(mxfp4_gemv16_fused_kernel<2, true>, mxfp4_gemv16_fused_kernel<2, false>); break;
+    case 4: go(mxfp4_gemv16_fused_kernel<4, true>, mxfp4_gemv16_fused_kernel<4, false>); break;
+    case 8: go(mxfp4_gemv16_fused_kernel<8, true>, mxfp4_gemv16_fused_kernel<8, false>); break;
+    default: return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_mxfp4_quantize(const uint16_t *W, const float *s, int64_t N, int64_t K,
                                  uint8_t *codes, uint8_t *scales, hipStream_t st)

@@ -90,6 +90,14 @@ hipError_t launch_w4a16_gemv_awq(const uint16_t *X, int64_t M, int64_t N, int64_
 hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
                             const float *sw, int64_t M, int64_t N, int64_t K, uint16_t *Y,
                             int32_t *acc_out, hipStream_t st);
+// The W8A8 (fp8 = false) or E4M3 (fp8 = true) decode layer with the per-token
+// quantizer fused in: codes and scales bit for bit those of the row
+// quantizer, also written to ws_codes [M, K] / ws_scale [M] by one block.
+// hipErrorNotSupported unless M <= 16, M * K <= 16384, K % 1024 == 0 and
+// K <= 8192; acc_out (INT8 only) as for launch_w8a8_gemm.
+hipError_t launch_linear8_fused(const uint16_t *X, const float *s, int64_t M, int64_t N, int64_t K,
+                                const uint8_t *Wq, const float *sw, uint16_t *Y, int32_t *acc_out,
+                                uint8_t *ws_codes, float *ws_scale, bool fp8, hipStream_t st);
 // FP8 E4M3 path: per-row quantizers (codes as bytes) and the GEMM (K % 128
 // == 0; hipErrorNotSupported otherwise).
 hipError_t launch_fp8_weight(const uint16_t *W, const float *s, int64_t N, int64_t K, uint8_t *Wq,
@@ -105,6 +113,11 @@ hipError_t launch_mxfp4_quantize(const uint16_t *W, const float *s, int64_t N, i
 hipError_t launch_mxfp4_gemm(const uint8_t *Xq, const float *sx, const uint8_t *codes,
                              const uint8_t *scales, int64_t M, int64_t N, int64_t K, uint16_t *Y,
                              hipStream_t st);
+// The MXFP4 decode layer with the per-token E4M3 quantizer fused in (as
+// launch_linear8_fused; also needs 16-byte aligned scales).
+hipError_t launch_mxfp4_linear_fused(const uint16_t *X, const float *s, int64_t M, int64_t N, int64_t K,
+                                     const uint8_t *codes, const uint8_t *scales, uint16_t *Y,
+                                     uint8_t *ws_codes, float *ws_scale, hipStream_t st);
 // NF4 weights: the level table (fp16 bit patterns, ascending), the quantizer
 // (codes [N, K/2], fp32 scales [N, K/64]) and the decode GEMV over row chunks
 // of X (K % 128 == 0; hipErrorNotSupported otherwise).

@@ -14,6 +14,7 @@
 #include <type_traits>
 
 #include "q4_internal.hpp"
+#include "row_codes.hpp"
 
 namespace q4k {
 namespace {
@@ -252,37 +253,6 @@ __device__ __forceinline__ void load_row_chunk(const uint16_t *__restrict__ row,
     }
 }
 
-// Row formats: INT8 codes rint(v / scale) clipped to +-127, or FP8 E4M3
-// codes of v / scale (the nearest E4M3 value, ties to even, sign kept on
-// zero; the hardware conversion v_cvt_pk_fp8_f32 rounds to nearest even and
-// the quotient is clamped to +-448 first, so nothing saturates in it). The
-// scale is max |v| / 127 or max |v| / 448 (Quantization operators guide
-// §2.1, §4.2).
-template <bool FP8> constexpr float kRowMax = FP8 ? 448.0f : 127.0f;
-
-// four quotients -> four code bytes (quotient i in byte i)
-template <bool FP8>
-__device__ __forceinline__ uint32_t row_codes4(float q0, float q1, float q2, float q3)
-{
-    if constexpr (FP8) {
-        auto c = [](float q) { return fminf(fmaxf(q, -448.0f), 448.0f); };
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(q0), c(q1), 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(c(q2), c(q3), w, true);
-        return (uint32_t)w;
-    } else {
-        // clamp to [-127, 127] (integer bounds, so clamping before rounding
-        // is the same as after), then 1.5 * 2^23 + q rounds q to the nearest
-        // integer, ties to even, and leaves it (two's complement) in the low
-        // byte of the sum's bits; three byte permutes pack the four codes
-        auto c = [](float q) {
-            return __builtin_bit_cast(uint32_t, fminf(fmaxf(q, -127.0f), 127.0f) + 12582912.0f);
-        };
-        const uint32_t p01 = __builtin_amdgcn_perm(c(q1), c(q0), 0x0c0c0400u);
-        const uint32_t p23 = __builtin_amdgcn_perm(c(q3), c(q2), 0x0c0c0400u);
-        return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
-    }
-}
-
 template <bool FP8>
 __device__ __forceinline__ u32x2 row_codes8(const float v[8], float scale)
 {
@@ -338,24 +308,6 @@ __global__ __launch_bounds__(kThreads) void q8_rows_generic_kernel(const uint16_
         }
         if (threadIdx.x == 0) scale_out[r] = scale;
     }
-}
-
-// Quotients without a division. For binary32 (or binary16-valued) a and a
-// binary32 b the exact quotient a / b never lies on the midpoint between two
-// binary32 neighbours, and when it does not it is at least 2^-49 (relative)
-// away from one: with a = A 2^ea (A < 2^24) and a midpoint m (25 significant
-// bits), a - m b is a nonzero multiple of 2^(ea - 25), so at least 2^-49 of
-// a. So a product a * r in fp64 with r within 2^-50 of 1 / b (relative; the
-// fp64 rounding of the product adds 2^-53) rounds to the same binary32 value
-// as a / b:
-// fl32(fl64(a * r)) = fl32(a / b). r is the hardware's fp64 reciprocal
-// refined by two Newton steps (each squares the relative error; rounding
-// keeps it near 2^-53). b must be finite and nonzero.
-__device__ __forceinline__ double recip64(double b)
-{
-    double r = __builtin_amdgcn_rcp(b);
-    r = fma(fma(-b, r, 1.0), r, r);
-    return fma(fma(-b, r, 1.0), r, r);
 }
 
 // max over each half-wavefront (lanes 0-31 and 32-63 each end with their own):

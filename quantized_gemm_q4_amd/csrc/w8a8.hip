@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include "q4_internal.hpp"
+#include "row_codes.hpp"
 
 namespace q4k {
 namespace {
@@ -547,7 +548,137 @@ __global__ __launch_bounds__(I8G_WAVES * 64) void w8a8_gemv16_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode with the activation quantizer fused in (M * K <= 16384, M <= 16,
+// K % 1024 == 0, K <= 8192): the separate per-token pass is a launch of its
+// own for a few KB of X, so every block quantizes X itself. A block issues
+// its X loads (one 8-element chunk per thread and pass, row-major, with the
+// smoothing factors), then its weight loads, then forms x' = x / s, the
+// per-row maxima (LDS max on the float bit patterns, which order as the
+// values for x' >= 0), the scales max / 127 (or / 448) by IEEE division and
+// the codes rint(x' / scale) -- the arithmetic of the row quantizer, so the
+// codes and scales are bit for bit those of q8_quantize_act /
+// fp8_quantize_act -- into LDS, while its weight bytes are on the way. The
+// decode GEMV then reads its X fragments from LDS. Block 0 also writes the
+// codes and scales to the caller's workspace, which therefore holds what the
+// two-launch form leaves there.
+template <bool FP8, bool HAS_S, int SPW>
+__global__ __launch_bounds__(512) void w8a8_gemv16_fused_kernel(
+    const uint16_t *__restrict__ X, const float *__restrict__ s, const uint8_t *__restrict__ Wq,
+    const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y,
+    int32_t *__restrict__ acc_out, uint8_t *__restrict__ ws_codes, float *__restrict__ ws_scale)
+{
+    static_assert(SPW == 1 || SPW == 2 || SPW == 4 || SPW == 8, "steps per wavefront");
+    __shared__ __attribute__((aligned(16))) uint8_t xq[kFusedMaxMK];
+    __shared__ uint32_t rmax[16];
+    __shared__ float rscale[16];
+    __shared__ int red[8][4][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int n0 = (int)blockIdx.x * 16;
+    const int64_t nrow = n0 + l16 < N ? n0 + l16 : N - 1;
+    const int m = l16 < M ? l16 : M - 1;
+    const int s0 = wave * SPW;
+    const int nchunks = (M * K) >> 3;
+
+    FusedX fx;
+    fused_load_x<HAS_S>(fx, X, s, nchunks, K);
+    intx4 wlo[SPW], whi[SPW];
+#pragma unroll
+    for (int t = 0; t < SPW; t++) {
+        const uint8_t *wp = Wq + nrow * K + (s0 + t) * 128 + 16 * g;
+        wlo[t] = *reinterpret_cast<const intx4 *>(wp);
+        whi[t] = *reinterpret_cast<const intx4 *>(wp + 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load goes out before the quantizer's arithmetic
+    fused_quantize_x<FP8, HAS_S>(fx, nchunks, M, K, xq, rmax, rscale, ws_codes, ws_scale);
+
+    // 4. the decode GEMV with its X fragments from LDS
+    intx4 xlo[SPW], xhi[SPW];
+#pragma unroll
+    for (int t = 0; t < SPW; t++) {
+        const uint8_t *xp = xq + m * K + (s0 + t) * 128 + 16 * g;
+        xlo[t] = *reinterpret_cast<const intx4 *>(xp);
+        xhi[t] = *reinterpret_cast<const intx4 *>(xp + 64);
+    }
+    if constexpr (FP8) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < SPW; t++) {
+            const intx8 w8 = __builtin_shufflevector(wlo[t], whi[t], 0, 1, 2, 3, 4, 5, 6, 7);
+            const intx8 a8 = __builtin_shufflevector(xlo[t], xhi[t], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w8, a8, acc, 0, 0, 0, 127, 0, 127);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const float pr = acc[r];   // through a scalar: bit_cast of a vector element reads element 0
+            red[wave][r][lane] = __builtin_bit_cast(int, pr);
+        }
+    } else {
+        intx4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < SPW; t++) {
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo[t], xlo[t], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi[t], xhi[t], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r++) red[wave][r][lane] = acc[r];
+    }
+    __syncthreads();
+    if (tid < 256) {
+        const int r = tid >> 6, l = tid & 63;
+        const int mm = l & 15;                     // the result's column: X row
+        const int nn = n0 + 4 * (l >> 4) + r;      // its row: weight row
+        float f;
+        int vi = 0;
+        if constexpr (FP8) {
+            float vf = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 8; w++) vf += __builtin_bit_cast(float, red[w][r][l]);
+            f = vf;
+        } else {
+#pragma unroll
+            for (int w = 0; w < 8; w++) vi += red[w][r][l];
+            f = (float)vi;
+        }
+        if (mm < M && nn < N) {
+            if (!FP8 && acc_out) acc_out[(int64_t)mm * N + nn] = vi;
+            f = f * rscale[mm];
+            f = f * sw[nn];
+            asm volatile("" : "+v"(f));   // two fp32 roundings, then fp16 (no fused multiply-convert)
+            Y[(int64_t)mm * N + nn] = f2h(f);
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_linear8_fused(const uint16_t *X, const float *s, int64_t M, int64_t N, int64_t K,
+                                const uint8_t *Wq, const float *sw, uint16_t *Y, int32_t *acc_out,
+                                uint8_t *ws_codes, float *ws_scale, bool fp8, hipStream_t st)
+{
+    if (M < 1 || M > 16 || M * K > kFusedMaxMK || K % 1024 != 0 || K > 8192 ||
+        N * K >= (int64_t)1 << 31 || N < 1)
+        return hipErrorNotSupported;
+    const int blocks = (int)((N + 15) / 16);
+    auto go = [&](auto kernel) {
+        kernel<<<blocks, 512, 0, st>>>(X, s, Wq, sw, (int)M, (int)N, (int)K, Y, acc_out, ws_codes, ws_scale);
+    };
+#define Q4_FUSED_K(F8, HS)                                                                          \
+    do {                                                                                            \
+        switch (K / 1024) {                                                                         \
+        case 1: go(w8a8_gemv16_fused_kernel<F8, HS, 1>); break;                                     \
+        case 2: go(w8a8_gemv16_fused_kernel<F8, HS, 2>); break;                                     \
+        case 4: go(w8a8_gemv16_fused_kernel<F8, HS, 4>); break;                                     \
+        case 8: go(w8a8_gemv16_fused_kernel<F8, HS, 8>); break;                                     \
+        default: return hipErrorNotSupported;                                                       \
+        }                                                                                           \
+    } while (0)
+    if (fp8) { if (s) Q4_FUSED_K(true, true); else Q4_FUSED_K(true, false); }
+    else { if (s) Q4_FUSED_K(false, true); else Q4_FUSED_K(false, false); }
+#undef Q4_FUSED_K
+    return hipGetLastError();
+}
 
 hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq, const float *sw,
                             int64_t M, int64_t N, int64_t K, uint16_t *Y, int32_t *acc_out,

@@ -298,3 +298,25 @@ def test_quantize_out_must_match(orc):
         q4.q4_quantize_pack(W, g=32, out=(good[0], good[1].float(), good[2]))
     with pytest.raises(ValueError):
         q4.q4_quantize_pack(W, g=32, out=(good[0].cpu(), good[1], good[2]))
+
+
+def test_debug_mode_synchronises_and_logs():
+    """Q4_DEBUG=1: every call waits for its stream and logs itself to stderr
+    (run in a child process: the mode is read when the library loads)."""
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import torch, quantized_gemm_q4_amd as q4\n"
+        "W = torch.randn(64, 256, device='cuda').half()\n"
+        "c, s, z = q4.q4_quantize_pack(W)\n"
+        "Y = q4.w4a16_linear(torch.randn(3, 256, device='cuda').half(), c, s, z)\n"
+        "print('rows', Y.shape[0])\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, Q4_DEBUG="1", PYTHONPATH=root)
+    proc = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True,
+                          text=True, timeout=120)
+    assert proc.returncode == 0, proc.stderr[-2000:]
+    assert "rows 3" in proc.stdout
+    assert "[q4] q4_quantize_pack: ok" in proc.stderr
+    assert "[q4] w4a16_linear: ok" in proc.stderr
