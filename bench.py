@@ -451,6 +451,18 @@ def main():
                             "bytes": nb}
             del cps, codes, sc
         extra["nf4_decode"] = res
+        # the prefill shape (M = 2048, K = 4096, N = 11008) on the NF4 large-M GEMM
+        w = workloads.prefill()
+        codes, sc = q4.nf4_quantize(gpu(w["W"]))
+        X = gpu(w["X"])
+        Y = torch.empty((2048, 11008), dtype=torch.float16, device=dev)
+        for _ in range(3):
+            q4.nf4_linear(X, codes, sc, out=Y)
+        tp = timed(lambda i: q4.nf4_linear(X, codes, sc, out=Y), 30) / 30
+        flops = 2 * 2048 * 11008 * 4096
+        extra["nf4_prefill"] = {"shape": [2048, 11008, 4096], "us": tp * 1e6, "TFLOP/s": flops / tp / 1e12,
+                                "frac_mfma_fp16": flops / tp / 1e12 / FP16_MFMA_PEAK_TFLOPS}
+        del codes, sc, X, Y
         torch.cuda.empty_cache()
 
     # ---- known-size copy: scales the HBM byte counters (profiling runs only) -

@@ -449,13 +449,17 @@ Q4_API q4_status mxfp4_linear(const void *X, int64_t M, int64_t N, int64_t K,
  *   W fp16 [N, K] (16-byte aligned, K % 64 == 0); codes u8 [N, K/2] output,
  *   two codes per byte along K (even k in the low nibble), 4-byte aligned;
  *   scales fp32 [N, K/64] output. Codes and scales are bit-exact.
- * nf4_linear -- Y = X * W_hat^T, fp32 accumulation, fp16 output; the levels
- *   enter the matrix cores exactly and each 64-block's fp32 partial sum is
- *   multiplied by its scale. Built for decode: X is processed in row chunks
- *   of at most 16 (fewer when K is large), each chunk reading the whole
- *   weight once. X fp16 [M, K] and codes 16-byte aligned; scales 8-byte
- *   aligned; K % 128 == 0 and at most 28672; Y fp16 [M, N] output.
- * Accuracy: as for w4a16_linear.
+ * nf4_linear -- Y = X * W_hat^T, fp32 accumulation, fp16 output. Up to 48
+ *   rows (decode): the levels enter the matrix cores exactly and each
+ *   64-block's fp32 partial sum is multiplied by its scale; X is processed in
+ *   row chunks of at most 16 (fewer when K is large), each chunk reading the
+ *   whole weight once. Above 48 rows (prefill): a tiled GEMM that reads the
+ *   weight once per tile of rows, with w_hat = level * scale rounded once to
+ *   fp16 as the matrix-core operand. X fp16 [M, K] and codes 16-byte aligned;
+ *   scales 8-byte aligned; K % 128 == 0 and at most 28672; Y fp16 [M, N]
+ *   output.
+ * Accuracy: as for w4a16_linear (decode: as its GEMV; above 48 rows: as its
+ *   large-M GEMM, one fp16 rounding of w_hat).
  * Errors: INVALID_ARG, UNSUPPORTED (K too large for the LDS), MISALIGNED, HIP.
  * -------------------------------------------------------------------------- */
 Q4_API void nf4_levels(uint16_t *out);

@@ -9,6 +9,7 @@
 
 #include "../../include/q4.h"
 #include "q4_internal.hpp"
+#include "nf4_lut.hpp"
 
 namespace {
 

@@ -118,12 +118,15 @@ hipError_t launch_mxfp4_gemm(const uint8_t *Xq, const float *sx, const uint8_t *
 hipError_t launch_mxfp4_linear_fused(const uint16_t *X, const float *s, int64_t M, int64_t N, int64_t K,
                                      const uint8_t *codes, const uint8_t *scales, uint16_t *Y,
                                      uint8_t *ws_codes, float *ws_scale, hipStream_t st);
-// NF4 weights: the level table (fp16 bit patterns, ascending), the quantizer
+// NF4 weights (the level table is kNf4Levels in nf4_lut.hpp): the quantizer
 // (codes [N, K/2], fp32 scales [N, K/64]) and the decode GEMV over row chunks
 // of X (K % 128 == 0; hipErrorNotSupported otherwise).
-extern const uint16_t kNf4Levels[16];
 hipError_t launch_nf4_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *codes, float *scales,
                                hipStream_t st);
+// The NF4 form of the large-M W4A16 GEMM (tiles of 256 rows, levels times
+// scales dequantized into LDS; K % 128 == 0); hipErrorNotSupported otherwise.
+hipError_t launch_nf4_gemm(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                          const float *scales, uint16_t *Y, hipStream_t st);
 hipError_t launch_nf4_linear(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
                              const float *scales, uint16_t *Y, hipStream_t st);
 

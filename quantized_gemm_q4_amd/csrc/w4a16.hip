@@ -19,6 +19,7 @@
 // never expanded in memory.
 #include <cstdlib>
 
+#include "nf4_lut.hpp"
 #include "w4a16_dequant.hpp"
 
 namespace q4k {
@@ -875,7 +876,24 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int p, uint32_t zad
     return __builtin_bit_cast(uint32_t, v * __builtin_bit_cast(half2v, s2));
 }
 
-template <int NU, int WM, bool ASYM>
+// NF4 form (NF4 = true): the codes index the 16 NF4 levels (nf4_dequant8), the
+// scales are fp32, one per 64 weights (gshift = 1: two 32-wide steps), and
+// each dequantized weight is f2h(level * scale): the fp32 product of the
+// exact level and scale, rounded to fp16.
+__device__ __forceinline__ u32x4 nf4_scaled8(uint32_t w, float sf)
+{
+    const u32x4 lv = nf4_dequant8(w);
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const uint32_t d = lv[p];
+        const float lo = h2f((uint16_t)(d & 0xffffu)) * sf, hi = h2f((uint16_t)(d >> 16)) * sf;
+        r[p] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
+    }
+    return r;
+}
+
+template <int NU, int WM, bool ASYM, bool NF4 = false>
 __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
     const uint16_t *__restrict__ X, int M, int N, int K, int gshift,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
@@ -925,7 +943,8 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
     auto load_w = [&](int k, int q) {
         const uint32_t grp = (uint32_t)k >> gshift;
         wc[q] = *reinterpret_cast<const u32x4 *>(codes + coff + (uint32_t)k * 16u);
-        ws[q] = scales[soff + grp];
+        if (NF4) ws[q] = reinterpret_cast<const uint32_t *>(scales)[soff + grp];   // fp32 bits
+        else ws[q] = scales[soff + grp];
         if (ASYM) wz[q] = zeros[zoff + (grp >> 1)];   // nibble picked at use: no wait here
     };
 
@@ -980,7 +999,11 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
             for (int q = 0; q < PPF; q++) {
                 const int pr = f * PPF + q;
                 if (pr < 16) {
-                    out[pr & 3] = dequant_pair(wc[wq][pr >> 2], pr & 3, zadd, s2);
+                    if (NF4) {
+                        if ((pr & 3) == 0) out = nf4_scaled8(wc[wq][pr >> 2], __builtin_bit_cast(float, ws[wq]));
+                    } else {
+                        out[pr & 3] = dequant_pair(wc[wq][pr >> 2], pr & 3, zadd, s2);
+                    }
                     if ((pr & 3) == 3)
                         *reinterpret_cast<u32x4 *>(dq_row + dq_cs * ((pr >> 2) ^ dq_swz)) = out;
                 }
@@ -1009,8 +1032,9 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
         unsigned char *const row = sb[0] + dq_off;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const u32x4 out = {dequant_pair(wc[0][i], 0, zadd, s2), dequant_pair(wc[0][i], 1, zadd, s2),
-                               dequant_pair(wc[0][i], 2, zadd, s2), dequant_pair(wc[0][i], 3, zadd, s2)};
+            const u32x4 out = NF4 ? nf4_scaled8(wc[0][i], __builtin_bit_cast(float, ws[0]))
+                                  : u32x4{dequant_pair(wc[0][i], 0, zadd, s2), dequant_pair(wc[0][i], 1, zadd, s2),
+                                          dequant_pair(wc[0][i], 2, zadd, s2), dequant_pair(wc[0][i], 3, zadd, s2)};
             *reinterpret_cast<u32x4 *>(row + dq_cs * (i ^ dq_swz)) = out;
         }
     }
@@ -1156,6 +1180,34 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t 
 }
 
 }  // namespace
+
+hipError_t launch_nf4_gemm(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                          const float *scales, uint16_t *Y, hipStream_t st)
+{
+    if (M < 1 || N < 1 || K % 128 != 0 || M * K * 2 >= ((int64_t)1 << 31) || N * (K / 2) >= ((int64_t)1 << 31))
+        return hipErrorNotSupported;
+    const int m = (int)M, n = (int)N, k = (int)K;
+    const int tiles_m = (m + GBM - 1) / GBM;
+    int best = gemm_nu_override();
+    if (best == 0) {   // the tile width rule of launch_w4a16
+        int64_t best_cost = 0;
+        const int nus[3] = {4, 8, 11};
+        for (int c = 0; c < 3; c++) {
+            const int64_t tiles = (int64_t)tiles_m * ((n + 32 * nus[c] - 1) / (32 * nus[c]));
+            const int64_t cost = (tiles + 255) / 256 * (nus[c] + 2);
+            if (best == 0 || cost < best_cost) { best = nus[c]; best_cost = cost; }
+        }
+    }
+    const int tiles = tiles_m * ((n + 32 * best - 1) / (32 * best));
+    const uint16_t *sc = reinterpret_cast<const uint16_t *>(scales);
+    auto launch = [&](auto kernel, int threads) {
+        kernel<<<tiles, threads, 0, st>>>(X, m, n, k, 1, codes, sc, nullptr, tiles_m, Y);
+    };
+    if (best == 4) launch(w4a16_gemm_kernel<4, 2, false, true>, 256);
+    else if (best == 8) launch(w4a16_gemm_kernel<8, 2, false, true>, 256);
+    else launch(w4a16_gemm_kernel<11, 1, false, true>, 512);
+    return hipGetLastError();
+}
 
 hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,
                         const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,

@@ -8,7 +8,7 @@ import pytest
 
 import quantized_gemm_q4_amd as q4
 import workloads
-from parity import check_gemm, gpu, host
+from parity import check_gemm, gpu, host, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -71,3 +71,43 @@ def test_decode_workload(orc, N):
     Y = host(q4.nf4_linear(gpu(w["X"]), codes, sc))
     Yref, B = orc.nf4_ref(w["X"], codes_ref, sc_ref)
     check_gemm(Y, Yref, B, f"nf4 decode N={N}")
+
+
+# M > 48: the large-M GEMM with the NF4 weight dequantized (level * block
+# scale, rounded once to fp16) into LDS, at each tile width, ragged in M and N.
+@pytest.mark.parametrize("nu", [4, 8, 11])
+@pytest.mark.parametrize("M,N,K", [(49, 100, 256), (300, 1000, 768), (513, 383, 1280), (256, 352, 128)])
+def test_large_m_shapes(orc, monkeypatch, nu, M, N, K):
+    monkeypatch.setenv("Q4_GEMM_NU", str(nu))
+    run_linear(orc, M, N, K, M * 5 + N + K + nu)
+
+
+@pytest.mark.parametrize("nu", [4, 11])
+def test_large_m_one_hot(orc, monkeypatch, nu):
+    """X[m, k(m)] = 1: Y[m, n] is the dequantized weight w_hat[n, k(m)] as the
+    GEMM forms it (the fp32 product of the level and the block scale, rounded
+    to fp16), bit for bit: pins the level lookup, the block-scale indexing and
+    the k order."""
+    monkeypatch.setenv("Q4_GEMM_NU", str(nu))
+    M, N, K = 300, 385, 512
+    rng = np.random.default_rng(nu)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    codes, sc = orc.nf4_quantize(W)
+    kk = (np.arange(M) * 7 + 3) % K
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), kk] = 1.0
+    Y = host(q4.nf4_linear(gpu(X), gpu(codes), gpu(sc)))
+    lv = orc.nf4_levels().astype(np.float32)
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(N, K)
+    w32 = lv[nib] * np.repeat(sc, 64, axis=1)          # fp32 products (exact level x fp32 scale)
+    expect = w32[:, kk].T.astype(np.float16)
+    assert np.array_equal(Y.view(np.uint16), expect.view(np.uint16))
+
+
+def test_prefill_shape_sampled(orc):
+    w = workloads.prefill()
+    codes, sc = q4.nf4_quantize(gpu(w["W"]))
+    Y = host(q4.nf4_linear(gpu(w["X"]), codes, sc))
+    rows = sample_rows(w["X"].shape[0])
+    Yref, B = orc.nf4_ref(w["X"], host(codes), host(sc), rows=rows)
+    check_gemm(Y[rows], Yref, B, "nf4 prefill shape")
