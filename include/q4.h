@@ -452,15 +452,17 @@ Q4_API q4_status mxfp4_linear(const void *X, int64_t M, int64_t N, int64_t K,
  * nf4_linear -- Y = X * W_hat^T, fp32 accumulation, fp16 output. Up to 48
  *   rows (decode): the levels enter the matrix cores exactly and each
  *   64-block's fp32 partial sum is multiplied by its scale; X is processed in
- *   row chunks of at most 16 (fewer when K is large), each chunk reading the
- *   whole weight once. Above 48 rows (prefill): a tiled GEMM that reads the
- *   weight once per tile of rows, with w_hat = level * scale rounded once to
- *   fp16 as the matrix-core operand. X fp16 [M, K] and codes 16-byte aligned;
- *   scales 8-byte aligned; K % 128 == 0 and at most 28672; Y fp16 [M, N]
- *   output.
+ *   passes of at most 16 rows (at most 8 when 9 rows of X do not fit the
+ *   LDS), each pass reading the whole weight once. Above 48 rows (prefill): a
+ *   tiled GEMM that reads the weight once per tile of rows, with
+ *   w_hat = level * scale rounded once to fp16 as the matrix-core operand
+ *   (the scale is taken as fp16, which every scale nf4_quantize writes is).
+ *   X fp16 [M, K] and codes 16-byte aligned; scales 8-byte aligned;
+ *   K % 128 == 0; Y fp16 [M, N] output.
  * Accuracy: as for w4a16_linear (decode: as its GEMV; above 48 rows: as its
  *   large-M GEMM, one fp16 rounding of w_hat).
- * Errors: INVALID_ARG, UNSUPPORTED (K too large for the LDS), MISALIGNED, HIP.
+ * Errors: INVALID_ARG, UNSUPPORTED (N * K / 2 >= 2^32 - 256: the weight
+ *   outgrows the kernels' 32-bit offsets), MISALIGNED, HIP.
  * -------------------------------------------------------------------------- */
 Q4_API void nf4_levels(uint16_t *out);
 Q4_API q4_status nf4_quantize(const void *W, int64_t N, int64_t K, uint8_t *codes, float *scales,

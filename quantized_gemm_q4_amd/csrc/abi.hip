@@ -597,10 +597,9 @@ Q4_API q4_status nf4_quantize(const void *W, int64_t N, int64_t K, uint8_t *code
 Q4_API q4_status nf4_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
                             const float *scales, void *Y, void *stream)
 {
-    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K % 128 == 0,
+    Q4_REQUIRE(M >= 0 && N >= 0 && K > 0 && M <= kIntMax && N <= kIntMax && K <= kIntMax && K % 128 == 0,
                Q4_ERR_INVALID_ARG, "nf4_linear: bad shape M=%lld N=%lld K=%lld (K a multiple of 128)",
                (long long)M, (long long)N, (long long)K);
-    Q4_REQUIRE(K <= 28672, Q4_ERR_UNSUPPORTED, "nf4_linear: K=%lld larger than 28672", (long long)K);
     Q4_REQUIRE(N * (K / 2) < 0xFFFFFF00LL, Q4_ERR_UNSUPPORTED, "nf4_linear: weight of %lld x %lld too large",
                (long long)N, (long long)K);
     if (M == 0 || N == 0) return ok();

@@ -96,28 +96,159 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const uint16_t *__res
 }
 
 // ---------------------------------------------------------------------------
-// Decode GEMV (M <= 16 rows of X per launch). A block of 8 wavefronts owns 16
-// output channels and all of K; wavefront w takes the 128-wide k-blocks
-// w, w + 8, w + 16, ..., four at a time: the four k-blocks' code runs (lane
-// (r16, q): row r16, k = 32q .. 32q + 31 of the k-block, 16 bytes) and block
-// scales are issued together, then computed. X (M rows, natural order) is
-// staged in LDS by the whole block. MFMA t of a k-block pairs code dword t
-// with X[m][32q + 8t .. + 7]. A k-block spans two 64-blocks with their own
-// scales while an MFMA sums over all four lane groups q, so each k-block runs
-// two MFMA chains: lanes q < 2 feed the first with their levels and the
-// second with zeros, lanes q >= 2 the other way round; the chains' fp32
-// results are scaled by the column's two block scales. The wavefronts'
-// partial sums meet in LDS.
-constexpr int NF4_WAVES = 8, NF4_PF = 4;
+// Decode GEMVs (M <= 16 rows of X per launch). A block of 8 wavefronts owns
+// 16 output channels and all of K; wavefront w takes the 128-wide k-blocks
+// w, w + 8, w + 16, ..., four at a time (a batch): the batch's code runs
+// (lane (r16, q): column r16, k = 32q .. 32q + 31 of the k-block, 16 bytes)
+// and block scales are issued together, then computed. MFMA t of a k-block
+// pairs code dword t with X[.][32q + 8t .. + 7]. X sits in LDS with each run
+// of 8 k stored in the order the lookup yields the levels (0, 2, 4, 6, 1, 3,
+// 5, 7), so the fragments pair up without a shuffle. A k-block spans two
+// 64-blocks (lanes q < 2 and q >= 2) with their own scales while an MFMA sums
+// over all four lane groups, so the two halves must land in different
+// accumulators. A lane that feeds zeros reads them from a zero run in LDS
+// (its k-block stride set to 0). The wavefronts' partial sums meet in LDS.
+constexpr int NF4_WAVES = 8, NF4_PF = 4, NF4_ZERO_BYTES = NF4_WAVES * 64;   // zero runs: one of 64 B per wavefront
+constexpr size_t NF4_RED_BYTES = (size_t)NF4_WAVES * 4 * 64 * 4;
 
+__device__ __forceinline__ u32x4 nf4_permute_x(u32x4 v)   // x0..x7 -> x0 x2 x4 x6 x1 x3 x5 x7
+{
+    return u32x4{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+                 __builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+}
+
+__device__ __forceinline__ void nf4_load_batch(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
+                                               uint32_t nrow, uint32_t kh, uint32_t ks, int KB, int kb0, int q,
+                                               u32x4 (&cw)[NF4_PF], u32x2 (&sc)[NF4_PF])
+{
+#pragma unroll
+    for (int p = 0; p < NF4_PF; p++) {
+        const int kb = kb0 + p * NF4_WAVES;
+        const int kc = kb < KB ? kb : KB - 1;   // past the end: a valid k-block, not used
+        sc[p] = *reinterpret_cast<const u32x2 *>(scales + (nrow * ks + (uint32_t)kc * 2u));
+        cw[p] = *reinterpret_cast<const u32x4 *>(codes + (nrow * kh + (uint32_t)kc * 64u + (uint32_t)q * 16u));
+    }
+}
+
+__device__ __forceinline__ void nf4_reduce_store(float *red, const floatx4 &acc, bool paired, int M, int N,
+                                                 uint16_t *__restrict__ Y)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int r = 0; r < 4; r++) red[(wave * 4 + r) * 64 + lane] = acc[r];
+    __syncthreads();
+    if (paired) {
+        // output row 2 (l >> 4) + j is the sum of D rows 4 (l >> 4) + 2j, + 2j + 1
+        if (threadIdx.x < 128) {
+            const int j = threadIdx.x >> 6, l = threadIdx.x & 63;
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NF4_WAVES; w++) v += red[(w * 4 + 2 * j) * 64 + l] + red[(w * 4 + 2 * j + 1) * 64 + l];
+            const int m = 2 * (l >> 4) + j;
+            const int nn = blockIdx.x * 16 + (l & 15);
+            if (m < M && nn < N) Y[(int64_t)m * N + nn] = f2h(v);
+        }
+    } else if (threadIdx.x < 256) {
+        const int r = threadIdx.x >> 6, l = threadIdx.x & 63;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NF4_WAVES; w++) v += red[(w * 4 + r) * 64 + l];
+        const int m = 4 * (l >> 4) + r;
+        const int nn = blockIdx.x * 16 + (l & 15);
+        if (m < M && nn < N) Y[(int64_t)m * N + nn] = f2h(v);
+    }
+}
+
+// M <= 8: A-row 2m + h carries X[m] in the lanes of half h and zeros in the
+// others, so D row 2m + h holds half h of row m's sum: one MFMA per 32 k,
+// each row scaled by its half's block scale. Each wavefront fetches the X
+// runs of its own batch (lane l, load i: row i, k-block kb0 + 8 (l >> 4),
+// 16 bytes at 8 (l & 15)) before the batch's codes, so they land first, and
+// writes them to an LDS region of its own ([row][k-block of the batch][128
+// k], M KB): no block barrier stands between the loads and the compute, and
+// K is not bounded by the LDS.
+template <int MAXR>   // rows per pass at most (1, 2, 4, 8): the X registers per lane
+__global__ __launch_bounds__(NF4_WAVES * 64) void nf4_gemv_paired_kernel(const uint16_t *__restrict__ X, int M,
+                                                                         int N, int K,
+                                                                         const uint8_t *__restrict__ codes,
+                                                                         const float *__restrict__ scales,
+                                                                         uint16_t *__restrict__ Y)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned char *xw = smem + (size_t)wave * M * 1024;                          // this wavefront's X runs
+    unsigned char *zw = smem + (size_t)NF4_WAVES * M * 1024 + wave * 64;          // and its zero run
+    const uint16_t *zs = reinterpret_cast<const uint16_t *>(zw);
+    float *red = reinterpret_cast<float *>(smem + (size_t)NF4_WAVES * M * 1024 + NF4_WAVES * 64);
+    const int r16 = lane & 15, q = lane >> 4;
+    const int n = blockIdx.x * 16 + r16;
+    const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
+    const uint32_t kh = (uint32_t)K >> 1, ks = (uint32_t)K >> 6;
+    const int KB = K >> 7;
+
+    if (lane < 4) *reinterpret_cast<u32x4 *>(zw + lane * 16) = u32x4{0u, 0u, 0u, 0u};   // read after the barrier below
+
+    const bool live = (r16 >> 1) < M && (r16 & 1) == (q >> 1);
+    const uint16_t *fa = live ? reinterpret_cast<const uint16_t *>(xw + (r16 >> 1) * 1024) + q * 32 : zs;
+    const int pstride = live ? 128 : 0;   // elements from one k-block of the batch to the next
+
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kb0 = wave; kb0 < KB; kb0 += NF4_WAVES * NF4_PF) {
+        const int kx = kb0 + NF4_WAVES * q;   // this lane's X k-block
+        u32x4 xv[MAXR];
+#pragma unroll
+        for (int i = 0; i < MAXR; i++)
+            if (i < M && kx < KB)
+                xv[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)i * K + (int64_t)kx * 128 + r16 * 8);
+        u32x4 cw[NF4_PF];
+        u32x2 sc[NF4_PF];
+        nf4_load_batch(codes, scales, nrow, kh, ks, KB, kb0, q, cw, sc);
+        // the previous batch's LDS reads come before these writes, and the
+        // writes before this batch's reads by other lanes of the wavefront:
+        // keep the compiler from moving LDS accesses across either point
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < MAXR; i++)
+            if (i < M && kx < KB)
+                *reinterpret_cast<u32x4 *>(xw + (i * 4 + q) * 256 + r16 * 16) = nf4_permute_x(xv[i]);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int p = 0; p < NF4_PF; p++) {
+            const int kb = kb0 + p * NF4_WAVES;
+            if (kb >= KB) break;
+            floatx4 pa = {0.f, 0.f, 0.f, 0.f};
+            const uint16_t *f = fa + p * pstride;
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8 *>(f + t * 8),
+                                                            __builtin_bit_cast(half8, nf4_levels8_kperm(cw[p][t])),
+                                                            pa, 0, 0, 0);
+            // (element to a scalar first: a bit_cast of an ext_vector element
+            // directly reads element 0 with this compiler)
+            const uint32_t s0u = sc[p][0], s1u = sc[p][1];
+            const float s0 = __builtin_bit_cast(float, s0u), s1 = __builtin_bit_cast(float, s1u);
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[r] = fmaf(pa[r], (r & 1) ? s1 : s0, acc[r]);   // D row 4q + r: half r & 1
+        }
+        asm volatile("" ::: "memory");
+    }
+    nf4_reduce_store(red, acc, true, M, N, Y);
+}
+
+// 9 to 16 rows: two MFMA chains over the same levels, A-row m carrying X[m]
+// in half 0's lanes for the first chain and in half 1's for the second. The
+// block stages all M rows of X in LDS first.
 __global__ __launch_bounds__(NF4_WAVES * 64) void nf4_gemv_kernel(const uint16_t *__restrict__ X, int M, int N,
                                                                   int K, const uint8_t *__restrict__ codes,
                                                                   const float *__restrict__ scales,
                                                                   uint16_t *__restrict__ Y)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);                       // [M][K]
-    float *red = reinterpret_cast<float *>(smem + (size_t)M * K * 2);       // [8][4][64]
+    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);                                    // [M][K], k-permuted
+    const uint16_t *zs = reinterpret_cast<const uint16_t *>(smem + (size_t)M * K * 2);   // 64 zeros
+    float *red = reinterpret_cast<float *>(smem + (size_t)M * K * 2 + NF4_ZERO_BYTES);  // [8][4][64]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, q = lane >> 4;
     const int n = blockIdx.x * 16 + r16;
@@ -127,56 +258,42 @@ __global__ __launch_bounds__(NF4_WAVES * 64) void nf4_gemv_kernel(const uint16_t
 
     const int xchunks = (M * K) >> 3;
     for (int c = threadIdx.x; c < xchunks; c += NF4_WAVES * 64)
-        *reinterpret_cast<u32x4 *>(xs + c * 8) = *reinterpret_cast<const u32x4 *>(X + (int64_t)c * 8);
+        *reinterpret_cast<u32x4 *>(xs + c * 8) = nf4_permute_x(*reinterpret_cast<const u32x4 *>(X + (int64_t)c * 8));
+    if (threadIdx.x < NF4_ZERO_BYTES / 16)
+        *reinterpret_cast<u32x4 *>(smem + (size_t)M * K * 2 + threadIdx.x * 16) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
 
-    const uint16_t *xrow = xs + (r16 < M ? r16 : M - 1) * K + q * 32;
-    const bool first = q < 2;
+    const bool half1 = q >= 2;
+    const uint16_t *xr = xs + (r16 < M ? r16 : M - 1) * K + q * 32;
+    const uint16_t *xa = half1 ? zs : xr, *xb = half1 ? xr : zs;
+    const int sa = half1 ? 0 : 128, sb = half1 ? 128 : 0;
+
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int kb0 = wave; kb0 < KB; kb0 += NF4_WAVES * NF4_PF) {
         u32x4 cw[NF4_PF];
         u32x2 sc[NF4_PF];
-#pragma unroll
-        for (int p = 0; p < NF4_PF; p++) {
-            const int kb = kb0 + p * NF4_WAVES;
-            const int kc = kb < KB ? kb : KB - 1;   // past the end: a valid k-block, not used
-            sc[p] = *reinterpret_cast<const u32x2 *>(scales + (nrow * ks + (uint32_t)kc * 2u));
-            cw[p] = *reinterpret_cast<const u32x4 *>(codes + (nrow * kh + (uint32_t)kc * 64u + q * 16u));
-        }
+        nf4_load_batch(codes, scales, nrow, kh, ks, KB, kb0, q, cw, sc);
 #pragma unroll
         for (int p = 0; p < NF4_PF; p++) {
             const int kb = kb0 + p * NF4_WAVES;
             if (kb >= KB) break;
             floatx4 pa = {0.f, 0.f, 0.f, 0.f}, pb = {0.f, 0.f, 0.f, 0.f};
+            const uint16_t *fa = xa + kb * sa, *fb = xb + kb * sb;
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                const half8 a = *reinterpret_cast<const half8 *>(xrow + kb * 128 + t * 8);
-                const u32x4 w = nf4_dequant8(cw[p][t]);
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8, first ? w : z), pa, 0, 0, 0);
-                pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8, first ? z : w), pb, 0, 0, 0);
+                const half8 w = __builtin_bit_cast(half8, nf4_levels8_kperm(cw[p][t]));
+                pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8 *>(fa + t * 8), w, pa,
+                                                            0, 0, 0);
+                pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8 *>(fb + t * 8), w, pb,
+                                                            0, 0, 0);
             }
-            // (element to a scalar first: a bit_cast of an ext_vector element
-            // directly reads element 0 with this compiler)
             const uint32_t s0u = sc[p][0], s1u = sc[p][1];
             const float s0 = __builtin_bit_cast(float, s0u), s1 = __builtin_bit_cast(float, s1u);
 #pragma unroll
             for (int r = 0; r < 4; r++) acc[r] = fmaf(pb[r], s1, fmaf(pa[r], s0, acc[r]));
         }
     }
-
-#pragma unroll
-    for (int r = 0; r < 4; r++) red[(wave * 4 + r) * 64 + lane] = acc[r];
-    __syncthreads();
-    if (threadIdx.x < 256) {
-        const int r = threadIdx.x >> 6, l = threadIdx.x & 63;
-        float v = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NF4_WAVES; w++) v += red[(w * 4 + r) * 64 + l];
-        const int m = 4 * (l >> 4) + r;
-        const int nn = blockIdx.x * 16 + (l & 15);
-        if (m < M && nn < N) Y[(int64_t)m * N + nn] = f2h(v);
-    }
+    nf4_reduce_store(red, acc, false, M, N, Y);
 }
 
 }  // namespace
@@ -206,21 +323,42 @@ hipError_t launch_nf4_linear(const uint16_t *X, int64_t M, int64_t N, int64_t K,
     }
     const int64_t blocks = (N + 15) / 16;
     if (blocks > 0x7fffffff) return hipErrorNotSupported;
-    const size_t red = (size_t)NF4_WAVES * 4 * 64 * 4;
-    // up to 16 rows of X per pass, within the 160 KB of LDS; past 64 KB the
-    // kernel needs the larger dynamic allocation enabled (once per process)
+    // The two-chain form stages all of a pass's rows in LDS (up to 16, within
+    // 160 KB); the paired form needs 8 KB per row whatever K is. Past 64 KB
+    // the kernels need the larger dynamic allocation enabled (once per process).
     constexpr size_t kMaxLds = 160 * 1024;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&nf4_gemv_kernel),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       (int)kMaxLds);
+    const size_t extra = (size_t)NF4_ZERO_BYTES + NF4_RED_BYTES;
+    static const hipError_t attr = [] {
+        const void *const fns[] = {reinterpret_cast<const void *>(&nf4_gemv_paired_kernel<8>),
+                                   reinterpret_cast<const void *>(&nf4_gemv_kernel)};
+        for (const void *f : fns) {
+            const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }();
     if (attr != hipSuccess) return attr;
-    const int64_t rows = std::min<int64_t>(16, (int64_t)((kMaxLds - red) / ((size_t)K * 2)));
-    if (rows < 1) return hipErrorNotSupported;
-    for (int64_t m0 = 0; m0 < M; m0 += rows) {
-        const int m = (int)std::min<int64_t>(rows, M - m0);
-        const size_t lds = (size_t)m * K * 2 + red;
-        nf4_gemv_kernel<<<(unsigned)blocks, NF4_WAVES * 64, lds, st>>>(X + m0 * K, m, (int)N, (int)K, codes,
-                                                                      scales, Y + m0 * N);
+    const int64_t rows_tc = std::min<int64_t>(16, (int64_t)((kMaxLds - extra) / ((size_t)K * 2)));
+    for (int64_t m0 = 0; m0 < M;) {
+        const int64_t left = M - m0;
+        if (left <= 8 || rows_tc <= 8) {
+            const int m = (int)std::min<int64_t>(8, left);
+            const size_t lds = (size_t)NF4_WAVES * m * 1024 + extra;
+            const dim3 grid((unsigned)blocks), block(NF4_WAVES * 64);
+            const uint16_t *Xm = X + m0 * K;
+            uint16_t *Ym = Y + m0 * N;
+            if (m == 1) nf4_gemv_paired_kernel<1><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym);
+            else if (m == 2) nf4_gemv_paired_kernel<2><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym);
+            else if (m <= 4) nf4_gemv_paired_kernel<4><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym);
+            else nf4_gemv_paired_kernel<8><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym);
+            m0 += m;
+        } else {
+            const int m = (int)std::min<int64_t>(rows_tc, left);
+            const size_t lds = (size_t)m * K * 2 + extra;
+            nf4_gemv_kernel<<<(unsigned)blocks, NF4_WAVES * 64, lds, st>>>(X + m0 * K, m, (int)N, (int)K, codes,
+                                                                          scales, Y + m0 * N);
+            m0 += m;
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

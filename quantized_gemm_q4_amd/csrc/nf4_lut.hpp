@@ -29,22 +29,35 @@ constexpr uint32_t nf4_hi_bytes(int d)
 constexpr uint32_t kNf4Lo0 = nf4_lo_bytes(0), kNf4Lo1 = nf4_lo_bytes(1), kNf4Hi0 = nf4_hi_bytes(0),
                    kNf4Hi1 = nf4_hi_bytes(1);
 
-// 8 codes (one dword, code i in nibble i) -> 8 fp16 levels in k order,
-// as 4 dwords of pairs (codes 2p, 2p + 1 in dword p)
+// 8 codes (one dword, code i in nibble i) -> their 8 fp16 levels as 4 dwords
+// of pairs, in the k order 0, 2, 4, 6, 1, 3, 5, 7 (codes 0, 2 in dword 0,
+// 4, 6 in dword 1, 1, 3 in dword 2, 5, 7 in dword 3): the order the lookup
+// produces them in, for callers that store X in the same order.
+// Magnitude index j: 7 - c below 8 (negative levels), c - 8 from 8 up; with
+// b8 the code's bit 3 (8 or 0 per nibble), b8 - b8 / 8 is 7 or 0, and
+// ~(c ^ that) & 7 is j. The sign bit of a negative level is set from ~bit 3.
+__device__ __forceinline__ u32x4 nf4_levels8_kperm(uint32_t d)
+{
+    const uint32_t b8 = d & 0x88888888u;
+    const uint32_t t = b8 - (b8 >> 3);
+    // v_bitop3 (bit (a << 2 | b << 1 | c) of the table is f(a, b, c)):
+    // 0x82 is ~(a ^ b) & c, 0xF2 is a | (~b & c). Written out as builtins so
+    // the compiler keeps the mask before the shift and the NOT inside.
+    const uint32_t jA = __builtin_amdgcn_bitop3_b32(d, t, 0x07070707u, 0x82);        // codes 0, 2, 4, 6
+    const uint32_t jB = __builtin_amdgcn_bitop3_b32(d, t, 0x70707070u, 0x82) >> 4;   // codes 1, 3, 5, 7
+    const uint32_t loA = __builtin_amdgcn_perm(kNf4Lo1, kNf4Lo0, jA), loB = __builtin_amdgcn_perm(kNf4Lo1, kNf4Lo0, jB);
+    const uint32_t hiA = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(kNf4Hi1, kNf4Hi0, jA), d << 4, 0x80808080u, 0xF2);
+    const uint32_t hiB = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(kNf4Hi1, kNf4Hi0, jB), d, 0x80808080u, 0xF2);
+    return u32x4{__builtin_amdgcn_perm(hiA, loA, 0x05010400u), __builtin_amdgcn_perm(hiA, loA, 0x07030602u),
+                 __builtin_amdgcn_perm(hiB, loB, 0x05010400u), __builtin_amdgcn_perm(hiB, loB, 0x07030602u)};
+}
+
+// The same 8 levels in natural k order (code 2p, 2p + 1 in dword p).
 __device__ __forceinline__ u32x4 nf4_dequant8(uint32_t d)
 {
-    const uint32_t pos = (d >> 3) & 0x11111111u;                  // 1 where the level is positive
-    const uint32_t neg = pos ^ 0x11111111u;
-    const uint32_t j = (d ^ (neg * 7u)) & 0x77777777u;            // magnitude index per nibble
-    const uint32_t jA = j & 0x0F0F0F0Fu, jB = (j >> 4) & 0x0F0F0F0Fu;   // codes 0,2,4,6 / 1,3,5,7
-    const uint32_t loA = __builtin_amdgcn_perm(kNf4Lo1, kNf4Lo0, jA), loB = __builtin_amdgcn_perm(kNf4Lo1, kNf4Lo0, jB);
-    const uint32_t hiA = __builtin_amdgcn_perm(kNf4Hi1, kNf4Hi0, jA) | ((neg << 7) & 0x80808080u);
-    const uint32_t hiB = __builtin_amdgcn_perm(kNf4Hi1, kNf4Hi0, jB) | ((neg << 3) & 0x80808080u);
-    // fp16 of codes 0, 2 | 4, 6 and 1, 3 | 5, 7, then pairs in k order
-    const uint32_t a01 = __builtin_amdgcn_perm(hiA, loA, 0x05010400u), a23 = __builtin_amdgcn_perm(hiA, loA, 0x07030602u);
-    const uint32_t b01 = __builtin_amdgcn_perm(hiB, loB, 0x05010400u), b23 = __builtin_amdgcn_perm(hiB, loB, 0x07030602u);
-    return u32x4{__builtin_amdgcn_perm(b01, a01, 0x05040100u), __builtin_amdgcn_perm(b01, a01, 0x07060302u),
-                 __builtin_amdgcn_perm(b23, a23, 0x05040100u), __builtin_amdgcn_perm(b23, a23, 0x07060302u)};
+    const u32x4 v = nf4_levels8_kperm(d);
+    return u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u), __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+                 __builtin_amdgcn_perm(v[3], v[1], 0x05040100u), __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
 }
 
 }  // namespace q4k

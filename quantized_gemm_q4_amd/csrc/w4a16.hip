@@ -876,19 +876,24 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int p, uint32_t zad
     return __builtin_bit_cast(uint32_t, v * __builtin_bit_cast(half2v, s2));
 }
 
-// NF4 form (NF4 = true): the codes index the 16 NF4 levels (nf4_dequant8), the
-// scales are fp32, one per 64 weights (gshift = 1: two 32-wide steps), and
-// each dequantized weight is f2h(level * scale): the fp32 product of the
-// exact level and scale, rounded to fp16.
+// NF4 form (NF4 = true): the codes index the 16 NF4 levels (nf4_dequant8),
+// the scales are fp32, one per 64 weights (gshift = 1: two 32-wide steps),
+// and each dequantized weight is fp16(level * scale), the exact product
+// rounded once. One packed fp16 multiply gives that when
+// the scale is an fp16 value, which every scale the NF4 quantizer writes is
+// (the max |w| of fp16 weights, or the 1e-8 floor of an all-zero block:
+// that rounds to fp16 0, and so does every level * 1e-8, with the level's
+// sign either way).
 __device__ __forceinline__ u32x4 nf4_scaled8(uint32_t w, float sf)
 {
     const u32x4 lv = nf4_dequant8(w);
+    const _Float16 h = (_Float16)sf;
+    const half2v s2 = {h, h};
     u32x4 r;
 #pragma unroll
     for (int p = 0; p < 4; p++) {
-        const uint32_t d = lv[p];
-        const float lo = h2f((uint16_t)(d & 0xffffu)) * sf, hi = h2f((uint16_t)(d >> 16)) * sf;
-        r[p] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
+        const uint32_t d = lv[p];   // a scalar first: a bit_cast of a vector element reads element 0 here
+        r[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d) * s2);
     }
     return r;
 }

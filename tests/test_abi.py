@@ -173,7 +173,8 @@ def layers(*descs):
     (lambda L: L.nf4_quantize(MISAL, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.nf4_quantize(FAKE, 0, 128, None, None, None), q4.Q4_OK),
     (lambda L: L.nf4_linear(FAKE, 1, 16, 192, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
-    (lambda L: L.nf4_linear(FAKE, 1, 16, 32768, FAKE, FAKE, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.nf4_linear(FAKE, 1, 16, 1 << 31, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.nf4_linear(FAKE, 1, 1 << 20, 1 << 14, FAKE, FAKE, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
     (lambda L: L.nf4_linear(FAKE, 1, 16, 256, FAKE, FAKE + 4, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.nf4_linear(FAKE, 1, 16, 256, None, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.nf4_linear(FAKE, 0, 16, 256, None, None, None, None), q4.Q4_OK),

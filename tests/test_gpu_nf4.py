@@ -55,9 +55,14 @@ def run_linear(orc, M, N, K, seed):
     return check_gemm(Y, Yref, B, f"nf4 M={M} N={N} K={K}")
 
 
+# up to 8 rows per pass the two 64-block halves ride in paired MFMA rows, 9 to
+# 16 in two MFMA chains; large K passes fewer rows at a time, and past 9 rows
+# of X in the LDS only paired passes of 8 (K = 32768)
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (1, 300, 1024), (3, 77, 256), (16, 300, 640),
                                    (17, 129, 384), (40, 64, 4096), (1, 11008, 4096), (2, 4096, 11008),
-                                   (5, 1000, 8192), (16, 11008, 4096), (64, 1000, 4096)])
+                                   (5, 1000, 8192), (16, 11008, 4096), (64, 1000, 4096),
+                                   (8, 500, 2048), (9, 257, 1024), (12, 130, 28672), (1, 64, 32768),
+                                   (12, 40, 32768)])
 def test_linear_shapes(orc, M, N, K):
     run_linear(orc, M, N, K, M * 71 + N + K)
 
