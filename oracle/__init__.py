@@ -76,6 +76,8 @@ def _load():
         "orc_mxfp4_gemm": (None, [_u8p, _i64, _i64, _u8p, _u8p, _i64, _i64p, _i64, _f64p, _f64p]),
         "orc_nf4_quantize": (None, [_u16p, _i64, _i64, _u16p, _u8p, _f32p]),
         "orc_nf4_ref": (None, [_u16p, _i64, _i64, _u8p, _f32p, _u16p, _i64, _i64p, _i64, _f64p, _f64p]),
+        "orc_nvfp4_quantize": (None, [_u16p, _i64, _i64, _u8p, _u8p]),
+        "orc_nvfp4_ref": (None, [_u16p, _i64, _i64, _u8p, _u8p, _i64, _i64p, _i64, _f64p, _f64p]),
         "orc_num_threads": (_int, []),
     }
     for name, (res, args) in sig.items():
@@ -467,4 +469,45 @@ def nf4_ref(X, codes, scales, rows=None):
     B = np.empty((n_rows, N), np.float64)
     _load().orc_nf4_ref(_ptr(X, _u16p), M, K, _ptr(codes, _u8p), _ptr(scales, _f32p),
                         _ptr(lv, _u16p), N, _ptr(r, _i64p), n_rows, _ptr(Y, _f64p), _ptr(B, _f64p))
+    return Y, B
+
+
+# NVFP4 (Quantization notes, FP4 item: E2M1 values, one FP8 E4M3 scale per
+# block of 16; orc_nvfp4_quantize states the steps and the reading of the
+# sketch's rounding line)
+def nvfp4_quantize(W):
+    """NVFP4 of W [N, K] (K % 16 == 0): (codes uint8 [N, K/2], E4M3 scale bytes uint8 [N, K/16])."""
+    W = _half_bits(W)
+    N, K = W.shape
+    assert K % 16 == 0
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.zeros((N, K // 16), np.uint8)
+    _load().orc_nvfp4_quantize(_ptr(W, _u16p), N, K, _ptr(codes, _u8p), _ptr(scales, _u8p))
+    return codes, scales
+
+
+def nvfp4_dequant(codes, scales) -> np.ndarray:
+    """fp64 w_hat = e2m1(code) * e4m3(scale) of an NVFP4 weight [N, K]."""
+    lut4 = np.array([e2m1_decode(c) for c in range(16)], np.float64)
+    lut8 = np.array([e4m3_decode(c) for c in range(256)], np.float64)
+    codes = np.asarray(codes, dtype=np.uint8)
+    u = np.empty((codes.shape[0], codes.shape[1] * 2), np.uint8)
+    u[:, 0::2] = codes & 0xF
+    u[:, 1::2] = codes >> 4
+    return lut4[u] * np.repeat(lut8[np.asarray(scales, dtype=np.uint8)], 16, axis=1)
+
+
+def nvfp4_ref(X, codes, scales, rows=None):
+    """fp64 Y = X W_hat^T and B = |X| |W_hat|^T for an NVFP4 weight."""
+    X = _half_bits(X)
+    M, K = X.shape
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    N = codes.shape[0]
+    r = _rows(rows)
+    n_rows = M if r is None else r.size
+    Y = np.empty((n_rows, N), np.float64)
+    B = np.empty((n_rows, N), np.float64)
+    _load().orc_nvfp4_ref(_ptr(X, _u16p), M, K, _ptr(codes, _u8p), _ptr(scales, _u8p), N,
+                          _ptr(r, _i64p), n_rows, _ptr(Y, _f64p), _ptr(B, _f64p))
     return Y, B

@@ -741,3 +741,70 @@ int orc_num_threads(void) { return omp_get_max_threads(); }
 #else
 int orc_num_threads(void) { return 1; }
 #endif
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4 weights (Quantization notes, FP4 item: FP4 E2M1 values with one FP8
+ * scale per block of 16 (4 + 8/16 = 4.5 bits per weight); its NVFP4-style
+ * sketch takes the block's max |w|, the scale amax / 6 cast to FP8 E4M3, and
+ * the FP4 value of w / scale clipped to +-6). The sketch's line that rounds
+ * w / scale * 6 to an integer is read as what the rest of the item says: the
+ * E2M1 value of w / scale.
+ *   scale = e4m3(fl32(amax / 6))   (nearest, ties to even, saturating at 448)
+ *   code  = e2m1(fl32(w / scale))  (nearest, ties to even, saturating at 6);
+ *           every code of a block whose scale is 0 (amax / 6 at most 2^-10,
+ *           half the smallest E4M3 subnormal) is 0
+ *   w_hat = e2m1(code) * e4m3(scale)
+ * Codes [N, K/2] (two per byte along K, even k in the low nibble), scales
+ * E4M3 bytes [N, K/16].                                                      */
+void orc_nvfp4_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *codes, uint8_t *scales)
+{
+    const int64_t nb = K / 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t b = 0; b < nb; b++) {
+            float v[16], amax = 0.0f;
+            for (int i = 0; i < 16; i++) {
+                v[i] = orc_h2f(W[n * K + b * 16 + i]);
+                if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+            }
+            const unsigned sc = orc_e4m3_encode(amax / 6.0f);
+            const float scale = orc_e4m3_decode(sc);
+            scales[n * nb + b] = (uint8_t)sc;
+            for (int i = 0; i < 16; i += 2) {
+                unsigned lo = 0, hi = 0;
+                if (scale > 0.0f) {
+                    lo = orc_e2m1_encode(v[i] / scale);
+                    hi = orc_e2m1_encode(v[i + 1] / scale);
+                }
+                codes[n * (K / 2) + b * 8 + i / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+}
+
+/* Y = X W_hat^T and B = |X| |W_hat|^T in fp64 for the listed rows of X (all
+ * when rows == NULL), w_hat = e2m1(code) * e4m3(scale of its block of 16).   */
+void orc_nvfp4_ref(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes,
+                   const uint8_t *scales, int64_t N, const int64_t *rows, int64_t n_rows,
+                   double *Y, double *B)
+{
+    if (!rows) n_rows = M;
+    const int64_t nb = K / 16;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t i = 0; i < n_rows; i++) {
+            int64_t m = rows ? rows[i] : i;
+            double y = 0.0, bb = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                uint8_t byte = codes[n * (K / 2) + k / 2];
+                unsigned c = (k & 1) ? (byte >> 4) : (byte & 0xFu);
+                double w = (double)orc_e2m1_decode(c) * (double)orc_e4m3_decode(scales[n * nb + k / 16]);
+                double x = (double)orc_h2f(X[m * K + k]);
+                y += x * w;
+                bb += fabs(x) * fabs(w);
+            }
+            Y[i * N + n] = y;
+            B[i * N + n] = bb;
+        }
+    }
+}
