@@ -26,7 +26,7 @@ The JSON line also carries:
                 quantize + pack GB/s, batched decode M = 16 / 64.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
-                       [--only decode|prefill|w8a8|fp8|mxfp4|nf4|quant|batched] [--eager]
+                       [--only decode|prefill|w8a8|fp8|mxfp4|nf4|nvfp4|quant|batched] [--eager]
                        [--copy-calibration]
 """
 from __future__ import annotations
@@ -78,7 +78,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", default=None, choices=["decode", "prefill", "w8a8", "fp8", "mxfp4", "nf4",
+    ap.add_argument("--only", default=None, choices=["decode", "prefill", "w8a8", "fp8", "mxfp4", "nf4", "nvfp4",
                                                      "quant", "batched"])
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -432,36 +432,43 @@ def main():
         extra["mxfp4_w4a8"] = res
         torch.cuda.empty_cache()
 
-    # ---- NF4 decode (M = 1, K = 4096, N = 11008 and 4096) --------------------------
-    if only in (None, "nf4"):
+    # ---- NF4 and NVFP4: decode (M = 1, K = 4096, N = 11008 and 4096) and the
+    # prefill shape (M = 2048) on the large-M GEMM ------------------------------------
+    lut_formats = {
+        # name: (quantize, linear, scale bytes per weight)
+        "nf4": (q4.nf4_quantize, q4.nf4_linear, 4 / 64),
+        "nvfp4": (q4.nvfp4_quantize, q4.nvfp4_linear, 1 / 16),
+    }
+    for fmt, (quant, linear, sbpw) in lut_formats.items():
+        if only not in (None, fmt):
+            continue
         res = {}
         for N in (11008, 4096):
             w = workloads.decode(N)
             X = gpu(w["X"])
-            codes, sc = q4.nf4_quantize(gpu(w["W"]))
-            nb = N * 4096 // 2 + N * 4096 // 64 * 4 + 4096 * 2 + N * 2
+            codes, sc = quant(gpu(w["W"]))
+            nb = int(N * 4096 // 2 + N * 4096 * sbpw + 4096 * 2 + N * 2)
             copies = max(2, math.ceil(MALL_BYTES / nb) + 1)
             cps = [(codes.clone(), sc.clone()) for _ in range(copies)]
             Y = torch.empty((1, N), dtype=torch.float16, device=dev)
-            gr = graph_of(lambda i: q4.nf4_linear(X, *cps[i % copies], out=Y), copies)
+            gr = graph_of(lambda i: linear(X, *cps[i % copies], out=Y), copies)
             gr()
             reps = max(1, 2000 // copies)
             tt = timed(lambda i: gr(), reps) / (reps * copies)
             res[f"n{N}"] = {"us": tt * 1e6, "GB/s": nb / tt / 1e9, "frac_hbm": nb / tt / 1e9 / HBM_PEAK_GBS,
                             "bytes": nb}
             del cps, codes, sc
-        extra["nf4_decode"] = res
-        # the prefill shape (M = 2048, K = 4096, N = 11008) on the NF4 large-M GEMM
+        extra[f"{fmt}_decode"] = res
         w = workloads.prefill()
-        codes, sc = q4.nf4_quantize(gpu(w["W"]))
+        codes, sc = quant(gpu(w["W"]))
         X = gpu(w["X"])
         Y = torch.empty((2048, 11008), dtype=torch.float16, device=dev)
         for _ in range(3):
-            q4.nf4_linear(X, codes, sc, out=Y)
-        tp = timed(lambda i: q4.nf4_linear(X, codes, sc, out=Y), 30) / 30
+            linear(X, codes, sc, out=Y)
+        tp = timed(lambda i: linear(X, codes, sc, out=Y), 30) / 30
         flops = 2 * 2048 * 11008 * 4096
-        extra["nf4_prefill"] = {"shape": [2048, 11008, 4096], "us": tp * 1e6, "TFLOP/s": flops / tp / 1e12,
-                                "frac_mfma_fp16": flops / tp / 1e12 / FP16_MFMA_PEAK_TFLOPS}
+        extra[f"{fmt}_prefill"] = {"shape": [2048, 11008, 4096], "us": tp * 1e6, "TFLOP/s": flops / tp / 1e12,
+                                   "frac_mfma_fp16": flops / tp / 1e12 / FP16_MFMA_PEAK_TFLOPS}
         del codes, sc, X, Y
         torch.cuda.empty_cache()
 

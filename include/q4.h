@@ -471,6 +471,36 @@ Q4_API q4_status nf4_linear(const void *X, int64_t M, int64_t N, int64_t K, cons
                             const float *scales, void *Y, void *stream);
 
 /* ----------------------------------------------------------------------------
+ * NVFP4 weights (Quantization notes, FP4 item: FP4 E2M1 values with one FP8
+ * E4M3 scale per block of 16 along K, 4 + 8/16 = 4.5 bits per weight; its
+ * NVFP4-style sketch: scale = E4M3(amax / 6), code = the E2M1 value of
+ * w / scale, clipped to +-6).
+ *
+ * nvfp4_quantize -- per block of 16: scale = e4m3(fl32(amax / 6)) (nearest,
+ *   ties to even, saturating at 448); code = e2m1(fl32(w / scale)) (nearest,
+ *   ties to even, saturating at 6, sign kept on zero), or 0 for every weight
+ *   of a block whose scale is 0 (amax / 6 at most 2^-10);
+ *   w_hat = e2m1(code) * e4m3(scale). W fp16 [N, K] (16-byte aligned,
+ *   K % 16 == 0); codes u8 [N, K/2] output, two codes per byte along K (even
+ *   k in the low nibble), 4-byte aligned; scales u8 [N, K/16] output, E4M3
+ *   bytes. Codes and scales are bit-exact.
+ * nvfp4_linear -- Y = X * W_hat^T, fp32 accumulation, fp16 output. w_hat is
+ *   exact in fp16 (at most 6 significant bits, within [2^-10, 2688]), so the
+ *   block scale is folded into the fp16 matrix-core operand without a
+ *   rounding. Up to 48 rows: a decode GEMV, passes of at most 16 rows, each
+ *   reading the weight once; above 48 rows the tiled GEMM of w4a16_linear.
+ *   X fp16 [M, K] and codes 16-byte aligned; scales 2-byte aligned;
+ *   K % 128 == 0; Y fp16 [M, N] output.
+ * Accuracy: |Y - Y_ref| <= 2^-10 * sum_k |x||w_hat| (+2^-25) elementwise
+ *   against the exact product over the dequantized weight.
+ * Errors: INVALID_ARG, UNSUPPORTED (N * K / 2 >= 2^32 - 256), MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status nvfp4_quantize(const void *W, int64_t N, int64_t K, uint8_t *codes, uint8_t *scales,
+                                void *stream);
+Q4_API q4_status nvfp4_linear(const void *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                              const uint8_t *scales, void *Y, void *stream);
+
+/* ----------------------------------------------------------------------------
  * smoothquant_scales -- the SmoothQuant migration factor from calibration
  * activations (Operators guide §5.1; Core ideas §2.4; Quantization notes,
  * SmoothQuant):

@@ -26,6 +26,8 @@ Functions (same names as the C ABI):
   nf4_levels() -> 16 fp16 levels (host)
   nf4_quantize(W) -> (codes, scales)                         absmax per 64
   nf4_linear(X, codes, scales) -> Y
+  nvfp4_quantize(W) -> (codes, scales)                       E4M3 scale per 16
+  nvfp4_linear(X, codes, scales) -> Y
 """
 from __future__ import annotations
 
@@ -80,6 +82,8 @@ SIGNATURES = {
     "nf4_levels": (None, [_vp]),
     "nf4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "nf4_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "nvfp4_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -575,4 +579,28 @@ def nf4_linear(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, out: 
         raise ValueError(f"codes {tuple(codes.shape)} / scales {tuple(scales.shape)} do not match K={K}")
     Y = _output(out, M, N, X.device)
     _check(lib().nf4_linear(_ptr(X), M, N, K, _ptr(codes), _ptr(scales), _ptr(Y), _stream(X)))
+    return Y
+
+
+def nvfp4_quantize(W: torch.Tensor):
+    """NVFP4 of W fp16 [N, K]: (codes uint8 [N, K/2], E4M3 scale bytes uint8 [N, K/16])."""
+    _need(W, torch.float16, "W", 2)
+    N, K = W.shape
+    codes = _empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scales = _empty((N, max(K // 16, 0)), dtype=torch.uint8, device=W.device)
+    _check(lib().nvfp4_quantize(_ptr(W), N, K, _ptr(codes), _ptr(scales), _stream(W)))
+    return codes, scales
+
+
+def nvfp4_linear(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor | None = None):
+    """Y fp16 [M, N] = X W_hat^T with W_hat = e2m1(code) * e4m3(scale) (NVFP4)."""
+    _need(X, torch.float16, "X", 2)
+    _need(codes, torch.uint8, "codes", 2)
+    _need(scales, torch.uint8, "scales", 2)
+    M, K = X.shape
+    N = codes.shape[0]
+    if codes.shape[1] * 2 != K or tuple(scales.shape) != (N, K // 16):
+        raise ValueError(f"codes {tuple(codes.shape)} / scales {tuple(scales.shape)} do not match K={K}")
+    Y = _output(out, M, N, X.device)
+    _check(lib().nvfp4_linear(_ptr(X), M, N, K, _ptr(codes), _ptr(scales), _ptr(Y), _stream(X)))
     return Y

@@ -15,6 +15,7 @@
 // the epilogue is y = fp16(acc * x_scale[m]).
 #include <type_traits>
 
+#include "fp4_codes.hpp"
 #include "q4_internal.hpp"
 #include "row_codes.hpp"
 
@@ -26,18 +27,8 @@ namespace {
 // four lanes one block of 32; the block's max |v| is a quad reduction. The
 // scale is the smallest power of two 2^(e - 127) with amax <= 6 * 2^(e - 127),
 // found from amax's exponent with one exact comparison (e = 0 for an all-zero
-// block); v * 2^(127 - e) is exact, and its E2M1 code is counted against the
-// rounding thresholds of the format with ties to the even code:
-// 0.25 (down), 0.75 (up), 1.25 (down), 1.75 (up), 2.5 (down), 3.5 (up),
-// 5 (down).
-__device__ __forceinline__ uint32_t e2m1_code(float x)
-{
-    const float a = fabsf(x);
-    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                       (uint32_t)(a > 5.0f);
-    return c | ((__builtin_bit_cast(uint32_t, x) >> 28) & 8u);   // sign bit of x
-}
+// block); v * 2^(127 - e) is exact, and e2m1_code (fp4_codes.hpp) counts it
+// against the format's rounding thresholds with ties to the even code.
 
 __device__ __forceinline__ float quad_max(float a)
 {

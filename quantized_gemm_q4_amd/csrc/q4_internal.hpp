@@ -129,5 +129,14 @@ hipError_t launch_nf4_gemm(const uint16_t *X, int64_t M, int64_t N, int64_t K, c
                           const float *scales, uint16_t *Y, hipStream_t st);
 hipError_t launch_nf4_linear(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
                              const float *scales, uint16_t *Y, hipStream_t st);
+// NVFP4 weights: the quantizer (codes [N, K/2], E4M3 scale bytes [N, K/16];
+// K % 16 == 0), the large-M GEMM form and the layer (decode GEMV up to 48
+// rows; K % 128 == 0, hipErrorNotSupported otherwise).
+hipError_t launch_nvfp4_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *codes, uint8_t *scales,
+                                 hipStream_t st);
+hipError_t launch_nvfp4_gemm(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                            const uint8_t *scales, uint16_t *Y, hipStream_t st);
+hipError_t launch_nvfp4_linear(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                               const uint8_t *scales, uint16_t *Y, hipStream_t st);
 
 }  // namespace q4k

@@ -19,6 +19,7 @@
 // never expanded in memory.
 #include <cstdlib>
 
+#include "fp4_codes.hpp"
 #include "nf4_lut.hpp"
 #include "w4a16_dequant.hpp"
 
@@ -876,7 +877,7 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int p, uint32_t zad
     return __builtin_bit_cast(uint32_t, v * __builtin_bit_cast(half2v, s2));
 }
 
-// NF4 form (NF4 = true): the codes index the 16 NF4 levels (nf4_dequant8),
+// NF4 form (FMT = kFmtNf4): the codes index the 16 NF4 levels (nf4_dequant8),
 // the scales are fp32, one per 64 weights (gshift = 1: two 32-wide steps),
 // and each dequantized weight is fp16(level * scale), the exact product
 // rounded once. One packed fp16 multiply gives that when
@@ -898,7 +899,14 @@ __device__ __forceinline__ u32x4 nf4_scaled8(uint32_t w, float sf)
     return r;
 }
 
-template <int NU, int WM, bool ASYM, bool NF4 = false>
+// Weight formats of the large-M GEMM: INT4 with group scales (and zero-points),
+// NF4 (fp32 scale per 64), NVFP4 (E2M1 codes, E4M3 scale per 16: the two
+// scale bytes of a 32-wide step load as the INT4 form's one fp16 scale does,
+// gshift = 0, and scale the code dwords 0-1 and 2-3 of the step; e2m1 * e4m3
+// is exact in fp16, nvfp4_scaled8).
+constexpr int kFmtInt4 = 0, kFmtNf4 = 1, kFmtNvfp4 = 2;
+
+template <int NU, int WM, bool ASYM, int FMT = kFmtInt4>
 __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
     const uint16_t *__restrict__ X, int M, int N, int K, int gshift,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
@@ -948,7 +956,7 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
     auto load_w = [&](int k, int q) {
         const uint32_t grp = (uint32_t)k >> gshift;
         wc[q] = *reinterpret_cast<const u32x4 *>(codes + coff + (uint32_t)k * 16u);
-        if (NF4) ws[q] = reinterpret_cast<const uint32_t *>(scales)[soff + grp];   // fp32 bits
+        if (FMT == kFmtNf4) ws[q] = reinterpret_cast<const uint32_t *>(scales)[soff + grp];   // fp32 bits
         else ws[q] = scales[soff + grp];
         if (ASYM) wz[q] = zeros[zoff + (grp >> 1)];   // nibble picked at use: no wait here
     };
@@ -1004,8 +1012,11 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
             for (int q = 0; q < PPF; q++) {
                 const int pr = f * PPF + q;
                 if (pr < 16) {
-                    if (NF4) {
+                    if (FMT == kFmtNf4) {
                         if ((pr & 3) == 0) out = nf4_scaled8(wc[wq][pr >> 2], __builtin_bit_cast(float, ws[wq]));
+                    } else if (FMT == kFmtNvfp4) {
+                        if ((pr & 3) == 0)
+                            out = nvfp4_scaled8(wc[wq][pr >> 2], e4m3_half2((ws[wq] >> (8 * (pr >> 3))) & 0xFFu));
                     } else {
                         out[pr & 3] = dequant_pair(wc[wq][pr >> 2], pr & 3, zadd, s2);
                     }
@@ -1037,7 +1048,8 @@ __global__ __launch_bounds__(512 / WM, 1) void w4a16_gemm_kernel(
         unsigned char *const row = sb[0] + dq_off;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const u32x4 out = NF4 ? nf4_scaled8(wc[0][i], __builtin_bit_cast(float, ws[0]))
+            const u32x4 out = FMT == kFmtNf4     ? nf4_scaled8(wc[0][i], __builtin_bit_cast(float, ws[0]))
+                              : FMT == kFmtNvfp4 ? nvfp4_scaled8(wc[0][i], e4m3_half2((ws[0] >> (8 * (i >> 1))) & 0xFFu))
                                   : u32x4{dequant_pair(wc[0][i], 0, zadd, s2), dequant_pair(wc[0][i], 1, zadd, s2),
                                           dequant_pair(wc[0][i], 2, zadd, s2), dequant_pair(wc[0][i], 3, zadd, s2)};
             *reinterpret_cast<u32x4 *>(row + dq_cs * (i ^ dq_swz)) = out;
@@ -1186,8 +1198,13 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t 
 
 }  // namespace
 
-hipError_t launch_nf4_gemm(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
-                          const float *scales, uint16_t *Y, hipStream_t st)
+namespace {
+
+// The lookup-decoded formats on the large-M GEMM (symmetric, no zero-points):
+// the INT4 form's tile width rule, FMT's B-fragment producer.
+template <int FMT>
+hipError_t launch_lut_gemm(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                           const uint16_t *sc, int gshift, uint16_t *Y, hipStream_t st)
 {
     if (M < 1 || N < 1 || K % 128 != 0 || M * K * 2 >= ((int64_t)1 << 31) || N * (K / 2) >= ((int64_t)1 << 31))
         return hipErrorNotSupported;
@@ -1204,14 +1221,29 @@ hipError_t launch_nf4_gemm(const uint16_t *X, int64_t M, int64_t N, int64_t K, c
         }
     }
     const int tiles = tiles_m * ((n + 32 * best - 1) / (32 * best));
-    const uint16_t *sc = reinterpret_cast<const uint16_t *>(scales);
     auto launch = [&](auto kernel, int threads) {
-        kernel<<<tiles, threads, 0, st>>>(X, m, n, k, 1, codes, sc, nullptr, tiles_m, Y);
+        kernel<<<tiles, threads, 0, st>>>(X, m, n, k, gshift, codes, sc, nullptr, tiles_m, Y);
     };
-    if (best == 4) launch(w4a16_gemm_kernel<4, 2, false, true>, 256);
-    else if (best == 8) launch(w4a16_gemm_kernel<8, 2, false, true>, 256);
-    else launch(w4a16_gemm_kernel<11, 1, false, true>, 512);
+    if (best == 4) launch(w4a16_gemm_kernel<4, 2, false, FMT>, 256);
+    else if (best == 8) launch(w4a16_gemm_kernel<8, 2, false, FMT>, 256);
+    else launch(w4a16_gemm_kernel<11, 1, false, FMT>, 512);
     return hipGetLastError();
+}
+
+}  // namespace
+
+// NF4: fp32 scales, one per 64 = two 32-wide steps (gshift 1)
+hipError_t launch_nf4_gemm(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                          const float *scales, uint16_t *Y, hipStream_t st)
+{
+    return launch_lut_gemm<kFmtNf4>(X, M, N, K, codes, reinterpret_cast<const uint16_t *>(scales), 1, Y, st);
+}
+
+// NVFP4: two E4M3 scale bytes per 32-wide step, read as one 16-bit unit (gshift 0)
+hipError_t launch_nvfp4_gemm(const uint16_t *X, int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                            const uint8_t *scales, uint16_t *Y, hipStream_t st)
+{
+    return launch_lut_gemm<kFmtNvfp4>(X, M, N, K, codes, reinterpret_cast<const uint16_t *>(scales), 0, Y, st);
 }
 
 hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,

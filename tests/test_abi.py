@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared_functions()) <= exported
     # nothing else of ours leaks out (internal launchers are hidden)
-    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "fp8", "mxfp4", "nf4", "awq", "smoothquant", "_ZN3q4k"))}
+    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "fp8", "mxfp4", "nf4", "nvfp4", "awq", "smoothquant", "_ZN3q4k"))}
     assert ours == set(declared_functions())
 
 
@@ -178,6 +178,17 @@ def layers(*descs):
     (lambda L: L.nf4_linear(FAKE, 1, 16, 256, FAKE, FAKE + 4, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.nf4_linear(FAKE, 1, 16, 256, None, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.nf4_linear(FAKE, 0, 16, 256, None, None, None, None), q4.Q4_OK),
+    (lambda L: L.nvfp4_quantize(FAKE, 4, 40, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.nvfp4_quantize(MISAL, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.nvfp4_quantize(FAKE, 4, 128, FAKE + 2, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.nvfp4_quantize(FAKE, 0, 128, None, None, None), q4.Q4_OK),
+    (lambda L: L.nvfp4_quantize(FAKE, 4, 128, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.nvfp4_linear(FAKE, 1, 16, 192, FAKE, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.nvfp4_linear(FAKE, 1, 1 << 20, 1 << 14, FAKE, FAKE, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.nvfp4_linear(FAKE, 1, 16, 256, FAKE, FAKE + 1, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.nvfp4_linear(FAKE, 1, 16, 256, FAKE + 8, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.nvfp4_linear(FAKE, 1, 16, 256, None, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.nvfp4_linear(FAKE, 0, 16, 256, None, None, None, None), q4.Q4_OK),
     (lambda L: L.awq_scale_weight(FAKE, FAKE, 4, 12, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.awq_scale_weight(FAKE, None, 4, 16, FAKE, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.awq_scale_weight(MISAL, FAKE, 4, 16, FAKE, None), q4.Q4_ERR_MISALIGNED),
