@@ -118,7 +118,10 @@ void orc_f2h_array(const float *x, int64_t n, uint16_t *out)
  *     the same s; a scale that rounds to 0 is replaced by 1.0;
  *   - round first, then add zp (the order the formula is written in);
  *   - true division x / s, not a multiply by 1/s;
- *   - symmetric codes are stored offset-binary, u = q + 8.
+ *   - symmetric codes are stored offset-binary, u = q + 8;
+ *   - a group holding a NaN or an infinity is flagged: its scale is the fp16
+ *     NaN 0x7e00 and its codes and zero-point are 0 (the other groups are
+ *     quantized as if it were not there).
  * Packing: codes[n][i] = u[n][2i] | u[n][2i+1] << 4 (even k in the low
  * nibble); zeros[n][i] = zp[n][2i] | zp[n][2i+1] << 4, a zero nibble pads an
  * odd group count. All arrays row-major.                                    */
@@ -126,6 +129,14 @@ void orc_f2h_array(const float *x, int64_t n, uint16_t *out)
 static void quant_group(const uint16_t *w, int g, int sym, uint8_t *u,
                         uint16_t *scale16, int *zp_out)
 {
+    for (int k = 0; k < g; k++) {
+        if (!isfinite(orc_h2f(w[k]))) {        /* flagged group: NaN scale, codes and zp 0 */
+            for (int j = 0; j < g; j++) u[j] = 0;
+            *scale16 = 0x7e00;
+            *zp_out = 0;
+            return;
+        }
+    }
     float lo = 0.0f, hi = 0.0f, amax = 0.0f;
     for (int k = 0; k < g; k++) {
         float x = orc_h2f(w[k]);
@@ -298,16 +309,24 @@ void orc_awq_scale_act(const uint16_t *X, const float *s, int64_t M, int64_t K,
  *   a_n = max(max_k |w'|, 1e-8)    (the 1e-8 floor of the Method boundaries
  *                                   example's clamp_min)
  *   sw[n] = a_n / 127
- *   q = clip(rne(w' / sw[n]), -127, 127)                                    */
+ *   q = clip(rne(w' / sw[n]), -127, 127)
+ * A row whose w' holds a NaN or an infinity is flagged: sw[n] = NaN, codes 0. */
 void orc_q8_quantize_weight(const uint16_t *W, const float *s, int64_t N,
                             int64_t K, int8_t *Wq, float *sw)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; n++) {
         float a = 0.0f;
+        int bad = 0;
         for (int64_t k = 0; k < K; k++) {
             float w = orc_h2f(W[n * K + k]) * (s ? s[k] : 1.0f);
+            if (!isfinite(w)) bad = 1;
             if (fabsf(w) > a) a = fabsf(w);
+        }
+        if (bad) {                              /* flagged row: NaN scale, codes 0 */
+            for (int64_t k = 0; k < K; k++) Wq[n * K + k] = 0;
+            sw[n] = NAN;
+            continue;
         }
         if (a < 1e-8f) a = 1e-8f;
         float scale = a / 127.0f;
@@ -327,17 +346,25 @@ void orc_q8_quantize_weight(const uint16_t *W, const float *s, int64_t N,
  * guide §5.1 transform X / s and §5.3 the online divide):
  *   x'[m][k] = x / s[k]            (fp32 division; s == NULL: x' = x)
  *   a_m = max(max_k |x'|, 1e-8),  sx[m] = a_m / 127,
- *   q = clip(rne(x' / sx[m]), -127, 127)                                   */
+ *   q = clip(rne(x' / sx[m]), -127, 127)
+ * A row whose x' holds a NaN or an infinity is flagged: sx[m] = NaN, codes 0. */
 void orc_q8_quantize_act(const uint16_t *X, const float *s, int64_t M,
                          int64_t K, int8_t *Xq, float *sx)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; m++) {
         float a = 0.0f;
+        int bad = 0;
         for (int64_t k = 0; k < K; k++) {
             float x = orc_h2f(X[m * K + k]);
             if (s) x = x / s[k];
+            if (!isfinite(x)) bad = 1;
             if (fabsf(x) > a) a = fabsf(x);
+        }
+        if (bad) {                              /* flagged row: NaN scale, codes 0 */
+            for (int64_t k = 0; k < K; k++) Xq[m * K + k] = 0;
+            sx[m] = NAN;
+            continue;
         }
         if (a < 1e-8f) a = 1e-8f;
         float scale = a / 127.0f;
@@ -500,15 +527,23 @@ unsigned orc_e4m3_encode(float x)
 
 /* One row of the FP8 quantizer: v[k] = x * s[k] (weight, mul != 0) or
  * x / s[k] (activation), a = max(max_k |v|, 1e-8), scale = a / 448,
- * q[k] = e4m3(v[k] / scale).                                                */
+ * q[k] = e4m3(v[k] / scale). A row whose v holds a NaN or an infinity is
+ * flagged: scale NaN, codes 0.                                              */
 static void fp8_row(const uint16_t *x, const float *s, int64_t K, int mul, uint8_t *q,
                     float *scale_out)
 {
     float a = 0.0f;
+    int bad = 0;
     for (int64_t k = 0; k < K; k++) {
         float v = orc_h2f(x[k]);
         if (s) v = mul ? v * s[k] : v / s[k];
+        if (!isfinite(v)) bad = 1;
         if (fabsf(v) > a) a = fabsf(v);
+    }
+    if (bad) {                                  /* flagged row: NaN scale, codes 0 */
+        for (int64_t k = 0; k < K; k++) q[k] = 0;
+        *scale_out = NAN;
+        return;
     }
     if (a < 1e-8f) a = 1e-8f;
     float scale = a / 448.0f;
@@ -595,7 +630,9 @@ unsigned orc_e2m1_encode(float x)
  *   scale = 2^(e - 127) with e the smallest integer such that amax <= 6 * 2^(e - 127)
  *           (the smallest power of two that keeps every element in range;
  *           e = 0 for an all-zero block; e <= 254),
- *   code  = e2m1(v / scale) (exact division by a power of two).
+ *   code  = e2m1(v / scale) (exact division by a power of two);
+ * a block whose v holds a NaN or an infinity is flagged: scale byte 0xff
+ * (E8M0's NaN), codes 0.
  * Codes packed two per byte along K (even k in the low nibble) [N, K/2];
  * scales E8M0 bytes [N, K/32].                                               */
 void orc_mxfp4_quantize_weight(const uint16_t *W, const float *s, int64_t N, int64_t K,
@@ -606,10 +643,17 @@ void orc_mxfp4_quantize_weight(const uint16_t *W, const float *s, int64_t N, int
     for (int64_t n = 0; n < N; n++) {
         for (int64_t b = 0; b < nb; b++) {
             float v[32], amax = 0.0f;
+            int bad = 0;
             for (int i = 0; i < 32; i++) {
                 int64_t k = b * 32 + i;
                 v[i] = orc_h2f(W[n * K + k]) * (s ? s[k] : 1.0f);
+                if (!isfinite(v[i])) bad = 1;
                 if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+            }
+            if (bad) {                          /* flagged block: E8M0 NaN 0xff, codes 0 */
+                scales[n * nb + b] = 0xff;
+                for (int i = 0; i < 16; i++) codes[n * (K / 2) + b * 16 + i] = 0;
+                continue;
             }
             int e = 0;
             if (amax > 0.0f) {
@@ -668,7 +712,8 @@ void orc_mxfp4_gemm(const uint8_t *Xq, int64_t M, int64_t K, const uint8_t *code
 
 /* codes [N, K/2] (two per byte along K, even k in the low nibble), scales
  * fp32 [N, K/64]: scale = max(max_block |w|, 1e-8), x = w / scale (fp32
- * IEEE), code = the first index i minimising fabsf(x - level[i]) (fp32).    */
+ * IEEE), code = the first index i minimising fabsf(x - level[i]) (fp32).
+ * A block holding a NaN or an infinity is flagged: scale NaN, codes 0.      */
 void orc_nf4_quantize(const uint16_t *W, int64_t N, int64_t K, const uint16_t *levels,
                       uint8_t *codes, float *scales)
 {
@@ -679,9 +724,16 @@ void orc_nf4_quantize(const uint16_t *W, int64_t N, int64_t K, const uint16_t *l
     for (int64_t n = 0; n < N; n++) {
         for (int64_t b = 0; b < nb; b++) {
             float a = 0.0f;
+            int bad = 0;
             for (int i = 0; i < 64; i++) {
                 float v = fabsf(orc_h2f(W[n * K + b * 64 + i]));
+                if (!isfinite(v)) bad = 1;
                 if (v > a) a = v;
+            }
+            if (bad) {                          /* flagged block: NaN scale, codes 0 */
+                scales[n * nb + b] = NAN;
+                for (int i = 0; i < 32; i++) codes[n * (K / 2) + b * 32 + i] = 0;
+                continue;
             }
             if (a < 1e-8f) a = 1e-8f;
             scales[n * nb + b] = a;
@@ -754,6 +806,8 @@ int orc_num_threads(void) { return 1; }
  *           every code of a block whose scale is 0 (amax / 6 at most 2^-10,
  *           half the smallest E4M3 subnormal) is 0
  *   w_hat = e2m1(code) * e4m3(scale)
+ * A block holding a NaN or an infinity is flagged: scale byte 0x7f (E4M3's
+ * NaN), codes 0.
  * Codes [N, K/2] (two per byte along K, even k in the low nibble), scales
  * E4M3 bytes [N, K/16].                                                      */
 void orc_nvfp4_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *codes, uint8_t *scales)
@@ -763,9 +817,16 @@ void orc_nvfp4_quantize(const uint16_t *W, int64_t N, int64_t K, uint8_t *codes,
     for (int64_t n = 0; n < N; n++) {
         for (int64_t b = 0; b < nb; b++) {
             float v[16], amax = 0.0f;
+            int bad = 0;
             for (int i = 0; i < 16; i++) {
                 v[i] = orc_h2f(W[n * K + b * 16 + i]);
+                if (!isfinite(v[i])) bad = 1;
                 if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+            }
+            if (bad) {                          /* flagged block: E4M3 NaN 0x7f, codes 0 */
+                scales[n * nb + b] = 0x7f;
+                for (int i = 0; i < 8; i++) codes[n * (K / 2) + b * 8 + i] = 0;
+                continue;
             }
             const unsigned sc = orc_e4m3_encode(amax / 6.0f);
             const float scale = orc_e4m3_decode(sc);

@@ -116,3 +116,29 @@ def out_buffer(shape, dtype):
     binding's allocator (guarded during the GPU tests)."""
     import quantized_gemm_q4_amd as q4
     return q4._empty(shape, dtype, dev())
+
+
+def poisoned(W: np.ndarray, seed: int, count: int = 6):
+    """A copy of the fp16 matrix W with NaN, +Inf and -Inf written into
+    `count` seeded cells (cycling through the three), the cells, and a clean
+    copy with those cells set to 0: inputs for the flagged-group rule (a
+    group holding a non-finite value gets the format's NaN scale and zero
+    codes; every other group is quantized as in the clean copy)."""
+    rng = np.random.default_rng(seed)
+    Wp = np.array(W, dtype=np.float16, copy=True)
+    clean = np.array(W, dtype=np.float16, copy=True)
+    rows = rng.integers(0, W.shape[0], count)
+    cols = rng.integers(0, W.shape[1], count)
+    vals = [np.float16(np.nan), np.float16(np.inf), np.float16(-np.inf)]
+    for i, (r, c) in enumerate(zip(rows, cols)):
+        Wp[r, c] = vals[i % 3]
+        clean[r, c] = 0
+    return Wp, list(zip(rows.tolist(), cols.tolist())), clean
+
+
+def flagged_mask(cells, shape, group: int):
+    """[rows, K // group] bool: the groups that hold a poisoned cell."""
+    m = np.zeros((shape[0], shape[1] // group), bool)
+    for r, c in cells:
+        m[r, c // group] = True
+    return m
