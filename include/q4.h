@@ -41,8 +41,17 @@
  *     call as Q4_ERR_HIP with the call's name in q4_last_error(), and each
  *     call writes one line ("[q4] <call>: ok" or the error) to stderr.
  *     Calls are then synchronous; off by default.
- *   - Inputs must be finite; non-finite inputs give unspecified codes and
- *     outputs (never an out-of-bounds access).
+ *   - Non-finite inputs are flagged, not hidden: every quantizer gives a
+ *     group (INT4 group, INT8 / E4M3 row, MXFP4 block of 32, NF4 block of
+ *     64, NVFP4 block of 16) whose values -- after the smoothing multiply or
+ *     divide where there is one -- hold a NaN or an infinity the format's NaN
+ *     as its scale (fp16 0x7e00, fp32 0x7fc00000, E8M0 0xff, E4M3 0x7f) and
+ *     0 as every code and zero-point; other groups are quantized as if it
+ *     were not there. The layers then carry NaN into exactly the outputs
+ *     that use a flagged group (a weight group: its output column; an
+ *     activation row: its output row). Non-finite values in X of the W4A16,
+ *     NF4 and NVFP4 layers, in awq_s or in smoothquant_scales' inputs give
+ *     unspecified outputs (never an out-of-bounds access).
  *   - Rounding is IEEE round-to-nearest-even everywhere; divisions are true
  *     IEEE divisions. Codes, scales, zero-points and int32 accumulators are
  *     bit-reproducible.

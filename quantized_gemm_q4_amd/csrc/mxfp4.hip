@@ -30,14 +30,12 @@ namespace {
 // block); v * 2^(127 - e) is exact, and e2m1_code (fp4_codes.hpp) counts it
 // against the format's rounding thresholds with ties to the even code.
 
-__device__ __forceinline__ float quad_max(float a)
+// max over a quad of |v| bit patterns (NaN and the infinities rank above
+// every finite value)
+__device__ __forceinline__ uint32_t quad_max_bits(uint32_t a)
 {
-    auto dpp = [](float v, auto ctrl) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                     decltype(ctrl)::value, 0xF, 0xF, false));
-    };
-    a = fmaxf(a, dpp(a, std::integral_constant<int, 0xB1>{}));   // quad swap 1 0 3 2
-    return fmaxf(a, dpp(a, std::integral_constant<int, 0x4E>{}));   // quad swap 2 3 0 1
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false));   // quad swap 1 0 3 2
+    return max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false));   // quad swap 2 3 0 1
 }
 
 template <bool HAS_S>
@@ -67,10 +65,14 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t *__r
             v[4 + i] *= b[i];
         }
     }
-    float m = 0.0f;
+    uint32_t m = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
-    const float amax = quad_max(m);   // the four lanes of a block are a quad (K % 32 == 0)
+    for (int i = 0; i < 8; i++) m = max(m, __builtin_bit_cast(uint32_t, v[i]) & 0x7fffffffu);
+    const uint32_t amax_bits = quad_max_bits(m);   // the four lanes of a block are a quad (K % 32 == 0)
+    // a block holding a NaN or an infinity is flagged: scale byte 0xff
+    // (E8M0's NaN), codes 0
+    const bool bad = amax_bits >= 0x7f800000u;
+    const float amax = bad ? 0.0f : __builtin_bit_cast(float, amax_bits);
     int e = 0;
     if (amax > 0.0f) {
         int ex;
@@ -86,8 +88,8 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t *__r
 #pragma unroll
     for (int i = 0; i < 8; i++) out |= e2m1_code(v[i] * mul) << (4 * i);
     if (live) {
-        *reinterpret_cast<uint32_t *>(codes + row * (K >> 1) + (k0 >> 1)) = out;
-        if ((threadIdx.x & 3) == 0) scales[row * (K >> 5) + (k0 >> 5)] = (uint8_t)e;
+        *reinterpret_cast<uint32_t *>(codes + row * (K >> 1) + (k0 >> 1)) = bad ? 0u : out;
+        if ((threadIdx.x & 3) == 0) scales[row * (K >> 5) + (k0 >> 5)] = bad ? (uint8_t)0xff : (uint8_t)e;
     }
 }
 

@@ -38,15 +38,13 @@ __device__ __forceinline__ double nf4_recip64(double b)
     return fma(fma(-b, r, 1.0), r, r);
 }
 
-__device__ __forceinline__ float max8(float a)
+// max over 8 lanes of |w| bit patterns (NaN and the infinities rank above
+// every finite value)
+__device__ __forceinline__ uint32_t max8_bits(uint32_t a)
 {
-    auto dpp = [](float v, auto ctrl) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                     decltype(ctrl)::value, 0xF, 0xF, false));
-    };
-    a = fmaxf(a, dpp(a, std::integral_constant<int, 0xB1>{}));    // quad swap 1 0 3 2
-    a = fmaxf(a, dpp(a, std::integral_constant<int, 0x4E>{}));    // quad swap 2 3 0 1
-    return fmaxf(a, dpp(a, std::integral_constant<int, 0x141>{}));   // half-row mirror
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false));    // quad swap 1 0 3 2
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false));    // quad swap 2 3 0 1
+    return max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x141, 0xF, 0xF, false));   // half-row mirror
 }
 
 __global__ __launch_bounds__(256) void nf4_quantize_kernel(const uint16_t *__restrict__ W, int64_t N,
@@ -65,10 +63,13 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const uint16_t *__res
         v[2 * i] = h2f((uint16_t)(raw[i] & 0xffffu));
         v[2 * i + 1] = h2f((uint16_t)(raw[i] >> 16));
     }
-    float m = 0.0f;
+    uint32_t m = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
-    const float a = fmaxf(max8(m), 1e-8f);
+    for (int i = 0; i < 8; i++) m = max(m, __builtin_bit_cast(uint32_t, v[i]) & 0x7fffffffu);
+    const uint32_t amax_bits = max8_bits(m);
+    // a block holding a NaN or an infinity is flagged: NaN scale, codes 0
+    const bool bad = amax_bits >= 0x7f800000u;
+    const float a = bad ? 1.0f : fmaxf(__builtin_bit_cast(float, amax_bits), 1e-8f);
     const double r = nf4_recip64((double)a);
     float lv[16];
 #pragma unroll
@@ -90,8 +91,8 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const uint16_t *__res
         out |= (uint32_t)best << (4 * i);
     }
     if (live) {
-        *reinterpret_cast<uint32_t *>(codes + row * (K >> 1) + (k0 >> 1)) = out;
-        if ((threadIdx.x & 7) == 0) scales[row * (K >> 6) + (k0 >> 6)] = a;
+        *reinterpret_cast<uint32_t *>(codes + row * (K >> 1) + (k0 >> 1)) = bad ? 0u : out;
+        if ((threadIdx.x & 7) == 0) scales[row * (K >> 6) + (k0 >> 6)] = bad ? __builtin_nanf("") : a;
     }
 }
 

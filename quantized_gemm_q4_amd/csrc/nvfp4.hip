@@ -47,13 +47,16 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t *__r
         v[2 * i] = h2f((uint16_t)(raw[i] & 0xffffu));
         v[2 * i + 1] = h2f((uint16_t)(raw[i] >> 16));
     }
-    float m = 0.0f;
+    // max of |w| bit patterns (NaN and the infinities rank above every finite
+    // value); the two lanes of a block are neighbours (chunks per row is even)
+    uint32_t m = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
-    // the two lanes of a block are neighbours (chunks per row is even)
-    const float amax =
-        fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, m), 0xB1, 0xF,
-                                                                       0xF, false)));
+    for (int i = 0; i < 8; i++) m = max(m, __builtin_bit_cast(uint32_t, v[i]) & 0x7fffffffu);
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+    // a block holding a NaN or an infinity is flagged: scale byte 0x7f
+    // (E4M3's NaN), codes 0
+    const bool bad = m >= 0x7f800000u;
+    const float amax = bad ? 0.0f : __builtin_bit_cast(float, m);
     const float q = (float)((double)amax * (1.0 / 6.0));   // fl32(amax / 6)
     const uint32_t sc = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(q, 448.0f), 0.0f, 0, false) & 0xFFu;
     const float scale = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t *__r
     }
     if (live) {
         *reinterpret_cast<uint32_t *>(codes + row * (K >> 1) + (k0 >> 1)) = out;
-        if ((threadIdx.x & 1) == 0) scales[row * (K >> 4) + (k0 >> 4)] = (uint8_t)sc;
+        if ((threadIdx.x & 1) == 0) scales[row * (K >> 4) + (k0 >> 4)] = bad ? (uint8_t)0x7f : (uint8_t)sc;
     }
 }
 

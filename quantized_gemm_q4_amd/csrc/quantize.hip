@@ -21,6 +21,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// |v| as a binary32 bit pattern: these order as the magnitudes, and NaN and
+// the infinities (0x7f800000 and above) rank above every finite value, so an
+// integer maximum over them finds a non-finite value (fmaxf skips NaN)
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __builtin_bit_cast(uint32_t, v) & 0x7fffffffu; }
+constexpr uint32_t kNonFinite = 0x7f800000u;
+
 // ---------------------------------------------------------------------------
 // INT4 quantize + pack. Each lane owns 16 consecutive weights of one group
 // (two 16-byte loads); the g/16 lanes of a group (2, 4 or 8, inside one
@@ -100,33 +108,41 @@ __global__ __launch_bounds__(kThreads) void q4_quantize_pack_kernel(
         d[i] = __builtin_bit_cast(half2v, e);
     }
 
-    // group statistics: (lo, -hi) as one fp16 pair, min-reduced over the group's lanes
+    // group statistics: (lo, -hi) as one fp16 pair, min-reduced over the
+    // group's lanes. Both paths let a NaN or an infinity through to the pair,
+    // which flags the group: the symmetric one takes max |x| on the 16-bit
+    // patterns (they order as the magnitudes, with the infinities and NaN
+    // above every finite value), the asymmetric one the IEEE 754-2019
+    // minimum / maximum (v_pk_minimum3_f16 / v_pk_maximum3_f16, which
+    // propagate NaN, unlike min / max), and so do the lane reductions.
     half2v st;
     if (SYM) {
-        half2v a = __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, d[0]) & 0x7fff7fffu);
+        u16x2 ab = __builtin_bit_cast(u16x2, __builtin_bit_cast(uint32_t, d[0]) & 0x7fff7fffu);
 #pragma unroll
         for (int i = 1; i < V / 2; i++)
-            a = __builtin_elementwise_max(a, __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, d[i]) & 0x7fff7fffu));
-        const _Float16 m = a[0] > a[1] ? a[0] : a[1];
-        st = half2v{(_Float16)0.0f, -m};
+            ab = __builtin_elementwise_max(ab, __builtin_bit_cast(u16x2, __builtin_bit_cast(uint32_t, d[i]) & 0x7fff7fffu));
+        const uint16_t m = ab[0] > ab[1] ? ab[0] : ab[1];
+        st = half2v{(_Float16)0.0f, -__builtin_bit_cast(_Float16, m)};
     } else {
         half2v mn = d[0], mx = d[0];
 #pragma unroll
         for (int i = 1; i < V / 2; i++) {
-            mn = __builtin_elementwise_min(mn, d[i]);
-            mx = __builtin_elementwise_max(mx, d[i]);
+            mn = __builtin_elementwise_minimum(mn, d[i]);
+            mx = __builtin_elementwise_maximum(mx, d[i]);
         }
-        const _Float16 lo = mn[0] < mn[1] ? mn[0] : mn[1];
-        const _Float16 hi = mx[0] > mx[1] ? mx[0] : mx[1];
-        st = half2v{lo, -hi};
+        st = half2v{__builtin_elementwise_minimum(mn[0], mn[1]), -__builtin_elementwise_maximum(mx[0], mx[1])};
     }
-    st = __builtin_elementwise_min(st, __builtin_bit_cast(half2v, dpp_lanes<0xB1>(__builtin_bit_cast(uint32_t, st))));
+    st = __builtin_elementwise_minimum(st, __builtin_bit_cast(half2v, dpp_lanes<0xB1>(__builtin_bit_cast(uint32_t, st))));
     if (LPG >= 4)
-        st = __builtin_elementwise_min(st, __builtin_bit_cast(half2v, dpp_lanes<0x4E>(__builtin_bit_cast(uint32_t, st))));
+        st = __builtin_elementwise_minimum(st, __builtin_bit_cast(half2v, dpp_lanes<0x4E>(__builtin_bit_cast(uint32_t, st))));
     if (LPG >= 8)
-        st = __builtin_elementwise_min(st, __builtin_bit_cast(half2v, dpp_lanes<0x141>(__builtin_bit_cast(uint32_t, st))));
-    const float lo = fminf((float)st[0], 0.0f);
-    const float hi = fmaxf(-(float)st[1], 0.0f);   // SYM: max |x|
+        st = __builtin_elementwise_minimum(st, __builtin_bit_cast(half2v, dpp_lanes<0x141>(__builtin_bit_cast(uint32_t, st))));
+    // a group holding a NaN or an infinity is flagged: its scale is the fp16
+    // NaN and its codes and zero-point are 0 (the arithmetic below then runs
+    // on an all-zero group)
+    const bool bad = !((float)st[0] >= -65504.0f && -(float)st[1] <= 65504.0f);
+    const float lo = bad ? 0.0f : fminf((float)st[0], 0.0f);
+    const float hi = bad ? 0.0f : fmaxf(-(float)st[1], 0.0f);   // SYM: max |x|
 
     const float s32 = SYM ? hi / 7.0f : (hi - lo) / 15.0f;   // IEEE division: rounded to fp16 next
     uint16_t s16 = f2h(s32);
@@ -175,6 +191,10 @@ __global__ __launch_bounds__(kThreads) void q4_quantize_pack_kernel(
         const uint32_t hi2 = __builtin_amdgcn_perm(b[4 * w + 3], b[4 * w + 2], 0x0c0c0400u);
         word[w] = __builtin_amdgcn_perm(hi2, lo2, 0x05040100u);
     }
+    if (bad) {
+        word = u32x2{0u, 0u};
+        s16 = 0x7e00u;
+    }
     if (valid) {
         *reinterpret_cast<u32x2 *>(codes + elem / 2) = word;
         if (li == 0) scales[n * G + j] = s16;
@@ -182,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void q4_quantize_pack_kernel(
     if (!SYM) {
         // zero-points of groups 2i and 2i + 1 meet through a lane swizzle
         // (xor LPG: the partner group's lanes); a missing last group packs 0
-        const int z = valid ? (int)zp : 0;
+        const int z = valid && !bad ? (int)zp : 0;
         const int zo = __builtin_amdgcn_ds_swizzle(z, (LPG << 10) | 0x1F);
         if (li == 0 && (gi & 1) == 0 && valid)
             zeros[n * ((G + 1) / 2) + (j >> 1)] = (uint8_t)(z | (zo << 4));
@@ -215,15 +235,15 @@ hipError_t launch_q4_g(const uint16_t *W, int64_t N, int64_t K, int sym, uint8_t
 // q = clip(rne(v / scale), -127, 127). The generic kernel (rows wider than
 // 8192) has one block per row, IEEE divisions, and reads the row twice; each
 // lane owns 8-element chunks (16-byte loads, 8-byte stores).
-__device__ __forceinline__ float block_max(float v, float *red)
+// the block's maximum of |v| bit patterns (256 threads)
+__device__ __forceinline__ uint32_t block_max_bits(uint32_t v, uint32_t *red)
 {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[wave] = v;
     __syncthreads();
-    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    return v;
+    return max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
 template <bool DIV>
@@ -268,12 +288,13 @@ __global__ __launch_bounds__(kThreads) void q8_rows_generic_kernel(const uint16_
                                                           int64_t K, uint8_t *__restrict__ Q,
                                                           float *__restrict__ scale_out)
 {
-    __shared__ float red[4];
+    __shared__ uint32_t red[4];
     const int64_t r = blockIdx.x;
     const uint16_t *row = X + r * K;
     uint8_t *qrow = Q + r * K;
     const int64_t step = (int64_t)kThreads * 8;
-    float a = 0.0f;
+    uint32_t ab = 0u;
+    // a row holding a NaN or an infinity is flagged: NaN scale, codes 0
     if (CPT > 0) {
         float v[CPT > 0 ? CPT : 1][8];
 #pragma unroll
@@ -282,38 +303,41 @@ __global__ __launch_bounds__(kThreads) void q8_rows_generic_kernel(const uint16_
             if (k0 < K) {
                 load_row_chunk<DIV>(row, s, k0, v[c]);
 #pragma unroll
-                for (int i = 0; i < 8; i++) a = fmaxf(a, fabsf(v[c][i]));
+                for (int i = 0; i < 8; i++) ab = max(ab, abs_bits(v[c][i]));
             }
         }
-        a = fmaxf(block_max(a, red), 1e-8f);
-        const float scale = a / kRowMax<FP8>;
+        ab = block_max_bits(ab, red);
+        const bool bad = ab >= kNonFinite;
+        const float scale = (bad ? 1.0f : fmaxf(__builtin_bit_cast(float, ab), 1e-8f)) / kRowMax<FP8>;
 #pragma unroll
         for (int c = 0; c < CPT; c++) {
             const int64_t k0 = threadIdx.x * 8 + c * step;
-            if (k0 < K) *reinterpret_cast<u32x2 *>(qrow + k0) = row_codes8<FP8>(v[c], scale);
+            if (k0 < K)
+                *reinterpret_cast<u32x2 *>(qrow + k0) = bad ? u32x2{0u, 0u} : row_codes8<FP8>(v[c], scale);
         }
-        if (threadIdx.x == 0) scale_out[r] = scale;
+        if (threadIdx.x == 0) scale_out[r] = bad ? __builtin_nanf("") : scale;
     } else {
         float v[8];
         for (int64_t k0 = threadIdx.x * 8; k0 < K; k0 += step) {
             load_row_chunk<DIV>(row, s, k0, v);
 #pragma unroll
-            for (int i = 0; i < 8; i++) a = fmaxf(a, fabsf(v[i]));
+            for (int i = 0; i < 8; i++) ab = max(ab, abs_bits(v[i]));
         }
-        a = fmaxf(block_max(a, red), 1e-8f);
-        const float scale = a / kRowMax<FP8>;
+        ab = block_max_bits(ab, red);
+        const bool bad = ab >= kNonFinite;
+        const float scale = (bad ? 1.0f : fmaxf(__builtin_bit_cast(float, ab), 1e-8f)) / kRowMax<FP8>;
         for (int64_t k0 = threadIdx.x * 8; k0 < K; k0 += step) {
             load_row_chunk<DIV>(row, s, k0, v);
-            *reinterpret_cast<u32x2 *>(qrow + k0) = row_codes8<FP8>(v, scale);
+            *reinterpret_cast<u32x2 *>(qrow + k0) = bad ? u32x2{0u, 0u} : row_codes8<FP8>(v, scale);
         }
-        if (threadIdx.x == 0) scale_out[r] = scale;
+        if (threadIdx.x == 0) scale_out[r] = bad ? __builtin_nanf("") : scale;
     }
 }
 
 // max over each half-wavefront (lanes 0-31 and 32-63 each end with their own):
 // DPP quad swaps, half-row and row mirrors, then a lane swizzle across 16
-// (a >= 0, finite: the bit patterns order as the values, so the lanes meet
-// with integer max, which needs no NaN canonicalisation)
+// (a holds |v| bits: they order as the magnitudes with NaN and the
+// infinities on top, so the lanes meet with integer max)
 __device__ __forceinline__ float halfwave_max(float a)
 {
     auto dpp = [](uint32_t v, auto ctrl) {
@@ -395,7 +419,7 @@ __global__ __launch_bounds__(T) void q8_rows_kernel(const uint16_t *__restrict__
 #pragma unroll
     for (int rr = 0; rr < RPB; rr++) {
         float v[CPT][8];
-        float a = 0.0f;
+        uint32_t ab = 0u;
 #pragma unroll
         for (int c = 0; c < CPT; c++) {
 #pragma unroll
@@ -406,13 +430,13 @@ __global__ __launch_bounds__(T) void q8_rows_kernel(const uint16_t *__restrict__
                 else if (DIV) v[c][i] = (float)((double)x * rd[c][i]);   // fl32(x / s)
                 else v[c][i] = x * sv[c][i];
             }
-            float m = fmaxf(fmaxf(fabsf(v[c][0]), fabsf(v[c][1])), fabsf(v[c][2]));
-            m = fmaxf(fmaxf(m, fabsf(v[c][3])), fabsf(v[c][4]));
-            m = fmaxf(fmaxf(m, fabsf(v[c][5])), fabsf(v[c][6]));
-            m = fmaxf(m, fabsf(v[c][7]));
-            if (kin[c]) a = fmaxf(a, m);   // chunks past K hold a clamped copy: not counted
+            uint32_t m = max(max(abs_bits(v[c][0]), abs_bits(v[c][1])), abs_bits(v[c][2]));
+            m = max(max(m, abs_bits(v[c][3])), abs_bits(v[c][4]));
+            m = max(max(m, abs_bits(v[c][5])), abs_bits(v[c][6]));
+            m = max(m, abs_bits(v[c][7]));
+            if (kin[c]) ab = max(ab, m);   // chunks past K hold a clamped copy: not counted
         }
-        a = halfwave_max(a);
+        float a = halfwave_max(__builtin_bit_cast(float, ab));
         if ((lane & 31) == 0) red[rr][wave * 2 + (lane >> 5)] = a;
         __syncthreads();
 #pragma unroll
@@ -421,7 +445,9 @@ __global__ __launch_bounds__(T) void q8_rows_kernel(const uint16_t *__restrict__
             const uint32_t m0 = m[0], m1 = m[1], m2 = m[2], m3 = m[3];
             a = __builtin_bit_cast(float, max(__builtin_bit_cast(uint32_t, a), max(max(m0, m1), max(m2, m3))));
         }
-        a = fmaxf(a, 1e-8f);
+        // a row holding a NaN or an infinity is flagged: NaN scale, codes 0
+        const bool bad = __builtin_bit_cast(uint32_t, a) >= kNonFinite;
+        a = bad ? 1.0f : fmaxf(a, 1e-8f);
         const float scale = a / kRowMax<FP8>;
         const double rs = recip64((double)scale);
         const int64_t r = r0 + rr;
@@ -431,11 +457,11 @@ __global__ __launch_bounds__(T) void q8_rows_kernel(const uint16_t *__restrict__
                 float q[8];
 #pragma unroll
                 for (int i = 0; i < 8; i++) q[i] = (float)((double)v[c][i] * rs);   // fl32(v / scale)
-                const u32x2 out = {row_codes4<FP8>(q[0], q[1], q[2], q[3]),
-                                   row_codes4<FP8>(q[4], q[5], q[6], q[7])};
+                u32x2 out = {row_codes4<FP8>(q[0], q[1], q[2], q[3]), row_codes4<FP8>(q[4], q[5], q[6], q[7])};
+                if (bad) out = u32x2{0u, 0u};
                 if (kin[c]) *reinterpret_cast<u32x2 *>(Q + r * K + kc[c]) = out;
             }
-            if (t == 0) scale_out[r] = scale;
+            if (t == 0) scale_out[r] = bad ? __builtin_nanf("") : scale;
         }
     }
 }

@@ -104,7 +104,7 @@ __device__ __forceinline__ void fused_quantize_x(const FusedX &f, int nchunks, i
 #pragma unroll
     for (int i = 0; i < kFusedChunks; i++) {
         const int c = tid + 512 * i;
-        float a = 0.0f;
+        uint32_t a = 0u;   // max of |v| bit patterns: NaN and the infinities rank above every finite value
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             const uint32_t d = f.xr[i][e >> 1];
@@ -115,14 +115,16 @@ __device__ __forceinline__ void fused_quantize_x(const FusedX &f, int nchunks, i
             } else {
                 v[i][e] = x;
             }
-            a = fmaxf(a, fabsf(v[i][e]));
+            a = max(a, __builtin_bit_cast(uint32_t, v[i][e]) & 0x7fffffffu);
         }
-        if (c < nchunks) atomicMax(&rmax[(c * 8) / K], __builtin_bit_cast(uint32_t, a));
+        if (c < nchunks) atomicMax(&rmax[(c * 8) / K], a);
     }
     __syncthreads();
+    // a row holding a NaN or an infinity is flagged: NaN scale, codes 0
     if (tid < M) {
+        const bool bad = rmax[tid] >= 0x7f800000u;
         const float a = fmaxf(__builtin_bit_cast(float, rmax[tid]), 1e-8f);
-        const float sc = a / kRowMax<FP8>;
+        const float sc = bad ? __builtin_nanf("") : a / kRowMax<FP8>;
         rscale[tid] = sc;
         if (blockIdx.x == 0) ws_scale[tid] = sc;
     }
@@ -131,11 +133,14 @@ __device__ __forceinline__ void fused_quantize_x(const FusedX &f, int nchunks, i
     for (int i = 0; i < kFusedChunks; i++) {
         const int c = tid + 512 * i;
         if (c < nchunks) {
-            const double rs = recip64((double)rscale[(c * 8) / K]);
+            const float sr = rscale[(c * 8) / K];
+            const bool bad = sr != sr;
+            const double rs = recip64((double)(bad ? 1.0f : sr));
             float q[8];
 #pragma unroll
             for (int e = 0; e < 8; e++) q[e] = (float)((double)v[i][e] * rs);
-            const u32x2 out = {row_codes4<FP8>(q[0], q[1], q[2], q[3]), row_codes4<FP8>(q[4], q[5], q[6], q[7])};
+            u32x2 out = {row_codes4<FP8>(q[0], q[1], q[2], q[3]), row_codes4<FP8>(q[4], q[5], q[6], q[7])};
+            if (bad) out = u32x2{0u, 0u};
             *reinterpret_cast<u32x2 *>(xq + c * 8) = out;
             if (blockIdx.x == 0) *reinterpret_cast<u32x2 *>(ws_codes + (int64_t)c * 8) = out;
         }
