@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_prefill_kernel(
 // all four share: one k-block of it (16 MT rows x 128 k, rows past M repeat
 // row M - 1) at a time goes straight from global memory into an R-slot LDS
 // ring with direct-to-LDS loads issued R - 1 k-blocks ahead; its 16-byte
-// chunks are XOR-swizzled (chunk c of row m at c ^ (m % 16)) so the
+// chunks are XOR-swizzled (chunk c of row m at c ^ xswz(m)) so the
 // fragment reads, 16 rows of one chunk, are conflict-free. Each wavefront
 // streams its own code runs, scales and zero-points through a DC-deep
 // register ring. One barrier per k-block: before it every wavefront waits
@@ -400,6 +400,18 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_prefill_kernel(
 // with (1, 1/16) and (-(1024 + zp), -(64 + zp)) leaves (u0 - zp, u1 - zp).
 // Each product x (u - zp) is exact in fp32; the fp32 partial sum of a k-block
 // is scaled by its group scale in fp32.
+// Swizzle of the X tiles of the batched kernels: the 16-byte chunk c of a
+// 256-byte row r is stored at c ^ xswz(r). A 16-lane fragment read touches
+// one chunk of 16 rows. On gfx950 a ds_read_b128 serves 16 lanes per cycle,
+// four groups of four lanes that share lane bit 5 and the parity of lane
+// bits 2-4 (lanes 0-3, 12-15, 20-23, 24-27 together), and 16 bytes of a
+// 256-byte bank row per lane (the grouping was fitted to the bank-conflict
+// counter on a set of probe patterns). With c ^ r the four lanes of a group
+// with row bits 2 and 3 swapped for q land on the same chunk (two-way
+// conflicts on every read); c ^ (r & 11) keeps every group on 16 distinct
+// chunks for each of the four MFMA steps.
+__device__ __forceinline__ int xswz(int r) { return r & 11; }
+
 __device__ __forceinline__ uint32_t unpack_pair(uint32_t w, int p, uint32_t zadd)
 {
     const uint32_t t = __builtin_amdgcn_perm(w, w, 0x01010101u * (uint32_t)p);
@@ -440,12 +452,12 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_kernel(
 
     // direct-to-LDS X loads: instruction j of wavefront wn fills rows
     // 4 (4 j + wn) .. + 3 of a slot; lane i: row 4 (4 j + wn) + i / 16, stored
-    // chunk i % 16, logical chunk (i % 16) ^ (row % 16)
+    // chunk i % 16, logical chunk (i % 16) ^ xswz(row % 16)
     uint32_t xoff[4];
 #pragma unroll
     for (int j = 0; j < MT; j++) {
         const int m = 4 * (4 * j + wn) + (lane >> 4);
-        const int c = (lane & 15) ^ (m & 15);
+        const int c = (lane & 15) ^ xswz(m);
         xoff[j] = ((uint32_t)(m < M ? m : M - 1) * (uint32_t)K + 8u * (uint32_t)c) * 2u;
     }
     const unsigned char *Xb = reinterpret_cast<const unsigned char *>(X);
@@ -515,7 +527,7 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_kernel(
 #pragma unroll
                 for (int mt = 0; mt < MT; mt++) {
                     const int m = mt * 16 + r16;
-                    const half8 a = *reinterpret_cast<const half8 *>(slot + m * 256 + 16 * ((4 * q + t) ^ r16));
+                    const half8 a = *reinterpret_cast<const half8 *>(slot + m * 256 + 16 * ((4 * q + t) ^ xswz(r16)));
                     part[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, part[mt], 0, 0, 0);
                 }
             }
@@ -561,57 +573,97 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_kernel(
 // registers. The ring kernel above keeps only R - 1 k-blocks of code runs in
 // flight per row, so HBM sees each 2 KB weight row as 64-byte pieces spread
 // over the whole kernel, and a step costs about one memory latency over the
-// ring depth. Here a wavefront issues the code runs, scales and zero-points
-// of all its KBS (<= 16) k-blocks at once, right behind the first R - 1 X
-// slots, so the weight streams at the rate of the decode GEMV; from then on
-// only X (L2-resident) goes through the R-slot LDS ring. The first X wait
-// also waits for the code runs (loads complete in order); that is the
-// weight's own stream time, paid once. Same operand order, unpack and
-// arithmetic as the ring kernel.
-template <int MT, int KS, int R, int KBS, bool ASYM>
-__global__ __launch_bounds__(256 * KS) void w4a16_batched_cres_kernel(
+// ring depth. Here each of the 4 KS compute wavefronts issues the code runs,
+// scales and zero-points of all its KBS (<= 16) k-blocks at once, so the
+// weight streams at the rate of the decode GEMV, and X (L2-resident) goes
+// through an R-slot LDS ring per k-split group that a wavefront of its own
+// fills: memory loads complete in order, so a compute wavefront that also
+// issued X loads would have to wait for all of its code runs before its
+// first X slot, and every MFMA would follow the weight stream instead of
+// overlapping it. With the loads split, step i waits only for the code run
+// of its own k-block (the compiler's in-order count) and for the block
+// barrier after which the loader has seen slot i land. Same operand order,
+// unpack and arithmetic as the ring kernel.
+template <int MT, int KS, int R, int KBS, bool ASYM, int NT>
+__global__ __launch_bounds__(64 * (NT + 1) * KS) void w4a16_batched_cres_kernel(
     const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
     uint16_t *__restrict__ Y)
 {
-    static_assert(MT <= 4 && KS * R * MT <= 32 && (KBS == 8 || KBS == 16) && (R - 2) * MT <= 63, "ring sizes");
+    constexpr int XI = MT * 4;                   // loader instructions per slot (1 KB each)
+    constexpr int CD = 5;                        // k-blocks of code runs in flight per wavefront
+    static_assert(MT <= 4 && KS * R * MT <= 32 && (KBS == 8 || KBS == 16) && (R - 2) * XI <= 63, "ring sizes");
     constexpr int SLOT = MT * 16 * 256;          // bytes of one k-block of X
     __shared__ __attribute__((aligned(1024))) unsigned char xs[32 * 16 * 256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = wave & 3, ks = wave >> 2;     // column tile, k-split group
+    const bool loader = wave >= NT * KS;         // waves NT KS .. (NT + 1) KS - 1 fill the X rings
+    const int wn = wave % NT, ks = loader ? wave - NT * KS : wave / NT;   // column tile, k-split group
     const int r16 = lane & 15, q = lane >> 4;
     const int kbase = ks * KBS;
     auto kblock = [&](int i) { return kbase + (i < KBS ? i : KBS - 1); };   // i may be past the end
     const uint32_t G = (uint32_t)(K >> 7), Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
-    const int n = blockIdx.x * 64 + wn * 16 + r16;
-    const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
     unsigned char *ring = xs + ks * R * SLOT;
 
-    // direct-to-LDS X loads: instruction j of wavefront wn fills rows
-    // 4 (4 j + wn) .. + 3 of a slot; lane i: row 4 (4 j + wn) + i / 16, stored
-    // chunk i % 16, logical chunk (i % 16) ^ (row % 16). (Fixed-size arrays:
-    // arrays sized by a template parameter and captured by the lambdas make
-    // this compiler drop the kernel's host stub.)
-    uint32_t xoff[4];
+    if (loader) {
+        // Slot j of the ring holds k-block kblock(j) of X, rows 0 .. 16 MT - 1
+        // (rows past M repeat row M - 1), 16 chunks of 16 bytes per row.
+        // Direct-to-LDS instruction e puts lane i at slot byte 1024 e + 16 i:
+        // chunk c = 64 e + i is row c / 16, stored chunk c % 16, logical chunk
+        // (c % 16) ^ xswz(row % 16).
+        // (a fixed-size array: one sized by a template parameter and captured
+        // by the lambda below makes this compiler drop the kernel's host stub)
+        uint32_t xoff[16];
 #pragma unroll
-    for (int j = 0; j < MT; j++) {
-        const int m = 4 * (4 * j + wn) + (lane >> 4);
-        const int c = (lane & 15) ^ (m & 15);
-        xoff[j] = ((uint32_t)(m < M ? m : M - 1) * (uint32_t)K + 8u * (uint32_t)c) * 2u;
+        for (int e = 0; e < XI; e++) {
+            const int m = (64 * e + lane) >> 4;
+            const int c = (lane & 15) ^ xswz(m & 15);
+            xoff[e] = ((uint32_t)(m < M ? m : M - 1) * (uint32_t)K + 8u * (uint32_t)c) * 2u;
+        }
+        const unsigned char *Xb = reinterpret_cast<const unsigned char *>(X);
+        auto issue_x = [&](int i) {
+            const int kc = kblock(i);
+            unsigned char *slot = ring + (i % R) * SLOT;
+#pragma unroll
+            for (int e = 0; e < XI; e++)
+                __builtin_amdgcn_global_load_lds(Xb + xoff[e] + (uint32_t)kc * 256u, slot + e * 1024, 16, 0, 0);
+        };
+#pragma unroll
+        for (int i = 0; i < R - 1; i++) issue_x(i);
+        // the compute wavefronts issue their code runs after this barrier, so
+        // the first X slots are ahead of the weight stream in the queues
+        __builtin_amdgcn_s_barrier();
+        // step i: slot i has landed once at most the later slots issued so
+        // far (R - 2, fewer near the end) are outstanding; after the barrier
+        // every compute wavefront is done with step i - 1, whose slot takes
+        // step i + R - 1 while there is one
+#pragma unroll
+        for (int i = 0; i < KBS; i++) {
+            asm volatile("" ::: "memory");
+            // (s_waitcnt takes a constant: one case per count, resolved once
+            // the loop is unrolled)
+            switch (i + R - 2 < KBS ? R - 2 : KBS - 1 - i) {
+            case 0: Q4_WAIT_VM_LGKM0(0); break;
+            case 1: Q4_WAIT_VM_LGKM0(XI); break;
+            case 2: Q4_WAIT_VM_LGKM0(2 * XI); break;
+            case 3: Q4_WAIT_VM_LGKM0(3 * XI); break;
+            case 4: Q4_WAIT_VM_LGKM0(4 * XI < 63 ? 4 * XI : 63); break;
+            case 5: Q4_WAIT_VM_LGKM0(5 * XI < 63 ? 5 * XI : 63); break;
+            default: Q4_WAIT_VM_LGKM0(6 * XI < 63 ? 6 * XI : 63); break;
+            }
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (i + R - 1 < KBS) issue_x(i + R - 1);
+        }
+        if (KS > 1) {
+            __syncthreads();
+            __syncthreads();
+        }
+        return;
     }
-    const unsigned char *Xb = reinterpret_cast<const unsigned char *>(X);
-    auto issue_x = [&](int i) {
-        const int kc = kblock(i);
-        unsigned char *slot = ring + (i % R) * SLOT;
-#pragma unroll
-        for (int j = 0; j < MT; j++)
-            __builtin_amdgcn_global_load_lds(Xb + xoff[j] + (uint32_t)kc * 256u, slot + (4 * j + wn) * 1024,
-                                             16, 0, 0);
-    };
 
-#pragma unroll
-    for (int i = 0; i < R - 1; i++) issue_x(i);
-    asm volatile("" ::: "memory");
+    const int n = blockIdx.x * (16 * NT) + wn * 16 + r16;
+    const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
+    __builtin_amdgcn_s_barrier();   // the loader's first X slots are issued
     // the group's scales and zero-points as whole runs (the host checks the
     // alignment): 2 KBS bytes of scales, KBS / 2 bytes of zero-points
     uint32_t sraw[8];
@@ -634,47 +686,61 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_cres_kernel(
             }
         }
     }
+    // Code runs: CD k-blocks ahead of the step that uses them. With every run
+    // of every wavefront requested at once the runs come back in no useful
+    // order and, loads completing in order, a wavefront's first k-block is
+    // complete only near the end of the whole stream; a short lead keeps the
+    // early k-blocks early.
     u32x4 cw[16];
-#pragma unroll
-    for (int i = 0; i < KBS; i++)
+    auto load_code = [&](int i) {
         cw[i] = *reinterpret_cast<const u32x4 *>(codes + (nrow * kh + (uint32_t)kblock(i) * 64u + q * 16u));
+    };
+#pragma unroll
+    for (int i = 0; i < CD; i++) load_code(i);
     asm volatile("" ::: "memory");
 
     floatx4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // Step i: wait until at most the X loads of steps i + 1 .. i + R - 2 are
-    // outstanding (for i <= R - 2 that also takes every code run, issued
-    // after X slot i: a stricter wait, never a looser one), meet the block
-    // (every wavefront is done with slot i - 1), refill slot i - 1 with step
-    // i + R - 1 (past the end: the last k-block again, into slots nobody
-    // reads), then compute step i from slot i.
+    // Step i: the block barrier (the loader has seen slot i land; this
+    // wavefront's reads of slot i - 1 are complete), then step i from slot i
+    // once the code run of k-block i is in (the compiler's wait).
 #pragma unroll
     for (int i = 0; i < KBS; i++) {
         asm volatile("" ::: "memory");
-        Q4_WAIT_VM_LGKM0((R - 2) * MT);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's LDS reads done
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue_x(i + R - 1);
-        asm volatile("" ::: "memory");
+        if (i + CD < KBS) load_code(i + CD);
         const unsigned char *slot = ring + (i % R) * SLOT;
         const uint32_t zp = (uint32_t)(zraw >> (4 * i)) & 15u;
         const uint32_t zadd = (0xE400u + zp) | ((0xD400u + 16u * zp) << 16);   // 1 at 1024, 1/16 at 64
         floatx4 part[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; mt++) part[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // all of the step's X fragments first: their LDS latency runs under
+        // the unpack instead of in front of each MFMA
+        half8 a[4][MT];
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++)
+                a[t][mt] = *reinterpret_cast<const half8 *>(slot + (mt * 16 + r16) * 256 + 16 * ((4 * q + t) ^ xswz(r16)));
+        // MFMA step t's four products issue with the unpack of step t + 1
+        // between them, one pair per product, so the VALU work runs in the
+        // matrix core's shadow instead of after it
+        u32x4 bv[2];
+        bv[0] = u32x4{unpack_pair(cw[i][0], 0, zadd), unpack_pair(cw[i][0], 1, zadd),
+                      unpack_pair(cw[i][0], 2, zadd), unpack_pair(cw[i][0], 3, zadd)};
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-            const uint32_t w = cw[i][t];
-            const u32x4 bv = {unpack_pair(w, 0, zadd), unpack_pair(w, 1, zadd),
-                              unpack_pair(w, 2, zadd), unpack_pair(w, 3, zadd)};
-            const half8 b = __builtin_bit_cast(half8, bv);
+            const half8 b = __builtin_bit_cast(half8, bv[t & 1]);
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++) {
-                const int m = mt * 16 + r16;
-                const half8 a = *reinterpret_cast<const half8 *>(slot + m * 256 + 16 * ((4 * q + t) ^ r16));
-                part[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, part[mt], 0, 0, 0);
+            for (int mt = 0; mt < 4; mt++) {
+                if (mt < MT) part[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t][mt], b, part[mt], 0, 0, 0);
+                if (t < 3) bv[(t + 1) & 1][mt] = unpack_pair(cw[i][t + 1], mt, zadd);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         const float s = h2f((uint16_t)(sraw[i >> 1] >> (16 * (i & 1))));
@@ -683,17 +749,16 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_cres_kernel(
 #pragma unroll
             for (int r = 0; r < 4; r++) acc[mt][r] = fmaf(part[mt][r], s, acc[mt][r]);
     }
-    Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
 
     if (KS > 1) {
         // the k-split groups' partial sums meet in LDS (group order fixed)
-        float *red = reinterpret_cast<float *>(xs);   // [KS - 1][4 wn][MT * 4][64]
+        float *red = reinterpret_cast<float *>(xs);   // [KS - 1][NT wn][MT * 4][64]
         __syncthreads();
         if (ks > 0) {
 #pragma unroll
             for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-                for (int r = 0; r < 4; r++) red[(((ks - 1) * 4 + wn) * MT * 4 + mt * 4 + r) * 64 + lane] = acc[mt][r];
+                for (int r = 0; r < 4; r++) red[(((ks - 1) * NT + wn) * MT * 4 + mt * 4 + r) * 64 + lane] = acc[mt][r];
         }
         __syncthreads();
         if (ks > 0) return;
@@ -702,7 +767,7 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_cres_kernel(
 #pragma unroll
             for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-                for (int r = 0; r < 4; r++) acc[mt][r] += red[(((g2 - 1) * 4 + wn) * MT * 4 + mt * 4 + r) * 64 + lane];
+                for (int r = 0; r < 4; r++) acc[mt][r] += red[(((g2 - 1) * NT + wn) * MT * 4 + mt * 4 + r) * 64 + lane];
     }
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
@@ -719,7 +784,7 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_cres_kernel(
 // wavefront (ks, wn) owns column tile wn over k-split group ks. All of X is
 // loaded once (through registers), stored in LDS in the operand k order of
 // the decode GEMV's unpack (each 16-byte chunk permuted to k offsets
-// 0,4,1,5,2,6,3,7) and XOR-swizzled (chunk c of row m at c ^ (m % 16)); then
+// 0,4,1,5,2,6,3,7) and XOR-swizzled (chunk c of row m at c ^ xswz(m % 16)); then
 // every scale, zero-point and code run of the wavefront's KBW k-blocks is
 // issued; one wait and one barrier make X visible, and from there the only
 // waits are the compiler's, in issue order, on the code runs. The unpack is
@@ -744,14 +809,14 @@ __global__ __launch_bounds__(64 * WN * KS) void w4a16_batched_xres_kernel(
     const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
 
     // X: 16 B chunk P (= k-block P / 256, row (P / 16) % 16, stored chunk
-    // P % 16) at LDS byte 16 P holds logical chunk (P % 16) ^ row, permuted
+    // P % 16) at LDS byte 16 P holds logical chunk (P % 16) ^ xswz(row), permuted
     constexpr int NCH = 32 * 16 * 16;                         // chunks when K = 4096
     constexpr int PER = (NCH + T - 1) / T;
     u32x4 xv[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) {
         const int P = tid + i * T;
-        const int kb = P >> 8, m = (P >> 4) & 15, c = (P & 15) ^ m;
+        const int kb = P >> 8, m = (P >> 4) & 15, c = (P & 15) ^ xswz(m);
         const int mc = m < M ? m : M - 1;
         xv[i] = u32x4{0u, 0u, 0u, 0u};
         if (kb < KB) xv[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)mc * K + kb * 128 + c * 8);
@@ -800,7 +865,7 @@ __global__ __launch_bounds__(64 * WN * KS) void w4a16_batched_xres_kernel(
         floatx4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-            const half8 a = *reinterpret_cast<const half8 *>(slot + 16 * ((4 * q + t) ^ r16));
+            const half8 a = *reinterpret_cast<const half8 *>(slot + 16 * ((4 * q + t) ^ xswz(r16)));
             part = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, dequant8(cw[p][t], zc), part, 0, 0, 0);
         }
         const uint32_t sw = sraw[p >> 1];
@@ -1120,6 +1185,15 @@ hipError_t launch_subg(const uint16_t *X, int64_t M, int N, int K, int g, const 
     return launch_subg_tiles<4, 2, 4>(X, M, N, K, g, codes, scales, zeros, Y, st);
 }
 
+// X ring depth of the whole-slice kernel: at most 32 k-blocks of 16 rows in
+// the 128 KB, at most 8 slots, and at most 63 loader instructions in flight
+// behind the slot a step waits for.
+constexpr int cres_ring(int mt, int ks)
+{
+    const int a = 32 / (mt * ks), b = 2 + 63 / (4 * mt);
+    return a < 8 ? (a < b ? a : b) : (8 < b ? 8 : b);
+}
+
 // Batched decode launcher (g = 128 assumed). K is split over KS groups of
 // wavefronts inside a block; each group's k-blocks must be a multiple of the
 // ring depth.
@@ -1163,15 +1237,25 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t 
     auto launch = [&](auto kernel, int ks) {
         kernel<<<blocks, 256 * ks, 0, st>>>(X, M, N, K, codes, scales, zeros, Y);
     };
+    // the whole-slice kernel: NT compute wavefronts (NT column tiles) and one
+    // X loader per k-split group; 3 column tiles when that still makes at most
+    // one round of blocks and 4 would leave CUs idle
+    const int cb3 = (N + 47) / 48, cb4 = (N + 63) / 64;
+    const bool nt3 = cb3 <= 256 && cb4 < 256;
+    auto launch_cres = [&](auto kernel, int ks, int nt) {
+        kernel<<<nt == 3 ? cb3 : cb4, 64 * (nt + 1) * ks, 0, st>>>(X, M, N, K, codes, scales, zeros, Y);
+    };
     // M > 16 with at most 16 k-blocks per k-split group: the wavefront's
     // weight slice is held in registers, only X goes through the LDS ring
     // (8 slots, or 4 when 4 m-tiles and 2 groups share the 128 KB)
     const bool runs_aligned = (reinterpret_cast<uintptr_t>(scales) & 15) == 0 &&
                               (!zeros || (reinterpret_cast<uintptr_t>(zeros) & 7) == 0);
     if (M > 16 && (KB == 8 || KB == 16 || KB == 32) && runs_aligned) {
-#define Q4_C(MT, KS, KBS)                                                                                  \
-    (zeros ? launch(w4a16_batched_cres_kernel<MT, KS, (32 / (MT * KS) > 8 ? 8 : 32 / (MT * KS)), KBS, true>, KS) \
-           : launch(w4a16_batched_cres_kernel<MT, KS, (32 / (MT * KS) > 8 ? 8 : 32 / (MT * KS)), KBS, false>, KS))
+#define Q4_C(MT, KS, KBS)                                                                                      \
+    (zeros ? (nt3 ? launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, true, 3>, KS, 3)     \
+                  : launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, true, 4>, KS, 4))    \
+           : (nt3 ? launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, false, 3>, KS, 3)    \
+                  : launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, false, 4>, KS, 4)))
         const bool mt2 = M <= 32;
         if (KB == 32) mt2 ? Q4_C(2, 2, 16) : Q4_C(4, 2, 16);
         else if (KB == 16) mt2 ? Q4_C(2, 2, 8) : Q4_C(4, 2, 8);
