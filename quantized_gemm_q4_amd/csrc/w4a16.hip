@@ -821,8 +821,11 @@ __global__ __launch_bounds__(64 * WN * KS) void w4a16_batched_xres_kernel(
         xv[i] = u32x4{0u, 0u, 0u, 0u};
         if (kb < KB) xv[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)mc * K + kb * 128 + c * 8);
     }
-    // then the scales and zero-points (needed first), then the code runs
+    // then the scales and zero-points (needed first), then the code runs,
+    // after a block barrier: every X load of the block is then ahead of the
+    // weight stream in the queues
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
     uint32_t sraw[KBW / 2], zraw = 0x88888888u;
     {
         const uint16_t *sp = scales + (nrow * G + kbase);
