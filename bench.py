@@ -17,7 +17,8 @@ The JSON line also carries:
   cpu_baseline  the CPU oracle (fp64 reference over the dequantized weights)
                 timed on this host's cores on the same step;
   extra         (every figure the median of 5 timed repeats) the same step as
-                two w4a16_linear launches, each layer alone,
+                two w4a16_linear launches, each layer alone, the harness's
+                floors (a one-element launch, device copies of the codes),
                 prefill (M = 2048, sym) TFLOP/s against the fp16 MFMA peak,
                 W8A8 (M = 2048, K = N = 8192) TOP/s against the int8 peak,
                 its FP8 E4M3 variant TFLOP/s against the fp8 peak, MXFP4
@@ -226,6 +227,11 @@ def main():
         ba = w4a16_bytes(1, 11008, 4096) + 4096 * 4
         extra["awq_decode_n11008"] = {"us": ta * 1e6, "GB/s": ba / ta / 1e9,
                                       "frac_hbm": ba / ta / 1e9 / HBM_PEAK_GBS}
+        # floors in the same harness (graph replays over the same number of
+        # copies), from library kernels: a one-element add per launch and
+        # device copies of the step's packed codes (read + write)
+        extra["floors"] = floors(graph_of, timed, reps, copies, dev,
+                                 [[L["copies"][c][0] for L in layers] for c in range(copies)])
         del layers
         torch.cuda.empty_cache()
 
@@ -489,6 +495,30 @@ def main():
         out.update(value=None, unit="GB/s", steps=0, warmup=args.warmup, ms_per_step=None,
                    config={"workload": f"partial run: {only}"})
     print(json.dumps(out), flush=True)
+
+
+def floors(graph_of, timed, reps, copies, dev, codes):
+    """Per-launch floors of the decode harness (graph replays over the weight
+    copies, as the GEMV figures): a one-element add, and device copies of the
+    packed codes of both layers and of the N = 11008 layer (codes[c] holds the
+    codes of the step's layers for weight copy c, N = 11008 first)."""
+    import torch
+    res = {}
+
+    def per_launch(fn):
+        g = graph_of(fn, copies)
+        g()
+        return timed(lambda i: g(), reps) / (reps * copies)
+
+    tiny = torch.zeros(1, device=dev)
+    res["launch_us"] = per_launch(lambda i: tiny.add_(1.0)) * 1e6
+    for name, sel in (("copy_step_codes", None), ("copy_n11008_codes", 0)):
+        src = [torch.cat([c.view(-1) for c in cs]) if sel is None else cs[sel].view(-1).clone() for cs in codes]
+        dst = torch.empty_like(src[0])
+        t = per_launch(lambda i: dst.copy_(src[i % copies]))
+        res[name] = {"bytes_moved": 2 * src[0].numel(), "us": t * 1e6, "GB/s": 2 * src[0].numel() / t / 1e9}
+        del src, dst
+    return res
 
 
 def measured_traffic():

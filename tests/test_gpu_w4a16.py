@@ -197,11 +197,12 @@ def test_batched_variants(orc, M, K, sym):
 
 
 # N large enough that 48-column blocks would not fit one round of the CUs:
-# the X-resident kernel then uses 64-column blocks (4 column tiles).
-@pytest.mark.parametrize("M", [8, 16])
+# the X-resident kernel (M <= 16) and the whole-slice kernel (16 < M <= 64,
+# one or two k-split groups) then use 64-column blocks (4 column tiles).
+@pytest.mark.parametrize("M,K", [(8, 1024), (16, 1024), (20, 1024), (64, 1024), (40, 4096)])
 @pytest.mark.parametrize("sym", [False, True])
-def test_batched_wide_n(orc, M, sym):
-    N, K = 12800, 1024
+def test_batched_wide_n(orc, M, K, sym):
+    N = 12800
     W, X = workloads.small_case(M * 11 + int(sym), M, N, K)
     run_case(orc, W, X, 128, sym, what=f"batched wide M={M} N={N} K={K} sym={sym}")
 
