@@ -1352,7 +1352,7 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
 {
     if (M == 0 || N == 0) return hipSuccess;
     const int m = (int)M, n = (int)N, k = (int)K;
-    if (g == 128 && M <= 16) {
+    if ((g == 128 || g == 64 || g == 32) && M <= 16) {
         const hipError_t e = launch_w4a16_gemv(X, M, N, K, g, codes, scales, zeros, Y, st);
         if (e != hipErrorNotSupported) return e;
     }

@@ -45,7 +45,17 @@ int gemv_waves_override()
 //
 // With SM (one X row only) x is replaced by the AWQ-scaled x'' = f2h(x /
 // as[k]) as it goes to LDS; the factors are loaded right behind X.
-template <int WAVES, int KBW, bool ASYM, bool ONE_ROW, bool SM = false>
+//
+// Group sizes 32 and 64 (GS): a lane's 16-byte code run covers the 32 k of
+// lane group q, which at g = 32 is a group of its own, so an MFMA step over
+// the four lane groups would mix four groups' scales. The four code dwords
+// of the four lane groups of a row are transposed first (v_permlane32_swap
+// across lane bit 5, v_permlane16_swap across lane bit 4): lane group q then
+// holds dword q of every 32-k run of the k-block, MFMA step t takes run t
+// (k = 32 t + 8 q .. + 7, one group at g = 32, half of one at g = 64) with
+// the X fragments read to match, and each group's exact fp32 partial sum is
+// multiplied by that group's scale, as for g = 128.
+template <int WAVES, int KBW, bool ASYM, bool ONE_ROW, bool SM = false, int GS = 128>
 __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M, int N, int K,
                                            const uint8_t *__restrict__ codes,
                                            const uint16_t *__restrict__ scales,
@@ -54,6 +64,9 @@ __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M
 {
     static_assert(!SM || ONE_ROW, "the fused activation scaling serves one X row");
     static_assert(KBW == 2 || KBW == 4 || KBW == 8, "vector scale / zero-point loads of 2, 4, 8 groups");
+    static_assert(GS == 128 || ((GS == 32 || GS == 64) && KBW <= 4 && !SM), "group sizes 32, 64 up to 4 k-blocks");
+    constexpr int GPK = 128 / GS;                            // groups per 128-wide k-block
+    constexpr int NS = KBW * GPK;                            // groups of the wavefront's k-blocks
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int kh = K >> 1;                                   // dwords per X row
     uint32_t *xs = reinterpret_cast<uint32_t *>(smem);      // [M][K/2] dwords
@@ -65,7 +78,7 @@ __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M
     const int kb0 = wave * KBW;
     const int n = blk * 16 + r16;
     const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
-    const uint32_t G = (uint32_t)K >> 7, Gz = (G + 1) >> 1;
+    const uint32_t G = (uint32_t)K / GS, Gz = (G + 1) >> 1;
     const int xchunks = K >> 3;                              // 16-byte chunks per X row
 
     // 1. loads: X, scales, zero-points, codes. With one X row each wavefront
@@ -91,23 +104,35 @@ __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M
     } else if ((int)threadIdx.x < xchunks) {
         x0 = *reinterpret_cast<const u32x4 *>(X + threadIdx.x * 8);
     }
-    uint32_t sraw[KBW / 2];
-    if constexpr (KBW == 8) {
-        const u32x4 s8 = *reinterpret_cast<const u32x4 *>(scales + (nrow * G + kb0));
+    // the scales (NS fp16) and zero-points (NS nibbles) of the wavefront's
+    // groups, as whole vector loads (the host checks their alignment)
+    uint32_t sraw[NS / 2];
+    {
+        const uint16_t *sp = scales + (nrow * G + (uint32_t)kb0 * GPK);
+        if constexpr (NS >= 8) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) sraw[i] = s8[i];
-    } else if constexpr (KBW == 4) {
-        const u32x2 s4 = *reinterpret_cast<const u32x2 *>(scales + (nrow * G + kb0));
-        sraw[0] = s4[0];
-        sraw[1] = s4[1];
-    } else {
-        sraw[0] = *reinterpret_cast<const uint32_t *>(scales + (nrow * G + kb0));
+            for (int v = 0; v < NS / 8; v++) {
+                const u32x4 s8 = reinterpret_cast<const u32x4 *>(sp)[v];
+#pragma unroll
+                for (int i = 0; i < 4; i++) sraw[4 * v + i] = s8[i];
+            }
+        } else if constexpr (NS == 4) {
+            const u32x2 s4 = *reinterpret_cast<const u32x2 *>(sp);
+            sraw[0] = s4[0];
+            sraw[1] = s4[1];
+        } else {
+            sraw[0] = *reinterpret_cast<const uint32_t *>(sp);
+        }
     }
-    uint32_t zraw = 0x88888888u;   // symmetric: zp = 8 (no branch, so no early wait)
+    uint64_t zraw = 0x8888888888888888ull;   // symmetric: zp = 8 (no branch, so no early wait)
     if (ASYM) {
-        if constexpr (KBW == 8) zraw = *reinterpret_cast<const uint32_t *>(zeros + (nrow * Gz + (kb0 >> 1)));
-        else if constexpr (KBW == 4) zraw = *reinterpret_cast<const uint16_t *>(zeros + (nrow * Gz + (kb0 >> 1)));
-        else zraw = zeros[nrow * Gz + (kb0 >> 1)];
+        const uint8_t *zp = zeros + (nrow * Gz + ((uint32_t)kb0 * GPK >> 1));
+        if constexpr (NS == 16) {
+            const u32x2 z = *reinterpret_cast<const u32x2 *>(zp);
+            zraw = (uint64_t)z[0] | ((uint64_t)z[1] << 32);
+        } else if constexpr (NS == 8) zraw = *reinterpret_cast<const uint32_t *>(zp);
+        else if constexpr (NS == 4) zraw = *reinterpret_cast<const uint16_t *>(zp);
+        else zraw = *zp;
     }
     u32x4 cw[KBW];
 #pragma unroll
@@ -142,28 +167,40 @@ __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M
         __syncthreads();
     }
 
-    // 3. compute, k-block by k-block. Each k-block has an accumulator of its
-    //    own, so one block's MFMA chain never waits on the previous block's
-    //    scaling (a shared accumulator serialises all of them).
-    const uint32_t *arow = xs + (r16 < M ? r16 : M - 1) * kh + q * 16 + kb0 * 64;
-    floatx4 part[KBW];
+    // 3. compute, k-block by k-block. Each group has an accumulator of its
+    //    own, so one group's MFMA chain never waits on the previous group's
+    //    scaling (a shared accumulator serialises all of them). MFMA step t
+    //    reads X chunk 4 q + t of the k-block (g = 128) or 4 t + q (g = 32,
+    //    64: the transposed code runs).
+    const uint32_t *arow = xs + (r16 < M ? r16 : M - 1) * kh + (GS == 128 ? q * 16 : q * 4) + kb0 * 64;
+    floatx4 part[NS];
 #pragma unroll
     for (int p = 0; p < KBW; p++) {
-        const ZeroConst zc = zero_const((zraw >> (4 * p)) & 15);
-        part[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+        u32x4 w = cw[p];
+        if constexpr (GS < 128) {
+            const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+            const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+            const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+            w = u32x4{s01[0], s01[1], s23[0], s23[1]};
+        }
+#pragma unroll
+        for (int j = 0; j < GPK; j++) part[p * GPK + j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-            const half8 a = *reinterpret_cast<const half8 *>(arow + p * 64 + t * 4);
-            part[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, dequant8(cw[p][t], zc), part[p], 0, 0, 0);
+            const int gi = p * GPK + t * GPK / 4;   // the wavefront's group of this step
+            const ZeroConst zc = zero_const((int)(zraw >> (4 * gi)) & 15);
+            const half8 a = *reinterpret_cast<const half8 *>(arow + p * 64 + (GS == 128 ? t * 4 : t * 16));
+            part[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, dequant8(w[t], zc), part[gi], 0, 0, 0);
         }
     }
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < KBW; p++) {
-        const uint32_t sw = sraw[p >> 1];
-        const float sc = h2f((uint16_t)((p & 1) ? (sw >> 16) : (sw & 0xffffu)));
+    for (int gi = 0; gi < NS; gi++) {
+        const uint32_t sw = sraw[gi >> 1];
+        const float sc = h2f((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xffffu)));
 #pragma unroll
-        for (int r = 0; r < 4; r++) acc[r] = fmaf(part[p][r], sc, acc[r]);
+        for (int r = 0; r < 4; r++) acc[r] = fmaf(part[gi][r], sc, acc[r]);
     }
 
 #pragma unroll
@@ -187,6 +224,16 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
     uint16_t *__restrict__ Y)
 {
     gemv_block<WAVES, KBW, ASYM, ONE_ROW>(X, M, N, K, codes, scales, zeros, Y, (int)blockIdx.x);
+}
+
+// The decode GEMV at group size 32 or 64 (KBW <= 4).
+template <int WAVES, int KBW, bool ASYM, bool ONE_ROW, int GS>
+__global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_sg_kernel(
+    const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    uint16_t *__restrict__ Y)
+{
+    gemv_block<WAVES, KBW, ASYM, ONE_ROW, false, GS>(X, M, N, K, codes, scales, zeros, Y, (int)blockIdx.x);
 }
 
 // The decode GEMV (one X row) on the AWQ-scaled x'' = f2h(x / awq_s[k]).
@@ -236,10 +283,11 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_multi_kernel(const uint
 // 4 or 8 per wavefront), X must fit in LDS next to the reduction buffer, and
 // the scale / zero-point runs of every layer must suit whole vector loads.
 bool pick_gemv(int64_t M, int64_t K, int64_t blocks, const uint16_t *const *scales,
-               const uint8_t *const *zeros, int count, int &waves_out, int &kbw_out, size_t &lds_out)
+               const uint8_t *const *zeros, int count, int &waves_out, int &kbw_out, size_t &lds_out,
+               int gs = 128)
 {
-    const int KB = (int)(K / 128);
-    const int G = KB, Gz = (G + 1) / 2;
+    const int KB = (int)(K / 128), gpk = 128 / gs;
+    const int G = (int)(K / gs), Gz = (G + 1) / 2;
     const int forced = gemv_waves_override();
     for (int waves : {16, 8, 4}) {
         if (forced && waves != forced) continue;
@@ -247,12 +295,16 @@ bool pick_gemv(int64_t M, int64_t K, int64_t blocks, const uint16_t *const *scal
         if (KB % waves != 0) continue;
         const int kbw = KB / waves;
         const size_t lds = (size_t)M * K * 2 + (size_t)waves * 4 * 64 * 4;
-        if ((kbw != 2 && kbw != 4 && kbw != 8) || lds > 64 * 1024) continue;
-        if (G % kbw != 0 || (kbw >= 4 && Gz % (kbw / 2) != 0)) continue;
+        if ((kbw != 2 && kbw != 4 && kbw != 8) || (gs < 128 && kbw > 4) || lds > 64 * 1024) continue;
+        // a wavefront loads the scales of its ns groups in pieces of up to 16
+        // bytes and their zero-points as one load of ns / 2 bytes: every row
+        // of both arrays must start on those boundaries
+        const int ns = kbw * gpk, ssz = ns * 2 < 16 ? ns * 2 : 16, zsz = ns / 2;
+        if ((2 * G) % ssz != 0 || (zsz > 1 && Gz % zsz != 0)) continue;
         bool ok = true;
         for (int i = 0; i < count; i++) {
-            if ((reinterpret_cast<uintptr_t>(scales[i]) & (kbw * 2 - 1)) != 0) ok = false;
-            if (zeros[i] && (reinterpret_cast<uintptr_t>(zeros[i]) & (kbw / 2 - 1)) != 0) ok = false;
+            if ((reinterpret_cast<uintptr_t>(scales[i]) & (ssz - 1)) != 0) ok = false;
+            if (zeros[i] && (reinterpret_cast<uintptr_t>(zeros[i]) & (zsz - 1)) != 0) ok = false;
         }
         if (!ok) continue;
         waves_out = waves;
@@ -293,18 +345,43 @@ hipError_t launch_w4a16_gemv(const uint16_t *X, int64_t M, int64_t N, int64_t K,
                              const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
                              uint16_t *Y, hipStream_t st)
 {
-    if (g != 128 || M > 16 || N * K / 2 >= (int64_t)0xFFFFFF00)   // 32-bit offsets in the kernel
+    if ((g != 128 && g != 64 && g != 32) || K % 128 != 0 || M > 16 ||
+        N * K / 2 >= (int64_t)0xFFFFFF00)   // 32-bit offsets in the kernel
         return hipErrorNotSupported;
     const int m = (int)M, n = (int)N, k = (int)K;
     const int blocks = (n + 15) / 16;
     int waves, kbw;
     size_t lds;
-    if (!pick_gemv(M, K, blocks, &scales, &zeros, 1, waves, kbw, lds)) return hipErrorNotSupported;
+    if (!pick_gemv(M, K, blocks, &scales, &zeros, 1, waves, kbw, lds, g)) return hipErrorNotSupported;
     const bool asym = zeros != nullptr, one_row = m == 1;
     auto launch = [&](auto kernel) {
         kernel<<<blocks, waves * 64, lds, st>>>(X, m, n, k, codes, scales, zeros, Y);
     };
-    Q4_GEMV_DISPATCH(w4a16_gemv_kernel);
+    if (g == 128) {
+        Q4_GEMV_DISPATCH(w4a16_gemv_kernel);
+        return hipGetLastError();
+    }
+    // group sizes 32 and 64: 2 or 4 k-blocks per wavefront
+    auto launch4 = [&](auto k_a1, auto k_a0, auto k_s1, auto k_s0) {
+        if (asym) one_row ? launch(k_a1) : launch(k_a0);
+        else one_row ? launch(k_s1) : launch(k_s0);
+    };
+#define Q4_SG(W, B, GS)                                                                           \
+    launch4(w4a16_gemv_sg_kernel<W, B, true, true, GS>, w4a16_gemv_sg_kernel<W, B, true, false, GS>, \
+            w4a16_gemv_sg_kernel<W, B, false, true, GS>, w4a16_gemv_sg_kernel<W, B, false, false, GS>)
+#define Q4_SG_W(GS)                                                                               \
+    do {                                                                                          \
+        if (waves == 4 && kbw == 4) Q4_SG(4, 4, GS);                                              \
+        else if (waves == 4) Q4_SG(4, 2, GS);                                                     \
+        else if (waves == 8 && kbw == 4) Q4_SG(8, 4, GS);                                         \
+        else if (waves == 8) Q4_SG(8, 2, GS);                                                     \
+        else if (kbw == 4) Q4_SG(16, 4, GS);                                                      \
+        else Q4_SG(16, 2, GS);                                                                    \
+    } while (0)
+    if (g == 64) Q4_SG_W(64);
+    else Q4_SG_W(32);
+#undef Q4_SG_W
+#undef Q4_SG
     return hipGetLastError();
 }
 

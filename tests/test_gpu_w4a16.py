@@ -253,6 +253,22 @@ def test_small_group_sizes(orc, M, N, K, g, sym):
     run_case(orc, W, X, g, sym, what=f"g={g} M={M} N={N} K={K} sym={sym}")
 
 
+# g = 32 and 64 on the decode GEMV (M <= 16, K a multiple of 128): the code
+# runs transposed across the four lane groups so that each MFMA step sums one
+# group; 2 and 4 k-blocks per wavefront (K = 1024 / 2048 / 4096 and the block
+# counts), one X row and several, ragged N, and the decode workload's shapes.
+GEMV_SMALL_G = [(1, 300, 1024), (1, 300, 2048), (3, 130, 2048), (7, 1000, 1024), (16, 300, 4096),
+                (1, 11008, 4096), (16, 4096, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_SMALL_G)
+@pytest.mark.parametrize("g", [32, 64])
+@pytest.mark.parametrize("sym", [False, True])
+def test_small_group_gemv(orc, M, N, K, g, sym):
+    W, X = workloads.small_case(M * 13 + N + K + g + int(sym), M, N, K)
+    run_case(orc, W, X, g, sym, what=f"gemv g={g} M={M} N={N} K={K} sym={sym}")
+
+
 @pytest.mark.parametrize("M", [1, 17, 65, 300])
 @pytest.mark.parametrize("g", [256, 384])
 @pytest.mark.parametrize("sym", [False, True])
@@ -262,12 +278,12 @@ def test_large_group_sizes(orc, M, g, sym):
     run_case(orc, W, X, g, sym, what=f"g={g} M={M} N={N} K={K} sym={sym}")
 
 
-@pytest.mark.parametrize("M,K", [(40, 192), (300, 512), (300, 96)])
+@pytest.mark.parametrize("M,K", [(40, 192), (300, 512), (300, 96), (1, 1024), (8, 1024), (16, 4096)])
 @pytest.mark.parametrize("g", [32, 64])
 def test_small_group_one_hot(orc, M, K, g):
-    """One-hot X through the small-group kernel and the large-M GEMM at g =
-    32 / 64: Y[m, n] = fp16(w_hat[n, k(m)]) exactly (pins each group's scale
-    and zero-point indexing)."""
+    """One-hot X through the small-group kernel, the decode GEMV (M <= 16) and
+    the large-M GEMM at g = 32 / 64: Y[m, n] = fp16(w_hat[n, k(m)]) exactly
+    (pins each group's scale and zero-point indexing and the lane transpose)."""
     if K % g:
         pytest.skip("K must be a multiple of g")
     N = 70
