@@ -790,13 +790,16 @@ __global__ __launch_bounds__(64 * (NT + 1) * KS) void w4a16_batched_cres_kernel(
 // waits are the compiler's, in issue order, on the code runs. The unpack is
 // the GEMV's (9 operations per 8 weights, 16 (u - zp) exact; the 1/16 is
 // folded into the fp32 group scale).
-template <int WN, int KS, int KBW, bool ASYM>
+template <int WN, int KS, int KBW, bool ASYM, int GS = 128>
 __global__ __launch_bounds__(64 * WN * KS) void w4a16_batched_xres_kernel(
     const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
     uint16_t *__restrict__ Y)
 {
     static_assert(KS * KBW <= 32, "X must fit the 128 KB of LDS");
+    static_assert(GS == 32 || GS == 64 || GS == 128, "group sizes");
+    constexpr int GPK = 128 / GS;                 // groups per 128-wide k-block
+    constexpr int NS = KBW * GPK;                 // groups of the wavefront's k-blocks
     constexpr int T = 64 * WN * KS;
     __shared__ __attribute__((aligned(1024))) unsigned char xs[32 * 16 * 256];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -804,7 +807,7 @@ __global__ __launch_bounds__(64 * WN * KS) void w4a16_batched_xres_kernel(
     const int r16 = lane & 15, q = lane >> 4;
     const int kbase = ks * KBW;
     const int KB = KS * KBW;
-    const uint32_t G = (uint32_t)KB, Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
+    const uint32_t G = (uint32_t)(KB * GPK), Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
     const int n = blockIdx.x * 16 * WN + wn * 16 + r16;
     const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
 
@@ -826,14 +829,21 @@ __global__ __launch_bounds__(64 * WN * KS) void w4a16_batched_xres_kernel(
     // weight stream in the queues
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    uint32_t sraw[KBW / 2], zraw = 0x88888888u;
-    {
-        const uint16_t *sp = scales + (nrow * G + kbase);
-        if constexpr (KBW == 8) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(sp);
+    // scales (NS fp16) and zero-points (NS nibbles) of the wavefront's groups
+    // as whole vector loads (the host checks the alignment)
+    uint32_t sraw[NS / 2], zr[(NS + 7) / 8];
 #pragma unroll
-            for (int i = 0; i < 4; i++) sraw[i] = v[i];
-        } else if constexpr (KBW == 4) {
+    for (int i = 0; i < (NS + 7) / 8; i++) zr[i] = 0x88888888u;
+    {
+        const uint16_t *sp = scales + (nrow * G + (uint32_t)kbase * GPK);
+        if constexpr (NS >= 8) {
+#pragma unroll
+            for (int v8 = 0; v8 < NS / 8; v8++) {
+                const u32x4 v = reinterpret_cast<const u32x4 *>(sp)[v8];
+#pragma unroll
+                for (int i = 0; i < 4; i++) sraw[4 * v8 + i] = v[i];
+            }
+        } else if constexpr (NS == 4) {
             const u32x2 v = *reinterpret_cast<const u32x2 *>(sp);
             sraw[0] = v[0];
             sraw[1] = v[1];
@@ -841,10 +851,18 @@ __global__ __launch_bounds__(64 * WN * KS) void w4a16_batched_xres_kernel(
             sraw[0] = *reinterpret_cast<const uint32_t *>(sp);
         }
         if (ASYM) {
-            const uint8_t *zpp = zeros + (nrow * Gz + (kbase >> 1));
-            if constexpr (KBW == 8) zraw = *reinterpret_cast<const uint32_t *>(zpp);
-            else if constexpr (KBW == 4) zraw = *reinterpret_cast<const uint16_t *>(zpp);
-            else zraw = *zpp;
+            const uint8_t *zpp = zeros + (nrow * Gz + ((uint32_t)kbase * GPK >> 1));
+            if constexpr (NS == 32) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(zpp);
+#pragma unroll
+                for (int i = 0; i < 4; i++) zr[i] = v[i];
+            } else if constexpr (NS == 16) {
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(zpp);
+                zr[0] = v[0];
+                zr[1] = v[1];
+            } else if constexpr (NS == 8) zr[0] = *reinterpret_cast<const uint32_t *>(zpp);
+            else if constexpr (NS == 4) zr[0] = *reinterpret_cast<const uint16_t *>(zpp);
+            else zr[0] = *zpp;
         }
     }
     asm volatile("" ::: "memory");
@@ -860,21 +878,41 @@ __global__ __launch_bounds__(64 * WN * KS) void w4a16_batched_xres_kernel(
     }
     __syncthreads();
 
+    // per k-block: at g = 32 / 64 the four code dwords of the row's four lane
+    // groups are transposed first (as in the decode GEMV), so MFMA step t
+    // sums one 32-k run (X chunk 4 t + q) inside one group; each group's
+    // exact partial sum is scaled by its own scale
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < KBW; p++) {
         const unsigned char *slot = xs + (kbase + p) * 4096 + r16 * 256;
-        const ZeroConst zc = zero_const((zraw >> (4 * p)) & 15);
-        floatx4 part = {0.f, 0.f, 0.f, 0.f};
+        u32x4 w = cw[p];
+        if constexpr (GS < 128) {
+            const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+            const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+            const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+            w = u32x4{s01[0], s01[1], s23[0], s23[1]};
+        }
+        floatx4 part[GPK];
+#pragma unroll
+        for (int j = 0; j < GPK; j++) part[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-            const half8 a = *reinterpret_cast<const half8 *>(slot + 16 * ((4 * q + t) ^ xswz(r16)));
-            part = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, dequant8(cw[p][t], zc), part, 0, 0, 0);
+            const int j = t * GPK / 4, gi = p * GPK + j;
+            const ZeroConst zc = zero_const((int)(zr[gi >> 3] >> (4 * (gi & 7))) & 15);
+            const int chunk = GS == 128 ? 4 * q + t : 4 * t + q;
+            const half8 a = *reinterpret_cast<const half8 *>(slot + 16 * (chunk ^ xswz(r16)));
+            part[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, dequant8(w[t], zc), part[j], 0, 0, 0);
         }
-        const uint32_t sw = sraw[p >> 1];
-        const float s = scale16((uint16_t)((p & 1) ? (sw >> 16) : (sw & 0xffffu)));
 #pragma unroll
-        for (int r = 0; r < 4; r++) acc[r] = fmaf(part[r], s, acc[r]);
+        for (int j = 0; j < GPK; j++) {
+            const int gi = p * GPK + j;
+            const uint32_t sw = sraw[gi >> 1];
+            const float s = scale16((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xffffu)));
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[r] = fmaf(part[j][r], s, acc[r]);
+        }
     }
 
     if (KS > 1) {
@@ -1213,11 +1251,12 @@ constexpr int cres_ring(int mt, int ks)
 // Batched decode launcher (g = 128 assumed). K is split over KS groups of
 // wavefronts inside a block; each group's k-blocks must be a multiple of the
 // ring depth.
-hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t *codes,
+hipError_t launch_batched(const uint16_t *X, int M, int N, int K, int g, const uint8_t *codes,
                           const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
                           hipStream_t st)
 {
-    if (M < 1 || M > 64 || K % 128 != 0) return hipErrorNotSupported;
+    if (M < 1 || M > 64 || K % 128 != 0 || (g != 128 && g != 64 && g != 32)) return hipErrorNotSupported;
+    const int gpk = 128 / g;
     // these kernels index the codes and X with 32-bit byte offsets; larger
     // operands take the skinny kernel (64-bit offsets)
     if ((int64_t)N * (K / 2) >= ((int64_t)1 << 32) - 256 || (int64_t)M * K * 2 >= ((int64_t)1 << 32))
@@ -1229,27 +1268,38 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, const uint8_t 
     // 3 column tiles per block when that fills the CUs better than 4
     if (M <= 16 && (KB == 8 || KB == 16 || KB == 32)) {
         const int kbw = KB / 4;
-        const int Gz = (KB + 1) / 2;
-        const bool aligned = (reinterpret_cast<uintptr_t>(scales) & (kbw * 2 - 1)) == 0 &&
-                             (!zeros || ((reinterpret_cast<uintptr_t>(zeros) & (kbw / 2 - 1)) == 0 &&
-                                         Gz % (kbw / 2) == 0));
+        // a wavefront's ns groups: scales in loads of up to 16 bytes, zero-points
+        // in one load of ns / 2 bytes; every row of both must start on them
+        const int G = KB * gpk, Gz = (G + 1) / 2, ns = kbw * gpk;
+        const int ssz = 2 * ns < 16 ? 2 * ns : 16, zsz = ns / 2;
+        const bool aligned = (reinterpret_cast<uintptr_t>(scales) & (ssz - 1)) == 0 && (2 * G) % ssz == 0 &&
+                             (!zeros || ((reinterpret_cast<uintptr_t>(zeros) & (zsz - 1)) == 0 &&
+                                         Gz % zsz == 0));
         if (aligned) {
             const int b4 = (N + 63) / 64, b3 = (N + 47) / 48;
             const bool three = b3 <= 256 && b4 < 256;   // every CU busy with 3, some idle with 4
             const int nb = three ? b3 : b4;
             auto go = [&](auto kernel, int wn) { kernel<<<nb, 256 * wn, 0, st>>>(X, M, N, K, codes, scales, zeros, Y); };
+#define Q4_XRES_G(WN, GS)                                                                             \
+    do {                                                                                              \
+        if (kbw == 8) zeros ? go(w4a16_batched_xres_kernel<WN, 4, 8, true, GS>, WN) : go(w4a16_batched_xres_kernel<WN, 4, 8, false, GS>, WN); \
+        else if (kbw == 4) zeros ? go(w4a16_batched_xres_kernel<WN, 4, 4, true, GS>, WN) : go(w4a16_batched_xres_kernel<WN, 4, 4, false, GS>, WN); \
+        else zeros ? go(w4a16_batched_xres_kernel<WN, 4, 2, true, GS>, WN) : go(w4a16_batched_xres_kernel<WN, 4, 2, false, GS>, WN); \
+    } while (0)
 #define Q4_XRES(WN)                                                                                   \
     do {                                                                                              \
-        if (kbw == 8) zeros ? go(w4a16_batched_xres_kernel<WN, 4, 8, true>, WN) : go(w4a16_batched_xres_kernel<WN, 4, 8, false>, WN); \
-        else if (kbw == 4) zeros ? go(w4a16_batched_xres_kernel<WN, 4, 4, true>, WN) : go(w4a16_batched_xres_kernel<WN, 4, 4, false>, WN); \
-        else zeros ? go(w4a16_batched_xres_kernel<WN, 4, 2, true>, WN) : go(w4a16_batched_xres_kernel<WN, 4, 2, false>, WN); \
+        if (g == 128) Q4_XRES_G(WN, 128);                                                             \
+        else if (g == 64) Q4_XRES_G(WN, 64);                                                          \
+        else Q4_XRES_G(WN, 32);                                                                       \
     } while (0)
             if (three) Q4_XRES(3);
             else Q4_XRES(4);
 #undef Q4_XRES
+#undef Q4_XRES_G
             return hipGetLastError();
         }
     }
+    if (g != 128) return hipErrorNotSupported;   // the kernels below sum whole 128-wide groups
     auto launch = [&](auto kernel, int ks) {
         kernel<<<blocks, 256 * ks, 0, st>>>(X, M, N, K, codes, scales, zeros, Y);
     };
@@ -1383,11 +1433,11 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
         else asym ? launch(w4a16_gemm_kernel<11, 1, true>, 512) : launch(w4a16_gemm_kernel<11, 1, false>, 512);
         return hipGetLastError();
     }
-    if (g % 128 != 0) return launch_subg(X, M, n, k, g, codes, scales, zeros, Y, st);
-    if (g == 128 && M <= 64) {
-        const hipError_t e = launch_batched(X, m, n, k, codes, scales, zeros, Y, st);
+    if ((g == 128 || g == 64 || g == 32) && M <= 64) {
+        const hipError_t e = launch_batched(X, m, n, k, g, codes, scales, zeros, Y, st);
         if (e != hipErrorNotSupported) return e;
     }
+    if (g % 128 != 0) return launch_subg(X, M, n, k, g, codes, scales, zeros, Y, st);
     if (M <= 16) return launch_skinny<1, 1, 8>(X, m, n, k, g, codes, scales, zeros, Y, st);
     if (M <= 32) return launch_skinny<2, 2, 4>(X, m, n, k, g, codes, scales, zeros, Y, st);
     if (M <= 64) return launch_skinny<4, 2, 4>(X, m, n, k, g, codes, scales, zeros, Y, st);

@@ -253,12 +253,14 @@ def test_small_group_sizes(orc, M, N, K, g, sym):
     run_case(orc, W, X, g, sym, what=f"g={g} M={M} N={N} K={K} sym={sym}")
 
 
-# g = 32 and 64 on the decode GEMV (M <= 16, K a multiple of 128): the code
-# runs transposed across the four lane groups so that each MFMA step sums one
-# group; 2 and 4 k-blocks per wavefront (K = 1024 / 2048 / 4096 and the block
-# counts), one X row and several, ragged N, and the decode workload's shapes.
+# g = 32 and 64 on the decode GEMV (M <= 16, X within its LDS) and on the
+# X-resident batched kernel (M <= 16 otherwise: K = 4096 with M >= 8, K = 2048
+# with M = 16; 3 or 4 column tiles per block): the code runs transposed
+# across the four lane groups so that each MFMA step sums one group; 2, 4 and
+# 8 k-blocks per wavefront, one X row and several, ragged N, and the decode
+# workload's shapes.
 GEMV_SMALL_G = [(1, 300, 1024), (1, 300, 2048), (3, 130, 2048), (7, 1000, 1024), (16, 300, 4096),
-                (1, 11008, 4096), (16, 4096, 4096)]
+                (1, 11008, 4096), (16, 4096, 4096), (8, 300, 4096), (16, 300, 2048), (10, 12800, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMV_SMALL_G)
