@@ -584,7 +584,7 @@ __global__ __launch_bounds__(256 * KS) void w4a16_batched_kernel(
 // of its own k-block (the compiler's in-order count) and for the block
 // barrier after which the loader has seen slot i land. Same operand order,
 // unpack and arithmetic as the ring kernel.
-template <int MT, int KS, int R, int KBS, bool ASYM, int NT>
+template <int MT, int KS, int R, int KBS, bool ASYM, int NT, int GS = 128>
 __global__ __launch_bounds__(64 * (NT + 1) * KS) void w4a16_batched_cres_kernel(
     const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
@@ -592,6 +592,9 @@ __global__ __launch_bounds__(64 * (NT + 1) * KS) void w4a16_batched_cres_kernel(
 {
     constexpr int XI = MT * 4;                   // loader instructions per slot (1 KB each)
     constexpr int CD = 5;                        // k-blocks of code runs in flight per wavefront
+    static_assert(GS == 32 || GS == 64 || GS == 128, "group sizes");
+    constexpr int GPK = 128 / GS;                // groups per 128-wide k-block
+    constexpr int NS = KBS * GPK;                // groups of the wavefront's k-blocks
     static_assert(MT <= 4 && KS * R * MT <= 32 && (KBS == 8 || KBS == 16) && (R - 2) * XI <= 63, "ring sizes");
     constexpr int SLOT = MT * 16 * 256;          // bytes of one k-block of X
     __shared__ __attribute__((aligned(1024))) unsigned char xs[32 * 16 * 256];
@@ -601,7 +604,7 @@ __global__ __launch_bounds__(64 * (NT + 1) * KS) void w4a16_batched_cres_kernel(
     const int r16 = lane & 15, q = lane >> 4;
     const int kbase = ks * KBS;
     auto kblock = [&](int i) { return kbase + (i < KBS ? i : KBS - 1); };   // i may be past the end
-    const uint32_t G = (uint32_t)(K >> 7), Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
+    const uint32_t G = (uint32_t)(K / GS), Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
     unsigned char *ring = xs + ks * R * SLOT;
 
     if (loader) {
@@ -664,25 +667,34 @@ __global__ __launch_bounds__(64 * (NT + 1) * KS) void w4a16_batched_cres_kernel(
     const int n = blockIdx.x * (16 * NT) + wn * 16 + r16;
     const uint32_t nrow = (uint32_t)(n < N ? n : N - 1);
     __builtin_amdgcn_s_barrier();   // the loader's first X slots are issued
-    // the group's scales and zero-points as whole runs (the host checks the
-    // alignment): 2 KBS bytes of scales, KBS / 2 bytes of zero-points
-    uint32_t sraw[8];
-    uint64_t zraw = 0x8888888888888888ull;
-    {
-        const u32x4 *sp = reinterpret_cast<const u32x4 *>(scales + (nrow * G + kbase));
+    // the k-split group's scales and zero-points as whole runs (the host
+    // checks the alignment): 2 NS bytes of scales, NS / 2 bytes of zero-points
+    uint32_t sraw[NS / 2], zr[NS / 8];
 #pragma unroll
-        for (int v = 0; v < KBS / 8; v++) {
+    for (int v = 0; v < NS / 8; v++) zr[v] = 0x88888888u;
+    {
+        const u32x4 *sp = reinterpret_cast<const u32x4 *>(scales + (nrow * G + (uint32_t)kbase * GPK));
+#pragma unroll
+        for (int v = 0; v < NS / 8; v++) {
             const u32x4 t = sp[v];
 #pragma unroll
             for (int e = 0; e < 4; e++) sraw[4 * v + e] = t[e];
         }
         if (ASYM) {
-            const uint8_t *zpp = zeros + (nrow * Gz + (kbase >> 1));
-            if constexpr (KBS == 16) {
+            const uint8_t *zpp = zeros + (nrow * Gz + ((uint32_t)kbase * GPK >> 1));
+            if constexpr (NS >= 32) {
+#pragma unroll
+                for (int v = 0; v < NS / 32; v++) {
+                    const u32x4 t = reinterpret_cast<const u32x4 *>(zpp)[v];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) zr[4 * v + e] = t[e];
+                }
+            } else if constexpr (NS == 16) {
                 const u32x2 t = *reinterpret_cast<const u32x2 *>(zpp);
-                zraw = (uint64_t)t[0] | ((uint64_t)t[1] << 32);
+                zr[0] = t[0];
+                zr[1] = t[1];
             } else {
-                zraw = *reinterpret_cast<const uint32_t *>(zpp);
+                zr[0] = *reinterpret_cast<const uint32_t *>(zpp);
             }
         }
     }
@@ -702,6 +714,22 @@ __global__ __launch_bounds__(64 * (NT + 1) * KS) void w4a16_batched_cres_kernel(
     floatx4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // Group gi's exact fp32 sums build in part[gi & 1] and are scaled into acc
+    // one MFMA step after the group's last one (the products have landed by
+    // then). The asm pins each scaling where it stands: left free, the
+    // compiler sinks all of them past the loop and keeps every group's
+    // partial sums live to the end (hundreds of registers at g = 32).
+    floatx4 part[2][MT];
+    const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    auto scale_group = [&](int gi) {
+        const float s = h2f((uint16_t)(sraw[gi >> 1] >> (16 * (gi & 1))));
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[mt][r] = fmaf(part[gi & 1][mt][r], s, acc[mt][r]);
+            asm volatile("" : "+v"(acc[mt]));
+        }
+    };
 
     // Step i: the block barrier (the loader has seen slot i land; this
     // wavefront's reads of slot i - 1 are complete), then step i from slot i
@@ -714,11 +742,23 @@ __global__ __launch_bounds__(64 * (NT + 1) * KS) void w4a16_batched_cres_kernel(
         asm volatile("" ::: "memory");
         if (i + CD < KBS) load_code(i + CD);
         const unsigned char *slot = ring + (i % R) * SLOT;
-        const uint32_t zp = (uint32_t)(zraw >> (4 * i)) & 15u;
-        const uint32_t zadd = (0xE400u + zp) | ((0xD400u + 16u * zp) << 16);   // 1 at 1024, 1/16 at 64
-        floatx4 part[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++) part[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // (1 at 1024, 1/16 at 64) of the zero-point of MFMA step t's group
+        auto zadd_of = [&](int t) {
+            const int gi = i * GPK + t * GPK / 4;
+            const uint32_t zp = (zr[gi >> 3] >> (4 * (gi & 7))) & 15u;
+            return (0xE400u + zp) | ((0xD400u + 16u * zp) << 16);
+        };
+        // at g = 32 / 64 the code dwords of the row's four lane groups are
+        // transposed (as in the decode GEMV): MFMA step t then sums the 32-k
+        // run t (X chunk 4 t + q), inside one group
+        u32x4 w = cw[i];
+        if constexpr (GS < 128) {
+            const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+            const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+            const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+            w = u32x4{s01[0], s01[1], s23[0], s23[1]};
+        }
         // all of the step's X fragments first: their LDS latency runs under
         // the unpack instead of in front of each MFMA
         half8 a[4][MT];
@@ -726,29 +766,35 @@ __global__ __launch_bounds__(64 * (NT + 1) * KS) void w4a16_batched_cres_kernel(
         for (int t = 0; t < 4; t++)
 #pragma unroll
             for (int mt = 0; mt < MT; mt++)
-                a[t][mt] = *reinterpret_cast<const half8 *>(slot + (mt * 16 + r16) * 256 + 16 * ((4 * q + t) ^ xswz(r16)));
+                a[t][mt] = *reinterpret_cast<const half8 *>(
+                    slot + (mt * 16 + r16) * 256 + 16 * ((GS == 128 ? 4 * q + t : 4 * t + q) ^ xswz(r16)));
         // MFMA step t's four products issue with the unpack of step t + 1
         // between them, one pair per product, so the VALU work runs in the
         // matrix core's shadow instead of after it
         u32x4 bv[2];
-        bv[0] = u32x4{unpack_pair(cw[i][0], 0, zadd), unpack_pair(cw[i][0], 1, zadd),
-                      unpack_pair(cw[i][0], 2, zadd), unpack_pair(cw[i][0], 3, zadd)};
+        {
+            const uint32_t z0 = zadd_of(0);
+            bv[0] = u32x4{unpack_pair(w[0], 0, z0), unpack_pair(w[0], 1, z0),
+                          unpack_pair(w[0], 2, z0), unpack_pair(w[0], 3, z0)};
+        }
 #pragma unroll
         for (int t = 0; t < 4; t++) {
             const half8 b = __builtin_bit_cast(half8, bv[t & 1]);
+            const uint32_t zn = t < 3 ? zadd_of(t + 1) : 0u;
+            const int gi = i * GPK + t * GPK / 4;          // the step's group
+            const bool first = t % (4 / GPK) == 0;         // its first step
 #pragma unroll
             for (int mt = 0; mt < 4; mt++) {
-                if (mt < MT) part[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t][mt], b, part[mt], 0, 0, 0);
-                if (t < 3) bv[(t + 1) & 1][mt] = unpack_pair(cw[i][t + 1], mt, zadd);
+                if (mt < MT)
+                    part[gi & 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        a[t][mt], b, first ? zero4 : part[gi & 1][mt], 0, 0, 0);
+                if (t < 3) bv[(t + 1) & 1][mt] = unpack_pair(w[t + 1], mt, zn);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (first && gi > 0) scale_group(gi - 1);
         }
-        const float s = h2f((uint16_t)(sraw[i >> 1] >> (16 * (i & 1))));
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) acc[mt][r] = fmaf(part[mt][r], s, acc[mt][r]);
     }
+    scale_group(NS - 1);
 
     if (KS > 1) {
         // the k-split groups' partial sums meet in LDS (group order fixed)
@@ -1299,7 +1345,6 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, int g, const u
             return hipGetLastError();
         }
     }
-    if (g != 128) return hipErrorNotSupported;   // the kernels below sum whole 128-wide groups
     auto launch = [&](auto kernel, int ks) {
         kernel<<<blocks, 256 * ks, 0, st>>>(X, M, N, K, codes, scales, zeros, Y);
     };
@@ -1314,21 +1359,28 @@ hipError_t launch_batched(const uint16_t *X, int M, int N, int K, int g, const u
     // M > 16 with at most 16 k-blocks per k-split group: the wavefront's
     // weight slice is held in registers, only X goes through the LDS ring
     // (8 slots, or 4 when 4 m-tiles and 2 groups share the 128 KB)
+    // (scales: whole 16-byte runs; zero-points: runs of KBS gpk / 2 bytes, at
+    // most 16 per load; every row of both arrays holds whole runs for these K)
+    const int kbs_z = (KB == 32 ? 16 : 8) * gpk / 2;
     const bool runs_aligned = (reinterpret_cast<uintptr_t>(scales) & 15) == 0 &&
-                              (!zeros || (reinterpret_cast<uintptr_t>(zeros) & 7) == 0);
+                              (!zeros || (reinterpret_cast<uintptr_t>(zeros) & ((kbs_z < 16 ? kbs_z : 16) - 1)) == 0);
     if (M > 16 && (KB == 8 || KB == 16 || KB == 32) && runs_aligned) {
-#define Q4_C(MT, KS, KBS)                                                                                      \
-    (zeros ? (nt3 ? launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, true, 3>, KS, 3)     \
-                  : launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, true, 4>, KS, 4))    \
-           : (nt3 ? launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, false, 3>, KS, 3)    \
-                  : launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, false, 4>, KS, 4)))
+#define Q4_C_G(MT, KS, KBS, GS)                                                                                    \
+    (zeros ? (nt3 ? launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, true, 3, GS>, KS, 3)     \
+                  : launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, true, 4, GS>, KS, 4))    \
+           : (nt3 ? launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, false, 3, GS>, KS, 3)    \
+                  : launch_cres(w4a16_batched_cres_kernel<MT, KS, cres_ring(MT, KS), KBS, false, 4, GS>, KS, 4)))
+#define Q4_C(MT, KS, KBS)                                                                                          \
+    (g == 128 ? Q4_C_G(MT, KS, KBS, 128) : g == 64 ? Q4_C_G(MT, KS, KBS, 64) : Q4_C_G(MT, KS, KBS, 32))
         const bool mt2 = M <= 32;
         if (KB == 32) mt2 ? Q4_C(2, 2, 16) : Q4_C(4, 2, 16);
         else if (KB == 16) mt2 ? Q4_C(2, 2, 8) : Q4_C(4, 2, 8);
         else mt2 ? Q4_C(2, 1, 8) : Q4_C(4, 1, 8);
 #undef Q4_C
+#undef Q4_C_G
         return hipGetLastError();
     }
+    if (g != 128) return hipErrorNotSupported;   // the ring kernel below sums whole 128-wide groups
 #define Q4_B(MT, KS)                                                                        \
     (zeros ? launch(w4a16_batched_kernel<MT, KS, 4, 4, true>, KS)                           \
            : launch(w4a16_batched_kernel<MT, KS, 4, 4, false>, KS))

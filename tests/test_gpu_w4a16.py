@@ -271,6 +271,22 @@ def test_small_group_gemv(orc, M, N, K, g, sym):
     run_case(orc, W, X, g, sym, what=f"gemv g={g} M={M} N={N} K={K} sym={sym}")
 
 
+# g = 32 and 64 on the batched kernel for 16 < M <= 64 (K = 1024, 2048 or
+# 4096; X streamed through an LDS ring): the same lane transpose, each group's
+# partial sum scaled when its last MFMA step ends; two and four 16-row tiles,
+# one and two k-split groups, 3 and 4 column tiles per block, ragged N.
+CRES_SMALL_G = [(17, 300, 1024), (32, 130, 2048), (33, 1000, 4096), (64, 300, 1024),
+                (20, 4096, 2048), (48, 12800, 1024), (40, 12800, 4096), (64, 11008, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", CRES_SMALL_G)
+@pytest.mark.parametrize("g", [32, 64])
+@pytest.mark.parametrize("sym", [False, True])
+def test_small_group_batched(orc, M, N, K, g, sym):
+    W, X = workloads.small_case(M * 11 + N + K + g + int(sym), M, N, K)
+    run_case(orc, W, X, g, sym, what=f"batched g={g} M={M} N={N} K={K} sym={sym}")
+
+
 @pytest.mark.parametrize("M", [1, 17, 65, 300])
 @pytest.mark.parametrize("g", [256, 384])
 @pytest.mark.parametrize("sym", [False, True])
@@ -280,12 +296,14 @@ def test_large_group_sizes(orc, M, g, sym):
     run_case(orc, W, X, g, sym, what=f"g={g} M={M} N={N} K={K} sym={sym}")
 
 
-@pytest.mark.parametrize("M,K", [(40, 192), (300, 512), (300, 96), (1, 1024), (8, 1024), (16, 4096)])
+@pytest.mark.parametrize("M,K", [(40, 192), (300, 512), (300, 96), (1, 1024), (8, 1024), (16, 4096),
+                                 (33, 2048), (64, 4096)])
 @pytest.mark.parametrize("g", [32, 64])
 def test_small_group_one_hot(orc, M, K, g):
-    """One-hot X through the small-group kernel, the decode GEMV (M <= 16) and
-    the large-M GEMM at g = 32 / 64: Y[m, n] = fp16(w_hat[n, k(m)]) exactly
-    (pins each group's scale and zero-point indexing and the lane transpose)."""
+    """One-hot X through the small-group kernel, the decode GEMV (M <= 16),
+    the batched kernel (16 < M <= 64) and the large-M GEMM at g = 32 / 64:
+    Y[m, n] = fp16(w_hat[n, k(m)]) exactly (pins each group's scale and
+    zero-point indexing and the lane transpose)."""
     if K % g:
         pytest.skip("K must be a multiple of g")
     N = 70
