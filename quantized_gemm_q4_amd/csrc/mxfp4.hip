@@ -122,42 +122,55 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t *__r
 // wait, never a looser one), and the group is first read 7 steps later,
 // after the wait for a younger stage and a barrier.
 constexpr int MBM = 256, MBN = 256, MBK = 64, MSTAGES = 6;
-constexpr int MX_BYTES = MBM * MBK;                       // 16 KB of X
 constexpr int MW_BYTES = MBN * MBK / 2;                   // 8 KB of codes
 constexpr int MOUT_STRIDE = MBN * 2 + 16;
+// a stage: X (BM rows x 64 B), the codes, the per-step scales (!SG)
+template <int BM> constexpr int mx_bytes = BM * MBK;
 template <bool SG> constexpr int ms_bytes = SG ? 0 : MBN * 2 * 4;   // per-step scales, one per dword
-template <bool SG> constexpr int mstage_bytes = MX_BYTES + MW_BYTES + ms_bytes<SG>;
+template <bool SG, int BM> constexpr int mstage_bytes = mx_bytes<BM> + MW_BYTES + ms_bytes<SG>;
 constexpr int MSG_BYTES = 2 * MBN * 16;                   // two groups of 8 steps' scales
-template <bool SG>
-constexpr int mlds_bytes = MBM * MOUT_STRIDE > MSTAGES * mstage_bytes<SG> + (SG ? MSG_BYTES : 0)
-                               ? MBM * MOUT_STRIDE
-                               : MSTAGES * mstage_bytes<SG> + (SG ? MSG_BYTES : 0);
+template <bool SG, int BM>
+constexpr int mlds_bytes = BM * MOUT_STRIDE > MSTAGES * mstage_bytes<SG, BM> + (SG ? MSG_BYTES : 0)
+                               ? BM * MOUT_STRIDE
+                               : MSTAGES * mstage_bytes<SG, BM> + (SG ? MSG_BYTES : 0);
 
-template <bool SG>
+// BM = 256: the whole tile. BM = 128 (a half tile, 64 x 64 per wavefront)
+// serves the tiles past the last full round of 256 blocks two CUs each, so
+// that, for example, the 344 tiles of a 2048 x 11008 output take one round
+// of full tiles and one of half tiles instead of two rounds of full ones;
+// tile0 is the first tile the launch covers.
+template <bool SG, int BM = MBM>
 __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
     const uint8_t *__restrict__ Xq, const float *__restrict__ sx, const uint8_t *__restrict__ Wc,
-    const uint8_t *__restrict__ Ws, int M, int N, int K, int tiles_m, uint16_t *__restrict__ Y)
+    const uint8_t *__restrict__ Ws, int M, int N, int K, int tiles_m, int tile0, uint16_t *__restrict__ Y)
 {
-    constexpr int MSTAGE_BYTES = mstage_bytes<SG>;
-    constexpr int LPS = SG ? 3 : 4;   // direct loads per stage and wavefront
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[mlds_bytes<SG>];
+    static_assert(BM == 256 || BM == 128, "full or half tiles");
+    constexpr int MT = BM / 64;                  // 32-row tiles per wavefront
+    constexpr int XL = BM / 128;                 // X loads per stage and wavefront
+    constexpr int MX_BYTES = mx_bytes<BM>;
+    constexpr int MSTAGE_BYTES = mstage_bytes<SG, BM>;
+    constexpr int LPS = XL + (SG ? 1 : 2);       // direct loads per stage and wavefront
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[mlds_bytes<SG, BM>];
     uint8_t *const sreg = lds + MSTAGES * MSTAGE_BYTES;   // SG: the two scale groups
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const int l32 = lane & 31, h = lane >> 5;
     const int blocks = gridDim.x, b = blockIdx.x;
-    const int t = (blocks % 8 == 0) ? (b % 8) * (blocks / 8) + b / 8 : b;
-    const int m0 = (t % tiles_m) * MBM, n0 = (t / tiles_m) * MBN;
+    const int ub = (blocks % 8 == 0) ? (b % 8) * (blocks / 8) + b / 8 : b;
+    const int t = tile0 + (BM == MBM ? ub : ub >> 1);
+    const int m0 = (t % tiles_m) * MBM + (BM == MBM ? 0 : (ub & 1) * BM), n0 = (t / tiles_m) * MBN;
     const int KT = K / MBK;
     const uint32_t KC = (uint32_t)K >> 1, KS = (uint32_t)K >> 5;   // bytes per code / scale row
 
     // direct-load addresses (rows past M or N read the last row)
     const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    // (a fixed-size array: one sized by a template parameter and captured by
+    // the lambda below makes this compiler drop the kernel's host stub)
     uint32_t xoff[2];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        int m = m0 + (2 * wave + j) * 16 + (lane >> 2);
+    for (int j = 0; j < XL; j++) {
+        int m = m0 + (XL * wave + j) * 16 + (lane >> 2);
         m = m < M ? m : M - 1;
         xoff[j] = (uint32_t)m * (uint32_t)K + 16 * dchunk;
     }
@@ -170,8 +183,8 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
     const uint32_t soff = (uint32_t)nw * KS + (lane & 1);
     auto issue = [&](uint8_t *stage, int kt) {
 #pragma unroll
-        for (int j = 0; j < 2; j++)
-            __builtin_amdgcn_global_load_lds(Xq + xoff[j] + (uint32_t)kt * MBK, stage + (2 * wave + j) * 1024,
+        for (int j = 0; j < XL; j++)
+            __builtin_amdgcn_global_load_lds(Xq + xoff[j] + (uint32_t)kt * MBK, stage + (XL * wave + j) * 1024,
                                              16, 0, 0);
         __builtin_amdgcn_global_load_lds(Wc + woff + (uint32_t)kt * 32, stage + MX_BYTES + wave * 1024, 16, 0, 0);
         if constexpr (!SG)
@@ -201,28 +214,28 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
     // W row wn*64 + 32 j + l32, code bytes 16h .. 16h + 15; its scale in
     // dword 2 row + h.
     const int swz = (l32 >> 2) & 3;
-    const int xa = (wm * 128 + l32) * MBK, xc0 = 16 * (h ^ swz), xc1 = 16 * ((2 + h) ^ swz);
+    const int xa = (wm * (BM / 2) + l32) * MBK, xc0 = 16 * (h ^ swz), xc1 = 16 * ((2 + h) ^ swz);
     const int wrow = wn * 64 + l32;
     const int wb = MX_BYTES + wrow * 32 + 16 * (h ^ ((l32 >> 3) & 1));   // half h of row wrow (swapped on bit 3)
     const int sb = MX_BYTES + MW_BYTES + (wrow * 2 + h) * 4;   // !SG: inside the stage
     const int sgb = wrow * 16 + h;                              // SG: inside a scale group
 
-    floatx16 acc[4][2];
+    floatx16 acc[MT][2];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < MT; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
     struct Frags {
-        intx8 a[4];
+        intx8 a[MT];
         intx4 w[2];
         int s[2];
     };
     auto read = [&](const uint8_t *stage, int step, Frags &f) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < MT; i++) {
             const intx4 lo = *reinterpret_cast<const intx4 *>(stage + xa + i * 32 * MBK + xc0);
             const intx4 hi = *reinterpret_cast<const intx4 *>(stage + xa + i * 32 * MBK + xc1);
             f.a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -234,9 +247,9 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
             else f.s[j] = stage[sb + j * 32 * 2 * 4];
         }
     };
-    auto mma_half = [&](const Frags &f, int s) {   // tiles i = 2s, 2s + 1
+    auto mma_half = [&](const Frags &f, int s) {   // row tiles i = s MT / 2 .. (s + 1) MT / 2 - 1
 #pragma unroll
-        for (int i = 2 * s; i < 2 * s + 2; i++)
+        for (int i = s * MT / 2; i < (s + 1) * MT / 2; i++)
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 const intx8 w8 = __builtin_shufflevector(f.w[j], intx4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -273,11 +286,20 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
             issue(lds + sc * MSTAGE_BYTES, k + MSTAGES < KT ? k + MSTAGES : KT - 1);
             if (SG && (k & 7) == 0) issue_scales((k >> 3) + 1);
             mma_half(f[u], 1);
+            if constexpr (BM == MBM) {
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                if (g >= 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM read
-                __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);               // DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+                for (int g = 0; g < 4; g++) {
+                    if (g >= 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM read
+                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);               // DS read
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < 2; g++) {
+                    __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);               // VMEM read
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);               // DS read
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+                }
             }
             sc = sn;
         }
@@ -285,10 +307,10 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
     Q4_WAIT_VM_LGKM0(0);   // the refetches past the end
 
     // Epilogue: y = f2h(acc * sx[m]) through an LDS-staged fp16 tile
-    float xsv[4];
+    float xsv[MT];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int m = m0 + wm * 128 + i * 32 + l32;
+    for (int i = 0; i < MT; i++) {
+        const int m = m0 + wm * (BM / 2) + i * 32 + l32;
         xsv[i] = sx[m < M ? m : M - 1];
     }
     __syncthreads();   // every wavefront is done with the stages
@@ -298,7 +320,7 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
         for (int q = 0; q < 4; q++) {
             const int nl = wn * 64 + j * 32 + 8 * q + 4 * h;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
+            for (int i = 0; i < MT; i++) {
                 uint32_t pk[2];
 #pragma unroll
                 for (int e2 = 0; e2 < 2; e2++) {
@@ -306,15 +328,15 @@ __global__ __launch_bounds__(512, 1) void mxfp4_gemm_kernel(
                     const uint32_t hi = f2h(acc[i][j][4 * q + 2 * e2 + 1] * xsv[i]);
                     pk[e2] = lo | (hi << 16);
                 }
-                const int ml = wm * 128 + i * 32 + l32;
+                const int ml = wm * (BM / 2) + i * 32 + l32;
                 *reinterpret_cast<u32x2 *>(lds + ml * MOUT_STRIDE + nl * 2) = u32x2{pk[0], pk[1]};
             }
         }
     __syncthreads();
     const bool vec_ok = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
 #pragma unroll 4
-    for (int it = 0; it < 16; it++) {
-        const int ml = wave * 32 + 2 * it + (lane >> 5);
+    for (int it = 0; it < BM / 16; it++) {
+        const int ml = wave * (BM / 8) + 2 * it + (lane >> 5);
         const int cl = (lane & 31) * 8;
         const int m = m0 + ml, n = n0 + cl;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + ml * MOUT_STRIDE + cl * 2);
@@ -727,13 +749,20 @@ hipError_t launch_mxfp4_gemm(const uint8_t *Xq, const float *sx, const uint8_t *
     }
 gemm:
     const int tiles_m = (int)((M + MBM - 1) / MBM), tiles_n = (int)((N + MBN - 1) / MBN);
+    const int tiles = tiles_m * tiles_n;
+    // whole rounds of 256 full tiles, then the rest as half tiles when they
+    // fit one round of 256 blocks (and the full tiles fill at least one)
+    const int full = tiles > 256 && 2 * (tiles % 256) <= 256 ? tiles - tiles % 256 : tiles;
     // 16-byte scale group loads need whole, aligned 16-byte runs per row
-    if (K % 512 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0)
-        mxfp4_gemm_kernel<true><<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N,
-                                                                 (int)K, tiles_m, Y);
-    else
-        mxfp4_gemm_kernel<false><<<tiles_m * tiles_n, 512, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N,
-                                                                  (int)K, tiles_m, Y);
+    const bool sg = K % 512 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0;
+    auto go = [&](auto k_full, auto k_half) {
+        k_full<<<full, 512, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N, (int)K, tiles_m, 0, Y);
+        if (full < tiles)
+            k_half<<<2 * (tiles - full), 512, 0, st>>>(Xq, sx, codes, scales, (int)M, (int)N, (int)K, tiles_m,
+                                                       full, Y);
+    };
+    if (sg) go(mxfp4_gemm_kernel<true, MBM>, mxfp4_gemm_kernel<true, MBM / 2>);
+    else go(mxfp4_gemm_kernel<false, MBM>, mxfp4_gemm_kernel<false, MBM / 2>);
     return hipGetLastError();
 }
 

@@ -76,6 +76,16 @@ def test_gemm_shapes(orc, M, N, K):
     run_gemm(orc, M, N, K, M * 137 + N * 11 + K)
 
 
+# More than 256 output tiles with a remainder: the whole rounds run as full
+# 256 x 256 tiles and the remaining tiles as two 128-row halves each (the
+# prefill shape's 344 tiles; 264 tiles with the per-step scale route, K % 512
+# != 0; M = 1900, where the last row tile is partial and its upper half lies
+# wholly past M). Sampled rows include every tile edge.
+@pytest.mark.parametrize("M,N,K", [(2048, 11008, 4096), (2048, 8448, 384), (1900, 8448, 512)])
+def test_gemm_tail_tiles(orc, M, N, K):
+    run_gemm(orc, M, N, K, M + N + K, rows=sample_rows(M))
+
+
 # Shapes that take the decode GEMVs (K a multiple of 1024): 16 weight rows per
 # block for M <= 16 (X staged in LDS up to 32 KB, else in registers), 32 rows
 # for 16 < M <= 32; each steps-per-wavefront variant (K = 1024 .. 8192),
