@@ -984,6 +984,161 @@ __global__ __launch_bounds__(64 * WN * KS) void w4a16_batched_xres_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Batched decode with X in registers (M <= 16, K = 1024 KBW). A block of 8
+// wavefronts owns NT column tiles of 16 output channels; wavefront w owns
+// k-blocks w KBW .. w KBW + KBW - 1 of all NT tiles. Lane (r16, q) loads the
+// X fragments of row r16 over its wavefront's k-range straight into
+// registers (64 bytes per k-block; rows >= M stay zero and are not read),
+// so a wavefront needs nothing from the others before its first product and
+// each X fragment feeds NT tiles' MFMAs. Loads go out as X, then scales and
+// zero-points, then the code runs k-block by k-block, all before the first
+// wait; each (k-block, tile) is computed once its run has landed. The 8
+// partial sums of each output meet in LDS in a fixed order. Unpack and
+// arithmetic as in the decode GEMV: 16 (u - zp) exact in fp16, each group's
+// exact fp32 partial multiplied by its scale (with the 1/16 folded in). The
+// four code dwords of a row are transposed across the lane groups, so MFMA
+// step t sums the 32-k run t of the k-block (one group at g = 32, half of
+// one at g = 64, a quarter at g = 128) and lane group q's X fragment is
+// k = 32 t + 8 q .. + 7: each X load instruction then reads 64 contiguous
+// bytes of each of 16 rows.
+template <int NT, int KBW, bool ASYM, int GS = 128>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void w4a16_batched_xreg_kernel(
+    const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    uint16_t *__restrict__ Y)
+{
+    static_assert(KBW == 2 || KBW == 4, "k-blocks per wavefront");
+    static_assert(GS == 32 || GS == 64 || GS == 128, "group sizes");
+    constexpr int WV = 8, GPK = 128 / GS, NS = KBW * GPK;   // NS: groups of a wavefront's k-blocks
+    __shared__ float red[WV * NT * 4 * 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int kb0 = wave * KBW;
+    const uint32_t G = (uint32_t)K / GS, Gz = (G + 1) >> 1, kh = (uint32_t)K >> 1;
+    const int n0 = (int)blockIdx.x * 16 * NT;
+
+    // 1. X fragments of the wavefront's k-range (zero first, then the load,
+    //    so rows >= M need no branch around a pending load)
+    u32x4 xa[KBW][4];
+#pragma unroll
+    for (int p = 0; p < KBW; p++)
+#pragma unroll
+        for (int t = 0; t < 4; t++) xa[p][t] = u32x4{0u, 0u, 0u, 0u};
+    if (r16 < M) {
+        const uint16_t *xr = X + ((uint32_t)r16 * (uint32_t)K + (uint32_t)kb0 * 128u);
+#pragma unroll
+        for (int p = 0; p < KBW; p++)
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                xa[p][t] = *reinterpret_cast<const u32x4 *>(xr + p * 128 + 32 * t + 8 * q);
+    }
+    asm volatile("" ::: "memory");
+    // 2. scales (NS fp16) and zero-points (NS nibbles) of each tile's row, as
+    //    whole vector loads (the host checks the alignment)
+    uint32_t nrow[NT];
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+        const int n = n0 + 16 * j + r16;
+        nrow[j] = (uint32_t)(n < N ? n : N - 1);
+    }
+    uint32_t sraw[NT][NS / 2], zr[NT][(NS + 7) / 8];
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+#pragma unroll
+        for (int i = 0; i < (NS + 7) / 8; i++) zr[j][i] = 0x88888888u;
+        const uint16_t *sp = scales + (nrow[j] * G + (uint32_t)kb0 * GPK);
+        if constexpr (NS >= 8) {
+#pragma unroll
+            for (int v8 = 0; v8 < NS / 8; v8++) {
+                const u32x4 v = reinterpret_cast<const u32x4 *>(sp)[v8];
+#pragma unroll
+                for (int i = 0; i < 4; i++) sraw[j][4 * v8 + i] = v[i];
+            }
+        } else if constexpr (NS == 4) {
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(sp);
+            sraw[j][0] = v[0];
+            sraw[j][1] = v[1];
+        } else {
+            sraw[j][0] = *reinterpret_cast<const uint32_t *>(sp);
+        }
+        if (ASYM) {
+            const uint8_t *zpp = zeros + (nrow[j] * Gz + ((uint32_t)kb0 * GPK >> 1));
+            if constexpr (NS == 16) {
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(zpp);
+                zr[j][0] = v[0];
+                zr[j][1] = v[1];
+            } else if constexpr (NS == 8) zr[j][0] = *reinterpret_cast<const uint32_t *>(zpp);
+            else if constexpr (NS == 4) zr[j][0] = *reinterpret_cast<const uint16_t *>(zpp);
+            else zr[j][0] = *zpp;
+        }
+    }
+    asm volatile("" ::: "memory");
+    // 3. the code runs, k-block by k-block, all issued before the first product
+    u32x4 cw[KBW][NT];
+#pragma unroll
+    for (int p = 0; p < KBW; p++)
+#pragma unroll
+        for (int j = 0; j < NT; j++)
+            cw[p][j] = *reinterpret_cast<const u32x4 *>(codes + (nrow[j] * kh + (uint32_t)(kb0 + p) * 64u + q * 16u));
+    // nothing is scheduled across this point: every load above is issued
+    // before the first wait for one of them
+    __builtin_amdgcn_sched_barrier(0);
+
+    floatx4 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; j++) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < KBW; p++) {
+        half8 a[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) a[t] = __builtin_bit_cast(half8, permute_x(xa[p][t]));
+#pragma unroll
+        for (int j = 0; j < NT; j++) {
+            u32x4 w = cw[p][j];
+            {
+                const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+                const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+                const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+                const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+                w = u32x4{s01[0], s01[1], s23[0], s23[1]};
+            }
+            floatx4 part[GPK];
+#pragma unroll
+            for (int jj = 0; jj < GPK; jj++) part[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const int jj = t * GPK / 4, gi = p * GPK + jj;
+                const ZeroConst zc = zero_const((int)(zr[j][gi >> 3] >> (4 * (gi & 7))) & 15);
+                part[jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], dequant8(w[t], zc), part[jj], 0, 0, 0);
+            }
+#pragma unroll
+            for (int jj = 0; jj < GPK; jj++) {
+                const int gi = p * GPK + jj;
+                const uint32_t sw = sraw[j][gi >> 1];
+                const float s = scale16((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xffffu)));
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[j][r] = fmaf(part[jj][r], s, acc[j][r]);
+            }
+        }
+    }
+
+    // 4. the wavefronts' partial sums meet in LDS, summed in wavefront order
+#pragma unroll
+    for (int j = 0; j < NT; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) red[((wave * NT + j) * 4 + r) * 64 + lane] = acc[j][r];
+    __syncthreads();
+    for (int e = (int)threadIdx.x; e < NT * 256; e += WV * 64) {
+        const int j = e >> 8, r = (e >> 6) & 3, l = e & 63;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WV; w++) v += red[((w * NT + j) * 4 + r) * 64 + l];
+        const int m = 4 * (l >> 4) + r, n = n0 + 16 * j + (l & 15);
+        if (m < M && n < N) Y[(int64_t)m * N + n] = f2h(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Large-M GEMM (prefill), M >= 256, g a power of two >= 128. Compute bound.
 //
 // A block of 8 / WM wavefronts owns a 256 x (32 NU) tile of Y; wavefront w
@@ -1294,6 +1449,39 @@ constexpr int cres_ring(int mt, int ks)
     return a < 8 ? (a < b ? a : b) : (8 < b ? 8 : b);
 }
 
+// The X-in-registers batched decode for 8 <= M <= 16, K = 2048 or 4096, g =
+// 32, 64 or 128, and N <= 4096 (one column tile per block, so at most 256
+// blocks, all resident); hipErrorNotSupported otherwise, or when the scale /
+// zero-point runs do not suit whole vector loads, or when Q4_XREG=0 (read at
+// every call; for A/B measurements). Below 8 rows the decode GEMV (X staged
+// in LDS) measured faster; with more column tiles per block (fewer blocks
+// for larger N) this kernel measured slower than the X-resident kernel.
+hipError_t launch_batched_xreg(const uint16_t *X, int M, int N, int K, int g, const uint8_t *codes,
+                               const uint16_t *scales, const uint8_t *zeros, uint16_t *Y,
+                               hipStream_t st)
+{
+    const char *e = std::getenv("Q4_XREG");
+    if ((e && std::atoi(e) == 0) || M < 8 || M > 16 || N > 4096 || (K != 2048 && K != 4096) ||
+        (g != 128 && g != 64 && g != 32))
+        return hipErrorNotSupported;
+    const int kbw = K / 1024, gpk = 128 / g;
+    const int G = K / g, Gz = (G + 1) / 2, ns = kbw * gpk;
+    const int ssz = 2 * ns < 16 ? 2 * ns : 16, zsz = ns / 2;   // bytes per scale / zero-point load
+    if ((reinterpret_cast<uintptr_t>(scales) & (ssz - 1)) != 0 || (2 * G) % ssz != 0 ||
+        (zeros && ((reinterpret_cast<uintptr_t>(zeros) & (zsz - 1)) != 0 || Gz % zsz != 0)))
+        return hipErrorNotSupported;
+    const int blocks = (N + 15) / 16;
+    auto go = [&](auto kernel) { kernel<<<blocks, 512, 0, st>>>(X, M, N, K, codes, scales, zeros, Y); };
+#define Q4_XREG_A(KBW, GS)                                                                       \
+    (zeros ? go(w4a16_batched_xreg_kernel<1, KBW, true, GS>) : go(w4a16_batched_xreg_kernel<1, KBW, false, GS>))
+#define Q4_XREG_G(KBW) (g == 128 ? Q4_XREG_A(KBW, 128) : g == 64 ? Q4_XREG_A(KBW, 64) : Q4_XREG_A(KBW, 32))
+    if (kbw == 4) Q4_XREG_G(4);
+    else Q4_XREG_G(2);
+#undef Q4_XREG_G
+#undef Q4_XREG_A
+    return hipGetLastError();
+}
+
 // Batched decode launcher (g = 128 assumed). K is split over KS groups of
 // wavefronts inside a block; each group's k-blocks must be a multiple of the
 // ring depth.
@@ -1454,6 +1642,10 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int 
 {
     if (M == 0 || N == 0) return hipSuccess;
     const int m = (int)M, n = (int)N, k = (int)K;
+    if ((g == 128 || g == 64 || g == 32) && M >= 8 && M <= 16) {
+        const hipError_t e = launch_batched_xreg(X, m, n, k, g, codes, scales, zeros, Y, st);
+        if (e != hipErrorNotSupported) return e;
+    }
     if ((g == 128 || g == 64 || g == 32) && M <= 16) {
         const hipError_t e = launch_w4a16_gemv(X, M, N, K, g, codes, scales, zeros, Y, st);
         if (e != hipErrorNotSupported) return e;

@@ -196,6 +196,39 @@ def test_batched_variants(orc, M, K, sym):
     run_case(orc, W, X, 128, sym, what=f"batched M={M} N={N} K={K} sym={sym}")
 
 
+# The X-in-registers batched decode (8 <= M <= 16, K = 2048 or 4096, N <=
+# 4096): g = 32 / 64 / 128, symmetric and asymmetric, ragged N (the last
+# column tile runs past N) and M below 16 (rows of the X fragments past M
+# are zero); the second decode layer's shape (N = 4096).
+@pytest.mark.parametrize("M,N", [(8, 1000), (11, 1000), (16, 1000), (16, 4096)])
+@pytest.mark.parametrize("K", [2048, 4096])
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("sym", [False, True])
+def test_batched_xreg(orc, M, N, K, g, sym):
+    W, X = workloads.small_case(M * 17 + N + K + g * 3 + int(sym), M, N, K)
+    run_case(orc, W, X, g, sym, what=f"xreg g={g} M={M} N={N} K={K} sym={sym}")
+
+
+@pytest.mark.parametrize("K", [2048, 4096])
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_batched_xreg_one_hot(orc, K, g):
+    """One-hot X rows whose k lie in different wavefronts' k-ranges, k-blocks
+    and lane groups: Y[m, n] = fp16(w_hat[n, k(m)]) exactly (pins the X
+    fragment order, the lane transpose of the code runs and the scale and
+    zero-point indexing)."""
+    M, N = 16, 100
+    rng = np.random.default_rng(K + g)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    codes, scales, zeros = orc.q4_quantize_pack(W, g=g, sym=False)
+    kk = (np.arange(M) * 1031 + 7) % K
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), kk] = 1.0
+    Y = host(q4.w4a16_linear(gpu(X), gpu(codes), gpu(scales.view(np.float16)), gpu(zeros), g=g))
+    w_hat = orc.q4_dequant(codes, scales, zeros, K, g)
+    expect = w_hat[:, kk].T.astype(np.float16)
+    assert np.array_equal(Y.view(np.uint16), expect.view(np.uint16))
+
+
 # N large enough that 48-column blocks would not fit one round of the CUs:
 # the X-resident kernel (M <= 16) and the whole-slice kernel (16 < M <= 64,
 # one or two k-split groups) then use 64-column blocks (4 column tiles).
