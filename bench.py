@@ -24,7 +24,8 @@ The JSON line also carries:
                 its FP8 E4M3 variant TFLOP/s against the fp8 peak, MXFP4
                 weights x E4M3 activations on that layer and on the prefill
                 shape, NF4 decode GB/s,
-                quantize + pack GB/s, batched decode M = 16 / 64.
+                quantize + pack GB/s, batched decode M = 16 / 64 (N = 11008) and
+                M = 8 / 16 (N = 4096).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
                        [--only decode|prefill|w8a8|fp8|mxfp4|nf4|nvfp4|quant|batched] [--eager]
@@ -257,6 +258,26 @@ def main():
             extra[f"batched_m{M}"] = {"us": tt * 1e6, "GB/s": nb / tt / 1e9,
                                       "frac_hbm": nb / tt / 1e9 / HBM_PEAK_GBS,
                                       "TFLOP/s": 2 * M * 11008 * 4096 / tt / 1e12}
+        del cps, packed
+        # the second decode layer's shape (N = 4096): 8 <= M <= 16 runs the
+        # X-in-registers batched kernel
+        w4 = workloads.decode(4096)
+        packed = q4.q4_quantize_pack(gpu(w4["W"]), g=128, sym=False)
+        bytes1 = w4a16_bytes(16, 4096, 4096)
+        copies = max(2, math.ceil(MALL_BYTES / bytes1) + 1)
+        cps = [tuple(t.clone() for t in packed) for _ in range(copies)]
+        X16 = workloads.quant(16)["X"]
+        for M in (8, 16):
+            X = gpu(X16[:M])
+            Y = torch.empty((M, 4096), dtype=torch.float16, device=dev)
+            gr = graph_of(lambda i: q4.w4a16_linear(X, *cps[i % copies], out=Y), copies)
+            gr()
+            reps = max(1, 1000 // copies)
+            tt = timed(lambda i: gr(), reps) / (reps * copies)
+            nb = w4a16_bytes(M, 4096, 4096)
+            extra[f"batched_m{M}_n4096"] = {"us": tt * 1e6, "GB/s": nb / tt / 1e9,
+                                            "frac_hbm": nb / tt / 1e9 / HBM_PEAK_GBS,
+                                            "TFLOP/s": 2 * M * 4096 * 4096 / tt / 1e12}
         del cps, packed
         torch.cuda.empty_cache()
 
