@@ -55,7 +55,7 @@ int gemv_waves_override()
 // (k = 32 t + 8 q .. + 7, one group at g = 32, half of one at g = 64) with
 // the X fragments read to match, and each group's exact fp32 partial sum is
 // multiplied by that group's scale, as for g = 128.
-template <int WAVES, int KBW, bool ASYM, bool ONE_ROW, bool SM = false, int GS = 128>
+template <int WAVES, int KBW, bool ASYM, bool ONE_ROW, bool SM = false, int GS = 128, bool PW = false>
 __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M, int N, int K,
                                            const uint8_t *__restrict__ codes,
                                            const uint16_t *__restrict__ scales,
@@ -63,6 +63,7 @@ __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M
                                            int blk, const float *__restrict__ as = nullptr)
 {
     static_assert(!SM || ONE_ROW, "the fused activation scaling serves one X row");
+    static_assert(!PW || !ONE_ROW, "per-wavefront staging of several rows");
     static_assert(KBW == 2 || KBW == 4 || KBW == 8, "vector scale / zero-point loads of 2, 4, 8 groups");
     static_assert(GS == 128 || ((GS == 32 || GS == 64) && KBW <= 4 && !SM), "group sizes 32, 64 up to 4 k-blocks");
     constexpr int GPK = 128 / GS;                            // groups per 128-wide k-block
@@ -89,7 +90,20 @@ __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M
     u32x4 xw[XW];
     floatx4 asl[XW], ash[XW];   // SM: the factors of the chunk's 8 columns
     u32x4 x0 = {0u, 0u, 0u, 0u};
-    if (ONE_ROW) {
+    // PW (2 <= M <= 32 / KBW): each wavefront stages the M rows of its own
+    // k-range, chunk j = lane + 64 i being row j / (16 KBW), chunk j % (16 KBW)
+    // of the k-range; at most 8 chunks per lane
+    constexpr int PWC = PW ? 8 : 1;
+    u32x4 xp[PWC];
+    if (PW) {
+#pragma unroll
+        for (int i = 0; i < PWC; i++) xp[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < PWC; i++) {
+            const int j = lane + 64 * i, m = j / (16 * KBW), c = j % (16 * KBW);
+            if (m < M) xp[i] = *reinterpret_cast<const u32x4 *>(X + (m * K + kb0 * 128 + c * 8));
+        }
+    } else if (ONE_ROW) {
 #pragma unroll
         for (int i = 0; i < XW; i++) {
             const int c = lane + 64 * i;
@@ -140,7 +154,17 @@ __device__ __forceinline__ void gemv_block(const uint16_t *__restrict__ X, int M
         cw[p] = *reinterpret_cast<const u32x4 *>(codes + (nrow * (uint32_t)kh + (kb0 + p) * 64 + q * 16));
 
     // 2. X to LDS in the operand order
-    if (ONE_ROW) {
+    if (PW) {
+        // only this wavefront reads its k-range of every row: no barrier
+#pragma unroll
+        for (int i = 0; i < PWC; i++) {
+            const int j = lane + 64 * i, m = j / (16 * KBW), c = j % (16 * KBW);
+            if (m < M) *reinterpret_cast<u32x4 *>(xs + m * kh + kb0 * 64 + c * 4) = permute_x(xp[i]);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    } else if (ONE_ROW) {
         // only this wavefront reads its k-range: LDS keeps one wavefront's
         // accesses in order, so no barrier
 #pragma unroll
@@ -234,6 +258,17 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_sg_kernel(
     uint16_t *__restrict__ Y)
 {
     gemv_block<WAVES, KBW, ASYM, ONE_ROW, false, GS>(X, M, N, K, codes, scales, zeros, Y, (int)blockIdx.x);
+}
+
+// The decode GEMV for 2 <= M <= 32 / KBW rows, each wavefront staging the
+// rows of its own k-range (no block barrier before the compute).
+template <int WAVES, int KBW, bool ASYM, int GS>
+__global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_pw_kernel(
+    const uint16_t *__restrict__ X, int M, int N, int K, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    uint16_t *__restrict__ Y)
+{
+    gemv_block<WAVES, KBW, ASYM, false, false, GS, true>(X, M, N, K, codes, scales, zeros, Y, (int)blockIdx.x);
 }
 
 // The decode GEMV (one X row) on the AWQ-scaled x'' = f2h(x / awq_s[k]).
@@ -357,6 +392,32 @@ hipError_t launch_w4a16_gemv(const uint16_t *X, int64_t M, int64_t N, int64_t K,
     auto launch = [&](auto kernel) {
         kernel<<<blocks, waves * 64, lds, st>>>(X, m, n, k, codes, scales, zeros, Y);
     };
+    // several rows that fit 8 staging chunks per lane: per-wavefront staging
+    // (Q4_GEMV_PW=0 keeps the block-staged form; read at every call)
+    const char *pw_env = std::getenv("Q4_GEMV_PW");
+    if (m > 1 && m * kbw <= 32 && !(pw_env && std::atoi(pw_env) == 0)) {
+        auto pw2 = [&](auto k_a, auto k_s) { asym ? launch(k_a) : launch(k_s); };
+#define Q4_PW(W, B, GS) pw2(w4a16_gemv_pw_kernel<W, B, true, GS>, w4a16_gemv_pw_kernel<W, B, false, GS>)
+#define Q4_PW_WB(GS)                                                                              \
+    do {                                                                                          \
+        if (waves == 4 && kbw == 4) Q4_PW(4, 4, GS);                                              \
+        else if (waves == 4) Q4_PW(4, 2, GS);                                                     \
+        else if (waves == 8 && kbw == 4) Q4_PW(8, 4, GS);                                         \
+        else if (waves == 8) Q4_PW(8, 2, GS);                                                     \
+        else if (kbw == 4) Q4_PW(16, 4, GS);                                                      \
+        else Q4_PW(16, 2, GS);                                                                    \
+    } while (0)
+        if (g == 128 && kbw == 8) {
+            if (waves == 4) Q4_PW(4, 8, 128);
+            else if (waves == 8) Q4_PW(8, 8, 128);
+            else Q4_PW(16, 8, 128);
+        } else if (g == 128) Q4_PW_WB(128);
+        else if (g == 64) Q4_PW_WB(64);   // pick_gemv gives g < 128 at most 4 k-blocks per wavefront
+        else Q4_PW_WB(32);
+#undef Q4_PW_WB
+#undef Q4_PW
+        return hipGetLastError();
+    }
     if (g == 128) {
         Q4_GEMV_DISPATCH(w4a16_gemv_kernel);
         return hipGetLastError();

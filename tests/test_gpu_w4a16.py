@@ -171,13 +171,18 @@ def test_errors_and_empty():
 # (wavefronts per block x k-blocks per wavefront): (11008, 4096) -> 4 x 8,
 # (4096, 4096) -> 8 x 4, (1000, 4096) -> 16 x 2 with a ragged last tile,
 # (4096, 8192) -> 8 x 8; M up to 7 (X must fit in 64 KiB of LDS).
+# With several X rows each wavefront stages the rows of its own k-range
+# (M * k-blocks per wavefront <= 32); Q4_GEMV_PW=0 forces the block-staged
+# form that larger M * k-blocks take.
 @pytest.mark.parametrize("M,N,K", [(1, 11008, 4096), (3, 11008, 4096), (1, 4096, 4096),
                                    (7, 4096, 4096), (2, 1000, 4096), (1, 4096, 8192),
-                                   (5, 4096, 8192)])
+                                   (5, 4096, 8192), (8, 11008, 4096), (4, 4096, 16384)])
 @pytest.mark.parametrize("sym", [False, True])
-def test_gemv_variants(orc, M, N, K, sym):
+@pytest.mark.parametrize("pw", ["1", "0"])
+def test_gemv_variants(orc, monkeypatch, M, N, K, sym, pw):
+    monkeypatch.setenv("Q4_GEMV_PW", pw)
     W, X = workloads.small_case(M * 13 + N + K * 3 + int(sym), M, N, K)
-    run_case(orc, W, X, 128, sym, what=f"gemv M={M} N={N} K={K} sym={sym}")
+    run_case(orc, W, X, 128, sym, what=f"gemv M={M} N={N} K={K} sym={sym} pw={pw}")
 
 
 # Shapes that route to each variant of the batched-decode kernels (8 <= M <=
@@ -299,7 +304,9 @@ GEMV_SMALL_G = [(1, 300, 1024), (1, 300, 2048), (3, 130, 2048), (7, 1000, 1024),
 @pytest.mark.parametrize("M,N,K", GEMV_SMALL_G)
 @pytest.mark.parametrize("g", [32, 64])
 @pytest.mark.parametrize("sym", [False, True])
-def test_small_group_gemv(orc, M, N, K, g, sym):
+@pytest.mark.parametrize("pw", ["1", "0"])
+def test_small_group_gemv(orc, monkeypatch, M, N, K, g, sym, pw):
+    monkeypatch.setenv("Q4_GEMV_PW", pw)
     W, X = workloads.small_case(M * 13 + N + K + g + int(sym), M, N, K)
     run_case(orc, W, X, g, sym, what=f"gemv g={g} M={M} N={N} K={K} sym={sym}")
 
