@@ -78,6 +78,9 @@ def _load():
         "orc_nf4_ref": (None, [_u16p, _i64, _i64, _u8p, _f32p, _u16p, _i64, _i64p, _i64, _f64p, _f64p]),
         "orc_nvfp4_quantize": (None, [_u16p, _i64, _i64, _u8p, _u8p]),
         "orc_nvfp4_ref": (None, [_u16p, _i64, _i64, _u8p, _u8p, _i64, _i64p, _i64, _f64p, _f64p]),
+        "orc_layernorm_quant_smooth": (None, [_u16p, _f32p, _f32p, _f32p, ctypes.c_double, _i64, _i64,
+                                              _i8p, _f32p, _f32p, _f64p]),
+        "orc_u128_to_double": (ctypes.c_double, [ctypes.c_uint64, ctypes.c_uint64]),
         "orc_num_threads": (_int, []),
     }
     for name, (res, args) in sig.items():
@@ -511,3 +514,32 @@ def nvfp4_ref(X, codes, scales, rows=None):
     _load().orc_nvfp4_ref(_ptr(X, _u16p), M, K, _ptr(codes, _u8p), _ptr(scales, _u8p), N,
                           _ptr(r, _i64p), n_rows, _ptr(Y, _f64p), _ptr(B, _f64p))
     return Y, B
+
+
+# --- LayerNorm with the SmoothQuant divide and the per-token INT8 quantizer ---
+
+def layernorm_quant_smooth(X, gamma, beta, s=None, eps: float = 1e-5, want_x: bool = False):
+    """LayerNorm of each fp16 row of X (exact sums, fp64 statistics), the
+    divide by s folded into the affine step, then per-token INT8 codes
+    (Quantization operators guide §5.3, deployment fusion). Returns
+    (Xq int8 [M,K], sx f32 [M]) and, with want_x, also x' f32 [M,K] and the
+    row statistics f64 [M,3] (mean, biased variance, 1/sqrt(var + eps))."""
+    X = _half_bits(X)
+    M, K = X.shape
+    gamma = np.ascontiguousarray(np.asarray(gamma, dtype=np.float32))
+    beta = np.ascontiguousarray(np.asarray(beta, dtype=np.float32))
+    assert gamma.shape == (K,) and beta.shape == (K,) and eps > 0
+    s = _smooth(s)
+    Xq = np.empty((M, K), np.int8)
+    sx = np.empty(M, np.float32)
+    xs = np.empty((M, K), np.float32) if want_x else None
+    st = np.empty((M, 3), np.float64) if want_x else None
+    _load().orc_layernorm_quant_smooth(_ptr(X, _u16p), _ptr(gamma, _f32p), _ptr(beta, _f32p),
+                                       _ptr(s, _f32p), float(eps), M, K, _ptr(Xq, _i8p),
+                                       _ptr(sx, _f32p), _ptr(xs, _f32p), _ptr(st, _f64p))
+    return (Xq, sx, xs, st) if want_x else (Xq, sx)
+
+
+def u128_to_double(v: int) -> float:
+    """The oracle's fp64 rounding of an unsigned 128-bit integer."""
+    return _load().orc_u128_to_double(v >> 64, v & ((1 << 64) - 1))

@@ -22,8 +22,9 @@
  * under the default FE_TONEAREST mode. The GEMM references are exact: fp64
  * sums of exactly dequantized operands (W4A16) and int64 sums (W8A8).
  *
- * Precondition for every function: inputs are finite. Non-finite inputs give
- * unspecified codes.
+ * Non-finite inputs: every quantizer flags a group (or row) whose values hold
+ * a NaN or an infinity with the format's NaN scale and zero codes; the GEMM
+ * references carry NaN into the outputs that use such a group.
  */
 #include <math.h>
 #include <stdint.h>
@@ -868,4 +869,112 @@ void orc_nvfp4_ref(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes
             B[i * N + n] = bb;
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* LayerNorm, the SmoothQuant divide and the per-token INT8 quantizer as one
+ * operation (Quantization operators guide §5.3, deployment fusion: the
+ * online X / s is folded into the epilogue of the LayerNorm that produces
+ * the activations, and its output is quantized straight away; Method
+ * boundaries, SmoothQuant section: the scale may be folded into the
+ * preceding norm). For each row x of X (fp16, length K):
+ *   S1 = sum_k x_k, S2 = sum_k x_k^2          (exact: fp16 values are
+ *        integer multiples of 2^-24, so the sums are taken on the integers
+ *        a_k = x_k 2^24, S1 in int64, S2 in a 128-bit integer)
+ *   mean = fl64(S1) / K                       (fp64, one rounding)
+ *   ex2  = fl64(S2) / K                       (S2 rounded once to fp64)
+ *   var  = max(ex2 - mean * mean, 0)          (fp64; the biased variance of
+ *                                              LayerNorm)
+ *   r    = 1 / sqrt(var + eps)                (fp64, correctly rounded)
+ *   g_k  = gamma_k / s_k, b_k = beta_k / s_k  (fp64 divisions of the fp32
+ *        parameters: the divide by s folded into the affine step; s == NULL
+ *        means s = 1)
+ *   x'_k = fl32(fma((x_k - mean) * r, g_k, b_k))
+ * then the per-token quantizer of orc_q8_quantize_act on x':
+ *   a = max(max_k |x'_k|, 1e-8), sx = a / 127 (fp32),
+ *   q_k = clip(rne(x'_k / sx), -127, 127)     (fp32 division).
+ * A row holding a non-finite x_k, or whose x' is not finite, is flagged:
+ * sx = NaN, codes 0. eps must be positive. Optional outputs: xs [M, K] (x'),
+ * stats [M, 3] (mean, var, r).                                              */
+static int64_t half_units(uint16_t h)   /* h * 2^24 for a finite fp16 h */
+{
+    int e = (h >> 10) & 0x1f;
+    int64_t f = h & 0x3ff;
+    int64_t a = e ? (1024 + f) << (e - 1) : f;
+    return (h >> 15) ? -a : a;
+}
+
+void orc_layernorm_quant_smooth(const uint16_t *X, const float *gamma, const float *beta,
+                                const float *s, double eps, int64_t M, int64_t K,
+                                int8_t *Xq, float *sx, float *xs, double *stats)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        const uint16_t *x = X + m * K;
+        float *xp = xs ? xs + m * K : (float *)malloc((size_t)K * sizeof(float));
+        int bad = 0;
+        for (int64_t k = 0; k < K; k++)
+            if (!isfinite(orc_h2f(x[k]))) bad = 1;
+        double mean = NAN, var = NAN, r = NAN;
+        if (!bad) {
+            int64_t s1 = 0;
+            unsigned __int128 s2 = 0;
+            for (int64_t k = 0; k < K; k++) {
+                int64_t a = half_units(x[k]);
+                s1 += a;
+                s2 += (unsigned __int128)(a < 0 ? -a : a) * (unsigned __int128)(a < 0 ? -a : a);
+            }
+            mean = ldexp((double)s1, -24) / (double)K;
+            double ex2 = ldexp((double)s2, -48) / (double)K;
+            double mm = mean * mean;
+            var = ex2 - mm;
+            if (var < 0.0) var = 0.0;
+            double sd = sqrt(var + eps);
+            r = 1.0 / sd;
+            for (int64_t k = 0; k < K; k++) {
+                double sk = s ? (double)s[k] : 1.0;
+                double g = (double)gamma[k] / sk;
+                double b = (double)beta[k] / sk;
+                double d = (double)orc_h2f(x[k]) - mean;
+                double nk = d * r;
+                xp[k] = (float)fma(nk, g, b);
+                if (!isfinite(xp[k])) bad = 1;
+            }
+        }
+        if (stats) {
+            stats[3 * m] = mean;
+            stats[3 * m + 1] = var;
+            stats[3 * m + 2] = r;
+        }
+        if (bad) {                              /* flagged row: NaN scale, codes 0 */
+            for (int64_t k = 0; k < K; k++) {
+                Xq[m * K + k] = 0;
+                if (xs) xp[k] = NAN;
+            }
+            sx[m] = NAN;
+        } else {
+            float a = 0.0f;
+            for (int64_t k = 0; k < K; k++)
+                if (fabsf(xp[k]) > a) a = fabsf(xp[k]);
+            if (a < 1e-8f) a = 1e-8f;
+            float scale = a / 127.0f;
+            for (int64_t k = 0; k < K; k++) {
+                int q = (int)rintf(xp[k] / scale);
+                if (q < -127) q = -127;
+                if (q > 127) q = 127;
+                Xq[m * K + k] = (int8_t)q;
+            }
+            sx[m] = scale;
+        }
+        if (!xs) free(xp);
+    }
+}
+
+/* The fp64 value of an unsigned 128-bit integer hi 2^64 + lo, as the cast
+ * above rounds it (exposed so the tests can check that rounding against an
+ * independent one).                                                        */
+double orc_u128_to_double(uint64_t hi, uint64_t lo)
+{
+    unsigned __int128 v = ((unsigned __int128)hi << 64) | lo;
+    return (double)v;
 }
