@@ -257,6 +257,32 @@ Q4_API q4_status q8_quantize_act(const void *X, const float *smooth_s, int64_t M
                                  int64_t K, int8_t *Xq, float *x_scale, void *stream);
 
 /* ----------------------------------------------------------------------------
+ * layernorm_quant_smooth -- LayerNorm, the SmoothQuant divide and the
+ * per-token INT8 quantizer in one pass (Operators guide §5.3, deployment
+ * fusion: the online X / s folded into the LayerNorm epilogue, then INT8;
+ * Method boundaries, SmoothQuant: the scale folded into the preceding norm).
+ * Its output feeds w8a8_gemm directly, in place of q8_quantize_act on the
+ * norm's fp16 output. Per row x of X:
+ *   mean, var = the mean and biased variance of x, from exact sums of the
+ *               fp16 values (fp64: mean = S1 / K, var = max(S2 / K - mean^2, 0)),
+ *   r         = 1 / sqrt(var + eps) (fp64),
+ *   x'[k]     = fl32(fma((x[k] - mean) * r, gamma[k] / s[k], beta[k] / s[k]))
+ *               (fp64; smooth_s == NULL means s = 1),
+ *   x_scale[m] = max(max_k |x'|, 1e-8) / 127,
+ *   Xq        = clip(rne(x' / x_scale[m]), -127, 127).
+ * A row holding a NaN or an infinity, or whose x' is not finite, gets a NaN
+ * scale and zero codes.
+ * X fp16 [M, K]; gamma, beta fp32 [K]; smooth_s fp32 [K] or NULL; Xq int8
+ * [M, K] and x_scale fp32 [M] outputs. X, gamma, beta, smooth_s and Xq
+ * 16-byte aligned; K a multiple of 8 up to 8192; eps > 0 and finite.
+ * Errors: INVALID_ARG (shape, eps, null pointer), UNSUPPORTED (K > 8192),
+ *         MISALIGNED, HIP.
+ * -------------------------------------------------------------------------- */
+Q4_API q4_status layernorm_quant_smooth(const void *X, const float *gamma, const float *beta,
+                                        const float *smooth_s, double eps, int64_t M, int64_t K,
+                                        int8_t *Xq, float *x_scale, void *stream);
+
+/* ----------------------------------------------------------------------------
  * w8a8_gemm -- INT8 GEMM with exact int32 accumulation and the scale
  * epilogue (Operators guide §2.3 INT8 GEMM + DequantizeOp, §5.2 path A):
  *   acc[m][n] = sum_k Xq[m][k] * Wq[n][k]   (exact; |acc| <= 127^2 K),

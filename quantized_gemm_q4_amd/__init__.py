@@ -12,6 +12,7 @@ Functions (same names as the C ABI):
   w4a16_linear_multi(X, [(codes, scales, zeros), ...], g=128) -> [Y, ...]
   q8_quantize_weight(W, smooth_s=None) -> (Wq, w_scale)
   q8_quantize_act(X, smooth_s=None) -> (Xq, x_scale)
+  layernorm_quant_smooth(X, gamma, beta, smooth_s=None, eps=1e-5) -> (Xq, x_scale)
   w8a8_gemm(Xq, x_scale, Wq, w_scale, acc_out=None) -> Y
   w8a8_linear(X, Wq, w_scale, smooth_s=None, workspace=None, acc_out=None) -> Y
   w8a8_linear_noalloc(X, Wq, w_scale, smooth_s=None, acc_out=None) -> Y  (no workspace)
@@ -65,6 +66,7 @@ SIGNATURES = {
                                         ctypes.c_size_t, _vp]),
     "q8_quantize_weight": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "q8_quantize_act": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "layernorm_quant_smooth": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "w8a8_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
@@ -331,6 +333,23 @@ def q8_quantize_act(X: torch.Tensor, smooth_s: torch.Tensor | None = None, out=N
     _need_smooth(smooth_s, K)
     Xq, sx = _row_outputs(out, M, K, torch.int8, X.device)
     _check(lib().q8_quantize_act(_ptr(X), _ptr(smooth_s), M, K, _ptr(Xq), _ptr(sx), _stream(X)))
+    return Xq, sx
+
+
+def layernorm_quant_smooth(X: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
+                           smooth_s: torch.Tensor | None = None, eps: float = 1e-5, out=None):
+    """LayerNorm of each row of X with the divide by smooth_s folded into
+    gamma and beta, then per-token INT8: (Xq int8 [M, K], x_scale fp32 [M])."""
+    _need(X, torch.float16, "X", 2)
+    M, K = X.shape
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        _need(t, torch.float32, name, 1)
+        if t.numel() != K:
+            raise ValueError(f"{name} has {t.numel()} entries, K={K}")
+    _need_smooth(smooth_s, K)
+    Xq, sx = _row_outputs(out, M, K, torch.int8, X.device)
+    _check(lib().layernorm_quant_smooth(_ptr(X), _ptr(gamma), _ptr(beta), _ptr(smooth_s), float(eps), M, K,
+                                        _ptr(Xq), _ptr(sx), _stream(X)))
     return Xq, sx
 
 

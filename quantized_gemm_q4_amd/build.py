@@ -31,6 +31,7 @@ SOURCES = {
     "nf4.hip": ["-ffp-contract=off"],
     "nvfp4.hip": ["-ffp-contract=off"],
     "awq.hip": ["-ffp-contract=off"],
+    "layernorm.hip": ["-ffp-contract=off"],
 }
 
 

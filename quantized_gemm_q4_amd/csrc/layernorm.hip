@@ -1,0 +1,251 @@
+// LayerNorm with the SmoothQuant divide and the per-token INT8 quantizer in
+// one pass on gfx950 (Quantization operators guide, section 5.3: the online
+// X / s folded into the epilogue of the LayerNorm that produces the
+// activations, then INT8; Method boundaries, SmoothQuant section: the scale
+// folded into the preceding norm). The activation is read once (fp16) and
+// written once (int8 codes + one fp32 scale per row); the fp16 normalised
+// activation of an unfused norm never reaches HBM.
+//
+// Arithmetic, per row x of length K <= 8192 (the codes are integers decided
+// by floating point, so every step is reproducible bit for bit):
+//   - S1 = sum x and S2 = sum x^2 exactly. An fp16 value is a multiple of
+//     2^-24 below 2^16, so S1 (below 2^29) is exact in fp64 in any order.
+//     x^2 (exact in fp64) is split as h + l with h = x^2 rounded to a
+//     multiple of 2^-8 by adding and subtracting 1.5 * 2^44 (whose fp64
+//     spacing is 2^-8) and l = x^2 - h (|l| <= 2^-9, a multiple of 2^-48):
+//     the sum of the h (multiples of 2^-8 below 2^45) and the sum of the l
+//     (multiples of 2^-48 below 2^4) are each exact in fp64 in any order, and
+//     one fp64 addition of the two is S2 rounded once.
+//   - mean = S1 / K, ex2 = S2 / K, var = max(ex2 - mean * mean, 0),
+//     r = 1 / sqrt(var + eps), all fp64 correctly rounded (no contraction:
+//     this file is built with -ffp-contract=off).
+//   - g_k = gamma_k / s_k, b_k = beta_k / s_k in fp64, computed once per
+//     block into LDS; x'_k = fl32(fma((x_k - mean) * r, g_k, b_k)).
+//   - the per-token quantizer: scale = max(max |x'|, 1e-8) / 127 (IEEE fp32
+//     division), codes rint(fl32(x' / scale)) clipped to +-127, the quotient
+//     formed as fl32(fl64(x' * rcp(scale))), equal to the fp32 division.
+//   - a row with a non-finite x (its statistics, and so every x', are then
+//     NaN) or a non-finite x' gets a NaN scale and zero codes.
+#include "q4_internal.hpp"
+#include "row_codes.hpp"
+
+namespace q4k {
+namespace {
+
+typedef double double2v __attribute__((ext_vector_type(2)));
+
+constexpr int kLnWaves = 8;                       // one row per wavefront
+constexpr double kSplit = 26388279066624.0;       // 1.5 * 2^44, fp64 spacing 2^-8
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+    return v;
+}
+
+// Lane l of a wavefront owns the 8-column chunks l, l + 64, ... of a row
+// (chunk c = columns 8c .. 8c + 7), so each load instruction reads 1 KB of
+// the row contiguously.
+template <int CPL, bool EXACT>
+__device__ __forceinline__ void load_row(u32x4 (&xr)[CPL], const uint16_t *__restrict__ X, int64_t m,
+                                         int K, int nch, int lane)
+{
+    const uint16_t *row = X + m * K + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < CPL; i++)
+        if (EXACT || lane + 64 * i < nch) xr[i] = *reinterpret_cast<const u32x4 *>(row + 512 * i);
+}
+
+__device__ __forceinline__ double half_at(const u32x4 &v, int e)
+{
+    const uint32_t d = v[e >> 1];
+    return (double)h2f((uint16_t)((e & 1) ? (d >> 16) : (d & 0xffffu)));
+}
+
+// LDS: the folded parameters as 16-byte pieces, piece-major: piece j of
+// chunk c (columns 8c + 2j, 8c + 2j + 1) at index j * nch + c, so the 64
+// lanes of one read take 64 consecutive pieces (no bank conflicts).
+// EXACT: K = 512 CPL, every lane owns CPL whole chunks (no per-chunk tests).
+template <int CPL, bool EXACT>
+__global__ __launch_bounds__(kLnWaves * 64) void ln_quant_kernel(
+    const uint16_t *__restrict__ X, const float *__restrict__ gamma, const float *__restrict__ beta,
+    const float *__restrict__ s, double eps, int M, int K, int8_t *__restrict__ Xq,
+    float *__restrict__ sx)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int nch = K >> 3;
+    double2v *G = reinterpret_cast<double2v *>(smem);
+    double2v *B = G + 4 * nch;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int stride = gridDim.x * kLnWaves;
+    int m = blockIdx.x * kLnWaves + wave;
+
+    // 1. the wavefront's first row is in flight while the block folds 1/s
+    u32x4 xr[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; i++) xr[i] = u32x4{0u, 0u, 0u, 0u};
+    if (m < M) load_row<CPL, EXACT>(xr, X, m, K, nch, lane);
+
+    for (int c = threadIdx.x; c < nch; c += kLnWaves * 64) {
+        const floatx4 g0 = *reinterpret_cast<const floatx4 *>(gamma + 8 * c);
+        const floatx4 g1 = *reinterpret_cast<const floatx4 *>(gamma + 8 * c + 4);
+        const floatx4 b0 = *reinterpret_cast<const floatx4 *>(beta + 8 * c);
+        const floatx4 b1 = *reinterpret_cast<const floatx4 *>(beta + 8 * c + 4);
+        floatx4 s0 = {1.f, 1.f, 1.f, 1.f}, s1 = {1.f, 1.f, 1.f, 1.f};
+        if (s) {
+            s0 = *reinterpret_cast<const floatx4 *>(s + 8 * c);
+            s1 = *reinterpret_cast<const floatx4 *>(s + 8 * c + 4);
+        }
+        double g[8], b[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const double sk = (double)(e < 4 ? s0[e] : s1[e - 4]);
+            g[e] = (double)(e < 4 ? g0[e] : g1[e - 4]) / sk;
+            b[e] = (double)(e < 4 ? b0[e] : b1[e - 4]) / sk;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            G[j * nch + c] = double2v{g[2 * j], g[2 * j + 1]};
+            B[j * nch + c] = double2v{b[2 * j], b[2 * j + 1]};
+        }
+    }
+    __syncthreads();
+
+    for (; m < M; m += stride) {
+        // 2. exact row sums (two accumulator sets for more independent adds)
+        double s1[2] = {0.0, 0.0}, hh[2] = {0.0, 0.0}, hl[2] = {0.0, 0.0};
+#pragma unroll
+        for (int i = 0; i < CPL; i++) {
+            if (EXACT || lane + 64 * i < nch) {
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const double x = half_at(xr[i], e);
+                    const double x2 = x * x;
+                    const double h = (x2 + kSplit) - kSplit;
+                    s1[i & 1] += x;
+                    hh[i & 1] += h;
+                    hl[i & 1] += x2 - h;
+                }
+            }
+        }
+        // the normalisation converts x again rather than keep 16 chunks of
+        // fp64 values alive across the reductions
+#pragma unroll
+        for (int i = 0; i < CPL; i++) asm volatile("" : "+v"(xr[i]));
+        const double S1 = wave_sum(s1[0] + s1[1]);
+        const double Hh = wave_sum(hh[0] + hh[1]);
+        const double Hl = wave_sum(hl[0] + hl[1]);
+        const double mean = S1 / (double)K;
+        const double ex2 = (Hh + Hl) / (double)K;
+        const double mm = mean * mean;
+        double var = ex2 - mm;
+        if (var < 0.0) var = 0.0;   // a NaN stays NaN
+        const double r = 1.0 / sqrt(var + eps);
+
+        // 3. x' and the row maximum, taken on the |x'| bit patterns as
+        //    integers so that a NaN or an infinity ranks above every finite
+        //    value (a non-finite x has made the statistics NaN)
+        float xp[CPL][8];
+        uint32_t amax = 0u;
+#pragma unroll
+        for (int i = 0; i < CPL; i++) {
+            const int c = lane + 64 * i;
+            if (EXACT || c < nch) {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const double2v gp = G[j * nch + c], bp = B[j * nch + c];
+#pragma unroll
+                    for (int t = 0; t < 2; t++) {
+                        const int e = 2 * j + t;
+                        const double n = (half_at(xr[i], e) - mean) * r;
+                        xp[i][e] = (float)fma(n, gp[t], bp[t]);
+                        amax = max(amax, __builtin_bit_cast(uint32_t, xp[i][e]) & 0x7fffffffu);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) xp[i][e] = 0.0f;
+            }
+        }
+        amax = wave_max(amax);
+
+        // 4. scale and codes
+        const bool bad = amax >= 0x7f800000u;
+        const float sc = bad ? __builtin_nanf("") : fmaxf(__builtin_bit_cast(float, amax), 1e-8f) / kRowMax<false>;
+        const double rs = recip64((double)(bad ? 1.0f : sc));
+        int8_t *qrow = Xq + (int64_t)m * K;
+#pragma unroll
+        for (int i = 0; i < CPL; i++) {
+            const int c = lane + 64 * i;
+            if (EXACT || c < nch) {
+                float q[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) q[e] = (float)((double)xp[i][e] * rs);
+                u32x2 out = {row_codes4<false>(q[0], q[1], q[2], q[3]),
+                             row_codes4<false>(q[4], q[5], q[6], q[7])};
+                if (bad) out = u32x2{0u, 0u};
+                *reinterpret_cast<u32x2 *>(qrow + 8 * c) = out;
+            }
+        }
+        if (lane == 0) sx[m] = sc;
+        // the next row's loads (after the codes, so that the raw row and x'
+        // are never both held: 16 chunks of each would not fit the registers)
+        const int mn = m + stride;
+        if (mn < M) load_row<CPL, EXACT>(xr, X, mn, K, nch, lane);
+    }
+}
+
+template <int CPL, bool EXACT>
+hipError_t launch_cpl(const uint16_t *X, const float *gamma, const float *beta, const float *s,
+                      double eps, int64_t M, int64_t K, int8_t *Xq, float *sx, hipStream_t stream)
+{
+    const size_t lds = (size_t)K * 16;   // folded gamma and beta, fp64
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&ln_quant_kernel<CPL, EXACT>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       kLnMaxK * 16);
+    if (attr != hipSuccess) return attr;
+    const int per_cu = lds <= 80 * 1024 ? 2 : 1;
+    const int64_t want = (M + kLnWaves - 1) / kLnWaves;
+    const int blocks = (int)(want < 256 * per_cu ? want : 256 * per_cu);
+    hipLaunchKernelGGL((ln_quant_kernel<CPL, EXACT>), dim3(blocks), dim3(kLnWaves * 64), lds, stream, X, gamma, beta, s,
+                       eps, (int)M, (int)K, Xq, sx);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Shape, alignment and eps were validated by the C-ABI layer (K a multiple
+// of 8 up to kLnMaxK, X / gamma / beta / s 16-byte aligned, Xq 8-byte
+// aligned, eps > 0 and finite, M >= 1).
+hipError_t launch_layernorm_quant(const uint16_t *X, const float *gamma, const float *beta, const float *s,
+                                  double eps, int64_t M, int64_t K, int8_t *Xq, float *sx,
+                                  hipStream_t stream)
+{
+    const int cpl = (int)((K / 8 + 63) / 64);   // chunks per lane
+    if (K % 512 == 0) {   // whole chunks on every lane
+        switch (cpl) {
+#define Q4_LN_CASE(n) \
+        case n: return launch_cpl<n, true>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+            Q4_LN_CASE(1) Q4_LN_CASE(2) Q4_LN_CASE(3) Q4_LN_CASE(4) Q4_LN_CASE(5) Q4_LN_CASE(6)
+            Q4_LN_CASE(7) Q4_LN_CASE(8) Q4_LN_CASE(9) Q4_LN_CASE(10) Q4_LN_CASE(11) Q4_LN_CASE(12)
+            Q4_LN_CASE(13) Q4_LN_CASE(14) Q4_LN_CASE(15) Q4_LN_CASE(16)
+#undef Q4_LN_CASE
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (cpl <= 1) return launch_cpl<1, false>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+    if (cpl <= 2) return launch_cpl<2, false>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+    if (cpl <= 4) return launch_cpl<4, false>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+    if (cpl <= 8) return launch_cpl<8, false>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+    return launch_cpl<16, false>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+}
+
+}  // namespace q4k

@@ -54,6 +54,12 @@ hipError_t launch_q8_weight(const uint16_t *W, const float *s, int64_t N, int64_
                             int8_t *Wq, float *sw, hipStream_t st);
 hipError_t launch_q8_act(const uint16_t *X, const float *s, int64_t M, int64_t K,
                          int8_t *Xq, float *sx, hipStream_t st);
+// LayerNorm + SmoothQuant divide + per-token INT8 (K a multiple of 8 up to
+// kLnMaxK, where the kernel's fp64 row sums are exact).
+constexpr int kLnMaxK = 8192;
+hipError_t launch_layernorm_quant(const uint16_t *X, const float *gamma, const float *beta, const float *s,
+                                  double eps, int64_t M, int64_t K, int8_t *Xq, float *sx,
+                                  hipStream_t stream);
 hipError_t launch_smooth_scales(const uint16_t *Xcal, int64_t R, const uint16_t *W, int64_t N,
                                 int64_t K, float alpha, float *s, hipStream_t st);
 hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t N, int64_t K, int g,

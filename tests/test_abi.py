@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared_functions()) <= exported
     # nothing else of ours leaks out (internal launchers are hidden)
-    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "fp8", "mxfp4", "nf4", "nvfp4", "awq", "smoothquant", "_ZN3q4k"))}
+    ours = {s for s in exported if s.startswith(("q4", "w4a16", "w8a8", "q8", "fp8", "mxfp4", "nf4", "nvfp4", "awq", "smoothquant", "layernorm", "_ZN3q4k"))}
     assert ours == set(declared_functions())
 
 
@@ -116,6 +116,15 @@ def layers(*descs):
     (lambda L: L.q8_quantize_weight(FAKE, MISAL, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.q8_quantize_act(FAKE, None, 4, 128, MISAL, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.q8_quantize_act(FAKE, None, 4, 128, None, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.layernorm_quant_smooth(FAKE, FAKE, FAKE, None, 1e-5, 4, 100, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.layernorm_quant_smooth(FAKE, FAKE, FAKE, None, 0.0, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.layernorm_quant_smooth(FAKE, FAKE, FAKE, None, float("nan"), 4, 128, FAKE, FAKE, None),
+     q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.layernorm_quant_smooth(FAKE, FAKE, FAKE, None, 1e-5, 4, 8200, FAKE, FAKE, None), q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.layernorm_quant_smooth(FAKE, None, FAKE, None, 1e-5, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.layernorm_quant_smooth(FAKE, FAKE, MISAL, None, 1e-5, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.layernorm_quant_smooth(FAKE, FAKE, FAKE, MISAL, 1e-5, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
+    (lambda L: L.layernorm_quant_smooth(None, None, None, None, 1e-5, 0, 128, None, None, None), q4.Q4_OK),
     (lambda L: L.w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 140000, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.w8a8_gemm(MISAL, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, None, None), q4.Q4_ERR_MISALIGNED),

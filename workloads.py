@@ -20,6 +20,11 @@ Workloads (Llama-shaped layers; K is the input width, N the output width):
   w8a8      M = 2048, K = 8192, N = 8192; X ~ N(0, 1) with 1% of the
             K-channels x30; calibration X [512, 8192] from the same law and the
             same outlier channels; W ~ N(0, 0.02).
+  layernorm the w8a8 workload's X read as the hidden state in front of the
+            norm, with fp32 norm parameters gamma = 1 + 0.1 N(0, 1) (the
+            outlier channels x30, where LLM norms carry their outliers),
+            beta = 0.05 N(0, 1) and smoothing factors s = exp(0.5 N(0, 1))
+            (seeds 5005, 6005, 7005).
 
 Seeds: W 1000+c, X 2000+c, calibration X 3000+c, outlier permutation 4000+c,
 for workload number c = 1..5 in the order above. The outlier set is the first
@@ -129,3 +134,14 @@ def small_case(seed: int, M: int, N: int, K: int, x_outlier_mult: float = 30.0):
     W = normal_fp16(seed, (N, K), W_SIGMA)
     X = normal_fp16(seed + 1, (M, K), 1.0, (cols, x_outlier_mult) if cols.size else None)
     return W, X
+
+
+def layernorm_params(K: int, c: int = 5):
+    """fp32 LayerNorm weight and bias and fp32 smoothing factors for a
+    hidden width K (seeds 5000+c, 6000+c, 7000+c; gamma's outlier channels
+    are the w8a8 workload's)."""
+    gamma = np.float32(1.0) + np.float32(0.1) * rng(5000 + c).standard_normal(K, dtype=np.float32)
+    gamma[outlier_channels(seeds(c)["outliers"], K)] *= np.float32(30.0)
+    beta = np.float32(0.05) * rng(6000 + c).standard_normal(K, dtype=np.float32)
+    s = np.exp(np.float32(0.5) * rng(7000 + c).standard_normal(K, dtype=np.float32)).astype(np.float32)
+    return dict(gamma=gamma, beta=beta, s=s)
