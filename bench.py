@@ -344,6 +344,26 @@ def main():
                          "gemm_us": tg * 1e6, "gemm_TOP/s": ops / tg / 1e12,
                          "gemm_frac_mfma_int8": ops / tg / 1e12 / INT8_MFMA_PEAK_TOPS,
                          "act_quant_us": ta * 1e6, "act_quant_GB/s": abytes / ta / 1e9}
+        # the LayerNorm in front of the layer with the divide by s and the
+        # per-token quantizer fused in (X read as the hidden state before the
+        # norm), against the unfused pair: torch's fp16 layer_norm writing the
+        # normalised X, then q8_quantize_act on it
+        p = workloads.layernorm_params(K)
+        gam, bet, sln = gpu(p["gamma"]), gpu(p["beta"]), gpu(p["s"])
+        gn = graph_of(lambda i: q4.layernorm_quant_smooth(X, gam, bet, sln, 1e-5, out=(Xq, sx)), 8)
+        gn()
+        tn = timed(lambda i: gn(), reps) / (reps * 8)
+        g16, b16 = gam.half(), bet.half()
+        gu = graph_of(lambda i: q4.q8_quantize_act(torch.nn.functional.layer_norm(X, (K,), g16, b16, 1e-5), sln,
+                                                   out=(Xq, sx)), 8)
+        gu()
+        tu = timed(lambda i: gu(), reps) / (reps * 8)
+        nbytes = M * K * 2 + 3 * K * 4 + M * K + M * 4
+        extra["w8a8"]["norm_quant_fused"] = {
+            "us": tn * 1e6, "GB/s": nbytes / tn / 1e9, "frac_hbm": nbytes / tn / 1e9 / HBM_PEAK_GBS,
+            "bytes": nbytes, "unfused_layer_norm_then_act_quant_us": tu * 1e6,
+            "layer_with_fused_norm_us": (tn + tg) * 1e6, "over_gemm_alone": (tn + tg) / tg}
+        del gu, gn
         del Wq, Xq
         # the decode workload's N = 11008 layer (M = 1) with INT8 weights: the decode GEMV
         w = workloads.decode(11008)

@@ -36,6 +36,7 @@ typedef double double2v __attribute__((ext_vector_type(2)));
 
 constexpr int kLnWaves = 8;                       // one row per wavefront
 constexpr double kSplit = 26388279066624.0;       // 1.5 * 2^44, fp64 spacing 2^-8
+static_assert(kLnMaxK / 8 <= 2 * kLnWaves * 64, "the fold takes at most two chunks per thread");
 
 __device__ __forceinline__ double wave_sum(double v)
 {
@@ -60,8 +61,10 @@ __device__ __forceinline__ void load_row(u32x4 (&xr)[CPL], const uint16_t *__res
 {
     const uint16_t *row = X + m * K + 8 * lane;
 #pragma unroll
-    for (int i = 0; i < CPL; i++)
+    for (int i = 0; i < CPL; i++) {
         if (EXACT || lane + 64 * i < nch) xr[i] = *reinterpret_cast<const u32x4 *>(row + 512 * i);
+        __builtin_amdgcn_sched_barrier(0);   // issued in chunk order, so chunk i lands i-th
+    }
 }
 
 __device__ __forceinline__ double half_at(const u32x4 &v, int e)
@@ -88,38 +91,53 @@ __global__ __launch_bounds__(kLnWaves * 64) void ln_quant_kernel(
     const int stride = gridDim.x * kLnWaves;
     int m = blockIdx.x * kLnWaves + wave;
 
-    // 1. the wavefront's first row is in flight while the block folds 1/s
+    // 1. the block's parameters are requested first, then the wavefront's
+    //    row; loads complete in order, so the fold waits only for the
+    //    parameters while the row is still on its way. Thread t folds the
+    //    chunks t and t + 512 (nch <= 1024).
+    floatx4 pg[2][2], pb[2][2], ps[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const int c = (int)threadIdx.x + kLnWaves * 64 * u;
+        const int cc = c < nch ? c : 0;
+        pg[u][0] = *reinterpret_cast<const floatx4 *>(gamma + 8 * cc);
+        pg[u][1] = *reinterpret_cast<const floatx4 *>(gamma + 8 * cc + 4);
+        pb[u][0] = *reinterpret_cast<const floatx4 *>(beta + 8 * cc);
+        pb[u][1] = *reinterpret_cast<const floatx4 *>(beta + 8 * cc + 4);
+        ps[u][0] = ps[u][1] = floatx4{1.f, 1.f, 1.f, 1.f};
+        if (s) {
+            ps[u][0] = *reinterpret_cast<const floatx4 *>(s + 8 * cc);
+            ps[u][1] = *reinterpret_cast<const floatx4 *>(s + 8 * cc + 4);
+        }
+    }
+    // every wavefront issues a row (the last one when it has none), so the
+    // count of loads in flight is the same on every path
     u32x4 xr[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; i++) xr[i] = u32x4{0u, 0u, 0u, 0u};
-    if (m < M) load_row<CPL, EXACT>(xr, X, m, K, nch, lane);
+    load_row<CPL, EXACT>(xr, X, m < M ? m : M - 1, K, nch, lane);
 
-    for (int c = threadIdx.x; c < nch; c += kLnWaves * 64) {
-        const floatx4 g0 = *reinterpret_cast<const floatx4 *>(gamma + 8 * c);
-        const floatx4 g1 = *reinterpret_cast<const floatx4 *>(gamma + 8 * c + 4);
-        const floatx4 b0 = *reinterpret_cast<const floatx4 *>(beta + 8 * c);
-        const floatx4 b1 = *reinterpret_cast<const floatx4 *>(beta + 8 * c + 4);
-        floatx4 s0 = {1.f, 1.f, 1.f, 1.f}, s1 = {1.f, 1.f, 1.f, 1.f};
-        if (s) {
-            s0 = *reinterpret_cast<const floatx4 *>(s + 8 * c);
-            s1 = *reinterpret_cast<const floatx4 *>(s + 8 * c + 4);
-        }
-        double g[8], b[8];
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const double sk = (double)(e < 4 ? s0[e] : s1[e - 4]);
-            g[e] = (double)(e < 4 ? g0[e] : g1[e - 4]) / sk;
-            b[e] = (double)(e < 4 ? b0[e] : b1[e - 4]) / sk;
-        }
+    for (int u = 0; u < 2; u++) {
+        const int c = (int)threadIdx.x + kLnWaves * 64 * u;
+        if (c < nch) {
+            double g[8], b[8];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            G[j * nch + c] = double2v{g[2 * j], g[2 * j + 1]};
-            B[j * nch + c] = double2v{b[2 * j], b[2 * j + 1]};
+            for (int e = 0; e < 8; e++) {
+                const double sk = (double)ps[u][e >> 2][e & 3];
+                g[e] = (double)pg[u][e >> 2][e & 3] / sk;
+                b[e] = (double)pb[u][e >> 2][e & 3] / sk;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                G[j * nch + c] = double2v{g[2 * j], g[2 * j + 1]};
+                B[j * nch + c] = double2v{b[2 * j], b[2 * j + 1]};
+            }
         }
     }
     __syncthreads();
 
-    for (; m < M; m += stride) {
+    while (m < M) {
         // 2. exact row sums (two accumulator sets for more independent adds)
         double s1[2] = {0.0, 0.0}, hh[2] = {0.0, 0.0}, hl[2] = {0.0, 0.0};
 #pragma unroll
@@ -135,6 +153,7 @@ __global__ __launch_bounds__(kLnWaves * 64) void ln_quant_kernel(
                     hl[i & 1] += x2 - h;
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);   // chunk i's sums as soon as it lands
         }
         // the normalisation converts x again rather than keep 16 chunks of
         // fp64 values alive across the reductions
@@ -198,8 +217,9 @@ __global__ __launch_bounds__(kLnWaves * 64) void ln_quant_kernel(
         if (lane == 0) sx[m] = sc;
         // the next row's loads (after the codes, so that the raw row and x'
         // are never both held: 16 chunks of each would not fit the registers)
-        const int mn = m + stride;
-        if (mn < M) load_row<CPL, EXACT>(xr, X, mn, K, nch, lane);
+        m += stride;
+        if (m >= M) break;
+        load_row<CPL, EXACT>(xr, X, m, K, nch, lane);
     }
 }
 
