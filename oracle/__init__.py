@@ -80,6 +80,8 @@ def _load():
         "orc_nvfp4_ref": (None, [_u16p, _i64, _i64, _u8p, _u8p, _i64, _i64p, _i64, _f64p, _f64p]),
         "orc_layernorm_quant_smooth": (None, [_u16p, _f32p, _f32p, _f32p, ctypes.c_double, _i64, _i64,
                                               _i8p, _f32p, _f32p, _f64p]),
+        "orc_layernorm_quant_smooth_fp8": (None, [_u16p, _f32p, _f32p, _f32p, ctypes.c_double, _i64, _i64,
+                                                  _u8p, _f32p]),
         "orc_u128_to_double": (ctypes.c_double, [ctypes.c_uint64, ctypes.c_uint64]),
         "orc_num_threads": (_int, []),
     }
@@ -538,6 +540,22 @@ def layernorm_quant_smooth(X, gamma, beta, s=None, eps: float = 1e-5, want_x: bo
                                        _ptr(s, _f32p), float(eps), M, K, _ptr(Xq, _i8p),
                                        _ptr(sx, _f32p), _ptr(xs, _f32p), _ptr(st, _f64p))
     return (Xq, sx, xs, st) if want_x else (Xq, sx)
+
+
+def layernorm_quant_smooth_fp8(X, gamma, beta, s=None, eps: float = 1e-5):
+    """The same LayerNorm with per-token FP8 E4M3 codes (scale max|x'| / 448).
+    Returns (Xq E4M3 bytes [M,K], sx f32 [M])."""
+    X = _half_bits(X)
+    M, K = X.shape
+    gamma = np.ascontiguousarray(np.asarray(gamma, dtype=np.float32))
+    beta = np.ascontiguousarray(np.asarray(beta, dtype=np.float32))
+    assert gamma.shape == (K,) and beta.shape == (K,) and eps > 0
+    s = _smooth(s)
+    Xq = np.empty((M, K), np.uint8)
+    sx = np.empty(M, np.float32)
+    _load().orc_layernorm_quant_smooth_fp8(_ptr(X, _u16p), _ptr(gamma, _f32p), _ptr(beta, _f32p),
+                                           _ptr(s, _f32p), float(eps), M, K, _ptr(Xq, _u8p), _ptr(sx, _f32p))
+    return Xq, sx
 
 
 def u128_to_double(v: int) -> float:

@@ -904,48 +904,57 @@ static int64_t half_units(uint16_t h)   /* h * 2^24 for a finite fp16 h */
     return (h >> 15) ? -a : a;
 }
 
+/* The LayerNorm part for one row: x' into xp, the statistics into st (mean,
+ * var, r; NaN for a row with a non-finite x); returns 1 when the row is
+ * flagged (a non-finite x or x').                                          */
+static int ln_row(const uint16_t *x, const float *gamma, const float *beta, const float *s,
+                  double eps, int64_t K, float *xp, double *st)
+{
+    int bad = 0;
+    for (int64_t k = 0; k < K; k++)
+        if (!isfinite(orc_h2f(x[k]))) bad = 1;
+    double mean = NAN, var = NAN, r = NAN;
+    if (!bad) {
+        int64_t s1 = 0;
+        unsigned __int128 s2 = 0;
+        for (int64_t k = 0; k < K; k++) {
+            int64_t a = half_units(x[k]);
+            s1 += a;
+            s2 += (unsigned __int128)(a < 0 ? -a : a) * (unsigned __int128)(a < 0 ? -a : a);
+        }
+        mean = ldexp((double)s1, -24) / (double)K;
+        double ex2 = ldexp((double)s2, -48) / (double)K;
+        double mm = mean * mean;
+        var = ex2 - mm;
+        if (var < 0.0) var = 0.0;
+        double sd = sqrt(var + eps);
+        r = 1.0 / sd;
+        for (int64_t k = 0; k < K; k++) {
+            double sk = s ? (double)s[k] : 1.0;
+            double g = (double)gamma[k] / sk;
+            double b = (double)beta[k] / sk;
+            double d = (double)orc_h2f(x[k]) - mean;
+            double nk = d * r;
+            xp[k] = (float)fma(nk, g, b);
+            if (!isfinite(xp[k])) bad = 1;
+        }
+    }
+    if (st) {
+        st[0] = mean;
+        st[1] = var;
+        st[2] = r;
+    }
+    return bad;
+}
+
 void orc_layernorm_quant_smooth(const uint16_t *X, const float *gamma, const float *beta,
                                 const float *s, double eps, int64_t M, int64_t K,
                                 int8_t *Xq, float *sx, float *xs, double *stats)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; m++) {
-        const uint16_t *x = X + m * K;
         float *xp = xs ? xs + m * K : (float *)malloc((size_t)K * sizeof(float));
-        int bad = 0;
-        for (int64_t k = 0; k < K; k++)
-            if (!isfinite(orc_h2f(x[k]))) bad = 1;
-        double mean = NAN, var = NAN, r = NAN;
-        if (!bad) {
-            int64_t s1 = 0;
-            unsigned __int128 s2 = 0;
-            for (int64_t k = 0; k < K; k++) {
-                int64_t a = half_units(x[k]);
-                s1 += a;
-                s2 += (unsigned __int128)(a < 0 ? -a : a) * (unsigned __int128)(a < 0 ? -a : a);
-            }
-            mean = ldexp((double)s1, -24) / (double)K;
-            double ex2 = ldexp((double)s2, -48) / (double)K;
-            double mm = mean * mean;
-            var = ex2 - mm;
-            if (var < 0.0) var = 0.0;
-            double sd = sqrt(var + eps);
-            r = 1.0 / sd;
-            for (int64_t k = 0; k < K; k++) {
-                double sk = s ? (double)s[k] : 1.0;
-                double g = (double)gamma[k] / sk;
-                double b = (double)beta[k] / sk;
-                double d = (double)orc_h2f(x[k]) - mean;
-                double nk = d * r;
-                xp[k] = (float)fma(nk, g, b);
-                if (!isfinite(xp[k])) bad = 1;
-            }
-        }
-        if (stats) {
-            stats[3 * m] = mean;
-            stats[3 * m + 1] = var;
-            stats[3 * m + 2] = r;
-        }
+        int bad = ln_row(X + m * K, gamma, beta, s, eps, K, xp, stats ? stats + 3 * m : NULL);
         if (bad) {                              /* flagged row: NaN scale, codes 0 */
             for (int64_t k = 0; k < K; k++) {
                 Xq[m * K + k] = 0;
@@ -967,6 +976,32 @@ void orc_layernorm_quant_smooth(const uint16_t *X, const float *gamma, const flo
             sx[m] = scale;
         }
         if (!xs) free(xp);
+    }
+}
+
+/* The same LayerNorm with the FP8 E4M3 per-token quantizer of
+ * orc_fp8_quantize_act in place of the INT8 one (the FP8 variant of the
+ * path): scale = max(max_k |x'|, 1e-8) / 448, codes e4m3(x' / scale).       */
+void orc_layernorm_quant_smooth_fp8(const uint16_t *X, const float *gamma, const float *beta,
+                                    const float *s, double eps, int64_t M, int64_t K,
+                                    uint8_t *Xq, float *sx)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        float *xp = (float *)malloc((size_t)K * sizeof(float));
+        if (ln_row(X + m * K, gamma, beta, s, eps, K, xp, NULL)) {
+            for (int64_t k = 0; k < K; k++) Xq[m * K + k] = 0;
+            sx[m] = NAN;
+        } else {
+            float a = 0.0f;
+            for (int64_t k = 0; k < K; k++)
+                if (fabsf(xp[k]) > a) a = fabsf(xp[k]);
+            if (a < 1e-8f) a = 1e-8f;
+            float scale = a / 448.0f;
+            for (int64_t k = 0; k < K; k++) Xq[m * K + k] = (uint8_t)orc_e4m3_encode(xp[k] / scale);
+            sx[m] = scale;
+        }
+        free(xp);
     }
 }
 

@@ -18,7 +18,10 @@ quantizer (Quantization operators guide §5.3, deployment fusion). CPU only.
   * the codes are the per-token quantizer's: every code within half a step
     of x' / sx, the largest |x'| of a row at +-127;
   * a row holding a NaN or an infinity, or whose x' overflows fp32, is
-    flagged (NaN scale, zero codes) and no other row changes.
+    flagged (NaN scale, zero codes) and no other row changes;
+  * the FP8 form: the same x' with scale max|x'| / 448, every code equal to
+    torch's float8_e4m3fn cast of fl32(x' / scale), the row maximum at
+    +-448, flagged rows as in the INT8 form.
 """
 from fractions import Fraction
 
@@ -197,3 +200,20 @@ def test_nonfinite_rows_flagged(orc):
     s2[5] = 1e-3
     q, sc = orc.layernorm_quant_smooth(X, gamma, big, s2)
     assert np.isnan(sc).all() and (q == 0).all()
+
+
+def test_fp8_form(orc):
+    M, K = 24, 2048
+    X = _act(M, K)
+    X[3, 9] = np.float16(np.nan)
+    gamma, beta, s = _params(K)
+    q8, sx8, xs, _ = orc.layernorm_quant_smooth(X, gamma, beta, s, 1e-5, want_x=True)
+    q, sx = orc.layernorm_quant_smooth_fp8(X, gamma, beta, s, 1e-5)
+    ok = np.isfinite(sx8)
+    assert np.array_equal(np.isnan(sx), ~ok) and (q[~ok] == 0).all()
+    a = np.abs(xs[ok]).max(axis=1)
+    np.testing.assert_array_equal(sx[ok], (np.maximum(a, np.float32(1e-8)) / np.float32(448)).astype(np.float32))
+    quot = (xs[ok] / sx[ok][:, None]).astype(np.float32)
+    ref = torch.from_numpy(quot).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(q[ok], ref)
+    assert ((q[ok] & 0x7F) == 0x7E).any(axis=1).all()   # the row maximum at +-448
