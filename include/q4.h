@@ -282,6 +282,16 @@ Q4_API q4_status layernorm_quant_smooth(const void *X, const float *gamma, const
                                         const float *smooth_s, double eps, int64_t M, int64_t K,
                                         int8_t *Xq, float *x_scale, void *stream);
 
+/* layernorm_quant_smooth_fp8 -- the same LayerNorm with the FP8 E4M3
+ * per-token quantizer of fp8_quantize_act (Operators guide §4.2, §5.3):
+ *   x_scale[m] = max(max_k |x'|, 1e-8) / 448,
+ *   Xq = the nearest E4M3 value of fl32(x' / x_scale[m]) (ties to even, sign
+ *        kept on zero), as bytes; feeds fp8_gemm.
+ * Arguments, layout, flags and errors as layernorm_quant_smooth. */
+Q4_API q4_status layernorm_quant_smooth_fp8(const void *X, const float *gamma, const float *beta,
+                                            const float *smooth_s, double eps, int64_t M, int64_t K,
+                                            uint8_t *Xq, float *x_scale, void *stream);
+
 /* ----------------------------------------------------------------------------
  * w8a8_gemm -- INT8 GEMM with exact int32 accumulation and the scale
  * epilogue (Operators guide §2.3 INT8 GEMM + DequantizeOp, §5.2 path A):

@@ -13,6 +13,7 @@ Functions (same names as the C ABI):
   q8_quantize_weight(W, smooth_s=None) -> (Wq, w_scale)
   q8_quantize_act(X, smooth_s=None) -> (Xq, x_scale)
   layernorm_quant_smooth(X, gamma, beta, smooth_s=None, eps=1e-5) -> (Xq, x_scale)
+  layernorm_quant_smooth_fp8(X, gamma, beta, smooth_s=None, eps=1e-5) -> (Xq E4M3, x_scale)
   w8a8_gemm(Xq, x_scale, Wq, w_scale, acc_out=None) -> Y
   w8a8_linear(X, Wq, w_scale, smooth_s=None, workspace=None, acc_out=None) -> Y
   w8a8_linear_noalloc(X, Wq, w_scale, smooth_s=None, acc_out=None) -> Y  (no workspace)
@@ -67,6 +68,7 @@ SIGNATURES = {
     "q8_quantize_weight": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "q8_quantize_act": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "layernorm_quant_smooth": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]),
+    "layernorm_quant_smooth_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_double, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "w8a8_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
@@ -336,21 +338,32 @@ def q8_quantize_act(X: torch.Tensor, smooth_s: torch.Tensor | None = None, out=N
     return Xq, sx
 
 
+def _layernorm_quant(name: str, code_dtype, X, gamma, beta, smooth_s, eps, out):
+    _need(X, torch.float16, "X", 2)
+    M, K = X.shape
+    for pname, t in (("gamma", gamma), ("beta", beta)):
+        _need(t, torch.float32, pname, 1)
+        if t.numel() != K:
+            raise ValueError(f"{pname} has {t.numel()} entries, K={K}")
+    _need_smooth(smooth_s, K)
+    Xq, sx = _row_outputs(out, M, K, code_dtype, X.device)
+    _check(getattr(lib(), name)(_ptr(X), _ptr(gamma), _ptr(beta), _ptr(smooth_s), float(eps), M, K,
+                                _ptr(Xq), _ptr(sx), _stream(X)))
+    return Xq, sx
+
+
 def layernorm_quant_smooth(X: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
                            smooth_s: torch.Tensor | None = None, eps: float = 1e-5, out=None):
     """LayerNorm of each row of X with the divide by smooth_s folded into
     gamma and beta, then per-token INT8: (Xq int8 [M, K], x_scale fp32 [M])."""
-    _need(X, torch.float16, "X", 2)
-    M, K = X.shape
-    for name, t in (("gamma", gamma), ("beta", beta)):
-        _need(t, torch.float32, name, 1)
-        if t.numel() != K:
-            raise ValueError(f"{name} has {t.numel()} entries, K={K}")
-    _need_smooth(smooth_s, K)
-    Xq, sx = _row_outputs(out, M, K, torch.int8, X.device)
-    _check(lib().layernorm_quant_smooth(_ptr(X), _ptr(gamma), _ptr(beta), _ptr(smooth_s), float(eps), M, K,
-                                        _ptr(Xq), _ptr(sx), _stream(X)))
-    return Xq, sx
+    return _layernorm_quant("layernorm_quant_smooth", torch.int8, X, gamma, beta, smooth_s, eps, out)
+
+
+def layernorm_quant_smooth_fp8(X: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
+                               smooth_s: torch.Tensor | None = None, eps: float = 1e-5, out=None):
+    """The same LayerNorm with per-token FP8 E4M3 codes:
+    (Xq E4M3 bytes uint8 [M, K], x_scale fp32 [M])."""
+    return _layernorm_quant("layernorm_quant_smooth_fp8", torch.uint8, X, gamma, beta, smooth_s, eps, out)
 
 
 def w8a8_gemm(Xq: torch.Tensor, x_scale: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,

@@ -271,26 +271,41 @@ Q4_API q4_status q8_quantize_act(const void *X, const float *smooth_s, int64_t M
     return done(e, "q8_quantize_act", stream);
 }
 
+static q4_status layernorm_quant_common(const char *what, const void *X, const float *gamma, const float *beta,
+                                        const float *smooth_s, double eps, int64_t M, int64_t K, void *Xq,
+                                        float *x_scale, bool fp8, void *stream)
+{
+    Q4_REQUIRE(M >= 0 && K > 0 && M <= kIntMax && K % 8 == 0, Q4_ERR_INVALID_ARG,
+               "%s: bad shape M=%lld K=%lld (K must be a positive multiple of 8)", what, (long long)M,
+               (long long)K);
+    Q4_REQUIRE(eps > 0.0 && eps <= 1.7976931348623157e308, Q4_ERR_INVALID_ARG, "%s: eps must be positive and finite",
+               what);
+    Q4_REQUIRE(K <= q4k::kLnMaxK, Q4_ERR_UNSUPPORTED, "%s: K=%lld above %d (the exact row sums need K <= %d)", what,
+               (long long)K, q4k::kLnMaxK, q4k::kLnMaxK);
+    if (M == 0) return ok();
+    Q4_REQUIRE(X && gamma && beta && Xq && x_scale, Q4_ERR_INVALID_ARG, "%s: null pointer", what);
+    Q4_REQUIRE(aligned16(X) && aligned16(gamma) && aligned16(beta) && aligned16(Xq) &&
+                   (!smooth_s || aligned16(smooth_s)),
+               Q4_ERR_MISALIGNED, "%s: X, gamma, beta, smooth_s and Xq must be 16-byte aligned", what);
+    hipError_t e = q4k::launch_layernorm_quant(static_cast<const uint16_t *>(X), gamma, beta, smooth_s, eps, M, K,
+                                               Xq, x_scale, fp8, static_cast<hipStream_t>(stream));
+    return done(e, what, stream);
+}
+
 Q4_API q4_status layernorm_quant_smooth(const void *X, const float *gamma, const float *beta,
                                         const float *smooth_s, double eps, int64_t M, int64_t K,
                                         int8_t *Xq, float *x_scale, void *stream)
 {
-    Q4_REQUIRE(M >= 0 && K > 0 && M <= kIntMax && K % 8 == 0, Q4_ERR_INVALID_ARG,
-               "layernorm_quant_smooth: bad shape M=%lld K=%lld (K must be a positive multiple of 8)",
-               (long long)M, (long long)K);
-    Q4_REQUIRE(eps > 0.0 && eps <= 1.7976931348623157e308, Q4_ERR_INVALID_ARG,
-               "layernorm_quant_smooth: eps must be positive and finite");
-    Q4_REQUIRE(K <= q4k::kLnMaxK, Q4_ERR_UNSUPPORTED,
-               "layernorm_quant_smooth: K=%lld above %d (the exact row sums need K <= %d)", (long long)K,
-               q4k::kLnMaxK, q4k::kLnMaxK);
-    if (M == 0) return ok();
-    Q4_REQUIRE(X && gamma && beta && Xq && x_scale, Q4_ERR_INVALID_ARG, "layernorm_quant_smooth: null pointer");
-    Q4_REQUIRE(aligned16(X) && aligned16(gamma) && aligned16(beta) && aligned16(Xq) &&
-                   (!smooth_s || aligned16(smooth_s)),
-               Q4_ERR_MISALIGNED, "layernorm_quant_smooth: X, gamma, beta, smooth_s and Xq must be 16-byte aligned");
-    hipError_t e = q4k::launch_layernorm_quant(static_cast<const uint16_t *>(X), gamma, beta, smooth_s, eps, M, K,
-                                               Xq, x_scale, static_cast<hipStream_t>(stream));
-    return done(e, "layernorm_quant_smooth", stream);
+    return layernorm_quant_common("layernorm_quant_smooth", X, gamma, beta, smooth_s, eps, M, K, Xq, x_scale,
+                                  false, stream);
+}
+
+Q4_API q4_status layernorm_quant_smooth_fp8(const void *X, const float *gamma, const float *beta,
+                                            const float *smooth_s, double eps, int64_t M, int64_t K,
+                                            uint8_t *Xq, float *x_scale, void *stream)
+{
+    return layernorm_quant_common("layernorm_quant_smooth_fp8", X, gamma, beta, smooth_s, eps, M, K, Xq, x_scale,
+                                  true, stream);
 }
 
 // Preconditions of the INT8 GEMM, checked before anything is launched (also

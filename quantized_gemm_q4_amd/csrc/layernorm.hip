@@ -77,10 +77,12 @@ __device__ __forceinline__ double half_at(const u32x4 &v, int e)
 // chunk c (columns 8c + 2j, 8c + 2j + 1) at index j * nch + c, so the 64
 // lanes of one read take 64 consecutive pieces (no bank conflicts).
 // EXACT: K = 512 CPL, every lane owns CPL whole chunks (no per-chunk tests).
-template <int CPL, bool EXACT>
+// FP8: E4M3 codes with scale max|x'| / 448 (the FP8 path's row quantizer)
+// instead of INT8 with max|x'| / 127.
+template <int CPL, bool EXACT, bool FP8>
 __global__ __launch_bounds__(kLnWaves * 64) void ln_quant_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ gamma, const float *__restrict__ beta,
-    const float *__restrict__ s, double eps, int M, int K, int8_t *__restrict__ Xq,
+    const float *__restrict__ s, double eps, int M, int K, uint8_t *__restrict__ Xq,
     float *__restrict__ sx)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -198,9 +200,9 @@ __global__ __launch_bounds__(kLnWaves * 64) void ln_quant_kernel(
 
         // 4. scale and codes
         const bool bad = amax >= 0x7f800000u;
-        const float sc = bad ? __builtin_nanf("") : fmaxf(__builtin_bit_cast(float, amax), 1e-8f) / kRowMax<false>;
+        const float sc = bad ? __builtin_nanf("") : fmaxf(__builtin_bit_cast(float, amax), 1e-8f) / kRowMax<FP8>;
         const double rs = recip64((double)(bad ? 1.0f : sc));
-        int8_t *qrow = Xq + (int64_t)m * K;
+        uint8_t *qrow = Xq + (int64_t)m * K;
 #pragma unroll
         for (int i = 0; i < CPL; i++) {
             const int c = lane + 64 * i;
@@ -208,8 +210,8 @@ __global__ __launch_bounds__(kLnWaves * 64) void ln_quant_kernel(
                 float q[8];
 #pragma unroll
                 for (int e = 0; e < 8; e++) q[e] = (float)((double)xp[i][e] * rs);
-                u32x2 out = {row_codes4<false>(q[0], q[1], q[2], q[3]),
-                             row_codes4<false>(q[4], q[5], q[6], q[7])};
+                u32x2 out = {row_codes4<FP8>(q[0], q[1], q[2], q[3]),
+                             row_codes4<FP8>(q[4], q[5], q[6], q[7])};
                 if (bad) out = u32x2{0u, 0u};
                 *reinterpret_cast<u32x2 *>(qrow + 8 * c) = out;
             }
@@ -223,37 +225,32 @@ __global__ __launch_bounds__(kLnWaves * 64) void ln_quant_kernel(
     }
 }
 
-template <int CPL, bool EXACT>
+template <int CPL, bool EXACT, bool FP8>
 hipError_t launch_cpl(const uint16_t *X, const float *gamma, const float *beta, const float *s,
-                      double eps, int64_t M, int64_t K, int8_t *Xq, float *sx, hipStream_t stream)
+                      double eps, int64_t M, int64_t K, uint8_t *Xq, float *sx, hipStream_t stream)
 {
     const size_t lds = (size_t)K * 16;   // folded gamma and beta, fp64
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&ln_quant_kernel<CPL, EXACT>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&ln_quant_kernel<CPL, EXACT, FP8>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        kLnMaxK * 16);
     if (attr != hipSuccess) return attr;
     const int per_cu = lds <= 80 * 1024 ? 2 : 1;
     const int64_t want = (M + kLnWaves - 1) / kLnWaves;
     const int blocks = (int)(want < 256 * per_cu ? want : 256 * per_cu);
-    hipLaunchKernelGGL((ln_quant_kernel<CPL, EXACT>), dim3(blocks), dim3(kLnWaves * 64), lds, stream, X, gamma, beta, s,
+    hipLaunchKernelGGL((ln_quant_kernel<CPL, EXACT, FP8>), dim3(blocks), dim3(kLnWaves * 64), lds, stream, X, gamma, beta, s,
                        eps, (int)M, (int)K, Xq, sx);
     return hipGetLastError();
 }
 
-}  // namespace
-
-// Shape, alignment and eps were validated by the C-ABI layer (K a multiple
-// of 8 up to kLnMaxK, X / gamma / beta / s 16-byte aligned, Xq 8-byte
-// aligned, eps > 0 and finite, M >= 1).
-hipError_t launch_layernorm_quant(const uint16_t *X, const float *gamma, const float *beta, const float *s,
-                                  double eps, int64_t M, int64_t K, int8_t *Xq, float *sx,
-                                  hipStream_t stream)
+template <bool FP8>
+hipError_t launch_fmt(const uint16_t *X, const float *gamma, const float *beta, const float *s, double eps,
+                      int64_t M, int64_t K, uint8_t *Xq, float *sx, hipStream_t stream)
 {
     const int cpl = (int)((K / 8 + 63) / 64);   // chunks per lane
     if (K % 512 == 0) {   // whole chunks on every lane
         switch (cpl) {
 #define Q4_LN_CASE(n) \
-        case n: return launch_cpl<n, true>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+        case n: return launch_cpl<n, true, FP8>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
             Q4_LN_CASE(1) Q4_LN_CASE(2) Q4_LN_CASE(3) Q4_LN_CASE(4) Q4_LN_CASE(5) Q4_LN_CASE(6)
             Q4_LN_CASE(7) Q4_LN_CASE(8) Q4_LN_CASE(9) Q4_LN_CASE(10) Q4_LN_CASE(11) Q4_LN_CASE(12)
             Q4_LN_CASE(13) Q4_LN_CASE(14) Q4_LN_CASE(15) Q4_LN_CASE(16)
@@ -261,11 +258,25 @@ hipError_t launch_layernorm_quant(const uint16_t *X, const float *gamma, const f
         default: return hipErrorInvalidValue;
         }
     }
-    if (cpl <= 1) return launch_cpl<1, false>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
-    if (cpl <= 2) return launch_cpl<2, false>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
-    if (cpl <= 4) return launch_cpl<4, false>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
-    if (cpl <= 8) return launch_cpl<8, false>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
-    return launch_cpl<16, false>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+    if (cpl <= 1) return launch_cpl<1, false, FP8>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+    if (cpl <= 2) return launch_cpl<2, false, FP8>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+    if (cpl <= 4) return launch_cpl<4, false, FP8>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+    if (cpl <= 8) return launch_cpl<8, false, FP8>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+    return launch_cpl<16, false, FP8>(X, gamma, beta, s, eps, M, K, Xq, sx, stream);
+}
+
+}  // namespace
+
+// Shape, alignment and eps were validated by the C-ABI layer (K a multiple
+// of 8 up to kLnMaxK, X / gamma / beta / s / Xq 16-byte aligned, eps > 0
+// and finite, M >= 1). Xq receives INT8 codes, or E4M3 bytes with fp8.
+hipError_t launch_layernorm_quant(const uint16_t *X, const float *gamma, const float *beta, const float *s,
+                                  double eps, int64_t M, int64_t K, void *Xq, float *sx, bool fp8,
+                                  hipStream_t stream)
+{
+    uint8_t *q = static_cast<uint8_t *>(Xq);
+    return fp8 ? launch_fmt<true>(X, gamma, beta, s, eps, M, K, q, sx, stream)
+               : launch_fmt<false>(X, gamma, beta, s, eps, M, K, q, sx, stream);
 }
 
 }  // namespace q4k

@@ -58,7 +58,7 @@ hipError_t launch_q8_act(const uint16_t *X, const float *s, int64_t M, int64_t K
 // kLnMaxK, where the kernel's fp64 row sums are exact).
 constexpr int kLnMaxK = 8192;
 hipError_t launch_layernorm_quant(const uint16_t *X, const float *gamma, const float *beta, const float *s,
-                                  double eps, int64_t M, int64_t K, int8_t *Xq, float *sx,
+                                  double eps, int64_t M, int64_t K, void *Xq, float *sx, bool fp8,
                                   hipStream_t stream);
 hipError_t launch_smooth_scales(const uint16_t *Xcal, int64_t R, const uint16_t *W, int64_t N,
                                 int64_t K, float alpha, float *s, hipStream_t st);

@@ -125,6 +125,12 @@ def layers(*descs):
     (lambda L: L.layernorm_quant_smooth(FAKE, FAKE, MISAL, None, 1e-5, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.layernorm_quant_smooth(FAKE, FAKE, FAKE, MISAL, 1e-5, 4, 128, FAKE, FAKE, None), q4.Q4_ERR_MISALIGNED),
     (lambda L: L.layernorm_quant_smooth(None, None, None, None, 1e-5, 0, 128, None, None, None), q4.Q4_OK),
+    (lambda L: L.layernorm_quant_smooth_fp8(FAKE, FAKE, FAKE, None, 1e-5, 4, 8200, FAKE, FAKE, None),
+     q4.Q4_ERR_UNSUPPORTED),
+    (lambda L: L.layernorm_quant_smooth_fp8(FAKE, FAKE, FAKE, None, -1.0, 4, 128, FAKE, FAKE, None),
+     q4.Q4_ERR_INVALID_ARG),
+    (lambda L: L.layernorm_quant_smooth_fp8(FAKE, FAKE, FAKE, None, 1e-5, 4, 128, MISAL, FAKE, None),
+     q4.Q4_ERR_MISALIGNED),
     (lambda L: L.w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 140000, FAKE, None, None), q4.Q4_ERR_INVALID_ARG),
     (lambda L: L.w8a8_gemm(MISAL, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, None, None), q4.Q4_ERR_MISALIGNED),

@@ -107,3 +107,24 @@ def test_lookup_layers(orc, fmt, M):
     X = gpu(X0)
     Y = torch.empty((M, 2048), dtype=torch.float16, device=X.device)
     check_replays(lambda: lin(X, c, s, out=Y), lambda Xr: [lin(Xr, c, s)], X, [Y], M + 3)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_layernorm_quant(orc, fp8):
+    """The LayerNorm with the divide and the per-token quantizer fused in
+    (INT8 and E4M3 forms), as a serving loop would capture it."""
+    M, K = 64, 4096
+    p = workloads.layernorm_params(K)
+    gam, bet, s = gpu(p["gamma"]), gpu(p["beta"]), gpu(p["s"])
+    X0 = np.random.default_rng(31).standard_normal((M, K)).astype(np.float16)
+    X = gpu(X0)
+    fn = q4.layernorm_quant_smooth_fp8 if fp8 else q4.layernorm_quant_smooth
+    ref = orc.layernorm_quant_smooth_fp8 if fp8 else orc.layernorm_quant_smooth
+    q = torch.empty((M, K), dtype=torch.uint8 if fp8 else torch.int8, device=X.device)
+    sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    fn(X, gam, bet, s, 1e-5, out=(q, sx))
+    rq, rs = ref(X0, p["gamma"], p["beta"], p["s"], 1e-5)
+    assert np.array_equal(host(q), rq) and np.array_equal(host(sx).view(np.uint32), rs.view(np.uint32))
+    call = lambda: fn(X, gam, bet, s, 1e-5, out=(q, sx))
+    eager = lambda Xr: fn(Xr, gam, bet, s, 1e-5)
+    check_replays(call, eager, X, [q, sx], seed=37)

@@ -4,7 +4,8 @@ W8A8-shaped workload (2048 x 8192), on every chunk layout of the kernel
 (K a multiple of 512, and K that leaves partial chunks), on rows whose
 squares a running fp64 sum would round differently, constant rows,
 fp16-extreme rows, more rows than wavefronts (rows revisited by the grid
-stride), and flagged rows (NaN / infinity in X, x' past the fp32 range)."""
+stride), and flagged rows (NaN / infinity in X, x' past the fp32 range);
+the FP8 E4M3 form on the same cases."""
 import numpy as np
 import pytest
 
@@ -29,9 +30,11 @@ def _x(M, K, seed):
     return X.astype(np.float16)
 
 
-def _check(orc, X, gamma, beta, s, eps=1e-5):
-    ref_q, ref_s = orc.layernorm_quant_smooth(X, gamma, beta, s, eps)
-    Xq, sx = q4.layernorm_quant_smooth(gpu(X), gpu(gamma), gpu(beta), None if s is None else gpu(s), eps)
+def _check(orc, X, gamma, beta, s, eps=1e-5, fp8=False):
+    ref = orc.layernorm_quant_smooth_fp8 if fp8 else orc.layernorm_quant_smooth
+    fn = q4.layernorm_quant_smooth_fp8 if fp8 else q4.layernorm_quant_smooth
+    ref_q, ref_s = ref(X, gamma, beta, s, eps)
+    Xq, sx = fn(gpu(X), gpu(gamma), gpu(beta), None if s is None else gpu(s), eps)
     got_q, got_s = host(Xq), host(sx)
     bad = np.nonzero((got_q != ref_q).any(axis=1) | (got_s.view(np.uint32) != ref_s.view(np.uint32)))[0]
     assert bad.size == 0, f"rows {bad[:8]} differ (of {X.shape[0]})"
@@ -111,3 +114,19 @@ def test_eps(orc, eps):
     X = _x(6, 1024, 12)
     X[2] = np.float16(0.5)   # var = 0: x' = b only through eps
     _check(orc, X, gamma, beta, s, eps)
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (33, 1024), (9, 8192), (5, 200), (3, 4104)])
+def test_fp8_shapes(orc, M, K):
+    gamma, beta, s = _params(K, M + K + 1)
+    X = _x(M, K, 3 * M + K + 1)
+    if M > 2:
+        X[1, 0] = np.float16(np.inf)
+    _check(orc, X, gamma, beta, s, fp8=True)
+
+
+def test_fp8_workload_full(orc):
+    X = workloads.w8a8()["X"]
+    p = workloads.layernorm_params(X.shape[1])
+    q, sx = _check(orc, X, p["gamma"], p["beta"], p["s"], fp8=True)
+    assert ((q & 0x7F) == 0x7E).any(axis=1).all() and np.isfinite(sx).all()
