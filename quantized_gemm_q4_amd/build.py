@@ -16,10 +16,15 @@ ARCH = "gfx950"
 # Kernels that turn floating point into integer codes (and the W8A8
 # epilogue) are built without FMA contraction; every TU keeps IEEE-correct
 # fp32 division and square root and no fast-math. Packed fp32 VALU forms are
-# disabled on the device.
+# disabled on the device. Kernel arguments are preloaded into scalar
+# registers (as many as fit the user SGPRs; the code object keeps a fallback
+# that loads them itself), so a wavefront issues its first memory loads
+# without waiting for a kernel-argument load: decode GEMV N = 11008 6.75 ->
+# 6.23 us, batched decode 2-5% faster.
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden",
           "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-kernarg-preload-count=16",
           "-Wall", "-Wno-unused-command-line-argument"]
 SOURCES = {
     "abi.hip": [],
