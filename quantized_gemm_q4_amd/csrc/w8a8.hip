@@ -14,6 +14,9 @@
 // fp32 roundings then one fp16 rounding, the same expression as the pages'.
 #include <type_traits>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "q4_internal.hpp"
 #include "row_codes.hpp"
 
@@ -413,6 +416,70 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
 
 
 // ---------------------------------------------------------------------------
+// X operand of the INT8 / FP8 decode GEMVs. Both read, for step s of
+// wavefront w (k = 128 (w SPW + s) ..), the 16-byte runs 16 g and 64 + 16 g
+// of X row m = min(l16, M - 1). With XS (M * SPW <= 32) each wavefront loads
+// its own M x 128 SPW bytes of X once, as 16-byte chunks (chunk j = lane +
+// 64 i is row j / (8 SPW), piece j % (8 SPW)), before its weight loads,
+// stores them to its own LDS region and reads its fragments back after a
+// wave barrier: a handful of load instructions per wavefront instead of 2 SPW
+// per lane, nearly all of them repeats of the same X bytes. Otherwise each
+// lane loads its fragments directly.
+// Q4_GEMV_XS0 (set, not "0"): the direct X loads even where the staging
+// applies (for A/B timing and the tests of both forms). Read at every call.
+bool gemv_x_direct()
+{
+    const char *e = std::getenv("Q4_GEMV_XS0");
+    return e && *e && std::strcmp(e, "0") != 0;
+}
+
+template <int SPW, bool XS>
+struct GemvX {
+    static constexpr int kChunks = XS ? (32 * 8 + 63) / 64 : 1;   // M * 8 SPW <= 256 chunks
+    intx4 c[kChunks];
+    intx4 lo[SPW], hi[SPW];
+
+    __device__ __forceinline__ void load(const uint8_t *__restrict__ Xq, int M, int K, int s0, int m, int g,
+                                         int lane)
+    {
+        if constexpr (XS) {
+#pragma unroll
+            for (int i = 0; i < kChunks; i++) {
+                const int j = lane + 64 * i, r = j / (8 * SPW), p = j % (8 * SPW);
+                if (r < M) c[i] = *reinterpret_cast<const intx4 *>(Xq + (int64_t)r * K + s0 * 128 + 16 * p);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < SPW; s++) {
+                const uint8_t *xp = Xq + (int64_t)m * K + (s0 + s) * 128 + 16 * g;
+                lo[s] = *reinterpret_cast<const intx4 *>(xp);
+                hi[s] = *reinterpret_cast<const intx4 *>(xp + 64);
+            }
+        }
+    }
+    // xs: this wavefront's LDS region, M x 128 SPW bytes
+    __device__ __forceinline__ void stage(intx4 *xs, int M, int m, int g, int lane)
+    {
+        if constexpr (XS) {
+#pragma unroll
+            for (int i = 0; i < kChunks; i++) {
+                const int j = lane + 64 * i;
+                if (j / (8 * SPW) < M) xs[j] = c[i];
+            }
+            // other lanes of this wavefront read what these lanes wrote
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int s = 0; s < SPW; s++) {
+                lo[s] = xs[m * 8 * SPW + 8 * s + g];
+                hi[s] = xs[m * 8 * SPW + 8 * s + 4 + g];
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
 // FP8 decode GEMV, M <= 16, K % 1024 == 0 (K <= 8192): the E4M3 GEMM's tiles
 // would use one row in 256, so a block owns 16 weight rows and its 8
 // wavefronts split K into 128-k steps, each one v_mfma_scale_f32_16x16x128_
@@ -424,13 +491,14 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_large_kernel(
 // epilogue is the GEMM's, y = fp16((acc * sx[m]) * sw[n]).
 constexpr int F8G_WAVES = 8;
 
-template <int SPW>
+template <int SPW, bool XS>
 __global__ __launch_bounds__(F8G_WAVES * 64) void fp8_gemv16_kernel(
     const uint8_t *__restrict__ Xq, const float *__restrict__ sx, const uint8_t *__restrict__ Wq,
     const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y)
 {
     static_assert(SPW == 1 || SPW == 2 || SPW == 4 || SPW == 8, "steps per wavefront");
     __shared__ float red[F8G_WAVES][4][64];
+    __shared__ intx4 xsm[XS ? F8G_WAVES * 32 * 8 : 1];   // per wavefront M x 128 SPW bytes, M * SPW <= 32
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, g = lane >> 4;
     const int n0 = (int)blockIdx.x * 16;
@@ -438,13 +506,9 @@ __global__ __launch_bounds__(F8G_WAVES * 64) void fp8_gemv16_kernel(
     const int m = l16 < M ? l16 : M - 1;
     const int s0 = wave * SPW;
 
-    intx4 xlo[SPW], xhi[SPW], wlo[SPW], whi[SPW];
-#pragma unroll
-    for (int s = 0; s < SPW; s++) {
-        const uint8_t *xp = Xq + (int64_t)m * K + (s0 + s) * 128 + 16 * g;
-        xlo[s] = *reinterpret_cast<const intx4 *>(xp);
-        xhi[s] = *reinterpret_cast<const intx4 *>(xp + 64);
-    }
+    GemvX<SPW, XS> x;
+    x.load(Xq, M, K, s0, m, g, lane);
+    intx4 wlo[SPW], whi[SPW];
 #pragma unroll
     for (int s = 0; s < SPW; s++) {
         const uint8_t *wp = Wq + nrow * K + (s0 + s) * 128 + 16 * g;
@@ -452,12 +516,13 @@ __global__ __launch_bounds__(F8G_WAVES * 64) void fp8_gemv16_kernel(
         whi[s] = *reinterpret_cast<const intx4 *>(wp + 64);
     }
     __builtin_amdgcn_sched_barrier(0);   // every load goes out before the first product
+    x.stage(xsm + wave * 32 * 8, M, m, g, lane);
 
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < SPW; s++) {
         const intx8 w8 = __builtin_shufflevector(wlo[s], whi[s], 0, 1, 2, 3, 4, 5, 6, 7);
-        const intx8 a = __builtin_shufflevector(xlo[s], xhi[s], 0, 1, 2, 3, 4, 5, 6, 7);
+        const intx8 a = __builtin_shufflevector(x.lo[s], x.hi[s], 0, 1, 2, 3, 4, 5, 6, 7);
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w8, a, acc, 0, 0, 0, 127, 0, 127);
     }
 
@@ -491,7 +556,7 @@ __global__ __launch_bounds__(F8G_WAVES * 64) void fp8_gemv16_kernel(
 // and acc_out (when given) receives the int32 sums.
 constexpr int I8G_WAVES = 8;
 
-template <int SPW>
+template <int SPW, bool XS>
 __global__ __launch_bounds__(I8G_WAVES * 64) void w8a8_gemv16_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ sx, const int8_t *__restrict__ Wq,
     const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y,
@@ -499,6 +564,7 @@ __global__ __launch_bounds__(I8G_WAVES * 64) void w8a8_gemv16_kernel(
 {
     static_assert(SPW == 1 || SPW == 2 || SPW == 4 || SPW == 8, "steps per wavefront");
     __shared__ int red[I8G_WAVES][4][64];
+    __shared__ intx4 xsm[XS ? I8G_WAVES * 32 * 8 : 1];   // per wavefront M x 128 SPW bytes, M * SPW <= 32
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, g = lane >> 4;
     const int n0 = (int)blockIdx.x * 16;
@@ -506,13 +572,9 @@ __global__ __launch_bounds__(I8G_WAVES * 64) void w8a8_gemv16_kernel(
     const int m = l16 < M ? l16 : M - 1;
     const int s0 = wave * SPW;
 
-    intx4 xlo[SPW], xhi[SPW], wlo[SPW], whi[SPW];
-#pragma unroll
-    for (int s = 0; s < SPW; s++) {
-        const int8_t *xp = Xq + (int64_t)m * K + (s0 + s) * 128 + 16 * g;
-        xlo[s] = *reinterpret_cast<const intx4 *>(xp);
-        xhi[s] = *reinterpret_cast<const intx4 *>(xp + 64);
-    }
+    GemvX<SPW, XS> x;
+    x.load(reinterpret_cast<const uint8_t *>(Xq), M, K, s0, m, g, lane);
+    intx4 wlo[SPW], whi[SPW];
 #pragma unroll
     for (int s = 0; s < SPW; s++) {
         const int8_t *wp = Wq + nrow * K + (s0 + s) * 128 + 16 * g;
@@ -520,12 +582,13 @@ __global__ __launch_bounds__(I8G_WAVES * 64) void w8a8_gemv16_kernel(
         whi[s] = *reinterpret_cast<const intx4 *>(wp + 64);
     }
     __builtin_amdgcn_sched_barrier(0);   // every load goes out before the first product
+    x.stage(xsm + wave * 32 * 8, M, m, g, lane);
 
     intx4 acc = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < SPW; s++) {
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo[s], xlo[s], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi[s], xhi[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo[s], x.lo[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi[s], x.hi[s], acc, 0, 0, 0);
     }
 
 #pragma unroll
@@ -690,11 +753,12 @@ hipError_t launch_w8a8_gemm(const int8_t *Xq, const float *sx, const int8_t *Wq,
         auto go = [&](auto kernel) {
             kernel<<<blocks, I8G_WAVES * 64, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N, (int)K, Y, acc_out);
         };
+        const bool xs = M * (K / 1024) <= 32 && !gemv_x_direct();   // X staged per wavefront
         switch (K / 1024) {
-        case 1: go(w8a8_gemv16_kernel<1>); return hipGetLastError();
-        case 2: go(w8a8_gemv16_kernel<2>); return hipGetLastError();
-        case 4: go(w8a8_gemv16_kernel<4>); return hipGetLastError();
-        case 8: go(w8a8_gemv16_kernel<8>); return hipGetLastError();
+        case 1: xs ? go(w8a8_gemv16_kernel<1, true>) : go(w8a8_gemv16_kernel<1, false>); return hipGetLastError();
+        case 2: xs ? go(w8a8_gemv16_kernel<2, true>) : go(w8a8_gemv16_kernel<2, false>); return hipGetLastError();
+        case 4: xs ? go(w8a8_gemv16_kernel<4, true>) : go(w8a8_gemv16_kernel<4, false>); return hipGetLastError();
+        case 8: xs ? go(w8a8_gemv16_kernel<8, true>) : go(w8a8_gemv16_kernel<8, false>); return hipGetLastError();
         default: break;   // K = 3, 5, 6, 7 x 1024: the GEMMs
         }
     }
@@ -720,11 +784,12 @@ hipError_t launch_fp8_gemm(const uint8_t *Xq, const float *sx, const uint8_t *Wq
         auto go = [&](auto kernel) {
             kernel<<<blocks, F8G_WAVES * 64, 0, st>>>(Xq, sx, Wq, sw, (int)M, (int)N, (int)K, Y);
         };
+        const bool xs = M * (K / 1024) <= 32 && !gemv_x_direct();   // X staged per wavefront
         switch (K / 1024) {
-        case 1: go(fp8_gemv16_kernel<1>); return hipGetLastError();
-        case 2: go(fp8_gemv16_kernel<2>); return hipGetLastError();
-        case 4: go(fp8_gemv16_kernel<4>); return hipGetLastError();
-        case 8: go(fp8_gemv16_kernel<8>); return hipGetLastError();
+        case 1: xs ? go(fp8_gemv16_kernel<1, true>) : go(fp8_gemv16_kernel<1, false>); return hipGetLastError();
+        case 2: xs ? go(fp8_gemv16_kernel<2, true>) : go(fp8_gemv16_kernel<2, false>); return hipGetLastError();
+        case 4: xs ? go(fp8_gemv16_kernel<4, true>) : go(fp8_gemv16_kernel<4, false>); return hipGetLastError();
+        case 8: xs ? go(fp8_gemv16_kernel<8, true>) : go(fp8_gemv16_kernel<8, false>); return hipGetLastError();
         default: break;   // K = 3, 5, 6, 7 x 1024: the GEMM
         }
     }

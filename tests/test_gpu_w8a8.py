@@ -81,7 +81,11 @@ def test_gemm_shapes(orc, M, N, K):
 @pytest.mark.parametrize("M,N,K", [(1, 300, 1024), (5, 77, 2048), (16, 1000, 4096),
                                    (3, 64, 8192), (1, 11008, 4096), (7, 33, 3072),
                                    (16, 17, 1024)])
-def test_gemv_shapes(orc, M, N, K):
+@pytest.mark.parametrize("xs0", ["0", "1"])
+def test_gemv_shapes(orc, M, N, K, xs0, monkeypatch):
+    """Both forms of the decode GEMV's X operand: staged per wavefront in LDS
+    (M * K / 1024 <= 32) and loaded directly per lane (Q4_GEMV_XS0=1)."""
+    monkeypatch.setenv("Q4_GEMV_XS0", xs0)
     test_gemm_shapes(orc, M, N, K)
 
 
