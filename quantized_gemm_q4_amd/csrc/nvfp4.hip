@@ -74,12 +74,13 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(const uint16_t *__r
 
 // ---------------------------------------------------------------------------
 // Decode GEMV (M <= 16 rows of X per pass). A block of 8 wavefronts owns 16
-// output channels and all of K; wavefront w takes the 128-wide k-blocks w,
-// w + 8, w + 16, ..., four at a time (a batch). Lane (r16, q) holds column
+// output channels and all of K; wavefront w takes the 128-wide k-blocks in
+// batches of four consecutive ones (4w .. 4w + 3, then 32 further on, ...), so
+// a batch's 32 scale bytes of a row are one window of two 16-byte loads. Lane (r16, q) holds column
 // r16's code run for k = 32q .. 32q + 31 of a k-block (16 bytes, two blocks
 // of 16) and those two blocks' scale bytes; MFMA t pairs code dword t (scaled
 // by block t / 2) with X[r16][32q + 8t .. + 7]. Each wavefront fetches the X
-// runs of its own batch (lane l, load i: row i, k-block kb0 + 8 (l >> 4),
+// runs of its own batch (lane l, load i: row i, k-block kb0 + (l >> 4),
 // 16 bytes at 8 (l & 15)) before its codes, so they land first, and writes
 // them to an LDS region of its own ([row][k-block of the batch][128 k],
 // M KB): no block barrier stands between the loads and the compute. A-rows
@@ -91,7 +92,7 @@ template <int MAXR>   // rows per pass at most (1, 2, 4, 8, 16): the X registers
 __global__ __launch_bounds__(NV_WAVES * 64) void nvfp4_gemv_kernel(const uint16_t *__restrict__ X, int M, int N,
                                                                    int K, const uint8_t *__restrict__ codes,
                                                                    const uint8_t *__restrict__ scales,
-                                                                   uint16_t *__restrict__ Y)
+                                                                   uint16_t *__restrict__ Y, int vsc)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -112,8 +113,8 @@ __global__ __launch_bounds__(NV_WAVES * 64) void nvfp4_gemv_kernel(const uint16_
     const int pstride = live ? 128 : 0;   // elements from one k-block of the batch to the next
 
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kb0 = wave; kb0 < KB; kb0 += NV_WAVES * NV_PF) {
-        const int kx = kb0 + NV_WAVES * q;   // this lane's X k-block
+    for (int kb0 = NV_PF * wave; kb0 < KB; kb0 += NV_WAVES * NV_PF) {
+        const int kx = kb0 + q;   // this lane's X k-block
         u32x4 xv[MAXR];
 #pragma unroll
         for (int i = 0; i < MAXR; i++)
@@ -121,12 +122,32 @@ __global__ __launch_bounds__(NV_WAVES * 64) void nvfp4_gemv_kernel(const uint16_
                 xv[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)i * K + (int64_t)kx * 128 + r16 * 8);
         u32x4 cw[NV_PF];
         uint32_t sc[NV_PF];
+        // the batch's 4 k-blocks are consecutive: their 32 scale bytes of the
+        // row are one window, two 16-byte loads (vsc: the host found the
+        // window aligned); otherwise a 2-byte load per k-block
+        const bool win = vsc && kb0 + NV_PF <= KB;
+        u32x4 sw0 = {0u, 0u, 0u, 0u}, sw1 = {0u, 0u, 0u, 0u};
+        if (win) {
+            const uint8_t *sp = scales + (nrow * ks + (uint32_t)kb0 * 8u);
+            sw0 = *reinterpret_cast<const u32x4 *>(sp);
+            sw1 = *reinterpret_cast<const u32x4 *>(sp + 16);
+        }
 #pragma unroll
         for (int p = 0; p < NV_PF; p++) {
-            const int kb = kb0 + p * NV_WAVES;
+            const int kb = kb0 + p;
             const int kc = kb < KB ? kb : KB - 1;   // past the end: a valid k-block, not used
-            sc[p] = *reinterpret_cast<const uint16_t *>(scales + (nrow * ks + (uint32_t)kc * 8u + (uint32_t)q * 2u));
+            if (!win)
+                sc[p] = *reinterpret_cast<const uint16_t *>(scales + (nrow * ks + (uint32_t)kc * 8u + (uint32_t)q * 2u));
             cw[p] = *reinterpret_cast<const u32x4 *>(codes + (nrow * kh + (uint32_t)kc * 64u + (uint32_t)q * 16u));
+        }
+        if (win) {
+            // byte 8 p + 2 q of the window: dword 2 p + q / 2, half q % 2
+#pragma unroll
+            for (int p = 0; p < NV_PF; p++) {
+                const u32x4 &w4 = p < 2 ? sw0 : sw1;
+                const uint32_t lo = w4[(2 * p) & 3], hi = w4[(2 * p + 1) & 3];
+                sc[p] = ((q & 2) ? hi : lo) >> ((q & 1) * 16) & 0xFFFFu;
+            }
         }
         // the previous batch's LDS reads come before these writes, and the
         // writes before this batch's reads by other lanes of the wavefront:
@@ -140,7 +161,7 @@ __global__ __launch_bounds__(NV_WAVES * 64) void nvfp4_gemv_kernel(const uint16_
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int p = 0; p < NV_PF; p++) {
-            const int kb = kb0 + p * NV_WAVES;
+            const int kb = kb0 + p;
             if (kb >= KB) break;
             const half2v s0 = e4m3_half2(sc[p] & 0xFFu), s1 = e4m3_half2(sc[p] >> 8);
             const uint16_t *f = fa + p * pstride;
@@ -198,17 +219,20 @@ hipError_t launch_nvfp4_linear(const uint16_t *X, int64_t M, int64_t N, int64_t 
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&nvfp4_gemv_kernel<16>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
+    // the scale windows of a wavefront's batches are 16-byte aligned when
+    // every row starts on 16 bytes (K / 16 a multiple of 16) and so does the array
+    const int vsc = (K % 256 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) ? 1 : 0;
     for (int64_t m0 = 0; m0 < M; m0 += 16) {
         const int m = (int)std::min<int64_t>(16, M - m0);
         const size_t lds = (size_t)NV_WAVES * m * 1024 + NV_ZERO_BYTES + NV_RED_BYTES;
         const dim3 grid((unsigned)blocks), block(NV_WAVES * 64);
         const uint16_t *Xm = X + m0 * K;
         uint16_t *Ym = Y + m0 * N;
-        if (m == 1) nvfp4_gemv_kernel<1><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym);
-        else if (m == 2) nvfp4_gemv_kernel<2><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym);
-        else if (m <= 4) nvfp4_gemv_kernel<4><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym);
-        else if (m <= 8) nvfp4_gemv_kernel<8><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym);
-        else nvfp4_gemv_kernel<16><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym);
+        if (m == 1) nvfp4_gemv_kernel<1><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym, vsc);
+        else if (m == 2) nvfp4_gemv_kernel<2><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym, vsc);
+        else if (m <= 4) nvfp4_gemv_kernel<4><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym, vsc);
+        else if (m <= 8) nvfp4_gemv_kernel<8><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym, vsc);
+        else nvfp4_gemv_kernel<16><<<grid, block, lds, st>>>(Xm, m, (int)N, (int)K, codes, scales, Ym, vsc);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
